@@ -1,0 +1,223 @@
+"""Python binding of libfp8bs (block-scaled FP8 quantization and GEMM on AMD MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels behind the
+C ABI declared in ``include/fp8bs.h``.  PyTorch provides device memory and the current HIP
+stream.  There is no CPU fallback: if the shared library is missing or a GPU is not present,
+calls raise.
+
+Names follow the C ABI: ``quantize_blockwise`` (fp8_quantize_blockwise), ``quantize_delayed``
+(fp8_quantize_delayed), ``gemm_blockscaled`` (fp8_gemm_blockscaled), ``grouped_gemm``
+(fp8_grouped_gemm), ``cast_fp32`` (fp8_cast_fp32).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfp8bs.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "fp8bs.h")
+
+E4M3, E5M2 = 0, 1
+BLOCK_1x128, BLOCK_128x128, PER_TENSOR = 0, 1, 2
+SCALE_FP32, SCALE_POW2 = 0, 1
+FPROP, DGRAD, WGRAD = 0, 1, 2
+
+OK = 0
+ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_WORKSPACE, ERR_ARG = (
+    -1, -2, -3, -4, -5, -6, -7)
+
+
+class Fp8bsError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions include/fp8bs.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load libfp8bs.so (after torch, so that one HIP runtime is shared)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m block_scaled_quantize_amd.build`")
+    lib = ctypes.CDLL(path)
+    i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    lib.fp8bs_status_string.argtypes = [i32]
+    lib.fp8bs_status_string.restype = ctypes.c_char_p
+    lib.fp8_quantize_blockwise.argtypes = [vp, i64, i64, i64, i32, i32, i32, vp, i64, vp, vp]
+    lib.fp8_quantize_delayed.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.fp8_quantize_delayed_workspace_size.argtypes = []
+    lib.fp8_quantize_delayed_workspace_size.restype = sz
+    lib.fp8_cast_fp32.argtypes = [vp, i64, i32, vp, vp]
+    lib.fp8_gemm_blockscaled.argtypes = [i32, i64, i64, i64, vp, i64, i32, i32, vp, vp, i64, i32,
+                                         i32, vp, vp, i64, vp]
+    lib.fp8_grouped_gemm.argtypes = [ctypes.c_int32, vp, i64, i64, i64, vp, i64, i32, vp, vp,
+                                     i64, i32, vp, vp, i64, vp]
+    for name in ("fp8_quantize_blockwise", "fp8_quantize_delayed", "fp8_cast_fp32",
+                 "fp8_gemm_blockscaled", "fp8_grouped_gemm"):
+        getattr(lib, name).restype = i32
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().fp8bs_status_string(status).decode()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != OK:
+        raise Fp8bsError(rc, what)
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    return t.data_ptr()
+
+
+def _ceil(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def scale_shape(rows: int, cols: int, gran: int) -> tuple[int, ...]:
+    """Shape of the dequantization-factor array of a [rows, cols] matrix."""
+    if gran == BLOCK_1x128:
+        return (_ceil(cols, 128), rows)
+    if gran == BLOCK_128x128:
+        return (_ceil(rows, 128), _ceil(cols, 128))
+    return (1,)
+
+
+# ----------------------------------------------------------------------------- quantization
+
+def quantize_blockwise(x: torch.Tensor, fmt: int, gran: int, mode: int = SCALE_FP32,
+                       q: torch.Tensor | None = None, scale_inv: torch.Tensor | None = None,
+                       stream=None):
+    """Blockwise quantization of a 2-D bf16 matrix (rows may be strided).
+
+    Returns (codes uint8 [rows, cols], scale_inv float32 in the C ABI layout)."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 matrix with unit column stride")
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if scale_inv is None:
+        scale_inv = torch.empty(scale_shape(rows, cols, gran), dtype=torch.float32, device=x.device)
+    _check(load().fp8_quantize_blockwise(_ptr(x), rows, cols, x.stride(0), fmt, gran, mode,
+                                         _ptr(q), q.stride(0), _ptr(scale_inv), _stream(stream)),
+           "fp8_quantize_blockwise")
+    return q, scale_inv
+
+
+def delayed_workspace_size() -> int:
+    return int(load().fp8_quantize_delayed_workspace_size())
+
+
+class DelayedState:
+    """Device-resident delayed-scaling state: amax history (newest first) and scale."""
+
+    def __init__(self, hist_len: int = 16, device="cuda"):
+        self.hist_len = hist_len
+        self.history = torch.zeros(hist_len, dtype=torch.float32, device=device)
+        self.scale = torch.ones(1, dtype=torch.float32, device=device)
+        self.workspace = torch.empty(delayed_workspace_size(), dtype=torch.uint8, device=device)
+
+
+def quantize_delayed(x: torch.Tensor, fmt: int, state: DelayedState, mode: int = SCALE_FP32,
+                     margin: int = 0, q: torch.Tensor | None = None,
+                     scale_inv_used: torch.Tensor | None = None, stream=None):
+    """One delayed-scaling step on a contiguous bf16 tensor; advances ``state`` on the device.
+
+    Returns (codes uint8 with x's shape, scale_inv_used float32[1])."""
+    if x.dtype != torch.bfloat16 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bf16 tensor")
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scale_inv_used is None:
+        scale_inv_used = torch.empty(1, dtype=torch.float32, device=x.device)
+    _check(load().fp8_quantize_delayed(_ptr(x), x.numel(), fmt, mode, margin, state.hist_len,
+                                       _ptr(state.history), _ptr(state.scale), _ptr(q),
+                                       _ptr(scale_inv_used), _ptr(state.workspace),
+                                       state.workspace.numel(), _stream(stream)),
+           "fp8_quantize_delayed")
+    return q, scale_inv_used
+
+
+def cast_fp32(x: torch.Tensor, fmt: int, q: torch.Tensor | None = None, stream=None):
+    """Saturating RNE cast of fp32 values to FP8 codes."""
+    if x.dtype != torch.float32 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous fp32 tensor")
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _check(load().fp8_cast_fp32(_ptr(x), x.numel(), fmt, _ptr(q), _stream(stream)), "fp8_cast_fp32")
+    return q
+
+
+# ----------------------------------------------------------------------------- GEMM
+
+def gemm_blockscaled(layout: int, a: torch.Tensor, fa: int, ga: int, sa: torch.Tensor,
+                     b: torch.Tensor, fb: int, gb: int, sb: torch.Tensor,
+                     c: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Block-scaled FP8 GEMM, bf16 output.  a, b are uint8 code matrices as stored:
+    FPROP a[M,K], b[N,K]; DGRAD a[M,K], b[K,N]; WGRAD a[K,M], b[K,N]."""
+    if a.dtype != torch.uint8 or b.dtype != torch.uint8 or a.dim() != 2 or b.dim() != 2:
+        raise ValueError("a and b must be 2-D uint8 code matrices")
+    if layout == FPROP:
+        (M, K), N = a.shape, b.shape[0]
+        if b.shape[1] != K:
+            raise ValueError("K mismatch")
+    elif layout == DGRAD:
+        (M, K), N = a.shape, b.shape[1]
+        if b.shape[0] != K:
+            raise ValueError("K mismatch")
+    elif layout == WGRAD:
+        (K, M), N = a.shape, b.shape[1]
+        if b.shape[0] != K:
+            raise ValueError("K mismatch")
+    else:
+        raise ValueError("unknown layout")
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _check(load().fp8_gemm_blockscaled(layout, M, N, K, _ptr(a), a.stride(0), fa, ga, _ptr(sa),
+                                       _ptr(b), b.stride(0), fb, gb, _ptr(sb), _ptr(c),
+                                       c.stride(0), _stream(stream)), "fp8_gemm_blockscaled")
+    return c
+
+
+def grouped_gemm(offsets: torch.Tensor, a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor,
+                 sb: torch.Tensor, fa: int = E4M3, fb: int = E4M3,
+                 c: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Grouped FP8 GEMM: rows [offsets[g], offsets[g+1]) of a[total_M, K] times b[g][N, K]^T.
+    offsets is a device int64 tensor of num_groups + 1 entries."""
+    if offsets.dtype != torch.int64 or b.dim() != 3:
+        raise ValueError("offsets must be int64 and b must be [G, N, K]")
+    G, N, K = b.shape
+    total_m = a.shape[0]
+    if c is None:
+        c = torch.empty((total_m, N), dtype=torch.bfloat16, device=a.device)
+    _check(load().fp8_grouped_gemm(G, _ptr(offsets), total_m, N, K, _ptr(a), a.stride(0), fa,
+                                   _ptr(sa), _ptr(b), b.stride(1), fb, _ptr(sb), _ptr(c),
+                                   c.stride(0), _stream(stream)), "fp8_grouped_gemm")
+    return c

@@ -1,0 +1,613 @@
+// Block-scaled FP8 GEMM for gfx950 (CDNA4): dense fprop / dgrad / wgrad and grouped (MoE).
+//
+// Method: "NVIDIA NeMo RL logra una aceleración del 48% con entrenamiento de precisión FP8 de
+// extremo a extremo", section "El avance técnico": linear layers run FP8 math on 128x128 weight
+// tiles and 1x128 activation blocks, output BF16; section "Ganancias de rendimiento en el
+// mundo real": the same recipe on an MoE model's experts.  Gradients may be E5M2
+// ("Infraestructura de Entrenamiento FP8 ...", section "El panorama de la precisión numérica").
+//
+// Design
+//  * Output tile BM x 128 per workgroup of 4 waves (2 x 2), 128-byte K blocks, so one K block is
+//    exactly one scale block.  Each wave owns a (BM/2) x 64 sub-tile made of 16x16 pieces.
+//  * One V_MFMA_F32_16X16X128_F8F6F4 consumes a full 128-wide K block: its fp32 result P is the
+//    partial sum of one scale block, folded as acc += P * (sa[m, kb] * sb[n-block, kb]).  With
+//    per-tensor scales on both operands the MFMA accumulates directly and the product of the two
+//    scales is applied once in the epilogue.
+//  * The MFMA's "A" operand is the weight side (rows = n) and its "B" operand the activation side
+//    (columns = m), so each lane ends with 4 consecutive n of one output row: 8-byte bf16 stores.
+//  * Global -> LDS by buffer_load ... lds (no VGPR staging), 3 LDS stages so loads run two K
+//    blocks ahead; bounds come from the buffer descriptors (rows past the matrix read as zero).
+//  * LDS tiles are rows of 128 bytes with a 16-byte-chunk XOR swizzle (chunk ^ (row & 7)).
+//    K-major operands (rows = m or n) are read with ds_read_b128; MN-major operands (rows = k,
+//    dgrad / wgrad) are read with ds_read_b64_tr_b8, which transposes 8x8 byte blocks across
+//    lanes, so no separate transpose pass is needed.
+//  * Workgroup ids are remapped so that each XCD (ids round-robin over 8 XCDs) works on a
+//    compact group of tiles and its L2 is reused.
+#include <float.h>
+
+#include <algorithm>
+
+#include "common.h"
+
+namespace fp8bs {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+constexpr int kThreads = 256;
+constexpr int kBN = 128;
+constexpr int kStages = 3;
+constexpr int kGroupM = 8;  // tile-rows per L2 group in the tile order
+
+template <int BM>
+struct Tile {
+  static constexpr int kXBytes = BM * 128;
+  static constexpr int kWBytes = kBN * 128;
+  static constexpr int kSaBytes = BM * 4;
+  static constexpr int kStage = kXBytes + kWBytes + kSaBytes;
+  static constexpr int kLds = kStage * kStages;
+  static constexpr int kWM = BM / 2;         // rows of m per wave
+  static constexpr int kNJ = kWM / 16;       // 16-wide m pieces per wave
+  static constexpr int kXLoads = BM / 32;    // 1 KB DMA blocks of the X tile per wave
+  static constexpr int kWLoads = kBN / 32;   // ... of the W tile per wave
+  static constexpr int kSaWaves = BM / 64;   // waves that load 64 scale words each
+};
+
+struct GemmParams {
+  int64_t M, N, K;
+  const uint8_t* A;   // activation side (rows m)
+  int64_t lda;
+  const uint8_t* B;   // weight side (rows n)
+  int64_t ldb;
+  const float* sa;    // sa(m, kb) = sa[kb * sa_ks + (m / sa_rdiv) * sa_rs]
+  int64_t sa_ks, sa_rs, sa_bytes;
+  int sa_rdiv;
+  const float* sb;    // sb(n, kb) = sb[kb * sb_ks + (n / 128) * sb_rs]
+  int64_t sb_ks, sb_rs;
+  uint16_t* C;
+  int64_t ldc;
+  int tiles_m, tiles_n;
+  int c_vec;          // 8-byte output stores are aligned
+  // grouped GEMM only
+  const int64_t* offsets;
+  int num_groups;
+  int64_t b_group_stride;   // bytes between experts' weights
+  int64_t sb_group_stride;  // floats between experts' scales
+};
+
+// ------------------------------------------------------------------ low-level helpers
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, uint64_t nbytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t n = nbytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)nbytes;
+  u32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));   // stride 0
+  r.z = __builtin_amdgcn_readfirstlane(n);
+  r.w = 0x00020000u;                                           // raw 32-bit data format
+  return r;
+}
+
+// 16 bytes per lane from buffer offset voff to LDS address lds + 16 * lane.  Offsets at or past
+// the descriptor's size read as zero.
+__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(lds) : "memory", "m0");
+}
+// 4 bytes per lane to LDS address lds + 4 * lane.
+__device__ __forceinline__ void dma4(u32x4 rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(lds) : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding (N < 64).  The
+// empty asm statements keep the compiler from moving LDS accesses across the wait.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (outstanding LDS DMA is tracked
+// explicitly with wait_vm); also a compiler barrier for memory accesses.
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>(p);
+}
+
+// K-major tile fragment: 32 bytes k = 32g .. 32g+31 of tile row r.
+__device__ __forceinline__ v8i frag_kmajor(const uint8_t* tile, int r, int g) {
+  const uint8_t* row = tile + r * 128;
+  const int sw = r & 7;
+  uint4 lo = *reinterpret_cast<const uint4*>(row + (((2 * g) ^ sw) << 4));
+  uint4 hi = *reinterpret_cast<const uint4*>(row + (((2 * g + 1) ^ sw) << 4));
+  v8i v;
+  v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+  v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  return v;
+}
+
+// MN-major tile fragment (tile = [halves][128 k][128 cols]): 32 bytes k = 32g .. 32g+31 of
+// column c = col0 + li (col0 a multiple of 16).  Four 8x8 byte transposes across lanes: source
+// lane 2j + h of each 16-lane group points at row k0 + j, bytes col0 + 8h .. +8.
+__device__ __forceinline__ v8i frag_mnmajor(const uint8_t* tile, int col0, int li, int g) {
+  const uint8_t* half = tile + (col0 >> 7) * 16384;
+  const int chunk = (col0 & 127) >> 4;
+  v8i v;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int k = 32 * g + 8 * t + (li >> 1);
+    const uint8_t* p = half + k * 128 + ((chunk ^ (k & 7)) << 4) + 8 * (li & 1);
+    v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)p);
+    v[2 * t] = r.x;
+    v[2 * t + 1] = r.y;
+  }
+  return v;
+}
+
+template <bool KMAJOR>
+__device__ __forceinline__ v8i fragment(const uint8_t* tile, int idx, int li, int g) {
+  if constexpr (KMAJOR) return frag_kmajor(tile, idx, g);
+  else return frag_mnmajor(tile, idx - li, li, g);
+}
+
+// Per-lane DMA source offsets for a tile side.  K-major: rows of the tile are matrix rows
+// (m or n), the K block starts at the descriptor base.  MN-major: rows of the tile are k, the
+// 128-column halves sit at +128 * h.  Instruction q of the tile covers LDS bytes
+// [1024 q, 1024 q + 1024) = 8 rows of 128 bytes; lane i fills row 8q' + i / 8 at physical
+// chunk i % 8, whose logical chunk is (i % 8) ^ (i / 8).
+template <bool KMAJOR>
+__device__ __forceinline__ uint32_t dma_voffset(int q, int lane, int64_t ld) {
+  const int rl = lane >> 3;
+  const int c = (lane & 7) ^ rl;
+  if constexpr (KMAJOR) {
+    return (uint32_t)((int64_t)(8 * q + rl) * ld + 16 * c);
+  } else {
+    const int h = q >> 4, qq = q & 15;
+    return (uint32_t)((int64_t)(8 * qq + rl) * ld + 128 * h + 16 * c);
+  }
+}
+
+// Zero the bytes of a K-major tile whose k is at or beyond krem (last, partial K block).
+template <int ROWS>
+__device__ __forceinline__ void zero_k_tail(uint8_t* tile, int krem) {
+  for (int id = threadIdx.x; id < ROWS * 8; id += kThreads) {
+    const int r = id >> 3, c = id & 7;
+    uint8_t* p = tile + r * 128 + ((c ^ (r & 7)) << 4);
+    if (16 * c >= krem) {
+      *reinterpret_cast<uint4*>(p) = make_uint4(0, 0, 0, 0);
+    } else if (16 * c + 16 > krem) {
+      for (int b = krem - 16 * c; b < 16; ++b) p[b] = 0;
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  bf2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// ------------------------------------------------------------------ one output tile
+// Computes C[m0 .. m_end) x [n0 .. n0 + 128) (columns clipped to N) with the operand roles of
+// LAYOUT; A points at the activation-side matrix, Bw at the weight-side matrix of this tile's
+// group, sbw at the group's weight scales.
+template <int LAYOUT, int FA, int FB, bool FOLD, int BM>
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, int64_t m0,
+                                          int64_t m_end, int64_t n0, const uint8_t* Bw,
+                                          const float* sbw) {
+  using T = Tile<BM>;
+  constexpr bool XK = LAYOUT != FP8BS_WGRAD;   // activation side K-major?
+  constexpr bool WK = LAYOUT == FP8BS_FPROP;   // weight side K-major?
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int wm = w & 1, wn = w >> 1;
+  const int li = lane & 15, g = lane >> 4;
+  const int64_t K = p.K;
+  const int nkb = (int)((K + 127) >> 7);
+  const int krem = (int)(K - (int64_t)(nkb - 1) * 128);
+  const uint32_t lds0 = lds_addr(smem);
+
+  // DMA source offsets (fixed across K blocks) and LDS destinations (per stage + offset).
+  uint32_t xoff[T::kXLoads], woff[T::kWLoads];
+#pragma unroll
+  for (int q = 0; q < T::kXLoads; ++q) xoff[q] = dma_voffset<XK>(w * T::kXLoads + q, lane, p.lda);
+#pragma unroll
+  for (int q = 0; q < T::kWLoads; ++q) woff[q] = dma_voffset<WK>(w * T::kWLoads + q, lane, p.ldb);
+  const bool sa_loader = w < T::kSaWaves;
+  uint32_t saoff = 0xFFFFFFFFu;
+  {
+    const int64_t row = m0 + w * 64 + lane;
+    if (row < m_end) saoff = (uint32_t)(((row / p.sa_rdiv) * p.sa_rs) * 4);
+  }
+
+  // Bytes of each operand addressable from the K block's base (bounds of the descriptors).
+  const int64_t a_rows = XK ? m_end : K;           // rows of the stored activation matrix
+  const int64_t w_rows = WK ? p.N : K;
+
+  auto issue = [&](int kb) {
+    const int st = kb % kStages;
+    const uint32_t sbase = lds0 + st * T::kStage;
+    const int64_t k0 = (int64_t)kb * 128;
+    // activation side
+    {
+      const uint8_t* base;
+      int64_t avail;
+      if constexpr (XK) {
+        base = p.A + m0 * p.lda + k0;
+        avail = (a_rows - m0) * p.lda - k0;
+      } else {
+        base = p.A + k0 * p.lda + m0;
+        avail = (a_rows - k0) * p.lda - m0;
+      }
+      const u32x4 r = make_rsrc(base, avail > 0 ? (uint64_t)avail : 0);
+#pragma unroll
+      for (int q = 0; q < T::kXLoads; ++q)
+        dma16(r, xoff[q], __builtin_amdgcn_readfirstlane(sbase + (w * T::kXLoads + q) * 1024));
+    }
+    // weight side
+    {
+      const uint8_t* base;
+      int64_t avail;
+      if constexpr (WK) {
+        base = Bw + n0 * p.ldb + k0;
+        avail = (w_rows - n0) * p.ldb - k0;
+      } else {
+        base = Bw + k0 * p.ldb + n0;
+        avail = (w_rows - k0) * p.ldb - n0;
+      }
+      const u32x4 r = make_rsrc(base, avail > 0 ? (uint64_t)avail : 0);
+#pragma unroll
+      for (int q = 0; q < T::kWLoads; ++q)
+        dma16(r, woff[q], __builtin_amdgcn_readfirstlane(sbase + T::kXBytes + (w * T::kWLoads + q) * 1024));
+    }
+    // activation scales of the K block (one word per tile row)
+    if constexpr (FOLD) {
+      if (sa_loader) {
+        const int64_t off = kb * p.sa_ks;
+        const u32x4 r = make_rsrc(p.sa + off, (uint64_t)(p.sa_bytes - off * 4));
+        dma4(r, saoff, __builtin_amdgcn_readfirstlane(sbase + T::kXBytes + T::kWBytes + w * 256));
+      }
+    }
+  };
+  // loads per K block issued by this wave (the vmcnt bookkeeping is per wave)
+  constexpr int kPerStage = T::kXLoads + T::kWLoads;
+  const int per_stage = kPerStage + ((FOLD && sa_loader) ? 1 : 0);
+
+  v4f acc[4][T::kNJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < T::kNJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  if (nkb > 0) issue(0);
+  if (nkb > 1) issue(1);
+  const int64_t nblk = n0 >> 7;
+  for (int kb = 0; kb < nkb; ++kb) {
+    // Stage kb must have landed: only stage kb+1's loads may still be outstanding.
+    if (kb + 1 < nkb) {
+      if (per_stage == kPerStage + 1) wait_vm<kPerStage + 1>();
+      else wait_vm<kPerStage>();
+    } else {
+      wait_vm<0>();
+    }
+    barrier();
+    if (kb + 2 < nkb) issue(kb + 2);
+    uint8_t* st = smem + (kb % kStages) * T::kStage;
+    const uint8_t* xt = st;
+    const uint8_t* wt = st + T::kXBytes;
+    const float* sat = reinterpret_cast<const float*>(st + T::kXBytes + T::kWBytes);
+    if (kb == nkb - 1 && krem < 128 && (XK || WK)) {
+      if constexpr (XK) zero_k_tail<BM>(st, krem);
+      if constexpr (WK) zero_k_tail<kBN>(st + T::kXBytes, krem);
+      __syncthreads();
+    }
+    float sbv = 1.0f;
+    if constexpr (FOLD) sbv = sbw[kb * p.sb_ks + nblk * p.sb_rs];
+
+    v8i wf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wf[i] = fragment<WK>(wt, wn * 64 + 16 * i + li, li, g);
+#pragma unroll
+    for (int j = 0; j < T::kNJ; ++j) {
+      const int mrow = wm * T::kWM + 16 * j + li;
+      const v8i xf = fragment<XK>(xt, mrow, li, g);
+      if constexpr (FOLD) {
+        const float c = sat[mrow] * sbv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const v4f pv = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              wf[i], xf, v4f{0.f, 0.f, 0.f, 0.f}, FB, FA, 0, 0, 0, 0);
+          acc[i][j] += pv * c;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[i], xf, acc[i][j], FB,
+                                                                       FA, 0, 0, 0, 0);
+      }
+    }
+    // every wave is done with this stage before it is refilled two iterations later: the
+    // barrier at the top of the next iteration orders it.
+  }
+
+  float post = 1.0f;
+  if constexpr (!FOLD) post = nkb > 0 ? p.sa[0] * sbw[0] : 0.0f;
+
+  // Epilogue: lane holds C[m][n .. n+3] of each piece.
+#pragma unroll
+  for (int j = 0; j < T::kNJ; ++j) {
+    const int64_t m = m0 + wm * T::kWM + 16 * j + li;
+    if (m >= m_end) continue;
+    uint16_t* crow = p.C + m * p.ldc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t n = n0 + wn * 64 + 16 * i + 4 * g;
+      v4f v = acc[i][j];
+      if constexpr (!FOLD) v = v * post;
+      if (nkb == 0) v = v4f{0.f, 0.f, 0.f, 0.f};
+      const uint32_t lo = pack_bf16x2(v[0], v[1]);
+      const uint32_t hi = pack_bf16x2(v[2], v[3]);
+      if (p.c_vec && n + 4 <= p.N) {
+        *reinterpret_cast<uint2*>(crow + n) = make_uint2(lo, hi);
+      } else {
+        const uint16_t h[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < p.N) crow[n + e] = h[e];
+      }
+    }
+  }
+}
+
+// Map a linear workgroup id to a tile so that each of the 8 XCDs (ids are dealt round robin)
+// gets a contiguous range of tiles, ordered in groups of kGroupM tile-rows for L2 reuse.
+__device__ __forceinline__ void tile_of(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  const int q = total / 8, r = total % 8;
+  const int xcd = id % 8, local = id / 8;
+  const int pid = xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+  const int width = kGroupM * tiles_n;
+  const int grp = pid / width;
+  const int first = grp * kGroupM;
+  const int gsz = min(tiles_m - first, kGroupM);
+  const int in = pid % width;
+  tm = first + in % gsz;
+  tn = in / gsz;
+}
+
+template <int LAYOUT, int FA, int FB, bool FOLD, int BM>
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int tm, tn;
+  tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM;
+  gemm_tile<LAYOUT, FA, FB, FOLD, BM>(p, smem, m0, std::min<int64_t>(m0 + BM, p.M),
+                                      (int64_t)tn * kBN, p.B, p.sb);
+}
+
+// Grouped: a persistent grid walks the concatenation of every group's m tiles (times the n
+// tiles).  Each workgroup first builds the prefix count of m tiles per group in LDS, then maps
+// each of its tiles to (group, m tile, n tile) by binary search.
+constexpr int kMaxGroups = 1024;
+
+template <int FA, int FB, int BM>
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int s_prefix[kMaxGroups + 1];
+  __shared__ int s_wave_sum[kThreads / 64];
+  const int G = p.num_groups;
+  // tiles per group (offsets are clamped to [0, M] and made non-decreasing)
+  int carry = 0;
+  for (int base = 0; base < G; base += kThreads) {
+    const int gi = base + threadIdx.x;
+    int tiles = 0;
+    if (gi < G) {
+      const int64_t lo = std::min<int64_t>(std::max<int64_t>(p.offsets[gi], 0), p.M);
+      const int64_t hi = std::min<int64_t>(std::max<int64_t>(p.offsets[gi + 1], lo), p.M);
+      tiles = (int)((hi - lo + BM - 1) / BM);
+    }
+    // inclusive scan across the workgroup
+    int v = tiles;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(v, off);
+      if (lane >= off) v += o;
+    }
+    if (lane == 63) s_wave_sum[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int before = carry;
+    for (int w = 0; w < (int)(threadIdx.x >> 6); ++w) before += s_wave_sum[w];
+    if (gi < G) s_prefix[gi + 1] = before + v;
+    int total = carry;
+    for (int w = 0; w < kThreads / 64; ++w) total += s_wave_sum[w];
+    carry = total;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) s_prefix[0] = 0;
+  __syncthreads();
+  const int m_tiles = s_prefix[G];
+  const int total = m_tiles * p.tiles_n;
+  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    const int mt = tile / p.tiles_n, tn = tile % p.tiles_n;
+    int lo = 0, hi = G - 1;   // last group with s_prefix[g] <= mt
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_prefix[mid] <= mt) lo = mid; else hi = mid - 1;
+    }
+    const int gi = lo;
+    const int64_t glo = std::min<int64_t>(std::max<int64_t>(p.offsets[gi], 0), p.M);
+    const int64_t ghi = std::min<int64_t>(std::max<int64_t>(p.offsets[gi + 1], glo), p.M);
+    const int64_t m0 = glo + (int64_t)(mt - s_prefix[gi]) * BM;
+    gemm_tile<FP8BS_FPROP, FA, FB, true, BM>(p, smem, m0, std::min<int64_t>(m0 + BM, ghi),
+                                             (int64_t)tn * kBN, p.B + gi * p.b_group_stride,
+                                             p.sb + gi * p.sb_group_stride);
+    __syncthreads();   // the next tile refills the LDS stages
+  }
+}
+
+template <typename KernelT>
+int launch_gemm(KernelT kernel, int blocks, int lds, hipStream_t st, const GemmParams& p) {
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+    return FP8BS_ERR_LAUNCH;
+  void* args[] = {const_cast<GemmParams*>(&p)};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(blocks),
+                                 dim3(kThreads), args, lds, st);
+  return e == hipSuccess ? FP8BS_OK : FP8BS_ERR_LAUNCH;
+}
+
+template <int LAYOUT, int FA, int FB>
+int dispatch_fold(bool fold, bool small_m, const GemmParams& p, hipStream_t st) {
+  constexpr int kBig = 256, kSmall = 128;
+  if (small_m) {
+    const int blocks = p.tiles_m * p.tiles_n;
+    return fold ? launch_gemm(gemm_kernel<LAYOUT, FA, FB, true, kSmall>, blocks, Tile<kSmall>::kLds, st, p)
+                : launch_gemm(gemm_kernel<LAYOUT, FA, FB, false, kSmall>, blocks, Tile<kSmall>::kLds, st, p);
+  }
+  const int blocks = p.tiles_m * p.tiles_n;
+  return fold ? launch_gemm(gemm_kernel<LAYOUT, FA, FB, true, kBig>, blocks, Tile<kBig>::kLds, st, p)
+              : launch_gemm(gemm_kernel<LAYOUT, FA, FB, false, kBig>, blocks, Tile<kBig>::kLds, st, p);
+}
+
+template <int LAYOUT>
+int dispatch_formats(int fa, int fb, bool fold, bool small_m, const GemmParams& p,
+                     hipStream_t st) {
+  if (fa == FP8BS_E4M3 && fb == FP8BS_E4M3) return dispatch_fold<LAYOUT, FP8BS_E4M3, FP8BS_E4M3>(fold, small_m, p, st);
+  if (fa == FP8BS_E5M2 && fb == FP8BS_E4M3) return dispatch_fold<LAYOUT, FP8BS_E5M2, FP8BS_E4M3>(fold, small_m, p, st);
+  if (fa == FP8BS_E4M3 && fb == FP8BS_E5M2) return dispatch_fold<LAYOUT, FP8BS_E4M3, FP8BS_E5M2>(fold, small_m, p, st);
+  return dispatch_fold<LAYOUT, FP8BS_E5M2, FP8BS_E5M2>(fold, small_m, p, st);
+}
+
+// Scale indexing for one operand.  rows: the operand's output dimension (m or n);
+// kmajor: the operand is stored [rows, K] (else [K, rows]).
+struct ScaleIndex {
+  int64_t ks, rs, bytes;
+  int rdiv;
+};
+
+bool scale_index(int gran, bool kmajor, bool weight_side, int64_t rows, int64_t K,
+                 ScaleIndex& s) {
+  const int64_t kblocks = ceil_div(K, 128), rblocks = ceil_div(rows, 128);
+  if (gran == FP8BS_PER_TENSOR) {
+    s = {0, 0, 4, 1};
+    return true;
+  }
+  if (gran == FP8BS_BLOCK_1x128) {
+    if (!kmajor || weight_side) return false;   // 1x128 must run along K, activation side only
+    s = {rows, 1, kblocks * rows * 4, 1};       // float[K/128][rows]
+    return true;
+  }
+  if (gran == FP8BS_BLOCK_128x128) {
+    if (kmajor) s = {1, kblocks, rblocks * kblocks * 4, 128};   // float[rows/128][K/128]
+    else s = {rblocks, 1, kblocks * rblocks * 4, 128};          // float[K/128][rows/128]
+    return true;
+  }
+  return false;
+}
+
+}  // namespace
+}  // namespace fp8bs
+
+using namespace fp8bs;
+
+extern "C" int fp8_gemm_blockscaled(int layout, int64_t M, int64_t N, int64_t K, const void* A,
+                                    int64_t lda, int fa, int ga, const float* scale_inv_a,
+                                    const void* B, int64_t ldb, int fb, int gb,
+                                    const float* scale_inv_b, void* C_bf16, int64_t ldc,
+                                    void* stream) {
+  if (layout < FP8BS_FPROP || layout > FP8BS_WGRAD || !fmt_ok(fa) || !fmt_ok(fb) || ga < 0 ||
+      ga > 2 || gb < 0 || gb > 2)
+    return FP8BS_ERR_ARG;
+  if (M < 0 || N < 0 || K < 0) return FP8BS_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP8BS_OK;
+  if (!C_bf16 || (K > 0 && (!A || !B || !scale_inv_a || !scale_inv_b))) return FP8BS_ERR_NULL;
+  const bool xk = layout != FP8BS_WGRAD, wk = layout == FP8BS_FPROP;
+  const int64_t a_width = xk ? K : M, b_width = wk ? K : N;
+  if (ldc < N || (K > 0 && (lda < a_width || ldb < b_width))) return FP8BS_ERR_SHAPE;
+  // 32-bit buffer offsets inside a tile: 256 rows of the pitch must stay below 2^31.
+  if (lda >= (int64_t(1) << 23) || ldb >= (int64_t(1) << 23)) return FP8BS_ERR_SHAPE;
+  if (M > (int64_t(1) << 31) - 256 || N > (int64_t(1) << 31) - 256) return FP8BS_ERR_SHAPE;
+  if (K > 0 && (!aligned16(A) || !aligned16(B) || lda % 16 || ldb % 16)) return FP8BS_ERR_ALIGN;
+  if (!aligned4(C_bf16) || ldc % 2) return FP8BS_ERR_ALIGN;
+  ScaleIndex sa{}, sb{};
+  if (!scale_index(ga, xk, false, M, K, sa) || !scale_index(gb, wk, true, N, K, sb))
+    return FP8BS_ERR_UNSUPPORTED;
+  GemmParams p{};
+  p.M = M; p.N = N; p.K = K;
+  p.A = static_cast<const uint8_t*>(A); p.lda = lda;
+  p.B = static_cast<const uint8_t*>(B); p.ldb = ldb;
+  p.sa = scale_inv_a; p.sa_ks = sa.ks; p.sa_rs = sa.rs; p.sa_bytes = sa.bytes; p.sa_rdiv = sa.rdiv;
+  p.sb = scale_inv_b; p.sb_ks = sb.ks; p.sb_rs = sb.rs;
+  p.C = static_cast<uint16_t*>(C_bf16); p.ldc = ldc;
+  p.c_vec = (reinterpret_cast<uintptr_t>(C_bf16) % 8 == 0) && (ldc % 4 == 0);
+  const bool small_m = M <= 128 * 64;   // more, smaller tiles while the grid is under-filled
+  const int bm = small_m ? 128 : 256;
+  p.tiles_m = (int)ceil_div(M, bm);
+  p.tiles_n = (int)ceil_div(N, kBN);
+  if ((int64_t)p.tiles_m * p.tiles_n > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
+  const bool fold = !(ga == FP8BS_PER_TENSOR && gb == FP8BS_PER_TENSOR);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (layout) {
+    case FP8BS_FPROP: return dispatch_formats<FP8BS_FPROP>(fa, fb, fold, small_m, p, st);
+    case FP8BS_DGRAD: return dispatch_formats<FP8BS_DGRAD>(fa, fb, fold, small_m, p, st);
+    default: return dispatch_formats<FP8BS_WGRAD>(fa, fb, fold, small_m, p, st);
+  }
+}
+
+extern "C" int fp8_grouped_gemm(int32_t num_groups, const int64_t* group_offsets,
+                                int64_t total_M, int64_t N, int64_t K, const void* A,
+                                int64_t lda, int fa, const float* scale_inv_a, const void* B,
+                                int64_t ldb, int fb, const float* scale_inv_b, void* C_bf16,
+                                int64_t ldc, void* stream) {
+  if (!fmt_ok(fa) || !fmt_ok(fb) || num_groups < 0 || num_groups > kMaxGroups)
+    return FP8BS_ERR_ARG;
+  if (total_M < 0 || N < 0 || K < 0) return FP8BS_ERR_SHAPE;
+  if (total_M == 0 || N == 0 || num_groups == 0) return FP8BS_OK;
+  if (K == 0) return FP8BS_ERR_SHAPE;
+  if (!group_offsets || !A || !B || !scale_inv_a || !scale_inv_b || !C_bf16) return FP8BS_ERR_NULL;
+  if (lda < K || ldb < K || ldc < N) return FP8BS_ERR_SHAPE;
+  if (lda >= (int64_t(1) << 23) || ldb >= (int64_t(1) << 23)) return FP8BS_ERR_SHAPE;
+  if (total_M > (int64_t(1) << 31) - 256 || N > (int64_t(1) << 31) - 256) return FP8BS_ERR_SHAPE;
+  if (!aligned16(A) || !aligned16(B) || lda % 16 || ldb % 16) return FP8BS_ERR_ALIGN;
+  if (!aligned4(C_bf16) || ldc % 2 || (reinterpret_cast<uintptr_t>(group_offsets) & 7))
+    return FP8BS_ERR_ALIGN;
+  constexpr int BM = 128;
+  GemmParams p{};
+  p.M = total_M; p.N = N; p.K = K;
+  p.A = static_cast<const uint8_t*>(A); p.lda = lda;
+  p.B = static_cast<const uint8_t*>(B); p.ldb = ldb;
+  p.sa = scale_inv_a; p.sa_ks = total_M; p.sa_rs = 1; p.sa_rdiv = 1;
+  p.sa_bytes = ceil_div(K, 128) * total_M * 4;
+  p.sb = scale_inv_b; p.sb_ks = 1; p.sb_rs = ceil_div(K, 128);
+  p.C = static_cast<uint16_t*>(C_bf16); p.ldc = ldc;
+  p.c_vec = (reinterpret_cast<uintptr_t>(C_bf16) % 8 == 0) && (ldc % 4 == 0);
+  p.tiles_n = (int)ceil_div(N, kBN);
+  p.tiles_m = (int)(ceil_div(total_M, BM) + num_groups);   // upper bound on m tiles
+  p.offsets = group_offsets;
+  p.num_groups = num_groups;
+  p.b_group_stride = N * ldb;
+  p.sb_group_stride = ceil_div(N, 128) * ceil_div(K, 128);
+  if ((int64_t)p.tiles_m * p.tiles_n > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int blocks = (int)std::min<int64_t>((int64_t)p.tiles_m * p.tiles_n, std::max(cus, 1));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  constexpr int lds = Tile<BM>::kLds;
+  if (fa == FP8BS_E4M3 && fb == FP8BS_E4M3) return launch_gemm(grouped_gemm_kernel<FP8BS_E4M3, FP8BS_E4M3, BM>, blocks, lds, st, p);
+  if (fa == FP8BS_E5M2 && fb == FP8BS_E4M3) return launch_gemm(grouped_gemm_kernel<FP8BS_E5M2, FP8BS_E4M3, BM>, blocks, lds, st, p);
+  if (fa == FP8BS_E4M3 && fb == FP8BS_E5M2) return launch_gemm(grouped_gemm_kernel<FP8BS_E4M3, FP8BS_E5M2, BM>, blocks, lds, st, p);
+  return launch_gemm(grouped_gemm_kernel<FP8BS_E5M2, FP8BS_E5M2, BM>, blocks, lds, st, p);
+}

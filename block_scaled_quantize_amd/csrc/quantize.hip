@@ -1,0 +1,380 @@
+// FP8 quantization kernels for gfx950: blockwise (1x128 / 128x128) and per-tensor delayed.
+//
+// Method: "NVIDIA NeMo RL logra una aceleración del 48% con entrenamiento de precisión FP8 de
+// extremo a extremo", section "El avance técnico" (E4M3 blocks: 1x128 for activations,
+// 128x128 for weights) and section "Por qué esto es importante para la economía de la IA"
+// (power-of-2 scales); "Infraestructura de Entrenamiento FP8: Precisión Numérica de Nueva
+// Generación", section "Transformer Engine: la base de software" (delayed scaling with an amax
+// history) and section "El panorama de la precisión numérica" (E4M3 / E5M2).
+//
+// Design (HBM-bound, one pass): each block is read once into registers, its amax is reduced
+// in registers (packed 16-bit max over magnitude bits, then DPP across the lanes that share
+// the block), the scale is computed in the same pass, and the scaled values are converted
+// with the packed hardware FP8 convert and written once.  Every lane moves 32 bytes of input
+// (two 16-byte loads) and 16 bytes of output (one 16-byte store) per 16 elements.
+#include <float.h>
+
+#include "common.h"
+
+namespace fp8bs {
+namespace {
+
+constexpr int kThreads = 256;
+
+// ---------------------------------------------------------------- element access
+// Load 16 consecutive bf16 of row r starting at column c0 into 8 dwords.  Elements outside the
+// matrix read as +0 (they do not change an amax).  VEC: 16-byte aligned rows.
+template <bool VEC>
+__device__ __forceinline__ void load16(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                       int64_t ld, int64_t r, int64_t c0, uint32_t (&d)[8]) {
+  if (r >= rows || c0 >= cols) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) d[i] = 0u;
+    return;
+  }
+  const uint16_t* p = x + r * ld + c0;
+  if (VEC && c0 + 16 <= cols) {
+    uint4 a = *reinterpret_cast<const uint4*>(p);
+    uint4 b = *reinterpret_cast<const uint4*>(p + 8);
+    d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w;
+    d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t lo = (c0 + 2 * i < cols) ? (uint32_t)p[2 * i] : 0u;
+    uint32_t hi = (c0 + 2 * i + 1 < cols) ? (uint32_t)p[2 * i + 1] : 0u;
+    d[i] = lo | (hi << 16);
+  }
+}
+
+// Store 16 codes of row r starting at column c0 (only those inside the matrix).
+template <bool VEC>
+__device__ __forceinline__ void store16(uint8_t* __restrict__ q, int64_t rows, int64_t cols,
+                                        int64_t ld, int64_t r, int64_t c0, uint4 v) {
+  if (r >= rows || c0 >= cols) return;
+  uint8_t* p = q + r * ld + c0;
+  if (VEC && c0 + 16 <= cols) {
+    *reinterpret_cast<uint4*>(p) = v;
+    return;
+  }
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (c0 + i < cols) p[i] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
+}
+
+template <int FMT>
+__device__ __forceinline__ uint4 encode_block_values(const uint32_t (&d)[8], float s,
+                                                     bool finite_block) {
+  if (finite_block) return encode16<FMT, true>(d, s);
+  return patch_nan16(encode16<FMT, false>(d, s), d);
+}
+
+// ---------------------------------------------------------------- 1x128 blocks
+// Workgroup tile: kRows1 rows x one 128-column block.  8 lanes share a row block (16 elements
+// each); each thread handles kRowsPerThread row blocks kRows1/kRowsPerThread rows apart.
+// Scales go to scale_inv[colblock][row]: the tile's kRows1 scales are contiguous.
+constexpr int kRowsPerThread = 2;
+constexpr int kRows1 = (kThreads / 8) * kRowsPerThread;  // 64
+
+template <int FMT, bool POW2, bool VEC>
+__global__ __launch_bounds__(kThreads) void quant_1x128_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale_inv) {
+  const int t = threadIdx.x;
+  const int64_t cb = blockIdx.y;
+  const int64_t c0 = cb * 128 + (t & 7) * 16;
+  const int64_t r0 = (int64_t)blockIdx.x * kRows1 + (t >> 3);
+  uint32_t d[kRowsPerThread][8];
+#pragma unroll
+  for (int j = 0; j < kRowsPerThread; ++j)
+    load16<VEC>(x, rows, cols, ld_x, r0 + j * (kThreads / 8), c0, d[j]);
+#pragma unroll
+  for (int j = 0; j < kRowsPerThread; ++j) {
+    const int64_t r = r0 + j * (kThreads / 8);
+    const uint32_t amax = group8_max(amax16_bits(d[j]));
+    const float s = scale_from_amax_bits<FMT, POW2>(amax);
+    const uint4 v = encode_block_values<FMT>(d[j], s, amax < 0x7F80u);
+    store16<VEC>(q, rows, cols, ld_q, r, c0, v);
+    if ((t & 7) == 0 && r < rows) scale_inv[cb * rows + r] = 1.0f / s;
+  }
+}
+
+// ---------------------------------------------------------------- 128x128 tiles
+// One workgroup per tile.  Thread t covers columns (t % 8) * 16 .. +16 of rows
+// t / 8 + 32 * i, i = 0..3; the tile amax is reduced across the workgroup through LDS.
+template <int FMT, bool POW2, bool VEC>
+__global__ __launch_bounds__(kThreads) void quant_128x128_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale_inv) {
+  __shared__ uint32_t wave_amax[kThreads / 64];
+  const int t = threadIdx.x;
+  const int64_t tr = blockIdx.x, tc = blockIdx.y;
+  const int64_t c0 = tc * 128 + (t & 7) * 16;
+  const int64_t rbase = tr * 128 + (t >> 3);
+  uint32_t d[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) load16<VEC>(x, rows, cols, ld_x, rbase + 32 * i, c0, d[i]);
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t a = amax16_bits(d[i]);
+    m = m > a ? m : a;
+  }
+  m = wave_max(m);
+  if ((t & 63) == 0) wave_amax[t >> 6] = m;
+  __syncthreads();
+  uint32_t amax = wave_amax[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) amax = amax > wave_amax[w] ? amax : wave_amax[w];
+  const float s = scale_from_amax_bits<FMT, POW2>(amax);
+  const bool finite = amax < 0x7F80u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    store16<VEC>(q, rows, cols, ld_q, rbase + 32 * i, c0, encode_block_values<FMT>(d[i], s, finite));
+  if (t == 0) scale_inv[tr * gridDim.y + tc] = 1.0f / s;
+}
+
+// ---------------------------------------------------------------- delayed per-tensor
+// Pass 1: cast with the scale held in the state and reduce this tensor's amax into one
+// partial per workgroup (no atomics, so the result is deterministic).  Grid-stride loop over
+// 16-element chunks; the grid is capped at kDelayedBlocks workgroups.
+constexpr int kDelayedBlocks = 2048;
+
+template <int FMT, bool VEC>
+__global__ __launch_bounds__(kThreads) void delayed_cast_kernel(
+    const uint16_t* __restrict__ x, int64_t numel, const float* __restrict__ scale,
+    uint8_t* __restrict__ q, uint32_t* __restrict__ partial) {
+  __shared__ uint32_t wave_amax[kThreads / 64];
+  const float s = *scale;
+  const int64_t nchunks = (numel + 15) / 16;
+  uint32_t m = 0;
+  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < nchunks;
+       c += (int64_t)gridDim.x * kThreads) {
+    uint32_t d[8];
+    load16<VEC>(x, 1, numel, numel, 0, c * 16, d);
+    const uint32_t a = amax16_bits(d);
+    m = m > a ? m : a;
+    uint4 v = encode16<FMT, false>(d, s);
+    if (a > 0x7F80u) v = patch_nan16(v, d);
+    store16<VEC>(q, 1, numel, numel, 0, c * 16, v);
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) wave_amax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = wave_amax[0];
+    for (int w = 1; w < kThreads / 64; ++w) r = r > wave_amax[w] ? r : wave_amax[w];
+    partial[blockIdx.x] = r;
+  }
+}
+
+// Pass 2 (one workgroup): reduce the partials, push the amax into the history (newest first),
+// reduce the history with "max" and derive the scale for the next step.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void delayed_finalize_kernel(
+    const uint32_t* __restrict__ partial, int nparts, int margin, int pow2, int hist_len,
+    float* __restrict__ history, float* __restrict__ scale, float* __restrict__ scale_inv_used) {
+  __shared__ uint32_t red[kThreads / 64];
+  __shared__ float hist_max[kThreads / 64];
+  __shared__ int hist_nan[kThreads / 64];
+  const int t = threadIdx.x;
+  uint32_t m = 0;
+  for (int i = t; i < nparts; i += kThreads) m = m > partial[i] ? m : partial[i];
+  m = wave_max(m);
+  if ((t & 63) == 0) red[t >> 6] = m;
+  __syncthreads();
+  uint32_t a16 = red[0];
+  for (int w = 1; w < kThreads / 64; ++w) a16 = a16 > red[w] ? a16 : red[w];
+  const float a = __uint_as_float(a16 << 16);   // NaN pattern if any input was NaN
+  const float s_old = *scale;
+
+  // Shift the history by one (read everything before anyone writes).
+  float mine[4];
+  int cnt = 0;
+  for (int i = t; i < hist_len && cnt < 4; i += kThreads, ++cnt) mine[cnt] = i == 0 ? a : history[i - 1];
+  __syncthreads();
+  float hm = 0.0f;
+  int hn = 0;
+  cnt = 0;
+  for (int i = t; i < hist_len && cnt < 4; i += kThreads, ++cnt) {
+    history[i] = mine[cnt];
+    const float v = mine[cnt];
+    if (v != v) hn = 1;
+    else if (v > hm) hm = v;
+  }
+  // block-reduce max and NaN flag
+  for (int off = 32; off >= 1; off >>= 1) {
+    float o = __shfl_xor(hm, off);
+    hm = hm > o ? hm : o;
+    hn |= __shfl_xor(hn, off);
+  }
+  if ((t & 63) == 0) {
+    hist_max[t >> 6] = hm;
+    hist_nan[t >> 6] = hn;
+  }
+  __syncthreads();
+  if (t == 0) {
+    float r = hist_max[0];
+    int nan = hist_nan[0];
+    for (int w = 1; w < kThreads / 64; ++w) {
+      r = r > hist_max[w] ? r : hist_max[w];
+      nan |= hist_nan[w];
+    }
+    *scale_inv_used = 1.0f / s_old;
+    *scale = nan ? s_old : scale_from_amax_f32<FMT>(r, margin, pow2 != 0, s_old);
+  }
+}
+
+// ---------------------------------------------------------------- plain cast of fp32
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void cast_fp32_kernel(const float* __restrict__ x,
+                                                            int64_t n, uint8_t* __restrict__ q) {
+  const int64_t n4 = (n + 3) / 4;
+  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < n4;
+       c += (int64_t)gridDim.x * kThreads) {
+    float v[4];
+    const int64_t i0 = c * 4;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = i0 + k < n ? x[i0 + k] : 0.0f;
+    constexpr float F = Format<FMT>::fmax;
+    uint32_t w = cvt4<FMT>(__builtin_amdgcn_fmed3f(v[0], -F, F), __builtin_amdgcn_fmed3f(v[1], -F, F),
+                           __builtin_amdgcn_fmed3f(v[2], -F, F), __builtin_amdgcn_fmed3f(v[3], -F, F));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t b = __float_as_uint(v[k]);
+      if ((b & 0x7FFFFFFFu) > 0x7F800000u)
+        w = (w & ~(0xFFu << (8 * k))) | ((0x7Fu | ((b >> 24) & 0x80u)) << (8 * k));
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (i0 + k < n) q[i0 + k] = (uint8_t)(w >> (8 * k));
+  }
+}
+
+template <int FMT, bool POW2, bool VEC>
+int launch_blockwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int gran,
+                     uint8_t* q, int64_t ld_q, float* s, hipStream_t st) {
+  if (gran == FP8BS_BLOCK_1x128) {
+    dim3 grid((unsigned)ceil_div(rows, kRows1), (unsigned)ceil_div(cols, 128));
+    return launch(quant_1x128_kernel<FMT, POW2, VEC>, grid, dim3(kThreads), st, x, rows, cols,
+                  ld_x, q, ld_q, s);
+  }
+  dim3 grid((unsigned)ceil_div(rows, 128), (unsigned)ceil_div(cols, 128));
+  return launch(quant_128x128_kernel<FMT, POW2, VEC>, grid, dim3(kThreads), st, x, rows, cols,
+                ld_x, q, ld_q, s);
+}
+
+template <int FMT>
+int dispatch_blockwise(bool pow2, bool vec, const uint16_t* x, int64_t rows, int64_t cols,
+                       int64_t ld_x, int gran, uint8_t* q, int64_t ld_q, float* s,
+                       hipStream_t st) {
+  if (pow2)
+    return vec ? launch_blockwise<FMT, true, true>(x, rows, cols, ld_x, gran, q, ld_q, s, st)
+               : launch_blockwise<FMT, true, false>(x, rows, cols, ld_x, gran, q, ld_q, s, st);
+  return vec ? launch_blockwise<FMT, false, true>(x, rows, cols, ld_x, gran, q, ld_q, s, st)
+             : launch_blockwise<FMT, false, false>(x, rows, cols, ld_x, gran, q, ld_q, s, st);
+}
+
+}  // namespace
+}  // namespace fp8bs
+
+using namespace fp8bs;
+
+extern "C" int fp8_quantize_blockwise(const void* x_bf16, int64_t rows, int64_t cols,
+                                      int64_t ld_x, int fmt, int gran, int mode, void* q_out,
+                                      int64_t ld_q, float* scale_inv_out, void* stream) {
+  if (!fmt_ok(fmt) || (gran != FP8BS_BLOCK_1x128 && gran != FP8BS_BLOCK_128x128) ||
+      (mode != FP8BS_SCALE_FP32 && mode != FP8BS_SCALE_POW2))
+    return FP8BS_ERR_ARG;
+  if (rows < 0 || cols < 0 || ld_x < cols || ld_q < cols) return FP8BS_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return FP8BS_OK;
+  if (!x_bf16 || !q_out || !scale_inv_out) return FP8BS_ERR_NULL;
+  const int64_t nb_rows = gran == FP8BS_BLOCK_1x128 ? ceil_div(rows, kRows1) : ceil_div(rows, 128);
+  if (nb_rows > 0x7FFFFFFF || ceil_div(cols, 128) > 65535) return FP8BS_ERR_SHAPE;
+  if (rows > INT64_MAX / ld_x) return FP8BS_ERR_SHAPE;
+  if (!aligned4(scale_inv_out)) return FP8BS_ERR_ALIGN;
+  const bool vec = aligned16(x_bf16) && aligned16(q_out) && ld_x % 8 == 0 && ld_q % 16 == 0;
+  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
+  uint8_t* q = static_cast<uint8_t*>(q_out);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool pow2 = mode == FP8BS_SCALE_POW2;
+  if (fmt == FP8BS_E4M3)
+    return dispatch_blockwise<FP8BS_E4M3>(pow2, vec, x, rows, cols, ld_x, gran, q, ld_q,
+                                          scale_inv_out, st);
+  return dispatch_blockwise<FP8BS_E5M2>(pow2, vec, x, rows, cols, ld_x, gran, q, ld_q,
+                                        scale_inv_out, st);
+}
+
+extern "C" size_t fp8_quantize_delayed_workspace_size(void) {
+  return sizeof(uint32_t) * kDelayedBlocks;
+}
+
+extern "C" int fp8_quantize_delayed(const void* x_bf16, int64_t numel, int fmt, int mode,
+                                    int margin, int hist_len, float* amax_history, float* scale,
+                                    void* q_out, float* scale_inv_used, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  if (!fmt_ok(fmt) || (mode != FP8BS_SCALE_FP32 && mode != FP8BS_SCALE_POW2) ||
+      hist_len < 1 || hist_len > 1024 || margin < 0 || margin > 64)
+    return FP8BS_ERR_ARG;
+  if (numel < 0) return FP8BS_ERR_SHAPE;
+  if (!amax_history || !scale || !scale_inv_used || (numel > 0 && (!x_bf16 || !q_out)))
+    return FP8BS_ERR_NULL;
+  if (!workspace || workspace_bytes < fp8_quantize_delayed_workspace_size())
+    return FP8BS_ERR_WORKSPACE;
+  if (!aligned4(workspace) || !aligned4(amax_history) || !aligned4(scale) ||
+      !aligned4(scale_inv_used))
+    return FP8BS_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t nchunks = (numel + 15) / 16;
+  const int blocks = (int)std::min<int64_t>(kDelayedBlocks, std::max<int64_t>(1, ceil_div(nchunks, kThreads)));
+  const bool vec = aligned16(x_bf16) && aligned16(q_out);
+  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
+  uint8_t* q = static_cast<uint8_t*>(q_out);
+  uint32_t* part = static_cast<uint32_t*>(workspace);
+  int rc;
+  if (fmt == FP8BS_E4M3)
+    rc = vec ? launch(delayed_cast_kernel<FP8BS_E4M3, true>, dim3(blocks), dim3(kThreads), st, x, numel, scale, q, part)
+             : launch(delayed_cast_kernel<FP8BS_E4M3, false>, dim3(blocks), dim3(kThreads), st, x, numel, scale, q, part);
+  else
+    rc = vec ? launch(delayed_cast_kernel<FP8BS_E5M2, true>, dim3(blocks), dim3(kThreads), st, x, numel, scale, q, part)
+             : launch(delayed_cast_kernel<FP8BS_E5M2, false>, dim3(blocks), dim3(kThreads), st, x, numel, scale, q, part);
+  if (rc != FP8BS_OK) return rc;
+  const int pow2 = mode == FP8BS_SCALE_POW2;
+  if (fmt == FP8BS_E4M3)
+    return launch(delayed_finalize_kernel<FP8BS_E4M3>, dim3(1), dim3(kThreads), st,
+                  (const uint32_t*)part, blocks, margin, pow2, hist_len, amax_history, scale,
+                  scale_inv_used);
+  return launch(delayed_finalize_kernel<FP8BS_E5M2>, dim3(1), dim3(kThreads), st,
+                (const uint32_t*)part, blocks, margin, pow2, hist_len, amax_history, scale,
+                scale_inv_used);
+}
+
+extern "C" int fp8_cast_fp32(const float* x, int64_t n, int fmt, void* q_out, void* stream) {
+  if (!fmt_ok(fmt)) return FP8BS_ERR_ARG;
+  if (n < 0) return FP8BS_ERR_SHAPE;
+  if (n == 0) return FP8BS_OK;
+  if (!x || !q_out) return FP8BS_ERR_NULL;
+  if (!aligned4(x)) return FP8BS_ERR_ALIGN;
+  const int blocks = (int)std::min<int64_t>(8192, std::max<int64_t>(1, ceil_div(ceil_div(n, 4), kThreads)));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* q = static_cast<uint8_t*>(q_out);
+  if (fmt == FP8BS_E4M3)
+    return launch(cast_fp32_kernel<FP8BS_E4M3>, dim3(blocks), dim3(kThreads), st, x, n, q);
+  return launch(cast_fp32_kernel<FP8BS_E5M2>, dim3(blocks), dim3(kThreads), st, x, n, q);
+}
+
+extern "C" const char* fp8bs_status_string(int status) {
+  switch (status) {
+    case FP8BS_OK: return "ok";
+    case FP8BS_ERR_NULL: return "a required pointer is NULL";
+    case FP8BS_ERR_SHAPE: return "invalid size or pitch";
+    case FP8BS_ERR_ALIGN: return "pointer or pitch misaligned";
+    case FP8BS_ERR_UNSUPPORTED: return "unsupported operand/scale combination";
+    case FP8BS_ERR_LAUNCH: return "kernel launch failed";
+    case FP8BS_ERR_WORKSPACE: return "workspace missing or too small";
+    case FP8BS_ERR_ARG: return "argument out of range";
+    default: return "unknown status";
+  }
+}

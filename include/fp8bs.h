@@ -1,0 +1,191 @@
+/*
+ * fp8bs.h -- C ABI of the block-scaled FP8 linear-layer library for AMD MI355X (gfx950).
+ *
+ * The operations are the FP8 linear-layer path described in two public pages:
+ *  [P1] "Infraestructura de Entrenamiento FP8: Precisión Numérica de Nueva Generación"
+ *       (introl.com blog): section "El panorama de la precisión numérica" (E4M3: 4 exponent /
+ *       3 mantissa bits, range +-448; E5M2: 5 / 2 bits, wider range, used for gradients),
+ *       section "Transformer Engine: la base de software" (delayed scaling with margin 0, an
+ *       amax history of 16 reduced with "max", HYBRID = E4M3 forward / E5M2 backward),
+ *       section "Estrategias de escalado y estabilidad" (per-tensor, block and delayed scaling).
+ *  [P3] "NVIDIA NeMo RL logra una aceleración del 48% con entrenamiento de precisión FP8 de
+ *       extremo a extremo" (hotbookzone.com): section "El avance técnico" (E4M3 block
+ *       quantization, 128x128 tiles for weights and 1x128 blocks for activations; linear layers
+ *       run FP8 math, the rest stays BF16), section "Ganancias de rendimiento en el mundo real"
+ *       (quantization-kernel overhead; per-step scale recalibration; MoE), section "Por qué
+ *       esto es importante para la economía de la IA" (power-of-2 scale factors).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller (for example PyTorch tensors).
+ *    The library never allocates, frees or synchronizes; work is enqueued on `stream`
+ *    (a hipStream_t; NULL means the default stream) and completes asynchronously.
+ *  - Matrices are row-major; `ld*` arguments are row pitches in ELEMENTS.
+ *  - Codes are one byte per element in the OCP E4M3 (bias 7, no infinities, NaN = S.1111.111,
+ *    max 448) or E5M2 (bias 15, IEEE-like, max 57344) layout.
+ *  - Every scale array holds DEQUANTIZATION factors: value = decode(code) * scale_inv.
+ *    Scale layouts:
+ *      1x128 blocks of a [R, C] matrix ....... float[ceil(C/128)][R]  (column block major)
+ *      128x128 tiles of a [R, C] matrix ...... float[ceil(R/128)][ceil(C/128)]
+ *      per tensor ............................. float[1]
+ *  - Quantization: for each block, amax = max |x|; s = fl32(FMAX / amax) (IEEE division);
+ *    amax == 0 or non-finite -> s = 1; s == +inf -> FLT_MAX; power-of-2 mode rounds s down to
+ *    2^floor(log2 s); each code = round-to-nearest-even of fl32(x * s), saturating at +-FMAX
+ *    (infinities included), NaN -> 0x7F with the input's sign; scale_inv = fl32(1 / s).
+ *    Edge blocks are clipped to the tensor.
+ *  - Return value: FP8BS_OK (0) or a negative status.  Arguments are validated on the host
+ *    before anything is enqueued; on error nothing is launched.  A fault inside a kernel
+ *    surfaces at the caller's next synchronization, as for any HIP launch.
+ *  - Entry points are reentrant: the library keeps no state between calls.
+ */
+#ifndef FP8BS_H
+#define FP8BS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- enums and status codes */
+typedef enum { FP8BS_E4M3 = 0, FP8BS_E5M2 = 1 } fp8bs_format;
+
+typedef enum {
+  FP8BS_BLOCK_1x128 = 0,   /* one row by 128 consecutive columns of the stored matrix */
+  FP8BS_BLOCK_128x128 = 1, /* 128x128 tile of the stored matrix */
+  FP8BS_PER_TENSOR = 2     /* one scale for the whole tensor */
+} fp8bs_granularity;
+
+typedef enum { FP8BS_SCALE_FP32 = 0, FP8BS_SCALE_POW2 = 1 } fp8bs_scale_mode;
+
+typedef enum {
+  FP8BS_FPROP = 0, /* C[M,N] = A[M,K] . B[N,K]^T   (A = X, B = W: forward)              */
+  FP8BS_DGRAD = 1, /* C[M,N] = A[M,K] . B[K,N]     (A = dY, B = W, K = out-features)     */
+  FP8BS_WGRAD = 2  /* C[M,N] = A[K,M]^T . B[K,N]   (A = dY, B = X, K = tokens; C = dW)    */
+} fp8bs_layout;
+
+enum {
+  FP8BS_OK = 0,
+  FP8BS_ERR_NULL = -1,        /* a required pointer is NULL */
+  FP8BS_ERR_SHAPE = -2,       /* negative size, pitch smaller than the row, size overflow */
+  FP8BS_ERR_ALIGN = -3,       /* pointer or pitch misaligned for the vectorized kernel */
+  FP8BS_ERR_UNSUPPORTED = -4, /* valid but unsupported combination (e.g. 1x128 on an MN-major operand) */
+  FP8BS_ERR_LAUNCH = -5,      /* the HIP launch itself failed */
+  FP8BS_ERR_WORKSPACE = -6,   /* workspace missing or too small */
+  FP8BS_ERR_ARG = -7          /* an enum or scalar argument out of range */
+};
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char* fp8bs_status_string(int status);
+
+/* ---------------------------------------------------------------- quantization */
+
+/*
+ * Blockwise quantization of a bf16 matrix x[rows, cols] (pitch ld_x elements) into codes
+ * q_out[rows, cols] (pitch ld_q bytes) and per-block dequantization factors scale_inv_out.
+ * [P3] "El avance técnico": 1x128 blocks (activations) and 128x128 tiles (weights), E4M3;
+ * [P3] "Por qué esto es importante ...": power-of-2 mode; [P1] "El panorama ...": formats.
+ *   fmt:  FP8BS_E4M3 or FP8BS_E5M2.
+ *   gran: FP8BS_BLOCK_1x128 (scale_inv_out is float[ceil(cols/128)][rows]) or
+ *         FP8BS_BLOCK_128x128 (scale_inv_out is float[ceil(rows/128)][ceil(cols/128)]).
+ *   mode: FP8BS_SCALE_FP32 or FP8BS_SCALE_POW2.
+ * rows == 0 or cols == 0 is a no-op.  Requirements: ld_x >= cols, ld_q >= cols.  Any pitch and
+ * alignment is accepted; 16-byte aligned rows (ld_x % 8 == 0, ld_q % 16 == 0, aligned bases)
+ * take the vectorized path.
+ * Errors: FP8BS_ERR_NULL, FP8BS_ERR_SHAPE, FP8BS_ERR_ARG, FP8BS_ERR_LAUNCH.
+ */
+int fp8_quantize_blockwise(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                           int fmt, int gran, int mode, void* q_out, int64_t ld_q,
+                           float* scale_inv_out, void* stream);
+
+/*
+ * One step of per-tensor delayed scaling on a contiguous bf16 tensor x[numel].
+ * [P1] "Transformer Engine: la base de software": the scale used in a step comes from the
+ * largest magnitudes recorded in earlier steps (history of hist_len, reduced with "max",
+ * margin), so no reduction over the current tensor sits in front of the cast.
+ * State (caller-owned device memory, read and updated in place):
+ *   amax_history: float[hist_len], newest first; start it at zeros.
+ *   scale:        float[1], the scale the NEXT call will use; start it at 1.0f.
+ * Per call: q_out[i] = encode(fl32(x[i] * scale)); *scale_inv_used = fl32(1 / scale);
+ *   then amax = max |x| (NaN if any element is NaN) is pushed at history[0] (older entries
+ *   shift by one), and if r = max(history) is positive and finite,
+ *   scale = fl32(fl32(FMAX / r) / 2^margin) (FLT_MAX if that overflows; rounded down to a
+ *   power of two in FP8BS_SCALE_POW2 mode); otherwise scale is kept.
+ * workspace: device memory of at least fp8_quantize_delayed_workspace_size() bytes, 16-byte
+ *   aligned, owned by the caller, no initialization needed; calls that share a workspace
+ *   must be ordered on one stream.
+ * Limits: 1 <= hist_len <= 1024, 0 <= margin <= 64.  numel == 0 still advances the state
+ *   (amax = 0).  Errors: FP8BS_ERR_NULL, FP8BS_ERR_SHAPE, FP8BS_ERR_ARG,
+ *   FP8BS_ERR_WORKSPACE, FP8BS_ERR_LAUNCH.
+ */
+int fp8_quantize_delayed(const void* x_bf16, int64_t numel, int fmt, int mode, int margin,
+                         int hist_len, float* amax_history, float* scale, void* q_out,
+                         float* scale_inv_used, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Bytes of workspace fp8_quantize_delayed needs (a constant). */
+size_t fp8_quantize_delayed_workspace_size(void);
+
+/*
+ * Saturating round-to-nearest-even cast of fp32 values to FP8 codes, no scaling
+ * (q_out[i] = encode(x[i])).  The precision-conversion step of [P1] "Transformer Engine: la
+ * base de software", exposed on its own.  Errors: FP8BS_ERR_NULL, FP8BS_ERR_SHAPE,
+ * FP8BS_ERR_ARG, FP8BS_ERR_LAUNCH.
+ */
+int fp8_cast_fp32(const float* x, int64_t n, int fmt, void* q_out, void* stream);
+
+/* ---------------------------------------------------------------- GEMM */
+
+/*
+ * Block-scaled FP8 x FP8 GEMM with fp32 accumulation and bf16 output.
+ * [P3] "El avance técnico": linear layers run FP8 math with 128x128 weight / 1x128 activation
+ * scales; the output stays BF16.  For each 128-wide block kb of the contraction, the fp32
+ * partial sum of code products is multiplied by scale_a(m, kb) * scale_b(n, kb) and added to
+ * the fp32 accumulator; C = bf16_rne(accumulator).
+ *   layout: FP8BS_FPROP  A[M,K] pitch lda,  B[N,K] pitch ldb, C = A . B^T
+ *           FP8BS_DGRAD  A[M,K] pitch lda,  B[K,N] pitch ldb, C = A . B
+ *           FP8BS_WGRAD  A[K,M] pitch lda,  B[K,N] pitch ldb, C = A^T . B
+ *   fa, fb: operand formats (any mix of E4M3 / E5M2, e.g. E5M2 gradients).
+ *   ga, gb: granularity of each operand's scales, laid out as described at the top of this
+ *           file on the operand's STORED matrix.  Supported: a K-major operand ([.,K] stored)
+ *           takes 1x128 (A only), 128x128 or per-tensor; an MN-major operand ([K,.] stored)
+ *           takes 128x128 or per-tensor.  Other combinations return FP8BS_ERR_UNSUPPORTED.
+ *   C_bf16: [M,N] pitch ldc (elements).
+ * M, N or K == 0: C is left untouched when M or N is 0; with K == 0, C is set to zeros.
+ * Requirements: 16-byte aligned A and B with lda % 16 == 0 and ldb % 16 == 0, 4-byte aligned C
+ * with ldc % 2 == 0 (FP8BS_ERR_ALIGN otherwise); pitches at least the row widths.
+ * Errors: FP8BS_ERR_NULL, FP8BS_ERR_SHAPE, FP8BS_ERR_ALIGN, FP8BS_ERR_UNSUPPORTED,
+ * FP8BS_ERR_ARG, FP8BS_ERR_LAUNCH.
+ */
+int fp8_gemm_blockscaled(int layout, int64_t M, int64_t N, int64_t K,
+                         const void* A, int64_t lda, int fa, int ga, const float* scale_inv_a,
+                         const void* B, int64_t ldb, int fb, int gb, const float* scale_inv_b,
+                         void* C_bf16, int64_t ldc, void* stream);
+
+/*
+ * Grouped (mixture-of-experts) block-scaled FP8 GEMM.  [P3] "Ganancias de rendimiento en el
+ * mundo real": the FP8 recipe applied to an MoE model's expert layers.
+ * Rows [group_offsets[g], group_offsets[g+1]) of A (tokens sorted by expert) are multiplied
+ * by expert g's weight: C[r, :] = A[r, :] . B[g]^T for those rows.
+ *   group_offsets: DEVICE int64[num_groups + 1], non-decreasing, offsets[0] = 0,
+ *                  offsets[num_groups] = total_M (empty groups allowed).  Offsets that break
+ *                  these rules make the kernel skip the offending rows; they never cause an
+ *                  out-of-range access.
+ *   A:  [total_M, K] codes (format fa), pitch lda; scale_inv_a: 1x128 blocks,
+ *       float[ceil(K/128)][total_M].
+ *   B:  [num_groups][N][K] codes (format fb), rows of pitch ldb, groups of stride N * ldb;
+ *       scale_inv_b: float[num_groups][ceil(N/128)][ceil(K/128)].
+ *   C:  [total_M, N] bf16, pitch ldc.
+ * Alignment as for fp8_gemm_blockscaled.  Errors: FP8BS_ERR_NULL, FP8BS_ERR_SHAPE,
+ * FP8BS_ERR_ALIGN, FP8BS_ERR_ARG, FP8BS_ERR_LAUNCH.
+ */
+int fp8_grouped_gemm(int32_t num_groups, const int64_t* group_offsets, int64_t total_M,
+                     int64_t N, int64_t K, const void* A, int64_t lda, int fa,
+                     const float* scale_inv_a, const void* B, int64_t ldb, int fb,
+                     const float* scale_inv_b, void* C_bf16, int64_t ldc, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BS_H */

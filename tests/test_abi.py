@@ -1,0 +1,138 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+* the shared library loads and exports every function include/fp8bs.h declares;
+* invalid arguments are rejected by host-side validation with the documented status codes,
+  before anything is enqueued (null device pointers never get dereferenced here).
+"""
+import ctypes
+
+import pytest
+
+import block_scaled_quantize_amd as bsq
+
+FAKE = 1 << 40          # a 16-byte aligned non-null address that is never dereferenced
+FAKE_ODD = FAKE + 1
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bsq.load()
+    names = bsq.declared_functions()
+    assert set(names) >= {"fp8_quantize_blockwise", "fp8_quantize_delayed",
+                          "fp8_quantize_delayed_workspace_size", "fp8_gemm_blockscaled",
+                          "fp8_grouped_gemm", "fp8_cast_fp32", "fp8bs_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5, -6, -7, 99):
+        assert isinstance(bsq.status_string(s), str) and bsq.status_string(s)
+
+
+def test_workspace_size_constant():
+    assert bsq.delayed_workspace_size() > 0
+    assert bsq.delayed_workspace_size() == bsq.delayed_workspace_size()
+
+
+def q_blockwise(**kw):
+    a = dict(x=FAKE, rows=4, cols=256, ld_x=256, fmt=0, gran=0, mode=0, q=FAKE, ld_q=256,
+             s=FAKE, stream=None)
+    a.update(kw)
+    return bsq.load().fp8_quantize_blockwise(a["x"], a["rows"], a["cols"], a["ld_x"], a["fmt"],
+                                             a["gran"], a["mode"], a["q"], a["ld_q"], a["s"],
+                                             a["stream"])
+
+
+def test_quantize_blockwise_validation():
+    assert q_blockwise(fmt=2) == bsq.ERR_ARG
+    assert q_blockwise(gran=2) == bsq.ERR_ARG        # per-tensor is the delayed entry point
+    assert q_blockwise(mode=5) == bsq.ERR_ARG
+    assert q_blockwise(rows=-1) == bsq.ERR_SHAPE
+    assert q_blockwise(ld_x=100) == bsq.ERR_SHAPE
+    assert q_blockwise(ld_q=100) == bsq.ERR_SHAPE
+    assert q_blockwise(x=None) == bsq.ERR_NULL
+    assert q_blockwise(q=None) == bsq.ERR_NULL
+    assert q_blockwise(s=None) == bsq.ERR_NULL
+    assert q_blockwise(s=FAKE + 2) == bsq.ERR_ALIGN
+    assert q_blockwise(rows=0) == bsq.OK                # empty: no-op, nothing launched
+    assert q_blockwise(cols=0, x=None) == bsq.OK
+
+
+def q_delayed(**kw):
+    a = dict(x=FAKE, n=1024, fmt=0, mode=0, margin=0, hist=16, h=FAKE, s=FAKE, q=FAKE, siu=FAKE,
+             ws=FAKE, wsb=bsq.delayed_workspace_size())
+    a.update(kw)
+    return bsq.load().fp8_quantize_delayed(a["x"], a["n"], a["fmt"], a["mode"], a["margin"],
+                                           a["hist"], a["h"], a["s"], a["q"], a["siu"], a["ws"],
+                                           a["wsb"], None)
+
+
+def test_quantize_delayed_validation():
+    assert q_delayed(hist=0) == bsq.ERR_ARG
+    assert q_delayed(hist=1025) == bsq.ERR_ARG
+    assert q_delayed(margin=-1) == bsq.ERR_ARG
+    assert q_delayed(margin=65) == bsq.ERR_ARG
+    assert q_delayed(fmt=7) == bsq.ERR_ARG
+    assert q_delayed(n=-5) == bsq.ERR_SHAPE
+    assert q_delayed(h=None) == bsq.ERR_NULL
+    assert q_delayed(x=None) == bsq.ERR_NULL
+    assert q_delayed(ws=None) == bsq.ERR_WORKSPACE
+    assert q_delayed(wsb=4) == bsq.ERR_WORKSPACE
+    assert q_delayed(s=FAKE_ODD) == bsq.ERR_ALIGN
+
+
+def gemm(**kw):
+    a = dict(layout=0, M=256, N=256, K=256, A=FAKE, lda=256, fa=0, ga=0, sa=FAKE, B=FAKE,
+             ldb=256, fb=0, gb=1, sb=FAKE, C=FAKE, ldc=256)
+    a.update(kw)
+    return bsq.load().fp8_gemm_blockscaled(a["layout"], a["M"], a["N"], a["K"], a["A"], a["lda"],
+                                           a["fa"], a["ga"], a["sa"], a["B"], a["ldb"], a["fb"],
+                                           a["gb"], a["sb"], a["C"], a["ldc"], None)
+
+
+def test_gemm_validation():
+    assert gemm(layout=3) == bsq.ERR_ARG
+    assert gemm(fa=2) == bsq.ERR_ARG
+    assert gemm(gb=3) == bsq.ERR_ARG
+    assert gemm(M=-1) == bsq.ERR_SHAPE
+    assert gemm(lda=128) == bsq.ERR_SHAPE
+    assert gemm(ldc=100) == bsq.ERR_SHAPE
+    assert gemm(A=None) == bsq.ERR_NULL
+    assert gemm(C=None) == bsq.ERR_NULL
+    assert gemm(A=FAKE_ODD) == bsq.ERR_ALIGN
+    assert gemm(lda=264) == bsq.ERR_ALIGN
+    assert gemm(ldc=257) == bsq.ERR_ALIGN
+    # 1x128 scales only on a K-major activation operand
+    assert gemm(gb=0) == bsq.ERR_UNSUPPORTED                   # weight side 1x128
+    assert gemm(layout=2, ga=0, gb=1) == bsq.ERR_UNSUPPORTED   # wgrad: A is MN-major
+    assert gemm(layout=1, ga=0, gb=0) == bsq.ERR_UNSUPPORTED   # dgrad: B is MN-major
+    assert gemm(M=0) == bsq.OK and gemm(N=0, C=None) == bsq.OK
+
+
+def grouped(**kw):
+    a = dict(G=4, off=FAKE, M=512, N=256, K=256, A=FAKE, lda=256, fa=0, sa=FAKE, B=FAKE,
+             ldb=256, fb=0, sb=FAKE, C=FAKE, ldc=256)
+    a.update(kw)
+    return bsq.load().fp8_grouped_gemm(a["G"], a["off"], a["M"], a["N"], a["K"], a["A"], a["lda"],
+                                       a["fa"], a["sa"], a["B"], a["ldb"], a["fb"], a["sb"], a["C"],
+                                       a["ldc"], None)
+
+
+def test_grouped_validation():
+    assert grouped(G=-1) == bsq.ERR_ARG
+    assert grouped(G=5000) == bsq.ERR_ARG
+    assert grouped(fb=9) == bsq.ERR_ARG
+    assert grouped(K=0) == bsq.ERR_SHAPE
+    assert grouped(off=None) == bsq.ERR_NULL
+    assert grouped(lda=64) == bsq.ERR_SHAPE
+    assert grouped(off=FAKE + 4) == bsq.ERR_ALIGN
+    assert grouped(M=0) == bsq.OK and grouped(G=0) == bsq.OK
+
+
+def test_cast_validation():
+    lib = bsq.load()
+    assert lib.fp8_cast_fp32(FAKE, 16, 3, FAKE, None) == bsq.ERR_ARG
+    assert lib.fp8_cast_fp32(FAKE, -1, 0, FAKE, None) == bsq.ERR_SHAPE
+    assert lib.fp8_cast_fp32(None, 16, 0, FAKE, None) == bsq.ERR_NULL
+    assert lib.fp8_cast_fp32(FAKE + 2, 16, 0, FAKE, None) == bsq.ERR_ALIGN
+    assert lib.fp8_cast_fp32(None, 0, 0, None, None) == bsq.OK

@@ -1,0 +1,228 @@
+"""GPU parity of the block-scaled FP8 GEMM (dense and grouped) against the oracle's fp64
+reference: rel. Frobenius <= 1e-2 (gate) and <= 4e-3 (alarm), and every element within one bf16
+rounding plus the fp32-accumulation bound (see helpers.gemm_check).
+
+The operand codes and scales are produced by the ORACLE quantizer from seeded synthetic bf16
+data, so these tests exercise the GEMM alone.  Layouts: fprop, dgrad, wgrad; scales: 1x128 on
+the activation side, 128x128 tiles on the weight side, or per tensor; formats E4M3 / E5M2 mixed
+("NVIDIA NeMo RL logra una aceleración del 48% ...", section "El avance técnico";
+"Infraestructura de Entrenamiento FP8 ...", section "El panorama de la precisión numérica").
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_quantize_amd as bsq
+import oracle
+import synth
+from helpers import abs_product, gemm_check, logical_to_gpu_scales
+
+pytestmark = pytest.mark.gpu
+
+FP, DG, WG = bsq.FPROP, bsq.DGRAD, bsq.WGRAD
+B1, B128, PT = bsq.BLOCK_1x128, bsq.BLOCK_128x128, bsq.PER_TENSOR
+E4, E5 = bsq.E4M3, bsq.E5M2
+
+
+def quantize_operand(x: torch.Tensor, fmt, gran):
+    """Oracle quantization of a stored bf16 matrix; returns (codes, logical scales)."""
+    if gran == PT:
+        st = oracle.DelayedState(1)
+        from helpers import bits
+        b = bits(x)
+        oracle.delayed_step(b, fmt, oracle.SCALE_FP32, 0, st)       # calibrate on x itself
+        q, siu = oracle.delayed_step(b, fmt, oracle.SCALE_FP32, 0, st)
+        return q, np.array([[siu]], dtype=np.float32)
+    from helpers import bits
+    return oracle.quantize_blockwise(bits(x), fmt, gran, oracle.SCALE_FP32)
+
+
+def to_device_codes(q: np.ndarray, ld: int) -> torch.Tensor:
+    rows, cols = q.shape
+    store = torch.full((rows, ld), 0x7F, dtype=torch.uint8)     # NaN codes in the padding
+    store[:, :cols] = torch.from_numpy(q)
+    return store.cuda()[:, :cols]
+
+
+def device_scales(s: np.ndarray, gran) -> torch.Tensor:
+    if gran == PT:
+        return torch.from_numpy(s.reshape(1).astype(np.float32)).cuda()
+    return logical_to_gpu_scales(s, gran)
+
+
+def run_gemm(gpu, layout, M, N, K, fa, ga, fb, gb, seed=0, pad=0, rows=None, c_guard=True):
+    ashape = (M, K) if layout != WG else (K, M)
+    bshape = (N, K) if layout == FP else (K, N)
+    a = synth.activations_with_outliers(*ashape, seed, f"gemm/A{layout}") if ga == B1 else \
+        synth.normal(ashape, 1.0, seed, f"gemm/A{layout}")
+    b = synth.normal(bshape, 0.02, seed, f"gemm/B{layout}")
+    qa, sa = quantize_operand(a, fa, ga)
+    qb, sb = quantize_operand(b, fb, gb)
+    lda = -(-ashape[1] // 16) * 16 + pad
+    ldb = -(-bshape[1] // 16) * 16 + pad
+    ad, bd = to_device_codes(qa, lda), to_device_codes(qb, ldb)
+    ldc = N + (8 if c_guard else 0)
+    cstore = torch.full((M + 1, ldc), -7.0, dtype=torch.bfloat16, device="cuda")
+    c = cstore[:M, :N]
+    gpu.gemm_blockscaled(layout, ad, fa, ga, device_scales(sa, ga), bd, fb, gb,
+                         device_scales(sb, gb), c=c)
+    torch.cuda.synchronize()
+    if c_guard:
+        assert torch.all(cstore[:M, N:] == -7.0) and torch.all(cstore[M] == -7.0), "guard overwritten"
+    # reference on all rows or on a sample of output rows
+    adq = oracle.dequantize(qa, fa, ga, sa)
+    bdq = oracle.dequantize(qb, fb, gb, sb)
+    if rows is not None:
+        if layout == WG:
+            adq = adq[:, rows]
+        else:
+            adq = adq[rows]
+        cg = c[torch.as_tensor(rows, device="cuda")]
+    else:
+        cg = c
+    if layout == FP:
+        ref = adq @ bdq.T
+    elif layout == DG:
+        ref = adq @ bdq
+    else:
+        ref = adq.T @ bdq
+    return gemm_check(cg, ref, abs_product(layout, adq, bdq), f"layout {layout} {M}x{N}x{K}")
+
+
+def test_tiny_config(gpu):
+    # X[64,256] ~ N(0,1) 1x128, W[256,256] ~ N(0,0.02) 128x128, Y = X W^T
+    x = synth.normal((64, 256), 1.0, 0, "tiny/X")
+    w = synth.normal((256, 256), 0.02, 0, "tiny/W")
+    qa, sa = quantize_operand(x, E4, B1)
+    qb, sb = quantize_operand(w, E4, B128)
+    c = gpu.gemm_blockscaled(FP, torch.from_numpy(qa).cuda(), E4, B1, device_scales(sa, B1),
+                             torch.from_numpy(qb).cuda(), E4, B128, device_scales(sb, B128))
+    adq, bdq = oracle.dequantize(qa, E4, B1, sa), oracle.dequantize(qb, E4, B128, sb)
+    gemm_check(c, adq @ bdq.T, abs_product(FP, adq, bdq), "tiny")
+
+
+SHAPES = [(64, 128, 128), (300, 260, 200), (129, 384, 512), (1000, 1000, 1000), (4160, 256, 384),
+          (1, 129, 33), (255, 127, 129)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_fprop_block_scales(gpu, M, N, K):
+    run_gemm(gpu, FP, M, N, K, E4, B1, E4, B128)
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES[:4])
+@pytest.mark.parametrize("ga,gb", [(PT, PT), (B1, PT), (PT, B128), (B128, B128)])
+def test_fprop_other_scale_kinds(gpu, M, N, K, ga, gb):
+    run_gemm(gpu, FP, M, N, K, E4, ga, E4, gb)
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("fa,ga,fb,gb", [(E5, B1, E4, B128), (E5, PT, E4, PT), (E4, B128, E5, PT)])
+def test_dgrad(gpu, M, N, K, fa, ga, fb, gb):
+    run_gemm(gpu, DG, M, N, K, fa, ga, fb, gb)
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("fa,ga,fb,gb", [(E5, PT, E4, PT), (E4, B128, E4, B128), (E5, PT, E5, B128)])
+def test_wgrad(gpu, M, N, K, fa, ga, fb, gb):
+    run_gemm(gpu, WG, M, N, K, fa, ga, fb, gb)
+
+
+def test_padded_pitches_with_nan_padding(gpu):
+    # the padding bytes hold NaN codes: they must never enter the sums
+    run_gemm(gpu, FP, 200, 200, 200, E4, B1, E4, B128, pad=48)
+    run_gemm(gpu, DG, 200, 200, 200, E5, B1, E4, B128, pad=32)
+    run_gemm(gpu, WG, 200, 200, 200, E5, PT, E4, PT, pad=16)
+
+
+def test_k_zero_and_empty(gpu):
+    a = torch.zeros((5, 0), dtype=torch.uint8, device="cuda")
+    b = torch.zeros((7, 0), dtype=torch.uint8, device="cuda")
+    s = torch.ones(1, device="cuda")
+    c = torch.full((5, 8), 3.0, dtype=torch.bfloat16, device="cuda")[:, :7]
+    gpu.gemm_blockscaled(FP, a, E4, PT, s, b, E4, PT, s, c=c)
+    assert torch.all(c == 0)
+    e = torch.zeros((0, 16), dtype=torch.uint8, device="cuda")
+    out = gpu.gemm_blockscaled(FP, e, E4, PT, s, torch.zeros((4, 16), dtype=torch.uint8, device="cuda"), E4, PT, s)
+    assert out.shape == (0, 4)
+
+
+@pytest.mark.parametrize("name,N,K", [("qkv", 6144, 4096), ("down", 4096, 14336)])
+def test_llama8b_fprop_full_size_sampled_rows(gpu, name, N, K):
+    """M = 8192 tokens, the launch configuration the benchmark times; 192 sampled rows are
+    checked against the fp64 reference."""
+    rows = np.sort(np.random.Generator(np.random.PCG64(1)).choice(8192, 192, replace=False))
+    run_gemm(gpu, FP, 8192, N, K, E4, B1, E4, B128, rows=rows, c_guard=False)
+
+
+def test_llama8b_backward_full_size_sampled(gpu):
+    rows = np.sort(np.random.Generator(np.random.PCG64(2)).choice(4096, 128, replace=False))
+    run_gemm(gpu, DG, 8192, 4096, 4096, E5, PT, E4, PT, rows=rows * 2, c_guard=False)
+    run_gemm(gpu, WG, 4096, 4096, 8192, E5, PT, E4, PT, rows=rows, c_guard=False)
+
+
+def test_deterministic(gpu):
+    qa = torch.randint(0, 0x7E, (512, 1024), dtype=torch.uint8, device="cuda")
+    qb = torch.randint(0, 0x7E, (768, 1024), dtype=torch.uint8, device="cuda")
+    sa = torch.rand((8, 512), device="cuda") + 0.5
+    sb = torch.rand((6, 8), device="cuda") + 0.5
+    c1 = gpu.gemm_blockscaled(FP, qa, E4, B1, sa, qb, E4, B128, sb)
+    c2 = gpu.gemm_blockscaled(FP, qa, E4, B1, sa, qb, E4, B128, sb)
+    assert torch.equal(c1.view(torch.int16), c2.view(torch.int16))
+
+
+# ----------------------------------------------------------------------------- grouped
+
+def run_grouped(gpu, counts, N, K, seed=0, sample_rows=None):
+    counts = np.asarray(counts, dtype=np.int64)
+    G = len(counts)
+    off = synth.offsets_from_counts(counts)
+    total = int(off[-1])
+    x = synth.normal((total, K), 1.0, seed, "grouped/A")
+    qa, sa = quantize_operand(x, E4, B1)
+    qbs, sbs = [], []
+    for g in range(G):
+        w = synth.normal((N, K), 0.02, seed, f"grouped/W{g}")
+        q, s = quantize_operand(w, E4, B128)
+        qbs.append(q)
+        sbs.append(s)
+    qbs, sbs = np.stack(qbs), np.stack(sbs)
+    c = gpu.grouped_gemm(torch.from_numpy(off).cuda(), torch.from_numpy(qa).cuda(),
+                         logical_to_gpu_scales(sa, B1), torch.from_numpy(qbs).cuda(),
+                         torch.from_numpy(sbs).cuda())
+    torch.cuda.synchronize()
+    if sample_rows is None:
+        ref = oracle.grouped_gemm(off, qa, sa, E4, qbs, sbs, E4)
+        ad = oracle.dequantize(qa, E4, B1, sa)
+        mag = np.zeros_like(ref)
+        for g in range(G):
+            r0, r1 = off[g], off[g + 1]
+            if r1 > r0:
+                mag[r0:r1] = np.abs(ad[r0:r1]) @ np.abs(oracle.dequantize(qbs[g], E4, B128, sbs[g])).T
+        return gemm_check(c, ref, mag, f"grouped {G} groups")
+    # sampled rows: the reference of each sampled row uses its own group's weight
+    ad = oracle.dequantize(qa[sample_rows], E4, B1, sa[sample_rows])
+    grp = np.searchsorted(off, sample_rows, side="right") - 1
+    ref = np.zeros((len(sample_rows), N))
+    mag = np.zeros_like(ref)
+    for g in np.unique(grp):
+        wd = oracle.dequantize(qbs[g], E4, B128, sbs[g])
+        sel = grp == g
+        ref[sel] = ad[sel] @ wd.T
+        mag[sel] = np.abs(ad[sel]) @ np.abs(wd).T
+    return gemm_check(c[torch.as_tensor(sample_rows, device="cuda")], ref, mag, "grouped sampled")
+
+
+def test_grouped_small_with_empty_groups(gpu):
+    run_grouped(gpu, [5, 0, 130, 1, 0, 257, 128], 256, 384)
+
+
+def test_grouped_ragged_k_and_n(gpu):
+    run_grouped(gpu, [100, 3, 0, 60], 200, 272)
+
+
+def test_grouped_moe_config_sampled(gpu):
+    """128 experts, 16384 tokens, top-8 Zipf(1.1) routing -> 131072 rows, gate/up 2048 -> 1536."""
+    counts = synth.moe_routing(16384, 128, 8, 1.1, 0)
+    rows = np.sort(np.random.Generator(np.random.PCG64(3)).choice(int(counts.sum()), 256, replace=False))
+    run_grouped(gpu, counts, 1536, 2048, sample_rows=rows)
