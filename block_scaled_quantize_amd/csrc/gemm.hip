@@ -25,6 +25,8 @@
 //    compact group of tiles and its L2 is reused.
 #include <float.h>
 
+#include <stdlib.h>
+
 #include <algorithm>
 
 #include "common.h"
@@ -38,23 +40,37 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int kThreads = 256;
-constexpr int kBN = 128;
-constexpr int kStages = 3;
-constexpr int kGroupM = 8;  // tile-rows per L2 group in the tile order
+constexpr int kGroupM = 8;      // tile-rows per L2 group in the tile order
+constexpr int kLdsBytes = 160 * 1024;
 
-template <int BM>
-struct Tile {
+// Tile configuration: BM x BN output tile, WAVES_M x WAVES_N waves, each wave owning a
+// (BM / WAVES_M) x (BN / WAVES_N) block of 16x16 pieces.  Three LDS stages when they fit in
+// the 160 KiB of a CU, else two.
+template <int BM_, int BN_, int WAVES_M, int WAVES_N>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int kWaves = WAVES_M * WAVES_N;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kWavesM = WAVES_M, kWavesN = WAVES_N;
+  static constexpr int kWTM = BM / WAVES_M;   // m extent of a wave
+  static constexpr int kWTN = BN / WAVES_N;   // n extent of a wave
+  static constexpr int kNJ = kWTM / 16;       // 16-wide m pieces per wave
+  static constexpr int kNI = kWTN / 16;       // 16-wide n pieces per wave
   static constexpr int kXBytes = BM * 128;
-  static constexpr int kWBytes = kBN * 128;
-  static constexpr int kSaBytes = BM * 4;
+  static constexpr int kWBytes = BN * 128;
+  static constexpr int kSbWords = 64;
+  static constexpr int kSaBytes = (BM + kSbWords) * 4;  // BM activation scales, weight scales
   static constexpr int kStage = kXBytes + kWBytes + kSaBytes;
+  static constexpr int kStages = 3 * kStage <= kLdsBytes ? 3 : 2;
   static constexpr int kLds = kStage * kStages;
-  static constexpr int kWM = BM / 2;         // rows of m per wave
-  static constexpr int kNJ = kWM / 16;       // 16-wide m pieces per wave
-  static constexpr int kXLoads = BM / 32;    // 1 KB DMA blocks of the X tile per wave
-  static constexpr int kWLoads = kBN / 32;   // ... of the W tile per wave
-  static constexpr int kSaWaves = BM / 64;   // waves that load 64 scale words each
+  static constexpr int kXLoads = BM / 8 / kWaves;   // 1 KB DMA blocks of the X tile per wave
+  static constexpr int kWLoads = BN / 8 / kWaves;   // ... of the W tile per wave
+  static constexpr int kSaWaves = BM / 64;          // waves that load 64 scale words each
+  static constexpr int kSbWave = (BM / 64) % kWaves;  // wave that loads the weight scales
+  static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "DMA split");
+  static_assert(kSaWaves <= kWaves, "scale loaders");
+  static_assert(kWTN <= 128 && 128 % kWTN == 0, "a wave's n range lies in one 128 block");
+  static_assert(2 * kStage <= kLdsBytes, "LDS");
 };
 
 struct GemmParams {
@@ -67,7 +83,7 @@ struct GemmParams {
   int64_t sa_ks, sa_rs, sa_bytes;
   int sa_rdiv;
   const float* sb;    // sb(n, kb) = sb[kb * sb_ks + (n / 128) * sb_rs]
-  int64_t sb_ks, sb_rs;
+  int64_t sb_ks, sb_rs, sb_bytes;
   uint16_t* C;
   int64_t ldc;
   int tiles_m, tiles_n;
@@ -179,9 +195,9 @@ __device__ __forceinline__ uint32_t dma_voffset(int q, int lane, int64_t ld) {
 }
 
 // Zero the bytes of a K-major tile whose k is at or beyond krem (last, partial K block).
-template <int ROWS>
+template <int ROWS, int THREADS>
 __device__ __forceinline__ void zero_k_tail(uint8_t* tile, int krem) {
-  for (int id = threadIdx.x; id < ROWS * 8; id += kThreads) {
+  for (int id = threadIdx.x; id < ROWS * 8; id += THREADS) {
     const int r = id >> 3, c = id & 7;
     uint8_t* p = tile + r * 128 + ((c ^ (r & 7)) << 4);
     if (16 * c >= krem) {
@@ -198,48 +214,58 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vm_upto(int n) {
+  // n is wave-uniform and in {N, N+1, N+2}
+  if (n == N + 2) wait_vm<N + 2>();
+  else if (n == N + 1) wait_vm<N + 1>();
+  else wait_vm<N>();
+}
+
 // ------------------------------------------------------------------ one output tile
-// Computes C[m0 .. m_end) x [n0 .. n0 + 128) (columns clipped to N) with the operand roles of
+// Computes C[m0 .. m_end) x [n0 .. n0 + BN) (columns clipped to N) with the operand roles of
 // LAYOUT; A points at the activation-side matrix, Bw at the weight-side matrix of this tile's
-// group, sbw at the group's weight scales.
-template <int LAYOUT, int FA, int FB, bool FOLD, int BM>
+// group, sbw at the group's weight scales (sb_bytes bytes).
+template <class C, int LAYOUT, int FA, int FB, bool FOLD>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, int64_t m0,
                                           int64_t m_end, int64_t n0, const uint8_t* Bw,
-                                          const float* sbw) {
-  using T = Tile<BM>;
+                                          const float* sbw, int64_t sb_bytes) {
   constexpr bool XK = LAYOUT != FP8BS_WGRAD;   // activation side K-major?
   constexpr bool WK = LAYOUT == FP8BS_FPROP;   // weight side K-major?
+  constexpr int BM = C::BM, BN = C::BN, NI = C::kNI, NJ = C::kNJ;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int wm = w & 1, wn = w >> 1;
+  const int wm = w % C::kWavesM, wn = w / C::kWavesM;
   const int li = lane & 15, g = lane >> 4;
   const int64_t K = p.K;
   const int nkb = (int)((K + 127) >> 7);
   const int krem = (int)(K - (int64_t)(nkb - 1) * 128);
   const uint32_t lds0 = lds_addr(smem);
+  const int64_t nblk0 = n0 >> 7;
 
-  // DMA source offsets (fixed across K blocks) and LDS destinations (per stage + offset).
-  uint32_t xoff[T::kXLoads], woff[T::kWLoads];
+  // DMA source offsets (fixed across K blocks).
+  uint32_t xoff[C::kXLoads], woff[C::kWLoads];
 #pragma unroll
-  for (int q = 0; q < T::kXLoads; ++q) xoff[q] = dma_voffset<XK>(w * T::kXLoads + q, lane, p.lda);
+  for (int q = 0; q < C::kXLoads; ++q) xoff[q] = dma_voffset<XK>(w * C::kXLoads + q, lane, p.lda);
 #pragma unroll
-  for (int q = 0; q < T::kWLoads; ++q) woff[q] = dma_voffset<WK>(w * T::kWLoads + q, lane, p.ldb);
-  const bool sa_loader = w < T::kSaWaves;
-  uint32_t saoff = 0xFFFFFFFFu;
+  for (int q = 0; q < C::kWLoads; ++q) woff[q] = dma_voffset<WK>(w * C::kWLoads + q, lane, p.ldb);
+  const bool sa_loader = w < C::kSaWaves;
+  const bool sb_loader = w == C::kSbWave;
+  uint32_t saoff = 0xFFFFFFFFu, sboff = 0xFFFFFFFFu;
   {
     const int64_t row = m0 + w * 64 + lane;
     if (row < m_end) saoff = (uint32_t)(((row / p.sa_rdiv) * p.sa_rs) * 4);
+    const int64_t nb = nblk0 + lane;
+    if (lane < BN / 128 && nb * 128 < p.N) sboff = (uint32_t)(nb * p.sb_rs * 4);
   }
 
-  // Bytes of each operand addressable from the K block's base (bounds of the descriptors).
-  const int64_t a_rows = XK ? m_end : K;           // rows of the stored activation matrix
+  // Rows of each stored operand, for the descriptor bounds.
+  const int64_t a_rows = XK ? m_end : K;
   const int64_t w_rows = WK ? p.N : K;
 
   auto issue = [&](int kb) {
-    const int st = kb % kStages;
-    const uint32_t sbase = lds0 + st * T::kStage;
+    const uint32_t sbase = lds0 + (kb % C::kStages) * C::kStage;
     const int64_t k0 = (int64_t)kb * 128;
-    // activation side
     {
       const uint8_t* base;
       int64_t avail;
@@ -252,10 +278,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
       }
       const u32x4 r = make_rsrc(base, avail > 0 ? (uint64_t)avail : 0);
 #pragma unroll
-      for (int q = 0; q < T::kXLoads; ++q)
-        dma16(r, xoff[q], __builtin_amdgcn_readfirstlane(sbase + (w * T::kXLoads + q) * 1024));
+      for (int q = 0; q < C::kXLoads; ++q)
+        dma16(r, xoff[q], __builtin_amdgcn_readfirstlane(sbase + (w * C::kXLoads + q) * 1024));
     }
-    // weight side
     {
       const uint8_t* base;
       int64_t avail;
@@ -268,77 +293,97 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
       }
       const u32x4 r = make_rsrc(base, avail > 0 ? (uint64_t)avail : 0);
 #pragma unroll
-      for (int q = 0; q < T::kWLoads; ++q)
-        dma16(r, woff[q], __builtin_amdgcn_readfirstlane(sbase + T::kXBytes + (w * T::kWLoads + q) * 1024));
+      for (int q = 0; q < C::kWLoads; ++q)
+        dma16(r, woff[q], __builtin_amdgcn_readfirstlane(sbase + C::kXBytes + (w * C::kWLoads + q) * 1024));
     }
-    // activation scales of the K block (one word per tile row)
+    // Scales of the K block: one activation word per tile row, then one weight word per
+    // 128-column block of the tile (lanes past those read outside the descriptor: zeros).
     if constexpr (FOLD) {
       if (sa_loader) {
         const int64_t off = kb * p.sa_ks;
         const u32x4 r = make_rsrc(p.sa + off, (uint64_t)(p.sa_bytes - off * 4));
-        dma4(r, saoff, __builtin_amdgcn_readfirstlane(sbase + T::kXBytes + T::kWBytes + w * 256));
+        dma4(r, saoff, __builtin_amdgcn_readfirstlane(sbase + C::kXBytes + C::kWBytes + w * 256));
+      }
+      if (sb_loader) {
+        const int64_t off = kb * p.sb_ks;
+        const u32x4 r = make_rsrc(sbw + off, (uint64_t)(sb_bytes - off * 4));
+        dma4(r, sboff, __builtin_amdgcn_readfirstlane(sbase + C::kXBytes + C::kWBytes + BM * 4));
       }
     }
   };
-  // loads per K block issued by this wave (the vmcnt bookkeeping is per wave)
-  constexpr int kPerStage = T::kXLoads + T::kWLoads;
-  const int per_stage = kPerStage + ((FOLD && sa_loader) ? 1 : 0);
+  // DMA instructions per K block issued by this wave (vmcnt is counted per wave).
+  constexpr int kPerStage = C::kXLoads + C::kWLoads;
+  const int per_stage =
+      kPerStage + ((FOLD && sa_loader) ? 1 : 0) + ((FOLD && sb_loader) ? 1 : 0);
 
-  v4f acc[4][T::kNJ];
+  v4f acc[NI][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < T::kNJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  if (nkb > 0) issue(0);
-  if (nkb > 1) issue(1);
-  const int64_t nblk = n0 >> 7;
+  for (int s = 0; s < C::kStages - 1; ++s)
+    if (s < nkb) issue(s);
   for (int kb = 0; kb < nkb; ++kb) {
-    // Stage kb must have landed: only stage kb+1's loads may still be outstanding.
-    if (kb + 1 < nkb) {
-      if (per_stage == kPerStage + 1) wait_vm<kPerStage + 1>();
-      else wait_vm<kPerStage>();
+    // Stage kb must have landed; the loads of later stages may still be in flight.
+    if constexpr (C::kStages == 3) {
+      if (kb + 1 < nkb) wait_vm_upto<kPerStage>(per_stage);
+      else wait_vm<0>();
     } else {
       wait_vm<0>();
     }
     barrier();
-    if (kb + 2 < nkb) issue(kb + 2);
-    uint8_t* st = smem + (kb % kStages) * T::kStage;
+    if (kb + C::kStages - 1 < nkb) issue(kb + C::kStages - 1);
+    uint8_t* st = smem + (kb % C::kStages) * C::kStage;
     const uint8_t* xt = st;
-    const uint8_t* wt = st + T::kXBytes;
-    const float* sat = reinterpret_cast<const float*>(st + T::kXBytes + T::kWBytes);
+    const uint8_t* wt = st + C::kXBytes;
+    const float* sat = reinterpret_cast<const float*>(st + C::kXBytes + C::kWBytes);
     if (kb == nkb - 1 && krem < 128 && (XK || WK)) {
-      if constexpr (XK) zero_k_tail<BM>(st, krem);
-      if constexpr (WK) zero_k_tail<kBN>(st + T::kXBytes, krem);
+      if constexpr (XK) zero_k_tail<BM, C::kThreads>(st, krem);
+      if constexpr (WK) zero_k_tail<BN, C::kThreads>(st + C::kXBytes, krem);
       __syncthreads();
     }
-    float sbv = 1.0f;
-    if constexpr (FOLD) sbv = sbw[kb * p.sb_ks + nblk * p.sb_rs];
-
-    v8i wf[4];
+    v8i wf[NI];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wf[i] = fragment<WK>(wt, wn * 64 + 16 * i + li, li, g);
+    for (int i = 0; i < NI; ++i) wf[i] = fragment<WK>(wt, wn * C::kWTN + 16 * i + li, li, g);
+    if constexpr (FOLD) {
+      // Software pipeline over the m pieces: the MFMAs of piece j are issued while the partial
+      // sums of piece j-1 are folded into the accumulators.
+      const float sbv = sat[BM + (wn * C::kWTN) / 128];
+      v4f P[2][NI];
+      float cprev = 0.0f;
+      v8i xf = fragment<XK>(xt, wm * C::kWTM + li, li, g);
 #pragma unroll
-    for (int j = 0; j < T::kNJ; ++j) {
-      const int mrow = wm * T::kWM + 16 * j + li;
-      const v8i xf = fragment<XK>(xt, mrow, li, g);
-      if constexpr (FOLD) {
+      for (int j = 0; j < NJ; ++j) {
+        const int mrow = wm * C::kWTM + 16 * j + li;
+        v8i xnext;
+        if (j + 1 < NJ) xnext = fragment<XK>(xt, mrow + 16, li, g);
         const float c = sat[mrow] * sbv;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const v4f pv = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+        for (int i = 0; i < NI; ++i)
+          P[j & 1][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               wf[i], xf, v4f{0.f, 0.f, 0.f, 0.f}, FB, FA, 0, 0, 0, 0);
-          acc[i][j] += pv * c;
-        }
-      } else {
+        if (j > 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < NI; ++i) acc[i][j - 1] += P[(j - 1) & 1][i] * cprev;
+        }
+        cprev = c;
+        if (j + 1 < NJ) xf = xnext;
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) acc[i][NJ - 1] += P[(NJ - 1) & 1][i] * cprev;
+    } else {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const v8i xf = fragment<XK>(xt, wm * C::kWTM + 16 * j + li, li, g);
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[i], xf, acc[i][j], FB,
                                                                        FA, 0, 0, 0, 0);
       }
     }
-    // every wave is done with this stage before it is refilled two iterations later: the
-    // barrier at the top of the next iteration orders it.
+    // A stage is refilled kStages-1 iterations after it was read; the barrier at the top of
+    // the next iteration orders every wave's reads before that refill is issued.
   }
 
   float post = 1.0f;
@@ -346,13 +391,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
 
   // Epilogue: lane holds C[m][n .. n+3] of each piece.
 #pragma unroll
-  for (int j = 0; j < T::kNJ; ++j) {
-    const int64_t m = m0 + wm * T::kWM + 16 * j + li;
+  for (int j = 0; j < NJ; ++j) {
+    const int64_t m = m0 + wm * C::kWTM + 16 * j + li;
     if (m >= m_end) continue;
     uint16_t* crow = p.C + m * p.ldc;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t n = n0 + wn * 64 + 16 * i + 4 * g;
+    for (int i = 0; i < NI; ++i) {
+      const int64_t n = n0 + wn * C::kWTN + 16 * i + 4 * g;
       v4f v = acc[i][j];
       if constexpr (!FOLD) v = v * post;
       if (nkb == 0) v = v4f{0.f, 0.f, 0.f, 0.f};
@@ -386,14 +431,14 @@ __device__ __forceinline__ void tile_of(int id, int tiles_m, int tiles_n, int& t
   tn = in / gsz;
 }
 
-template <int LAYOUT, int FA, int FB, bool FOLD, int BM>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
+template <class C, int LAYOUT, int FA, int FB, bool FOLD>
+__global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int tm, tn;
   tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM;
-  gemm_tile<LAYOUT, FA, FB, FOLD, BM>(p, smem, m0, std::min<int64_t>(m0 + BM, p.M),
-                                      (int64_t)tn * kBN, p.B, p.sb);
+  const int64_t m0 = (int64_t)tm * C::BM;
+  gemm_tile<C, LAYOUT, FA, FB, FOLD>(p, smem, m0, std::min<int64_t>(m0 + C::BM, p.M),
+                                     (int64_t)tn * C::BN, p.B, p.sb, p.sb_bytes);
 }
 
 // Grouped: a persistent grid walks the concatenation of every group's m tiles (times the n
@@ -401,15 +446,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 // each of its tiles to (group, m tile, n tile) by binary search.
 constexpr int kMaxGroups = 1024;
 
-template <int FA, int FB, int BM>
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p) {
+template <class C, int FA, int FB>
+__global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_prefix[kMaxGroups + 1];
-  __shared__ int s_wave_sum[kThreads / 64];
+  __shared__ int s_wave_sum[C::kWaves];
+  constexpr int BM = C::BM;
   const int G = p.num_groups;
-  // tiles per group (offsets are clamped to [0, M] and made non-decreasing)
+  // m tiles per group (offsets clamped to [0, M] and made non-decreasing), prefix-summed
   int carry = 0;
-  for (int base = 0; base < G; base += kThreads) {
+  for (int base = 0; base < G; base += C::kThreads) {
     const int gi = base + threadIdx.x;
     int tiles = 0;
     if (gi < G) {
@@ -417,7 +463,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
       const int64_t hi = std::min<int64_t>(std::max<int64_t>(p.offsets[gi + 1], lo), p.M);
       tiles = (int)((hi - lo + BM - 1) / BM);
     }
-    // inclusive scan across the workgroup
     int v = tiles;
     const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -431,7 +476,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     for (int w = 0; w < (int)(threadIdx.x >> 6); ++w) before += s_wave_sum[w];
     if (gi < G) s_prefix[gi + 1] = before + v;
     int total = carry;
-    for (int w = 0; w < kThreads / 64; ++w) total += s_wave_sum[w];
+    for (int w = 0; w < C::kWaves; ++w) total += s_wave_sum[w];
     carry = total;
     __syncthreads();
   }
@@ -450,44 +495,69 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     const int64_t glo = std::min<int64_t>(std::max<int64_t>(p.offsets[gi], 0), p.M);
     const int64_t ghi = std::min<int64_t>(std::max<int64_t>(p.offsets[gi + 1], glo), p.M);
     const int64_t m0 = glo + (int64_t)(mt - s_prefix[gi]) * BM;
-    gemm_tile<FP8BS_FPROP, FA, FB, true, BM>(p, smem, m0, std::min<int64_t>(m0 + BM, ghi),
-                                             (int64_t)tn * kBN, p.B + gi * p.b_group_stride,
-                                             p.sb + gi * p.sb_group_stride);
+    gemm_tile<C, FP8BS_FPROP, FA, FB, true>(p, smem, m0, std::min<int64_t>(m0 + BM, ghi),
+                                            (int64_t)tn * C::BN, p.B + gi * p.b_group_stride,
+                                            p.sb + gi * p.sb_group_stride,
+                                            p.sb_group_stride * 4);
     __syncthreads();   // the next tile refills the LDS stages
   }
 }
 
 template <typename KernelT>
-int launch_gemm(KernelT kernel, int blocks, int lds, hipStream_t st, const GemmParams& p) {
+int launch_gemm(KernelT kernel, int blocks, int threads, int lds, hipStream_t st,
+                const GemmParams& p) {
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
     return FP8BS_ERR_LAUNCH;
   void* args[] = {const_cast<GemmParams*>(&p)};
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(blocks),
-                                 dim3(kThreads), args, lds, st);
+                                 dim3(threads), args, lds, st);
   return e == hipSuccess ? FP8BS_OK : FP8BS_ERR_LAUNCH;
 }
 
-template <int LAYOUT, int FA, int FB>
-int dispatch_fold(bool fold, bool small_m, const GemmParams& p, hipStream_t st) {
-  constexpr int kBig = 256, kSmall = 128;
-  if (small_m) {
-    const int blocks = p.tiles_m * p.tiles_n;
-    return fold ? launch_gemm(gemm_kernel<LAYOUT, FA, FB, true, kSmall>, blocks, Tile<kSmall>::kLds, st, p)
-                : launch_gemm(gemm_kernel<LAYOUT, FA, FB, false, kSmall>, blocks, Tile<kSmall>::kLds, st, p);
-  }
+// Tile configurations.
+using CfgA = Cfg<256, 128, 2, 2>;   // 4 waves, 128 x 64 per wave, 3 stages
+using CfgB = Cfg<256, 128, 4, 2>;   // 8 waves, 64 x 64 per wave, 3 stages
+using CfgC = Cfg<256, 256, 2, 4>;   // 8 waves, 128 x 64 per wave, 2 stages
+using CfgD = Cfg<128, 128, 2, 2>;   // 4 waves, 64 x 64 per wave (small M, grouped)
+
+template <class C, int LAYOUT, int FA, int FB>
+int launch_dense(bool fold, GemmParams p, hipStream_t st) {
+  p.tiles_m = (int)ceil_div(p.M, C::BM);
+  p.tiles_n = (int)ceil_div(p.N, C::BN);
+  if ((int64_t)p.tiles_m * p.tiles_n > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
   const int blocks = p.tiles_m * p.tiles_n;
-  return fold ? launch_gemm(gemm_kernel<LAYOUT, FA, FB, true, kBig>, blocks, Tile<kBig>::kLds, st, p)
-              : launch_gemm(gemm_kernel<LAYOUT, FA, FB, false, kBig>, blocks, Tile<kBig>::kLds, st, p);
+  return fold ? launch_gemm(gemm_kernel<C, LAYOUT, FA, FB, true>, blocks, C::kThreads, C::kLds, st, p)
+              : launch_gemm(gemm_kernel<C, LAYOUT, FA, FB, false>, blocks, C::kThreads, C::kLds, st, p);
+}
+
+// Variant choice: the largest tile that still gives every CU at least one workgroup (two
+// waves per SIMD hide LDS and MFMA latency best).  FP8BS_GEMM_VARIANT (A, B, C or D) overrides
+// the choice, for tuning and tests.
+char pick_variant(int64_t M, int64_t N) {
+  const char* e = getenv("FP8BS_GEMM_VARIANT");
+  if (e && (e[0] == 'A' || e[0] == 'B' || e[0] == 'C' || e[0] == 'D')) return e[0];
+  if (ceil_div(M, 256) * ceil_div(N, 256) >= 256) return 'C';
+  if (ceil_div(M, 256) * ceil_div(N, 128) >= 256) return 'B';
+  return 'D';
+}
+
+template <int LAYOUT, int FA, int FB>
+int dispatch_variant(bool fold, const GemmParams& p, hipStream_t st) {
+  switch (pick_variant(p.M, p.N)) {
+    case 'B': return launch_dense<CfgB, LAYOUT, FA, FB>(fold, p, st);
+    case 'C': return launch_dense<CfgC, LAYOUT, FA, FB>(fold, p, st);
+    case 'D': return launch_dense<CfgD, LAYOUT, FA, FB>(fold, p, st);
+    default: return launch_dense<CfgA, LAYOUT, FA, FB>(fold, p, st);
+  }
 }
 
 template <int LAYOUT>
-int dispatch_formats(int fa, int fb, bool fold, bool small_m, const GemmParams& p,
-                     hipStream_t st) {
-  if (fa == FP8BS_E4M3 && fb == FP8BS_E4M3) return dispatch_fold<LAYOUT, FP8BS_E4M3, FP8BS_E4M3>(fold, small_m, p, st);
-  if (fa == FP8BS_E5M2 && fb == FP8BS_E4M3) return dispatch_fold<LAYOUT, FP8BS_E5M2, FP8BS_E4M3>(fold, small_m, p, st);
-  if (fa == FP8BS_E4M3 && fb == FP8BS_E5M2) return dispatch_fold<LAYOUT, FP8BS_E4M3, FP8BS_E5M2>(fold, small_m, p, st);
-  return dispatch_fold<LAYOUT, FP8BS_E5M2, FP8BS_E5M2>(fold, small_m, p, st);
+int dispatch_formats(int fa, int fb, bool fold, const GemmParams& p, hipStream_t st) {
+  if (fa == FP8BS_E4M3 && fb == FP8BS_E4M3) return dispatch_variant<LAYOUT, FP8BS_E4M3, FP8BS_E4M3>(fold, p, st);
+  if (fa == FP8BS_E5M2 && fb == FP8BS_E4M3) return dispatch_variant<LAYOUT, FP8BS_E5M2, FP8BS_E4M3>(fold, p, st);
+  if (fa == FP8BS_E4M3 && fb == FP8BS_E5M2) return dispatch_variant<LAYOUT, FP8BS_E4M3, FP8BS_E5M2>(fold, p, st);
+  return dispatch_variant<LAYOUT, FP8BS_E5M2, FP8BS_E5M2>(fold, p, st);
 }
 
 // Scale indexing for one operand.  rows: the operand's output dimension (m or n);
@@ -549,20 +619,15 @@ extern "C" int fp8_gemm_blockscaled(int layout, int64_t M, int64_t N, int64_t K,
   p.A = static_cast<const uint8_t*>(A); p.lda = lda;
   p.B = static_cast<const uint8_t*>(B); p.ldb = ldb;
   p.sa = scale_inv_a; p.sa_ks = sa.ks; p.sa_rs = sa.rs; p.sa_bytes = sa.bytes; p.sa_rdiv = sa.rdiv;
-  p.sb = scale_inv_b; p.sb_ks = sb.ks; p.sb_rs = sb.rs;
+  p.sb = scale_inv_b; p.sb_ks = sb.ks; p.sb_rs = sb.rs; p.sb_bytes = sb.bytes;
   p.C = static_cast<uint16_t*>(C_bf16); p.ldc = ldc;
   p.c_vec = (reinterpret_cast<uintptr_t>(C_bf16) % 8 == 0) && (ldc % 4 == 0);
-  const bool small_m = M <= 128 * 64;   // more, smaller tiles while the grid is under-filled
-  const int bm = small_m ? 128 : 256;
-  p.tiles_m = (int)ceil_div(M, bm);
-  p.tiles_n = (int)ceil_div(N, kBN);
-  if ((int64_t)p.tiles_m * p.tiles_n > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
   const bool fold = !(ga == FP8BS_PER_TENSOR && gb == FP8BS_PER_TENSOR);
   hipStream_t st = static_cast<hipStream_t>(stream);
   switch (layout) {
-    case FP8BS_FPROP: return dispatch_formats<FP8BS_FPROP>(fa, fb, fold, small_m, p, st);
-    case FP8BS_DGRAD: return dispatch_formats<FP8BS_DGRAD>(fa, fb, fold, small_m, p, st);
-    default: return dispatch_formats<FP8BS_WGRAD>(fa, fb, fold, small_m, p, st);
+    case FP8BS_FPROP: return dispatch_formats<FP8BS_FPROP>(fa, fb, fold, p, st);
+    case FP8BS_DGRAD: return dispatch_formats<FP8BS_DGRAD>(fa, fb, fold, p, st);
+    default: return dispatch_formats<FP8BS_WGRAD>(fa, fb, fold, p, st);
   }
 }
 
@@ -583,7 +648,7 @@ extern "C" int fp8_grouped_gemm(int32_t num_groups, const int64_t* group_offsets
   if (!aligned16(A) || !aligned16(B) || lda % 16 || ldb % 16) return FP8BS_ERR_ALIGN;
   if (!aligned4(C_bf16) || ldc % 2 || (reinterpret_cast<uintptr_t>(group_offsets) & 7))
     return FP8BS_ERR_ALIGN;
-  constexpr int BM = 128;
+  using C = CfgD;
   GemmParams p{};
   p.M = total_M; p.N = N; p.K = K;
   p.A = static_cast<const uint8_t*>(A); p.lda = lda;
@@ -593,21 +658,21 @@ extern "C" int fp8_grouped_gemm(int32_t num_groups, const int64_t* group_offsets
   p.sb = scale_inv_b; p.sb_ks = 1; p.sb_rs = ceil_div(K, 128);
   p.C = static_cast<uint16_t*>(C_bf16); p.ldc = ldc;
   p.c_vec = (reinterpret_cast<uintptr_t>(C_bf16) % 8 == 0) && (ldc % 4 == 0);
-  p.tiles_n = (int)ceil_div(N, kBN);
-  p.tiles_m = (int)(ceil_div(total_M, BM) + num_groups);   // upper bound on m tiles
+  p.tiles_n = (int)ceil_div(N, C::BN);
+  p.tiles_m = (int)(ceil_div(total_M, C::BM) + num_groups);   // upper bound on m tiles
   p.offsets = group_offsets;
   p.num_groups = num_groups;
   p.b_group_stride = N * ldb;
   p.sb_group_stride = ceil_div(N, 128) * ceil_div(K, 128);
   if ((int64_t)p.tiles_m * p.tiles_n > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
   int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess)
-    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
   const int blocks = (int)std::min<int64_t>((int64_t)p.tiles_m * p.tiles_n, std::max(cus, 1));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  constexpr int lds = Tile<BM>::kLds;
-  if (fa == FP8BS_E4M3 && fb == FP8BS_E4M3) return launch_gemm(grouped_gemm_kernel<FP8BS_E4M3, FP8BS_E4M3, BM>, blocks, lds, st, p);
-  if (fa == FP8BS_E5M2 && fb == FP8BS_E4M3) return launch_gemm(grouped_gemm_kernel<FP8BS_E5M2, FP8BS_E4M3, BM>, blocks, lds, st, p);
-  if (fa == FP8BS_E4M3 && fb == FP8BS_E5M2) return launch_gemm(grouped_gemm_kernel<FP8BS_E4M3, FP8BS_E5M2, BM>, blocks, lds, st, p);
-  return launch_gemm(grouped_gemm_kernel<FP8BS_E5M2, FP8BS_E5M2, BM>, blocks, lds, st, p);
+  if (fa == FP8BS_E4M3 && fb == FP8BS_E4M3) return launch_gemm(grouped_gemm_kernel<C, FP8BS_E4M3, FP8BS_E4M3>, blocks, C::kThreads, C::kLds, st, p);
+  if (fa == FP8BS_E5M2 && fb == FP8BS_E4M3) return launch_gemm(grouped_gemm_kernel<C, FP8BS_E5M2, FP8BS_E4M3>, blocks, C::kThreads, C::kLds, st, p);
+  if (fa == FP8BS_E4M3 && fb == FP8BS_E5M2) return launch_gemm(grouped_gemm_kernel<C, FP8BS_E4M3, FP8BS_E5M2>, blocks, C::kThreads, C::kLds, st, p);
+  return launch_gemm(grouped_gemm_kernel<C, FP8BS_E5M2, FP8BS_E5M2>, blocks, C::kThreads, C::kLds, st, p);
 }

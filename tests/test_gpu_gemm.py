@@ -61,7 +61,7 @@ def run_gemm(gpu, layout, M, N, K, fa, ga, fb, gb, seed=0, pad=0, rows=None, c_g
     lda = -(-ashape[1] // 16) * 16 + pad
     ldb = -(-bshape[1] // 16) * 16 + pad
     ad, bd = to_device_codes(qa, lda), to_device_codes(qb, ldb)
-    ldc = N + (8 if c_guard else 0)
+    ldc = -(-N // 2) * 2 + (8 if c_guard else 0)   # even pitch; N odd exercises 2-byte stores
     cstore = torch.full((M + 1, ldc), -7.0, dtype=torch.bfloat16, device="cuda")
     c = cstore[:M, :N]
     gpu.gemm_blockscaled(layout, ad, fa, ga, device_scales(sa, ga), bd, fb, gb,
@@ -226,3 +226,13 @@ def test_grouped_moe_config_sampled(gpu):
     counts = synth.moe_routing(16384, 128, 8, 1.1, 0)
     rows = np.sort(np.random.Generator(np.random.PCG64(3)).choice(int(counts.sum()), 256, replace=False))
     run_grouped(gpu, counts, 1536, 2048, sample_rows=rows)
+
+
+@pytest.mark.parametrize("variant", ["A", "B", "C", "D"])
+@pytest.mark.parametrize("layout,fa,ga,fb,gb", [(FP, E4, B1, E4, B128), (DG, E5, B1, E4, B128),
+                                                 (WG, E5, PT, E4, B128)])
+def test_every_tile_variant(gpu, monkeypatch, variant, layout, fa, ga, fb, gb):
+    """Each tile configuration the library can pick (FP8BS_GEMM_VARIANT forces one)."""
+    monkeypatch.setenv("FP8BS_GEMM_VARIANT", variant)
+    run_gemm(gpu, layout, 520, 390, 392, fa, ga, fb, gb)
+    run_gemm(gpu, layout, 256, 256, 256, fa, ga, fb, gb)
