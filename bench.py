@@ -15,7 +15,7 @@ cpu_baseline: the CPU oracle (C quantizer + NumPy fp64 GEMM) on a bounded row sa
 same step, on the host's cores.
 
 Other workloads (--workload): quant-sweep (HBM-bound quantizer), moe (grouped GEMM),
-backward (delayed-scaled dgrad / wgrad), tiny.  Each prints one JSON line.
+backward (delayed-scaled dgrad / wgrad), copy (counter calibration).  Each prints one JSON line.
 """
 from __future__ import annotations
 
@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b-fprop",
-                    choices=["llama8b-fprop", "quant-sweep", "moe", "backward", "tiny"])
+                    choices=["llama8b-fprop", "quant-sweep", "moe", "backward", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tokens", type=int, default=8192)
     return ap.parse_args()
@@ -185,7 +185,7 @@ def bench_llama8b(args):
     return result
 
 
-def cpu_baseline_8b(layers, M, rows: int = 64):
+def cpu_baseline_8b(layers, M, rows: int = 1024):
     """The oracle on a row sample of the same step: quantize `rows` activation rows (1x128),
     the full weight (128x128), dequantize and multiply in fp64.  Scaled to TFLOP/s of the
     sample's GEMM flops."""
@@ -207,6 +207,221 @@ def cpu_baseline_8b(layers, M, rows: int = 64):
                        f"re-quantized), {dt:.1f} s")
 
 
+# ----------------------------------------------------------------------------- quantizer sweep
+
+SWEEP_SHAPES = [(4096, 4096), (32768, 4096), (131072, 4096), (1152, 14336), (9344, 14336),
+                (37504, 14336)]
+
+
+def bench_quant_sweep(args):
+    """HBM-bound quantizer on Student-t(3) bf16 tensors of 16M / 128M / 512M elements (rows of
+    4096 or 14336), 1x128 and 128x128 E4M3, fp32 and power-of-2 scales.  Buffers rotate over
+    more than 512 MiB so that the 256 MiB last-level cache does not serve the inputs."""
+    import block_scaled_quantize_amd as bsq
+    import synth
+    bsq.load()
+    dev = torch.device("cuda", 0)
+    cases = {}
+    for rows, cols in SWEEP_SHAPES:
+        n = rows * cols
+        nbuf = max(1, -(-(600 << 20) // (3 * n)))
+        log(f"sweep {rows}x{cols}: {nbuf} rotating buffers")
+        base = synth.student_t((rows, cols), 3.0, 0, f"bench/sweep/{rows}x{cols}").to(dev)
+        xs = [base] + [base.roll(i, 0) for i in range(1, nbuf)]
+        for gran in (bsq.BLOCK_1x128, bsq.BLOCK_128x128):
+            qs = [torch.empty((rows, cols), dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+            ss = [torch.empty(bsq.scale_shape(rows, cols, gran), dtype=torch.float32, device=dev)
+                  for _ in range(nbuf)]
+            for mode in (bsq.SCALE_FP32, bsq.SCALE_POW2):
+                def run(i):
+                    bsq.quantize_blockwise(xs[i % nbuf], bsq.E4M3, gran, mode, q=qs[i % nbuf],
+                                           scale_inv=ss[i % nbuf])
+                for i in range(args.warmup):
+                    run(i)
+                torch.cuda.synchronize()
+                iters = max(args.steps, 10)
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(iters)]
+                for i in range(iters):
+                    ev[i][0].record()
+                    run(i)
+                    ev[i][1].record()
+                torch.cuda.synchronize()
+                ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+                nb = ss[0].numel() * 4
+                byts = 3.0 * n + nb
+                key = f"{rows}x{cols}/{'1x128' if gran == 0 else '128x128'}/{'fp32' if mode == 0 else 'pow2'}"
+                cases[key] = dict(us=round(ms * 1e3, 2), gbps=round(byts / ms / 1e6, 1),
+                                  hbm_frac=round(byts / ms / 1e6 / HBM_PEAK_GBPS, 4), bytes=byts)
+                log(f"  {key}: {ms * 1e3:.1f} us, {byts / ms / 1e6:.0f} GB/s")
+            del qs, ss
+        del xs, base
+        torch.cuda.empty_cache()
+    head = cases["131072x4096/1x128/fp32"]
+    res = dict(metric="quantize GB/s (bf16 -> E4M3 codes + scales), % of MI355X HBM peak",
+               value=head["gbps"], unit="GB/s", n_gpus=1, steps=max(args.steps, 10),
+               warmup=args.warmup, ms_per_step=head["us"] / 1e3, higher_is_better=True,
+               scaling="weak", vs_baseline=None, dtype="bf16 -> u8 (E4M3) + fp32 scales",
+               data="synthetic",
+               config=dict(workload="quantizer-sweep", headline="131072x4096 1x128 fp32-scale",
+                           distribution="Student-t(3)"),
+               roofline=dict(bound="hbm", achieved=head["gbps"], peak=HBM_PEAK_GBPS, unit="GB/s",
+                             frac=head["hbm_frac"], traffic=None,
+                             kernel="quant_1x128_kernel<E4M3,fp32,vec>",
+                             per_launch_bytes=head["bytes"], mean_launch_us=head["us"]),
+               cases=cases)
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build()
+        x = synth.student_t((4096, 4096), 3.0, 0, "bench/sweep/4096x4096")
+        xb = x.contiguous().view(torch.int16).numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < 10.0:
+            oracle.quantize_blockwise(xb, oracle.E4M3, oracle.BLOCK_1x128, oracle.SCALE_FP32)
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+        res["cpu_baseline"] = dict(value=round((3.0 * xb.size + 4 * xb.size / 128) / dt / 1e9, 3),
+                                   unit="GB/s", cores=cpu_cores(), kind="oracle",
+                                   sample=f"4096x4096 1x128 fp32, {reps} repetitions in {dt * reps:.1f} s")
+    return res
+
+
+# ----------------------------------------------------------------------------- MoE grouped
+
+def bench_moe(args):
+    """Grouped FP8 GEMM of a Qwen3-30B-A3B-shaped MoE layer: 128 experts, 16384 tokens routed
+    top-8 with Zipf(1.1) popularity (131072 rows sorted by expert); gate/up 2048 -> 1536 and
+    down 768 -> 2048 per expert, 1x128 activation / 128x128 weight E4M3 scales, bf16 out."""
+    import block_scaled_quantize_amd as bsq
+    import synth
+    bsq.load()
+    dev = torch.device("cuda", 0)
+    counts = synth.moe_routing(16384, 128, 8, 1.1, 0)
+    off = torch.from_numpy(synth.offsets_from_counts(counts)).to(dev)
+    T = int(counts.sum())
+    out = {}
+    total_flops, total_ms = 0.0, 0.0
+    for name, K, N in (("gate_up", 2048, 1536), ("down", 768, 2048)):
+        x = synth.normal((T, K), 1.0, 0, f"bench/moe/{name}/X").to(dev)
+        qx, sx = bsq.quantize_blockwise(x, bsq.E4M3, bsq.BLOCK_1x128)
+        del x
+        qw = torch.empty((128, N, K), dtype=torch.uint8, device=dev)
+        sw = torch.empty((128, N // 128, K // 128), dtype=torch.float32, device=dev)
+        for e in range(128):
+            w = synth.normal((N, K), 0.02, 0, f"bench/moe/{name}/W{e}").to(dev)
+            bsq.quantize_blockwise(w, bsq.E4M3, bsq.BLOCK_128x128, q=qw[e], scale_inv=sw[e])
+        c = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+        for _ in range(args.warmup):
+            bsq.grouped_gemm(off, qx, sx, qw, sw, c=c)
+        torch.cuda.synchronize()
+        iters = max(args.steps, 5)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        for a, b in ev:
+            a.record()
+            bsq.grouped_gemm(off, qx, sx, qw, sw, c=c)
+            b.record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        flops = 2.0 * T * N * K
+        byts = T * K + 128 * N * K + 2 * T * N + 4 * T * K / 128 + 4 * 128 * (N // 128) * (K // 128)
+        t_mfma = flops / (FP8_PEAK_TFLOPS * 1e12)
+        t_hbm = byts / (HBM_PEAK_GBPS * 1e9)
+        bound = "mfma" if t_mfma >= t_hbm else "hbm"
+        out[name] = dict(us=round(ms * 1e3, 1), tflops=round(flops / ms / 1e9, 1), gbps=round(byts / ms / 1e6, 1),
+                         bound=bound, frac_of_binding_roofline=round(max(t_mfma, t_hbm) / (ms / 1e3), 4))
+        total_flops += flops
+        total_ms += ms
+        log(f"moe {name}: {ms * 1e3:.1f} us {flops / ms / 1e9:.0f} TFLOP/s ({bound}-bound)")
+        del qx, sx, qw, sw, c
+        torch.cuda.empty_cache()
+    gu = out["gate_up"]
+    return dict(metric="grouped block-scaled FP8 GEMM TFLOP/s (MoE experts)",
+                value=round(total_flops / total_ms / 1e9, 1), unit="TFLOP/s", n_gpus=1,
+                steps=max(args.steps, 5), warmup=args.warmup, ms_per_step=round(total_ms, 4),
+                higher_is_better=True, scaling="weak", vs_baseline=None,
+                dtype="fp8e4m3 x fp8e4m3 -> fp32 acc -> bf16", data="synthetic",
+                config=dict(workload="qwen3-30b-a3b-moe-experts", experts=128, tokens=16384, topk=8,
+                            routing="Zipf(1.1)", rows=T),
+                roofline=dict(bound=gu["bound"], achieved=gu["tflops"], peak=FP8_PEAK_TFLOPS,
+                              unit="TFLOP/s", frac=round(gu["tflops"] / FP8_PEAK_TFLOPS, 4),
+                              traffic=None, kernel="grouped_gemm_kernel<128x128>"),
+                layers=out)
+
+
+# ----------------------------------------------------------------------------- backward
+
+def bench_backward(args):
+    """8B-shaped backward linear layers with per-tensor delayed scaling (history 16, max,
+    margin 0): X and W in E4M3, dY ~ N(0, 1e-3) in E5M2; per layer one delayed quantization of
+    each tensor, dgrad dX = dY . W and wgrad dW = dY^T . X.  Steps draw fresh X and dY."""
+    import block_scaled_quantize_amd as bsq
+    import synth
+    bsq.load()
+    dev = torch.device("cuda", 0)
+    M = args.tokens
+    layers = []
+    for name, k, n in LAYERS_8B:
+        L = dict(name=name, K=k, N=n,
+                 x=synth.activations_with_outliers(M, k, 0, f"bench/bwd/{name}/X").to(dev),
+                 w=synth.normal((n, k), 0.02, 0, f"bench/bwd/{name}/W").to(dev),
+                 dy=synth.normal((M, n), 1e-3, 0, f"bench/bwd/{name}/dY").to(dev),
+                 sx=bsq.DelayedState(16), sw=bsq.DelayedState(16), sdy=bsq.DelayedState(16),
+                 dx=torch.empty((M, k), dtype=torch.bfloat16, device=dev),
+                 dw=torch.empty((n, k), dtype=torch.bfloat16, device=dev))
+        layers.append(L)
+    flops = sum(4.0 * M * L["N"] * L["K"] for L in layers)
+
+    def step():
+        for L in layers:
+            qx, six = bsq.quantize_delayed(L["x"], bsq.E4M3, L["sx"])
+            qw, siw = bsq.quantize_delayed(L["w"], bsq.E4M3, L["sw"])
+            qdy, sidy = bsq.quantize_delayed(L["dy"], bsq.E5M2, L["sdy"])
+            bsq.gemm_blockscaled(bsq.DGRAD, qdy, bsq.E5M2, bsq.PER_TENSOR, sidy, qw, bsq.E4M3,
+                                 bsq.PER_TENSOR, siw, c=L["dx"])
+            bsq.gemm_blockscaled(bsq.WGRAD, qdy, bsq.E5M2, bsq.PER_TENSOR, sidy, qx, bsq.E4M3,
+                                 bsq.PER_TENSOR, six, c=L["dw"])
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    return dict(metric="block-scaled FP8 GEMM TFLOP/s, backward (dgrad + wgrad, delayed scaling)",
+                value=round(flops / dt / 1e12, 2), unit="TFLOP/s", n_gpus=1, steps=args.steps,
+                warmup=args.warmup, ms_per_step=round(dt * 1e3, 4), higher_is_better=True,
+                scaling="weak", vs_baseline=None, dtype="fp8e5m2 x fp8e4m3 -> fp32 acc -> bf16",
+                data="synthetic",
+                config=dict(workload="llama3.1-8b-backward-linear", tokens=M,
+                            scaling="per-tensor delayed, history 16, max, margin 0"),
+                roofline=None)
+
+
+def bench_copy(args):
+    """A plain 1 GiB device copy (torch), the calibration kernel for the HBM byte counters."""
+    dev = torch.device("cuda", 0)
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(args.warmup):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(args.steps):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / args.steps
+    return dict(metric="device copy GB/s (read + write)", value=round(2 * n / ms / 1e6, 1),
+                unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+                ms_per_step=round(ms, 4), higher_is_better=True, scaling="weak",
+                vs_baseline=None, dtype="u8", data="synthetic",
+                config=dict(workload="copy-1GiB", bytes_read=n, bytes_written=n), roofline=None)
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -221,6 +436,14 @@ def main():
     torch.cuda.set_device(0)
     if args.workload == "llama8b-fprop":
         res = bench_llama8b(args)
+    elif args.workload == "quant-sweep":
+        res = bench_quant_sweep(args)
+    elif args.workload == "moe":
+        res = bench_moe(args)
+    elif args.workload == "backward":
+        res = bench_backward(args)
+    elif args.workload == "copy":
+        res = bench_copy(args)
     else:
         raise SystemExit(f"workload {args.workload} is not available yet")
     print(json.dumps(res), flush=True)

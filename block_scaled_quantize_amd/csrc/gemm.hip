@@ -17,7 +17,10 @@
 //    (columns = m), so each lane ends with 4 consecutive n of one output row: 8-byte bf16 stores.
 //  * Global -> LDS by buffer_load ... lds (no VGPR staging), 3 LDS stages so loads run two K
 //    blocks ahead; bounds come from the buffer descriptors (rows past the matrix read as zero).
-//  * LDS tiles are rows of 128 bytes with a 16-byte-chunk XOR swizzle (chunk ^ (row & 7)).
+//  * LDS tiles are rows of 128 bytes with a 16-byte-chunk XOR swizzle chosen so that the lanes
+//    the 64-bank LDS serves together hit distinct banks: ds_read_b128 serves 16 lanes (16
+//    consecutive rows of a K-major tile) per pass, ds_read_b64_tr_b8 32 lanes (rows k0+j and
+//    k0+32+j, j < 8, of an MN-major tile).
 //    K-major operands (rows = m or n) are read with ds_read_b128; MN-major operands (rows = k,
 //    dgrad / wgrad) are read with ds_read_b64_tr_b8, which transposes 8x8 byte blocks across
 //    lanes, so no separate transpose pass is needed.
@@ -137,6 +140,15 @@ __device__ __forceinline__ void barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Physical 16-byte chunk of logical chunk c in tile row r.  K-major tiles: rows of the same
+// parity share a 128-byte bank half, so the chunk is permuted by r / 2.  MN-major tiles: the two
+// 8-row bands 32 rows apart that one transpose read serves together use the two halves of the
+// chunk space.
+__device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz_mn(int k) { return ((k >> 1) & 3) | (((k >> 5) & 1) << 2); }
+template <bool KMAJOR>
+__device__ __forceinline__ int swz(int r) { return KMAJOR ? swz_k(r) : swz_mn(r); }
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>(p);
 }
@@ -144,7 +156,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // K-major tile fragment: 32 bytes k = 32g .. 32g+31 of tile row r.
 __device__ __forceinline__ v8i frag_kmajor(const uint8_t* tile, int r, int g) {
   const uint8_t* row = tile + r * 128;
-  const int sw = r & 7;
+  const int sw = swz_k(r);
   uint4 lo = *reinterpret_cast<const uint4*>(row + (((2 * g) ^ sw) << 4));
   uint4 hi = *reinterpret_cast<const uint4*>(row + (((2 * g + 1) ^ sw) << 4));
   v8i v;
@@ -163,7 +175,7 @@ __device__ __forceinline__ v8i frag_mnmajor(const uint8_t* tile, int col0, int l
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int k = 32 * g + 8 * t + (li >> 1);
-    const uint8_t* p = half + k * 128 + ((chunk ^ (k & 7)) << 4) + 8 * (li & 1);
+    const uint8_t* p = half + k * 128 + ((chunk ^ swz_mn(k)) << 4) + 8 * (li & 1);
     v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)p);
     v[2 * t] = r.x;
     v[2 * t + 1] = r.y;
@@ -181,16 +193,19 @@ __device__ __forceinline__ v8i fragment(const uint8_t* tile, int idx, int li, in
 // (m or n), the K block starts at the descriptor base.  MN-major: rows of the tile are k, the
 // 128-column halves sit at +128 * h.  Instruction q of the tile covers LDS bytes
 // [1024 q, 1024 q + 1024) = 8 rows of 128 bytes; lane i fills row 8q' + i / 8 at physical
-// chunk i % 8, whose logical chunk is (i % 8) ^ (i / 8).
+// chunk i % 8, which holds logical chunk (i % 8) ^ swz(row).
 template <bool KMAJOR>
 __device__ __forceinline__ uint32_t dma_voffset(int q, int lane, int64_t ld) {
   const int rl = lane >> 3;
-  const int c = (lane & 7) ^ rl;
   if constexpr (KMAJOR) {
-    return (uint32_t)((int64_t)(8 * q + rl) * ld + 16 * c);
+    const int row = 8 * q + rl;
+    const int c = (lane & 7) ^ swz_k(row);
+    return (uint32_t)((int64_t)row * ld + 16 * c);
   } else {
     const int h = q >> 4, qq = q & 15;
-    return (uint32_t)((int64_t)(8 * qq + rl) * ld + 128 * h + 16 * c);
+    const int row = 8 * qq + rl;
+    const int c = (lane & 7) ^ swz_mn(row);
+    return (uint32_t)((int64_t)row * ld + 128 * h + 16 * c);
   }
 }
 
@@ -199,7 +214,7 @@ template <int ROWS, int THREADS>
 __device__ __forceinline__ void zero_k_tail(uint8_t* tile, int krem) {
   for (int id = threadIdx.x; id < ROWS * 8; id += THREADS) {
     const int r = id >> 3, c = id & 7;
-    uint8_t* p = tile + r * 128 + ((c ^ (r & 7)) << 4);
+    uint8_t* p = tile + r * 128 + ((c ^ swz_k(r)) << 4);
     if (16 * c >= krem) {
       *reinterpret_cast<uint4*>(p) = make_uint4(0, 0, 0, 0);
     } else if (16 * c + 16 > krem) {
@@ -322,68 +337,97 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int s = 0; s < C::kStages - 1; ++s)
-    if (s < nkb) issue(s);
-  for (int kb = 0; kb < nkb; ++kb) {
-    // Stage kb must have landed; the loads of later stages may still be in flight.
+  // Pipeline.  Stages hold K blocks kb .. kb + kStages - 1.
+  auto wait_next = [&](int next) {
+    // stage `next` must be complete; stage next + 1 may still be in flight (3 stages)
     if constexpr (C::kStages == 3) {
-      if (kb + 1 < nkb) wait_vm_upto<kPerStage>(per_stage);
+      if (next + 1 < nkb) wait_vm_upto<kPerStage>(per_stage);
       else wait_vm<0>();
     } else {
       wait_vm<0>();
     }
-    barrier();
-    if (kb + C::kStages - 1 < nkb) issue(kb + C::kStages - 1);
-    uint8_t* st = smem + (kb % C::kStages) * C::kStage;
-    const uint8_t* xt = st;
-    const uint8_t* wt = st + C::kXBytes;
-    const float* sat = reinterpret_cast<const float*>(st + C::kXBytes + C::kWBytes);
+  };
+  auto stage_ptr = [&](int kb) { return smem + (kb % C::kStages) * C::kStage; };
+  auto prepare = [&](int kb) {
+    // ragged K: the last block's bytes past K are zeroed before anyone reads them
     if (kb == nkb - 1 && krem < 128 && (XK || WK)) {
+      uint8_t* st = stage_ptr(kb);
       if constexpr (XK) zero_k_tail<BM, C::kThreads>(st, krem);
       if constexpr (WK) zero_k_tail<BN, C::kThreads>(st + C::kXBytes, krem);
       __syncthreads();
     }
-    v8i wf[NI];
+  };
+  // One K block: MFMAs of m piece j are issued while piece j-1 is folded.  The fragments of the
+  // first piece (xf, c0) and the weight fragments wf are loaded by the caller.
+  auto mma_block = [&](const uint8_t* st, v8i (&wf)[NI], v8i xf, float c0, float sbv,
+                       v4f (&P)[NI], float& cprev) {
+    const float* sat = reinterpret_cast<const float*>(st + C::kXBytes + C::kWBytes);
+    float ccur = c0;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) wf[i] = fragment<WK>(wt, wn * C::kWTN + 16 * i + li, li, g);
-    if constexpr (FOLD) {
-      // Software pipeline over the m pieces: the MFMAs of piece j are issued while the partial
-      // sums of piece j-1 are folded into the accumulators.
-      const float sbv = sat[BM + (wn * C::kWTN) / 128];
-      v4f P[2][NI];
-      float cprev = 0.0f;
-      v8i xf = fragment<XK>(xt, wm * C::kWTM + li, li, g);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int mrow = wm * C::kWTM + 16 * j + li;
-        v8i xnext;
-        if (j + 1 < NJ) xnext = fragment<XK>(xt, mrow + 16, li, g);
-        const float c = sat[mrow] * sbv;
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-          P[j & 1][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              wf[i], xf, v4f{0.f, 0.f, 0.f, 0.f}, FB, FA, 0, 0, 0, 0);
-        if (j > 0) {
-#pragma unroll
-          for (int i = 0; i < NI; ++i) acc[i][j - 1] += P[(j - 1) & 1][i] * cprev;
-        }
-        cprev = c;
-        if (j + 1 < NJ) xf = xnext;
+    for (int j = 0; j < NJ; ++j) {
+      const int mrow = wm * C::kWTM + 16 * j + li;
+      v8i xnext;
+      float cnext = 0.0f;
+      if (j + 1 < NJ) {
+        xnext = fragment<XK>(st, mrow + 16, li, g);
+        if constexpr (FOLD) cnext = sat[mrow + 16] * sbv;
       }
 #pragma unroll
-      for (int i = 0; i < NI; ++i) acc[i][NJ - 1] += P[(NJ - 1) & 1][i] * cprev;
-    } else {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const v8i xf = fragment<XK>(xt, wm * C::kWTM + 16 * j + li, li, g);
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
+      for (int i = 0; i < NI; ++i) {
+        if constexpr (FOLD) {
+          const v4f pn = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              wf[i], xf, v4f{0.f, 0.f, 0.f, 0.f}, FB, FA, 0, 0, 0, 0);
+          if (j > 0) acc[i][j - 1] += P[i] * cprev;   // piece j-1, issued one round earlier
+          P[i] = pn;
+        } else {
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[i], xf, acc[i][j], FB,
                                                                        FA, 0, 0, 0, 0);
+        }
+      }
+      cprev = ccur;
+      if (j + 1 < NJ) {
+        xf = xnext;
+        ccur = cnext;
       }
     }
-    // A stage is refilled kStages-1 iterations after it was read; the barrier at the top of
-    // the next iteration orders every wave's reads before that refill is issued.
+  };
+  auto load_w = [&](const uint8_t* st, v8i (&wf)[NI]) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) wf[i] = fragment<WK>(st + C::kXBytes, wn * C::kWTN + 16 * i + li, li, g);
+  };
+  auto first_piece = [&](const uint8_t* st, v8i& xf, float& c0, float& sbv) {
+    const float* sat = reinterpret_cast<const float*>(st + C::kXBytes + C::kWBytes);
+    xf = fragment<XK>(st, wm * C::kWTM + li, li, g);
+    if constexpr (FOLD) {
+      sbv = sat[BM + (wn * C::kWTN) / 128];
+      c0 = sat[wm * C::kWTM + li] * sbv;
+    }
+  };
+
+  for (int s = 0; s < C::kStages - 1; ++s)
+    if (s < nkb) issue(s);
+
+  // The barrier at the top of iteration kb publishes stage kb (every wave has waited for its
+  // own DMA of it) and proves that every wave has finished reading stage kb - 1, whose slot
+  // then receives block kb + kStages - 1.
+  for (int kb = 0; kb < nkb; ++kb) {
+    wait_next(kb);
+    barrier();
+    if (kb + C::kStages - 1 < nkb) issue(kb + C::kStages - 1);
+    prepare(kb);
+    const uint8_t* st = stage_ptr(kb);
+    v8i wf[NI], xf;
+    float c0 = 0.0f, sbv = 1.0f;
+    load_w(st, wf);
+    first_piece(st, xf, c0, sbv);
+    v4f P[NI];
+    float cprev = 0.0f;
+    mma_block(st, wf, xf, c0, sbv, P, cprev);
+    if constexpr (FOLD) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) acc[i][NJ - 1] += P[i] * cprev;
+    }
+    // (the next iteration's barrier orders every wave's reads of this stage before its refill)
   }
 
   float post = 1.0f;

@@ -34,8 +34,10 @@ __device__ __forceinline__ void load16(const uint16_t* __restrict__ x, int64_t r
   }
   const uint16_t* p = x + r * ld + c0;
   if (VEC && c0 + 16 <= cols) {
-    uint4 a = *reinterpret_cast<const uint4*>(p);
-    uint4 b = *reinterpret_cast<const uint4*>(p + 8);
+    // read-once stream: non-temporal loads keep it from evicting useful cache lines
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    const v4u a = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+    const v4u b = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p + 8));
     d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w;
     d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
     return;
@@ -74,7 +76,8 @@ __device__ __forceinline__ uint4 encode_block_values(const uint32_t (&d)[8], flo
 // ---------------------------------------------------------------- 1x128 blocks
 // Workgroup tile: kRows1 rows x one 128-column block.  8 lanes share a row block (16 elements
 // each); each thread handles kRowsPerThread row blocks kRows1/kRowsPerThread rows apart.
-// Scales go to scale_inv[colblock][row]: the tile's kRows1 scales are contiguous.
+// Scales go to scale_inv[colblock][row]: the tile's kRows1 scales are contiguous.  The 1-D
+// grid runs column blocks fastest, so workgroups in flight together stream contiguous rows.
 constexpr int kRowsPerThread = 2;
 constexpr int kRows1 = (kThreads / 8) * kRowsPerThread;  // 64
 
@@ -83,9 +86,10 @@ __global__ __launch_bounds__(kThreads) void quant_1x128_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale_inv) {
   const int t = threadIdx.x;
-  const int64_t cb = blockIdx.y;
+  const int64_t nbc = (cols + 127) >> 7;
+  const int64_t cb = blockIdx.x % nbc;
   const int64_t c0 = cb * 128 + (t & 7) * 16;
-  const int64_t r0 = (int64_t)blockIdx.x * kRows1 + (t >> 3);
+  const int64_t r0 = (int64_t)(blockIdx.x / nbc) * kRows1 + (t >> 3);
   uint32_t d[kRowsPerThread][8];
 #pragma unroll
   for (int j = 0; j < kRowsPerThread; ++j)
@@ -110,7 +114,8 @@ __global__ __launch_bounds__(kThreads) void quant_128x128_kernel(
     uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale_inv) {
   __shared__ uint32_t wave_amax[kThreads / 64];
   const int t = threadIdx.x;
-  const int64_t tr = blockIdx.x, tc = blockIdx.y;
+  const int64_t nbc = (cols + 127) >> 7;
+  const int64_t tr = blockIdx.x / nbc, tc = blockIdx.x % nbc;
   const int64_t c0 = tc * 128 + (t & 7) * 16;
   const int64_t rbase = tr * 128 + (t >> 3);
   uint32_t d[4][8];
@@ -133,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void quant_128x128_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     store16<VEC>(q, rows, cols, ld_q, rbase + 32 * i, c0, encode_block_values<FMT>(d[i], s, finite));
-  if (t == 0) scale_inv[tr * gridDim.y + tc] = 1.0f / s;
+  if (t == 0) scale_inv[tr * nbc + tc] = 1.0f / s;
 }
 
 // ---------------------------------------------------------------- delayed per-tensor
@@ -257,11 +262,11 @@ template <int FMT, bool POW2, bool VEC>
 int launch_blockwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int gran,
                      uint8_t* q, int64_t ld_q, float* s, hipStream_t st) {
   if (gran == FP8BS_BLOCK_1x128) {
-    dim3 grid((unsigned)ceil_div(rows, kRows1), (unsigned)ceil_div(cols, 128));
+    dim3 grid((unsigned)(ceil_div(rows, kRows1) * ceil_div(cols, 128)));
     return launch(quant_1x128_kernel<FMT, POW2, VEC>, grid, dim3(kThreads), st, x, rows, cols,
                   ld_x, q, ld_q, s);
   }
-  dim3 grid((unsigned)ceil_div(rows, 128), (unsigned)ceil_div(cols, 128));
+  dim3 grid((unsigned)(ceil_div(rows, 128) * ceil_div(cols, 128)));
   return launch(quant_128x128_kernel<FMT, POW2, VEC>, grid, dim3(kThreads), st, x, rows, cols,
                 ld_x, q, ld_q, s);
 }
@@ -292,7 +297,7 @@ extern "C" int fp8_quantize_blockwise(const void* x_bf16, int64_t rows, int64_t 
   if (rows == 0 || cols == 0) return FP8BS_OK;
   if (!x_bf16 || !q_out || !scale_inv_out) return FP8BS_ERR_NULL;
   const int64_t nb_rows = gran == FP8BS_BLOCK_1x128 ? ceil_div(rows, kRows1) : ceil_div(rows, 128);
-  if (nb_rows > 0x7FFFFFFF || ceil_div(cols, 128) > 65535) return FP8BS_ERR_SHAPE;
+  if (nb_rows * ceil_div(cols, 128) > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
   if (rows > INT64_MAX / ld_x) return FP8BS_ERR_SHAPE;
   if (!aligned4(scale_inv_out)) return FP8BS_ERR_ALIGN;
   const bool vec = aligned16(x_bf16) && aligned16(q_out) && ld_x % 8 == 0 && ld_q % 16 == 0;
