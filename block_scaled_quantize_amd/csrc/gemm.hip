@@ -375,10 +375,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         if constexpr (FOLD) {
+          // Unit i: the MFMA of (piece j, n piece i) and the fold of (piece j-1, n piece i),
+          // whose MFMA was issued NI MFMAs earlier and has completed.  The scheduling barrier
+          // keeps the compiler from pulling the fold of an MFMA right behind that MFMA (which
+          // would stall the wave on every MFMA result).
           const v4f pn = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               wf[i], xf, v4f{0.f, 0.f, 0.f, 0.f}, FB, FA, 0, 0, 0, 0);
-          if (j > 0) acc[i][j - 1] += P[i] * cprev;   // piece j-1, issued one round earlier
+          if (j > 0) acc[i][j - 1] += P[i] * cprev;
           P[i] = pn;
+          __builtin_amdgcn_sched_barrier(0);
         } else {
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[i], xf, acc[i][j], FB,
                                                                        FA, 0, 0, 0, 0);
@@ -631,6 +636,25 @@ bool scale_index(int gran, bool kmajor, bool weight_side, int64_t rows, int64_t 
   return false;
 }
 
+// Grouped GEMM tile choice (FP8BS_GROUPED_VARIANT = B, C or D overrides, for tuning).
+char pick_grouped_variant() {
+  const char* e = getenv("FP8BS_GROUPED_VARIANT");
+  if (e && (e[0] == 'B' || e[0] == 'C' || e[0] == 'D')) return e[0];
+  return 'C';   // fastest on the MoE shapes despite 10% padding in ragged 256-row tiles
+}
+
+template <class C>
+int launch_grouped(int fa, int fb, int cus, GemmParams p, hipStream_t st) {
+  p.tiles_n = (int)ceil_div(p.N, C::BN);
+  p.tiles_m = (int)(ceil_div(p.M, C::BM) + p.num_groups);   // upper bound on m tiles
+  if ((int64_t)p.tiles_m * p.tiles_n > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
+  const int blocks = (int)std::min<int64_t>((int64_t)p.tiles_m * p.tiles_n, std::max(cus, 1));
+  if (fa == FP8BS_E4M3 && fb == FP8BS_E4M3) return launch_gemm(grouped_gemm_kernel<C, FP8BS_E4M3, FP8BS_E4M3>, blocks, C::kThreads, C::kLds, st, p);
+  if (fa == FP8BS_E5M2 && fb == FP8BS_E4M3) return launch_gemm(grouped_gemm_kernel<C, FP8BS_E5M2, FP8BS_E4M3>, blocks, C::kThreads, C::kLds, st, p);
+  if (fa == FP8BS_E4M3 && fb == FP8BS_E5M2) return launch_gemm(grouped_gemm_kernel<C, FP8BS_E4M3, FP8BS_E5M2>, blocks, C::kThreads, C::kLds, st, p);
+  return launch_gemm(grouped_gemm_kernel<C, FP8BS_E5M2, FP8BS_E5M2>, blocks, C::kThreads, C::kLds, st, p);
+}
+
 }  // namespace
 }  // namespace fp8bs
 
@@ -692,7 +716,6 @@ extern "C" int fp8_grouped_gemm(int32_t num_groups, const int64_t* group_offsets
   if (!aligned16(A) || !aligned16(B) || lda % 16 || ldb % 16) return FP8BS_ERR_ALIGN;
   if (!aligned4(C_bf16) || ldc % 2 || (reinterpret_cast<uintptr_t>(group_offsets) & 7))
     return FP8BS_ERR_ALIGN;
-  using C = CfgD;
   GemmParams p{};
   p.M = total_M; p.N = N; p.K = K;
   p.A = static_cast<const uint8_t*>(A); p.lda = lda;
@@ -702,21 +725,18 @@ extern "C" int fp8_grouped_gemm(int32_t num_groups, const int64_t* group_offsets
   p.sb = scale_inv_b; p.sb_ks = 1; p.sb_rs = ceil_div(K, 128);
   p.C = static_cast<uint16_t*>(C_bf16); p.ldc = ldc;
   p.c_vec = (reinterpret_cast<uintptr_t>(C_bf16) % 8 == 0) && (ldc % 4 == 0);
-  p.tiles_n = (int)ceil_div(N, C::BN);
-  p.tiles_m = (int)(ceil_div(total_M, C::BM) + num_groups);   // upper bound on m tiles
   p.offsets = group_offsets;
   p.num_groups = num_groups;
   p.b_group_stride = N * ldb;
   p.sb_group_stride = ceil_div(N, 128) * ceil_div(K, 128);
-  if ((int64_t)p.tiles_m * p.tiles_n > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
-  const int blocks = (int)std::min<int64_t>((int64_t)p.tiles_m * p.tiles_n, std::max(cus, 1));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (fa == FP8BS_E4M3 && fb == FP8BS_E4M3) return launch_gemm(grouped_gemm_kernel<C, FP8BS_E4M3, FP8BS_E4M3>, blocks, C::kThreads, C::kLds, st, p);
-  if (fa == FP8BS_E5M2 && fb == FP8BS_E4M3) return launch_gemm(grouped_gemm_kernel<C, FP8BS_E5M2, FP8BS_E4M3>, blocks, C::kThreads, C::kLds, st, p);
-  if (fa == FP8BS_E4M3 && fb == FP8BS_E5M2) return launch_gemm(grouped_gemm_kernel<C, FP8BS_E4M3, FP8BS_E5M2>, blocks, C::kThreads, C::kLds, st, p);
-  return launch_gemm(grouped_gemm_kernel<C, FP8BS_E5M2, FP8BS_E5M2>, blocks, C::kThreads, C::kLds, st, p);
+  switch (pick_grouped_variant()) {
+    case 'C': return launch_grouped<CfgC>(fa, fb, cus, p, st);
+    case 'D': return launch_grouped<CfgD>(fa, fb, cus, p, st);
+    default: return launch_grouped<CfgB>(fa, fb, cus, p, st);
+  }
 }

@@ -34,10 +34,8 @@ __device__ __forceinline__ void load16(const uint16_t* __restrict__ x, int64_t r
   }
   const uint16_t* p = x + r * ld + c0;
   if (VEC && c0 + 16 <= cols) {
-    // read-once stream: non-temporal loads keep it from evicting useful cache lines
-    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-    const v4u a = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
-    const v4u b = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p + 8));
+    const uint4 a = *reinterpret_cast<const uint4*>(p);
+    const uint4 b = *reinterpret_cast<const uint4*>(p + 8);
     d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w;
     d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
     return;

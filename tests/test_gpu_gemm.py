@@ -236,3 +236,10 @@ def test_every_tile_variant(gpu, monkeypatch, variant, layout, fa, ga, fb, gb):
     monkeypatch.setenv("FP8BS_GEMM_VARIANT", variant)
     run_gemm(gpu, layout, 520, 390, 392, fa, ga, fb, gb)
     run_gemm(gpu, layout, 256, 256, 256, fa, ga, fb, gb)
+
+
+@pytest.mark.parametrize("variant", ["B", "C", "D"])
+def test_grouped_every_tile_variant(gpu, monkeypatch, variant):
+    """Each tile configuration the grouped kernel can use (FP8BS_GROUPED_VARIANT forces one)."""
+    monkeypatch.setenv("FP8BS_GROUPED_VARIANT", variant)
+    run_grouped(gpu, [5, 0, 300, 1, 0, 257, 128, 513], 384, 400)
