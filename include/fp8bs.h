@@ -167,6 +167,7 @@ int fp8_gemm_blockscaled(int layout, int64_t M, int64_t N, int64_t K,
  * mundo real": the FP8 recipe applied to an MoE model's expert layers.
  * Rows [group_offsets[g], group_offsets[g+1]) of A (tokens sorted by expert) are multiplied
  * by expert g's weight: C[r, :] = A[r, :] . B[g]^T for those rows.
+ *   num_groups:    0 .. 1024 (FP8BS_ERR_ARG beyond).
  *   group_offsets: DEVICE int64[num_groups + 1], non-decreasing, offsets[0] = 0,
  *                  offsets[num_groups] = total_M (empty groups allowed).  Offsets that break
  *                  these rules make the kernel skip the offending rows; they never cause an
