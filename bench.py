@@ -10,9 +10,11 @@ HBM before timing: activations N(0,1) with 1% of the channels scaled by 50, weig
 value = sum of the GEMMs' 2*M*N*K over the step / step time (TFLOP/s, quantization included).
 roofline: the dominant kernel (the block-scaled GEMM) -- algorithmic flops per launch (mean
 over the four shapes) / mean launch duration measured with HIP events on the launch stream,
-against the MI355X dense FP8 MFMA peak.
-cpu_baseline: the CPU oracle (C quantizer + NumPy fp64 GEMM) on a bounded row sample of the
-same step, on the host's cores.
+against the MI355X dense FP8 MFMA peak.  traffic: HBM bytes per launch (mean over the four
+shapes) from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, calibrated on a plain copy;
+null when the GEMM sources differ from the ones the counters were taken on.
+cpu_baseline: the CPU oracle (C quantizer + NumPy fp64 GEMM) on the same step (all rows of all
+four layers), on the host's cores.
 
 Other workloads (--workload): quant-sweep (HBM-bound quantizer), moe (grouped GEMM),
 backward (delayed-scaled dgrad / wgrad), copy (counter calibration).  Each prints one JSON line.
@@ -33,6 +35,8 @@ import torch  # noqa: E402
 
 FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
+GEMM_COUNTERS = os.path.join(ROOT, "profiles", "gemm_kernel_llama8b_fprop_counters.txt")
+GEMM_SOURCES = [os.path.join(ROOT, "block_scaled_quantize_amd", "csrc", f) for f in ("gemm.hip", "common.h")]
 
 LAYERS_8B = [("qkv", 4096, 6144), ("o", 4096, 4096), ("gate_up", 4096, 28672), ("down", 14336, 4096)]
 
@@ -74,6 +78,32 @@ class EventTimer:
 
     def total_ms(self, key) -> float:
         return float(sum(s.elapsed_time(e) for s, e in self.pairs.get(key, [])))
+
+
+def measured_traffic(counter_file: str, sources) -> dict:
+    """HBM bytes per launch from a committed counter summary (key = value lines), if it was
+    taken on the current kernel sources (sha256 over the source files), else None."""
+    import hashlib
+    out = dict(bytes=None, algorithmic=None, source="none")
+    try:
+        kv = {}
+        for line in open(counter_file):
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+        h = hashlib.sha256()
+        for p in sources:
+            with open(p, "rb") as f:
+                h.update(f.read())
+    except OSError:
+        return out
+    out["algorithmic"] = float(kv["mean_algorithmic_bytes_per_launch"])
+    if kv.get("source_sha256") == h.hexdigest():
+        out["bytes"] = float(kv["mean_hbm_bytes_per_launch"])
+        out["source"] = os.path.relpath(counter_file, ROOT)
+    else:
+        out["source"] = "stale: kernel sources changed since the counters were taken"
+    return out
 
 
 def cpu_cores() -> int:
@@ -161,6 +191,7 @@ def bench_llama8b(args):
     mean_launch_flops = float(np.mean(gemm_flops))
     mean_launch_ms = float(np.mean(gemm_ms))
     achieved = mean_launch_flops / mean_launch_ms / 1e9
+    traffic = measured_traffic(GEMM_COUNTERS, GEMM_SOURCES)
     result = dict(
         metric="block-scaled FP8 GEMM TFLOP/s (+quantize GB/s), % of MI355X FP8/HBM peak",
         value=round(flops / dt / 1e12, 2), unit="TFLOP/s", n_gpus=1, steps=args.steps,
@@ -172,8 +203,11 @@ def bench_llama8b(args):
                     act_scales="1x128 E4M3", weight_scales="128x128 E4M3 (re-quantized every step)",
                     parallelism="single GPU"),
         roofline=dict(bound="mfma", achieved=round(achieved, 1), peak=FP8_PEAK_TFLOPS,
-                      unit="TFLOP/s", frac=round(achieved / FP8_PEAK_TFLOPS, 4), traffic=None,
-                      kernel="gemm_kernel<FPROP,E4M3,E4M3,fold,BM=256>",
+                      unit="TFLOP/s", frac=round(achieved / FP8_PEAK_TFLOPS, 4),
+                      traffic=traffic["bytes"], traffic_unit="HBM bytes per launch",
+                      traffic_algorithmic=traffic["algorithmic"], traffic_source=traffic["source"],
+                      # the tile chooser takes the 256x256 tile for all four shapes
+                      kernel="gemm_kernel<Cfg<256,256,2,4>,FPROP,E4M3,E4M3,fold>",
                       per_launch_flops=mean_launch_flops, mean_launch_us=round(mean_launch_ms * 1e3, 2)),
         gemm_only_tflops=round(sum(gemm_flops) / sum(gemm_ms) / 1e9, 1),
         quant_gbps=round(q_bytes / q_ms / 1e6, 1),
@@ -185,26 +219,41 @@ def bench_llama8b(args):
     return result
 
 
-def cpu_baseline_8b(layers, M, rows: int = 1024):
-    """The oracle on a row sample of the same step: quantize `rows` activation rows (1x128),
-    the full weight (128x128), dequantize and multiply in fp64.  Scaled to TFLOP/s of the
-    sample's GEMM flops."""
+def cpu_baseline_8b(layers, M, rows: int | None = None, min_seconds: float = 10.0):
+    """The oracle on the same step (by default all M rows; `rows` bounds the sample): quantize
+    the activation rows (1x128) and the full weight (128x128), dequantize and multiply in fp64;
+    the step is repeated until min_seconds have passed.  TFLOP/s of the GEMM flops done."""
     import oracle
     oracle.build()
+    rows = M if rows is None else min(rows, M)
+    host = [(L["x"][:rows].cpu().contiguous().view(torch.int16).numpy().view(np.uint16),
+             L["w"].cpu().contiguous().view(torch.int16).numpy().view(np.uint16), L) for L in layers]
     t0 = time.perf_counter()
-    flops = 0.0
-    for L in layers:
-        xs = L["x"][:rows].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
-        ws = L["w"].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
-        qx, sx = oracle.quantize_blockwise(xs, oracle.E4M3, oracle.BLOCK_1x128, oracle.SCALE_FP32)
-        qw, sw = oracle.quantize_blockwise(ws, oracle.E4M3, oracle.BLOCK_128x128, oracle.SCALE_FP32)
-        oracle.gemm(oracle.FPROP, qx, oracle.E4M3, oracle.BLOCK_1x128, sx, qw, oracle.E4M3,
-                    oracle.BLOCK_128x128, sw)
-        flops += 2.0 * rows * L["N"] * L["K"]
+    flops, reps = 0.0, 0
+    while reps == 0 or time.perf_counter() - t0 < min_seconds:
+        for xs, ws, L in host:
+            qx, sx = oracle.quantize_blockwise(xs, oracle.E4M3, oracle.BLOCK_1x128, oracle.SCALE_FP32)
+            qw, sw = oracle.quantize_blockwise(ws, oracle.E4M3, oracle.BLOCK_128x128, oracle.SCALE_FP32)
+            oracle.gemm(oracle.FPROP, qx, oracle.E4M3, oracle.BLOCK_1x128, sx, qw, oracle.E4M3,
+                        oracle.BLOCK_128x128, sw)
+            flops += 2.0 * rows * L["N"] * L["K"]
+        reps += 1
     dt = time.perf_counter() - t0
-    return dict(value=round(flops / dt / 1e12, 5), unit="TFLOP/s", cores=cpu_cores(), kind="oracle",
+    blas = blas_threads()
+    return dict(value=round(flops / dt / 1e12, 5), unit="TFLOP/s", cores=max(cpu_cores(), blas),
+                kind="oracle",
                 sample=f"{rows} of {M} token rows per layer (all four layers, full weights "
-                       f"re-quantized), {dt:.1f} s")
+                       f"re-quantized) x {reps} repetitions, {dt:.1f} s; C oracle threads "
+                       f"{cpu_cores()}, BLAS threads {blas}")
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:  # pragma: no cover - optional dependency
+        return 1
 
 
 # ----------------------------------------------------------------------------- quantizer sweep
@@ -345,7 +394,7 @@ def bench_moe(args):
                             routing="Zipf(1.1)", rows=T),
                 roofline=dict(bound=gu["bound"], achieved=gu["tflops"], peak=FP8_PEAK_TFLOPS,
                               unit="TFLOP/s", frac=round(gu["tflops"] / FP8_PEAK_TFLOPS, 4),
-                              traffic=None, kernel="grouped_gemm_kernel<128x128>"),
+                              traffic=None, kernel="grouped_gemm_kernel<Cfg<256,256,2,4>,E4M3,E4M3>"),
                 layers=out)
 
 
