@@ -16,8 +16,10 @@ null when the GEMM sources differ from the ones the counters were taken on.
 cpu_baseline: the CPU oracle (C quantizer + NumPy fp64 GEMM) on the same step (all rows of all
 four layers), on the host's cores.
 
-Other workloads (--workload): quant-sweep (HBM-bound quantizer), moe (grouped GEMM),
-backward (delayed-scaled dgrad / wgrad), copy (counter calibration).  Each prints one JSON line.
+Other workloads (--workload): llama8b-fprop-pow2 (the same step with power-of-2 scales, the
+GEMM applying them as E8M0 block scales in the MFMA), quant-sweep (HBM-bound quantizer), moe
+(grouped GEMM; --pow2 for power-of-2 scales), backward (delayed-scaled dgrad / wgrad), copy
+(counter calibration).  Each prints one JSON line.
 """
 from __future__ import annotations
 
@@ -36,7 +38,9 @@ import torch  # noqa: E402
 FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 GEMM_COUNTERS = os.path.join(ROOT, "profiles", "gemm_kernel_llama8b_fprop_counters.txt")
-GEMM_SOURCES = [os.path.join(ROOT, "block_scaled_quantize_amd", "csrc", f) for f in ("gemm.hip", "common.h")]
+GEMM_COUNTERS_POW2 = os.path.join(ROOT, "profiles", "gemm_kernel_pow2_llama8b_fprop_counters.txt")
+GEMM_SOURCES = [os.path.join(ROOT, "block_scaled_quantize_amd", "csrc", f)
+                for f in ("gemm_impl.h", "gemm.hip", "common.h")]
 
 LAYERS_8B = [("qkv", 4096, 6144), ("o", 4096, 4096), ("gate_up", 4096, 28672), ("down", 14336, 4096)]
 
@@ -51,8 +55,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b-fprop",
-                    choices=["llama8b-fprop", "quant-sweep", "moe", "backward", "copy"])
+                    choices=["llama8b-fprop", "llama8b-fprop-pow2", "quant-sweep", "moe", "backward",
+                             "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pow2", action="store_true", help="moe: power-of-2 scales (E8M0 in the MFMA)")
     ap.add_argument("--tokens", type=int, default=8192)
     return ap.parse_args()
 
@@ -115,10 +121,12 @@ def cpu_cores() -> int:
 
 # ----------------------------------------------------------------------------- 8B fprop
 
-def bench_llama8b(args):
+def bench_llama8b(args, pow2: bool = False):
+    """pow2: power-of-2 block scales (SCALE_POW2 quantization, fp8_gemm_blockscaled_pow2)."""
     import block_scaled_quantize_amd as bsq
     import synth
     bsq.load()
+    mode = bsq.SCALE_POW2 if pow2 else bsq.SCALE_FP32
     M = args.tokens
     dev = torch.device("cuda", 0)
     layers = []
@@ -139,14 +147,16 @@ def bench_llama8b(args):
     def step(timer=None):
         for L in layers:
             def qx():
-                bsq.quantize_blockwise(L["x"], bsq.E4M3, bsq.BLOCK_1x128, q=L["qx"], scale_inv=L["sx"])
+                bsq.quantize_blockwise(L["x"], bsq.E4M3, bsq.BLOCK_1x128, mode, q=L["qx"],
+                                       scale_inv=L["sx"])
 
             def qw():
-                bsq.quantize_blockwise(L["w"], bsq.E4M3, bsq.BLOCK_128x128, q=L["qw"], scale_inv=L["sw"])
+                bsq.quantize_blockwise(L["w"], bsq.E4M3, bsq.BLOCK_128x128, mode, q=L["qw"],
+                                       scale_inv=L["sw"])
 
             def mm():
                 bsq.gemm_blockscaled(bsq.FPROP, L["qx"], bsq.E4M3, bsq.BLOCK_1x128, L["sx"], L["qw"],
-                                     bsq.E4M3, bsq.BLOCK_128x128, L["sw"], c=L["y"])
+                                     bsq.E4M3, bsq.BLOCK_128x128, L["sw"], c=L["y"], pow2=pow2)
             if timer is None:
                 qx(); qw(); mm()
             else:
@@ -191,23 +201,24 @@ def bench_llama8b(args):
     mean_launch_flops = float(np.mean(gemm_flops))
     mean_launch_ms = float(np.mean(gemm_ms))
     achieved = mean_launch_flops / mean_launch_ms / 1e9
-    traffic = measured_traffic(GEMM_COUNTERS, GEMM_SOURCES)
+    traffic = measured_traffic(GEMM_COUNTERS_POW2 if pow2 else GEMM_COUNTERS, GEMM_SOURCES)
+    scales = "power-of-2 (E8M0 in the MFMA)" if pow2 else "fp32"
     result = dict(
         metric="block-scaled FP8 GEMM TFLOP/s (+quantize GB/s), % of MI355X FP8/HBM peak",
         value=round(flops / dt / 1e12, 2), unit="TFLOP/s", n_gpus=1, steps=args.steps,
         warmup=args.warmup, ms_per_step=round(dt * 1e3, 4), higher_is_better=True,
         scaling="weak", vs_baseline=None, dtype="fp8e4m3 x fp8e4m3 -> fp32 acc -> bf16",
         data="synthetic",
-        config=dict(workload="llama3.1-8b-fprop-linear", tokens=M,
+        config=dict(workload="llama3.1-8b-fprop-linear" + ("-pow2" if pow2 else ""), tokens=M,
                     layers="qkv 4096->6144, o 4096->4096, gate_up 4096->28672, down 14336->4096",
                     act_scales="1x128 E4M3", weight_scales="128x128 E4M3 (re-quantized every step)",
-                    parallelism="single GPU"),
+                    scale_values=scales, parallelism="single GPU"),
         roofline=dict(bound="mfma", achieved=round(achieved, 1), peak=FP8_PEAK_TFLOPS,
                       unit="TFLOP/s", frac=round(achieved / FP8_PEAK_TFLOPS, 4),
                       traffic=traffic["bytes"], traffic_unit="HBM bytes per launch",
                       traffic_algorithmic=traffic["algorithmic"], traffic_source=traffic["source"],
                       # the tile chooser takes the 256x256 tile for all four shapes
-                      kernel="gemm_kernel<Cfg<256,256,2,4>,FPROP,E4M3,E4M3,fold>",
+                      kernel="gemm_kernel<Cfg<256,256,2,4>,FPROP,E4M3,E4M3,%s>" % ("hw" if pow2 else "fold"),
                       per_launch_flops=mean_launch_flops, mean_launch_us=round(mean_launch_ms * 1e3, 2)),
         gemm_only_tflops=round(sum(gemm_flops) / sum(gemm_ms) / 1e9, 1),
         quant_gbps=round(q_bytes / q_ms / 1e6, 1),
@@ -215,11 +226,11 @@ def bench_llama8b(args):
         layers=per_layer,
     )
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_8b(layers, M)
+        result["cpu_baseline"] = cpu_baseline_8b(layers, M, mode=mode)
     return result
 
 
-def cpu_baseline_8b(layers, M, rows: int | None = None, min_seconds: float = 10.0):
+def cpu_baseline_8b(layers, M, rows: int | None = None, min_seconds: float = 10.0, mode: int = 0):
     """The oracle on the same step (by default all M rows; `rows` bounds the sample): quantize
     the activation rows (1x128) and the full weight (128x128), dequantize and multiply in fp64;
     the step is repeated until min_seconds have passed.  TFLOP/s of the GEMM flops done."""
@@ -232,8 +243,8 @@ def cpu_baseline_8b(layers, M, rows: int | None = None, min_seconds: float = 10.
     flops, reps = 0.0, 0
     while reps == 0 or time.perf_counter() - t0 < min_seconds:
         for xs, ws, L in host:
-            qx, sx = oracle.quantize_blockwise(xs, oracle.E4M3, oracle.BLOCK_1x128, oracle.SCALE_FP32)
-            qw, sw = oracle.quantize_blockwise(ws, oracle.E4M3, oracle.BLOCK_128x128, oracle.SCALE_FP32)
+            qx, sx = oracle.quantize_blockwise(xs, oracle.E4M3, oracle.BLOCK_1x128, mode)
+            qw, sw = oracle.quantize_blockwise(ws, oracle.E4M3, oracle.BLOCK_128x128, mode)
             oracle.gemm(oracle.FPROP, qx, oracle.E4M3, oracle.BLOCK_1x128, sx, qw, oracle.E4M3,
                         oracle.BLOCK_128x128, sw)
             flops += 2.0 * rows * L["N"] * L["K"]
@@ -353,22 +364,23 @@ def bench_moe(args):
     total_flops, total_ms = 0.0, 0.0
     for name, K, N in (("gate_up", 2048, 1536), ("down", 768, 2048)):
         x = synth.normal((T, K), 1.0, 0, f"bench/moe/{name}/X").to(dev)
-        qx, sx = bsq.quantize_blockwise(x, bsq.E4M3, bsq.BLOCK_1x128)
+        mode = bsq.SCALE_POW2 if args.pow2 else bsq.SCALE_FP32
+        qx, sx = bsq.quantize_blockwise(x, bsq.E4M3, bsq.BLOCK_1x128, mode)
         del x
         qw = torch.empty((128, N, K), dtype=torch.uint8, device=dev)
         sw = torch.empty((128, N // 128, K // 128), dtype=torch.float32, device=dev)
         for e in range(128):
             w = synth.normal((N, K), 0.02, 0, f"bench/moe/{name}/W{e}").to(dev)
-            bsq.quantize_blockwise(w, bsq.E4M3, bsq.BLOCK_128x128, q=qw[e], scale_inv=sw[e])
+            bsq.quantize_blockwise(w, bsq.E4M3, bsq.BLOCK_128x128, mode, q=qw[e], scale_inv=sw[e])
         c = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
         for _ in range(args.warmup):
-            bsq.grouped_gemm(off, qx, sx, qw, sw, c=c)
+            bsq.grouped_gemm(off, qx, sx, qw, sw, c=c, pow2=args.pow2)
         torch.cuda.synchronize()
         iters = max(args.steps, 5)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
         for a, b in ev:
             a.record()
-            bsq.grouped_gemm(off, qx, sx, qw, sw, c=c)
+            bsq.grouped_gemm(off, qx, sx, qw, sw, c=c, pow2=args.pow2)
             b.record()
         torch.cuda.synchronize()
         ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
@@ -390,11 +402,14 @@ def bench_moe(args):
                 steps=max(args.steps, 5), warmup=args.warmup, ms_per_step=round(total_ms, 4),
                 higher_is_better=True, scaling="weak", vs_baseline=None,
                 dtype="fp8e4m3 x fp8e4m3 -> fp32 acc -> bf16", data="synthetic",
-                config=dict(workload="qwen3-30b-a3b-moe-experts", experts=128, tokens=16384, topk=8,
+                config=dict(workload="qwen3-30b-a3b-moe-experts" + ("-pow2" if args.pow2 else ""),
+                            experts=128, tokens=16384, topk=8,
                             routing="Zipf(1.1)", rows=T),
                 roofline=dict(bound=gu["bound"], achieved=gu["tflops"], peak=FP8_PEAK_TFLOPS,
                               unit="TFLOP/s", frac=round(gu["tflops"] / FP8_PEAK_TFLOPS, 4),
-                              traffic=None, kernel="grouped_gemm_kernel<Cfg<256,256,2,4>,E4M3,E4M3>"),
+                              traffic=None,
+                              kernel="grouped_gemm_kernel<Cfg<256,256,2,4>,E4M3,E4M3,%s>"
+                                     % ("hw" if args.pow2 else "fold")),
                 layers=out)
 
 
@@ -485,6 +500,8 @@ def main():
     torch.cuda.set_device(0)
     if args.workload == "llama8b-fprop":
         res = bench_llama8b(args)
+    elif args.workload == "llama8b-fprop-pow2":
+        res = bench_llama8b(args, pow2=True)
     elif args.workload == "quant-sweep":
         res = bench_quant_sweep(args)
     elif args.workload == "moe":

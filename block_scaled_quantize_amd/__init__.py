@@ -68,8 +68,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
                                          i32, vp, vp, i64, vp]
     lib.fp8_grouped_gemm.argtypes = [ctypes.c_int32, vp, i64, i64, i64, vp, i64, i32, vp, vp,
                                      i64, i32, vp, vp, i64, vp]
+    lib.fp8_gemm_blockscaled_pow2.argtypes = lib.fp8_gemm_blockscaled.argtypes
+    lib.fp8_grouped_gemm_pow2.argtypes = lib.fp8_grouped_gemm.argtypes
     for name in ("fp8_quantize_blockwise", "fp8_quantize_delayed", "fp8_cast_fp32",
-                 "fp8_gemm_blockscaled", "fp8_grouped_gemm"):
+                 "fp8_gemm_blockscaled", "fp8_grouped_gemm", "fp8_gemm_blockscaled_pow2",
+                 "fp8_grouped_gemm_pow2"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -179,9 +182,10 @@ def cast_fp32(x: torch.Tensor, fmt: int, q: torch.Tensor | None = None, stream=N
 
 def gemm_blockscaled(layout: int, a: torch.Tensor, fa: int, ga: int, sa: torch.Tensor,
                      b: torch.Tensor, fb: int, gb: int, sb: torch.Tensor,
-                     c: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                     c: torch.Tensor | None = None, stream=None, pow2: bool = False) -> torch.Tensor:
     """Block-scaled FP8 GEMM, bf16 output.  a, b are uint8 code matrices as stored:
-    FPROP a[M,K], b[N,K]; DGRAD a[M,K], b[K,N]; WGRAD a[K,M], b[K,N]."""
+    FPROP a[M,K], b[N,K]; DGRAD a[M,K], b[K,N]; WGRAD a[K,M], b[K,N].  pow2=True calls
+    fp8_gemm_blockscaled_pow2 (scales must be powers of two; applied by the MFMA)."""
     if a.dtype != torch.uint8 or b.dtype != torch.uint8 or a.dim() != 2 or b.dim() != 2:
         raise ValueError("a and b must be 2-D uint8 code matrices")
     if layout == FPROP:
@@ -200,24 +204,27 @@ def gemm_blockscaled(layout: int, a: torch.Tensor, fa: int, ga: int, sa: torch.T
         raise ValueError("unknown layout")
     if c is None:
         c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
-    _check(load().fp8_gemm_blockscaled(layout, M, N, K, _ptr(a), a.stride(0), fa, ga, _ptr(sa),
-                                       _ptr(b), b.stride(0), fb, gb, _ptr(sb), _ptr(c),
-                                       c.stride(0), _stream(stream)), "fp8_gemm_blockscaled")
+    name = "fp8_gemm_blockscaled_pow2" if pow2 else "fp8_gemm_blockscaled"
+    _check(getattr(load(), name)(layout, M, N, K, _ptr(a), a.stride(0), fa, ga, _ptr(sa),
+                                 _ptr(b), b.stride(0), fb, gb, _ptr(sb), _ptr(c),
+                                 c.stride(0), _stream(stream)), name)
     return c
 
 
 def grouped_gemm(offsets: torch.Tensor, a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor,
                  sb: torch.Tensor, fa: int = E4M3, fb: int = E4M3,
-                 c: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                 c: torch.Tensor | None = None, stream=None, pow2: bool = False) -> torch.Tensor:
     """Grouped FP8 GEMM: rows [offsets[g], offsets[g+1]) of a[total_M, K] times b[g][N, K]^T.
-    offsets is a device int64 tensor of num_groups + 1 entries."""
+    offsets is a device int64 tensor of num_groups + 1 entries.  pow2=True calls
+    fp8_grouped_gemm_pow2 (power-of-two scales applied by the MFMA)."""
     if offsets.dtype != torch.int64 or b.dim() != 3:
         raise ValueError("offsets must be int64 and b must be [G, N, K]")
     G, N, K = b.shape
     total_m = a.shape[0]
     if c is None:
         c = torch.empty((total_m, N), dtype=torch.bfloat16, device=a.device)
-    _check(load().fp8_grouped_gemm(G, _ptr(offsets), total_m, N, K, _ptr(a), a.stride(0), fa,
-                                   _ptr(sa), _ptr(b), b.stride(1), fb, _ptr(sb), _ptr(c),
-                                   c.stride(0), _stream(stream)), "fp8_grouped_gemm")
+    name = "fp8_grouped_gemm_pow2" if pow2 else "fp8_grouped_gemm"
+    _check(getattr(load(), name)(G, _ptr(offsets), total_m, N, K, _ptr(a), a.stride(0), fa,
+                                 _ptr(sa), _ptr(b), b.stride(1), fb, _ptr(sb), _ptr(c),
+                                 c.stride(0), _stream(stream)), name)
     return c

@@ -17,8 +17,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfp8bs.so")
-SOURCES = ["quantize.hip", "gemm.hip"]
-HEADERS = [os.path.join(CSRC, "common.h"), os.path.join(INCLUDE, "fp8bs.h")]
+SOURCES = ["quantize.hip", "gemm.hip", "gemm_pow2.hip"]
+HEADERS = [os.path.join(CSRC, "common.h"), os.path.join(CSRC, "gemm_impl.h"),
+           os.path.join(INCLUDE, "fp8bs.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -1,0 +1,797 @@
+// Block-scaled FP8 GEMM for gfx950 (CDNA4): device code and launch helpers shared by the dense
+// and grouped entry points (gemm.hip: fp32 scales; gemm_pow2.hip: power-of-2 scales applied by
+// the MFMA itself).
+//
+// Method: "NVIDIA NeMo RL logra una aceleración del 48% con entrenamiento de precisión FP8 de
+// extremo a extremo", section "El avance técnico": linear layers run FP8 math on 128x128 weight
+// tiles and 1x128 activation blocks, output BF16; section "Ganancias de rendimiento en el
+// mundo real": the same recipe on an MoE model's experts; section "Por qué esto es importante
+// para la economía de la IA": power-of-2 scale factors.  Gradients may be E5M2 ("Infraestructura
+// de Entrenamiento FP8 ...", section "El panorama de la precisión numérica").
+//
+// Design
+//  * Output tile BM x BN per workgroup (256x256 with 8 waves, 256x128 with 8 or 4 waves, 128x128
+//    with 4 waves), 128-byte K blocks, so one K block is exactly one scale block.  Each wave owns
+//    a (BM / waves_m) x (BN / waves_n) sub-tile made of 16x16 pieces.
+//  * One V_MFMA_F32_16X16X128_F8F6F4 consumes a full 128-wide K block.  Three ways to apply the
+//    scales: fp32 block scales -- the MFMA result P is the partial sum of one scale block, folded
+//    as acc += P * (sa[m, kb] * sb[n-block, kb]); per-tensor scales on both operands -- the MFMA
+//    accumulates directly and the product of the two scales is applied once in the epilogue;
+//    power-of-2 block scales -- their exponents go to the MFMA's own E8M0 scale operands (one
+//    per lane: the lane's row and 32-wide k chunk) and the MFMA accumulates directly.
+//  * The MFMA's "A" operand is the weight side (rows = n) and its "B" operand the activation side
+//    (columns = m), so each lane ends with 4 consecutive n of one output row: 8-byte bf16 stores.
+//  * Global -> LDS by buffer_load ... lds (no VGPR staging), 2 or 3 LDS stages; bounds come from
+//    the buffer descriptors (rows past the matrix read as zero).
+//  * LDS tiles are rows of 128 bytes with a 16-byte-chunk XOR swizzle chosen so that the lanes
+//    the 64-bank LDS serves together hit distinct banks: ds_read_b128 serves 16 lanes (16
+//    consecutive rows of a K-major tile) per pass, ds_read_b64_tr_b8 32 lanes (rows k0+j and
+//    k0+32+j, j < 8, of an MN-major tile).
+//    K-major operands (rows = m or n) are read with ds_read_b128; MN-major operands (rows = k,
+//    dgrad / wgrad) are read with ds_read_b64_tr_b8, which transposes 8x8 byte blocks across
+//    lanes, so no separate transpose pass is needed.
+//  * Workgroup ids are remapped so that each XCD (ids round-robin over 8 XCDs) works on a
+//    compact group of tiles and its L2 is reused.
+#pragma once
+
+#include <float.h>
+
+#include <stdlib.h>
+
+#include <algorithm>
+
+#include "common.h"
+
+namespace fp8bs {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// How the block scales are applied (see the design notes above).
+constexpr int kScaleFold = 0;     // fp32 block scales, folded between K blocks
+constexpr int kScaleTensor = 1;   // per-tensor scales on both operands, applied in the epilogue
+constexpr int kScaleHw = 2;       // power-of-2 block scales, applied by the MFMA (E8M0)
+
+constexpr int kGroupM = 8;      // tile-rows per L2 group in the tile order
+constexpr int kLdsBytes = 160 * 1024;
+
+// Tile configuration: BM x BN output tile, WAVES_M x WAVES_N waves, each wave owning a
+// (BM / WAVES_M) x (BN / WAVES_N) block of 16x16 pieces.  Three LDS stages when they fit in
+// the 160 KiB of a CU, else two.
+template <int BM_, int BN_, int WAVES_M, int WAVES_N>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int kWaves = WAVES_M * WAVES_N;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kWavesM = WAVES_M, kWavesN = WAVES_N;
+  static constexpr int kWTM = BM / WAVES_M;   // m extent of a wave
+  static constexpr int kWTN = BN / WAVES_N;   // n extent of a wave
+  static constexpr int kNJ = kWTM / 16;       // 16-wide m pieces per wave
+  static constexpr int kNI = kWTN / 16;       // 16-wide n pieces per wave
+  static constexpr int kXBytes = BM * 128;
+  static constexpr int kWBytes = BN * 128;
+  static constexpr int kSbWords = 64;
+  static constexpr int kSaBytes = (BM + kSbWords) * 4;  // BM activation scales, weight scales
+  static constexpr int kStage = kXBytes + kWBytes + kSaBytes;
+  static constexpr int kStages = 3 * kStage <= kLdsBytes ? 3 : 2;
+  static constexpr int kLds = kStage * kStages;
+  static constexpr int kXLoads = BM / 8 / kWaves;   // 1 KB DMA blocks of the X tile per wave
+  static constexpr int kWLoads = BN / 8 / kWaves;   // ... of the W tile per wave
+  static constexpr int kSaWaves = BM / 64;          // waves that load 64 scale words each
+  static constexpr int kSbWave = (BM / 64) % kWaves;  // wave that loads the weight scales
+  static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "DMA split");
+  static_assert(kSaWaves <= kWaves, "scale loaders");
+  static_assert(kWTN <= 128 && 128 % kWTN == 0, "a wave's n range lies in one 128 block");
+  static_assert(2 * kStage <= kLdsBytes, "LDS");
+};
+
+struct GemmParams {
+  int64_t M, N, K;
+  const uint8_t* A;   // activation side (rows m)
+  int64_t lda;
+  const uint8_t* B;   // weight side (rows n)
+  int64_t ldb;
+  const float* sa;    // sa(m, kb) = sa[kb * sa_ks + (m / sa_rdiv) * sa_rs]
+  int64_t sa_ks, sa_rs, sa_bytes;
+  int sa_rdiv;
+  const float* sb;    // sb(n, kb) = sb[kb * sb_ks + (n / 128) * sb_rs]
+  int64_t sb_ks, sb_rs, sb_bytes;
+  uint16_t* C;
+  int64_t ldc;
+  int tiles_m, tiles_n;
+  int c_vec;          // 8-byte output stores are aligned
+  // grouped GEMM only
+  const int64_t* offsets;
+  int num_groups;
+  int64_t b_group_stride;   // bytes between experts' weights
+  int64_t sb_group_stride;  // floats between experts' scales
+};
+
+// ------------------------------------------------------------------ low-level helpers
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, uint64_t nbytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t n = nbytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)nbytes;
+  u32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));   // stride 0
+  r.z = __builtin_amdgcn_readfirstlane(n);
+  r.w = 0x00020000u;                                           // raw 32-bit data format
+  return r;
+}
+
+// 16 bytes per lane from buffer offset voff to LDS address lds + 16 * lane.  Offsets at or past
+// the descriptor's size read as zero.
+__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(lds) : "memory", "m0");
+}
+// 4 bytes per lane to LDS address lds + 4 * lane.
+__device__ __forceinline__ void dma4(u32x4 rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(lds) : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding (N < 64).  The
+// empty asm statements keep the compiler from moving LDS accesses across the wait.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (outstanding LDS DMA is tracked
+// explicitly with wait_vm); also a compiler barrier for memory accesses.
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Physical 16-byte chunk of logical chunk c in tile row r.  K-major tiles: rows of the same
+// parity share a 128-byte bank half, so the chunk is permuted by r / 2.  MN-major tiles: the two
+// 8-row bands 32 rows apart that one transpose read serves together use the two halves of the
+// chunk space.
+__device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz_mn(int k) { return ((k >> 1) & 3) | (((k >> 5) & 1) << 2); }
+template <bool KMAJOR>
+__device__ __forceinline__ int swz(int r) { return KMAJOR ? swz_k(r) : swz_mn(r); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>(p);
+}
+
+// K-major tile fragment: 32 bytes k = 32g .. 32g+31 of tile row r.
+__device__ __forceinline__ v8i frag_kmajor(const uint8_t* tile, int r, int g) {
+  const uint8_t* row = tile + r * 128;
+  const int sw = swz_k(r);
+  uint4 lo = *reinterpret_cast<const uint4*>(row + (((2 * g) ^ sw) << 4));
+  uint4 hi = *reinterpret_cast<const uint4*>(row + (((2 * g + 1) ^ sw) << 4));
+  v8i v;
+  v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+  v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  return v;
+}
+
+// MN-major tile fragment (tile = [halves][128 k][128 cols]): 32 bytes k = 32g .. 32g+31 of
+// column c = col0 + li (col0 a multiple of 16).  Four 8x8 byte transposes across lanes: source
+// lane 2j + h of each 16-lane group points at row k0 + j, bytes col0 + 8h .. +8.
+__device__ __forceinline__ v8i frag_mnmajor(const uint8_t* tile, int col0, int li, int g) {
+  const uint8_t* half = tile + (col0 >> 7) * 16384;
+  const int chunk = (col0 & 127) >> 4;
+  v8i v;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int k = 32 * g + 8 * t + (li >> 1);
+    const uint8_t* p = half + k * 128 + ((chunk ^ swz_mn(k)) << 4) + 8 * (li & 1);
+    v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)p);
+    v[2 * t] = r.x;
+    v[2 * t + 1] = r.y;
+  }
+  return v;
+}
+
+template <bool KMAJOR>
+__device__ __forceinline__ v8i fragment(const uint8_t* tile, int idx, int li, int g) {
+  if constexpr (KMAJOR) return frag_kmajor(tile, idx, g);
+  else return frag_mnmajor(tile, idx - li, li, g);
+}
+
+// Per-lane DMA source offsets for a tile side.  K-major: rows of the tile are matrix rows
+// (m or n), the K block starts at the descriptor base.  MN-major: rows of the tile are k, the
+// 128-column halves sit at +128 * h.  Instruction q of the tile covers LDS bytes
+// [1024 q, 1024 q + 1024) = 8 rows of 128 bytes; lane i fills row 8q' + i / 8 at physical
+// chunk i % 8, which holds logical chunk (i % 8) ^ swz(row).
+template <bool KMAJOR>
+__device__ __forceinline__ uint32_t dma_voffset(int q, int lane, int64_t ld) {
+  const int rl = lane >> 3;
+  if constexpr (KMAJOR) {
+    const int row = 8 * q + rl;
+    const int c = (lane & 7) ^ swz_k(row);
+    return (uint32_t)((int64_t)row * ld + 16 * c);
+  } else {
+    const int h = q >> 4, qq = q & 15;
+    const int row = 8 * qq + rl;
+    const int c = (lane & 7) ^ swz_mn(row);
+    return (uint32_t)((int64_t)row * ld + 128 * h + 16 * c);
+  }
+}
+
+// Zero the bytes of a K-major tile whose k is at or beyond krem (last, partial K block).
+template <int ROWS, int THREADS>
+__device__ __forceinline__ void zero_k_tail(uint8_t* tile, int krem) {
+  for (int id = threadIdx.x; id < ROWS * 8; id += THREADS) {
+    const int r = id >> 3, c = id & 7;
+    uint8_t* p = tile + r * 128 + ((c ^ swz_k(r)) << 4);
+    if (16 * c >= krem) {
+      *reinterpret_cast<uint4*>(p) = make_uint4(0, 0, 0, 0);
+    } else if (16 * c + 16 > krem) {
+      for (int b = krem - 16 * c; b < 16; ++b) p[b] = 0;
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  bf2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm_upto(int n) {
+  // n is wave-uniform and in {N, N+1, N+2}
+  if (n == N + 2) wait_vm<N + 2>();
+  else if (n == N + 1) wait_vm<N + 1>();
+  else wait_vm<N>();
+}
+
+// ------------------------------------------------------------------ one output tile
+// Computes C[m0 .. m_end) x [n0 .. n0 + BN) (columns clipped to N) with the operand roles of
+// LAYOUT; A points at the activation-side matrix, Bw at the weight-side matrix of this tile's
+// group, sbw at the group's weight scales (sb_bytes bytes).
+// E8M0 code of a power-of-two scale: its binary32 exponent field (2^-127, the one subnormal
+// power of two a scale can take, has field 0 and is E8M0 code 0 as well).
+__device__ __forceinline__ int e8m0_of(float s) {
+  return (int)((__builtin_bit_cast(uint32_t, s) >> 23) & 0xFF);
+}
+
+template <class C, int LAYOUT, int FA, int FB, int SM>
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, int64_t m0,
+                                          int64_t m_end, int64_t n0, const uint8_t* Bw,
+                                          const float* sbw, int64_t sb_bytes) {
+  constexpr bool XK = LAYOUT != FP8BS_WGRAD;   // activation side K-major?
+  constexpr bool WK = LAYOUT == FP8BS_FPROP;   // weight side K-major?
+  constexpr bool FOLD = SM == kScaleFold;
+  constexpr bool HW = SM == kScaleHw;
+  constexpr bool STAGED = SM != kScaleTensor;   // block scales staged in LDS with the operands
+  constexpr int BM = C::BM, BN = C::BN, NI = C::kNI, NJ = C::kNJ;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int wm = w % C::kWavesM, wn = w / C::kWavesM;
+  const int li = lane & 15, g = lane >> 4;
+  const int64_t K = p.K;
+  const int nkb = (int)((K + 127) >> 7);
+  const int krem = (int)(K - (int64_t)(nkb - 1) * 128);
+  const uint32_t lds0 = lds_addr(smem);
+  const int64_t nblk0 = n0 >> 7;
+
+  // DMA source offsets (fixed across K blocks).
+  uint32_t xoff[C::kXLoads], woff[C::kWLoads];
+#pragma unroll
+  for (int q = 0; q < C::kXLoads; ++q) xoff[q] = dma_voffset<XK>(w * C::kXLoads + q, lane, p.lda);
+#pragma unroll
+  for (int q = 0; q < C::kWLoads; ++q) woff[q] = dma_voffset<WK>(w * C::kWLoads + q, lane, p.ldb);
+  const bool sa_loader = w < C::kSaWaves;
+  const bool sb_loader = w == C::kSbWave;
+  uint32_t saoff = 0xFFFFFFFFu, sboff = 0xFFFFFFFFu;
+  {
+    const int64_t row = m0 + w * 64 + lane;
+    if (row < m_end) saoff = (uint32_t)(((row / p.sa_rdiv) * p.sa_rs) * 4);
+    const int64_t nb = nblk0 + lane;
+    if (lane < BN / 128 && nb * 128 < p.N) sboff = (uint32_t)(nb * p.sb_rs * 4);
+  }
+
+  // Rows of each stored operand, for the descriptor bounds.
+  const int64_t a_rows = XK ? m_end : K;
+  const int64_t w_rows = WK ? p.N : K;
+
+  auto issue = [&](int kb) {
+    const uint32_t sbase = lds0 + (kb % C::kStages) * C::kStage;
+    const int64_t k0 = (int64_t)kb * 128;
+    {
+      const uint8_t* base;
+      int64_t avail;
+      if constexpr (XK) {
+        base = p.A + m0 * p.lda + k0;
+        avail = (a_rows - m0) * p.lda - k0;
+      } else {
+        base = p.A + k0 * p.lda + m0;
+        avail = (a_rows - k0) * p.lda - m0;
+      }
+      const u32x4 r = make_rsrc(base, avail > 0 ? (uint64_t)avail : 0);
+#pragma unroll
+      for (int q = 0; q < C::kXLoads; ++q)
+        dma16(r, xoff[q], __builtin_amdgcn_readfirstlane(sbase + (w * C::kXLoads + q) * 1024));
+    }
+    {
+      const uint8_t* base;
+      int64_t avail;
+      if constexpr (WK) {
+        base = Bw + n0 * p.ldb + k0;
+        avail = (w_rows - n0) * p.ldb - k0;
+      } else {
+        base = Bw + k0 * p.ldb + n0;
+        avail = (w_rows - k0) * p.ldb - n0;
+      }
+      const u32x4 r = make_rsrc(base, avail > 0 ? (uint64_t)avail : 0);
+#pragma unroll
+      for (int q = 0; q < C::kWLoads; ++q)
+        dma16(r, woff[q], __builtin_amdgcn_readfirstlane(sbase + C::kXBytes + (w * C::kWLoads + q) * 1024));
+    }
+    // Scales of the K block: one activation word per tile row, then one weight word per
+    // 128-column block of the tile (lanes past those read outside the descriptor: zeros).
+    if constexpr (STAGED) {
+      if (sa_loader) {
+        const int64_t off = kb * p.sa_ks;
+        const u32x4 r = make_rsrc(p.sa + off, (uint64_t)(p.sa_bytes - off * 4));
+        dma4(r, saoff, __builtin_amdgcn_readfirstlane(sbase + C::kXBytes + C::kWBytes + w * 256));
+      }
+      if (sb_loader) {
+        const int64_t off = kb * p.sb_ks;
+        const u32x4 r = make_rsrc(sbw + off, (uint64_t)(sb_bytes - off * 4));
+        dma4(r, sboff, __builtin_amdgcn_readfirstlane(sbase + C::kXBytes + C::kWBytes + BM * 4));
+      }
+    }
+  };
+  // DMA instructions per K block issued by this wave (vmcnt is counted per wave).
+  constexpr int kPerStage = C::kXLoads + C::kWLoads;
+  const int per_stage =
+      kPerStage + ((STAGED && sa_loader) ? 1 : 0) + ((STAGED && sb_loader) ? 1 : 0);
+
+  v4f acc[NI][NJ];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // Pipeline.  Stages hold K blocks kb .. kb + kStages - 1.
+  auto wait_next = [&](int next) {
+    // stage `next` must be complete; stage next + 1 may still be in flight (3 stages)
+    if constexpr (C::kStages == 3) {
+      if (next + 1 < nkb) wait_vm_upto<kPerStage>(per_stage);
+      else wait_vm<0>();
+    } else {
+      wait_vm<0>();
+    }
+  };
+  auto stage_ptr = [&](int kb) { return smem + (kb % C::kStages) * C::kStage; };
+  auto prepare = [&](int kb) {
+    // ragged K: the last block's bytes past K are zeroed before anyone reads them
+    if (kb == nkb - 1 && krem < 128 && (XK || WK)) {
+      uint8_t* st = stage_ptr(kb);
+      if constexpr (XK) zero_k_tail<BM, C::kThreads>(st, krem);
+      if constexpr (WK) zero_k_tail<BN, C::kThreads>(st + C::kXBytes, krem);
+      __syncthreads();
+    }
+  };
+  // One K block: MFMAs of m piece j are issued while piece j-1 is folded.  The fragments of the
+  // first piece (xf, c0) and the weight fragments wf are loaded by the caller.
+  auto mma_block = [&](const uint8_t* st, v8i (&wf)[NI], v8i xf, float c0, float sbv,
+                       v4f (&P)[NI], float& cprev) {
+    const float* sat = reinterpret_cast<const float*>(st + C::kXBytes + C::kWBytes);
+    float ccur = c0;
+    const int wbyte = HW ? e8m0_of(sbv) : 0;   // weight scale: one per wave and K block
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int mrow = wm * C::kWTM + 16 * j + li;
+      v8i xnext;
+      float cnext = 0.0f;
+      if (j + 1 < NJ) {
+        xnext = fragment<XK>(st, mrow + 16, li, g);
+        if constexpr (FOLD) cnext = sat[mrow + 16] * sbv;
+        if constexpr (HW) cnext = sat[mrow + 16];
+      }
+      const int xbyte = HW ? e8m0_of(ccur) : 0;   // activation scale of this lane's row
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        if constexpr (FOLD) {
+          // Unit i: the MFMA of (piece j, n piece i) and the fold of (piece j-1, n piece i),
+          // whose MFMA was issued NI MFMAs earlier and has completed.  The scheduling barrier
+          // keeps the compiler from pulling the fold of an MFMA right behind that MFMA (which
+          // would stall the wave on every MFMA result).
+          const v4f pn = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              wf[i], xf, v4f{0.f, 0.f, 0.f, 0.f}, FB, FA, 0, 0, 0, 0);
+          if (j > 0) acc[i][j - 1] += P[i] * cprev;
+          P[i] = pn;
+          __builtin_amdgcn_sched_barrier(0);
+        } else if constexpr (HW) {
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[i], xf, acc[i][j], FB,
+                                                                       FA, 0, wbyte, 0, xbyte);
+        } else {
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[i], xf, acc[i][j], FB,
+                                                                       FA, 0, 0, 0, 0);
+        }
+      }
+      cprev = ccur;
+      if (j + 1 < NJ) {
+        xf = xnext;
+        ccur = cnext;
+      }
+    }
+  };
+  auto load_w = [&](const uint8_t* st, v8i (&wf)[NI]) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) wf[i] = fragment<WK>(st + C::kXBytes, wn * C::kWTN + 16 * i + li, li, g);
+  };
+  auto first_piece = [&](const uint8_t* st, v8i& xf, float& c0, float& sbv) {
+    const float* sat = reinterpret_cast<const float*>(st + C::kXBytes + C::kWBytes);
+    xf = fragment<XK>(st, wm * C::kWTM + li, li, g);
+    if constexpr (FOLD) {
+      sbv = sat[BM + (wn * C::kWTN) / 128];
+      c0 = sat[wm * C::kWTM + li] * sbv;
+    }
+    if constexpr (HW) {
+      sbv = sat[BM + (wn * C::kWTN) / 128];
+      c0 = sat[wm * C::kWTM + li];
+    }
+  };
+
+  for (int s = 0; s < C::kStages - 1; ++s)
+    if (s < nkb) issue(s);
+
+  // The barrier at the top of iteration kb publishes stage kb (every wave has waited for its
+  // own DMA of it) and proves that every wave has finished reading stage kb - 1, whose slot
+  // then receives block kb + kStages - 1.
+  for (int kb = 0; kb < nkb; ++kb) {
+    wait_next(kb);
+    barrier();
+    prepare(kb);
+    const uint8_t* st = stage_ptr(kb);
+    v8i wf[NI], xf;
+    float c0 = 0.0f, sbv = 1.0f;
+    // The block's first fragments are requested before this wave's DMA of a later block: a DMA
+    // instruction can wait for the memory pipeline, and the LDS reads then complete meanwhile.
+    first_piece(st, xf, c0, sbv);
+    load_w(st, wf);
+    if (kb + C::kStages - 1 < nkb) issue(kb + C::kStages - 1);
+    v4f P[NI];
+    float cprev = 0.0f;
+    mma_block(st, wf, xf, c0, sbv, P, cprev);
+    if constexpr (FOLD) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) acc[i][NJ - 1] += P[i] * cprev;
+    }
+    // (the next iteration's barrier orders every wave's reads of this stage before its refill)
+  }
+
+  float post = 1.0f;
+  if constexpr (SM == kScaleTensor) post = nkb > 0 ? p.sa[0] * sbw[0] : 0.0f;
+
+  // Epilogue: lane holds C[m][n .. n+3] of each piece.
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int64_t m = m0 + wm * C::kWTM + 16 * j + li;
+    if (m >= m_end) continue;
+    uint16_t* crow = p.C + m * p.ldc;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int64_t n = n0 + wn * C::kWTN + 16 * i + 4 * g;
+      v4f v = acc[i][j];
+      if constexpr (SM == kScaleTensor) v = v * post;
+      if (nkb == 0) v = v4f{0.f, 0.f, 0.f, 0.f};
+      const uint32_t lo = pack_bf16x2(v[0], v[1]);
+      const uint32_t hi = pack_bf16x2(v[2], v[3]);
+      if (p.c_vec && n + 4 <= p.N) {
+        *reinterpret_cast<uint2*>(crow + n) = make_uint2(lo, hi);
+      } else {
+        const uint16_t h[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < p.N) crow[n + e] = h[e];
+      }
+    }
+  }
+}
+
+// Map a linear workgroup id to a tile so that each of the 8 XCDs (ids are dealt round robin)
+// gets a contiguous range of tiles, ordered in groups of kGroupM tile-rows for L2 reuse.
+__device__ __forceinline__ void tile_of(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  const int q = total / 8, r = total % 8;
+  const int xcd = id % 8, local = id / 8;
+  const int pid = xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+  const int width = kGroupM * tiles_n;
+  const int grp = pid / width;
+  const int first = grp * kGroupM;
+  const int gsz = min(tiles_m - first, kGroupM);
+  const int in = pid % width;
+  tm = first + in % gsz;
+  tn = in / gsz;
+}
+
+template <class C, int LAYOUT, int FA, int FB, int SM>
+__global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int tm, tn;
+  tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * C::BM;
+  gemm_tile<C, LAYOUT, FA, FB, SM>(p, smem, m0, std::min<int64_t>(m0 + C::BM, p.M),
+                                   (int64_t)tn * C::BN, p.B, p.sb, p.sb_bytes);
+}
+
+// Grouped: a persistent grid walks the concatenation of every group's m tiles (times the n
+// tiles).  Each workgroup first builds the prefix count of m tiles per group in LDS, then maps
+// each of its tiles to (group, m tile, n tile) by binary search.
+constexpr int kMaxGroups = 1024;
+
+template <class C, int FA, int FB, int SM>
+__global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(GemmParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int s_prefix[kMaxGroups + 1];
+  __shared__ int s_wave_sum[C::kWaves];
+  constexpr int BM = C::BM;
+  const int G = p.num_groups;
+  // m tiles per group (offsets clamped to [0, M] and made non-decreasing), prefix-summed
+  int carry = 0;
+  for (int base = 0; base < G; base += C::kThreads) {
+    const int gi = base + threadIdx.x;
+    int tiles = 0;
+    if (gi < G) {
+      const int64_t lo = std::min<int64_t>(std::max<int64_t>(p.offsets[gi], 0), p.M);
+      const int64_t hi = std::min<int64_t>(std::max<int64_t>(p.offsets[gi + 1], lo), p.M);
+      tiles = (int)((hi - lo + BM - 1) / BM);
+    }
+    int v = tiles;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(v, off);
+      if (lane >= off) v += o;
+    }
+    if (lane == 63) s_wave_sum[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int before = carry;
+    for (int w = 0; w < (int)(threadIdx.x >> 6); ++w) before += s_wave_sum[w];
+    if (gi < G) s_prefix[gi + 1] = before + v;
+    int total = carry;
+    for (int w = 0; w < C::kWaves; ++w) total += s_wave_sum[w];
+    carry = total;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) s_prefix[0] = 0;
+  __syncthreads();
+  const int m_tiles = s_prefix[G];
+  const int total = m_tiles * p.tiles_n;
+  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    const int mt = tile / p.tiles_n, tn = tile % p.tiles_n;
+    int lo = 0, hi = G - 1;   // last group with s_prefix[g] <= mt
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_prefix[mid] <= mt) lo = mid; else hi = mid - 1;
+    }
+    const int gi = lo;
+    const int64_t glo = std::min<int64_t>(std::max<int64_t>(p.offsets[gi], 0), p.M);
+    const int64_t ghi = std::min<int64_t>(std::max<int64_t>(p.offsets[gi + 1], glo), p.M);
+    const int64_t m0 = glo + (int64_t)(mt - s_prefix[gi]) * BM;
+    gemm_tile<C, FP8BS_FPROP, FA, FB, SM>(p, smem, m0, std::min<int64_t>(m0 + BM, ghi),
+                                          (int64_t)tn * C::BN, p.B + gi * p.b_group_stride,
+                                          p.sb + gi * p.sb_group_stride,
+                                          p.sb_group_stride * 4);
+    __syncthreads();   // the next tile refills the LDS stages
+  }
+}
+
+template <typename KernelT>
+int launch_gemm(KernelT kernel, int blocks, int threads, int lds, hipStream_t st,
+                const GemmParams& p) {
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+    return FP8BS_ERR_LAUNCH;
+  void* args[] = {const_cast<GemmParams*>(&p)};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(blocks),
+                                 dim3(threads), args, lds, st);
+  return e == hipSuccess ? FP8BS_OK : FP8BS_ERR_LAUNCH;
+}
+
+// Tile configurations.
+using CfgA = Cfg<256, 128, 2, 2>;   // 4 waves, 128 x 64 per wave, 3 stages
+using CfgB = Cfg<256, 128, 4, 2>;   // 8 waves, 64 x 64 per wave, 3 stages
+using CfgC = Cfg<256, 256, 2, 4>;   // 8 waves, 128 x 64 per wave, 2 stages
+using CfgD = Cfg<128, 128, 2, 2>;   // 4 waves, 64 x 64 per wave (small M, grouped)
+
+template <class C, int LAYOUT, int FA, int FB, int SM>
+int launch_dense(GemmParams p, hipStream_t st) {
+  p.tiles_m = (int)ceil_div(p.M, C::BM);
+  p.tiles_n = (int)ceil_div(p.N, C::BN);
+  if ((int64_t)p.tiles_m * p.tiles_n > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
+  return launch_gemm(gemm_kernel<C, LAYOUT, FA, FB, SM>, p.tiles_m * p.tiles_n, C::kThreads,
+                     C::kLds, st, p);
+}
+
+// Variant choice: the largest tile that still gives every CU at least one workgroup (two
+// waves per SIMD hide LDS and MFMA latency best).  FP8BS_GEMM_VARIANT (A, B, C or D) overrides
+// the choice, for tuning and tests.
+char pick_variant(int64_t M, int64_t N) {
+  const char* e = getenv("FP8BS_GEMM_VARIANT");
+  if (e && (e[0] == 'A' || e[0] == 'B' || e[0] == 'C' || e[0] == 'D')) return e[0];
+  if (ceil_div(M, 256) * ceil_div(N, 256) >= 256) return 'C';
+  if (ceil_div(M, 256) * ceil_div(N, 128) >= 256) return 'B';
+  return 'D';
+}
+
+template <int LAYOUT, int FA, int FB, int SM>
+int dispatch_variant(const GemmParams& p, hipStream_t st) {
+  switch (pick_variant(p.M, p.N)) {
+    case 'B': return launch_dense<CfgB, LAYOUT, FA, FB, SM>(p, st);
+    case 'C': return launch_dense<CfgC, LAYOUT, FA, FB, SM>(p, st);
+    case 'D': return launch_dense<CfgD, LAYOUT, FA, FB, SM>(p, st);
+    default: return launch_dense<CfgA, LAYOUT, FA, FB, SM>(p, st);
+  }
+}
+
+template <int LAYOUT, int SM>
+int dispatch_formats(int fa, int fb, const GemmParams& p, hipStream_t st) {
+  if (fa == FP8BS_E4M3 && fb == FP8BS_E4M3) return dispatch_variant<LAYOUT, FP8BS_E4M3, FP8BS_E4M3, SM>(p, st);
+  if (fa == FP8BS_E5M2 && fb == FP8BS_E4M3) return dispatch_variant<LAYOUT, FP8BS_E5M2, FP8BS_E4M3, SM>(p, st);
+  if (fa == FP8BS_E4M3 && fb == FP8BS_E5M2) return dispatch_variant<LAYOUT, FP8BS_E4M3, FP8BS_E5M2, SM>(p, st);
+  return dispatch_variant<LAYOUT, FP8BS_E5M2, FP8BS_E5M2, SM>(p, st);
+}
+
+template <int SM>
+int dispatch_dense(int layout, int fa, int fb, const GemmParams& p, hipStream_t st) {
+  switch (layout) {
+    case FP8BS_FPROP: return dispatch_formats<FP8BS_FPROP, SM>(fa, fb, p, st);
+    case FP8BS_DGRAD: return dispatch_formats<FP8BS_DGRAD, SM>(fa, fb, p, st);
+    default: return dispatch_formats<FP8BS_WGRAD, SM>(fa, fb, p, st);
+  }
+}
+
+// Scale indexing for one operand.  rows: the operand's output dimension (m or n);
+// kmajor: the operand is stored [rows, K] (else [K, rows]).
+struct ScaleIndex {
+  int64_t ks, rs, bytes;
+  int rdiv;
+};
+
+bool scale_index(int gran, bool kmajor, bool weight_side, int64_t rows, int64_t K,
+                 ScaleIndex& s) {
+  const int64_t kblocks = ceil_div(K, 128), rblocks = ceil_div(rows, 128);
+  if (gran == FP8BS_PER_TENSOR) {
+    s = {0, 0, 4, 1};
+    return true;
+  }
+  if (gran == FP8BS_BLOCK_1x128) {
+    if (!kmajor || weight_side) return false;   // 1x128 must run along K, activation side only
+    s = {rows, 1, kblocks * rows * 4, 1};       // float[K/128][rows]
+    return true;
+  }
+  if (gran == FP8BS_BLOCK_128x128) {
+    if (kmajor) s = {1, kblocks, rblocks * kblocks * 4, 128};   // float[rows/128][K/128]
+    else s = {rblocks, 1, kblocks * rblocks * 4, 128};          // float[K/128][rows/128]
+    return true;
+  }
+  return false;
+}
+
+// Grouped GEMM tile choice (FP8BS_GROUPED_VARIANT = B, C or D overrides, for tuning).
+char pick_grouped_variant() {
+  const char* e = getenv("FP8BS_GROUPED_VARIANT");
+  if (e && (e[0] == 'B' || e[0] == 'C' || e[0] == 'D')) return e[0];
+  return 'C';   // fastest on the MoE shapes despite 10% padding in ragged 256-row tiles
+}
+
+template <class C, int SM>
+int launch_grouped(int fa, int fb, int cus, GemmParams p, hipStream_t st) {
+  p.tiles_n = (int)ceil_div(p.N, C::BN);
+  p.tiles_m = (int)(ceil_div(p.M, C::BM) + p.num_groups);   // upper bound on m tiles
+  if ((int64_t)p.tiles_m * p.tiles_n > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
+  const int blocks = (int)std::min<int64_t>((int64_t)p.tiles_m * p.tiles_n, std::max(cus, 1));
+  if (fa == FP8BS_E4M3 && fb == FP8BS_E4M3) return launch_gemm(grouped_gemm_kernel<C, FP8BS_E4M3, FP8BS_E4M3, SM>, blocks, C::kThreads, C::kLds, st, p);
+  if (fa == FP8BS_E5M2 && fb == FP8BS_E4M3) return launch_gemm(grouped_gemm_kernel<C, FP8BS_E5M2, FP8BS_E4M3, SM>, blocks, C::kThreads, C::kLds, st, p);
+  if (fa == FP8BS_E4M3 && fb == FP8BS_E5M2) return launch_gemm(grouped_gemm_kernel<C, FP8BS_E4M3, FP8BS_E5M2, SM>, blocks, C::kThreads, C::kLds, st, p);
+  return launch_gemm(grouped_gemm_kernel<C, FP8BS_E5M2, FP8BS_E5M2, SM>, blocks, C::kThreads, C::kLds, st, p);
+}
+
+template <int SM>
+int dispatch_grouped(int fa, int fb, int cus, const GemmParams& p, hipStream_t st) {
+  switch (pick_grouped_variant()) {
+    case 'C': return launch_grouped<CfgC, SM>(fa, fb, cus, p, st);
+    case 'D': return launch_grouped<CfgD, SM>(fa, fb, cus, p, st);
+    default: return launch_grouped<CfgB, SM>(fa, fb, cus, p, st);
+  }
+}
+
+
+// ------------------------------------------------------------------ argument checks (host)
+// Validates the dense GEMM arguments and fills p.  tensor_only: both operands carry per-tensor
+// scales.  empty: nothing to compute (M == 0 or N == 0); the status is then FP8BS_OK.
+inline int dense_params(int layout, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                        int fa, int ga, const float* scale_inv_a, const void* B, int64_t ldb,
+                        int fb, int gb, const float* scale_inv_b, void* C_bf16, int64_t ldc,
+                        GemmParams& p, bool& tensor_only, bool& empty) {
+  empty = false;
+  if (layout < FP8BS_FPROP || layout > FP8BS_WGRAD || !fmt_ok(fa) || !fmt_ok(fb) || ga < 0 ||
+      ga > 2 || gb < 0 || gb > 2)
+    return FP8BS_ERR_ARG;
+  if (M < 0 || N < 0 || K < 0) return FP8BS_ERR_SHAPE;
+  if (M == 0 || N == 0) {
+    empty = true;
+    return FP8BS_OK;
+  }
+  if (!C_bf16 || (K > 0 && (!A || !B || !scale_inv_a || !scale_inv_b))) return FP8BS_ERR_NULL;
+  const bool xk = layout != FP8BS_WGRAD, wk = layout == FP8BS_FPROP;
+  const int64_t a_width = xk ? K : M, b_width = wk ? K : N;
+  if (ldc < N || (K > 0 && (lda < a_width || ldb < b_width))) return FP8BS_ERR_SHAPE;
+  // 32-bit buffer offsets inside a tile: 256 rows of the pitch must stay below 2^31.
+  if (lda >= (int64_t(1) << 23) || ldb >= (int64_t(1) << 23)) return FP8BS_ERR_SHAPE;
+  if (M > (int64_t(1) << 31) - 256 || N > (int64_t(1) << 31) - 256) return FP8BS_ERR_SHAPE;
+  if (K > 0 && (!aligned16(A) || !aligned16(B) || lda % 16 || ldb % 16)) return FP8BS_ERR_ALIGN;
+  if (!aligned4(C_bf16) || ldc % 2) return FP8BS_ERR_ALIGN;
+  ScaleIndex sa{}, sb{};
+  if (!scale_index(ga, xk, false, M, K, sa) || !scale_index(gb, wk, true, N, K, sb))
+    return FP8BS_ERR_UNSUPPORTED;
+  p = GemmParams{};
+  p.M = M; p.N = N; p.K = K;
+  p.A = static_cast<const uint8_t*>(A); p.lda = lda;
+  p.B = static_cast<const uint8_t*>(B); p.ldb = ldb;
+  p.sa = scale_inv_a; p.sa_ks = sa.ks; p.sa_rs = sa.rs; p.sa_bytes = sa.bytes; p.sa_rdiv = sa.rdiv;
+  p.sb = scale_inv_b; p.sb_ks = sb.ks; p.sb_rs = sb.rs; p.sb_bytes = sb.bytes;
+  p.C = static_cast<uint16_t*>(C_bf16); p.ldc = ldc;
+  p.c_vec = (reinterpret_cast<uintptr_t>(C_bf16) % 8 == 0) && (ldc % 4 == 0);
+  tensor_only = ga == FP8BS_PER_TENSOR && gb == FP8BS_PER_TENSOR;
+  return FP8BS_OK;
+}
+
+// Validates the grouped GEMM arguments and fills p (empty: nothing to compute, status OK).
+inline int grouped_params(int32_t num_groups, const int64_t* group_offsets, int64_t total_M,
+                          int64_t N, int64_t K, const void* A, int64_t lda, int fa,
+                          const float* scale_inv_a, const void* B, int64_t ldb, int fb,
+                          const float* scale_inv_b, void* C_bf16, int64_t ldc, GemmParams& p,
+                          bool& empty) {
+  empty = false;
+  if (!fmt_ok(fa) || !fmt_ok(fb) || num_groups < 0 || num_groups > kMaxGroups)
+    return FP8BS_ERR_ARG;
+  if (total_M < 0 || N < 0 || K < 0) return FP8BS_ERR_SHAPE;
+  if (total_M == 0 || N == 0 || num_groups == 0) {
+    empty = true;
+    return FP8BS_OK;
+  }
+  if (K == 0) return FP8BS_ERR_SHAPE;
+  if (!group_offsets || !A || !B || !scale_inv_a || !scale_inv_b || !C_bf16) return FP8BS_ERR_NULL;
+  if (lda < K || ldb < K || ldc < N) return FP8BS_ERR_SHAPE;
+  if (lda >= (int64_t(1) << 23) || ldb >= (int64_t(1) << 23)) return FP8BS_ERR_SHAPE;
+  if (total_M > (int64_t(1) << 31) - 256 || N > (int64_t(1) << 31) - 256) return FP8BS_ERR_SHAPE;
+  if (!aligned16(A) || !aligned16(B) || lda % 16 || ldb % 16) return FP8BS_ERR_ALIGN;
+  if (!aligned4(C_bf16) || ldc % 2 || (reinterpret_cast<uintptr_t>(group_offsets) & 7))
+    return FP8BS_ERR_ALIGN;
+  p = GemmParams{};
+  p.M = total_M; p.N = N; p.K = K;
+  p.A = static_cast<const uint8_t*>(A); p.lda = lda;
+  p.B = static_cast<const uint8_t*>(B); p.ldb = ldb;
+  p.sa = scale_inv_a; p.sa_ks = total_M; p.sa_rs = 1; p.sa_rdiv = 1;
+  p.sa_bytes = ceil_div(K, 128) * total_M * 4;
+  p.sb = scale_inv_b; p.sb_ks = 1; p.sb_rs = ceil_div(K, 128);
+  p.C = static_cast<uint16_t*>(C_bf16); p.ldc = ldc;
+  p.c_vec = (reinterpret_cast<uintptr_t>(C_bf16) % 8 == 0) && (ldc % 4 == 0);
+  p.offsets = group_offsets;
+  p.num_groups = num_groups;
+  p.b_group_stride = N * ldb;
+  p.sb_group_stride = ceil_div(N, 128) * ceil_div(K, 128);
+  return FP8BS_OK;
+}
+
+inline int device_cus() {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  return cus;
+}
+
+}  // namespace
+}  // namespace fp8bs

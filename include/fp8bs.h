@@ -185,6 +185,29 @@ int fp8_grouped_gemm(int32_t num_groups, const int64_t* group_offsets, int64_t t
                      const float* scale_inv_a, const void* B, int64_t ldb, int fb,
                      const float* scale_inv_b, void* C_bf16, int64_t ldc, void* stream);
 
+/* Block-scaled FP8 GEMM with power-of-2 scales -- "NVIDIA NeMo RL logra una aceleración del 48%
+ * ...", section "Por qué esto es importante para la economía de la IA" (the power-of-2 scale
+ * option).  Same arguments, layouts, granularities, scale arrays, results and errors as
+ * fp8_gemm_blockscaled; the difference is the precondition on the scales: every scale_inv value
+ * read must be a power of two in [2^-127, 2^127] (what fp8_quantize_blockwise writes in
+ * FP8BS_SCALE_POW2 mode).  Only the binary32 exponent field of each value is used: it is given
+ * to the matrix core as an E8M0 block scale, so the products are scaled and accumulated inside
+ * the MFMA with no per-block fold.  A scale that is not a power of two is taken as 2 raised to
+ * its exponent (the result is then that of the rounded-down scale); no error is reported for it.
+ * With per-tensor scales on both operands this call computes exactly what fp8_gemm_blockscaled
+ * computes. */
+int fp8_gemm_blockscaled_pow2(int layout, int64_t M, int64_t N, int64_t K,
+                              const void* A, int64_t lda, int fa, int ga, const float* scale_inv_a,
+                              const void* B, int64_t ldb, int fb, int gb, const float* scale_inv_b,
+                              void* C_bf16, int64_t ldc, void* stream);
+
+/* Grouped (MoE) GEMM with power-of-2 scales: fp8_grouped_gemm's arguments, layouts and errors,
+ * with the scale precondition and E8M0 use of fp8_gemm_blockscaled_pow2. */
+int fp8_grouped_gemm_pow2(int32_t num_groups, const int64_t* group_offsets, int64_t total_M,
+                          int64_t N, int64_t K, const void* A, int64_t lda, int fa,
+                          const float* scale_inv_a, const void* B, int64_t ldb, int fb,
+                          const float* scale_inv_b, void* C_bf16, int64_t ldc, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

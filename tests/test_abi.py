@@ -5,6 +5,7 @@
   before anything is enqueued (null device pointers never get dereferenced here).
 """
 import ctypes
+import functools
 
 import pytest
 
@@ -19,7 +20,8 @@ def test_library_exports_every_declared_symbol():
     names = bsq.declared_functions()
     assert set(names) >= {"fp8_quantize_blockwise", "fp8_quantize_delayed",
                           "fp8_quantize_delayed_workspace_size", "fp8_gemm_blockscaled",
-                          "fp8_grouped_gemm", "fp8_cast_fp32", "fp8bs_status_string"}
+                          "fp8_grouped_gemm", "fp8_cast_fp32", "fp8bs_status_string",
+                          "fp8_gemm_blockscaled_pow2", "fp8_grouped_gemm_pow2"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -81,16 +83,18 @@ def test_quantize_delayed_validation():
     assert q_delayed(s=FAKE_ODD) == bsq.ERR_ALIGN
 
 
-def gemm(**kw):
+def gemm(entry="fp8_gemm_blockscaled", **kw):
     a = dict(layout=0, M=256, N=256, K=256, A=FAKE, lda=256, fa=0, ga=0, sa=FAKE, B=FAKE,
              ldb=256, fb=0, gb=1, sb=FAKE, C=FAKE, ldc=256)
     a.update(kw)
-    return bsq.load().fp8_gemm_blockscaled(a["layout"], a["M"], a["N"], a["K"], a["A"], a["lda"],
-                                           a["fa"], a["ga"], a["sa"], a["B"], a["ldb"], a["fb"],
-                                           a["gb"], a["sb"], a["C"], a["ldc"], None)
+    return getattr(bsq.load(), entry)(a["layout"], a["M"], a["N"], a["K"], a["A"], a["lda"],
+                                      a["fa"], a["ga"], a["sa"], a["B"], a["ldb"], a["fb"],
+                                      a["gb"], a["sb"], a["C"], a["ldc"], None)
 
 
-def test_gemm_validation():
+@pytest.mark.parametrize("entry", ["fp8_gemm_blockscaled", "fp8_gemm_blockscaled_pow2"])
+def test_gemm_validation(entry):
+    gemm = functools.partial(globals()["gemm"], entry)
     assert gemm(layout=3) == bsq.ERR_ARG
     assert gemm(fa=2) == bsq.ERR_ARG
     assert gemm(gb=3) == bsq.ERR_ARG
@@ -109,16 +113,18 @@ def test_gemm_validation():
     assert gemm(M=0) == bsq.OK and gemm(N=0, C=None) == bsq.OK
 
 
-def grouped(**kw):
+def grouped(entry="fp8_grouped_gemm", **kw):
     a = dict(G=4, off=FAKE, M=512, N=256, K=256, A=FAKE, lda=256, fa=0, sa=FAKE, B=FAKE,
              ldb=256, fb=0, sb=FAKE, C=FAKE, ldc=256)
     a.update(kw)
-    return bsq.load().fp8_grouped_gemm(a["G"], a["off"], a["M"], a["N"], a["K"], a["A"], a["lda"],
-                                       a["fa"], a["sa"], a["B"], a["ldb"], a["fb"], a["sb"], a["C"],
-                                       a["ldc"], None)
+    return getattr(bsq.load(), entry)(a["G"], a["off"], a["M"], a["N"], a["K"], a["A"], a["lda"],
+                                      a["fa"], a["sa"], a["B"], a["ldb"], a["fb"], a["sb"], a["C"],
+                                      a["ldc"], None)
 
 
-def test_grouped_validation():
+@pytest.mark.parametrize("entry", ["fp8_grouped_gemm", "fp8_grouped_gemm_pow2"])
+def test_grouped_validation(entry):
+    grouped = functools.partial(globals()["grouped"], entry)
     assert grouped(G=-1) == bsq.ERR_ARG
     assert grouped(G=5000) == bsq.ERR_ARG
     assert grouped(fb=9) == bsq.ERR_ARG

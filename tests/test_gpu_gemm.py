@@ -24,17 +24,17 @@ B1, B128, PT = bsq.BLOCK_1x128, bsq.BLOCK_128x128, bsq.PER_TENSOR
 E4, E5 = bsq.E4M3, bsq.E5M2
 
 
-def quantize_operand(x: torch.Tensor, fmt, gran):
+def quantize_operand(x: torch.Tensor, fmt, gran, mode=oracle.SCALE_FP32):
     """Oracle quantization of a stored bf16 matrix; returns (codes, logical scales)."""
     if gran == PT:
         st = oracle.DelayedState(1)
         from helpers import bits
         b = bits(x)
-        oracle.delayed_step(b, fmt, oracle.SCALE_FP32, 0, st)       # calibrate on x itself
-        q, siu = oracle.delayed_step(b, fmt, oracle.SCALE_FP32, 0, st)
+        oracle.delayed_step(b, fmt, mode, 0, st)       # calibrate on x itself
+        q, siu = oracle.delayed_step(b, fmt, mode, 0, st)
         return q, np.array([[siu]], dtype=np.float32)
     from helpers import bits
-    return oracle.quantize_blockwise(bits(x), fmt, gran, oracle.SCALE_FP32)
+    return oracle.quantize_blockwise(bits(x), fmt, gran, mode)
 
 
 def to_device_codes(q: np.ndarray, ld: int) -> torch.Tensor:
@@ -50,14 +50,17 @@ def device_scales(s: np.ndarray, gran) -> torch.Tensor:
     return logical_to_gpu_scales(s, gran)
 
 
-def run_gemm(gpu, layout, M, N, K, fa, ga, fb, gb, seed=0, pad=0, rows=None, c_guard=True):
+def run_gemm(gpu, layout, M, N, K, fa, ga, fb, gb, seed=0, pad=0, rows=None, c_guard=True,
+             pow2=False):
+    """pow2: power-of-2 scales (SCALE_POW2 quantization) through fp8_gemm_blockscaled_pow2."""
+    mode = oracle.SCALE_POW2 if pow2 else oracle.SCALE_FP32
     ashape = (M, K) if layout != WG else (K, M)
     bshape = (N, K) if layout == FP else (K, N)
     a = synth.activations_with_outliers(*ashape, seed, f"gemm/A{layout}") if ga == B1 else \
         synth.normal(ashape, 1.0, seed, f"gemm/A{layout}")
     b = synth.normal(bshape, 0.02, seed, f"gemm/B{layout}")
-    qa, sa = quantize_operand(a, fa, ga)
-    qb, sb = quantize_operand(b, fb, gb)
+    qa, sa = quantize_operand(a, fa, ga, mode)
+    qb, sb = quantize_operand(b, fb, gb, mode)
     lda = -(-ashape[1] // 16) * 16 + pad
     ldb = -(-bshape[1] // 16) * 16 + pad
     ad, bd = to_device_codes(qa, lda), to_device_codes(qb, ldb)
@@ -65,7 +68,7 @@ def run_gemm(gpu, layout, M, N, K, fa, ga, fb, gb, seed=0, pad=0, rows=None, c_g
     cstore = torch.full((M + 1, ldc), -7.0, dtype=torch.bfloat16, device="cuda")
     c = cstore[:M, :N]
     gpu.gemm_blockscaled(layout, ad, fa, ga, device_scales(sa, ga), bd, fb, gb,
-                         device_scales(sb, gb), c=c)
+                         device_scales(sb, gb), c=c, pow2=pow2)
     torch.cuda.synchronize()
     if c_guard:
         assert torch.all(cstore[:M, N:] == -7.0) and torch.all(cstore[M] == -7.0), "guard overwritten"
@@ -173,23 +176,24 @@ def test_deterministic(gpu):
 
 # ----------------------------------------------------------------------------- grouped
 
-def run_grouped(gpu, counts, N, K, seed=0, sample_rows=None):
+def run_grouped(gpu, counts, N, K, seed=0, sample_rows=None, pow2=False):
+    mode = oracle.SCALE_POW2 if pow2 else oracle.SCALE_FP32
     counts = np.asarray(counts, dtype=np.int64)
     G = len(counts)
     off = synth.offsets_from_counts(counts)
     total = int(off[-1])
     x = synth.normal((total, K), 1.0, seed, "grouped/A")
-    qa, sa = quantize_operand(x, E4, B1)
+    qa, sa = quantize_operand(x, E4, B1, mode)
     qbs, sbs = [], []
     for g in range(G):
         w = synth.normal((N, K), 0.02, seed, f"grouped/W{g}")
-        q, s = quantize_operand(w, E4, B128)
+        q, s = quantize_operand(w, E4, B128, mode)
         qbs.append(q)
         sbs.append(s)
     qbs, sbs = np.stack(qbs), np.stack(sbs)
     c = gpu.grouped_gemm(torch.from_numpy(off).cuda(), torch.from_numpy(qa).cuda(),
                          logical_to_gpu_scales(sa, B1), torch.from_numpy(qbs).cuda(),
-                         torch.from_numpy(sbs).cuda())
+                         torch.from_numpy(sbs).cuda(), pow2=pow2)
     torch.cuda.synchronize()
     if sample_rows is None:
         ref = oracle.grouped_gemm(off, qa, sa, E4, qbs, sbs, E4)
@@ -243,3 +247,103 @@ def test_grouped_every_tile_variant(gpu, monkeypatch, variant):
     """Each tile configuration the grouped kernel can use (FP8BS_GROUPED_VARIANT forces one)."""
     monkeypatch.setenv("FP8BS_GROUPED_VARIANT", variant)
     run_grouped(gpu, [5, 0, 300, 1, 0, 257, 128, 513], 384, 400)
+
+
+# ----------------------------------------------------------------------------- power-of-2 scales
+# fp8_gemm_blockscaled_pow2 / fp8_grouped_gemm_pow2: power-of-2 scales ("NVIDIA NeMo RL ...",
+# section "Por qué esto es importante para la economía de la IA") given to the MFMA as E8M0 block
+# scales.  Same oracle and tolerance: a power-of-2 scale is exact in the fp64 reference.
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_pow2_fprop_block_scales(gpu, M, N, K):
+    run_gemm(gpu, FP, M, N, K, E4, B1, E4, B128, pow2=True)
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES[:4])
+@pytest.mark.parametrize("layout,fa,ga,fb,gb", [(FP, E4, B1, E4, PT), (FP, E4, PT, E4, B128),
+                                                 (FP, E4, PT, E4, PT), (FP, E4, B128, E5, B128),
+                                                 (DG, E5, B1, E4, B128), (DG, E5, PT, E4, B128),
+                                                 (WG, E5, PT, E4, B128), (WG, E4, B128, E4, B128)])
+def test_pow2_layouts_and_scale_kinds(gpu, M, N, K, layout, fa, ga, fb, gb):
+    run_gemm(gpu, layout, M, N, K, fa, ga, fb, gb, pow2=True)
+
+
+def test_pow2_padded_pitches_with_nan_padding(gpu):
+    run_gemm(gpu, FP, 200, 200, 200, E4, B1, E4, B128, pad=48, pow2=True)
+    run_gemm(gpu, DG, 200, 200, 200, E5, B1, E4, B128, pad=32, pow2=True)
+
+
+@pytest.mark.parametrize("variant", ["A", "B", "C", "D"])
+@pytest.mark.parametrize("layout,fa,ga,fb,gb", [(FP, E4, B1, E4, B128), (DG, E5, B1, E4, B128),
+                                                 (WG, E5, PT, E4, B128)])
+def test_pow2_every_tile_variant(gpu, monkeypatch, variant, layout, fa, ga, fb, gb):
+    monkeypatch.setenv("FP8BS_GEMM_VARIANT", variant)
+    run_gemm(gpu, layout, 520, 390, 392, fa, ga, fb, gb, pow2=True)
+
+
+def test_pow2_llama8b_fprop_full_size_sampled_rows(gpu):
+    rows = np.sort(np.random.Generator(np.random.PCG64(4)).choice(8192, 192, replace=False))
+    run_gemm(gpu, FP, 8192, 6144, 4096, E4, B1, E4, B128, rows=rows, c_guard=False, pow2=True)
+
+
+def test_pow2_extreme_exponents(gpu):
+    """Scales at the ends of the E8M0 range the quantizers can produce: 2^-127 (the subnormal
+    power of two, E8M0 code 0) on one operand and large powers on the other; codes of +-1."""
+    M, N, K = 64, 128, 256
+    qa = torch.full((M, K), 0x38, dtype=torch.uint8)          # E4M3 1.0
+    qa[:, 1::2] = 0xB8                                         # -1.0 on odd k
+    qa[::3, :] = 0x38
+    qb = torch.full((N, K), 0x38, dtype=torch.uint8)
+    sa = np.full((K // 128, M), 2.0 ** 100, dtype=np.float32)
+    sa[1, :] = 2.0 ** 60
+    sb = np.full((1, K // 128), 2.0 ** -127, dtype=np.float32)
+    sb[0, 1] = 2.0 ** -100
+    c = gpu.gemm_blockscaled(FP, qa.cuda(), E4, B1, torch.from_numpy(sa).cuda(), qb.cuda(), E4,
+                             B128, torch.from_numpy(sb).cuda(), pow2=True)
+    ad = oracle.dequantize(qa.numpy(), E4, B1, sa.T)
+    bd = oracle.dequantize(qb.numpy(), E4, B128, sb)
+    gemm_check(c, ad @ bd.T, np.abs(ad) @ np.abs(bd).T, "pow2 extremes")
+
+
+def test_pow2_uses_the_exponent_only(gpu):
+    """A scale that is not a power of two acts as 2^floor(log2 s): compare with the fp32-scale
+    entry given the rounded-down scales."""
+    qa = torch.randint(0, 0x7E, (300, 512), dtype=torch.uint8, device="cuda")
+    qb = torch.randint(0, 0x7E, (256, 512), dtype=torch.uint8, device="cuda")
+    sa = torch.rand((4, 300), device="cuda") * 3 + 0.1
+    sb = torch.rand((2, 4), device="cuda") * 3 + 0.1
+    down = lambda t: (t.view(torch.int32) & 0x7F800000).view(torch.float32)
+    c1 = gpu.gemm_blockscaled(FP, qa, E4, B1, sa, qb, E4, B128, sb, pow2=True).float()
+    c2 = gpu.gemm_blockscaled(FP, qa, E4, B1, down(sa), qb, E4, B128, down(sb)).float()
+    rel = float(torch.linalg.norm(c1 - c2) / torch.linalg.norm(c2))
+    assert rel < 2e-3, rel
+
+
+def test_pow2_agrees_with_fold_path(gpu):
+    """Same power-of-2 inputs through both entry points: equal up to accumulation order."""
+    x = synth.activations_with_outliers(1024, 2048, 5, "pow2/agree/X")
+    w = synth.normal((768, 2048), 0.02, 5, "pow2/agree/W")
+    qa, sa = quantize_operand(x, E4, B1, oracle.SCALE_POW2)
+    qb, sb = quantize_operand(w, E4, B128, oracle.SCALE_POW2)
+    args = (FP, torch.from_numpy(qa).cuda(), E4, B1, device_scales(sa, B1),
+            torch.from_numpy(qb).cuda(), E4, B128, device_scales(sb, B128))
+    c1 = gpu.gemm_blockscaled(*args, pow2=True).float()
+    c2 = gpu.gemm_blockscaled(*args).float()
+    rel = float(torch.linalg.norm(c1 - c2) / torch.linalg.norm(c2))
+    assert rel < 2e-3, rel
+
+
+def test_pow2_grouped_small_with_empty_groups(gpu):
+    run_grouped(gpu, [5, 0, 130, 1, 0, 257, 128], 256, 384, pow2=True)
+
+
+def test_pow2_grouped_moe_config_sampled(gpu):
+    counts = synth.moe_routing(16384, 128, 8, 1.1, 0)
+    rows = np.sort(np.random.Generator(np.random.PCG64(6)).choice(int(counts.sum()), 256, replace=False))
+    run_grouped(gpu, counts, 1536, 2048, sample_rows=rows, pow2=True)
+
+
+@pytest.mark.parametrize("variant", ["B", "C", "D"])
+def test_pow2_grouped_every_tile_variant(gpu, monkeypatch, variant):
+    monkeypatch.setenv("FP8BS_GROUPED_VARIANT", variant)
+    run_grouped(gpu, [5, 0, 300, 1, 0, 257, 128, 513], 384, 400, pow2=True)
