@@ -60,6 +60,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.fp8bs_status_string.argtypes = [i32]
     lib.fp8bs_status_string.restype = ctypes.c_char_p
     lib.fp8_quantize_blockwise.argtypes = [vp, i64, i64, i64, i32, i32, i32, vp, i64, vp, vp]
+    lib.fp8_quantize_columnwise_t.argtypes = [vp, i64, i64, i64, i32, i32, vp, i64, vp, vp]
     lib.fp8_quantize_delayed.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.fp8_quantize_delayed_workspace_size.argtypes = []
     lib.fp8_quantize_delayed_workspace_size.restype = sz
@@ -70,7 +71,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
                                      i64, i32, vp, vp, i64, vp]
     lib.fp8_gemm_blockscaled_pow2.argtypes = lib.fp8_gemm_blockscaled.argtypes
     lib.fp8_grouped_gemm_pow2.argtypes = lib.fp8_grouped_gemm.argtypes
-    for name in ("fp8_quantize_blockwise", "fp8_quantize_delayed", "fp8_cast_fp32",
+    for name in ("fp8_quantize_blockwise", "fp8_quantize_columnwise_t", "fp8_quantize_delayed",
+                 "fp8_cast_fp32",
                  "fp8_gemm_blockscaled", "fp8_grouped_gemm", "fp8_gemm_blockscaled_pow2",
                  "fp8_grouped_gemm_pow2"):
         getattr(lib, name).restype = i32
@@ -132,6 +134,27 @@ def quantize_blockwise(x: torch.Tensor, fmt: int, gran: int, mode: int = SCALE_F
                                          _ptr(q), q.stride(0), _ptr(scale_inv), _stream(stream)),
            "fp8_quantize_blockwise")
     return q, scale_inv
+
+
+def quantize_columnwise_t(x: torch.Tensor, fmt: int, mode: int = SCALE_FP32,
+                          qt: torch.Tensor | None = None, scale_inv: torch.Tensor | None = None,
+                          stream=None):
+    """Columnwise (128 rows x 1 column blocks) quantization of a 2-D bf16 matrix x[rows, cols],
+    codes written transposed.
+
+    Returns (codes uint8 [cols, rows] = the codes of x^T, scale_inv float32
+    [ceil(rows/128), cols] = the 1x128 scale layout of x^T)."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 matrix with unit column stride")
+    rows, cols = x.shape
+    if qt is None:
+        qt = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    if scale_inv is None:
+        scale_inv = torch.empty(((rows + 127) // 128, cols), dtype=torch.float32, device=x.device)
+    _check(load().fp8_quantize_columnwise_t(_ptr(x), rows, cols, x.stride(0), fmt, mode, _ptr(qt),
+                                            qt.stride(0), _ptr(scale_inv), _stream(stream)),
+           "fp8_quantize_columnwise_t")
+    return qt, scale_inv
 
 
 def delayed_workspace_size() -> int:

@@ -10,13 +10,14 @@ extern "C" int fp8_gemm_blockscaled(int layout, int64_t M, int64_t N, int64_t K,
                                     const float* scale_inv_b, void* C_bf16, int64_t ldc,
                                     void* stream) {
   GemmParams p{};
-  bool tensor_only = false, empty = false;
+  bool tensor_only = false, empty = false, b_rows = false;
   const int s = dense_params(layout, M, N, K, A, lda, fa, ga, scale_inv_a, B, ldb, fb, gb,
-                             scale_inv_b, C_bf16, ldc, p, tensor_only, empty);
+                             scale_inv_b, C_bf16, ldc, p, tensor_only, empty, b_rows);
   if (s != FP8BS_OK || empty) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return tensor_only ? dispatch_dense<kScaleTensor>(layout, fa, fb, p, st)
-                     : dispatch_dense<kScaleFold>(layout, fa, fb, p, st);
+  if (tensor_only) return dispatch_dense<kScaleTensor>(layout, fa, fb, p, st);
+  return b_rows ? dispatch_dense<kScaleFoldRows>(layout, fa, fb, p, st)
+                : dispatch_dense<kScaleFold>(layout, fa, fb, p, st);
 }
 
 extern "C" int fp8_grouped_gemm(int32_t num_groups, const int64_t* group_offsets,

@@ -55,6 +55,11 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 constexpr int kScaleFold = 0;     // fp32 block scales, folded between K blocks
 constexpr int kScaleTensor = 1;   // per-tensor scales on both operands, applied in the epilogue
 constexpr int kScaleHw = 2;       // power-of-2 block scales, applied by the MFMA (E8M0)
+// The same two block-scale modes with 1x128 weight-side scales (one per weight row and K block,
+// the layout of a transposed columnwise-quantized operand): the fold multiplies each output
+// element by its own sa[m] * sb[n]; the MFMA takes a per-lane E8M0 weight scale.
+constexpr int kScaleFoldRows = 3;
+constexpr int kScaleHwRows = 4;
 
 constexpr int kGroupM = 8;      // tile-rows per L2 group in the tile order
 constexpr int kLdsBytes = 160 * 1024;
@@ -74,7 +79,7 @@ struct Cfg {
   static constexpr int kNI = kWTN / 16;       // 16-wide n pieces per wave
   static constexpr int kXBytes = BM * 128;
   static constexpr int kWBytes = BN * 128;
-  static constexpr int kSbWords = 64;
+  static constexpr int kSbWords = BN;   // one weight scale per tile column at most (1x128)
   static constexpr int kSaBytes = (BM + kSbWords) * 4;  // BM activation scales, weight scales
   static constexpr int kStage = kXBytes + kWBytes + kSaBytes;
   static constexpr int kStages = 3 * kStage <= kLdsBytes ? 3 : 2;
@@ -83,6 +88,10 @@ struct Cfg {
   static constexpr int kWLoads = BN / 8 / kWaves;   // ... of the W tile per wave
   static constexpr int kSaWaves = BM / 64;          // waves that load 64 scale words each
   static constexpr int kSbWave = (BM / 64) % kWaves;  // wave that loads the weight scales
+  // 1x128 weight scales (one per tile column): BN / 64 waves load 64 words each.
+  static constexpr int kSbRowWaves = BN / 64;
+  static constexpr int kSbRowWave0 = (BM / 64) % kWaves;
+  static_assert(kSbRowWave0 + kSbRowWaves <= kWaves, "weight-scale loaders");
   static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "DMA split");
   static_assert(kSaWaves <= kWaves, "scale loaders");
   static_assert(kWTN <= 128 && 128 % kWTN == 0, "a wave's n range lies in one 128 block");
@@ -266,8 +275,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
                                           const float* sbw, int64_t sb_bytes) {
   constexpr bool XK = LAYOUT != FP8BS_WGRAD;   // activation side K-major?
   constexpr bool WK = LAYOUT == FP8BS_FPROP;   // weight side K-major?
-  constexpr bool FOLD = SM == kScaleFold;
-  constexpr bool HW = SM == kScaleHw;
+  constexpr bool ROWS = SM == kScaleFoldRows || SM == kScaleHwRows;   // 1x128 weight scales
+  constexpr bool FOLD = SM == kScaleFold || SM == kScaleFoldRows;
+  constexpr bool HW = SM == kScaleHw || SM == kScaleHwRows;
   constexpr bool STAGED = SM != kScaleTensor;   // block scales staged in LDS with the operands
   constexpr int BM = C::BM, BN = C::BN, NI = C::kNI, NJ = C::kNJ;
   const int lane = threadIdx.x & 63;
@@ -287,13 +297,20 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
 #pragma unroll
   for (int q = 0; q < C::kWLoads; ++q) woff[q] = dma_voffset<WK>(w * C::kWLoads + q, lane, p.ldb);
   const bool sa_loader = w < C::kSaWaves;
-  const bool sb_loader = w == C::kSbWave;
+  const bool sb_loader = ROWS ? (w >= C::kSbRowWave0 && w < C::kSbRowWave0 + C::kSbRowWaves)
+                              : w == C::kSbWave;
   uint32_t saoff = 0xFFFFFFFFu, sboff = 0xFFFFFFFFu;
   {
     const int64_t row = m0 + w * 64 + lane;
     if (row < m_end) saoff = (uint32_t)(((row / p.sa_rdiv) * p.sa_rs) * 4);
-    const int64_t nb = nblk0 + lane;
-    if (lane < BN / 128 && nb * 128 < p.N) sboff = (uint32_t)(nb * p.sb_rs * 4);
+    if constexpr (ROWS) {
+      // weight scale words n0 + 64 (w - w0) + lane (columns past N read as zero)
+      const int64_t n = n0 + (int64_t)(w - C::kSbRowWave0) * 64 + lane;
+      if (sb_loader && n < p.N) sboff = (uint32_t)(n * p.sb_rs * 4);
+    } else {
+      const int64_t nb = nblk0 + lane;
+      if (lane < BN / 128 && nb * 128 < p.N) sboff = (uint32_t)(nb * p.sb_rs * 4);
+    }
   }
 
   // Rows of each stored operand, for the descriptor bounds.
@@ -344,7 +361,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
       if (sb_loader) {
         const int64_t off = kb * p.sb_ks;
         const u32x4 r = make_rsrc(sbw + off, (uint64_t)(sb_bytes - off * 4));
-        dma4(r, sboff, __builtin_amdgcn_readfirstlane(sbase + C::kXBytes + C::kWBytes + BM * 4));
+        const uint32_t dst = sbase + C::kXBytes + C::kWBytes + BM * 4 +
+                             (ROWS ? (w - C::kSbRowWave0) * 256 : 0);
+        dma4(r, sboff, __builtin_amdgcn_readfirstlane(dst));
       }
     }
   };
@@ -382,10 +401,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
   // One K block: MFMAs of m piece j are issued while piece j-1 is folded.  The fragments of the
   // first piece (xf, c0) and the weight fragments wf are loaded by the caller.
   auto mma_block = [&](const uint8_t* st, v8i (&wf)[NI], v8i xf, float c0, float sbv,
-                       v4f (&P)[NI], float& cprev) {
+                       const v4f (&sbr)[NI], const int (&wbr)[NI], v4f (&P)[NI], float& cprev) {
     const float* sat = reinterpret_cast<const float*>(st + C::kXBytes + C::kWBytes);
     float ccur = c0;
-    const int wbyte = HW ? e8m0_of(sbv) : 0;   // weight scale: one per wave and K block
+    const int wbyte = (HW && !ROWS) ? e8m0_of(sbv) : 0;   // weight scale: one per wave and K block
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int mrow = wm * C::kWTM + 16 * j + li;
@@ -393,8 +412,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
       float cnext = 0.0f;
       if (j + 1 < NJ) {
         xnext = fragment<XK>(st, mrow + 16, li, g);
-        if constexpr (FOLD) cnext = sat[mrow + 16] * sbv;
-        if constexpr (HW) cnext = sat[mrow + 16];
+        if constexpr (FOLD && !ROWS) cnext = sat[mrow + 16] * sbv;
+        if constexpr (HW || ROWS) cnext = sat[mrow + 16];
       }
       const int xbyte = HW ? e8m0_of(ccur) : 0;   // activation scale of this lane's row
 #pragma unroll
@@ -406,12 +425,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
           // would stall the wave on every MFMA result).
           const v4f pn = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               wf[i], xf, v4f{0.f, 0.f, 0.f, 0.f}, FB, FA, 0, 0, 0, 0);
-          if (j > 0) acc[i][j - 1] += P[i] * cprev;
+          if (j > 0) {
+            if constexpr (ROWS) acc[i][j - 1] += P[i] * (sbr[i] * cprev);   // sb[n..n+3] * sa[m]
+            else acc[i][j - 1] += P[i] * cprev;
+          }
           P[i] = pn;
           __builtin_amdgcn_sched_barrier(0);
         } else if constexpr (HW) {
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[i], xf, acc[i][j], FB,
-                                                                       FA, 0, wbyte, 0, xbyte);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              wf[i], xf, acc[i][j], FB, FA, 0, ROWS ? wbr[i] : wbyte, 0, xbyte);
         } else {
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[i], xf, acc[i][j], FB,
                                                                        FA, 0, 0, 0, 0);
@@ -428,14 +450,23 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
 #pragma unroll
     for (int i = 0; i < NI; ++i) wf[i] = fragment<WK>(st + C::kXBytes, wn * C::kWTN + 16 * i + li, li, g);
   };
-  auto first_piece = [&](const uint8_t* st, v8i& xf, float& c0, float& sbv) {
+  auto first_piece = [&](const uint8_t* st, v8i& xf, float& c0, float& sbv, v4f (&sbr)[NI],
+                         int (&wbr)[NI]) {
     const float* sat = reinterpret_cast<const float*>(st + C::kXBytes + C::kWBytes);
     xf = fragment<XK>(st, wm * C::kWTM + li, li, g);
-    if constexpr (FOLD) {
+    if constexpr (ROWS) {
+      c0 = sat[wm * C::kWTM + li];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int ncol = wn * C::kWTN + 16 * i;
+        // fold: the scales of this lane's 4 output columns; MFMA: that of its A-operand row
+        if constexpr (FOLD) sbr[i] = *reinterpret_cast<const v4f*>(sat + BM + ncol + 4 * g);
+        if constexpr (HW) wbr[i] = e8m0_of(sat[BM + ncol + li]);
+      }
+    } else if constexpr (FOLD) {
       sbv = sat[BM + (wn * C::kWTN) / 128];
       c0 = sat[wm * C::kWTM + li] * sbv;
-    }
-    if constexpr (HW) {
+    } else if constexpr (HW) {
       sbv = sat[BM + (wn * C::kWTN) / 128];
       c0 = sat[wm * C::kWTM + li];
     }
@@ -454,17 +485,22 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
     const uint8_t* st = stage_ptr(kb);
     v8i wf[NI], xf;
     float c0 = 0.0f, sbv = 1.0f;
+    v4f sbr[NI];
+    int wbr[NI];
     // The block's first fragments are requested before this wave's DMA of a later block: a DMA
     // instruction can wait for the memory pipeline, and the LDS reads then complete meanwhile.
-    first_piece(st, xf, c0, sbv);
+    first_piece(st, xf, c0, sbv, sbr, wbr);
     load_w(st, wf);
     if (kb + C::kStages - 1 < nkb) issue(kb + C::kStages - 1);
     v4f P[NI];
     float cprev = 0.0f;
-    mma_block(st, wf, xf, c0, sbv, P, cprev);
+    mma_block(st, wf, xf, c0, sbv, sbr, wbr, P, cprev);
     if constexpr (FOLD) {
 #pragma unroll
-      for (int i = 0; i < NI; ++i) acc[i][NJ - 1] += P[i] * cprev;
+      for (int i = 0; i < NI; ++i) {
+        if constexpr (ROWS) acc[i][NJ - 1] += P[i] * (sbr[i] * cprev);
+        else acc[i][NJ - 1] += P[i] * cprev;
+      }
     }
     // (the next iteration's barrier orders every wave's reads of this stage before its refill)
   }
@@ -644,6 +680,10 @@ int dispatch_formats(int fa, int fb, const GemmParams& p, hipStream_t st) {
 
 template <int SM>
 int dispatch_dense(int layout, int fa, int fb, const GemmParams& p, hipStream_t st) {
+  if constexpr (SM == kScaleFoldRows || SM == kScaleHwRows) {
+    // 1x128 weight scales need a K-major weight operand: fprop only (checked by the caller)
+    return dispatch_formats<FP8BS_FPROP, SM>(fa, fb, p, st);
+  }
   switch (layout) {
     case FP8BS_FPROP: return dispatch_formats<FP8BS_FPROP, SM>(fa, fb, p, st);
     case FP8BS_DGRAD: return dispatch_formats<FP8BS_DGRAD, SM>(fa, fb, p, st);
@@ -666,7 +706,8 @@ bool scale_index(int gran, bool kmajor, bool weight_side, int64_t rows, int64_t 
     return true;
   }
   if (gran == FP8BS_BLOCK_1x128) {
-    if (!kmajor || weight_side) return false;   // 1x128 must run along K, activation side only
+    if (!kmajor) return false;                  // 1x128 blocks run along K: K-major operands only
+    (void)weight_side;
     s = {rows, 1, kblocks * rows * 4, 1};       // float[K/128][rows]
     return true;
   }
@@ -709,11 +750,12 @@ int dispatch_grouped(int fa, int fb, int cus, const GemmParams& p, hipStream_t s
 
 // ------------------------------------------------------------------ argument checks (host)
 // Validates the dense GEMM arguments and fills p.  tensor_only: both operands carry per-tensor
-// scales.  empty: nothing to compute (M == 0 or N == 0); the status is then FP8BS_OK.
+// scales.  b_rows: the weight side carries 1x128 scales.  empty: nothing to compute (M == 0 or
+// N == 0); the status is then FP8BS_OK.
 inline int dense_params(int layout, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                         int fa, int ga, const float* scale_inv_a, const void* B, int64_t ldb,
                         int fb, int gb, const float* scale_inv_b, void* C_bf16, int64_t ldc,
-                        GemmParams& p, bool& tensor_only, bool& empty) {
+                        GemmParams& p, bool& tensor_only, bool& empty, bool& b_rows) {
   empty = false;
   if (layout < FP8BS_FPROP || layout > FP8BS_WGRAD || !fmt_ok(fa) || !fmt_ok(fb) || ga < 0 ||
       ga > 2 || gb < 0 || gb > 2)
@@ -744,6 +786,7 @@ inline int dense_params(int layout, int64_t M, int64_t N, int64_t K, const void*
   p.C = static_cast<uint16_t*>(C_bf16); p.ldc = ldc;
   p.c_vec = (reinterpret_cast<uintptr_t>(C_bf16) % 8 == 0) && (ldc % 4 == 0);
   tensor_only = ga == FP8BS_PER_TENSOR && gb == FP8BS_PER_TENSOR;
+  b_rows = gb == FP8BS_BLOCK_1x128;   // only accepted for a K-major weight operand (fprop)
   return FP8BS_OK;
 }
 

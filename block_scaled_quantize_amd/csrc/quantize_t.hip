@@ -1,0 +1,190 @@
+// Columnwise (128x1) FP8 quantization with transposed output, for gfx950.
+//
+// Method: "NVIDIA NeMo RL logra una aceleración del 48% con entrenamiento de precisión FP8 de
+// extremo a extremo", section "El avance técnico": activations carry one scale per 128
+// consecutive elements along the dimension a GEMM contracts.  The weight gradient contracts
+// over tokens, so there the blocks of an activation or gradient X[tokens, features] run down a
+// column: 128 consecutive rows of one column.  This kernel computes those blocks and writes the
+// codes of X transposed, [features][tokens], so the weight-gradient GEMM reads them K-major
+// (tokens contiguous) with the scales in the 1x128 layout of the transposed matrix:
+// scale_inv[row block][column].  Scale rule, rounding, saturation and NaN handling are those
+// of the blockwise quantizer (power-of-2 option: section "Por qué esto es importante para la
+// economía de la IA").
+//
+// Design (HBM-bound, one pass): a workgroup of 256 lanes takes a 128-row x 128-column tile;
+// lane (row group g, column chunk c) loads rows 8g .. 8g+7 of columns 8c .. 8c+7 with 16-byte
+// loads, so each lane ends with 8 codes of 8 consecutive rows per column: one 8-byte store per
+// column into the transposed matrix.  The column maxima are reduced over the lane's 8 rows in
+// registers (packed 16-bit max of magnitude bits), across the 4 row groups of a wave by lane
+// shuffles and across the 4 waves through 1 KiB of LDS.
+#include <float.h>
+
+#include "common.h"
+
+namespace fp8bs {
+namespace {
+
+constexpr int kThreadsT = 256;
+
+// 8 consecutive bf16 of row r from column c on (elements outside the matrix read as +0).
+// VEC: 16-byte aligned rows.
+template <bool VEC>
+__device__ __forceinline__ uint4 load8(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                       int64_t ld, int64_t r, int64_t c) {
+  if (r >= rows || c >= cols) return make_uint4(0u, 0u, 0u, 0u);
+  const uint16_t* p = x + r * ld + c;
+  if (VEC && c + 8 <= cols) return *reinterpret_cast<const uint4*>(p);
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = (c + 2 * i < cols) ? (uint32_t)p[2 * i] : 0u;
+    const uint32_t hi = (c + 2 * i + 1 < cols) ? (uint32_t)p[2 * i + 1] : 0u;
+    w[i] = lo | (hi << 16);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <int FMT, bool POW2, bool VEC>
+__global__ __launch_bounds__(kThreadsT) void quant_128x1_t_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+    uint8_t* __restrict__ qt, int64_t ld_qt, float* __restrict__ scale_inv) {
+  __shared__ uint32_t s_max[4][16][4];   // [wave][column chunk][column pair], packed 16-bit
+  const int t = threadIdx.x;
+  const int lane = t & 63, wv = t >> 6;
+  const int cg = t & 15, rg = t >> 4;
+  const int64_t nbc = (cols + 127) >> 7;
+  const int64_t rb = blockIdx.x / nbc, cb = blockIdx.x % nbc;
+  const int64_t r0 = rb * 128 + 8 * rg;
+  const int64_t c0 = cb * 128 + 8 * cg;
+
+  uint32_t d[8][4];   // d[k][p]: row r0 + k, columns c0 + 2p (low half) and c0 + 2p + 1
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint4 v = load8<VEC>(x, rows, cols, ld_x, r0 + k, c0);
+    d[k][0] = v.x; d[k][1] = v.y; d[k][2] = v.z; d[k][3] = v.w;
+  }
+
+  // Column maxima: over this lane's 8 rows, then over the wave's 4 row groups (lanes that
+  // differ in bits 4 and 5 share the column chunk), then over the 4 waves.
+  uint32_t m[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    u16x2 v = mag2(d[0][p]);
+#pragma unroll
+    for (int k = 1; k < 8; ++k) v = max2(v, mag2(d[k][p]));
+    uint32_t b = __builtin_bit_cast(uint32_t, v);
+    b = __builtin_bit_cast(uint32_t, max2(__builtin_bit_cast(u16x2, b),
+                                           __builtin_bit_cast(u16x2, (uint32_t)__shfl_xor((int)b, 16))));
+    b = __builtin_bit_cast(uint32_t, max2(__builtin_bit_cast(u16x2, b),
+                                           __builtin_bit_cast(u16x2, (uint32_t)__shfl_xor((int)b, 32))));
+    m[p] = b;
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) s_max[wv][cg][p] = m[p];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    u16x2 v = __builtin_bit_cast(u16x2, s_max[0][cg][p]);
+#pragma unroll
+    for (int w = 1; w < 4; ++w) v = max2(v, __builtin_bit_cast(u16x2, s_max[w][cg][p]));
+    m[p] = __builtin_bit_cast(uint32_t, v);
+  }
+
+  float s[8];
+  bool finite = true;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t a = (j & 1) ? (m[j >> 1] >> 16) : (m[j >> 1] & 0xFFFFu);
+    s[j] = scale_from_amax_bits<FMT, POW2>(a);
+    finite = finite && a < 0x7F80u;
+  }
+
+  // Encode column by column: the 8 codes of column c0 + j are rows r0 .. r0 + 7 of the
+  // transposed matrix.  Columns of a block holding NaN/Inf (s = 1) take the clamped path with
+  // NaN codes patched; for finite blocks the clamp is a no-op.
+  const bool vec_rows = VEC && r0 + 8 <= rows;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int p = j >> 1;
+    float y[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y[k] = ((j & 1) ? bf16_hi(d[k][p]) : bf16_lo(d[k][p])) * s[j];
+    if (!finite) {
+      constexpr float F = Format<FMT>::fmax;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) y[k] = __builtin_amdgcn_fmed3f(y[k], -F, F);
+    }
+    uint32_t lo = cvt4<FMT>(y[0], y[1], y[2], y[3]);
+    uint32_t hi = cvt4<FMT>(y[4], y[5], y[6], y[7]);
+    if (!finite) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t b = ((j & 1) ? (d[k][p] >> 16) : d[k][p]) & 0xFFFFu;
+        if ((b & 0x7FFFu) > 0x7F80u) {
+          const uint32_t code = 0x7Fu | ((b >> 8) & 0x80u);
+          const int sh = 8 * (k & 3);
+          if (k < 4) lo = (lo & ~(0xFFu << sh)) | (code << sh);
+          else hi = (hi & ~(0xFFu << sh)) | (code << sh);
+        }
+      }
+    }
+    const int64_t c = c0 + j;
+    if (c < cols && r0 < rows) {
+      uint8_t* dst = qt + c * ld_qt + r0;
+      if (vec_rows) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (r0 + k < rows) dst[k] = (uint8_t)(((k < 4) ? lo : hi) >> (8 * (k & 3)));
+      }
+    }
+  }
+  if (rg == 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c0 + j < cols) scale_inv[rb * cols + c0 + j] = 1.0f / s[j];
+  }
+}
+
+template <int FMT>
+int dispatch_columnwise_t(bool pow2, bool vec, const uint16_t* x, int64_t rows, int64_t cols,
+                          int64_t ld_x, uint8_t* qt, int64_t ld_qt, float* s, hipStream_t st) {
+  const dim3 grid((unsigned)(ceil_div(rows, 128) * ceil_div(cols, 128)));
+  const dim3 block(kThreadsT);
+  if (pow2)
+    return vec ? launch(quant_128x1_t_kernel<FMT, true, true>, grid, block, st, x, rows, cols, ld_x, qt, ld_qt, s)
+               : launch(quant_128x1_t_kernel<FMT, true, false>, grid, block, st, x, rows, cols, ld_x, qt, ld_qt, s);
+  return vec ? launch(quant_128x1_t_kernel<FMT, false, true>, grid, block, st, x, rows, cols, ld_x, qt, ld_qt, s)
+             : launch(quant_128x1_t_kernel<FMT, false, false>, grid, block, st, x, rows, cols, ld_x, qt, ld_qt, s);
+}
+
+}  // namespace
+}  // namespace fp8bs
+
+using namespace fp8bs;
+
+extern "C" int fp8_quantize_columnwise_t(const void* x_bf16, int64_t rows, int64_t cols,
+                                         int64_t ld_x, int fmt, int mode, void* qt_out,
+                                         int64_t ld_qt, float* scale_inv_out, void* stream) {
+  if (!fmt_ok(fmt) || (mode != FP8BS_SCALE_FP32 && mode != FP8BS_SCALE_POW2)) return FP8BS_ERR_ARG;
+  if (rows < 0 || cols < 0 || ld_x < cols || ld_qt < rows) return FP8BS_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return FP8BS_OK;
+  if (!x_bf16 || !qt_out || !scale_inv_out) return FP8BS_ERR_NULL;
+  if (ceil_div(rows, 128) * ceil_div(cols, 128) > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
+  if (rows > INT64_MAX / ld_x || cols > INT64_MAX / ld_qt) return FP8BS_ERR_SHAPE;
+  if (!aligned4(scale_inv_out)) return FP8BS_ERR_ALIGN;
+  const bool vec = aligned16(x_bf16) && (reinterpret_cast<uintptr_t>(qt_out) & 7u) == 0 &&
+                   ld_x % 8 == 0 && ld_qt % 8 == 0;
+  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
+  uint8_t* qt = static_cast<uint8_t*>(qt_out);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool pow2 = mode == FP8BS_SCALE_POW2;
+  if (fmt == FP8BS_E4M3)
+    return dispatch_columnwise_t<FP8BS_E4M3>(pow2, vec, x, rows, cols, ld_x, qt, ld_qt,
+                                             scale_inv_out, st);
+  return dispatch_columnwise_t<FP8BS_E5M2>(pow2, vec, x, rows, cols, ld_x, qt, ld_qt,
+                                           scale_inv_out, st);
+}

@@ -99,6 +99,26 @@ int fp8_quantize_blockwise(const void* x_bf16, int64_t rows, int64_t cols, int64
                            float* scale_inv_out, void* stream);
 
 /*
+ * Columnwise quantization with transposed output: blocks of 128 consecutive rows of one column
+ * of x[rows, cols] (pitch ld_x elements), codes written transposed to qt_out[cols, rows] (pitch
+ * ld_qt bytes): qt_out[c][r] = enc(x[r][c] * s(r / 128, c)).  [P3] "El avance técnico": one
+ * scale per 128 consecutive activation elements along the contracted dimension -- for the
+ * weight gradient dW = dY^T . X that dimension is the token (row) dimension of dY and X.
+ * Scale rule, rounding, saturation, NaN/Inf handling and power-of-2 mode are those of
+ * fp8_quantize_blockwise (the result equals fp8_quantize_blockwise of x^T with 1x128 blocks).
+ *   scale_inv_out: float[ceil(rows/128)][cols] -- the 1x128 scale layout of the transposed
+ *                  matrix, as the GEMM reads it for a K-major operand with 1x128 blocks.
+ * rows == 0 or cols == 0 is a no-op.  Requirements: ld_x >= cols, ld_qt >= rows.  16-byte
+ * aligned input rows with 8-byte aligned output rows (ld_x % 8 == 0, ld_qt % 8 == 0, aligned
+ * bases) take the vectorized path.  Caller-owned device buffers; nothing is allocated.
+ * Errors: FP8BS_ERR_NULL, FP8BS_ERR_SHAPE, FP8BS_ERR_ALIGN (scale_inv_out not 4-byte
+ * aligned), FP8BS_ERR_ARG, FP8BS_ERR_LAUNCH.
+ */
+int fp8_quantize_columnwise_t(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                              int fmt, int mode, void* qt_out, int64_t ld_qt,
+                              float* scale_inv_out, void* stream);
+
+/*
  * One step of per-tensor delayed scaling on a contiguous bf16 tensor x[numel].
  * [P1] "Transformer Engine: la base de software": the scale used in a step comes from the
  * largest magnitudes recorded in earlier steps (history of hist_len, reduced with "max",
@@ -148,8 +168,10 @@ int fp8_cast_fp32(const float* x, int64_t n, int fmt, void* q_out, void* stream)
  *   fa, fb: operand formats (any mix of E4M3 / E5M2, e.g. E5M2 gradients).
  *   ga, gb: granularity of each operand's scales, laid out as described at the top of this
  *           file on the operand's STORED matrix.  Supported: a K-major operand ([.,K] stored)
- *           takes 1x128 (A only), 128x128 or per-tensor; an MN-major operand ([K,.] stored)
- *           takes 128x128 or per-tensor.  Other combinations return FP8BS_ERR_UNSUPPORTED.
+ *           takes 1x128, 128x128 or per-tensor; an MN-major operand ([K,.] stored) takes
+ *           128x128 or per-tensor.  Other combinations return FP8BS_ERR_UNSUPPORTED.
+ *           1x128 on both operands of FPROP is the blockwise weight gradient: with A = dY^T and
+ *           B = X^T as written by fp8_quantize_columnwise_t (K = tokens), C = dW = dY^T . X.
  *   C_bf16: [M,N] pitch ldc (elements).
  * M, N or K == 0: C is left untouched when M or N is 0; with K == 0, C is set to zeros.
  * Requirements: 16-byte aligned A and B with lda % 16 == 0 and ldb % 16 == 0, 4-byte aligned C

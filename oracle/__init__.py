@@ -172,6 +172,21 @@ def quantize_blockwise(x, fmt: int, gran: int, mode: int, nthreads: int | None =
     return q, si
 
 
+def quantize_columnwise_t(x, fmt: int, mode: int, nthreads: int | None = None):
+    """Columnwise quantization: blocks of 128 consecutive rows of one column of x[R, C], codes
+    returned transposed.  A block of 128 rows of column c of x is, by definition, a 1x128 block
+    of row c of x^T, so this is the blockwise 1x128 quantization of the transpose ("NVIDIA NeMo
+    RL ...", section "El avance técnico": one scale per 128 elements along the contracted
+    dimension, here the token dimension of the weight-gradient product).
+
+    Returns (codes uint8 [C, R] (of x^T), scale_inv float32 [C, ceil(R/128)] in logical block
+    order (row of x^T, block along R))."""
+    xb = _as_bf16_bits(x)
+    if xb.ndim != 2:
+        raise ValueError("expected a 2-D matrix")
+    return quantize_blockwise(np.ascontiguousarray(xb.T), fmt, BLOCK_1x128, mode, nthreads)
+
+
 @dataclass
 class DelayedState:
     """Per-tensor delayed-scaling state: amax history (newest first) and the current scale."""

@@ -106,9 +106,9 @@ def test_gemm_validation(entry):
     assert gemm(A=FAKE_ODD) == bsq.ERR_ALIGN
     assert gemm(lda=264) == bsq.ERR_ALIGN
     assert gemm(ldc=257) == bsq.ERR_ALIGN
-    # 1x128 scales only on a K-major activation operand
-    assert gemm(gb=0) == bsq.ERR_UNSUPPORTED                   # weight side 1x128
+    # 1x128 scales only on a K-major operand (fprop takes them on both sides)
     assert gemm(layout=2, ga=0, gb=1) == bsq.ERR_UNSUPPORTED   # wgrad: A is MN-major
+    assert gemm(layout=2, ga=1, gb=0) == bsq.ERR_UNSUPPORTED   # wgrad: B is MN-major
     assert gemm(layout=1, ga=0, gb=0) == bsq.ERR_UNSUPPORTED   # dgrad: B is MN-major
     assert gemm(M=0) == bsq.OK and gemm(N=0, C=None) == bsq.OK
 
@@ -133,6 +133,25 @@ def test_grouped_validation(entry):
     assert grouped(lda=64) == bsq.ERR_SHAPE
     assert grouped(off=FAKE + 4) == bsq.ERR_ALIGN
     assert grouped(M=0) == bsq.OK and grouped(G=0) == bsq.OK
+
+
+def qcol(**kw):
+    a = dict(x=FAKE, rows=256, cols=128, ldx=128, fmt=0, mode=0, qt=FAKE, ldqt=256, s=FAKE)
+    a.update(kw)
+    return bsq.load().fp8_quantize_columnwise_t(a["x"], a["rows"], a["cols"], a["ldx"], a["fmt"],
+                                                a["mode"], a["qt"], a["ldqt"], a["s"], None)
+
+
+def test_quantize_columnwise_validation():
+    assert qcol(fmt=2) == bsq.ERR_ARG
+    assert qcol(mode=5) == bsq.ERR_ARG
+    assert qcol(rows=-1) == bsq.ERR_SHAPE
+    assert qcol(ldx=100) == bsq.ERR_SHAPE
+    assert qcol(ldqt=255) == bsq.ERR_SHAPE          # the transposed rows hold `rows` codes
+    assert qcol(x=None) == bsq.ERR_NULL
+    assert qcol(s=None) == bsq.ERR_NULL
+    assert qcol(s=FAKE_ODD) == bsq.ERR_ALIGN
+    assert qcol(rows=0) == bsq.OK and qcol(cols=0, x=None) == bsq.OK
 
 
 def test_cast_validation():

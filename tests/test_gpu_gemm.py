@@ -347,3 +347,61 @@ def test_pow2_grouped_moe_config_sampled(gpu):
 def test_pow2_grouped_every_tile_variant(gpu, monkeypatch, variant):
     monkeypatch.setenv("FP8BS_GROUPED_VARIANT", variant)
     run_grouped(gpu, [5, 0, 300, 1, 0, 257, 128, 513], 384, 400, pow2=True)
+
+
+# ----------------------------------------------------------------------------- 1x128 x 1x128
+# Both operands with 1x128 scales along K (fprop layout): the blockwise weight gradient
+# dW = dY^T . X with dY^T and X^T quantized columnwise over tokens ("NVIDIA NeMo RL ...",
+# section "El avance técnico": one scale per 128 elements along the contracted dimension).
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("pow2", [False, True])
+def test_fprop_1x128_both_operands(gpu, M, N, K, pow2):
+    run_gemm(gpu, FP, M, N, K, E5, B1, E4, B1, pow2=pow2)
+
+
+@pytest.mark.parametrize("variant", ["A", "B", "C", "D"])
+@pytest.mark.parametrize("pow2", [False, True])
+def test_1x128_both_every_tile_variant(gpu, monkeypatch, variant, pow2):
+    monkeypatch.setenv("FP8BS_GEMM_VARIANT", variant)
+    run_gemm(gpu, FP, 520, 390, 392, E4, B1, E4, B1, pow2=pow2)
+    run_gemm(gpu, FP, 256, 256, 256, E5, B1, E5, B1, pow2=pow2)
+
+
+def wgrad_blockwise(gpu, tokens, n_out, k_in, fdy, pow2, rows=None, seed=0):
+    """dW[n_out, k_in] = dY^T . X: both operands quantized columnwise over tokens on the GPU,
+    multiplied by the fprop GEMM with 1x128 scales on both sides; checked against the oracle
+    (columnwise quantization of the same bf16 tensors, fp64 product)."""
+    mode = bsq.SCALE_POW2 if pow2 else bsq.SCALE_FP32
+    dy = synth.normal((tokens, n_out), 1e-3, seed, "wgrad/dY")
+    x = synth.activations_with_outliers(tokens, k_in, seed, "wgrad/X")
+    ld = -(-tokens // 16) * 16                         # GEMM pitch rule: multiple of 16
+    dyt = torch.empty((n_out, ld), dtype=torch.uint8, device="cuda")[:, :tokens]
+    xt = torch.empty((k_in, ld), dtype=torch.uint8, device="cuda")[:, :tokens]
+    _, sdy = gpu.quantize_columnwise_t(dy.cuda(), fdy, mode, qt=dyt)
+    _, sx = gpu.quantize_columnwise_t(x.cuda(), E4, mode, qt=xt)
+    dw = gpu.gemm_blockscaled(FP, dyt, fdy, B1, sdy, xt, E4, B1, sx, pow2=pow2)
+    torch.cuda.synchronize()
+    from helpers import bits
+    qdy, sdy_o = oracle.quantize_columnwise_t(bits(dy), fdy, mode)
+    qx, sx_o = oracle.quantize_columnwise_t(bits(x), E4, mode)
+    if rows is not None:
+        qdy, sdy_o = qdy[rows], sdy_o[rows]
+        dw = dw[torch.as_tensor(rows, device="cuda")]
+    a = oracle.dequantize(qdy, fdy, B1, sdy_o)         # dY^T rows
+    b = oracle.dequantize(qx, E4, B1, sx_o)            # X^T
+    return gemm_check(dw, a @ b.T, np.abs(a) @ np.abs(b).T, f"wgrad {tokens}x{n_out}x{k_in}")
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("fdy", [E4, E5])
+def test_blockwise_wgrad_end_to_end(gpu, pow2, fdy):
+    wgrad_blockwise(gpu, 1040, 384, 272, fdy, pow2)       # ragged last token block
+    wgrad_blockwise(gpu, 300, 130, 200, fdy, pow2)        # ragged everywhere
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_blockwise_wgrad_llama8b_qkv_sampled(gpu, pow2):
+    """dW of the qkv layer (6144 x 4096 over 8192 tokens), 128 sampled rows of dW."""
+    rows = np.sort(np.random.Generator(np.random.PCG64(7)).choice(6144, 128, replace=False))
+    wgrad_blockwise(gpu, 8192, 6144, 4096, E4, pow2, rows=rows)

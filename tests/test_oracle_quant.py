@@ -206,3 +206,57 @@ def test_pow2_scale_rounds_down(oracle_lib):
         assert m == 0.5
         assert s <= np.float32(448.0) / np.float32(amax)
         assert 2 * np.float64(s) > np.float64(np.float32(448.0) / np.float32(amax))
+
+
+# ----------------------------------------------------------------------------- columnwise (128x1)
+# oracle.quantize_columnwise_t: blocks of 128 consecutive rows of one column, codes transposed.
+# Pinned by closed forms on the column blocks themselves (the block maximum of every 128x1 block
+# lands on the +-FMAX code; each block's codes and scale depend only on that block) -- a wrong
+# block axis, a wrong transpose or a wrong ragged tail fails these.
+
+@pytest.mark.parametrize("fmt,mode", [(E4M3, FP32), (E5M2, FP32), (E4M3, POW2)])
+def test_columnwise_block_max_on_top_codes(oracle_lib, fmt, mode):
+    rows, cols = 300, 70                       # 3 row blocks, the last one ragged (44 rows)
+    x = synth.student_t((rows, cols), 3.0, 7, "pin/colwise")
+    # give each column its own magnitude so that row-wise blocks would differ from column blocks
+    x = (x.float() * torch.logspace(-3, 3, cols, base=2.0)).to(torch.bfloat16)
+    qt, si = oracle.quantize_columnwise_t(bits_of(x), fmt, mode)
+    assert qt.shape == (cols, rows) and si.shape == (cols, 3)
+    table = oracle.decode_table(fmt)
+    fmax = oracle.FMAX[fmt]
+    xf = x.float().numpy()
+    for c in range(cols):
+        for rb in range(3):
+            rs = slice(128 * rb, min(128 * rb + 128, rows))
+            blk = np.abs(xf[rs, c])
+            codes = qt[c, rs]                  # transposed: row c of qt holds column c of x
+            at_max = blk == blk.max()
+            mags = np.abs(table[codes])
+            if mode == FP32:
+                assert np.all((codes[at_max] & 0x7F) == MAXCODE[fmt])
+            else:
+                assert np.all((mags[at_max] >= fmax / 2) & (mags[at_max] <= fmax))
+            assert mags.max() <= fmax
+            # the sign of every nonzero code follows its element
+            nz = mags > 0
+            assert np.array_equal(np.signbit(table[codes][nz]), np.signbit(xf[rs, c][nz]))
+
+
+def test_columnwise_blocks_are_independent(oracle_lib):
+    rows, cols = 260, 9
+    xb = synth.random_bf16_bits((rows, cols), 8, "pin/colwise-ind") & np.uint16(0x7FFF)
+    xb[xb >= 0x7F80] = 0x4000
+    qt, si = oracle.quantize_columnwise_t(xb, E4M3, FP32)
+    # every 128x1 block quantized on its own (as a 1-column matrix) gives the same codes/scale
+    for c in range(cols):
+        for rb in range(3):
+            r0, r1 = 128 * rb, min(128 * rb + 128, rows)
+            qb, sb = oracle.quantize_columnwise_t(np.ascontiguousarray(xb[r0:r1, c:c + 1]), E4M3, FP32)
+            assert np.array_equal(qb[0], qt[c, r0:r1])
+            assert sb.shape == (1, 1) and sb[0, 0] == si[c, rb]
+    # changing one column leaves the others untouched
+    xb2 = xb.copy()
+    xb2[:, 4] = 0x3F80
+    qt2, si2 = oracle.quantize_columnwise_t(xb2, E4M3, FP32)
+    keep = [c for c in range(cols) if c != 4]
+    assert np.array_equal(qt2[keep], qt[keep]) and np.array_equal(si2[keep], si[keep])
