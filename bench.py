@@ -18,7 +18,8 @@ four layers), on the host's cores.
 
 Other workloads (--workload): llama8b-fprop-pow2 (the same step with power-of-2 scales, the
 GEMM applying them as E8M0 block scales in the MFMA), quant-sweep (HBM-bound quantizer), moe
-(grouped GEMM; --pow2 for power-of-2 scales), backward (delayed-scaled dgrad / wgrad), copy
+(grouped GEMM; --pow2 for power-of-2 scales), backward (delayed-scaled dgrad / wgrad),
+backward-blockwise (dgrad + blockwise wgrad on columnwise-quantized operands; --pow2), copy
 (counter calibration).  Each prints one JSON line.
 """
 from __future__ import annotations
@@ -56,9 +57,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b-fprop",
                     choices=["llama8b-fprop", "llama8b-fprop-pow2", "quant-sweep", "moe", "backward",
-                             "copy"])
+                             "backward-blockwise", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pow2", action="store_true", help="moe: power-of-2 scales (E8M0 in the MFMA)")
+    ap.add_argument("--pow2", action="store_true",
+                    help="moe, backward-blockwise: power-of-2 scales (E8M0 in the MFMA)")
     ap.add_argument("--tokens", type=int, default=8192)
     return ap.parse_args()
 
@@ -463,6 +465,88 @@ def bench_backward(args):
                 roofline=None)
 
 
+def bench_backward_blockwise(args):
+    """8B-shaped backward linear layers in the block recipe ("NVIDIA NeMo RL ...", section "El
+    avance técnico"; E4M3 gradients).  Per layer and step: dY quantized 1x128 along out-features
+    (dgrad operand) and columnwise over tokens (wgrad operand, transposed), X quantized columnwise
+    over tokens (transposed), W re-quantized 128x128; dgrad dX = dY . W (128x128 weight tiles),
+    wgrad dW = dY^T . X (1x128 scales on both operands).  --pow2: power-of-2 scales everywhere."""
+    import block_scaled_quantize_amd as bsq
+    import synth
+    bsq.load()
+    dev = torch.device("cuda", 0)
+    M = args.tokens
+    mode = bsq.SCALE_POW2 if args.pow2 else bsq.SCALE_FP32
+    E4, B1, B128 = bsq.E4M3, bsq.BLOCK_1x128, bsq.BLOCK_128x128
+    layers = []
+    for name, k, n in LAYERS_8B:
+        layers.append(dict(
+            name=name, K=k, N=n,
+            x=synth.activations_with_outliers(M, k, 0, f"bench/bwdb/{name}/X").to(dev),
+            w=synth.normal((n, k), 0.02, 0, f"bench/bwdb/{name}/W").to(dev),
+            dy=synth.normal((M, n), 1e-3, 0, f"bench/bwdb/{name}/dY").to(dev),
+            dx=torch.empty((M, k), dtype=torch.bfloat16, device=dev),
+            dw=torch.empty((n, k), dtype=torch.bfloat16, device=dev)))
+    torch.cuda.synchronize()
+    flops = sum(4.0 * M * L["N"] * L["K"] for L in layers)
+    timer = EventTimer()
+
+    def step(t=None):
+        def run(key, fn):
+            return fn() if t is None else t.time((key, L["name"]), fn)
+        for L in layers:
+            qdy, sdy = run("q_dy", lambda: bsq.quantize_blockwise(L["dy"], E4, B1, mode))
+            qw, sw = run("q_w", lambda: bsq.quantize_blockwise(L["w"], E4, B128, mode))
+            dyt, sdyt = run("q_dyT", lambda: bsq.quantize_columnwise_t(L["dy"], E4, mode))
+            xt, sxt = run("q_xT", lambda: bsq.quantize_columnwise_t(L["x"], E4, mode))
+            run("dgrad", lambda: bsq.gemm_blockscaled(bsq.DGRAD, qdy, E4, B1, sdy, qw, E4, B128, sw,
+                                                      c=L["dx"], pow2=args.pow2))
+            run("wgrad", lambda: bsq.gemm_blockscaled(bsq.FPROP, dyt, E4, B1, sdyt, xt, E4, B1, sxt,
+                                                      c=L["dw"], pow2=args.pow2))
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    for _ in range(max(3, min(args.steps, 10))):
+        step(timer)
+    torch.cuda.synchronize()
+    per = {}
+    for L in layers:
+        f = 2.0 * M * L["N"] * L["K"]
+        d = {}
+        for key in ("dgrad", "wgrad"):
+            ms = timer.mean_ms((key, L["name"]))
+            d[f"{key}_us"] = round(ms * 1e3, 2)
+            d[f"{key}_tflops"] = round(f / ms / 1e9, 1)
+        for key, byts in (("q_dyT", 3.0 * M * L["N"]), ("q_xT", 3.0 * M * L["K"])):
+            ms = timer.mean_ms((key, L["name"]))
+            d[f"{key}_us"] = round(ms * 1e3, 2)
+            d[f"{key}_gbps"] = round(byts / ms / 1e6, 1)
+        per[L["name"]] = d
+    wg_ms = [timer.mean_ms(("wgrad", L["name"])) for L in layers]
+    wg_f = [2.0 * M * L["N"] * L["K"] for L in layers]
+    achieved = float(np.mean(wg_f)) / float(np.mean(wg_ms)) / 1e9
+    return dict(metric="block-scaled FP8 GEMM TFLOP/s, backward (dgrad + blockwise wgrad)",
+                value=round(flops / dt / 1e12, 2), unit="TFLOP/s", n_gpus=1, steps=args.steps,
+                warmup=args.warmup, ms_per_step=round(dt * 1e3, 4), higher_is_better=True,
+                scaling="weak", vs_baseline=None, dtype="fp8e4m3 x fp8e4m3 -> fp32 acc -> bf16",
+                data="synthetic",
+                config=dict(workload="llama3.1-8b-backward-blockwise" + ("-pow2" if args.pow2 else ""),
+                            tokens=M, scaling="dY 1x128 (dgrad), dY^T and X^T columnwise 128x1 "
+                            "(wgrad), W 128x128"),
+                roofline=dict(bound="mfma", achieved=round(achieved, 1), peak=FP8_PEAK_TFLOPS,
+                              unit="TFLOP/s", frac=round(achieved / FP8_PEAK_TFLOPS, 4),
+                              traffic=None,
+                              kernel="gemm_kernel<Cfg<256,256,2,4>,FPROP,E4M3,E4M3,%s> (wgrad)"
+                                     % ("hw-rows" if args.pow2 else "fold-rows"),
+                              mean_launch_us=round(float(np.mean(wg_ms)) * 1e3, 2)),
+                layers=per)
+
+
 def bench_copy(args):
     """A plain 1 GiB device copy (torch), the calibration kernel for the HBM byte counters."""
     dev = torch.device("cuda", 0)
@@ -508,6 +592,8 @@ def main():
         res = bench_moe(args)
     elif args.workload == "backward":
         res = bench_backward(args)
+    elif args.workload == "backward-blockwise":
+        res = bench_backward_blockwise(args)
     elif args.workload == "copy":
         res = bench_copy(args)
     else:

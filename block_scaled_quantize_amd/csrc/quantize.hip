@@ -76,8 +76,8 @@ __device__ __forceinline__ uint4 encode_block_values(const uint32_t (&d)[8], flo
 // each); each thread handles kRowsPerThread row blocks kRows1/kRowsPerThread rows apart.
 // Scales go to scale_inv[colblock][row]: the tile's kRows1 scales are contiguous.  The 1-D
 // grid runs column blocks fastest, so workgroups in flight together stream contiguous rows.
-constexpr int kRowsPerThread = 2;
-constexpr int kRows1 = (kThreads / 8) * kRowsPerThread;  // 64
+constexpr int kRowsPerThread = 1;
+constexpr int kRows1 = (kThreads / 8) * kRowsPerThread;  // 32
 
 template <int FMT, bool POW2, bool VEC>
 __global__ __launch_bounds__(kThreads) void quant_1x128_kernel(

@@ -13,10 +13,12 @@
 //
 // Design (HBM-bound, one pass): a workgroup of 256 lanes takes a 128-row x 128-column tile;
 // lane (row group g, column chunk c) loads rows 8g .. 8g+7 of columns 8c .. 8c+7 with 16-byte
-// loads, so each lane ends with 8 codes of 8 consecutive rows per column: one 8-byte store per
-// column into the transposed matrix.  The column maxima are reduced over the lane's 8 rows in
-// registers (packed 16-bit max of magnitude bits), across the 4 row groups of a wave by lane
-// shuffles and across the 4 waves through 1 KiB of LDS.
+// loads, so each lane ends with the 8 codes of 8 consecutive rows per column.  The column
+// maxima are reduced over the lane's 8 rows in registers (packed 16-bit max of magnitude bits),
+// across the 4 row groups of a wave by lane shuffles and across the 4 waves through 1 KiB of
+// LDS.  The codes are staged in LDS as [column][row] (column pitch 136 bytes, so the 8-byte
+// writes of a wave spread over the banks) and leave as whole 128-byte rows of the transposed
+// matrix, 16 bytes per lane.
 #include <float.h>
 
 #include "common.h"
@@ -101,10 +103,9 @@ __global__ __launch_bounds__(kThreadsT) void quant_128x1_t_kernel(
     finite = finite && a < 0x7F80u;
   }
 
-  // Encode column by column: the 8 codes of column c0 + j are rows r0 .. r0 + 7 of the
-  // transposed matrix.  Columns of a block holding NaN/Inf (s = 1) take the clamped path with
-  // NaN codes patched; for finite blocks the clamp is a no-op.
-  const bool vec_rows = VEC && r0 + 8 <= rows;
+  // Encode column by column into an LDS tile [128 columns][128 rows] (column pitch 136 bytes),
+  // then write whole 128-byte column rows of the transposed matrix, 16 bytes per lane.
+  __shared__ __attribute__((aligned(16))) uint8_t s_t[128 * 136];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int p = j >> 1;
@@ -130,16 +131,26 @@ __global__ __launch_bounds__(kThreadsT) void quant_128x1_t_kernel(
         }
       }
     }
-    const int64_t c = c0 + j;
-    if (c < cols && r0 < rows) {
-      uint8_t* dst = qt + c * ld_qt + r0;
-      if (vec_rows) {
-        *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
-      } else {
+    *reinterpret_cast<uint2*>(s_t + (8 * cg + j) * 136 + 8 * rg) = make_uint2(lo, hi);
+  }
+  __syncthreads();
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-          if (r0 + k < rows) dst[k] = (uint8_t)(((k < 4) ? lo : hi) >> (8 * (k & 3)));
-      }
+  for (int u = 0; u < 4; ++u) {
+    const int col = (t >> 3) + 32 * u, chunk = t & 7;
+    const int64_t c = cb * 128 + col;
+    const int64_t r = rb * 128 + 16 * chunk;
+    if (c >= cols || r >= rows) continue;
+    const uint8_t* src = s_t + col * 136 + 16 * chunk;
+    const uint2 a = *reinterpret_cast<const uint2*>(src);
+    const uint2 b = *reinterpret_cast<const uint2*>(src + 8);
+    uint8_t* dst = qt + c * ld_qt + r;
+    if (VEC && r + 16 <= rows) {
+      *reinterpret_cast<uint4*>(dst) = make_uint4(a.x, a.y, b.x, b.y);
+    } else {
+      const uint32_t w4[4] = {a.x, a.y, b.x, b.y};
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if (r + k < rows) dst[k] = (uint8_t)(w4[k >> 2] >> (8 * (k & 3)));
     }
   }
   if (rg == 0) {
@@ -176,8 +187,7 @@ extern "C" int fp8_quantize_columnwise_t(const void* x_bf16, int64_t rows, int64
   if (ceil_div(rows, 128) * ceil_div(cols, 128) > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
   if (rows > INT64_MAX / ld_x || cols > INT64_MAX / ld_qt) return FP8BS_ERR_SHAPE;
   if (!aligned4(scale_inv_out)) return FP8BS_ERR_ALIGN;
-  const bool vec = aligned16(x_bf16) && (reinterpret_cast<uintptr_t>(qt_out) & 7u) == 0 &&
-                   ld_x % 8 == 0 && ld_qt % 8 == 0;
+  const bool vec = aligned16(x_bf16) && aligned16(qt_out) && ld_x % 8 == 0 && ld_qt % 16 == 0;
   const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
   uint8_t* qt = static_cast<uint8_t*>(qt_out);
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -109,8 +109,8 @@ int fp8_quantize_blockwise(const void* x_bf16, int64_t rows, int64_t cols, int64
  *   scale_inv_out: float[ceil(rows/128)][cols] -- the 1x128 scale layout of the transposed
  *                  matrix, as the GEMM reads it for a K-major operand with 1x128 blocks.
  * rows == 0 or cols == 0 is a no-op.  Requirements: ld_x >= cols, ld_qt >= rows.  16-byte
- * aligned input rows with 8-byte aligned output rows (ld_x % 8 == 0, ld_qt % 8 == 0, aligned
- * bases) take the vectorized path.  Caller-owned device buffers; nothing is allocated.
+ * aligned input and output rows (ld_x % 8 == 0, ld_qt % 16 == 0, aligned bases) take the
+ * vectorized path.  Caller-owned device buffers; nothing is allocated.
  * Errors: FP8BS_ERR_NULL, FP8BS_ERR_SHAPE, FP8BS_ERR_ALIGN (scale_inv_out not 4-byte
  * aligned), FP8BS_ERR_ARG, FP8BS_ERR_LAUNCH.
  */
