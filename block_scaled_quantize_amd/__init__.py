@@ -70,10 +70,13 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.fp8_grouped_gemm.argtypes = [ctypes.c_int32, vp, i64, i64, i64, vp, i64, i32, vp, vp,
                                      i64, i32, vp, vp, i64, vp]
     lib.fp8_gemm_blockscaled_pow2.argtypes = lib.fp8_gemm_blockscaled.argtypes
+    lib.fp8_gemm_blockscaled_qout.argtypes = [i64, i64, i64, vp, i64, i32, vp, vp, i64, i32, vp,
+                                              i32, vp, i64, i32, vp, i64, vp, vp]
     lib.fp8_grouped_gemm_pow2.argtypes = lib.fp8_grouped_gemm.argtypes
     for name in ("fp8_quantize_blockwise", "fp8_quantize_columnwise_t", "fp8_quantize_delayed",
                  "fp8_cast_fp32",
                  "fp8_gemm_blockscaled", "fp8_grouped_gemm", "fp8_gemm_blockscaled_pow2",
+                 "fp8_gemm_blockscaled_qout",
                  "fp8_grouped_gemm_pow2"):
         getattr(lib, name).restype = i32
     _lib = lib
@@ -92,6 +95,12 @@ def _check(rc: int, what: str) -> None:
 def _stream(stream=None) -> int:
     s = stream if stream is not None else torch.cuda.current_stream()
     return s.cuda_stream
+
+
+def _bf16_out(rows: int, cols: int, device) -> torch.Tensor:
+    """A bf16 output matrix whose row pitch is even (the GEMM's 4-byte store alignment)."""
+    ld = cols + (cols & 1)
+    return torch.empty((rows, ld), dtype=torch.bfloat16, device=device)[:, :cols]
 
 
 def _ptr(t: torch.Tensor | None) -> int | None:
@@ -226,12 +235,40 @@ def gemm_blockscaled(layout: int, a: torch.Tensor, fa: int, ga: int, sa: torch.T
     else:
         raise ValueError("unknown layout")
     if c is None:
-        c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+        c = _bf16_out(M, N, a.device)
     name = "fp8_gemm_blockscaled_pow2" if pow2 else "fp8_gemm_blockscaled"
     _check(getattr(load(), name)(layout, M, N, K, _ptr(a), a.stride(0), fa, ga, _ptr(sa),
                                  _ptr(b), b.stride(0), fb, gb, _ptr(sb), _ptr(c),
                                  c.stride(0), _stream(stream)), name)
     return c
+
+
+def gemm_blockscaled_qout(a: torch.Tensor, ga: int, sa: torch.Tensor, b: torch.Tensor, gb: int,
+                          sb: torch.Tensor, mode_out: int = SCALE_FP32, pow2_inputs: bool = False,
+                          want_bf16: bool = True, c: torch.Tensor | None = None,
+                          cq: torch.Tensor | None = None, cqs: torch.Tensor | None = None,
+                          stream=None):
+    """fprop GEMM (a[M,K] . b[N,K]^T, E4M3 codes) whose epilogue also quantizes the bf16 output
+    in 1x128 blocks (E4M3).  Returns (c bf16 [M,N] or None, cq uint8 [M,N],
+    cqs float32 [ceil(N/128), M])."""
+    if a.dtype != torch.uint8 or b.dtype != torch.uint8 or a.dim() != 2 or b.dim() != 2:
+        raise ValueError("a and b must be 2-D uint8 code matrices")
+    (M, K), N = a.shape, b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("K mismatch")
+    if c is None and want_bf16:
+        c = _bf16_out(M, N, a.device)
+    if cq is None:
+        cq = torch.empty((M, N), dtype=torch.uint8, device=a.device)
+    if cqs is None:
+        cqs = torch.empty(((N + 127) // 128, M), dtype=torch.float32, device=a.device)
+    _check(load().fp8_gemm_blockscaled_qout(M, N, K, _ptr(a), a.stride(0), ga, _ptr(sa), _ptr(b),
+                                            b.stride(0), gb, _ptr(sb), int(pow2_inputs),
+                                            _ptr(c) if c is not None else None,
+                                            c.stride(0) if c is not None else 0, mode_out,
+                                            _ptr(cq), cq.stride(0), _ptr(cqs), _stream(stream)),
+           "fp8_gemm_blockscaled_qout")
+    return c, cq, cqs
 
 
 def grouped_gemm(offsets: torch.Tensor, a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor,
@@ -245,7 +282,7 @@ def grouped_gemm(offsets: torch.Tensor, a: torch.Tensor, sa: torch.Tensor, b: to
     G, N, K = b.shape
     total_m = a.shape[0]
     if c is None:
-        c = torch.empty((total_m, N), dtype=torch.bfloat16, device=a.device)
+        c = _bf16_out(total_m, N, a.device)
     name = "fp8_grouped_gemm_pow2" if pow2 else "fp8_grouped_gemm"
     _check(getattr(load(), name)(G, _ptr(offsets), total_m, N, K, _ptr(a), a.stride(0), fa,
                                  _ptr(sa), _ptr(b), b.stride(1), fb, _ptr(sb), _ptr(c),

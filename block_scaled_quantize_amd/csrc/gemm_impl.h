@@ -109,10 +109,16 @@ struct GemmParams {
   int sa_rdiv;
   const float* sb;    // sb(n, kb) = sb[kb * sb_ks + (n / 128) * sb_rs]
   int64_t sb_ks, sb_rs, sb_bytes;
-  uint16_t* C;
+  uint16_t* C;        // may be null when the output is only wanted quantized
   int64_t ldc;
   int tiles_m, tiles_n;
   int c_vec;          // 8-byte output stores are aligned
+  // fused output quantization (1x128 blocks along N): codes Cq[M, N] (pitch ldcq) and
+  // dequantization factors cqs[ceil(N/128)][M]
+  uint8_t* Cq;
+  int64_t ldcq;
+  float* cqs;
+  int cq_vec;         // 4-byte code stores are aligned
   // grouped GEMM only
   const int64_t* offsets;
   int num_groups;
@@ -269,7 +275,90 @@ __device__ __forceinline__ int e8m0_of(float s) {
   return (int)((__builtin_bit_cast(uint32_t, s) >> 23) & 0xFF);
 }
 
-template <class C, int LAYOUT, int FA, int FB, int SM>
+// Fused output quantization: the tile's bf16 output values (exactly those the epilogue stores)
+// quantized in 1x128 blocks along N -- the blockwise quantizer's rule applied to the bf16
+// output, so the codes and scales equal those of quantizing the stored bf16 matrix.  A 128-column
+// block of a row spans the 64-column ranges of two waves (wn even / odd): each lane reduces its
+// values, the 4 lanes of a row reduce by shuffles, the two waves meet in LDS.
+template <class C, int SM, int QO, class Acc>
+__device__ __forceinline__ void quantize_out(const GemmParams& p, uint8_t* smem, const Acc& acc,
+                                             float post, int nkb, int64_t m0, int64_t m_end,
+                                             int64_t n0) {
+  constexpr int QF = (QO - 1) >> 1;
+  constexpr bool QP = ((QO - 1) & 1) != 0;
+  constexpr int NI = C::kNI, NJ = C::kNJ, BM = C::BM;
+  static_assert(C::kWTN == 64 && C::BN % 128 == 0, "a 128-column block spans two waves");
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int wm = w % C::kWavesM, wn = w / C::kWavesM;
+  const int li = lane & 15, g = lane >> 4;
+  // bf16 values of the lane: bv[i][j] = (v0, v1), (v2, v3)
+  uint32_t bv[NI][NJ][2];
+  uint32_t amax[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    u16x2 mx = {0, 0};
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      v4f v = acc[i][j];
+      if constexpr (SM == kScaleTensor) v = v * post;   // as the bf16 epilogue does
+      if (nkb == 0) v = v4f{0.f, 0.f, 0.f, 0.f};
+      bv[i][j][0] = pack_bf16x2(v[0], v[1]);
+      bv[i][j][1] = pack_bf16x2(v[2], v[3]);
+      mx = max2(mx, max2(mag2(bv[i][j][0]), mag2(bv[i][j][1])));
+    }
+    uint32_t a = hmax(mx);
+    a = max(a, (uint32_t)__shfl_xor((int)a, 16));
+    a = max(a, (uint32_t)__shfl_xor((int)a, 32));
+    amax[j] = a;
+  }
+  // every wave is past its last read of the operand stages: reuse them for the exchange
+  __syncthreads();
+  uint32_t* s_amax = reinterpret_cast<uint32_t*>(smem);   // [waves along n][BM]
+  if (g == 0) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) s_amax[wn * BM + wm * C::kWTM + 16 * j + li] = amax[j];
+  }
+  __syncthreads();
+  const int64_t blk = (n0 >> 7) + (wn >> 1);   // 128-column block of this wave
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int row = wm * C::kWTM + 16 * j + li;
+    const int64_t m = m0 + row;
+    const uint32_t a = max(s_amax[(wn & ~1) * BM + row], s_amax[(wn | 1) * BM + row]);
+    const float s = scale_from_amax_bits<QF, QP>(a);
+    const bool finite = a < 0x7F80u;
+    if (m >= m_end) continue;
+    uint8_t* qrow = p.Cq + m * p.ldcq;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int64_t n = n0 + wn * C::kWTN + 16 * i + 4 * g;
+      float y0 = bf16_lo(bv[i][j][0]) * s, y1 = bf16_hi(bv[i][j][0]) * s;
+      float y2 = bf16_lo(bv[i][j][1]) * s, y3 = bf16_hi(bv[i][j][1]) * s;
+      if (!finite) {
+        constexpr float F = Format<QF>::fmax;
+        y0 = __builtin_amdgcn_fmed3f(y0, -F, F);
+        y1 = __builtin_amdgcn_fmed3f(y1, -F, F);
+        y2 = __builtin_amdgcn_fmed3f(y2, -F, F);
+        y3 = __builtin_amdgcn_fmed3f(y3, -F, F);
+      }
+      uint32_t code = cvt4<QF>(y0, y1, y2, y3);
+      if (!finite) code = patch_nan_pair(patch_nan_pair(code, bv[i][j][0], 0), bv[i][j][1], 1);
+      if (p.cq_vec && n + 4 <= p.N) {
+        *reinterpret_cast<uint32_t*>(qrow + n) = code;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < p.N) qrow[n + e] = (uint8_t)(code >> (8 * e));
+      }
+    }
+    if (g == 0 && (wn & 1) == 0 && blk * 128 < p.N) p.cqs[blk * p.M + m] = 1.0f / s;
+  }
+}
+
+// QO: fused quantization of the output into 1x128 blocks along N, 0 = none, else
+// 1 + 2 * format + (power-of-2 scale ? 1 : 0).
+template <class C, int LAYOUT, int FA, int FB, int SM, int QO = 0>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, int64_t m0,
                                           int64_t m_end, int64_t n0, const uint8_t* Bw,
                                           const float* sbw, int64_t sb_bytes) {
@@ -509,29 +598,32 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
   if constexpr (SM == kScaleTensor) post = nkb > 0 ? p.sa[0] * sbw[0] : 0.0f;
 
   // Epilogue: lane holds C[m][n .. n+3] of each piece.
+  if (p.C) {
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int64_t m = m0 + wm * C::kWTM + 16 * j + li;
-    if (m >= m_end) continue;
-    uint16_t* crow = p.C + m * p.ldc;
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t m = m0 + wm * C::kWTM + 16 * j + li;
+      if (m >= m_end) continue;
+      uint16_t* crow = p.C + m * p.ldc;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int64_t n = n0 + wn * C::kWTN + 16 * i + 4 * g;
-      v4f v = acc[i][j];
-      if constexpr (SM == kScaleTensor) v = v * post;
-      if (nkb == 0) v = v4f{0.f, 0.f, 0.f, 0.f};
-      const uint32_t lo = pack_bf16x2(v[0], v[1]);
-      const uint32_t hi = pack_bf16x2(v[2], v[3]);
-      if (p.c_vec && n + 4 <= p.N) {
-        *reinterpret_cast<uint2*>(crow + n) = make_uint2(lo, hi);
-      } else {
-        const uint16_t h[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
+      for (int i = 0; i < NI; ++i) {
+        const int64_t n = n0 + wn * C::kWTN + 16 * i + 4 * g;
+        v4f v = acc[i][j];
+        if constexpr (SM == kScaleTensor) v = v * post;
+        if (nkb == 0) v = v4f{0.f, 0.f, 0.f, 0.f};
+        const uint32_t lo = pack_bf16x2(v[0], v[1]);
+        const uint32_t hi = pack_bf16x2(v[2], v[3]);
+        if (p.c_vec && n + 4 <= p.N) {
+          *reinterpret_cast<uint2*>(crow + n) = make_uint2(lo, hi);
+        } else {
+          const uint16_t h[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (n + e < p.N) crow[n + e] = h[e];
+          for (int e = 0; e < 4; ++e)
+            if (n + e < p.N) crow[n + e] = h[e];
+        }
       }
     }
   }
+  if constexpr (QO != 0) quantize_out<C, SM, QO>(p, smem, acc, post, nkb, m0, m_end, n0);
 }
 
 // Map a linear workgroup id to a tile so that each of the 8 XCDs (ids are dealt round robin)
@@ -550,13 +642,13 @@ __device__ __forceinline__ void tile_of(int id, int tiles_m, int tiles_n, int& t
   tn = in / gsz;
 }
 
-template <class C, int LAYOUT, int FA, int FB, int SM>
+template <class C, int LAYOUT, int FA, int FB, int SM, int QO = 0>
 __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int tm, tn;
   tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * C::BM;
-  gemm_tile<C, LAYOUT, FA, FB, SM>(p, smem, m0, std::min<int64_t>(m0 + C::BM, p.M),
+  gemm_tile<C, LAYOUT, FA, FB, SM, QO>(p, smem, m0, std::min<int64_t>(m0 + C::BM, p.M),
                                    (int64_t)tn * C::BN, p.B, p.sb, p.sb_bytes);
 }
 
@@ -640,12 +732,12 @@ using CfgB = Cfg<256, 128, 4, 2>;   // 8 waves, 64 x 64 per wave, 3 stages
 using CfgC = Cfg<256, 256, 2, 4>;   // 8 waves, 128 x 64 per wave, 2 stages
 using CfgD = Cfg<128, 128, 2, 2>;   // 4 waves, 64 x 64 per wave (small M, grouped)
 
-template <class C, int LAYOUT, int FA, int FB, int SM>
+template <class C, int LAYOUT, int FA, int FB, int SM, int QO = 0>
 int launch_dense(GemmParams p, hipStream_t st) {
   p.tiles_m = (int)ceil_div(p.M, C::BM);
   p.tiles_n = (int)ceil_div(p.N, C::BN);
   if ((int64_t)p.tiles_m * p.tiles_n > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
-  return launch_gemm(gemm_kernel<C, LAYOUT, FA, FB, SM>, p.tiles_m * p.tiles_n, C::kThreads,
+  return launch_gemm(gemm_kernel<C, LAYOUT, FA, FB, SM, QO>, p.tiles_m * p.tiles_n, C::kThreads,
                      C::kLds, st, p);
 }
 
@@ -660,13 +752,13 @@ char pick_variant(int64_t M, int64_t N) {
   return 'D';
 }
 
-template <int LAYOUT, int FA, int FB, int SM>
+template <int LAYOUT, int FA, int FB, int SM, int QO = 0>
 int dispatch_variant(const GemmParams& p, hipStream_t st) {
   switch (pick_variant(p.M, p.N)) {
-    case 'B': return launch_dense<CfgB, LAYOUT, FA, FB, SM>(p, st);
-    case 'C': return launch_dense<CfgC, LAYOUT, FA, FB, SM>(p, st);
-    case 'D': return launch_dense<CfgD, LAYOUT, FA, FB, SM>(p, st);
-    default: return launch_dense<CfgA, LAYOUT, FA, FB, SM>(p, st);
+    case 'B': return launch_dense<CfgB, LAYOUT, FA, FB, SM, QO>(p, st);
+    case 'C': return launch_dense<CfgC, LAYOUT, FA, FB, SM, QO>(p, st);
+    case 'D': return launch_dense<CfgD, LAYOUT, FA, FB, SM, QO>(p, st);
+    default: return launch_dense<CfgA, LAYOUT, FA, FB, SM, QO>(p, st);
   }
 }
 
@@ -755,7 +847,8 @@ int dispatch_grouped(int fa, int fb, int cus, const GemmParams& p, hipStream_t s
 inline int dense_params(int layout, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                         int fa, int ga, const float* scale_inv_a, const void* B, int64_t ldb,
                         int fb, int gb, const float* scale_inv_b, void* C_bf16, int64_t ldc,
-                        GemmParams& p, bool& tensor_only, bool& empty, bool& b_rows) {
+                        GemmParams& p, bool& tensor_only, bool& empty, bool& b_rows,
+                        bool c_optional = false) {
   empty = false;
   if (layout < FP8BS_FPROP || layout > FP8BS_WGRAD || !fmt_ok(fa) || !fmt_ok(fb) || ga < 0 ||
       ga > 2 || gb < 0 || gb > 2)
@@ -765,15 +858,16 @@ inline int dense_params(int layout, int64_t M, int64_t N, int64_t K, const void*
     empty = true;
     return FP8BS_OK;
   }
-  if (!C_bf16 || (K > 0 && (!A || !B || !scale_inv_a || !scale_inv_b))) return FP8BS_ERR_NULL;
+  if ((!C_bf16 && !c_optional) || (K > 0 && (!A || !B || !scale_inv_a || !scale_inv_b)))
+    return FP8BS_ERR_NULL;
   const bool xk = layout != FP8BS_WGRAD, wk = layout == FP8BS_FPROP;
   const int64_t a_width = xk ? K : M, b_width = wk ? K : N;
-  if (ldc < N || (K > 0 && (lda < a_width || ldb < b_width))) return FP8BS_ERR_SHAPE;
+  if ((C_bf16 && ldc < N) || (K > 0 && (lda < a_width || ldb < b_width))) return FP8BS_ERR_SHAPE;
   // 32-bit buffer offsets inside a tile: 256 rows of the pitch must stay below 2^31.
   if (lda >= (int64_t(1) << 23) || ldb >= (int64_t(1) << 23)) return FP8BS_ERR_SHAPE;
   if (M > (int64_t(1) << 31) - 256 || N > (int64_t(1) << 31) - 256) return FP8BS_ERR_SHAPE;
   if (K > 0 && (!aligned16(A) || !aligned16(B) || lda % 16 || ldb % 16)) return FP8BS_ERR_ALIGN;
-  if (!aligned4(C_bf16) || ldc % 2) return FP8BS_ERR_ALIGN;
+  if (C_bf16 && (!aligned4(C_bf16) || ldc % 2)) return FP8BS_ERR_ALIGN;
   ScaleIndex sa{}, sb{};
   if (!scale_index(ga, xk, false, M, K, sa) || !scale_index(gb, wk, true, N, K, sb))
     return FP8BS_ERR_UNSUPPORTED;

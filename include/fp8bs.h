@@ -207,6 +207,28 @@ int fp8_grouped_gemm(int32_t num_groups, const int64_t* group_offsets, int64_t t
                      const float* scale_inv_a, const void* B, int64_t ldb, int fb,
                      const float* scale_inv_b, void* C_bf16, int64_t ldc, void* stream);
 
+/* Block-scaled FP8 fprop GEMM with the output quantized in the epilogue.  [P3] "Ganancias de
+ * rendimiento en el mundo real" (the cost of separate quantization kernels) and "El avance
+ * técnico" (1x128 activation blocks, E4M3).
+ * Computes C = A . B^T (A[M,K], B[N,K], both E4M3) as fp8_gemm_blockscaled with layout
+ * FP8BS_FPROP does, and in the same kernel quantizes the bf16-rounded output in 1x128 blocks
+ * along N: Cq[M,N] (E4M3 codes, pitch ldcq bytes) and cq_scale_inv float[ceil(N/128)][M] are
+ * exactly what fp8_quantize_blockwise(C_bf16, FP8BS_E4M3, FP8BS_BLOCK_1x128, mode_out) would
+ * write -- the next layer's activation operand.
+ *   ga, gb:      as fp8_gemm_blockscaled for FPROP, except 1x128 on B (FP8BS_ERR_UNSUPPORTED).
+ *   pow2_inputs: 0 -- fp32 scales (fold); 1 -- the scales are powers of two and are applied by
+ *                the MFMA (the precondition of fp8_gemm_blockscaled_pow2).
+ *   C_bf16:      may be NULL (only the quantized output is written); else [M,N] pitch ldc.
+ *   mode_out:    FP8BS_SCALE_FP32 or FP8BS_SCALE_POW2 for the output's scales.
+ * Requirements: those of fp8_gemm_blockscaled; ldcq >= N; 4-byte aligned cq_scale_inv.
+ * Errors: FP8BS_ERR_NULL, FP8BS_ERR_SHAPE, FP8BS_ERR_ALIGN, FP8BS_ERR_UNSUPPORTED,
+ * FP8BS_ERR_ARG, FP8BS_ERR_LAUNCH. */
+int fp8_gemm_blockscaled_qout(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                              int ga, const float* scale_inv_a, const void* B, int64_t ldb,
+                              int gb, const float* scale_inv_b, int pow2_inputs, void* C_bf16,
+                              int64_t ldc, int mode_out, void* Cq, int64_t ldcq,
+                              float* cq_scale_inv, void* stream);
+
 /* Block-scaled FP8 GEMM with power-of-2 scales -- "NVIDIA NeMo RL logra una aceleración del 48%
  * ...", section "Por qué esto es importante para la economía de la IA" (the power-of-2 scale
  * option).  Same arguments, layouts, granularities, scale arrays, results and errors as

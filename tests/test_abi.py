@@ -154,6 +154,29 @@ def test_quantize_columnwise_validation():
     assert qcol(rows=0) == bsq.OK and qcol(cols=0, x=None) == bsq.OK
 
 
+def qout(**kw):
+    a = dict(M=256, N=256, K=256, A=FAKE, lda=256, ga=0, sa=FAKE, B=FAKE, ldb=256, gb=1, sb=FAKE,
+             p2=0, C=FAKE, ldc=256, mode=0, Cq=FAKE, ldcq=256, cqs=FAKE)
+    a.update(kw)
+    return bsq.load().fp8_gemm_blockscaled_qout(a["M"], a["N"], a["K"], a["A"], a["lda"], a["ga"],
+                                                a["sa"], a["B"], a["ldb"], a["gb"], a["sb"],
+                                                a["p2"], a["C"], a["ldc"], a["mode"], a["Cq"],
+                                                a["ldcq"], a["cqs"], None)
+
+
+def test_gemm_qout_validation():
+    assert qout(mode=2) == bsq.ERR_ARG
+    assert qout(p2=3) == bsq.ERR_ARG
+    assert qout(ga=5) == bsq.ERR_ARG
+    assert qout(Cq=None) == bsq.ERR_NULL
+    assert qout(cqs=None) == bsq.ERR_NULL
+    assert qout(A=None) == bsq.ERR_NULL
+    assert qout(ldcq=100) == bsq.ERR_SHAPE
+    assert qout(cqs=FAKE_ODD) == bsq.ERR_ALIGN
+    assert qout(gb=0) == bsq.ERR_UNSUPPORTED                 # 1x128 weight scales: not here
+    assert qout(M=0) == bsq.OK and qout(N=0, C=None) == bsq.OK
+
+
 def test_cast_validation():
     lib = bsq.load()
     assert lib.fp8_cast_fp32(FAKE, 16, 3, FAKE, None) == bsq.ERR_ARG
