@@ -19,7 +19,8 @@ four layers), on the host's cores.
 Other workloads (--workload): llama8b-fprop-pow2 (the same step with power-of-2 scales, the
 GEMM applying them as E8M0 block scales in the MFMA), quant-sweep (HBM-bound quantizer), moe
 (grouped GEMM; --pow2 for power-of-2 scales), backward (delayed-scaled dgrad / wgrad),
-backward-blockwise (dgrad + blockwise wgrad on columnwise-quantized operands; --pow2), copy
+backward-blockwise (dgrad + blockwise wgrad on columnwise-quantized operands; --pow2),
+llama8b-fprop-qout (the GEMM quantizing its own output against GEMM + quantizer), copy
 (counter calibration).  Each prints one JSON line.
 """
 from __future__ import annotations
@@ -57,7 +58,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b-fprop",
                     choices=["llama8b-fprop", "llama8b-fprop-pow2", "quant-sweep", "moe", "backward",
-                             "backward-blockwise", "copy"])
+                             "backward-blockwise", "llama8b-fprop-qout", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pow2", action="store_true",
                     help="moe, backward-blockwise: power-of-2 scales (E8M0 in the MFMA)")
@@ -547,6 +548,74 @@ def bench_backward_blockwise(args):
                 layers=per)
 
 
+def bench_fprop_qout(args):
+    """The 8B fprop layers with the output quantized in the GEMM epilogue (the next layer's 1x128
+    E4M3 operand), against the same GEMM followed by the separate quantizer.  Per layer and step:
+    the fused call writes bf16 + codes + scales; timed per launch with HIP events.  value = GEMM
+    flops / time of the fused launches."""
+    import block_scaled_quantize_amd as bsq
+    import synth
+    bsq.load()
+    dev = torch.device("cuda", 0)
+    M = args.tokens
+    E4, B1, B128 = bsq.E4M3, bsq.BLOCK_1x128, bsq.BLOCK_128x128
+    layers = []
+    for name, k, n in LAYERS_8B:
+        x = synth.activations_with_outliers(M, k, 0, f"bench/8b/{name}/X").to(dev)
+        w = synth.normal((n, k), 0.02, 0, f"bench/8b/{name}/W").to(dev)
+        qx, sx = bsq.quantize_blockwise(x, E4, B1)
+        qw, sw = bsq.quantize_blockwise(w, E4, B128)
+        layers.append(dict(name=name, K=k, N=n, qx=qx, sx=sx, qw=qw, sw=sw,
+                           y=torch.empty((M, n), dtype=torch.bfloat16, device=dev),
+                           yq=torch.empty((M, n), dtype=torch.uint8, device=dev),
+                           ys=torch.empty((n // 128, M), dtype=torch.float32, device=dev)))
+        del x, w
+    torch.cuda.synchronize()
+    timer = EventTimer()
+
+    def fused(L, bf16=True):
+        bsq.gemm_blockscaled_qout(L["qx"], B1, L["sx"], L["qw"], B128, L["sw"], want_bf16=bf16,
+                                  c=L["y"] if bf16 else None, cq=L["yq"], cqs=L["ys"])
+
+    def separate(L):
+        bsq.gemm_blockscaled(bsq.FPROP, L["qx"], E4, B1, L["sx"], L["qw"], E4, B128, L["sw"], c=L["y"])
+        bsq.quantize_blockwise(L["y"], E4, B1, q=L["yq"], scale_inv=L["ys"])
+
+    for _ in range(args.warmup):
+        for L in layers:
+            fused(L)
+            separate(L)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        for L in layers:
+            timer.time(("fused", L["name"]), lambda: fused(L))
+            timer.time(("codes_only", L["name"]), lambda: fused(L, False))
+            timer.time(("separate", L["name"]), lambda: separate(L))
+    torch.cuda.synchronize()
+    per, tot_f, tot_ms = {}, 0.0, 0.0
+    for L in layers:
+        f = 2.0 * M * L["N"] * L["K"]
+        d = {k + "_us": round(timer.mean_ms((k, L["name"])) * 1e3, 2)
+             for k in ("fused", "codes_only", "separate")}
+        d["fused_tflops"] = round(f / timer.mean_ms(("fused", L["name"])) / 1e9, 1)
+        per[L["name"]] = d
+        tot_f += f
+        tot_ms += timer.mean_ms(("fused", L["name"]))
+    sep_ms = sum(timer.mean_ms(("separate", L["name"])) for L in layers)
+    return dict(metric="block-scaled FP8 GEMM TFLOP/s with the output quantized in the epilogue",
+                value=round(tot_f / tot_ms / 1e9, 1), unit="TFLOP/s", n_gpus=1, steps=args.steps,
+                warmup=args.warmup, ms_per_step=round(tot_ms, 4), higher_is_better=True,
+                scaling="weak", vs_baseline=None, dtype="fp8e4m3 x fp8e4m3 -> fp32 acc -> bf16 + e4m3",
+                data="synthetic",
+                config=dict(workload="llama3.1-8b-fprop-qout", tokens=M,
+                            output="bf16 + E4M3 codes + 1x128 scales (fused) vs GEMM then quantizer"),
+                roofline=dict(bound="mfma", achieved=round(tot_f / tot_ms / 1e9, 1),
+                              peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
+                              frac=round(tot_f / tot_ms / 1e9 / FP8_PEAK_TFLOPS, 4), traffic=None,
+                              kernel="gemm_kernel<Cfg<256,256,2,4>,FPROP,E4M3,E4M3,fold,qout>"),
+                speedup_vs_separate=round(sep_ms / tot_ms, 4), layers=per)
+
+
 def bench_copy(args):
     """A plain 1 GiB device copy (torch), the calibration kernel for the HBM byte counters."""
     dev = torch.device("cuda", 0)
@@ -594,6 +663,8 @@ def main():
         res = bench_backward(args)
     elif args.workload == "backward-blockwise":
         res = bench_backward_blockwise(args)
+    elif args.workload == "llama8b-fprop-qout":
+        res = bench_fprop_qout(args)
     elif args.workload == "copy":
         res = bench_copy(args)
     else:
