@@ -39,6 +39,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -82,8 +83,10 @@ struct Cfg {
   static constexpr int kSbWords = BN;   // one weight scale per tile column at most (1x128)
   static constexpr int kSaBytes = (BM + kSbWords) * 4;  // BM activation scales, weight scales
   static constexpr int kStage = kXBytes + kWBytes + kSaBytes;
-  static constexpr int kStages = 3 * kStage <= kLdsBytes ? 3 : 2;
-  static constexpr int kLds = kStage * kStages;
+  static constexpr int kDummyBytes = 256;   // target of the scale DMAs of non-loading waves
+  static constexpr int kStages = 3 * kStage + kDummyBytes <= kLdsBytes ? 3 : 2;
+  static constexpr int kDummy = kStage * kStages;   // offset of the dummy slot
+  static constexpr int kLds = kDummy + kDummyBytes;
   static constexpr int kXLoads = BM / 8 / kWaves;   // 1 KB DMA blocks of the X tile per wave
   static constexpr int kWLoads = BN / 8 / kWaves;   // ... of the W tile per wave
   static constexpr int kSaWaves = BM / 64;          // waves that load 64 scale words each
@@ -95,7 +98,7 @@ struct Cfg {
   static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "DMA split");
   static_assert(kSaWaves <= kWaves, "scale loaders");
   static_assert(kWTN <= 128 && 128 % kWTN == 0, "a wave's n range lies in one 128 block");
-  static_assert(2 * kStage <= kLdsBytes, "LDS");
+  static_assert(2 * kStage + kDummyBytes <= kLdsBytes, "LDS");
 };
 
 struct GemmParams {
@@ -261,6 +264,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Wait until every LDS access of this wave has completed.
+__device__ __forceinline__ void wait_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14));   // lgkmcnt 0, others unchanged
+  asm volatile("" ::: "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm_upto(int n) {
   // n is wave-uniform and in {N, N+1, N+2}
@@ -410,8 +420,26 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
   const int64_t a_rows = XK ? m_end : K;
   const int64_t w_rows = WK ? p.N : K;
 
-  auto issue = [&](int kb) {
-    const uint32_t sbase = lds0 + (kb % C::kStages) * C::kStage;
+  // DMA instructions per K block issued by each wave (vmcnt is counted per wave).
+  constexpr int kPerStage = C::kXLoads + C::kWLoads + (STAGED ? 2 : 0);
+  // A block's DMA starts as soon as its slot is free, right after the barrier that ends the
+  // slot's previous block: one instruction after each MFMA unit of the last piece before the
+  // hand-over, the rest one per MFMA unit at the start of the next block.  (A burst would leave
+  // waves waiting to issue while the CU's address unit drains it; a later start lands later.)
+  // With 1x128 weight scales the fold doubles its VALU work per MFMA, and issuing the whole
+  // block after the hand-over piece's MFMAs measured faster.
+  constexpr bool kBurst = ROWS;
+  static_assert(kPerStage - NI <= (NJ - 1) * NI, "every DMA part precedes the next turn");
+  // DMA of one K block: the buffer descriptors (empty for blocks past the last: they read
+  // zeros into a slot no block reads) and the LDS stage; dma_part(d, q) issues this wave's q-th
+  // DMA instruction of the block (compile-time q once the callers' loops are unrolled).
+  struct BlockDma {
+    u32x4 x, w, sa, sb;
+    uint32_t sbase;
+  };
+  auto block_dma = [&](int kb) {
+    BlockDma d;
+    d.sbase = lds0 + (kb % C::kStages) * C::kStage;
     const int64_t k0 = (int64_t)kb * 128;
     {
       const uint8_t* base;
@@ -423,10 +451,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
         base = p.A + k0 * p.lda + m0;
         avail = (a_rows - k0) * p.lda - m0;
       }
-      const u32x4 r = make_rsrc(base, avail > 0 ? (uint64_t)avail : 0);
-#pragma unroll
-      for (int q = 0; q < C::kXLoads; ++q)
-        dma16(r, xoff[q], __builtin_amdgcn_readfirstlane(sbase + (w * C::kXLoads + q) * 1024));
+      d.x = make_rsrc(base, (avail > 0 && kb < nkb) ? (uint64_t)avail : 0);
     }
     {
       const uint8_t* base;
@@ -438,32 +463,43 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
         base = Bw + k0 * p.ldb + n0;
         avail = (w_rows - k0) * p.ldb - n0;
       }
-      const u32x4 r = make_rsrc(base, avail > 0 ? (uint64_t)avail : 0);
-#pragma unroll
-      for (int q = 0; q < C::kWLoads; ++q)
-        dma16(r, woff[q], __builtin_amdgcn_readfirstlane(sbase + C::kXBytes + (w * C::kWLoads + q) * 1024));
+      d.w = make_rsrc(base, (avail > 0 && kb < nkb) ? (uint64_t)avail : 0);
     }
-    // Scales of the K block: one activation word per tile row, then one weight word per
-    // 128-column block of the tile (lanes past those read outside the descriptor: zeros).
     if constexpr (STAGED) {
-      if (sa_loader) {
-        const int64_t off = kb * p.sa_ks;
-        const u32x4 r = make_rsrc(p.sa + off, (uint64_t)(p.sa_bytes - off * 4));
-        dma4(r, saoff, __builtin_amdgcn_readfirstlane(sbase + C::kXBytes + C::kWBytes + w * 256));
-      }
-      if (sb_loader) {
-        const int64_t off = kb * p.sb_ks;
-        const u32x4 r = make_rsrc(sbw + off, (uint64_t)(sb_bytes - off * 4));
-        const uint32_t dst = sbase + C::kXBytes + C::kWBytes + BM * 4 +
-                             (ROWS ? (w - C::kSbRowWave0) * 256 : 0);
-        dma4(r, sboff, __builtin_amdgcn_readfirstlane(dst));
-      }
+      const int64_t offa = kb * p.sa_ks, lefta = p.sa_bytes - offa * 4;
+      d.sa = make_rsrc(p.sa + offa, (lefta > 0 && kb < nkb) ? (uint64_t)lefta : 0);
+      const int64_t offb = kb * p.sb_ks, leftb = sb_bytes - offb * 4;
+      d.sb = make_rsrc(sbw + offb, (leftb > 0 && kb < nkb) ? (uint64_t)leftb : 0);
+    }
+    return d;
+  };
+  auto dma_part = [&](const BlockDma& d, int q) {
+    if (q < C::kXLoads) {
+      dma16(d.x, xoff[q], __builtin_amdgcn_readfirstlane(d.sbase + (w * C::kXLoads + q) * 1024));
+    } else if (q < C::kXLoads + C::kWLoads) {
+      const int qw = q - C::kXLoads;
+      dma16(d.w, woff[qw],
+            __builtin_amdgcn_readfirstlane(d.sbase + C::kXBytes + (w * C::kWLoads + qw) * 1024));
+    } else if (q == C::kXLoads + C::kWLoads) {
+      // Scales of the K block: one activation word per tile row, then one weight word per
+      // 128-column block of the tile (lanes past those read outside the descriptor: zeros).
+      // Every wave issues both scale DMAs, so that the block needs no branch: a wave that
+      // loads no scale reads outside the descriptor into the dummy slot.
+      dma4(d.sa, sa_loader ? saoff : 0xFFFFFFFFu,
+           __builtin_amdgcn_readfirstlane(sa_loader ? d.sbase + C::kXBytes + C::kWBytes + w * 256
+                                                    : lds0 + C::kDummy));
+    } else {
+      const uint32_t dst = d.sbase + C::kXBytes + C::kWBytes + BM * 4 +
+                           (ROWS ? (w - C::kSbRowWave0) * 256 : 0);
+      dma4(d.sb, sb_loader ? sboff : 0xFFFFFFFFu,
+           __builtin_amdgcn_readfirstlane(sb_loader ? dst : lds0 + C::kDummy));
     }
   };
-  // DMA instructions per K block issued by this wave (vmcnt is counted per wave).
-  constexpr int kPerStage = C::kXLoads + C::kWLoads;
-  const int per_stage =
-      kPerStage + ((STAGED && sa_loader) ? 1 : 0) + ((STAGED && sb_loader) ? 1 : 0);
+  auto issue = [&](int kb) {
+    const BlockDma d = block_dma(kb);
+#pragma unroll
+    for (int q = 0; q < kPerStage; ++q) dma_part(d, q);
+  };
 
   v4f acc[NI][NJ];
 #pragma unroll
@@ -471,15 +507,18 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // Pipeline.  Stages hold K blocks kb .. kb + kStages - 1.
-  auto wait_next = [&](int next) {
-    // stage `next` must be complete; stage next + 1 may still be in flight (3 stages)
-    if constexpr (C::kStages == 3) {
-      if (next + 1 < nkb) wait_vm_upto<kPerStage>(per_stage);
-      else wait_vm<0>();
-    } else {
-      wait_vm<0>();
-    }
+  // Pipeline.  Stages hold K blocks kb .. kb + kStages - 1.  The wait and barrier that publish
+  // block kb + 1 sit between the last two m pieces of block kb: while a wave waits there, the
+  // MFMA pipe still holds the MFMAs of piece NJ - 2, and the MFMAs of piece NJ - 1 run while
+  // the fragments of block kb + 1 are read (each weight fragment is re-read into its register
+  // right after the MFMA that last uses it).
+  // Every wave issues kPerStage DMA instructions per block, in block order, also for blocks
+  // past the last (their descriptors are empty: they read zeros into a slot no block reads), so
+  // vmcnt says which blocks have landed.
+  auto wait_next = [&]() {
+    // the next block must have landed; with 3 stages the one after it may still be in flight
+    if constexpr (C::kStages == 3) wait_vm<kPerStage>();
+    else wait_vm<0>();
   };
   auto stage_ptr = [&](int kb) { return smem + (kb % C::kStages) * C::kStage; };
   auto prepare = [&](int kb) {
@@ -491,13 +530,86 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
       __syncthreads();
     }
   };
-  // One K block: MFMAs of m piece j are issued while piece j-1 is folded.  The fragments of the
-  // first piece (xf, c0) and the weight fragments wf are loaded by the caller.
-  auto mma_block = [&](const uint8_t* st, v8i (&wf)[NI], v8i xf, float c0, float sbv,
-                       const v4f (&sbr)[NI], const int (&wbr)[NI], v4f (&P)[NI], float& cprev) {
-    const float* sat = reinterpret_cast<const float*>(st + C::kXBytes + C::kWBytes);
-    float ccur = c0;
-    const int wbyte = (HW && !ROWS) ? e8m0_of(sbv) : 0;   // weight scale: one per wave and K block
+  auto scales_of = [&](const uint8_t* st) {
+    return reinterpret_cast<const float*>(st + C::kXBytes + C::kWBytes);
+  };
+  // First m piece of a block: its fragment, and the factor c of its rows (fold: sa * sb; MFMA
+  // scales and 1x128 weight scales: sa); the block's weight scale sbv (one per wave).
+  auto first_x = [&](const uint8_t* st, v8i& xf, float& c, float& sbv) {
+    const float* sat = scales_of(st);
+    xf = fragment<XK>(st, wm * C::kWTM + li, li, g);
+    if constexpr (FOLD && !ROWS) {
+      sbv = sat[BM + (wn * C::kWTN) / 128];
+      c = sat[wm * C::kWTM + li] * sbv;
+    } else if constexpr (HW && !ROWS) {
+      sbv = sat[BM + (wn * C::kWTN) / 128];
+      c = sat[wm * C::kWTM + li];
+    } else if constexpr (ROWS) {
+      c = sat[wm * C::kWTM + li];
+    }
+  };
+  // 1x128 weight scales of a block: fold, those of this lane's 4 output columns; MFMA, that of
+  // its A-operand row.
+  auto fold_row_scales = [&](const uint8_t* st, v4f (&sbr)[NI]) {
+    if constexpr (ROWS && FOLD) {
+      const float* sat = scales_of(st);
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        sbr[i] = *reinterpret_cast<const v4f*>(sat + BM + wn * C::kWTN + 16 * i + 4 * g);
+    }
+  };
+  auto mfma_row_scales = [&](const uint8_t* st, int (&wbr)[NI]) {
+    if constexpr (ROWS && HW) {
+      const float* sat = scales_of(st);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) wbr[i] = e8m0_of(sat[BM + wn * C::kWTN + 16 * i + li]);
+    }
+  };
+  auto w_fragment = [&](const uint8_t* st, int i) {
+    return fragment<WK>(st + C::kXBytes, wn * C::kWTN + 16 * i + li, li, g);
+  };
+
+  for (int s = 0; s + 1 < C::kStages; ++s) issue(s);
+  v8i wf[NI], xf;
+  float ccur = 0.0f, sbv = 1.0f, cprev = 0.0f;
+  v4f sbr[NI], P[NI];
+  int wbr[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) P[i] = v4f{0.f, 0.f, 0.f, 0.f};   // pending products (fold)
+  if (nkb > 0) {
+    wait_next();
+    barrier();
+    prepare(0);
+    const uint8_t* st = stage_ptr(0);
+    first_x(st, xf, ccur, sbv);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) wf[i] = w_fragment(st, i);
+    fold_row_scales(st, sbr);
+    mfma_row_scales(st, wbr);
+    if constexpr (kBurst) {
+      issue(C::kStages - 1);
+    } else {
+      const BlockDma d = block_dma(C::kStages - 1);   // its first NI instructions
+#pragma unroll
+      for (int q = 0; q < NI && q < kPerStage; ++q) dma_part(d, q);
+    }
+  }
+
+  // One K block.  TURN: block kb + 1 follows; PREP: it is the last block (whose bytes past a
+  // ragged K are zeroed).  The variants keep every branch out of the common block, so that the
+  // compiler keeps each fold next to its MFMAs.
+  auto run_block = [&](int kb, auto turn_tag, auto prep_tag) {
+    constexpr bool TURN = decltype(turn_tag)::value;
+    constexpr bool PREP = decltype(prep_tag)::value;
+    const uint8_t* st = stage_ptr(kb);
+    const uint8_t* stn = stage_ptr(kb + 1);
+    const float* sat = scales_of(st);
+    const int wbyte = (HW && !ROWS) ? e8m0_of(sbv) : 0;   // weight scale of the block
+    // DMA of block kb + kStages - 1 (into the slot of block kb - 1): its first NI instructions
+    // were issued at the previous hand-over, the rest go here (the last block has none: that
+    // block would be past K).  DMA of block kb + kStages: started at this block's hand-over.
+    BlockDma dcont, dturn;
+    if constexpr (TURN && !kBurst) dcont = block_dma(kb + C::kStages - 1);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int mrow = wm * C::kWTM + 16 * j + li;
@@ -508,22 +620,41 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
         if constexpr (FOLD && !ROWS) cnext = sat[mrow + 16] * sbv;
         if constexpr (HW || ROWS) cnext = sat[mrow + 16];
       }
+      const bool turn = TURN && j == NJ - 1;   // block kb + 1 is published before this piece
+      if (turn) {
+        __builtin_amdgcn_sched_barrier(0);
+        wait_lds();   // this wave's reads of stage kb have completed
+        wait_next();
+        barrier();
+        if constexpr (PREP) prepare(kb + 1);
+        if constexpr (!kBurst) dturn = block_dma(kb + C::kStages);
+        first_x(stn, xnext, cnext, sbv);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       const int xbyte = HW ? e8m0_of(ccur) : 0;   // activation scale of this lane's row
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         if constexpr (FOLD) {
-          // Unit i: the MFMA of (piece j, n piece i) and the fold of (piece j-1, n piece i),
-          // whose MFMA was issued NI MFMAs earlier and has completed.  The scheduling barrier
-          // keeps the compiler from pulling the fold of an MFMA right behind that MFMA (which
-          // would stall the wave on every MFMA result).
+          // Unit i: the MFMA of (piece j, n piece i) and the fold of the previous piece's n
+          // piece i, whose MFMA was issued NI MFMAs earlier and has completed.  The scheduling
+          // barrier keeps the compiler from pulling the fold of an MFMA right behind that MFMA
+          // (which would stall the wave on every MFMA result).
           const v4f pn = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               wf[i], xf, v4f{0.f, 0.f, 0.f, 0.f}, FB, FA, 0, 0, 0, 0);
+          // (the empty asm pins the fold here: the compiler would otherwise sink it towards
+          // the accumulator's next use, keeping every pending product alive)
           if (j > 0) {
             if constexpr (ROWS) acc[i][j - 1] += P[i] * (sbr[i] * cprev);   // sb[n..n+3] * sa[m]
             else acc[i][j - 1] += P[i] * cprev;
+            asm volatile("" : "+v"(acc[i][j - 1]));
+          } else {
+            // the last piece of the previous block (zero products before the first block),
+            // with that block's weight scales (1x128: replaced after this piece's MFMAs)
+            if constexpr (ROWS) acc[i][NJ - 1] += P[i] * (sbr[i] * cprev);
+            else acc[i][NJ - 1] += P[i] * cprev;
+            asm volatile("" : "+v"(acc[i][NJ - 1]));
           }
           P[i] = pn;
-          __builtin_amdgcn_sched_barrier(0);
         } else if constexpr (HW) {
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               wf[i], xf, acc[i][j], FB, FA, 0, ROWS ? wbr[i] : wbyte, 0, xbyte);
@@ -531,71 +662,41 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[i], xf, acc[i][j], FB,
                                                                        FA, 0, 0, 0, 0);
         }
+        if (turn) {
+          wf[i] = w_fragment(stn, i);
+          if (!kBurst && i < kPerStage) dma_part(dturn, i);
+        } else if constexpr (TURN && !kBurst) {
+          const int q = NI + j * NI + i;
+          if (q < kPerStage) dma_part(dcont, q);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (turn) {
+        mfma_row_scales(stn, wbr);
+        if constexpr (kBurst) issue(kb + C::kStages);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (j == 0) {
+        fold_row_scales(st, sbr);   // first needed by the folds of this piece, in the next
+        __builtin_amdgcn_sched_barrier(0);
       }
       cprev = ccur;
-      if (j + 1 < NJ) {
+      if (j + 1 < NJ || TURN) {
         xf = xnext;
         ccur = cnext;
       }
     }
   };
-  auto load_w = [&](const uint8_t* st, v8i (&wf)[NI]) {
+  for (int kb = 0; kb + 2 < nkb; ++kb) run_block(kb, std::true_type{}, std::false_type{});
+  if (nkb >= 2) run_block(nkb - 2, std::true_type{}, std::true_type{});
+  if (nkb >= 1) run_block(nkb - 1, std::false_type{}, std::false_type{});
+  wait_vm<0>();   // DMAs of blocks past the last
+  if constexpr (FOLD) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) wf[i] = fragment<WK>(st + C::kXBytes, wn * C::kWTN + 16 * i + li, li, g);
-  };
-  auto first_piece = [&](const uint8_t* st, v8i& xf, float& c0, float& sbv, v4f (&sbr)[NI],
-                         int (&wbr)[NI]) {
-    const float* sat = reinterpret_cast<const float*>(st + C::kXBytes + C::kWBytes);
-    xf = fragment<XK>(st, wm * C::kWTM + li, li, g);
-    if constexpr (ROWS) {
-      c0 = sat[wm * C::kWTM + li];
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int ncol = wn * C::kWTN + 16 * i;
-        // fold: the scales of this lane's 4 output columns; MFMA: that of its A-operand row
-        if constexpr (FOLD) sbr[i] = *reinterpret_cast<const v4f*>(sat + BM + ncol + 4 * g);
-        if constexpr (HW) wbr[i] = e8m0_of(sat[BM + ncol + li]);
-      }
-    } else if constexpr (FOLD) {
-      sbv = sat[BM + (wn * C::kWTN) / 128];
-      c0 = sat[wm * C::kWTM + li] * sbv;
-    } else if constexpr (HW) {
-      sbv = sat[BM + (wn * C::kWTN) / 128];
-      c0 = sat[wm * C::kWTM + li];
+    for (int i = 0; i < NI; ++i) {
+      if constexpr (ROWS) acc[i][NJ - 1] += P[i] * (sbr[i] * cprev);
+      else acc[i][NJ - 1] += P[i] * cprev;
     }
-  };
-
-  for (int s = 0; s < C::kStages - 1; ++s)
-    if (s < nkb) issue(s);
-
-  // The barrier at the top of iteration kb publishes stage kb (every wave has waited for its
-  // own DMA of it) and proves that every wave has finished reading stage kb - 1, whose slot
-  // then receives block kb + kStages - 1.
-  for (int kb = 0; kb < nkb; ++kb) {
-    wait_next(kb);
-    barrier();
-    prepare(kb);
-    const uint8_t* st = stage_ptr(kb);
-    v8i wf[NI], xf;
-    float c0 = 0.0f, sbv = 1.0f;
-    v4f sbr[NI];
-    int wbr[NI];
-    // The block's first fragments are requested before this wave's DMA of a later block: a DMA
-    // instruction can wait for the memory pipeline, and the LDS reads then complete meanwhile.
-    first_piece(st, xf, c0, sbv, sbr, wbr);
-    load_w(st, wf);
-    if (kb + C::kStages - 1 < nkb) issue(kb + C::kStages - 1);
-    v4f P[NI];
-    float cprev = 0.0f;
-    mma_block(st, wf, xf, c0, sbv, sbr, wbr, P, cprev);
-    if constexpr (FOLD) {
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        if constexpr (ROWS) acc[i][NJ - 1] += P[i] * (sbr[i] * cprev);
-        else acc[i][NJ - 1] += P[i] * cprev;
-      }
-    }
-    // (the next iteration's barrier orders every wave's reads of this stage before its refill)
   }
 
   float post = 1.0f;
