@@ -188,41 +188,64 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>(p);
 }
 
-// K-major tile fragment: 32 bytes k = 32g .. 32g+31 of tile row r.
-__device__ __forceinline__ v8i frag_kmajor(const uint8_t* tile, int r, int g) {
-  const uint8_t* row = tile + r * 128;
-  const int sw = swz_k(r);
-  uint4 lo = *reinterpret_cast<const uint4*>(row + (((2 * g) ^ sw) << 4));
-  uint4 hi = *reinterpret_cast<const uint4*>(row + (((2 * g + 1) ^ sw) << 4));
+// Per-lane parts of the fragment addresses, computed once per tile.  A piece's rows (K-major)
+// or columns (MN-major) start at a multiple of 16, u, the same in every lane; the swizzle then
+// depends on the lane only, and the piece's address is the lane's base plus 128 u (K-major: an
+// immediate offset for constant u) or the base XOR the piece's chunk (MN-major).
+template <bool KMAJOR>
+struct FragBase {
+  int a[KMAJOR ? 2 : 4];
+};
+__device__ __forceinline__ FragBase<true> frag_base_k(int li, int g) {
+  const int sw = swz_k(li);
+  return FragBase<true>{{li * 128 + (((2 * g) ^ sw) << 4), li * 128 + (((2 * g + 1) ^ sw) << 4)}};
+}
+__device__ __forceinline__ FragBase<false> frag_base_mn(int li, int g) {
+  FragBase<false> b;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int k = 32 * g + 8 * t + (li >> 1);
+    b.a[t] = (k * 128 + 8 * (li & 1)) | (swz_mn(k) << 4);   // bits 4..6 of k * 128 + ... are 0
+  }
+  return b;
+}
+// The 32-byte MFMA fragment of lane (li, g) for the piece at u (u % 16 == 0, wave-uniform):
+// bytes k = 32g .. 32g+31 of tile row u + li (K-major tile), or of column u + li of an MN-major
+// tile ([halves][128 k][128 columns]), gathered by four 8x8 byte transposes across lanes (source
+// lane 2j + h of each 16-lane group points at row k0 + j, bytes 8h .. 8h + 7 of the chunk).
+__device__ __forceinline__ v8i frag_k_at(const uint8_t* tile, const FragBase<true>& b, int u) {
+  const uint8_t* base = tile + u * 128;
+  const uint4 lo = *reinterpret_cast<const uint4*>(base + b.a[0]);
+  const uint4 hi = *reinterpret_cast<const uint4*>(base + b.a[1]);
   v8i v;
   v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
   v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
   return v;
 }
-
-// MN-major tile fragment (tile = [halves][128 k][128 cols]): 32 bytes k = 32g .. 32g+31 of
-// column c = col0 + li (col0 a multiple of 16).  Four 8x8 byte transposes across lanes: source
-// lane 2j + h of each 16-lane group points at row k0 + j, bytes col0 + 8h .. +8.
-__device__ __forceinline__ v8i frag_mnmajor(const uint8_t* tile, int col0, int li, int g) {
-  const uint8_t* half = tile + (col0 >> 7) * 16384;
-  const int chunk = (col0 & 127) >> 4;
+__device__ __forceinline__ v8i frag_mn_at(const uint8_t* tile, const FragBase<false>& b, int u) {
+  const uint8_t* half = tile + (u >> 7) * 16384;
+  const int chunk = ((u & 127) >> 4) << 4;
   v8i v;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int k = 32 * g + 8 * t + (li >> 1);
-    const uint8_t* p = half + k * 128 + ((chunk ^ swz_mn(k)) << 4) + 8 * (li & 1);
+    const uint8_t* p = half + (b.a[t] ^ chunk);
     v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)p);
     v[2 * t] = r.x;
     v[2 * t + 1] = r.y;
   }
   return v;
 }
-
 template <bool KMAJOR>
-__device__ __forceinline__ v8i fragment(const uint8_t* tile, int idx, int li, int g) {
-  if constexpr (KMAJOR) return frag_kmajor(tile, idx, g);
-  else return frag_mnmajor(tile, idx - li, li, g);
+__device__ __forceinline__ v8i frag_at(const uint8_t* tile, const FragBase<KMAJOR>& b, int u) {
+  if constexpr (KMAJOR) return frag_k_at(tile, b, u);
+  else return frag_mn_at(tile, b, u);
 }
+template <bool KMAJOR>
+__device__ __forceinline__ FragBase<KMAJOR> frag_base(int li, int g) {
+  if constexpr (KMAJOR) return frag_base_k(li, g);
+  else return frag_base_mn(li, g);
+}
+
 
 // Per-lane DMA source offsets for a tile side.  K-major: rows of the tile are matrix rows
 // (m or n), the K block starts at the descriptor base.  MN-major: rows of the tile are k, the
@@ -530,6 +553,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
       __syncthreads();
     }
   };
+  // Fragment address bases (re-declared opaque at every block, so that the compiler computes a
+  // piece's address where it is used instead of keeping every piece's address live).
+  FragBase<XK> xb = frag_base<XK>(li, g);
+  FragBase<WK> wb = frag_base<WK>(li, g);
   auto scales_of = [&](const uint8_t* st) {
     return reinterpret_cast<const float*>(st + C::kXBytes + C::kWBytes);
   };
@@ -537,7 +564,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
   // scales and 1x128 weight scales: sa); the block's weight scale sbv (one per wave).
   auto first_x = [&](const uint8_t* st, v8i& xf, float& c, float& sbv) {
     const float* sat = scales_of(st);
-    xf = fragment<XK>(st, wm * C::kWTM + li, li, g);
+    xf = frag_at<XK>(st, xb, wm * C::kWTM);
     if constexpr (FOLD && !ROWS) {
       sbv = sat[BM + (wn * C::kWTN) / 128];
       c = sat[wm * C::kWTM + li] * sbv;
@@ -566,7 +593,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
     }
   };
   auto w_fragment = [&](const uint8_t* st, int i) {
-    return fragment<WK>(st + C::kXBytes, wn * C::kWTN + 16 * i + li, li, g);
+    return frag_at<WK>(st + C::kXBytes, wb, wn * C::kWTN + 16 * i);
   };
 
   for (int s = 0; s + 1 < C::kStages; ++s) issue(s);
@@ -605,6 +632,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
     const uint8_t* stn = stage_ptr(kb + 1);
     const float* sat = scales_of(st);
     const int wbyte = (HW && !ROWS) ? e8m0_of(sbv) : 0;   // weight scale of the block
+#pragma unroll
+    for (int t = 0; t < (XK ? 2 : 4); ++t) asm volatile("" : "+v"(xb.a[t]));
+#pragma unroll
+    for (int t = 0; t < (WK ? 2 : 4); ++t) asm volatile("" : "+v"(wb.a[t]));
     // DMA of block kb + kStages - 1 (into the slot of block kb - 1): its first NI instructions
     // were issued at the previous hand-over, the rest go here (the last block has none: that
     // block would be past K).  DMA of block kb + kStages: started at this block's hand-over.
@@ -616,7 +647,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
       v8i xnext;
       float cnext = 0.0f;
       if (j + 1 < NJ) {
-        xnext = fragment<XK>(st, mrow + 16, li, g);
+        xnext = frag_at<XK>(st, xb, wm * C::kWTM + 16 * j + 16);
         if constexpr (FOLD && !ROWS) cnext = sat[mrow + 16] * sbv;
         if constexpr (HW || ROWS) cnext = sat[mrow + 16];
       }
@@ -757,6 +788,12 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
                                    (int64_t)tn * C::BN, p.B, p.sb, p.sb_bytes);
 }
 
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Grouped: a persistent grid walks the concatenation of every group's m tiles (times the n
 // tiles).  Each workgroup first builds the prefix count of m tiles per group in LDS, then maps
 // each of its tiles to (group, m tile, n tile) by binary search.
@@ -801,20 +838,34 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(GemmParams
   const int m_tiles = s_prefix[G];
   const int total = m_tiles * p.tiles_n;
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    const int mt = tile / p.tiles_n, tn = tile % p.tiles_n;
+    // The parameters are read again from the argument segment for every tile (scalar loads),
+    // so that values derived from them are not kept live across the whole tile loop.
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef const __attribute__((address_space(4))) GemmParams* ParamPtr;
+    ParamPtr pp = (ParamPtr)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(pp));
+    const GemmParams q = *pp;
+#else
+    const GemmParams& q = p;   // (host pass: the body is never run there)
+#endif
+    const int mt = tile / q.tiles_n, tn = tile % q.tiles_n;
     int lo = 0, hi = G - 1;   // last group with s_prefix[g] <= mt
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (s_prefix[mid] <= mt) lo = mid; else hi = mid - 1;
     }
-    const int gi = lo;
-    const int64_t glo = std::min<int64_t>(std::max<int64_t>(p.offsets[gi], 0), p.M);
-    const int64_t ghi = std::min<int64_t>(std::max<int64_t>(p.offsets[gi + 1], glo), p.M);
-    const int64_t m0 = glo + (int64_t)(mt - s_prefix[gi]) * BM;
-    gemm_tile<C, FP8BS_FPROP, FA, FB, SM>(p, smem, m0, std::min<int64_t>(m0 + BM, ghi),
-                                          (int64_t)tn * C::BN, p.B + gi * p.b_group_stride,
-                                          p.sb + gi * p.sb_group_stride,
-                                          p.sb_group_stride * 4);
+    // (the tile's group and rows are the same in every lane: reading them as wave-uniform keeps
+    // the tile's address arithmetic in scalar registers)
+    const int gi = __builtin_amdgcn_readfirstlane(lo);
+    const int64_t glo =
+        uniform64(std::min<int64_t>(std::max<int64_t>(q.offsets[gi], 0), q.M));
+    const int64_t ghi =
+        uniform64(std::min<int64_t>(std::max<int64_t>(q.offsets[gi + 1], glo), q.M));
+    const int64_t m0 = glo + (int64_t)__builtin_amdgcn_readfirstlane(mt - s_prefix[gi]) * BM;
+    gemm_tile<C, FP8BS_FPROP, FA, FB, SM>(q, smem, m0, std::min<int64_t>(m0 + BM, ghi),
+                                          (int64_t)tn * C::BN, q.B + gi * q.b_group_stride,
+                                          q.sb + gi * q.sb_group_stride,
+                                          q.sb_group_stride * 4);
     __syncthreads();   // the next tile refills the LDS stages
   }
 }
