@@ -284,3 +284,73 @@ def rel_frobenius(c, ref) -> float:
     if den == 0.0:
         return 0.0 if num == 0.0 else float("inf")
     return float(num / den)
+
+
+# ----------------------------------------------------------------------------- FP8 KV cache
+
+def kv_cache_append(cache_codes: np.ndarray, cache_si: np.ndarray, new_bits, positions, fmt: int,
+                    mode: int) -> None:
+    """Write one new token per sequence into an FP8 KV cache, in place.
+
+    "NVIDIA NeMo RL ..." (hotbookzone.com), section "Ganancias de rendimiento en el mundo real":
+    FP8 is extended to the KV cache.  The pages give no cache format; the reading taken here is
+    the activation recipe of section "El avance técnico" applied to cached keys and values: each
+    128-element head vector of a token is one 1x128 block (E4M3 codes, fp32 scale), quantized
+    by the blockwise rule (``quantize_blockwise``).
+
+    cache_codes uint8 [B][T][KVH][128]; cache_si float32 [B][T][KVH] (dequantization factors);
+    new_bits: bf16 bit patterns [B][KVH][128]; positions int [B]: token slot of each sequence
+    (a slot outside [0, T) leaves that sequence's cache unchanged).
+    """
+    nb, t_cap, kvh, d = cache_codes.shape
+    if d != 128 or cache_si.shape != (nb, t_cap, kvh):
+        raise ValueError("cache shapes")
+    nbits = _as_bf16_bits(new_bits).reshape(nb, kvh, d)
+    for b in range(nb):
+        t = int(positions[b])
+        if t < 0 or t >= t_cap:
+            continue
+        q, si = quantize_blockwise(np.ascontiguousarray(nbits[b]), fmt, BLOCK_1x128, mode)
+        cache_codes[b, t] = q
+        cache_si[b, t] = si[:, 0]
+
+
+def attention_decode(q_bits, k_codes, k_si, v_codes, v_si, lens, sm_scale: float,
+                     fmt: int) -> np.ndarray:
+    """fp64 reference of one decode step of grouped-query attention over an FP8 KV cache.
+
+    For sequence b and query head h (KV head kv = h // (H // KVH)), with the cached keys and
+    values dequantized exactly (code value times the head vector's factor):
+        s_t = sm_scale * sum_d q[b,h,d] K[b,t,kv,d]     for t < L_b
+        out[b,h,:] = sum_t softmax(s)_t V[b,t,kv,:]
+    L_b = lens[b] clamped to [0, T]; a sequence with no cached token gives zeros (reading: there
+    is nothing to attend to).  "Ganancias de rendimiento en el mundo real" (FP8 KV cache and
+    attention) fixes no more than that the cache is FP8; the queries stay in bf16 and the
+    arithmetic is exact here (fp64).
+
+    q_bits: bf16 bits [B][H][128]; k_codes, v_codes: uint8 [B][T][KVH][128]; k_si, v_si: float32
+    [B][T][KVH].  Returns fp64 [B][H][128].
+    """
+    qb = _as_bf16_bits(q_bits)
+    nb, nh, d = qb.shape
+    _, t_cap, kvh, _ = k_codes.shape
+    if nh % kvh != 0:
+        raise ValueError("query heads must be a multiple of KV heads")
+    group = nh // kvh
+    q = (qb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    table = decode_table(fmt)
+    out = np.zeros((nb, nh, d), dtype=np.float64)
+    for b in range(nb):
+        n = min(max(int(lens[b]), 0), t_cap)
+        if n == 0:
+            continue
+        kd = table[k_codes[b, :n]] * k_si[b, :n, :, None].astype(np.float64)   # [n][KVH][D]
+        vd = table[v_codes[b, :n]] * v_si[b, :n, :, None].astype(np.float64)
+        for h in range(nh):
+            kv = h // group
+            s = (kd[:, kv, :] @ q[b, h]) * float(sm_scale)
+            s = s - s.max()
+            p = np.exp(s)
+            p = p / p.sum()
+            out[b, h] = p @ vd[:, kv, :]
+    return out
