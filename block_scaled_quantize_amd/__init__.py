@@ -73,6 +73,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.fp8_gemm_blockscaled_qout.argtypes = [i64, i64, i64, vp, i64, i32, vp, vp, i64, i32, vp,
                                               i32, vp, i64, i32, vp, i64, vp, vp]
     lib.fp8_grouped_gemm_pow2.argtypes = lib.fp8_grouped_gemm.argtypes
+    lib.fp8_kv_cache_append.argtypes = [i64, i64, i64, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp]
+    lib.fp8_attention_decode.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp,
+                                         ctypes.c_float, i32, vp, vp]
     for name in ("fp8_quantize_blockwise", "fp8_quantize_columnwise_t", "fp8_quantize_delayed",
                  "fp8_cast_fp32",
                  "fp8_gemm_blockscaled", "fp8_grouped_gemm", "fp8_gemm_blockscaled_pow2",
@@ -288,3 +291,50 @@ def grouped_gemm(offsets: torch.Tensor, a: torch.Tensor, sa: torch.Tensor, b: to
                                  _ptr(sa), _ptr(b), b.stride(1), fb, _ptr(sb), _ptr(c),
                                  c.stride(0), _stream(stream)), name)
     return c
+
+
+def kv_cache_append(k_new: torch.Tensor, v_new: torch.Tensor, positions: torch.Tensor,
+                    k_codes: torch.Tensor, k_scale_inv: torch.Tensor, v_codes: torch.Tensor,
+                    v_scale_inv: torch.Tensor, fmt: int = E4M3, mode: int = SCALE_FP32,
+                    stream=None) -> None:
+    """Quantize one new token per sequence (k_new, v_new: bf16 [B, KVH, 128]) into the FP8 cache
+    (codes uint8 [B, T, KVH, 128], factors float32 [B, T, KVH]) at slot positions[b] (device
+    int32 [B])."""
+    if k_codes.dim() != 4 or k_codes.shape[3] != 128:
+        raise ValueError("k_codes must be [B, T, KVH, 128]")
+    B, T, KVH, _ = k_codes.shape
+    for t, shape, dt in ((k_new, (B, KVH, 128), torch.bfloat16), (v_new, (B, KVH, 128), torch.bfloat16),
+                         (v_codes, (B, T, KVH, 128), torch.uint8),
+                         (k_scale_inv, (B, T, KVH), torch.float32),
+                         (v_scale_inv, (B, T, KVH), torch.float32), (positions, (B,), torch.int32)):
+        if tuple(t.shape) != shape or t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"expected a contiguous {dt} tensor of shape {shape}")
+    _check(load().fp8_kv_cache_append(B, KVH, T, _ptr(k_new), _ptr(v_new), _ptr(positions), fmt,
+                                      mode, _ptr(k_codes), _ptr(k_scale_inv), _ptr(v_codes),
+                                      _ptr(v_scale_inv), _stream(stream)), "fp8_kv_cache_append")
+
+
+def attention_decode(q: torch.Tensor, k_codes: torch.Tensor, k_scale_inv: torch.Tensor,
+                     v_codes: torch.Tensor, v_scale_inv: torch.Tensor, seq_lens: torch.Tensor,
+                     sm_scale: float, fmt: int = E4M3, out: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+    """One decode step of grouped-query attention (q: bf16 [B, H, 128]) over the FP8 cache;
+    returns bf16 [B, H, 128]."""
+    if q.dim() != 3 or q.shape[2] != 128 or q.dtype != torch.bfloat16 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bf16 [B, H, 128] tensor")
+    if k_codes.dim() != 4 or k_codes.shape[3] != 128:
+        raise ValueError("k_codes must be [B, T, KVH, 128]")
+    B, H, _ = q.shape
+    _, T, KVH, _ = k_codes.shape
+    for t, shape, dt in ((v_codes, (B, T, KVH, 128), torch.uint8), (k_codes, (B, T, KVH, 128), torch.uint8),
+                         (k_scale_inv, (B, T, KVH), torch.float32),
+                         (v_scale_inv, (B, T, KVH), torch.float32), (seq_lens, (B,), torch.int32)):
+        if tuple(t.shape) != shape or t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"expected a contiguous {dt} tensor of shape {shape}")
+    if out is None:
+        out = torch.empty((B, H, 128), dtype=torch.bfloat16, device=q.device)
+    _check(load().fp8_attention_decode(B, H, KVH, T, _ptr(q), _ptr(k_codes), _ptr(k_scale_inv),
+                                       _ptr(v_codes), _ptr(v_scale_inv), _ptr(seq_lens),
+                                       float(sm_scale), fmt, _ptr(out), _stream(stream)),
+           "fp8_attention_decode")
+    return out

@@ -17,7 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfp8bs.so")
-SOURCES = ["quantize.hip", "quantize_t.hip", "gemm.hip", "gemm_pow2.hip", "gemm_qout.hip"]
+SOURCES = ["quantize.hip", "quantize_t.hip", "gemm.hip", "gemm_pow2.hip", "gemm_qout.hip",
+           "attention.hip"]
 HEADERS = [os.path.join(CSRC, "common.h"), os.path.join(CSRC, "gemm_impl.h"),
            os.path.join(INCLUDE, "fp8bs.h")]
 

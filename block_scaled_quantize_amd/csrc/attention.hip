@@ -1,0 +1,314 @@
+// FP8 KV cache for gfx950: the cache writer and grouped-query decode attention over the cache.
+//
+// Method: "NVIDIA NeMo RL logra una aceleración del 48% con entrenamiento de precisión FP8 de
+// extremo a extremo", section "Ganancias de rendimiento en el mundo real": FP8 is extended to
+// the KV cache and to attention.  The pages fix no cache format; the one used here is the
+// activation recipe of section "El avance técnico" applied to cached keys and values: E4M3 (or
+// E5M2) codes with one fp32 scale per 128-element head vector, quantized by the blockwise 1x128
+// rule.  Attention reads the codes (half the bytes of a bf16 cache), dequantizes in registers
+// and computes in fp32.
+//
+// Cache layout: codes [B][T][KVH][128] (the KVH head vectors of a token adjacent, 128 bytes
+// each), dequantization factors float [B][T][KVH].
+//
+// Writer: 8 lanes per head vector (16 bf16 per lane, two 16-byte loads), the 1x128 rule of the
+// blockwise quantizer (amax over the 8 lanes by DPP, the same scale, encode and NaN handling).
+//
+// Decode attention (HBM-bound: every cached byte is read once per step): one workgroup of 4
+// waves per (sequence, KV head).  A wave takes 8 tokens per step (G <= 4 query heads per KV
+// head; 4 tokens for G = 8), 8 (16) lanes per token, each lane 16 (8) consecutive elements of
+// the key and value rows; dot products are reduced over the token's lanes, the softmax is kept
+// online in base 2 (running maximum per head, wave-uniform; running sums per lane), and the
+// four waves' partial results are merged through LDS at the end.
+#include <math.h>
+
+#include "common.h"
+
+namespace fp8bs {
+namespace {
+
+// ---------------------------------------------------------------- cache writer
+constexpr int kAppendThreads = 256;   // 32 head vectors per workgroup
+
+template <int FMT, bool POW2>
+__global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
+    int64_t B, int64_t KVH, int64_t T, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, const int32_t* __restrict__ positions,
+    uint8_t* __restrict__ k_codes, float* __restrict__ k_si, uint8_t* __restrict__ v_codes,
+    float* __restrict__ v_si) {
+  const int64_t vectors = 2 * KVH;   // K heads then V heads of one sequence
+  const int64_t b = blockIdx.y;
+  const int64_t gi = (int64_t)blockIdx.x * (kAppendThreads / 8) + (threadIdx.x >> 3);
+  const int l8 = threadIdx.x & 7;
+  if (gi >= vectors) return;
+  const int64_t pos = positions[b];
+  if (pos < 0 || pos >= T) return;
+  const bool is_v = gi >= KVH;
+  const int64_t kvh = is_v ? gi - KVH : gi;
+  const uint16_t* src = (is_v ? v_new : k_new) + (b * KVH + kvh) * 128 + l8 * 16;
+  const uint4 a = *reinterpret_cast<const uint4*>(src);
+  const uint4 c = *reinterpret_cast<const uint4*>(src + 8);
+  const uint32_t d[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+  const uint32_t amax = group8_max(amax16_bits(d));   // the 8 lanes of this head vector
+  const float s = scale_from_amax_bits<FMT, POW2>(amax);
+  const uint4 q = amax < 0x7F80u ? encode16<FMT, true>(d, s)
+                                 : patch_nan16(encode16<FMT, false>(d, s), d);
+  const int64_t row = (b * T + pos) * KVH + kvh;
+  *reinterpret_cast<uint4*>((is_v ? v_codes : k_codes) + row * 128 + l8 * 16) = q;
+  if (l8 == 0) (is_v ? v_si : k_si)[row] = 1.0f / s;
+}
+
+// ---------------------------------------------------------------- decode attention
+constexpr int kAttnWaves = 4;
+
+// Two FP8 codes (bytes 0, 1 of w, or 2, 3 for HIGH) to fp32.
+template <int FMT, bool HIGH>
+__device__ __forceinline__ void decode_pair(uint32_t w, float& a, float& b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  f2 r;
+  if constexpr (FMT == FP8BS_E4M3) r = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HIGH);
+  else r = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, HIGH);
+  a = r.x;
+  b = r.y;
+}
+
+template <int FMT, int DL>
+__device__ __forceinline__ void decode_row(const uint8_t* p, float (&f)[DL]) {
+  if constexpr (DL == 16) {
+    const uint4 w = *reinterpret_cast<const uint4*>(p);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      decode_pair<FMT, false>(ws[i], f[4 * i], f[4 * i + 1]);
+      decode_pair<FMT, true>(ws[i], f[4 * i + 2], f[4 * i + 3]);
+    }
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    const uint32_t ws[2] = {w.x, w.y};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      decode_pair<FMT, false>(ws[i], f[4 * i], f[4 * i + 1]);
+      decode_pair<FMT, true>(ws[i], f[4 * i + 2], f[4 * i + 3]);
+    }
+  }
+}
+
+template <int FMT, int G>
+__global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(
+    int64_t H, int64_t KVH, int64_t T, const uint16_t* __restrict__ q,
+    const uint8_t* __restrict__ k_codes, const float* __restrict__ k_si,
+    const uint8_t* __restrict__ v_codes, const float* __restrict__ v_si,
+    const int32_t* __restrict__ seq_lens, float score_scale, uint16_t* __restrict__ out) {
+  constexpr int DL = G <= 4 ? 16 : 8;   // elements of a row per lane
+  constexpr int LPT = 128 / DL;         // lanes per token
+  constexpr int TPS = 64 / LPT;         // tokens per wave step
+  __shared__ float s_acc[kAttnWaves][G][128];
+  __shared__ float s_m[kAttnWaves][G], s_l[kAttnWaves][G];
+
+  const int64_t b = blockIdx.x / KVH, kvh = blockIdx.x % KVH;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tg = lane / LPT, d0 = (lane % LPT) * DL;
+  int64_t len = seq_lens[b];
+  len = len < 0 ? 0 : (len > T ? T : len);
+
+  // queries of the group's heads, pre-multiplied by sm_scale * log2(e) (scores in base 2)
+  float qf[G][DL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const uint16_t* qp = q + ((b * H + kvh * G + g) * 128 + d0);
+#pragma unroll
+    for (int i = 0; i < DL; i += 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qp + i);
+      const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        qf[g][i + 2 * j] = bf16_lo(ws[j]) * score_scale;
+        qf[g][i + 2 * j + 1] = bf16_hi(ws[j]) * score_scale;
+      }
+    }
+  }
+
+  float m[G], l[G], acc[G][DL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < DL; ++i) acc[g][i] = 0.0f;
+  }
+
+  for (int64_t step = w; step * TPS < len; step += kAttnWaves) {
+    const int64_t t = step * TPS + tg;
+    const bool valid = t < len;
+    const int64_t row = (b * T + (valid ? t : len - 1)) * KVH + kvh;   // in bounds
+    float kf[DL];
+    decode_row<FMT, DL>(k_codes + row * 128 + d0, kf);
+    const float ks = k_si[row];
+    const float vs = v_si[row];
+    float vf[DL];
+    decode_row<FMT, DL>(v_codes + row * 128 + d0, vf);
+    if (!valid) {
+      // (a lane past the end re-reads the last token: its values must not reach acc, not even
+      // as 0 * inf)
+#pragma unroll
+      for (int i = 0; i < DL; ++i) vf[i] = 0.0f;
+    }
+    float s[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float dot = 0.0f;
+#pragma unroll
+      for (int i = 0; i < DL; ++i) dot = fmaf(qf[g][i], kf[i], dot);
+#pragma unroll
+      for (int off = 1; off < LPT; off <<= 1) dot += __shfl_xor(dot, off);
+      s[g] = valid ? dot * ks : -INFINITY;
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float mx = s[g];
+#pragma unroll
+      for (int off = LPT; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      const float mnew = fmaxf(m[g], mx);              // finite: token tg = 0 of a step is valid
+      const float alpha = exp2f(m[g] - mnew);          // 0 on the first step (m = -inf)
+      const float p = valid ? exp2f(s[g] - mnew) : 0.0f;
+      l[g] = l[g] * alpha + p;
+      const float pv = p * vs;
+#pragma unroll
+      for (int i = 0; i < DL; ++i) acc[g][i] = fmaf(pv, vf[i], acc[g][i] * alpha);
+      m[g] = mnew;
+    }
+  }
+
+  // sums over the wave's token groups, then the four waves through LDS
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) {
+      l[g] += __shfl_xor(l[g], off);
+#pragma unroll
+      for (int i = 0; i < DL; ++i) acc[g][i] += __shfl_xor(acc[g][i], off);
+    }
+  }
+  if (tg == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int i = 0; i < DL; ++i) s_acc[w][g][d0 + i] = acc[g][i];
+      if (lane == 0) {
+        s_m[w][g] = m[g];
+        s_l[w][g] = l[g];
+      }
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * 128; idx += 64 * kAttnWaves) {
+    const int g = idx >> 7, d = idx & 127;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kAttnWaves; ++v) mx = fmaxf(mx, s_m[v][g]);
+    float num = 0.0f, den = 0.0f;
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int v = 0; v < kAttnWaves; ++v) {
+        const float f = exp2f(s_m[v][g] - mx);   // 0 for a wave without tokens
+        num = fmaf(f, s_acc[v][g][d], num);
+        den = fmaf(f, s_l[v][g], den);
+      }
+    }
+    const float o = den > 0.0f ? num / den : 0.0f;   // no cached token: zeros
+    typedef __bf16 bf1;
+    const bf1 ob = (bf1)o;
+    out[(b * H + kvh * G + g) * 128 + d] = __builtin_bit_cast(uint16_t, ob);
+  }
+}
+
+template <int FMT>
+int dispatch_attn(int G, dim3 grid, hipStream_t st, int64_t H, int64_t KVH, int64_t T,
+                  const uint16_t* q, const uint8_t* kc, const float* ks, const uint8_t* vc,
+                  const float* vs, const int32_t* lens, float c, uint16_t* out) {
+  const dim3 block(64 * kAttnWaves);
+  switch (G) {
+    case 1: return launch(attn_decode_kernel<FMT, 1>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
+    case 2: return launch(attn_decode_kernel<FMT, 2>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
+    case 4: return launch(attn_decode_kernel<FMT, 4>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
+    case 8: return launch(attn_decode_kernel<FMT, 8>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
+    default: return FP8BS_ERR_UNSUPPORTED;
+  }
+}
+
+bool cache_sizes_ok(int64_t B, int64_t T, int64_t KVH) {
+  // B * T * KVH * 128 bytes must be addressable with 64-bit offsets
+  if (B < 0 || T < 0 || KVH < 0) return false;
+  if (B == 0 || T == 0 || KVH == 0) return true;
+  const int64_t lim = INT64_MAX / 256;
+  return T <= lim / B && KVH <= lim / (B * T);
+}
+
+}  // namespace
+}  // namespace fp8bs
+
+using namespace fp8bs;
+
+extern "C" int fp8_kv_cache_append(int64_t B, int64_t KVH, int64_t T, const void* k_new_bf16,
+                                   const void* v_new_bf16, const int32_t* positions, int fmt,
+                                   int mode, void* k_codes, float* k_scale_inv, void* v_codes,
+                                   float* v_scale_inv, void* stream) {
+  if (!fmt_ok(fmt) || (mode != FP8BS_SCALE_FP32 && mode != FP8BS_SCALE_POW2)) return FP8BS_ERR_ARG;
+  if (!cache_sizes_ok(B, T, KVH)) return FP8BS_ERR_SHAPE;
+  if (B == 0 || KVH == 0 || T == 0) return FP8BS_OK;
+  if (B > 65535 || ceil_div(2 * KVH, kAppendThreads / 8) > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
+  if (!k_new_bf16 || !v_new_bf16 || !positions || !k_codes || !k_scale_inv || !v_codes ||
+      !v_scale_inv)
+    return FP8BS_ERR_NULL;
+  if (!aligned16(k_new_bf16) || !aligned16(v_new_bf16) || !aligned16(k_codes) ||
+      !aligned16(v_codes) || !aligned4(k_scale_inv) || !aligned4(v_scale_inv) ||
+      !aligned4(positions))
+    return FP8BS_ERR_ALIGN;
+  const dim3 grid((unsigned)ceil_div(2 * KVH, kAppendThreads / 8), (unsigned)B);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint16_t* kn = static_cast<const uint16_t*>(k_new_bf16);
+  const uint16_t* vn = static_cast<const uint16_t*>(v_new_bf16);
+  uint8_t* kc = static_cast<uint8_t*>(k_codes);
+  uint8_t* vc = static_cast<uint8_t*>(v_codes);
+  const dim3 block(kAppendThreads);
+  const bool pow2 = mode == FP8BS_SCALE_POW2;
+  if (fmt == FP8BS_E4M3)
+    return pow2 ? launch(kv_append_kernel<FP8BS_E4M3, true>, grid, block, st, B, KVH, T, kn, vn, positions, kc, k_scale_inv, vc, v_scale_inv)
+                : launch(kv_append_kernel<FP8BS_E4M3, false>, grid, block, st, B, KVH, T, kn, vn, positions, kc, k_scale_inv, vc, v_scale_inv);
+  return pow2 ? launch(kv_append_kernel<FP8BS_E5M2, true>, grid, block, st, B, KVH, T, kn, vn, positions, kc, k_scale_inv, vc, v_scale_inv)
+              : launch(kv_append_kernel<FP8BS_E5M2, false>, grid, block, st, B, KVH, T, kn, vn, positions, kc, k_scale_inv, vc, v_scale_inv);
+}
+
+extern "C" int fp8_attention_decode(int64_t B, int64_t H, int64_t KVH, int64_t T,
+                                    const void* q_bf16, const void* k_codes,
+                                    const float* k_scale_inv, const void* v_codes,
+                                    const float* v_scale_inv, const int32_t* seq_lens,
+                                    float sm_scale, int fmt, void* out_bf16, void* stream) {
+  if (!fmt_ok(fmt)) return FP8BS_ERR_ARG;
+  if (H < 0 || !cache_sizes_ok(B, T, KVH)) return FP8BS_ERR_SHAPE;
+  if (B == 0 || H == 0) return FP8BS_OK;
+  if (KVH == 0 || H % KVH != 0) return FP8BS_ERR_SHAPE;
+  const int64_t G = H / KVH;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return FP8BS_ERR_UNSUPPORTED;
+  if (B * KVH > 0x7FFFFFFF || B > INT64_MAX / 256 / H) return FP8BS_ERR_SHAPE;
+  if (!isfinite(sm_scale)) return FP8BS_ERR_ARG;
+  if (!q_bf16 || !seq_lens || !out_bf16 ||
+      (T > 0 && (!k_codes || !k_scale_inv || !v_codes || !v_scale_inv)))
+    return FP8BS_ERR_NULL;
+  if (!aligned16(q_bf16) || (T > 0 && (!aligned16(k_codes) || !aligned16(v_codes) ||
+                                       !aligned4(k_scale_inv) || !aligned4(v_scale_inv))) ||
+      !aligned4(seq_lens) || !aligned4(out_bf16))
+    return FP8BS_ERR_ALIGN;
+  const float c = sm_scale * 1.4426950408889634f;   // scores in base 2 (exp2 in the kernel)
+  const dim3 grid((unsigned)(B * KVH));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint16_t* q = static_cast<const uint16_t*>(q_bf16);
+  const uint8_t* kc = static_cast<const uint8_t*>(k_codes);
+  const uint8_t* vc = static_cast<const uint8_t*>(v_codes);
+  uint16_t* out = static_cast<uint16_t*>(out_bf16);
+  if (fmt == FP8BS_E4M3)
+    return dispatch_attn<FP8BS_E4M3>((int)G, grid, st, H, KVH, T, q, kc, k_scale_inv, vc,
+                                     v_scale_inv, seq_lens, c, out);
+  return dispatch_attn<FP8BS_E5M2>((int)G, grid, st, H, KVH, T, q, kc, k_scale_inv, vc,
+                                   v_scale_inv, seq_lens, c, out);
+}

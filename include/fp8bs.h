@@ -252,6 +252,41 @@ int fp8_grouped_gemm_pow2(int32_t num_groups, const int64_t* group_offsets, int6
                           const float* scale_inv_a, const void* B, int64_t ldb, int fb,
                           const float* scale_inv_b, void* C_bf16, int64_t ldc, void* stream);
 
+/* FP8 KV cache: write one token per sequence.  [P3] "Ganancias de rendimiento en el mundo real"
+ * (FP8 extended to the KV cache); the cache format is the activation recipe of "El avance
+ * técnico" applied to keys and values: each 128-element head vector is one 1x128 block, E4M3
+ * (or E5M2) codes and an fp32 dequantization factor, by the rule of fp8_quantize_blockwise.
+ *   Cache (caller-owned device memory, capacity T tokens per sequence):
+ *     k_codes, v_codes:          uint8 [B][T][KVH][128] (16-byte aligned)
+ *     k_scale_inv, v_scale_inv:  float [B][T][KVH]
+ *   k_new_bf16, v_new_bf16: bf16 [B][KVH][128] (16-byte aligned), the new token's keys and
+ *   values; positions: device int32 [B], the slot t of each sequence's token (a slot outside
+ *   [0, T) leaves that sequence's cache unchanged).  Only the B written head-vector slots
+ *   (codes and factors) are touched.  mode: FP8BS_SCALE_FP32 or FP8BS_SCALE_POW2.
+ * B <= 65535.  Errors: FP8BS_ERR_ARG, FP8BS_ERR_SHAPE, FP8BS_ERR_NULL, FP8BS_ERR_ALIGN,
+ * FP8BS_ERR_LAUNCH. */
+int fp8_kv_cache_append(int64_t B, int64_t KVH, int64_t T, const void* k_new_bf16,
+                        const void* v_new_bf16, const int32_t* positions, int fmt, int mode,
+                        void* k_codes, float* k_scale_inv, void* v_codes, float* v_scale_inv,
+                        void* stream);
+
+/* Grouped-query decode attention over the FP8 KV cache of fp8_kv_cache_append.  [P3]
+ * "Ganancias de rendimiento en el mundo real" (FP8 KV cache and attention).
+ * For sequence b and query head h (KV head kv = h / (H / KVH)), with L_b = seq_lens[b]
+ * clamped to [0, T] and the cache dequantized (code value x the head vector's factor):
+ *   s_t = sm_scale * sum_d q[b][h][d] K[b][t][kv][d],  t < L_b
+ *   out[b][h][:] = sum_t softmax(s)_t V[b][t][kv][:]     (zeros when L_b = 0)
+ * computed in fp32 (softmax online, in base 2), output rounded to bf16.
+ *   q_bf16: [B][H][128] (16-byte aligned); seq_lens: device int32 [B]; out_bf16: [B][H][128].
+ *   H / KVH must be 1, 2, 4 or 8 (else FP8BS_ERR_UNSUPPORTED).  Tokens at or past L_b are
+ *   never read.  sm_scale must be finite.
+ * Errors: FP8BS_ERR_ARG, FP8BS_ERR_SHAPE, FP8BS_ERR_NULL, FP8BS_ERR_ALIGN,
+ * FP8BS_ERR_UNSUPPORTED, FP8BS_ERR_LAUNCH. */
+int fp8_attention_decode(int64_t B, int64_t H, int64_t KVH, int64_t T, const void* q_bf16,
+                         const void* k_codes, const float* k_scale_inv, const void* v_codes,
+                         const float* v_scale_inv, const int32_t* seq_lens, float sm_scale,
+                         int fmt, void* out_bf16, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -184,3 +184,58 @@ def test_cast_validation():
     assert lib.fp8_cast_fp32(None, 16, 0, FAKE, None) == bsq.ERR_NULL
     assert lib.fp8_cast_fp32(FAKE + 2, 16, 0, FAKE, None) == bsq.ERR_ALIGN
     assert lib.fp8_cast_fp32(None, 0, 0, None, None) == bsq.OK
+
+
+def kv_append(**kw):
+    a = dict(B=2, KVH=8, T=16, kn=FAKE, vn=FAKE, pos=FAKE, fmt=0, mode=0, kc=FAKE, ks=FAKE,
+             vc=FAKE, vs=FAKE)
+    a.update(kw)
+    return bsq.load().fp8_kv_cache_append(a["B"], a["KVH"], a["T"], a["kn"], a["vn"], a["pos"],
+                                          a["fmt"], a["mode"], a["kc"], a["ks"], a["vc"], a["vs"],
+                                          None)
+
+
+def test_kv_cache_append_validation():
+    assert kv_append(fmt=3) == bsq.ERR_ARG
+    assert kv_append(mode=2) == bsq.ERR_ARG
+    assert kv_append(B=-1) == bsq.ERR_SHAPE
+    assert kv_append(T=-1) == bsq.ERR_SHAPE
+    assert kv_append(B=70000) == bsq.ERR_SHAPE
+    assert kv_append(B=1 << 40, T=1 << 20) == bsq.ERR_SHAPE   # cache bytes overflow
+    assert kv_append(kn=None) == bsq.ERR_NULL
+    assert kv_append(pos=None) == bsq.ERR_NULL
+    assert kv_append(vs=None) == bsq.ERR_NULL
+    assert kv_append(kn=FAKE + 8) == bsq.ERR_ALIGN
+    assert kv_append(kc=FAKE + 4) == bsq.ERR_ALIGN
+    assert kv_append(ks=FAKE + 2) == bsq.ERR_ALIGN
+    assert kv_append(B=0, kn=None) == bsq.OK        # empty: nothing launched
+    assert kv_append(T=0, kn=None) == bsq.OK
+
+
+def attn(**kw):
+    a = dict(B=2, H=32, KVH=8, T=16, q=FAKE, kc=FAKE, ks=FAKE, vc=FAKE, vs=FAKE, lens=FAKE,
+             sm=0.088, fmt=0, out=FAKE)
+    a.update(kw)
+    return bsq.load().fp8_attention_decode(a["B"], a["H"], a["KVH"], a["T"], a["q"], a["kc"],
+                                           a["ks"], a["vc"], a["vs"], a["lens"], a["sm"],
+                                           a["fmt"], a["out"], None)
+
+
+def test_attention_decode_validation():
+    assert attn(fmt=2) == bsq.ERR_ARG
+    assert attn(sm=float("inf")) == bsq.ERR_ARG
+    assert attn(sm=float("nan")) == bsq.ERR_ARG
+    assert attn(H=-1) == bsq.ERR_SHAPE
+    assert attn(KVH=0) == bsq.ERR_SHAPE
+    assert attn(H=30, KVH=8) == bsq.ERR_SHAPE            # not a multiple
+    assert attn(H=48, KVH=3) == bsq.ERR_UNSUPPORTED      # 16 query heads per KV head
+    assert attn(H=24, KVH=8) == bsq.ERR_UNSUPPORTED      # 3
+    assert attn(q=None) == bsq.ERR_NULL
+    assert attn(lens=None) == bsq.ERR_NULL
+    assert attn(kc=None) == bsq.ERR_NULL
+    assert attn(out=None) == bsq.ERR_NULL
+    assert attn(q=FAKE + 8) == bsq.ERR_ALIGN
+    assert attn(vc=FAKE + 4) == bsq.ERR_ALIGN
+    assert attn(out=FAKE + 2) == bsq.ERR_ALIGN
+    assert attn(B=0, q=None) == bsq.OK                   # empty: nothing launched
+    assert attn(H=0, q=None) == bsq.OK
