@@ -20,7 +20,8 @@ Other workloads (--workload): llama8b-fprop-pow2 (the same step with power-of-2 
 GEMM applying them as E8M0 block scales in the MFMA), quant-sweep (HBM-bound quantizer), moe
 (grouped GEMM; --pow2 for power-of-2 scales), backward (delayed-scaled dgrad / wgrad),
 backward-blockwise (dgrad + blockwise wgrad on columnwise-quantized operands; --pow2),
-llama8b-fprop-qout (the GEMM quantizing its own output against GEMM + quantizer), copy
+llama8b-fprop-qout (the GEMM quantizing its own output against GEMM + quantizer), kv-decode
+(FP8 KV-cache write + grouped-query decode attention, Llama-3.1-8B attention shape), copy
 (counter calibration).  Each prints one JSON line.
 """
 from __future__ import annotations
@@ -58,7 +59,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b-fprop",
                     choices=["llama8b-fprop", "llama8b-fprop-pow2", "quant-sweep", "moe", "backward",
-                             "backward-blockwise", "llama8b-fprop-qout", "copy"])
+                             "backward-blockwise", "llama8b-fprop-qout", "kv-decode", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pow2", action="store_true",
                     help="moe, backward-blockwise: power-of-2 scales (E8M0 in the MFMA)")
@@ -616,6 +617,119 @@ def bench_fprop_qout(args):
                 speedup_vs_separate=round(sep_ms / tot_ms, 4), layers=per)
 
 
+def bench_kv_decode(args):
+    """One decode step over an FP8 KV cache ("NVIDIA NeMo RL ...", section "Ganancias de
+    rendimiento en el mundo real": FP8 KV cache and attention), Llama-3.1-8B attention shape
+    (32 query heads, 8 KV heads, head dim 128), 64 sequences with a 4096-token cache and seeded
+    lengths in [2048, 4096].  Per step: the step's new token of every sequence is quantized into
+    the cache (1x128 per head vector) and grouped-query attention reads the whole cache.
+    value = algorithmic bytes of the step / step time."""
+    import block_scaled_quantize_amd as bsq
+    bsq.load()
+    dev = torch.device("cuda", 0)
+    B, T, H, KVH, D = 64, 4096, 32, 8, 128
+    g = np.random.default_rng(11)
+    lens_np = g.integers(T // 2, T + 1, size=B).astype(np.int32)
+    lens = torch.from_numpy(lens_np).to(dev)
+    pos = (lens - 1).to(torch.int32)
+    gen = torch.Generator(device=dev).manual_seed(11)
+    kc = torch.empty((B, T, KVH, D), dtype=torch.uint8, device=dev)
+    vc = torch.empty_like(kc)
+    ks = torch.empty((B, T, KVH), dtype=torch.float32, device=dev)
+    vs = torch.empty_like(ks)
+    for b in range(B):   # fill the cache: synthetic N(0, 1) keys and values, 1x128 quantized
+        for codes, fac in ((kc, ks), (vc, vs)):
+            x = torch.randn((T * KVH, D), generator=gen, device=dev).to(torch.bfloat16)
+            bsq.quantize_blockwise(x, bsq.E4M3, bsq.BLOCK_1x128, bsq.SCALE_FP32,
+                                   q=codes[b].view(T * KVH, D), scale_inv=fac[b].view(1, T * KVH))
+    q = torch.randn((B, H, D), generator=gen, device=dev).to(torch.bfloat16)
+    kn = torch.randn((B, KVH, D), generator=gen, device=dev).to(torch.bfloat16)
+    vn = torch.randn((B, KVH, D), generator=gen, device=dev).to(torch.bfloat16)
+    out = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
+    sm = 1.0 / float(np.sqrt(D))
+    torch.cuda.synchronize()
+
+    def step(t=None):
+        def run(key, fn):
+            return fn() if t is None else t.time(key, fn)
+        run("append", lambda: bsq.kv_cache_append(kn, vn, pos, kc, ks, vc, vs))
+        run("decode", lambda: bsq.attention_decode(q, kc, ks, vc, vs, lens, sm, out=out))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    timer = EventTimer()
+    for _ in range(max(3, min(args.steps, 20))):
+        step(timer)
+    torch.cuda.synchronize()
+    tokens = int(lens_np.sum())
+    decode_bytes = tokens * KVH * (2 * D + 8) + 2 * (2 * B * H * D) + 4 * B
+    append_bytes = B * KVH * 2 * (2 * D + D + 4) + 4 * B
+    dec_ms = timer.mean_ms("decode")
+    app_ms = timer.mean_ms("append")
+    achieved = decode_bytes / dec_ms / 1e6
+    res = dict(metric="FP8 KV-cache decode step GB/s (cache write + grouped-query attention)",
+               value=round((decode_bytes + append_bytes) / dt / 1e9, 1), unit="GB/s", n_gpus=1,
+               steps=args.steps, warmup=args.warmup, ms_per_step=round(dt * 1e3, 4),
+               higher_is_better=True, scaling="weak", vs_baseline=None,
+               dtype="e4m3 cache, fp32 attention math, bf16 q/out", data="synthetic",
+               config=dict(workload="llama3.1-8b-attention-decode-fp8-kv", batch=B, cache_tokens=T,
+                           q_heads=H, kv_heads=KVH, head_dim=D, mean_len=round(tokens / B, 1)),
+               roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS,
+                             unit="GB/s", frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=None,
+                             kernel="attn_decode_kernel<E4M3, 4 query heads per KV head, 16 bytes per lane, 4 steps in flight>",
+                             mean_launch_us=round(dec_ms * 1e3, 2),
+                             bytes_per_launch=decode_bytes),
+               decode_us=round(dec_ms * 1e3, 2), append_us=round(app_ms * 1e3, 2),
+               bf16_cache_bytes_ratio=round((tokens * KVH * 4 * D) / (tokens * KVH * (2 * D + 8)), 3))
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_kv(lens_np, KVH, H, D, sm)
+    return res
+
+
+def cpu_baseline_kv(lens_np, KVH, H, D, sm, min_seconds: float = 10.0):
+    """The oracle's decode attention on two sample sequences of the workload's first two
+    lengths (synthetic values of the same distribution, quantized by the oracle), repeated to
+    >= min_seconds; GB/s of cache read."""
+    import oracle
+    import synth
+
+    def u16(t):
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    sample = []
+    for i in range(2):
+        n = int(lens_np[i])
+        cache = []
+        for kind in ("K", "V"):
+            x = synth.normal((n * KVH, D), 1.0, 11, f"bench/kv/{kind}{i}")
+            c, f = oracle.quantize_blockwise(u16(x), oracle.E4M3, oracle.BLOCK_1x128,
+                                             oracle.SCALE_FP32)
+            cache += [c.reshape(1, n, KVH, D), f.reshape(1, n, KVH)]
+        q = u16(synth.normal((1, H, D), 1.0, 11, f"bench/kv/q{i}")).reshape(1, H, D)
+        sample.append((q, cache, n))
+    nbytes, reps = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        for q, (kc, ks, vc, vs), n in sample:
+            oracle.attention_decode(q, kc, ks, vc, vs, [n], sm, oracle.E4M3)
+            nbytes += n * KVH * (2 * D + 8) + 4 * H * D
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=round(nbytes / dt / 1e9, 4), unit="GB/s", cores=blas_threads(),
+                kind="oracle",
+                sample=f"2 sequences of {int(lens_np[0])} and {int(lens_np[1])} tokens (32 query / 8 KV "
+                       f"heads) x {reps} repetitions, {dt:.1f} s; NumPy fp64, BLAS threads "
+                       f"{blas_threads()}")
+
+
 def bench_copy(args):
     """A plain 1 GiB device copy (torch), the calibration kernel for the HBM byte counters."""
     dev = torch.device("cuda", 0)
@@ -665,6 +779,8 @@ def main():
         res = bench_backward_blockwise(args)
     elif args.workload == "llama8b-fprop-qout":
         res = bench_fprop_qout(args)
+    elif args.workload == "kv-decode":
+        res = bench_kv_decode(args)
     elif args.workload == "copy":
         res = bench_copy(args)
     else:

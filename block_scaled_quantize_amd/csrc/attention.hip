@@ -72,36 +72,42 @@ __device__ __forceinline__ void decode_pair(uint32_t w, float& a, float& b) {
   b = r.y;
 }
 
-template <int FMT, int DL>
-__device__ __forceinline__ void decode_row(const uint8_t* p, float (&f)[DL]) {
+// A lane's DL cache bytes of one row (16 or 8), loaded ahead of their decode.
+template <int DL>
+struct Raw {
+  uint32_t w[DL / 4];
+};
+template <int DL>
+__device__ __forceinline__ Raw<DL> load_raw(const uint8_t* p) {
+  Raw<DL> r;
   if constexpr (DL == 16) {
-    const uint4 w = *reinterpret_cast<const uint4*>(p);
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      decode_pair<FMT, false>(ws[i], f[4 * i], f[4 * i + 1]);
-      decode_pair<FMT, true>(ws[i], f[4 * i + 2], f[4 * i + 3]);
-    }
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
   } else {
-    const uint2 w = *reinterpret_cast<const uint2*>(p);
-    const uint32_t ws[2] = {w.x, w.y};
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    r.w[0] = v.x; r.w[1] = v.y;
+  }
+  return r;
+}
+template <int FMT, int DL>
+__device__ __forceinline__ void decode_raw(const Raw<DL>& r, float (&f)[DL]) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      decode_pair<FMT, false>(ws[i], f[4 * i], f[4 * i + 1]);
-      decode_pair<FMT, true>(ws[i], f[4 * i + 2], f[4 * i + 3]);
-    }
+  for (int i = 0; i < DL / 4; ++i) {
+    decode_pair<FMT, false>(r.w[i], f[4 * i], f[4 * i + 1]);
+    decode_pair<FMT, true>(r.w[i], f[4 * i + 2], f[4 * i + 3]);
   }
 }
 
-template <int FMT, int G>
+template <int FMT, int G, int DLANE, int KBATCH>
 __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(
     int64_t H, int64_t KVH, int64_t T, const uint16_t* __restrict__ q,
     const uint8_t* __restrict__ k_codes, const float* __restrict__ k_si,
     const uint8_t* __restrict__ v_codes, const float* __restrict__ v_si,
     const int32_t* __restrict__ seq_lens, float score_scale, uint16_t* __restrict__ out) {
-  constexpr int DL = G <= 4 ? 16 : 8;   // elements of a row per lane
+  constexpr int DL = DLANE;             // elements of a row per lane (16 or 8)
   constexpr int LPT = 128 / DL;         // lanes per token
   constexpr int TPS = 64 / LPT;         // tokens per wave step
+  constexpr int kBatch = KBATCH;        // wave steps whose loads are in flight together
   __shared__ float s_acc[kAttnWaves][G][128];
   __shared__ float s_m[kAttnWaves][G], s_l[kAttnWaves][G];
 
@@ -137,45 +143,65 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(
     for (int i = 0; i < DL; ++i) acc[g][i] = 0.0f;
   }
 
-  for (int64_t step = w; step * TPS < len; step += kAttnWaves) {
-    const int64_t t = step * TPS + tg;
-    const bool valid = t < len;
-    const int64_t row = (b * T + (valid ? t : len - 1)) * KVH + kvh;   // in bounds
-    float kf[DL];
-    decode_row<FMT, DL>(k_codes + row * 128 + d0, kf);
-    const float ks = k_si[row];
-    const float vs = v_si[row];
-    float vf[DL];
-    decode_row<FMT, DL>(v_codes + row * 128 + d0, vf);
-    if (!valid) {
-      // (a lane past the end re-reads the last token: its values must not reach acc, not even
-      // as 0 * inf)
+  // Steps are taken kBatch at a time: the loads of all of them are issued before any is used,
+  // so that each wave keeps kBatch steps of cache rows in flight.
+  for (int64_t step0 = w; step0 * TPS < len; step0 += kAttnWaves * kBatch) {
+    Raw<DL> kr[kBatch], vr[kBatch];
+    float ks[kBatch], vs[kBatch];
+    bool valid[kBatch];
 #pragma unroll
-      for (int i = 0; i < DL; ++i) vf[i] = 0.0f;
-    }
-    float s[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float dot = 0.0f;
-#pragma unroll
-      for (int i = 0; i < DL; ++i) dot = fmaf(qf[g][i], kf[i], dot);
-#pragma unroll
-      for (int off = 1; off < LPT; off <<= 1) dot += __shfl_xor(dot, off);
-      s[g] = valid ? dot * ks : -INFINITY;
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t t = (step0 + u * kAttnWaves) * TPS + tg;
+      valid[u] = t < len;
+      const int64_t row = (b * T + (valid[u] ? t : len - 1)) * KVH + kvh;   // in bounds
+      kr[u] = load_raw<DL>(k_codes + row * 128 + d0);
+      vr[u] = load_raw<DL>(v_codes + row * 128 + d0);
+      ks[u] = k_si[row];
+      vs[u] = v_si[row];
     }
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float mx = s[g];
+    for (int u = 0; u < kBatch; ++u) {
+      float kf[DL], vf[DL];
+      decode_raw<FMT, DL>(kr[u], kf);
+      decode_raw<FMT, DL>(vr[u], vf);
+      if (!valid[u]) {
+        // (a lane past the end re-reads the last token: its values must not reach acc, not
+        // even as 0 * inf)
 #pragma unroll
-      for (int off = LPT; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-      const float mnew = fmaxf(m[g], mx);              // finite: token tg = 0 of a step is valid
-      const float alpha = exp2f(m[g] - mnew);          // 0 on the first step (m = -inf)
-      const float p = valid ? exp2f(s[g] - mnew) : 0.0f;
-      l[g] = l[g] * alpha + p;
-      const float pv = p * vs;
+        for (int i = 0; i < DL; ++i) vf[i] = 0.0f;
+      }
+      float s[G];
 #pragma unroll
-      for (int i = 0; i < DL; ++i) acc[g][i] = fmaf(pv, vf[i], acc[g][i] * alpha);
-      m[g] = mnew;
+      for (int g = 0; g < G; ++g) {
+        float dot = 0.0f;
+#pragma unroll
+        for (int i = 0; i < DL; ++i) dot = fmaf(qf[g][i], kf[i], dot);
+#pragma unroll
+        for (int off = 1; off < LPT; off <<= 1) dot += __shfl_xor(dot, off);
+        s[g] = valid[u] ? dot * ks[u] : -INFINITY;
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float mx = s[g];
+#pragma unroll
+        for (int off = LPT; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        // the step maximum is the same in every lane: a scalar branch, taken only when the
+        // running maximum grows (then the sums are rescaled; -inf for a step without a token
+        // never is)
+        mx = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(mx)));
+        if (mx > m[g]) {
+          const float alpha = __builtin_amdgcn_exp2f(m[g] - mx);   // 0 when m = -inf
+          l[g] *= alpha;
+#pragma unroll
+          for (int i = 0; i < DL; ++i) acc[g][i] *= alpha;
+          m[g] = mx;
+        }
+        const float p = valid[u] ? __builtin_amdgcn_exp2f(s[g] - m[g]) : 0.0f;
+        l[g] += p;
+        const float pv = p * vs[u];
+#pragma unroll
+        for (int i = 0; i < DL; ++i) acc[g][i] = fmaf(pv, vf[i], acc[g][i]);
+      }
     }
   }
 
@@ -210,7 +236,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(
     if (mx != -INFINITY) {
 #pragma unroll
       for (int v = 0; v < kAttnWaves; ++v) {
-        const float f = exp2f(s_m[v][g] - mx);   // 0 for a wave without tokens
+        const float f = __builtin_amdgcn_exp2f(s_m[v][g] - mx);   // 0 for a wave without tokens
         num = fmaf(f, s_acc[v][g][d], num);
         den = fmaf(f, s_l[v][g], den);
       }
@@ -228,10 +254,10 @@ int dispatch_attn(int G, dim3 grid, hipStream_t st, int64_t H, int64_t KVH, int6
                   const float* vs, const int32_t* lens, float c, uint16_t* out) {
   const dim3 block(64 * kAttnWaves);
   switch (G) {
-    case 1: return launch(attn_decode_kernel<FMT, 1>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
-    case 2: return launch(attn_decode_kernel<FMT, 2>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
-    case 4: return launch(attn_decode_kernel<FMT, 4>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
-    case 8: return launch(attn_decode_kernel<FMT, 8>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
+    case 1: return launch(attn_decode_kernel<FMT, 1, 16, 4>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
+    case 2: return launch(attn_decode_kernel<FMT, 2, 16, 4>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
+    case 4: return launch(attn_decode_kernel<FMT, 4, 16, 4>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
+    case 8: return launch(attn_decode_kernel<FMT, 8, 8, 4>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
     default: return FP8BS_ERR_UNSUPPORTED;
   }
 }
