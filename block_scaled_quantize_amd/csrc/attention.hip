@@ -89,6 +89,23 @@ __device__ __forceinline__ Raw<DL> load_raw(const uint8_t* p) {
   }
   return r;
 }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// The codes as bf16 pairs (exact: every FP8 value is a bf16 value).
+template <int FMT, int DL>
+__device__ __forceinline__ void decode_raw_bf16(const Raw<DL>& r, bf16x2 (&f)[DL / 2]) {
+#pragma unroll
+  for (int i = 0; i < DL / 4; ++i) {
+    if constexpr (FMT == FP8BS_E4M3) {
+      f[2 * i] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.w[i], 1.0f, false);
+      f[2 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.w[i], 1.0f, true);
+    } else {
+      f[2 * i] = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(r.w[i], 1.0f, false);
+      f[2 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(r.w[i], 1.0f, true);
+    }
+  }
+}
+
 template <int FMT, int DL>
 __device__ __forceinline__ void decode_raw(const Raw<DL>& r, float (&f)[DL]) {
 #pragma unroll
@@ -117,20 +134,19 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(
   int64_t len = seq_lens[b];
   len = len < 0 ? 0 : (len > T ? T : len);
 
-  // queries of the group's heads, pre-multiplied by sm_scale * log2(e) (scores in base 2)
-  float qf[G][DL];
+  // queries of the group's heads as bf16 pairs: q . k is summed by v_dot2_f32_bf16 (exact
+  // products, fp32 sums) against the keys decoded to bf16
+  bf16x2 qb[G][DL / 2];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const uint16_t* qp = q + ((b * H + kvh * G + g) * 128 + d0);
 #pragma unroll
     for (int i = 0; i < DL; i += 8) {
       const uint4 v = *reinterpret_cast<const uint4*>(qp + i);
-      const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        qf[g][i + 2 * j] = bf16_lo(ws[j]) * score_scale;
-        qf[g][i + 2 * j + 1] = bf16_hi(ws[j]) * score_scale;
-      }
+      qb[g][i / 2] = __builtin_bit_cast(bf16x2, v.x);
+      qb[g][i / 2 + 1] = __builtin_bit_cast(bf16x2, v.y);
+      qb[g][i / 2 + 2] = __builtin_bit_cast(bf16x2, v.z);
+      qb[g][i / 2 + 3] = __builtin_bit_cast(bf16x2, v.w);
     }
   }
 
@@ -161,8 +177,9 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      float kf[DL], vf[DL];
-      decode_raw<FMT, DL>(kr[u], kf);
+      bf16x2 kb[DL / 2];
+      float vf[DL];
+      decode_raw_bf16<FMT, DL>(kr[u], kb);
       decode_raw<FMT, DL>(vr[u], vf);
       if (!valid[u]) {
         // (a lane past the end re-reads the last token: its values must not reach acc, not
@@ -175,10 +192,10 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(
       for (int g = 0; g < G; ++g) {
         float dot = 0.0f;
 #pragma unroll
-        for (int i = 0; i < DL; ++i) dot = fmaf(qf[g][i], kf[i], dot);
+        for (int i = 0; i < DL / 2; ++i) dot = __builtin_amdgcn_fdot2_f32_bf16(qb[g][i], kb[i], dot, false);
 #pragma unroll
         for (int off = 1; off < LPT; off <<= 1) dot += __shfl_xor(dot, off);
-        s[g] = valid[u] ? dot * ks[u] : -INFINITY;
+        s[g] = valid[u] ? dot * (ks[u] * score_scale) : -INFINITY;   // base-2 logits
       }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
