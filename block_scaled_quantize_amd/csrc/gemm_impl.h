@@ -107,9 +107,9 @@ struct GemmParams {
   int64_t lda;
   const uint8_t* B;   // weight side (rows n)
   int64_t ldb;
-  const float* sa;    // sa(m, kb) = sa[kb * sa_ks + (m / sa_rdiv) * sa_rs]
+  const float* sa;    // sa(m, kb) = sa[kb * sa_ks + (m >> sa_rshift) * sa_rs]
   int64_t sa_ks, sa_rs, sa_bytes;
-  int sa_rdiv;
+  int sa_rshift;
   const float* sb;    // sb(n, kb) = sb[kb * sb_ks + (n / 128) * sb_rs]
   int64_t sb_ks, sb_rs, sb_bytes;
   uint16_t* C;        // may be null when the output is only wanted quantized
@@ -294,18 +294,32 @@ __device__ __forceinline__ void wait_lds() {
   asm volatile("" ::: "memory");
 }
 
+// Wait until at most min(n, N) vector-memory operations are outstanding (n >= 0, made
+// wave-uniform here so that the choice is a scalar branch).
 template <int N>
-__device__ __forceinline__ void wait_vm_upto(int n) {
-  // n is wave-uniform and in {N, N+1, N+2}
-  if (n == N + 2) wait_vm<N + 2>();
-  else if (n == N + 1) wait_vm<N + 1>();
-  else wait_vm<N>();
+__device__ __forceinline__ void wait_vm_atmost(int n) {
+  if constexpr (N == 0) {
+    wait_vm<0>();
+  } else {
+    if (__builtin_amdgcn_readfirstlane(n) >= N) wait_vm<N>();
+    else wait_vm_atmost<N - 1>(n);
+  }
 }
 
-// ------------------------------------------------------------------ one output tile
-// Computes C[m0 .. m_end) x [n0 .. n0 + BN) (columns clipped to N) with the operand roles of
-// LAYOUT; A points at the activation-side matrix, Bw at the weight-side matrix of this tile's
-// group, sbw at the group's weight scales (sb_bytes bytes).
+// One output tile: group g (0 for a dense GEMM), rows [m0, m_end), columns from n0.
+struct Tile {
+  int g, m0, m_end, n0;
+};
+// Pipeline state a persistent workgroup carries from one tile to the next: the LDS stage that
+// holds the tile's first K block, whether that block was issued during the previous tile, and
+// how many store instructions (at least) the previous tile's epilogue issued after it.  Vector
+// memory operations complete in issue order (one vmcnt for loads, stores and LDS DMA), so
+// waiting until at most that many are outstanding means the block has landed while the stores
+// may still drain.
+struct Carry {
+  int stage0, prefetched, stores;
+};
+
 // E8M0 code of a power-of-two scale: its binary32 exponent field (2^-127, the one subnormal
 // power of two a scale can take, has field 0 and is E8M0 code 0 as well).
 __device__ __forceinline__ int e8m0_of(float s) {
@@ -393,12 +407,23 @@ __device__ __forceinline__ void quantize_out(const GemmParams& p, uint8_t* smem,
   }
 }
 
+// ------------------------------------------------------------------ one output tile
+// Computes C[m0 .. m_end) x [n0 .. n0 + BN) of tile t (columns clipped to N) with the operand
+// roles of LAYOUT: A is the activation-side matrix; the weight side and its scales are those of
+// the tile's group (p.B + g * b_group_stride, p.sb + g * sb_group_stride, sb_bytes bytes).
 // QO: fused quantization of the output into 1x128 blocks along N, 0 = none, else
 // 1 + 2 * format + (power-of-2 scale ? 1 : 0).
-template <class C, int LAYOUT, int FA, int FB, int SM, int QO = 0>
-__device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, int64_t m0,
-                                          int64_t m_end, int64_t n0, const uint8_t* Bw,
-                                          const float* sbw, int64_t sb_bytes) {
+// PF (persistent workgroups, two LDS stages, no fused quantization): when has_next and the tile
+// has at least two K blocks, the next tile's first K block is loaded into the free stage while
+// this tile's last block runs, and the next tile starts without waiting for this tile's stores.
+template <class C, int LAYOUT, int FA, int FB, int SM, int QO = 0, bool PF = false>
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, const Tile& t,
+                                          const Tile& nt, bool has_next, Carry& cy) {
+  static_assert(!PF || (C::kStages == 2 && QO == 0), "cross-tile prefetch: two stages, bf16 out");
+  const int64_t m0 = t.m0, m_end = t.m_end, n0 = t.n0;
+  const uint8_t* Bw = p.B + (int64_t)t.g * p.b_group_stride;
+  const float* sbw = p.sb + (int64_t)t.g * p.sb_group_stride;
+  const int64_t sb_bytes = p.sb_bytes;
   constexpr bool XK = LAYOUT != FP8BS_WGRAD;   // activation side K-major?
   constexpr bool WK = LAYOUT == FP8BS_FPROP;   // weight side K-major?
   constexpr bool ROWS = SM == kScaleFoldRows || SM == kScaleHwRows;   // 1x128 weight scales
@@ -406,45 +431,50 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
   constexpr bool HW = SM == kScaleHw || SM == kScaleHwRows;
   constexpr bool STAGED = SM != kScaleTensor;   // block scales staged in LDS with the operands
   constexpr int BM = C::BM, BN = C::BN, NI = C::kNI, NJ = C::kNJ;
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  // (opaque per tile: in a persistent loop, values derived from the thread id are recomputed for
+  // each tile instead of being kept live across the whole loop)
+  int tid = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int w = tid >> 6;
   const int wm = w % C::kWavesM, wn = w / C::kWavesM;
   const int li = lane & 15, g = lane >> 4;
   const int64_t K = p.K;
   const int nkb = (int)((K + 127) >> 7);
   const int krem = (int)(K - (int64_t)(nkb - 1) * 128);
   const uint32_t lds0 = lds_addr(smem);
-  const int64_t nblk0 = n0 >> 7;
+  const int st0 = PF ? cy.stage0 : 0;   // LDS stage of block 0
+  // the next tile's first K block is loaded during this tile (as "block nkb")
+  const bool pf_live = PF && has_next && nkb >= 2;
 
-  // DMA source offsets (fixed across K blocks).
+  // DMA source offsets relative to a tile's origin (the same for every K block and tile).
   uint32_t xoff[C::kXLoads], woff[C::kWLoads];
 #pragma unroll
   for (int q = 0; q < C::kXLoads; ++q) xoff[q] = dma_voffset<XK>(w * C::kXLoads + q, lane, p.lda);
 #pragma unroll
   for (int q = 0; q < C::kWLoads; ++q) woff[q] = dma_voffset<WK>(w * C::kWLoads + q, lane, p.ldb);
-  const bool sa_loader = w < C::kSaWaves;
-  const bool sb_loader = ROWS ? (w >= C::kSbRowWave0 && w < C::kSbRowWave0 + C::kSbRowWaves)
-                              : w == C::kSbWave;
-  uint32_t saoff = 0xFFFFFFFFu, sboff = 0xFFFFFFFFu;
-  {
-    const int64_t row = m0 + w * 64 + lane;
-    if (row < m_end) saoff = (uint32_t)(((row / p.sa_rdiv) * p.sa_rs) * 4);
-    if constexpr (ROWS) {
-      // weight scale words n0 + 64 (w - w0) + lane (columns past N read as zero)
-      const int64_t n = n0 + (int64_t)(w - C::kSbRowWave0) * 64 + lane;
-      if (sb_loader && n < p.N) sboff = (uint32_t)(n * p.sb_rs * 4);
-    } else {
-      const int64_t nb = nblk0 + lane;
-      if (lane < BN / 128 && nb * 128 < p.N) sboff = (uint32_t)(nb * p.sb_rs * 4);
-    }
+  const int wu = __builtin_amdgcn_readfirstlane(w);   // (the wave index, as a scalar)
+  const bool sa_loader = wu < C::kSaWaves;
+  const bool sb_loader = ROWS ? (wu >= C::kSbRowWave0 && wu < C::kSbRowWave0 + C::kSbRowWaves)
+                              : wu == C::kSbWave;
+  // Scale words: tile row w * 64 + lane, and the weight scales of the tile's 128-column blocks
+  // (1x128 weight scales: tile column 64 (w - w0) + lane).  Rows past m_end and columns past N
+  // read other tiles' scales or, past the array, zeros; their outputs are never stored.  The
+  // tile's first scale row (m0 is a multiple of 128 whenever rows share a scale) and column
+  // block are added to the descriptor base.
+  uint32_t saoff = (uint32_t)((int64_t)((w * 64 + lane) >> p.sa_rshift) * p.sa_rs * 4);
+  uint32_t sboff = 0xFFFFFFFFu;
+  if constexpr (ROWS) {
+    if (sb_loader) sboff = (uint32_t)((int64_t)((w - C::kSbRowWave0) * 64 + lane) * p.sb_rs * 4);
+  } else {
+    if (lane < BN / 128) sboff = (uint32_t)((int64_t)lane * p.sb_rs * 4);
   }
 
-  // Rows of each stored operand, for the descriptor bounds.
-  const int64_t a_rows = XK ? m_end : K;
-  const int64_t w_rows = WK ? p.N : K;
-
   // DMA instructions per K block issued by each wave (vmcnt is counted per wave).
-  constexpr int kPerStage = C::kXLoads + C::kWLoads + (STAGED ? 2 : 0);
+  // Scale DMA instructions per wave and block: one when the activation-scale loaders and the
+  // weight-scale loaders are different waves (every tile configuration with 8 waves), else two.
+  constexpr bool kOneScale = C::kSaWaves + (ROWS ? C::kSbRowWaves : 1) <= C::kWaves;
+  constexpr int kPerStage = C::kXLoads + C::kWLoads + (STAGED ? (kOneScale ? 1 : 2) : 0);
   // A block's DMA starts as soon as its slot is free, right after the barrier that ends the
   // slot's previous block: one instruction after each MFMA unit of the last piece before the
   // hand-over, the rest one per MFMA unit at the start of the next block.  (A burst would leave
@@ -460,39 +490,54 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
     u32x4 x, w, sa, sb;
     uint32_t sbase;
   };
-  auto block_dma = [&](int kb) {
+  // NX (PF only): the block is "block nkb", the next tile's first block; its descriptors are
+  // built only in the two blocks that issue it, so the next tile adds no live registers to the
+  // common block.
+  auto block_dma = [&](int kb, auto nx_tag) {
+    constexpr bool NX = decltype(nx_tag)::value;
     BlockDma d;
-    d.sbase = lds0 + (kb % C::kStages) * C::kStage;
-    const int64_t k0 = (int64_t)kb * 128;
+    d.sbase = lds0 + ((kb + st0) % C::kStages) * C::kStage;
+    const bool live = NX ? pf_live : kb < nkb;
+    int64_t tm0 = m0, tme = m_end, tn0 = n0, kk = kb;
+    const uint8_t* tBw = Bw;
+    const float* tsb = sbw;
+    if constexpr (NX) {
+      tm0 = nt.m0; tme = nt.m_end; tn0 = nt.n0; kk = 0;
+      tBw = p.B + (int64_t)nt.g * p.b_group_stride;
+      tsb = p.sb + (int64_t)nt.g * p.sb_group_stride;
+    }
+    const int64_t k0 = kk * 128;
     {
       const uint8_t* base;
       int64_t avail;
-      if constexpr (XK) {
-        base = p.A + m0 * p.lda + k0;
-        avail = (a_rows - m0) * p.lda - k0;
+      if constexpr (XK) {   // rows past the tile's m_end read as zero
+        base = p.A + tm0 * p.lda + k0;
+        avail = (tme - tm0) * p.lda - k0;
       } else {
-        base = p.A + k0 * p.lda + m0;
-        avail = (a_rows - k0) * p.lda - m0;
+        base = p.A + k0 * p.lda + tm0;
+        avail = (K - k0) * p.lda - tm0;
       }
-      d.x = make_rsrc(base, (avail > 0 && kb < nkb) ? (uint64_t)avail : 0);
+      d.x = make_rsrc(base, (avail > 0 && live) ? (uint64_t)avail : 0);
     }
     {
       const uint8_t* base;
       int64_t avail;
       if constexpr (WK) {
-        base = Bw + n0 * p.ldb + k0;
-        avail = (w_rows - n0) * p.ldb - k0;
+        base = tBw + tn0 * p.ldb + k0;
+        avail = (p.N - tn0) * p.ldb - k0;
       } else {
-        base = Bw + k0 * p.ldb + n0;
-        avail = (w_rows - k0) * p.ldb - n0;
+        base = tBw + k0 * p.ldb + tn0;
+        avail = (K - k0) * p.ldb - tn0;
       }
-      d.w = make_rsrc(base, (avail > 0 && kb < nkb) ? (uint64_t)avail : 0);
+      d.w = make_rsrc(base, (avail > 0 && live) ? (uint64_t)avail : 0);
     }
     if constexpr (STAGED) {
-      const int64_t offa = kb * p.sa_ks, lefta = p.sa_bytes - offa * 4;
-      d.sa = make_rsrc(p.sa + offa, (lefta > 0 && kb < nkb) ? (uint64_t)lefta : 0);
-      const int64_t offb = kb * p.sb_ks, leftb = sb_bytes - offb * 4;
-      d.sb = make_rsrc(sbw + offb, (leftb > 0 && kb < nkb) ? (uint64_t)leftb : 0);
+      const int64_t offa = kk * p.sa_ks + (tm0 >> p.sa_rshift) * p.sa_rs;
+      const int64_t lefta = p.sa_bytes - offa * 4;
+      d.sa = make_rsrc(p.sa + offa, (lefta > 0 && live) ? (uint64_t)lefta : 0);
+      const int64_t offb = kk * p.sb_ks + (ROWS ? tn0 : (tn0 >> 7)) * p.sb_rs;
+      const int64_t leftb = sb_bytes - offb * 4;
+      d.sb = make_rsrc(tsb + offb, (leftb > 0 && live) ? (uint64_t)leftb : 0);
     }
     return d;
   };
@@ -503,11 +548,19 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
       const int qw = q - C::kXLoads;
       dma16(d.w, woff[qw],
             __builtin_amdgcn_readfirstlane(d.sbase + C::kXBytes + (w * C::kWLoads + qw) * 1024));
+    } else if (kOneScale && q == C::kXLoads + C::kWLoads) {
+      // Scales of the K block: one activation word per tile row (waves [0, kSaWaves)) and the
+      // weight words (the weight-scale loaders); every wave issues one such instruction, so
+      // the block needs no branch: the remaining waves read outside the descriptor into the
+      // dummy slot.
+      const uint32_t sbdst = d.sbase + C::kXBytes + C::kWBytes + BM * 4 +
+                             (ROWS ? (wu - C::kSbRowWave0) * 256 : 0);
+      dma4(sa_loader ? d.sa : d.sb, sa_loader ? saoff : (sb_loader ? sboff : 0xFFFFFFFFu),
+           __builtin_amdgcn_readfirstlane(
+               sa_loader ? d.sbase + C::kXBytes + C::kWBytes + wu * 256
+                         : (sb_loader ? sbdst : lds0 + C::kDummy)));
     } else if (q == C::kXLoads + C::kWLoads) {
-      // Scales of the K block: one activation word per tile row, then one weight word per
-      // 128-column block of the tile (lanes past those read outside the descriptor: zeros).
-      // Every wave issues both scale DMAs, so that the block needs no branch: a wave that
-      // loads no scale reads outside the descriptor into the dummy slot.
+      // (two scale instructions per wave: activation words, then weight words)
       dma4(d.sa, sa_loader ? saoff : 0xFFFFFFFFu,
            __builtin_amdgcn_readfirstlane(sa_loader ? d.sbase + C::kXBytes + C::kWBytes + w * 256
                                                     : lds0 + C::kDummy));
@@ -518,8 +571,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
            __builtin_amdgcn_readfirstlane(sb_loader ? dst : lds0 + C::kDummy));
     }
   };
-  auto issue = [&](int kb) {
-    const BlockDma d = block_dma(kb);
+  auto issue = [&](int kb, auto nx_tag) {
+    const BlockDma d = block_dma(kb, nx_tag);
 #pragma unroll
     for (int q = 0; q < kPerStage; ++q) dma_part(d, q);
   };
@@ -543,7 +596,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
     if constexpr (C::kStages == 3) wait_vm<kPerStage>();
     else wait_vm<0>();
   };
-  auto stage_ptr = [&](int kb) { return smem + (kb % C::kStages) * C::kStage; };
+  auto stage_ptr = [&](int kb) { return smem + ((kb + st0) % C::kStages) * C::kStage; };
   auto prepare = [&](int kb) {
     // ragged K: the last block's bytes past K are zeroed before anyone reads them
     if (kb == nkb - 1 && krem < 128 && (XK || WK)) {
@@ -596,7 +649,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
     return frag_at<WK>(st + C::kXBytes, wb, wn * C::kWTN + 16 * i);
   };
 
-  for (int s = 0; s + 1 < C::kStages; ++s) issue(s);
+  const bool prefetched = PF && cy.prefetched;   // block 0 was issued by the previous tile
+  if (!prefetched)
+    for (int s = 0; s + 1 < C::kStages; ++s) issue(s, std::false_type{});
   v8i wf[NI], xf;
   float ccur = 0.0f, sbv = 1.0f, cprev = 0.0f;
   v4f sbr[NI], P[NI];
@@ -604,7 +659,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
 #pragma unroll
   for (int i = 0; i < NI; ++i) P[i] = v4f{0.f, 0.f, 0.f, 0.f};   // pending products (fold)
   if (nkb > 0) {
-    wait_next();
+    // block 0 issued during the previous tile: only that tile's later stores may be pending
+    if (prefetched) wait_vm_atmost<NI * NJ>(cy.stores);
+    else wait_next();
     barrier();
     prepare(0);
     const uint8_t* st = stage_ptr(0);
@@ -614,9 +671,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
     fold_row_scales(st, sbr);
     mfma_row_scales(st, wbr);
     if constexpr (kBurst) {
-      issue(C::kStages - 1);
+      issue(C::kStages - 1, std::false_type{});
     } else {
-      const BlockDma d = block_dma(C::kStages - 1);   // its first NI instructions
+      const BlockDma d = block_dma(C::kStages - 1, std::false_type{});   // its first NI instructions
 #pragma unroll
       for (int q = 0; q < NI && q < kPerStage; ++q) dma_part(d, q);
     }
@@ -637,10 +694,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
 #pragma unroll
     for (int t = 0; t < (WK ? 2 : 4); ++t) asm volatile("" : "+v"(wb.a[t]));
     // DMA of block kb + kStages - 1 (into the slot of block kb - 1): its first NI instructions
-    // were issued at the previous hand-over, the rest go here (the last block has none: that
-    // block would be past K).  DMA of block kb + kStages: started at this block's hand-over.
+    // were issued at the previous hand-over, the rest go here (in the last block only when it
+    // is the next tile's first block, PF).  DMA of block kb + kStages: started at this block's
+    // hand-over.
+    constexpr bool CONT = (TURN || PF) && !kBurst;
     BlockDma dcont, dturn;
-    if constexpr (TURN && !kBurst) dcont = block_dma(kb + C::kStages - 1);
+    // (in the last block, PF: the next tile's first block)
+    if constexpr (CONT) dcont = block_dma(kb + C::kStages - 1, std::bool_constant<!TURN>{});
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int mrow = wm * C::kWTM + 16 * j + li;
@@ -658,7 +718,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
         wait_next();
         barrier();
         if constexpr (PREP) prepare(kb + 1);
-        if constexpr (!kBurst) dturn = block_dma(kb + C::kStages);
+        if constexpr (!kBurst) dturn = block_dma(kb + C::kStages, std::bool_constant<PF && PREP>{});
         first_x(stn, xnext, cnext, sbv);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -696,7 +756,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
         if (turn) {
           wf[i] = w_fragment(stn, i);
           if (!kBurst && i < kPerStage) dma_part(dturn, i);
-        } else if constexpr (TURN && !kBurst) {
+        } else if constexpr (CONT) {
           const int q = NI + j * NI + i;
           if (q < kPerStage) dma_part(dcont, q);
         }
@@ -704,7 +764,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
       }
       if (turn) {
         mfma_row_scales(stn, wbr);
-        if constexpr (kBurst) issue(kb + C::kStages);
+        if constexpr (kBurst) issue(kb + C::kStages, std::bool_constant<PF && PREP>{});
         __builtin_amdgcn_sched_barrier(0);
       }
       if (j == 0) {
@@ -721,7 +781,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
   for (int kb = 0; kb + 2 < nkb; ++kb) run_block(kb, std::true_type{}, std::false_type{});
   if (nkb >= 2) run_block(nkb - 2, std::true_type{}, std::true_type{});
   if (nkb >= 1) run_block(nkb - 1, std::false_type{}, std::false_type{});
-  wait_vm<0>();   // DMAs of blocks past the last
+  if (!pf_live) wait_vm<0>();   // DMAs of blocks past the last
   if constexpr (FOLD) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -760,6 +820,18 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
     }
   }
   if constexpr (QO != 0) quantize_out<C, SM, QO>(p, smem, acc, post, nkb, m0, m_end, n0);
+  if constexpr (PF) {
+    // Store instructions the wave issued above, at least: one per (n piece, m piece) whose first
+    // column and row lie inside the output (a lane of that piece stores).
+    int iv = 0, jv = 0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) jv += (m0 + wm * C::kWTM + 16 * j < m_end) ? 1 : 0;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) iv += (n0 + wn * C::kWTN + 16 * i < p.N) ? 1 : 0;
+    cy.stores = p.C ? iv * jv : 0;
+    cy.prefetched = pf_live ? 1 : 0;
+    cy.stage0 = (st0 + nkb) % C::kStages;
+  }
 }
 
 // Map a linear workgroup id to a tile so that each of the 8 XCDs (ids are dealt round robin)
@@ -783,38 +855,39 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int tm, tn;
   tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * C::BM;
-  gemm_tile<C, LAYOUT, FA, FB, SM, QO>(p, smem, m0, std::min<int64_t>(m0 + C::BM, p.M),
-                                   (int64_t)tn * C::BN, p.B, p.sb, p.sb_bytes);
-}
-
-__device__ __forceinline__ int64_t uniform64(int64_t v) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
+  const int m0 = tm * C::BM;
+  const Tile t{0, m0, (int)std::min<int64_t>((int64_t)m0 + C::BM, p.M), tn * C::BN};
+  Carry cy{0, 0, 0};
+  gemm_tile<C, LAYOUT, FA, FB, SM, QO>(p, smem, t, t, false, cy);
 }
 
 // Grouped: a persistent grid walks the concatenation of every group's m tiles (times the n
-// tiles).  Each workgroup first builds the prefix count of m tiles per group in LDS, then maps
-// each of its tiles to (group, m tile, n tile) by binary search.
+// tiles).  Each workgroup first builds, in LDS, the group bounds (clamped to [0, M] and made
+// non-decreasing) and the prefix count of m tiles per group, then maps each of its tiles to
+// (group, m tile, n tile) by binary search.  With two LDS stages the next tile's first K block
+// is loaded while the current tile finishes (see gemm_tile).
 constexpr int kMaxGroups = 1024;
 
 template <class C, int FA, int FB, int SM>
 __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_prefix[kMaxGroups + 1];
+  __shared__ int s_lo[kMaxGroups + 1];   // clamped group offsets (M < 2^31)
   __shared__ int s_wave_sum[C::kWaves];
   constexpr int BM = C::BM;
+  constexpr bool PF = C::kStages == 2;
   const int G = p.num_groups;
-  // m tiles per group (offsets clamped to [0, M] and made non-decreasing), prefix-summed
+  for (int gi = threadIdx.x; gi <= G; gi += C::kThreads)
+    s_lo[gi] = (int)std::min<int64_t>(std::max<int64_t>(p.offsets[gi], 0), p.M);
+  __syncthreads();
+  // m tiles per group, prefix-summed
   int carry = 0;
   for (int base = 0; base < G; base += C::kThreads) {
     const int gi = base + threadIdx.x;
     int tiles = 0;
     if (gi < G) {
-      const int64_t lo = std::min<int64_t>(std::max<int64_t>(p.offsets[gi], 0), p.M);
-      const int64_t hi = std::min<int64_t>(std::max<int64_t>(p.offsets[gi + 1], lo), p.M);
-      tiles = (int)((hi - lo + BM - 1) / BM);
+      const int lo = s_lo[gi], hi = std::max(s_lo[gi + 1], lo);
+      tiles = (hi - lo + BM - 1) / BM;
     }
     int v = tiles;
     const int lane = threadIdx.x & 63;
@@ -836,8 +909,34 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(GemmParams
   if (threadIdx.x == 0) s_prefix[0] = 0;
   __syncthreads();
   const int m_tiles = s_prefix[G];
-  const int total = m_tiles * p.tiles_n;
-  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+  const int tiles_n = p.tiles_n;
+  const int total = m_tiles * tiles_n;
+  // Workgroup id + k * gridDim stays on the XCD of the workgroup (the grid is a multiple of 8),
+  // and tile_of gives each XCD a contiguous range of the concatenated tiles in groups of m
+  // tiles, so the 32 workgroups of an XCD share A rows and expert weight tiles in its L2.
+  auto tile_at = [&](int id) {
+    int mt, tn;
+    tile_of(id, m_tiles, tiles_n, mt, tn);
+    int lo = 0, hi = G - 1;   // last group with s_prefix[g] <= mt
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_prefix[mid] <= mt) lo = mid; else hi = mid - 1;
+    }
+    // (the same in every lane: kept in scalar registers)
+    const int gi = __builtin_amdgcn_readfirstlane(lo);
+    const int glo = __builtin_amdgcn_readfirstlane(s_lo[gi]);
+    const int ghi = std::max(__builtin_amdgcn_readfirstlane(s_lo[gi + 1]), glo);
+    const int m0 = glo + __builtin_amdgcn_readfirstlane(mt - s_prefix[gi]) * BM;
+    return Tile{gi, m0, std::min(m0 + BM, ghi), __builtin_amdgcn_readfirstlane(tn) * C::BN};
+  };
+  int id = blockIdx.x;
+  if (id >= total) return;
+  Tile cur = tile_at(id);
+  Carry cy{0, 0, 0};
+  while (true) {
+    const int nid = id + (int)gridDim.x;
+    const bool has_next = nid < total;
+    const Tile nxt = has_next ? tile_at(nid) : cur;
     // The parameters are read again from the argument segment for every tile (scalar loads),
     // so that values derived from them are not kept live across the whole tile loop.
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -848,25 +947,11 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(GemmParams
 #else
     const GemmParams& q = p;   // (host pass: the body is never run there)
 #endif
-    const int mt = tile / q.tiles_n, tn = tile % q.tiles_n;
-    int lo = 0, hi = G - 1;   // last group with s_prefix[g] <= mt
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_prefix[mid] <= mt) lo = mid; else hi = mid - 1;
-    }
-    // (the tile's group and rows are the same in every lane: reading them as wave-uniform keeps
-    // the tile's address arithmetic in scalar registers)
-    const int gi = __builtin_amdgcn_readfirstlane(lo);
-    const int64_t glo =
-        uniform64(std::min<int64_t>(std::max<int64_t>(q.offsets[gi], 0), q.M));
-    const int64_t ghi =
-        uniform64(std::min<int64_t>(std::max<int64_t>(q.offsets[gi + 1], glo), q.M));
-    const int64_t m0 = glo + (int64_t)__builtin_amdgcn_readfirstlane(mt - s_prefix[gi]) * BM;
-    gemm_tile<C, FP8BS_FPROP, FA, FB, SM>(q, smem, m0, std::min<int64_t>(m0 + BM, ghi),
-                                          (int64_t)tn * C::BN, q.B + gi * q.b_group_stride,
-                                          q.sb + gi * q.sb_group_stride,
-                                          q.sb_group_stride * 4);
-    __syncthreads();   // the next tile refills the LDS stages
+    gemm_tile<C, FP8BS_FPROP, FA, FB, SM, 0, PF>(q, smem, cur, nxt, has_next, cy);
+    if (!has_next) break;
+    if (!cy.prefetched) __syncthreads();   // the next tile refills the LDS stages
+    cur = nxt;
+    id = nid;
   }
 }
 
@@ -943,25 +1028,25 @@ int dispatch_dense(int layout, int fa, int fb, const GemmParams& p, hipStream_t 
 // kmajor: the operand is stored [rows, K] (else [K, rows]).
 struct ScaleIndex {
   int64_t ks, rs, bytes;
-  int rdiv;
+  int rshift;   // scale row of operand row r: r >> rshift
 };
 
 bool scale_index(int gran, bool kmajor, bool weight_side, int64_t rows, int64_t K,
                  ScaleIndex& s) {
   const int64_t kblocks = ceil_div(K, 128), rblocks = ceil_div(rows, 128);
   if (gran == FP8BS_PER_TENSOR) {
-    s = {0, 0, 4, 1};
+    s = {0, 0, 4, 0};
     return true;
   }
   if (gran == FP8BS_BLOCK_1x128) {
     if (!kmajor) return false;                  // 1x128 blocks run along K: K-major operands only
     (void)weight_side;
-    s = {rows, 1, kblocks * rows * 4, 1};       // float[K/128][rows]
+    s = {rows, 1, kblocks * rows * 4, 0};       // float[K/128][rows]
     return true;
   }
   if (gran == FP8BS_BLOCK_128x128) {
-    if (kmajor) s = {1, kblocks, rblocks * kblocks * 4, 128};   // float[rows/128][K/128]
-    else s = {rblocks, 1, kblocks * rblocks * 4, 128};          // float[K/128][rows/128]
+    if (kmajor) s = {1, kblocks, rblocks * kblocks * 4, 7};   // float[rows/128][K/128]
+    else s = {rblocks, 1, kblocks * rblocks * 4, 7};          // float[K/128][rows/128]
     return true;
   }
   return false;
@@ -1031,7 +1116,7 @@ inline int dense_params(int layout, int64_t M, int64_t N, int64_t K, const void*
   p.M = M; p.N = N; p.K = K;
   p.A = static_cast<const uint8_t*>(A); p.lda = lda;
   p.B = static_cast<const uint8_t*>(B); p.ldb = ldb;
-  p.sa = scale_inv_a; p.sa_ks = sa.ks; p.sa_rs = sa.rs; p.sa_bytes = sa.bytes; p.sa_rdiv = sa.rdiv;
+  p.sa = scale_inv_a; p.sa_ks = sa.ks; p.sa_rs = sa.rs; p.sa_bytes = sa.bytes; p.sa_rshift = sa.rshift;
   p.sb = scale_inv_b; p.sb_ks = sb.ks; p.sb_rs = sb.rs; p.sb_bytes = sb.bytes;
   p.C = static_cast<uint16_t*>(C_bf16); p.ldc = ldc;
   p.c_vec = (reinterpret_cast<uintptr_t>(C_bf16) % 8 == 0) && (ldc % 4 == 0);
@@ -1066,7 +1151,7 @@ inline int grouped_params(int32_t num_groups, const int64_t* group_offsets, int6
   p.M = total_M; p.N = N; p.K = K;
   p.A = static_cast<const uint8_t*>(A); p.lda = lda;
   p.B = static_cast<const uint8_t*>(B); p.ldb = ldb;
-  p.sa = scale_inv_a; p.sa_ks = total_M; p.sa_rs = 1; p.sa_rdiv = 1;
+  p.sa = scale_inv_a; p.sa_ks = total_M; p.sa_rs = 1; p.sa_rshift = 0;
   p.sa_bytes = ceil_div(K, 128) * total_M * 4;
   p.sb = scale_inv_b; p.sb_ks = 1; p.sb_rs = ceil_div(K, 128);
   p.C = static_cast<uint16_t*>(C_bf16); p.ldc = ldc;
@@ -1075,6 +1160,7 @@ inline int grouped_params(int32_t num_groups, const int64_t* group_offsets, int6
   p.num_groups = num_groups;
   p.b_group_stride = N * ldb;
   p.sb_group_stride = ceil_div(N, 128) * ceil_div(K, 128);
+  p.sb_bytes = p.sb_group_stride * 4;   // one group's weight scales
   return FP8BS_OK;
 }
 
