@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
 }
 
 // ---------------------------------------------------------------- decode attention
-constexpr int kAttnWaves = 4;
+constexpr int kAttnWaves = 4;   // waves per workgroup (one workgroup per sequence and KV head)
 
 // Two FP8 codes (bytes 0, 1 of w, or 2, 3 for HIGH) to fp32.
 template <int FMT, bool HIGH>
@@ -115,8 +115,8 @@ __device__ __forceinline__ void decode_raw(const Raw<DL>& r, float (&f)[DL]) {
   }
 }
 
-template <int FMT, int G, int DLANE, int KBATCH>
-__global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(
+template <int FMT, int G, int DLANE, int KBATCH, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void attn_decode_kernel(
     int64_t H, int64_t KVH, int64_t T, const uint16_t* __restrict__ q,
     const uint8_t* __restrict__ k_codes, const float* __restrict__ k_si,
     const uint8_t* __restrict__ v_codes, const float* __restrict__ v_si,
@@ -125,8 +125,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(
   constexpr int LPT = 128 / DL;         // lanes per token
   constexpr int TPS = 64 / LPT;         // tokens per wave step
   constexpr int kBatch = KBATCH;        // wave steps whose loads are in flight together
-  __shared__ float s_acc[kAttnWaves][G][128];
-  __shared__ float s_m[kAttnWaves][G], s_l[kAttnWaves][G];
+  __shared__ float s_acc[WAVES][G][128];
+  __shared__ float s_m[WAVES][G], s_l[WAVES][G];
 
   const int64_t b = blockIdx.x / KVH, kvh = blockIdx.x % KVH;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -161,13 +161,13 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(
 
   // Steps are taken kBatch at a time: the loads of all of them are issued before any is used,
   // so that each wave keeps kBatch steps of cache rows in flight.
-  for (int64_t step0 = w; step0 * TPS < len; step0 += kAttnWaves * kBatch) {
+  for (int64_t step0 = w; step0 * TPS < len; step0 += WAVES * kBatch) {
     Raw<DL> kr[kBatch], vr[kBatch];
     float ks[kBatch], vs[kBatch];
     bool valid[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int64_t t = (step0 + u * kAttnWaves) * TPS + tg;
+      const int64_t t = (step0 + u * WAVES) * TPS + tg;
       valid[u] = t < len;
       const int64_t row = (b * T + (valid[u] ? t : len - 1)) * KVH + kvh;   // in bounds
       kr[u] = load_raw<DL>(k_codes + row * 128 + d0);
@@ -175,19 +175,13 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(
       ks[u] = k_si[row];
       vs[u] = v_si[row];
     }
+    // The batch's scores first, so that the running maximum is reduced across lanes once per
+    // batch and head; then the probabilities and the value sums.
+    float s[kBatch][G];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       bf16x2 kb[DL / 2];
-      float vf[DL];
       decode_raw_bf16<FMT, DL>(kr[u], kb);
-      decode_raw<FMT, DL>(vr[u], vf);
-      if (!valid[u]) {
-        // (a lane past the end re-reads the last token: its values must not reach acc, not
-        // even as 0 * inf)
-#pragma unroll
-        for (int i = 0; i < DL; ++i) vf[i] = 0.0f;
-      }
-      float s[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float dot = 0.0f;
@@ -195,25 +189,41 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(
         for (int i = 0; i < DL / 2; ++i) dot = __builtin_amdgcn_fdot2_f32_bf16(qb[g][i], kb[i], dot, false);
 #pragma unroll
         for (int off = 1; off < LPT; off <<= 1) dot += __shfl_xor(dot, off);
-        s[g] = valid[u] ? dot * (ks[u] * score_scale) : -INFINITY;   // base-2 logits
+        s[u][g] = valid[u] ? dot * (ks[u] * score_scale) : -INFINITY;   // base-2 logits
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float mx = s[0][g];
+#pragma unroll
+      for (int u = 1; u < kBatch; ++u) mx = fmaxf(mx, s[u][g]);
+#pragma unroll
+      for (int off = LPT; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      // the batch maximum is the same in every lane: a scalar branch, taken only when the
+      // running maximum grows (then the sums are rescaled; -inf for a batch without a token
+      // never is)
+      mx = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(mx)));
+      if (mx > m[g]) {
+        const float alpha = __builtin_amdgcn_exp2f(m[g] - mx);   // 0 when m = -inf
+        l[g] *= alpha;
+#pragma unroll
+        for (int i = 0; i < DL; ++i) acc[g][i] *= alpha;
+        m[g] = mx;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      float vf[DL];
+      decode_raw<FMT, DL>(vr[u], vf);
+      if (!valid[u]) {
+        // (a lane past the end re-reads the last token: its values must not reach acc, not
+        // even as 0 * inf)
+#pragma unroll
+        for (int i = 0; i < DL; ++i) vf[i] = 0.0f;
       }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        float mx = s[g];
-#pragma unroll
-        for (int off = LPT; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-        // the step maximum is the same in every lane: a scalar branch, taken only when the
-        // running maximum grows (then the sums are rescaled; -inf for a step without a token
-        // never is)
-        mx = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(mx)));
-        if (mx > m[g]) {
-          const float alpha = __builtin_amdgcn_exp2f(m[g] - mx);   // 0 when m = -inf
-          l[g] *= alpha;
-#pragma unroll
-          for (int i = 0; i < DL; ++i) acc[g][i] *= alpha;
-          m[g] = mx;
-        }
-        const float p = valid[u] ? __builtin_amdgcn_exp2f(s[g] - m[g]) : 0.0f;
+        const float p = valid[u] ? __builtin_amdgcn_exp2f(s[u][g] - m[g]) : 0.0f;
         l[g] += p;
         const float pv = p * vs[u];
 #pragma unroll
@@ -244,15 +254,15 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(
     }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * 128; idx += 64 * kAttnWaves) {
+  for (int idx = threadIdx.x; idx < G * 128; idx += 64 * WAVES) {
     const int g = idx >> 7, d = idx & 127;
     float mx = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < kAttnWaves; ++v) mx = fmaxf(mx, s_m[v][g]);
+    for (int v = 0; v < WAVES; ++v) mx = fmaxf(mx, s_m[v][g]);
     float num = 0.0f, den = 0.0f;
     if (mx != -INFINITY) {
 #pragma unroll
-      for (int v = 0; v < kAttnWaves; ++v) {
+      for (int v = 0; v < WAVES; ++v) {
         const float f = __builtin_amdgcn_exp2f(s_m[v][g] - mx);   // 0 for a wave without tokens
         num = fmaf(f, s_acc[v][g][d], num);
         den = fmaf(f, s_l[v][g], den);
@@ -271,10 +281,10 @@ int dispatch_attn(int G, dim3 grid, hipStream_t st, int64_t H, int64_t KVH, int6
                   const float* vs, const int32_t* lens, float c, uint16_t* out) {
   const dim3 block(64 * kAttnWaves);
   switch (G) {
-    case 1: return launch(attn_decode_kernel<FMT, 1, 16, 4>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
-    case 2: return launch(attn_decode_kernel<FMT, 2, 16, 4>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
-    case 4: return launch(attn_decode_kernel<FMT, 4, 16, 4>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
-    case 8: return launch(attn_decode_kernel<FMT, 8, 8, 4>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
+    case 1: return launch(attn_decode_kernel<FMT, 1, 16, 4, kAttnWaves>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
+    case 2: return launch(attn_decode_kernel<FMT, 2, 16, 4, kAttnWaves>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
+    case 4: return launch(attn_decode_kernel<FMT, 4, 16, 4, kAttnWaves>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
+    case 8: return launch(attn_decode_kernel<FMT, 8, 8, 4, kAttnWaves>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
     default: return FP8BS_ERR_UNSUPPORTED;
   }
 }
