@@ -17,9 +17,13 @@
 // Decode attention (HBM-bound: every cached byte is read once per step): one workgroup of 4
 // waves per (sequence, KV head).  A wave takes 8 tokens per step (G <= 4 query heads per KV
 // head; 4 tokens for G = 8), 8 (16) lanes per token, each lane 16 (8) consecutive elements of
-// the key and value rows; dot products are reduced over the token's lanes, the softmax is kept
-// online in base 2 (running maximum per head, wave-uniform; running sums per lane), and the
-// four waves' partial results are merged through LDS at the end.
+// the key and value rows, 4 steps per batch with all their loads in flight; dot products are
+// reduced over the token's lanes, the softmax is kept online in base 2 (running maximum per
+// head, wave-uniform, reduced across lanes once per batch; running sums per lane), and the
+// four waves' partial results are merged through LDS at the end.  For G <= 4 the value sums of
+// a batch (32 tokens) run on the matrix cores: the probabilities (x value factors) of each head,
+// split into bf16 hi + lo terms, times the value codes decoded exactly to bf16, read back from
+// LDS transposed (ds_read_b64_tr_b8) -- two v_mfma_f32_16x16x32_bf16 per 16 elements.
 #include <math.h>
 
 #include "common.h"
@@ -90,6 +94,27 @@ __device__ __forceinline__ Raw<DL> load_raw(const uint8_t* p) {
   return r;
 }
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+
+// Eight FP8 codes (bytes of w.x then w.y) as bf16 (exact).
+template <int FMT>
+__device__ __forceinline__ bf16x8 decode8_bf16(v2i w) {
+  bf16x2 a, b, c, d;
+  if constexpr (FMT == FP8BS_E4M3) {
+    a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false);
+    b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true);
+    c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false);
+    d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true);
+  } else {
+    a = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w.x, 1.0f, false);
+    b = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w.x, 1.0f, true);
+    c = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w.y, 1.0f, false);
+    d = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w.y, 1.0f, true);
+  }
+  return bf16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
 
 // The codes as bf16 pairs (exact: every FP8 value is a bf16 value).
 template <int FMT, int DL>
@@ -125,8 +150,19 @@ __global__ __launch_bounds__(64 * WAVES) void attn_decode_kernel(
   constexpr int LPT = 128 / DL;         // lanes per token
   constexpr int TPS = 64 / LPT;         // tokens per wave step
   constexpr int kBatch = KBATCH;        // wave steps whose loads are in flight together
+  // PVM: the value sums of a batch (32 tokens) run on the matrix cores as one
+  // v_mfma_f32_16x16x32_bf16 per 16 elements: A = probabilities (rows = heads, k = tokens),
+  // B = values (k = tokens, columns = elements), both in bf16 (FP8 codes decode exactly).
+  constexpr bool PVM = DL == 16;
+  constexpr int KT = kBatch * TPS;      // tokens per batch
+  static_assert(!PVM || (KT == 32 && G <= 16), "one MFMA K per batch, heads as MFMA rows");
   __shared__ float s_acc[WAVES][G][128];
   __shared__ float s_m[WAVES][G], s_l[WAVES][G];
+  // (PVM) per wave: the batch's value codes as token rows, and the probabilities x value
+  // factors of each head as two bf16 terms, hi + lo (their sum is within 2^-17 of the fp32
+  // weight, and each bf16 x bf16 product is exact in fp32: the sums keep fp32 accuracy)
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[PVM ? WAVES : 1][PVM ? KT * 128 : 16];
+  __shared__ __attribute__((aligned(16))) uint16_t s_p[PVM ? WAVES : 1][2][PVM ? G : 1][PVM ? KT : 8];
 
   const int64_t b = blockIdx.x / KVH, kvh = blockIdx.x % KVH;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -150,14 +186,19 @@ __global__ __launch_bounds__(64 * WAVES) void attn_decode_kernel(
     }
   }
 
-  float m[G], l[G], acc[G][DL];
+  float m[G], l[G], acc[PVM ? 1 : G][PVM ? 1 : DL];
+  v4f pacc[PVM ? 8 : 1];   // (PVM) value sums: lane < 16 holds heads 0..3 of element 16 cb + lane
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m[g] = -INFINITY;
     l[g] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < DL; ++i) acc[g][i] = 0.0f;
   }
+#pragma unroll
+  for (int g = 0; g < (PVM ? 1 : G); ++g)
+#pragma unroll
+    for (int i = 0; i < (PVM ? 1 : DL); ++i) acc[g][i] = 0.0f;
+#pragma unroll
+  for (int cb = 0; cb < (PVM ? 8 : 1); ++cb) pacc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // Steps are taken kBatch at a time: the loads of all of them are issued before any is used,
   // so that each wave keeps kBatch steps of cache rows in flight.
@@ -174,6 +215,16 @@ __global__ __launch_bounds__(64 * WAVES) void attn_decode_kernel(
       vr[u] = load_raw<DL>(v_codes + row * 128 + d0);
       ks[u] = k_si[row];
       vs[u] = v_si[row];
+    }
+    if constexpr (PVM) {
+      // value codes to this wave's LDS rows (token u * TPS + tg); tokens past the end as zeros,
+      // so that nothing but zero reaches the sums (0 x NaN would)
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const uint4 c = valid[u] ? make_uint4(vr[u].w[0], vr[u].w[1], vr[u].w[2], vr[u].w[3])
+                                 : make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(&s_v[w][(u * TPS + tg) * 128 + d0]) = c;
+      }
     }
     // The batch's scores first, so that the running maximum is reduced across lanes once per
     // batch and head; then the probabilities and the value sums.
@@ -206,11 +257,58 @@ __global__ __launch_bounds__(64 * WAVES) void attn_decode_kernel(
       if (mx > m[g]) {
         const float alpha = __builtin_amdgcn_exp2f(m[g] - mx);   // 0 when m = -inf
         l[g] *= alpha;
+        if constexpr (PVM) {
 #pragma unroll
-        for (int i = 0; i < DL; ++i) acc[g][i] *= alpha;
+          for (int cb = 0; cb < 8; ++cb) pacc[cb][g] *= alpha;
+        } else {
+#pragma unroll
+          for (int i = 0; i < DL; ++i) acc[g][i] *= alpha;
+        }
         m[g] = mx;
       }
     }
+    if constexpr (PVM) {
+      // probabilities x value factors, head g = lane % LPT written by the lanes of each token
+      const int gl = lane % LPT;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        float pw = 0.0f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float p = valid[u] ? __builtin_amdgcn_exp2f(s[u][g] - m[g]) : 0.0f;
+          l[g] += p;
+          if (gl == g) pw = p * vs[u];
+        }
+        if (gl < G) {
+          typedef __bf16 bf1;
+          const bf1 hi = (bf1)pw;
+          const bf1 lo = (bf1)(pw - (float)hi);
+          s_p[w][0][gl][u * TPS + tg] = __builtin_bit_cast(uint16_t, hi);
+          s_p[w][1][gl][u * TPS + tg] = __builtin_bit_cast(uint16_t, lo);
+        }
+      }
+      // A: the probabilities of head lane % 16 for tokens 8 (lane / 16) .. + 7 (zero rows past
+      // G); B: via transposing reads, the codes of those tokens at element 16 cb + lane % 16
+      // (lane 2j + h of each 16-lane group points at token row j, bytes 8h ..)
+      const int hq = lane & 15, kq = lane >> 4;
+      bf16x8 pa = bf16x8{}, pl = bf16x8{};
+      if (hq < G) {
+        pa = *reinterpret_cast<const bf16x8*>(&s_p[w][0][hq < G ? hq : 0][8 * kq]);
+        pl = *reinterpret_cast<const bf16x8*>(&s_p[w][1][hq < G ? hq : 0][8 * kq]);
+      }
+      const uint8_t* vrow = &s_v[w][(kq * 8 + (hq >> 1)) * 128 + 8 * (hq & 1)];
+      bf16x8 vb[8];
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) {
+        const v2i codes = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) v2i*)(vrow + 16 * cb));
+        vb[cb] = decode8_bf16<FMT>(codes);
+        pacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb[cb], pacc[cb], 0, 0, 0);
+      }
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb)
+        pacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb[cb], pacc[cb], 0, 0, 0);
+    } else {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       float vf[DL];
@@ -230,6 +328,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_decode_kernel(
         for (int i = 0; i < DL; ++i) acc[g][i] = fmaf(pv, vf[i], acc[g][i]);
       }
     }
+    }
   }
 
   // sums over the wave's token groups, then the four waves through LDS
@@ -238,11 +337,27 @@ __global__ __launch_bounds__(64 * WAVES) void attn_decode_kernel(
 #pragma unroll
     for (int off = LPT; off < 64; off <<= 1) {
       l[g] += __shfl_xor(l[g], off);
+      if constexpr (!PVM) {
 #pragma unroll
-      for (int i = 0; i < DL; ++i) acc[g][i] += __shfl_xor(acc[g][i], off);
+        for (int i = 0; i < DL; ++i) acc[g][i] += __shfl_xor(acc[g][i], off);
+      }
     }
   }
-  if (tg == 0) {
+  if constexpr (PVM) {
+    if (lane < 16) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) s_acc[w][g][16 * cb + lane] = pacc[cb][g];
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        s_m[w][g] = m[g];
+        s_l[w][g] = l[g];
+      }
+    }
+  } else if (tg == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
 #pragma unroll
