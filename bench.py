@@ -677,12 +677,12 @@ def bench_kv_decode(args):
                value=round((decode_bytes + append_bytes) / dt / 1e9, 1), unit="GB/s", n_gpus=1,
                steps=args.steps, warmup=args.warmup, ms_per_step=round(dt * 1e3, 4),
                higher_is_better=True, scaling="weak", vs_baseline=None,
-               dtype="e4m3 cache; fp32 scores and softmax; value sums on bf16 MFMA (hi + lo weights), fp32 accumulate; bf16 q/out", data="synthetic",
+               dtype="e4m3 cache; bf16 MFMA products (keys and values decoded exactly, weights as bf16 hi + lo), fp32 accumulate and softmax; bf16 q/out", data="synthetic",
                config=dict(workload="llama3.1-8b-attention-decode-fp8-kv", batch=B, cache_tokens=T,
                            q_heads=H, kv_heads=KVH, head_dim=D, mean_len=round(tokens / B, 1)),
                roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS,
                              unit="GB/s", frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=None,
-                             kernel="attn_decode_kernel<E4M3, 4 query heads per KV head, 16 bytes per lane, 4 steps in flight, 4 waves> (value sums on bf16 MFMA)",
+                             kernel="attn_decode_mma_kernel<E4M3, 4 query heads per KV head> (scores and value sums on bf16 MFMA)",
                              mean_launch_us=round(dec_ms * 1e3, 2),
                              bytes_per_launch=decode_bytes),
                decode_us=round(dec_ms * 1e3, 2), append_us=round(app_ms * 1e3, 2),

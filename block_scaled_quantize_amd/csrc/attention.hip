@@ -20,10 +20,9 @@
 // the key and value rows, 4 steps per batch with all their loads in flight; dot products are
 // reduced over the token's lanes, the softmax is kept online in base 2 (running maximum per
 // head, wave-uniform, reduced across lanes once per batch; running sums per lane), and the
-// four waves' partial results are merged through LDS at the end.  For G <= 4 the value sums of
-// a batch (32 tokens) run on the matrix cores: the probabilities (x value factors) of each head,
-// split into bf16 hi + lo terms, times the value codes decoded exactly to bf16, read back from
-// LDS transposed (ds_read_b64_tr_b8) -- two v_mfma_f32_16x16x32_bf16 per 16 elements.
+// four waves' partial results are merged through LDS at the end.  For G <= 4 query heads per
+// KV head both products run on the matrix cores (attn_decode_mma_kernel); the VALU kernel
+// (attn_decode_kernel) serves G = 8.
 #include <math.h>
 
 #include "common.h"
@@ -150,19 +149,8 @@ __global__ __launch_bounds__(64 * WAVES) void attn_decode_kernel(
   constexpr int LPT = 128 / DL;         // lanes per token
   constexpr int TPS = 64 / LPT;         // tokens per wave step
   constexpr int kBatch = KBATCH;        // wave steps whose loads are in flight together
-  // PVM: the value sums of a batch (32 tokens) run on the matrix cores as one
-  // v_mfma_f32_16x16x32_bf16 per 16 elements: A = probabilities (rows = heads, k = tokens),
-  // B = values (k = tokens, columns = elements), both in bf16 (FP8 codes decode exactly).
-  constexpr bool PVM = DL == 16;
-  constexpr int KT = kBatch * TPS;      // tokens per batch
-  static_assert(!PVM || (KT == 32 && G <= 16), "one MFMA K per batch, heads as MFMA rows");
   __shared__ float s_acc[WAVES][G][128];
   __shared__ float s_m[WAVES][G], s_l[WAVES][G];
-  // (PVM) per wave: the batch's value codes as token rows, and the probabilities x value
-  // factors of each head as two bf16 terms, hi + lo (their sum is within 2^-17 of the fp32
-  // weight, and each bf16 x bf16 product is exact in fp32: the sums keep fp32 accuracy)
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[PVM ? WAVES : 1][PVM ? KT * 128 : 16];
-  __shared__ __attribute__((aligned(16))) uint16_t s_p[PVM ? WAVES : 1][2][PVM ? G : 1][PVM ? KT : 8];
 
   const int64_t b = blockIdx.x / KVH, kvh = blockIdx.x % KVH;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -186,19 +174,14 @@ __global__ __launch_bounds__(64 * WAVES) void attn_decode_kernel(
     }
   }
 
-  float m[G], l[G], acc[PVM ? 1 : G][PVM ? 1 : DL];
-  v4f pacc[PVM ? 8 : 1];   // (PVM) value sums: lane < 16 holds heads 0..3 of element 16 cb + lane
+  float m[G], l[G], acc[G][DL];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m[g] = -INFINITY;
     l[g] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < DL; ++i) acc[g][i] = 0.0f;
   }
-#pragma unroll
-  for (int g = 0; g < (PVM ? 1 : G); ++g)
-#pragma unroll
-    for (int i = 0; i < (PVM ? 1 : DL); ++i) acc[g][i] = 0.0f;
-#pragma unroll
-  for (int cb = 0; cb < (PVM ? 8 : 1); ++cb) pacc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // Steps are taken kBatch at a time: the loads of all of them are issued before any is used,
   // so that each wave keeps kBatch steps of cache rows in flight.
@@ -215,16 +198,6 @@ __global__ __launch_bounds__(64 * WAVES) void attn_decode_kernel(
       vr[u] = load_raw<DL>(v_codes + row * 128 + d0);
       ks[u] = k_si[row];
       vs[u] = v_si[row];
-    }
-    if constexpr (PVM) {
-      // value codes to this wave's LDS rows (token u * TPS + tg); tokens past the end as zeros,
-      // so that nothing but zero reaches the sums (0 x NaN would)
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const uint4 c = valid[u] ? make_uint4(vr[u].w[0], vr[u].w[1], vr[u].w[2], vr[u].w[3])
-                                 : make_uint4(0u, 0u, 0u, 0u);
-        *reinterpret_cast<uint4*>(&s_v[w][(u * TPS + tg) * 128 + d0]) = c;
-      }
     }
     // The batch's scores first, so that the running maximum is reduced across lanes once per
     // batch and head; then the probabilities and the value sums.
@@ -257,58 +230,11 @@ __global__ __launch_bounds__(64 * WAVES) void attn_decode_kernel(
       if (mx > m[g]) {
         const float alpha = __builtin_amdgcn_exp2f(m[g] - mx);   // 0 when m = -inf
         l[g] *= alpha;
-        if constexpr (PVM) {
 #pragma unroll
-          for (int cb = 0; cb < 8; ++cb) pacc[cb][g] *= alpha;
-        } else {
-#pragma unroll
-          for (int i = 0; i < DL; ++i) acc[g][i] *= alpha;
-        }
+        for (int i = 0; i < DL; ++i) acc[g][i] *= alpha;
         m[g] = mx;
       }
     }
-    if constexpr (PVM) {
-      // probabilities x value factors, head g = lane % LPT written by the lanes of each token
-      const int gl = lane % LPT;
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        float pw = 0.0f;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float p = valid[u] ? __builtin_amdgcn_exp2f(s[u][g] - m[g]) : 0.0f;
-          l[g] += p;
-          if (gl == g) pw = p * vs[u];
-        }
-        if (gl < G) {
-          typedef __bf16 bf1;
-          const bf1 hi = (bf1)pw;
-          const bf1 lo = (bf1)(pw - (float)hi);
-          s_p[w][0][gl][u * TPS + tg] = __builtin_bit_cast(uint16_t, hi);
-          s_p[w][1][gl][u * TPS + tg] = __builtin_bit_cast(uint16_t, lo);
-        }
-      }
-      // A: the probabilities of head lane % 16 for tokens 8 (lane / 16) .. + 7 (zero rows past
-      // G); B: via transposing reads, the codes of those tokens at element 16 cb + lane % 16
-      // (lane 2j + h of each 16-lane group points at token row j, bytes 8h ..)
-      const int hq = lane & 15, kq = lane >> 4;
-      bf16x8 pa = bf16x8{}, pl = bf16x8{};
-      if (hq < G) {
-        pa = *reinterpret_cast<const bf16x8*>(&s_p[w][0][hq < G ? hq : 0][8 * kq]);
-        pl = *reinterpret_cast<const bf16x8*>(&s_p[w][1][hq < G ? hq : 0][8 * kq]);
-      }
-      const uint8_t* vrow = &s_v[w][(kq * 8 + (hq >> 1)) * 128 + 8 * (hq & 1)];
-      bf16x8 vb[8];
-#pragma unroll
-      for (int cb = 0; cb < 8; ++cb) {
-        const v2i codes = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) v2i*)(vrow + 16 * cb));
-        vb[cb] = decode8_bf16<FMT>(codes);
-        pacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb[cb], pacc[cb], 0, 0, 0);
-      }
-#pragma unroll
-      for (int cb = 0; cb < 8; ++cb)
-        pacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb[cb], pacc[cb], 0, 0, 0);
-    } else {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       float vf[DL];
@@ -328,7 +254,6 @@ __global__ __launch_bounds__(64 * WAVES) void attn_decode_kernel(
         for (int i = 0; i < DL; ++i) acc[g][i] = fmaf(pv, vf[i], acc[g][i]);
       }
     }
-    }
   }
 
   // sums over the wave's token groups, then the four waves through LDS
@@ -337,27 +262,11 @@ __global__ __launch_bounds__(64 * WAVES) void attn_decode_kernel(
 #pragma unroll
     for (int off = LPT; off < 64; off <<= 1) {
       l[g] += __shfl_xor(l[g], off);
-      if constexpr (!PVM) {
 #pragma unroll
-        for (int i = 0; i < DL; ++i) acc[g][i] += __shfl_xor(acc[g][i], off);
-      }
+      for (int i = 0; i < DL; ++i) acc[g][i] += __shfl_xor(acc[g][i], off);
     }
   }
-  if constexpr (PVM) {
-    if (lane < 16) {
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb) s_acc[w][g][16 * cb + lane] = pacc[cb][g];
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        s_m[w][g] = m[g];
-        s_l[w][g] = l[g];
-      }
-    }
-  } else if (tg == 0) {
+  if (tg == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
 #pragma unroll
@@ -390,15 +299,197 @@ __global__ __launch_bounds__(64 * WAVES) void attn_decode_kernel(
   }
 }
 
+// Decode attention with both products on the matrix cores, for G <= 4 query heads per KV head.
+// A wave takes 32 consecutive tokens per batch.  Scores: one v_mfma_f32_16x16x32_bf16 per 16
+// tokens and 32 elements, A = keys (row = token, loaded as 8-byte pieces in the operand layout
+// and decoded exactly to bf16), B = queries (column = head, zero past G); lane l then holds
+// the scores of head l % 16 for tokens 4 (l / 16) + r of each 16-token half.  Those 8 scores
+// per lane are already the A operand of the value sums (row = head, k slot j = token
+// pi(j) = 4 (l / 16) + j for j < 4, 16 + 4 (l / 16) + j - 4 otherwise), so the probabilities x
+// value factors never leave the registers; they are split into bf16 hi + lo terms (their sum
+// within 2^-17 of the fp32 weight; bf16 x bf16 products are exact in fp32).  Values: the rows
+// go to a per-wave LDS buffer and come back transposed (ds_read_b64_tr_b8: 8 tokens pi(j) of
+// one element per lane), decoded exactly to bf16; two MFMAs per 16 elements.  The softmax is
+// online in base 2 with a wave-uniform running maximum per head, reduced once per batch.
+template <int FMT, int G>
+__global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_mma_kernel(
+    int64_t H, int64_t KVH, int64_t T, const uint16_t* __restrict__ q,
+    const uint8_t* __restrict__ k_codes, const float* __restrict__ k_si,
+    const uint8_t* __restrict__ v_codes, const float* __restrict__ v_si,
+    const int32_t* __restrict__ seq_lens, float score_scale, uint16_t* __restrict__ out) {
+  static_assert(G >= 1 && G <= 4, "heads as MFMA columns / rows");
+  constexpr int W = kAttnWaves;
+  constexpr int KT = 32;   // tokens per batch
+  __shared__ float s_acc[W][G][128];
+  __shared__ float s_m[W][G], s_l[W][G];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[W][KT * 128];
+
+  const int64_t b = blockIdx.x / KVH, kvh = blockIdx.x % KVH;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = lane & 15, qg = lane >> 4;   // MFMA row / column, and k group
+  int64_t len = seq_lens[b];
+  len = len < 0 ? 0 : (len > T ? T : len);
+
+  // B operand of the scores: head col (zero past G), elements 32 c + 8 qg .. + 7
+  bf16x8 qf[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    qf[c] = bf16x8{};
+    if (col < G) {
+      const uint4 v = *reinterpret_cast<const uint4*>(
+          q + ((b * H + kvh * G + col) * 128 + 32 * c + 8 * qg));
+      qf[c] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  float m[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) m[g] = -INFINITY;
+  float lsum = 0.0f;   // head col, this lane's tokens
+  v4f pacc[8];         // lanes 0..15: heads 0..3 of element 16 cb + lane
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) pacc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
+  const int jj = col >> 1, hh = col & 1;   // the token row this lane points at in the value reads
+  const int prow = jj < 4 ? 4 * qg + jj : 16 + 4 * qg + (jj - 4);
+
+  auto row_of = [&](int64_t t) { return (b * T + (t < len ? t : len - 1)) * KVH + kvh; };
+  for (int64_t t0 = (int64_t)w * KT; t0 < len; t0 += W * KT) {
+    // all loads of the batch first: value rows (token 8u + lane / 8, 16 bytes), key pieces
+    // (token 16 ch + col, bytes 32 c + 8 qg), factors of the lane's score rows
+    uint4 vraw[4];
+    uint2 kraw[2][4];
+    float ksr[2][4], vsr[2][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      vraw[u] = *reinterpret_cast<const uint4*>(v_codes + row_of(t0 + 8 * u + (lane >> 3)) * 128 +
+                                                (lane & 7) * 16);
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+      const int64_t kr = row_of(t0 + 16 * ch + col) * 128 + 8 * qg;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) kraw[ch][c] = *reinterpret_cast<const uint2*>(k_codes + kr + 32 * c);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t sr = row_of(t0 + 16 * ch + 4 * qg + r);
+        ksr[ch][r] = k_si[sr];
+        vsr[ch][r] = v_si[sr];
+      }
+    }
+    // value rows to LDS, zero codes past the end (nothing but zero may reach the sums)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool ok = t0 + 8 * u + (lane >> 3) < len;
+      *reinterpret_cast<uint4*>(&s_v[w][(8 * u + (lane >> 3)) * 128 + (lane & 7) * 16]) =
+          ok ? vraw[u] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    // scores of the two 16-token halves
+    v4f sc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch)
+        sc[ch] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            decode8_bf16<FMT>(v2i{(int)kraw[ch][c].x, (int)kraw[ch][c].y}), qf[c], sc[ch], 0, 0, 0);
+    float s[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = col < G && t0 + 16 * ch + 4 * qg + r < len;
+        s[4 * ch + r] = ok ? sc[ch][r] * (ksr[ch][r] * score_scale) : -INFINITY;   // base 2
+        mx = fmaxf(mx, s[4 * ch + r]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // lane g holds head g's batch maximum: wave-uniform values, a scalar branch each, taken
+    // only when the running maximum grows
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mg = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), g));
+      if (mg > m[g]) {
+        const float alpha = __builtin_amdgcn_exp2f(m[g] - mg);   // 0 when m = -inf
+        if (col == g) lsum *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) pacc[cb][g] *= alpha;
+        m[g] = mg;
+      }
+    }
+    float mc = 0.0f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) mc = col == g ? m[g] : mc;
+    // probabilities x value factors: the A operand of the value sums, as bf16 hi + lo
+    bf16x8 pa, pl;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p = s[j] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s[j] - mc);
+      lsum += p;
+      const float pw = p * vsr[j >> 2][j & 3];
+      pa[j] = (__bf16)pw;
+      pl[j] = (__bf16)(pw - (float)pa[j]);
+    }
+    const uint8_t* vrow = &s_v[w][prow * 128 + 8 * hh];
+    bf16x8 vb[8];
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+      const v2i codes = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (__attribute__((address_space(3))) v2i*)(vrow + 16 * cb));
+      vb[cb] = decode8_bf16<FMT>(codes);
+      pacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb[cb], pacc[cb], 0, 0, 0);
+    }
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+      pacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb[cb], pacc[cb], 0, 0, 0);
+  }
+
+  // denominators over the 4 k groups; lanes 0..15 hold the value sums, lanes 0..G-1 the heads'
+  // denominators and maxima
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  if (lane < 16) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) s_acc[w][g][16 * cb + lane] = pacc[cb][g];
+  }
+  if (lane < G) {
+    float ml = 0.0f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) ml = lane == g ? m[g] : ml;
+    s_m[w][lane] = ml;
+    s_l[w][lane] = lsum;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * 128; idx += 64 * W) {
+    const int g = idx >> 7, d = idx & 127;
+    float mxw = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < W; ++v) mxw = fmaxf(mxw, s_m[v][g]);
+    float num = 0.0f, den = 0.0f;
+    if (mxw != -INFINITY) {
+#pragma unroll
+      for (int v = 0; v < W; ++v) {
+        const float f = __builtin_amdgcn_exp2f(s_m[v][g] - mxw);   // 0 for a wave without tokens
+        num = fmaf(f, s_acc[v][g][d], num);
+        den = fmaf(f, s_l[v][g], den);
+      }
+    }
+    const float o = den > 0.0f ? num / den : 0.0f;   // no cached token: zeros
+    typedef __bf16 bf1;
+    const bf1 ob = (bf1)o;
+    out[(b * H + kvh * G + g) * 128 + d] = __builtin_bit_cast(uint16_t, ob);
+  }
+}
+
 template <int FMT>
 int dispatch_attn(int G, dim3 grid, hipStream_t st, int64_t H, int64_t KVH, int64_t T,
                   const uint16_t* q, const uint8_t* kc, const float* ks, const uint8_t* vc,
                   const float* vs, const int32_t* lens, float c, uint16_t* out) {
   const dim3 block(64 * kAttnWaves);
   switch (G) {
-    case 1: return launch(attn_decode_kernel<FMT, 1, 16, 4, kAttnWaves>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
-    case 2: return launch(attn_decode_kernel<FMT, 2, 16, 4, kAttnWaves>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
-    case 4: return launch(attn_decode_kernel<FMT, 4, 16, 4, kAttnWaves>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
+    case 1: return launch(attn_decode_mma_kernel<FMT, 1>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
+    case 2: return launch(attn_decode_mma_kernel<FMT, 2>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
+    case 4: return launch(attn_decode_mma_kernel<FMT, 4>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
     case 8: return launch(attn_decode_kernel<FMT, 8, 8, 4, kAttnWaves>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
     default: return FP8BS_ERR_UNSUPPORTED;
   }
