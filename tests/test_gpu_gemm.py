@@ -242,6 +242,16 @@ def test_every_tile_variant(gpu, monkeypatch, variant, layout, fa, ga, fb, gb):
     run_gemm(gpu, layout, 256, 256, 256, fa, ga, fb, gb)
 
 
+@pytest.mark.parametrize("K,N", [(128, 256), (256, 384), (208, 256), (640, 512)])
+@pytest.mark.parametrize("pow2", [False, True])
+def test_grouped_persistent_tiles(gpu, K, N, pow2):
+    """More tiles than workgroups: each workgroup walks several tiles of different groups, the
+    next tile's first K block loaded while the current tile finishes (K blocks per tile: 1 --
+    nothing to overlap --, 2 -- the first block hands over --, 2 with a ragged K, 5)."""
+    counts = [3000] * 24 + [17, 0, 700]
+    run_grouped(gpu, counts, N, K, seed=K, pow2=pow2)
+
+
 @pytest.mark.parametrize("variant", ["B", "C", "D"])
 def test_grouped_every_tile_variant(gpu, monkeypatch, variant):
     """Each tile configuration the grouped kernel can use (FP8BS_GROUPED_VARIANT forces one)."""
