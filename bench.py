@@ -64,6 +64,10 @@ def parse():
     ap.add_argument("--pow2", action="store_true",
                     help="moe, backward-blockwise: power-of-2 scales (E8M0 in the MFMA)")
     ap.add_argument("--tokens", type=int, default=8192)
+    ap.add_argument("--kv-split", type=int, default=-1,
+                    help="kv-decode: tokens per chunk of fp8_attention_decode_split (0: unsplit, "
+                         "-1: the binding's choice for the batch)")
+    ap.add_argument("--kv-batch", type=int, default=64, help="kv-decode: sequences")
     return ap.parse_args()
 
 
@@ -621,13 +625,14 @@ def bench_kv_decode(args):
     """One decode step over an FP8 KV cache ("NVIDIA NeMo RL ...", section "Ganancias de
     rendimiento en el mundo real": FP8 KV cache and attention), Llama-3.1-8B attention shape
     (32 query heads, 8 KV heads, head dim 128), 64 sequences with a 4096-token cache and seeded
-    lengths in [2048, 4096].  Per step: the step's new token of every sequence is quantized into
+    lengths in [2048, 4096] (--kv-batch: another batch; --kv-split: chunked decode).  Per step: the
+    step's new token of every sequence is quantized into
     the cache (1x128 per head vector) and grouped-query attention reads the whole cache.
     value = algorithmic bytes of the step / step time."""
     import block_scaled_quantize_amd as bsq
     bsq.load()
     dev = torch.device("cuda", 0)
-    B, T, H, KVH, D = 64, 4096, 32, 8, 128
+    B, T, H, KVH, D = args.kv_batch, 4096, 32, 8, 128
     g = np.random.default_rng(11)
     lens_np = g.integers(T // 2, T + 1, size=B).astype(np.int32)
     lens = torch.from_numpy(lens_np).to(dev)
@@ -647,13 +652,20 @@ def bench_kv_decode(args):
     vn = torch.randn((B, KVH, D), generator=gen, device=dev).to(torch.bfloat16)
     out = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
     sm = 1.0 / float(np.sqrt(D))
+    split = (bsq.decode_split_tokens(B, KVH, T) if args.kv_split < 0
+             else (args.kv_split if args.kv_split > 0 else None))
+    ws = None
+    if split:
+        ws = torch.empty((bsq.attention_decode_workspace_size(B, H, KVH, T, split),),
+                         dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def step(t=None):
         def run(key, fn):
             return fn() if t is None else t.time(key, fn)
         run("append", lambda: bsq.kv_cache_append(kn, vn, pos, kc, ks, vc, vs))
-        run("decode", lambda: bsq.attention_decode(q, kc, ks, vc, vs, lens, sm, out=out))
+        run("decode", lambda: bsq.attention_decode(q, kc, ks, vc, vs, lens, sm, out=out,
+                                                   split_tokens=split, workspace=ws))
 
     for _ in range(args.warmup):
         step()
@@ -679,10 +691,12 @@ def bench_kv_decode(args):
                higher_is_better=True, scaling="weak", vs_baseline=None,
                dtype="e4m3 cache; bf16 MFMA products (keys and values decoded exactly, weights as bf16 hi + lo), fp32 accumulate and softmax; bf16 q/out", data="synthetic",
                config=dict(workload="llama3.1-8b-attention-decode-fp8-kv", batch=B, cache_tokens=T,
+                           split_tokens=split,
                            q_heads=H, kv_heads=KVH, head_dim=D, mean_len=round(tokens / B, 1)),
                roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS,
                              unit="GB/s", frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=None,
-                             kernel="attn_decode_mma_kernel<E4M3, 4 query heads per KV head> (scores and value sums on bf16 MFMA)",
+                             kernel="attn_decode_mma_kernel<E4M3, 4 query heads per KV head%s> (scores and value sums on bf16 MFMA)"
+                                    % (", split" if split else ""),
                              mean_launch_us=round(dec_ms * 1e3, 2),
                              bytes_per_launch=decode_bytes),
                decode_us=round(dec_ms * 1e3, 2), append_us=round(app_ms * 1e3, 2),

@@ -311,12 +311,17 @@ __global__ __launch_bounds__(64 * WAVES) void attn_decode_kernel(
 // go to a per-wave LDS buffer and come back transposed (ds_read_b64_tr_b8: 8 tokens pi(j) of
 // one element per lane), decoded exactly to bf16; two MFMAs per 16 elements.  The softmax is
 // online in base 2 with a wave-uniform running maximum per head, reduced once per batch.
-template <int FMT, int G>
+// SPLIT: the workgroup takes tokens [s * chunk, (s + 1) * chunk) of its sequence (workgroup id =
+// (sequence x KV head) x S + s) and writes its partial result -- per head the maximum logit, the
+// sum of weights and the weighted value sums -- to part[((b KVH + kv) S + s) G + g][130] for
+// attn_combine_kernel; otherwise it takes the whole sequence and writes the output.
+template <int FMT, int G, bool SPLIT = false>
 __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_mma_kernel(
     int64_t H, int64_t KVH, int64_t T, const uint16_t* __restrict__ q,
     const uint8_t* __restrict__ k_codes, const float* __restrict__ k_si,
     const uint8_t* __restrict__ v_codes, const float* __restrict__ v_si,
-    const int32_t* __restrict__ seq_lens, float score_scale, uint16_t* __restrict__ out) {
+    const int32_t* __restrict__ seq_lens, float score_scale, uint16_t* __restrict__ out,
+    int64_t chunk = 0, int S = 1, float* __restrict__ part = nullptr) {
   static_assert(G >= 1 && G <= 4, "heads as MFMA columns / rows");
   constexpr int W = kAttnWaves;
   constexpr int KT = 32;   // tokens per batch
@@ -324,11 +329,16 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_mma_kernel(
   __shared__ float s_m[W][G], s_l[W][G];
   __shared__ __attribute__((aligned(16))) uint8_t s_v[W][KT * 128];
 
-  const int64_t b = blockIdx.x / KVH, kvh = blockIdx.x % KVH;
+  const int64_t bh = SPLIT ? blockIdx.x / S : blockIdx.x;   // sequence x KV head
+  const int sp = SPLIT ? (int)(blockIdx.x % S) : 0;
+  const int64_t b = bh / KVH, kvh = bh % KVH;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15, qg = lane >> 4;   // MFMA row / column, and k group
   int64_t len = seq_lens[b];
   len = len < 0 ? 0 : (len > T ? T : len);
+  // this workgroup's tokens [tbeg, len)
+  const int64_t tbeg = SPLIT ? (int64_t)sp * chunk : 0;
+  if constexpr (SPLIT) len = len < tbeg + chunk ? len : tbeg + chunk;
 
   // B operand of the scores: head col (zero past G), elements 32 c + 8 qg .. + 7
   bf16x8 qf[4];
@@ -353,7 +363,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_mma_kernel(
   const int prow = jj < 4 ? 4 * qg + jj : 16 + 4 * qg + (jj - 4);
 
   auto row_of = [&](int64_t t) { return (b * T + (t < len ? t : len - 1)) * KVH + kvh; };
-  for (int64_t t0 = (int64_t)w * KT; t0 < len; t0 += W * KT) {
+  for (int64_t t0 = tbeg + (int64_t)w * KT; t0 < len; t0 += W * KT) {
     // all loads of the batch first: value rows (token 8u + lane / 8, 16 bytes), key pieces
     // (token 16 ch + col, bytes 32 c + 8 qg), factors of the lane's score rows
     uint4 vraw[4];
@@ -474,11 +484,47 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_mma_kernel(
         den = fmaf(f, s_l[v][g], den);
       }
     }
-    const float o = den > 0.0f ? num / den : 0.0f;   // no cached token: zeros
-    typedef __bf16 bf1;
-    const bf1 ob = (bf1)o;
-    out[(b * H + kvh * G + g) * 128 + d] = __builtin_bit_cast(uint16_t, ob);
+    if constexpr (SPLIT) {
+      float* pp = part + ((bh * S + sp) * G + g) * 130;
+      pp[2 + d] = num;
+      if (d == 0) {
+        pp[0] = mxw;   // -inf (and zero sums) for a workgroup without tokens
+        pp[1] = den;
+      }
+    } else {
+      const float o = den > 0.0f ? num / den : 0.0f;   // no cached token: zeros
+      typedef __bf16 bf1;
+      const bf1 ob = (bf1)o;
+      out[(b * H + kvh * G + g) * 128 + d] = __builtin_bit_cast(uint16_t, ob);
+    }
   }
+}
+
+// Merge of the S partial results of each (sequence, KV head): the same rescaling by the base-2
+// maximum as the merge of a workgroup's waves.  One workgroup per (sequence, KV head), one thread
+// per (head, element).
+template <int G>
+__global__ __launch_bounds__(128 * G) void attn_combine_kernel(int64_t H, int64_t KVH, int S,
+                                                               const float* __restrict__ part,
+                                                               uint16_t* __restrict__ out) {
+  const int64_t bh = blockIdx.x, b = bh / KVH, kvh = bh % KVH;
+  const int g = threadIdx.x >> 7, d = threadIdx.x & 127;
+  const float* base = part + (bh * S * G + g) * 130;
+  constexpr int kStride = G * 130;   // between the partials of consecutive splits
+  float mx = -INFINITY;
+  for (int sp = 0; sp < S; ++sp) mx = fmaxf(mx, base[sp * kStride]);
+  float num = 0.0f, den = 0.0f;
+  if (mx != -INFINITY) {
+    for (int sp = 0; sp < S; ++sp) {
+      const float f = __builtin_amdgcn_exp2f(base[sp * kStride] - mx);   // 0 for an empty split
+      num = fmaf(f, base[sp * kStride + 2 + d], num);
+      den = fmaf(f, base[sp * kStride + 1], den);
+    }
+  }
+  const float o = den > 0.0f ? num / den : 0.0f;
+  typedef __bf16 bf1;
+  const bf1 ob = (bf1)o;
+  out[(b * H + kvh * G + g) * 128 + d] = __builtin_bit_cast(uint16_t, ob);
 }
 
 template <int FMT>
@@ -487,10 +533,39 @@ int dispatch_attn(int G, dim3 grid, hipStream_t st, int64_t H, int64_t KVH, int6
                   const float* vs, const int32_t* lens, float c, uint16_t* out) {
   const dim3 block(64 * kAttnWaves);
   switch (G) {
-    case 1: return launch(attn_decode_mma_kernel<FMT, 1>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
-    case 2: return launch(attn_decode_mma_kernel<FMT, 2>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
-    case 4: return launch(attn_decode_mma_kernel<FMT, 4>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
+    case 1: return launch(attn_decode_mma_kernel<FMT, 1>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out, (int64_t)0, 1, (float*)nullptr);
+    case 2: return launch(attn_decode_mma_kernel<FMT, 2>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out, (int64_t)0, 1, (float*)nullptr);
+    case 4: return launch(attn_decode_mma_kernel<FMT, 4>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out, (int64_t)0, 1, (float*)nullptr);
     case 8: return launch(attn_decode_kernel<FMT, 8, 8, 4, kAttnWaves>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
+    default: return FP8BS_ERR_UNSUPPORTED;
+  }
+}
+
+// Split decode: S = ceil(T / chunk) workgroups per (sequence, KV head), then the merge.
+template <int FMT, int G>
+int launch_split(int64_t B, int64_t H, int64_t KVH, int64_t T, int64_t chunk, int S,
+                 hipStream_t st, const uint16_t* q, const uint8_t* kc, const float* ks,
+                 const uint8_t* vc, const float* vs, const int32_t* lens, float c, float* part,
+                 uint16_t* out) {
+  if (S > 0) {
+    const int r = launch(attn_decode_mma_kernel<FMT, G, true>, dim3((unsigned)(B * KVH * S)),
+                         dim3(64 * kAttnWaves), st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out,
+                         chunk, S, part);
+    if (r != FP8BS_OK) return r;
+  }
+  return launch(attn_combine_kernel<G>, dim3((unsigned)(B * KVH)), dim3(128 * G), st, H, KVH, S,
+                (const float*)part, out);
+}
+
+template <int FMT>
+int dispatch_split(int G, int64_t B, int64_t H, int64_t KVH, int64_t T, int64_t chunk, int S,
+                   hipStream_t st, const uint16_t* q, const uint8_t* kc, const float* ks,
+                   const uint8_t* vc, const float* vs, const int32_t* lens, float c, float* part,
+                   uint16_t* out) {
+  switch (G) {
+    case 1: return launch_split<FMT, 1>(B, H, KVH, T, chunk, S, st, q, kc, ks, vc, vs, lens, c, part, out);
+    case 2: return launch_split<FMT, 2>(B, H, KVH, T, chunk, S, st, q, kc, ks, vc, vs, lens, c, part, out);
+    case 4: return launch_split<FMT, 4>(B, H, KVH, T, chunk, S, st, q, kc, ks, vc, vs, lens, c, part, out);
     default: return FP8BS_ERR_UNSUPPORTED;
   }
 }
@@ -570,4 +645,56 @@ extern "C" int fp8_attention_decode(int64_t B, int64_t H, int64_t KVH, int64_t T
                                      v_scale_inv, seq_lens, c, out);
   return dispatch_attn<FP8BS_E5M2>((int)G, grid, st, H, KVH, T, q, kc, k_scale_inv, vc,
                                    v_scale_inv, seq_lens, c, out);
+}
+
+extern "C" size_t fp8_attention_decode_workspace_size(int64_t B, int64_t H, int64_t KVH,
+                                                      int64_t T, int64_t chunk) {
+  if (B <= 0 || H <= 0 || KVH <= 0 || T <= 0 || chunk <= 0 || H % KVH != 0) return 0;
+  if (!cache_sizes_ok(B, T, KVH)) return 0;
+  const int64_t S = ceil_div(T, chunk), G = H / KVH;
+  if (B * KVH > INT64_MAX / 4 / 130 / G / S) return 0;
+  return (size_t)(B * KVH * S * G * 130 * 4);
+}
+
+extern "C" int fp8_attention_decode_split(int64_t B, int64_t H, int64_t KVH, int64_t T,
+                                          const void* q_bf16, const void* k_codes,
+                                          const float* k_scale_inv, const void* v_codes,
+                                          const float* v_scale_inv, const int32_t* seq_lens,
+                                          float sm_scale, int fmt, int64_t chunk,
+                                          void* workspace, size_t workspace_bytes,
+                                          void* out_bf16, void* stream) {
+  if (!fmt_ok(fmt)) return FP8BS_ERR_ARG;
+  if (H < 0 || !cache_sizes_ok(B, T, KVH)) return FP8BS_ERR_SHAPE;
+  if (chunk <= 0 || chunk % 32 != 0) return FP8BS_ERR_SHAPE;
+  if (B == 0 || H == 0) return FP8BS_OK;
+  if (KVH == 0 || H % KVH != 0) return FP8BS_ERR_SHAPE;
+  const int64_t G = H / KVH;
+  if (G != 1 && G != 2 && G != 4) return FP8BS_ERR_UNSUPPORTED;
+  const int64_t S = ceil_div(T, chunk);
+  if (B * KVH > 0x7FFFFFFF || S > 0x7FFFFFFF / (B * KVH) || B > INT64_MAX / 256 / H)
+    return FP8BS_ERR_SHAPE;
+  if (!isfinite(sm_scale)) return FP8BS_ERR_ARG;
+  const size_t need = T > 0 ? fp8_attention_decode_workspace_size(B, H, KVH, T, chunk) : 0;
+  if (T > 0 && need == 0) return FP8BS_ERR_SHAPE;
+  if (!q_bf16 || !seq_lens || !out_bf16 ||
+      (T > 0 && (!k_codes || !k_scale_inv || !v_codes || !v_scale_inv || !workspace)))
+    return FP8BS_ERR_NULL;
+  if (workspace_bytes < need) return FP8BS_ERR_SHAPE;
+  if (!aligned16(q_bf16) || (T > 0 && (!aligned16(k_codes) || !aligned16(v_codes) ||
+                                       !aligned4(k_scale_inv) || !aligned4(v_scale_inv) ||
+                                       !aligned4(workspace))) ||
+      !aligned4(seq_lens) || !aligned4(out_bf16))
+    return FP8BS_ERR_ALIGN;
+  const float c = sm_scale * 1.4426950408889634f;   // scores in base 2 (exp2 in the kernel)
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint16_t* q = static_cast<const uint16_t*>(q_bf16);
+  const uint8_t* kc = static_cast<const uint8_t*>(k_codes);
+  const uint8_t* vc = static_cast<const uint8_t*>(v_codes);
+  float* part = static_cast<float*>(workspace);
+  uint16_t* out = static_cast<uint16_t*>(out_bf16);
+  if (fmt == FP8BS_E4M3)
+    return dispatch_split<FP8BS_E4M3>((int)G, B, H, KVH, T, chunk, (int)S, st, q, kc, k_scale_inv,
+                                      vc, v_scale_inv, seq_lens, c, part, out);
+  return dispatch_split<FP8BS_E5M2>((int)G, B, H, KVH, T, chunk, (int)S, st, q, kc, k_scale_inv,
+                                    vc, v_scale_inv, seq_lens, c, part, out);
 }

@@ -287,6 +287,31 @@ int fp8_attention_decode(int64_t B, int64_t H, int64_t KVH, int64_t T, const voi
                          const float* v_scale_inv, const int32_t* seq_lens, float sm_scale,
                          int fmt, void* out_bf16, void* stream);
 
+/* The same decode attention with each sequence split into chunks of `chunk` tokens (a positive
+ * multiple of 32), one workgroup per (sequence, KV head, chunk), and the chunks' partial results
+ * merged by a second kernel; the result is that of fp8_attention_decode up to fp32 rounding
+ * order.  Spreading long sequences over more workgroups keeps the GPU busy when sequence
+ * lengths differ.  [P3] "Ganancias de rendimiento en el mundo real".
+ *   workspace: caller-owned device memory of at least
+ *     fp8_attention_decode_workspace_size(B, H, KVH, T, chunk) bytes (4-byte aligned; may be
+ *     null when T = 0), holding per (sequence, KV head, chunk, query head) the chunk's maximum
+ *     logit, its sum of weights and its 128 weighted value sums (130 floats); its contents on
+ *     entry do not matter.  Calls that share a workspace on different streams race.
+ *   H / KVH must be 1, 2 or 4 (else FP8BS_ERR_UNSUPPORTED).  Other arguments as above.
+ * Errors: as fp8_attention_decode; FP8BS_ERR_SHAPE also for a chunk that is not a positive
+ * multiple of 32 or a workspace smaller than required. */
+int fp8_attention_decode_split(int64_t B, int64_t H, int64_t KVH, int64_t T, const void* q_bf16,
+                               const void* k_codes, const float* k_scale_inv,
+                               const void* v_codes, const float* v_scale_inv,
+                               const int32_t* seq_lens, float sm_scale, int fmt, int64_t chunk,
+                               void* workspace, size_t workspace_bytes, void* out_bf16,
+                               void* stream);
+
+/* Workspace bytes fp8_attention_decode_split needs: B * KVH * ceil(T / chunk) * (H / KVH) * 130 * 4;
+ * 0 for non-positive sizes, H not a multiple of KVH, or a size that overflows. */
+size_t fp8_attention_decode_workspace_size(int64_t B, int64_t H, int64_t KVH, int64_t T,
+                                           int64_t chunk);
+
 #ifdef __cplusplus
 }
 #endif

@@ -239,3 +239,56 @@ def test_attention_decode_validation():
     assert attn(out=FAKE + 2) == bsq.ERR_ALIGN
     assert attn(B=0, q=None) == bsq.OK                   # empty: nothing launched
     assert attn(H=0, q=None) == bsq.OK
+
+
+def attn_split(**kw):
+    a = dict(B=2, H=32, KVH=8, T=100, q=FAKE, kc=FAKE, ks=FAKE, vc=FAKE, vs=FAKE, lens=FAKE,
+             sm=0.088, fmt=0, chunk=32, ws=FAKE, wsb=1 << 20, out=FAKE)
+    a.update(kw)
+    return bsq.load().fp8_attention_decode_split(a["B"], a["H"], a["KVH"], a["T"], a["q"],
+                                                 a["kc"], a["ks"], a["vc"], a["vs"], a["lens"],
+                                                 a["sm"], a["fmt"], a["chunk"], a["ws"],
+                                                 a["wsb"], a["out"], None)
+
+
+def test_attention_decode_workspace_size():
+    # B * KVH * ceil(T / chunk) * (H / KVH) * 130 floats
+    assert bsq.attention_decode_workspace_size(2, 32, 8, 100, 32) == 2 * 8 * 4 * 4 * 130 * 4
+    assert bsq.attention_decode_workspace_size(64, 32, 8, 4096, 1024) == 64 * 8 * 4 * 4 * 130 * 4
+    assert bsq.attention_decode_workspace_size(1, 8, 8, 33, 32) == 8 * 2 * 1 * 130 * 4
+    assert bsq.attention_decode_workspace_size(0, 32, 8, 100, 32) == 0
+    assert bsq.attention_decode_workspace_size(2, 30, 8, 100, 32) == 0
+    assert bsq.attention_decode_workspace_size(2, 32, 8, 100, 0) == 0
+    assert bsq.attention_decode_workspace_size(1 << 40, 32, 8, 1 << 20, 32) == 0   # overflow
+
+
+def test_attention_decode_split_validation():
+    need = bsq.attention_decode_workspace_size(2, 32, 8, 100, 32)
+    assert attn_split(fmt=2) == bsq.ERR_ARG
+    assert attn_split(sm=float("nan")) == bsq.ERR_ARG
+    assert attn_split(chunk=0) == bsq.ERR_SHAPE
+    assert attn_split(chunk=48) == bsq.ERR_SHAPE             # not a multiple of 32
+    assert attn_split(chunk=-32) == bsq.ERR_SHAPE
+    assert attn_split(KVH=0) == bsq.ERR_SHAPE
+    assert attn_split(H=30, KVH=8) == bsq.ERR_SHAPE
+    assert attn_split(H=64, KVH=8) == bsq.ERR_UNSUPPORTED    # 8 query heads per KV head
+    assert attn_split(wsb=need - 4) == bsq.ERR_SHAPE         # workspace too small
+    assert attn_split(ws=None) == bsq.ERR_NULL
+    assert attn_split(q=None) == bsq.ERR_NULL
+    assert attn_split(kc=None) == bsq.ERR_NULL
+    assert attn_split(ws=FAKE + 2) == bsq.ERR_ALIGN
+    assert attn_split(q=FAKE + 8) == bsq.ERR_ALIGN
+    assert attn_split(B=0, q=None, ws=None) == bsq.OK        # empty: nothing launched
+    assert attn_split(H=0, q=None, ws=None) == bsq.OK
+
+
+def test_decode_split_tokens_choice():
+    # 64 sequences x 8 KV heads already give every CU two workgroups: unsplit
+    assert bsq.decode_split_tokens(64, 8, 4096) is None
+    assert bsq.decode_split_tokens(16, 8, 4096) == 1024     # 128 groups x 4 chunks
+    assert bsq.decode_split_tokens(4, 8, 4096) == 256       # 32 groups x 16 chunks
+    assert bsq.decode_split_tokens(1, 1, 100) == 256        # at least 256 tokens per chunk
+    for B, KVH, T in ((3, 8, 5000), (1, 4, 32768), (7, 2, 999)):
+        c = bsq.decode_split_tokens(B, KVH, T)
+        assert c % 256 == 0 and c >= 256
+        assert B * KVH * -(-T // c) <= 512 + B * KVH        # about the target, not far above

@@ -35,12 +35,13 @@ def make_cache(B, T, KVH, fmt, seed, name, std=1.0):
             vc.reshape(B, T, KVH, 128), vs.reshape(B, T, KVH))
 
 
-def run_decode(q_bits, kc, ks, vc, vs, lens, sm_scale, fmt):
+def run_decode(q_bits, kc, ks, vc, vs, lens, sm_scale, fmt, split=None):
     dev = "cuda"
     q = torch.from_numpy(q_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     out = bsq.attention_decode(q, t(kc), t(ks), t(vc), t(vs),
-                               torch.tensor(lens, dtype=torch.int32, device=dev), sm_scale, fmt)
+                               torch.tensor(lens, dtype=torch.int32, device=dev), sm_scale, fmt,
+                               split_tokens=split)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64)
 
@@ -71,6 +72,38 @@ def test_decode_parity_ragged(gpu, H, KVH, fmt):
     ref = oracle.attention_decode(q, kc, ks, vc, vs, lens, sm, fmt)
     check_close(out, ref, f"H={H} KVH={KVH} fmt={fmt}")
     assert np.all(out[0] == 0.0)
+
+
+@pytest.mark.parametrize("H,KVH", [(8, 8), (8, 4), (32, 8)])
+@pytest.mark.parametrize("fmt", [E4, E5])
+@pytest.mark.parametrize("split", [32, 96, 256])
+def test_decode_split_parity_ragged(gpu, H, KVH, fmt, split):
+    """fp8_attention_decode_split: chunks of 32, 96 and 256 tokens over sequences of 0, 1,
+    300, 137 and 33 tokens (empty chunks, one-token chunks, chunks ending mid-batch), against
+    the oracle, and against the unsplit entry point."""
+    B, T = 5, 300
+    kc, ks, vc, vs = make_cache(B, T, KVH, fmt, 1, f"attn/{H}/{KVH}")
+    q = q_bits_of(B, H, 1, f"attn/q/{H}/{KVH}")
+    lens = [0, 1, 300, 137, 33]
+    sm = 1.0 / math.sqrt(128)
+    out = run_decode(q, kc, ks, vc, vs, lens, sm, fmt, split=split)
+    ref = oracle.attention_decode(q, kc, ks, vc, vs, lens, sm, fmt)
+    check_close(out, ref, f"split {split} H={H} KVH={KVH} fmt={fmt}")
+    assert np.all(out[0] == 0.0)
+    whole = run_decode(q, kc, ks, vc, vs, lens, sm, fmt)
+    assert np.max(np.abs(out - whole)) <= 2.0 ** -7 * np.max(np.abs(whole))
+
+
+def test_decode_split_long_sequences(gpu):
+    """Split decode at the benchmark's chunk size, sequences up to 2100 tokens."""
+    B, T, H, KVH = 3, 2100, 32, 8
+    kc, ks, vc, vs = make_cache(B, T, KVH, E4, 4, "attn/split-long")
+    q = q_bits_of(B, H, 4, "attn/q/split-long")
+    lens = [2100, 1025, 1023]
+    sm = 1.0 / math.sqrt(128)
+    out = run_decode(q, kc, ks, vc, vs, lens, sm, E4, split=1024)
+    ref = oracle.attention_decode(q, kc, ks, vc, vs, lens, sm, E4)
+    check_close(out, ref, "split 1024, long sequences")
 
 
 def test_decode_sharp_and_flat_softmax(gpu):
