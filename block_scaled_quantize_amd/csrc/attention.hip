@@ -301,8 +301,9 @@ __global__ __launch_bounds__(64 * WAVES) void attn_decode_kernel(
 
 // Decode attention with both products on the matrix cores, for G <= 4 query heads per KV head.
 // A wave takes 32 consecutive tokens per batch.  Scores: one v_mfma_f32_16x16x32_bf16 per 16
-// tokens and 32 elements, A = keys (row = token, loaded as 8-byte pieces in the operand layout
-// and decoded exactly to bf16), B = queries (column = head, zero past G); lane l then holds
+// tokens and 32 elements, A = keys (row = token; the lanes of k group g feed elements
+// 32 g .. 32 g + 31 to the four MFMAs, so each loads 32 contiguous bytes of its token's row, decoded
+// exactly to bf16), B = queries (column = head, zero past G, the same element order); lane l holds
 // the scores of head l % 16 for tokens 4 (l / 16) + r of each 16-token half.  Those 8 scores
 // per lane are already the A operand of the value sums (row = head, k slot j = token
 // pi(j) = 4 (l / 16) + j for j < 4, 16 + 4 (l / 16) + j - 4 otherwise), so the probabilities x
@@ -310,7 +311,9 @@ __global__ __launch_bounds__(64 * WAVES) void attn_decode_kernel(
 // within 2^-17 of the fp32 weight; bf16 x bf16 products are exact in fp32).  Values: the rows
 // go to a per-wave LDS buffer and come back transposed (ds_read_b64_tr_b8: 8 tokens pi(j) of
 // one element per lane), decoded exactly to bf16; two MFMAs per 16 elements.  The softmax is
-// online in base 2 with a wave-uniform running maximum per head, reduced once per batch.
+// online in base 2 with a wave-uniform running maximum per head, reduced once per batch.  The
+// batch's 32 key and 32 value factors are loaded one per lane and handed out through LDS (memory
+// instructions, not bytes, set the pace here: 9 loads per lane and batch).
 // SPLIT: the workgroup takes tokens [s * chunk, (s + 1) * chunk) of its sequence (workgroup id =
 // (sequence x KV head) x S + s) and writes its partial result -- per head the maximum logit, the
 // sum of weights and the weighted value sums -- to part[((b KVH + kv) S + s) G + g][130] for
@@ -328,6 +331,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_mma_kernel(
   __shared__ float s_acc[W][G][128];
   __shared__ float s_m[W][G], s_l[W][G];
   __shared__ __attribute__((aligned(16))) uint8_t s_v[W][KT * 128];
+  __shared__ __attribute__((aligned(16))) float s_f[W][2 * KT];   // the batch's K, V factors
 
   const int64_t bh = SPLIT ? blockIdx.x / S : blockIdx.x;   // sequence x KV head
   const int sp = SPLIT ? (int)(blockIdx.x % S) : 0;
@@ -340,14 +344,16 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_mma_kernel(
   const int64_t tbeg = SPLIT ? (int64_t)sp * chunk : 0;
   if constexpr (SPLIT) len = len < tbeg + chunk ? len : tbeg + chunk;
 
-  // B operand of the scores: head col (zero past G), elements 32 c + 8 qg .. + 7
+  // B operand of the scores: head col (zero past G); MFMA c takes elements 32 qg + 8 c .. + 7
+  // in the lanes of k group qg (the keys use the same assignment: a contraction is free to pair
+  // its terms in any order), so each lane's key pieces are 32 contiguous bytes
   bf16x8 qf[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     qf[c] = bf16x8{};
     if (col < G) {
       const uint4 v = *reinterpret_cast<const uint4*>(
-          q + ((b * H + kvh * G + col) * 128 + 32 * c + 8 * qg));
+          q + ((b * H + kvh * G + col) * 128 + 32 * qg + 8 * c));
       qf[c] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -365,25 +371,30 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_mma_kernel(
   auto row_of = [&](int64_t t) { return (b * T + (t < len ? t : len - 1)) * KVH + kvh; };
   for (int64_t t0 = tbeg + (int64_t)w * KT; t0 < len; t0 += W * KT) {
     // all loads of the batch first: value rows (token 8u + lane / 8, 16 bytes), key pieces
-    // (token 16 ch + col, bytes 32 c + 8 qg), factors of the lane's score rows
+    // (token 16 ch + col, bytes 32 qg .. + 31), one factor per lane (lanes 0..31 the keys' of
+    // tokens 0..31, lanes 32..63 the values')
     uint4 vraw[4];
-    uint2 kraw[2][4];
-    float ksr[2][4], vsr[2][4];
+    uint4 kraw[2][2];
+    const float fac = (lane < 32 ? k_si : v_si)[row_of(t0 + (lane & 31))];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       vraw[u] = *reinterpret_cast<const uint4*>(v_codes + row_of(t0 + 8 * u + (lane >> 3)) * 128 +
                                                 (lane & 7) * 16);
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
-      const int64_t kr = row_of(t0 + 16 * ch + col) * 128 + 8 * qg;
+      const int64_t kr = row_of(t0 + 16 * ch + col) * 128 + 32 * qg;
+      kraw[ch][0] = *reinterpret_cast<const uint4*>(k_codes + kr);
+      kraw[ch][1] = *reinterpret_cast<const uint4*>(k_codes + kr + 16);
+    }
+    // the factors of the lane's score rows (tokens 16 ch + 4 qg + r) through LDS
+    s_f[w][lane] = fac;
+    float ksr[2][4], vsr[2][4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) kraw[ch][c] = *reinterpret_cast<const uint2*>(k_codes + kr + 32 * c);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t sr = row_of(t0 + 16 * ch + 4 * qg + r);
-        ksr[ch][r] = k_si[sr];
-        vsr[ch][r] = v_si[sr];
-      }
+    for (int ch = 0; ch < 2; ++ch) {
+      const float4 kf = *reinterpret_cast<const float4*>(&s_f[w][16 * ch + 4 * qg]);
+      const float4 vf4 = *reinterpret_cast<const float4*>(&s_f[w][KT + 16 * ch + 4 * qg]);
+      ksr[ch][0] = kf.x; ksr[ch][1] = kf.y; ksr[ch][2] = kf.z; ksr[ch][3] = kf.w;
+      vsr[ch][0] = vf4.x; vsr[ch][1] = vf4.y; vsr[ch][2] = vf4.z; vsr[ch][3] = vf4.w;
     }
     // value rows to LDS, zero codes past the end (nothing but zero may reach the sums)
 #pragma unroll
@@ -397,9 +408,12 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_mma_kernel(
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int ch = 0; ch < 2; ++ch)
-        sc[ch] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            decode8_bf16<FMT>(v2i{(int)kraw[ch][c].x, (int)kraw[ch][c].y}), qf[c], sc[ch], 0, 0, 0);
+      for (int ch = 0; ch < 2; ++ch) {
+        const uint4& kp = kraw[ch][c >> 1];
+        const v2i codes = (c & 1) ? v2i{(int)kp.z, (int)kp.w} : v2i{(int)kp.x, (int)kp.y};
+        sc[ch] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode8_bf16<FMT>(codes), qf[c], sc[ch],
+                                                         0, 0, 0);
+      }
     float s[8];
     float mx = -INFINITY;
 #pragma unroll
