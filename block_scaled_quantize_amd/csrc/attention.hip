@@ -97,6 +97,25 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 
+// Buffer resource over nbytes (at most 4 GiB - 1) from base: raw 32-bit data, offsets at or
+// past nbytes read as zero.
+__device__ __forceinline__ uint4 attn_rsrc(const void* base, uint64_t nbytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  uint4 r;
+  r.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  r.z = __builtin_amdgcn_readfirstlane(nbytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)nbytes);
+  r.w = 0x00020000u;
+  return r;
+}
+typedef unsigned int attn_u32x4 __attribute__((ext_vector_type(4)));
+// 16 bytes per lane from buffer offset voff to LDS address lds + 16 * lane.
+__device__ __forceinline__ void attn_dma16(uint4 rsrc, uint32_t voff, uint32_t lds) {
+  const attn_u32x4 r = {rsrc.x, rsrc.y, rsrc.z, rsrc.w};
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(r), "s"(lds) : "memory", "m0");
+}
+
 // Eight FP8 codes (bytes of w.x then w.y) as bf16 (exact).
 template <int FMT>
 __device__ __forceinline__ bf16x8 decode8_bf16(v2i w) {
@@ -369,17 +388,22 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_mma_kernel(
   const int prow = jj < 4 ? 4 * qg + jj : 16 + 4 * qg + (jj - 4);
 
   auto row_of = [&](int64_t t) { return (b * T + (t < len ? t : len - 1)) * KVH + kvh; };
+  // value rows of this (sequence, KV head) for the LDS DMA: token t at t * KVH * 128 from the
+  // first row; the bound ends after the last valid token, so rows past it read as zeros
+  const uint4 vrsrc = attn_rsrc(v_codes + (b * T * KVH + kvh) * 128,
+                                len > 0 ? (uint64_t)((len - 1) * KVH * 128 + 128) : 0);
+  const uint32_t vlds = (uint32_t)reinterpret_cast<uintptr_t>(&s_v[w][0]);
   for (int64_t t0 = tbeg + (int64_t)w * KT; t0 < len; t0 += W * KT) {
+    // value rows straight into this wave's LDS rows (token 8u + lane / 8, bytes (lane % 8) 16)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      attn_dma16(vrsrc, (uint32_t)((t0 + 8 * u + (lane >> 3)) * KVH * 128 + (lane & 7) * 16),
+                 __builtin_amdgcn_readfirstlane(vlds + u * 1024));
     // all loads of the batch first: value rows (token 8u + lane / 8, 16 bytes), key pieces
     // (token 16 ch + col, bytes 32 qg .. + 31), one factor per lane (lanes 0..31 the keys' of
     // tokens 0..31, lanes 32..63 the values')
-    uint4 vraw[4];
     uint4 kraw[2][2];
     const float fac = (lane < 32 ? k_si : v_si)[row_of(t0 + (lane & 31))];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      vraw[u] = *reinterpret_cast<const uint4*>(v_codes + row_of(t0 + 8 * u + (lane >> 3)) * 128 +
-                                                (lane & 7) * 16);
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
       const int64_t kr = row_of(t0 + 16 * ch + col) * 128 + 32 * qg;
@@ -395,13 +419,6 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_mma_kernel(
       const float4 vf4 = *reinterpret_cast<const float4*>(&s_f[w][KT + 16 * ch + 4 * qg]);
       ksr[ch][0] = kf.x; ksr[ch][1] = kf.y; ksr[ch][2] = kf.z; ksr[ch][3] = kf.w;
       vsr[ch][0] = vf4.x; vsr[ch][1] = vf4.y; vsr[ch][2] = vf4.z; vsr[ch][3] = vf4.w;
-    }
-    // value rows to LDS, zero codes past the end (nothing but zero may reach the sums)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const bool ok = t0 + 8 * u + (lane >> 3) < len;
-      *reinterpret_cast<uint4*>(&s_v[w][(8 * u + (lane >> 3)) * 128 + (lane & 7) * 16]) =
-          ok ? vraw[u] : make_uint4(0u, 0u, 0u, 0u);
     }
     // scores of the two 16-token halves
     v4f sc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
@@ -452,6 +469,9 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_mma_kernel(
       pa[j] = (__bf16)pw;
       pl[j] = (__bf16)(pw - (float)pa[j]);
     }
+    // the value rows' DMA has landed (issued before every load the scores waited for, and vector
+    // memory operations complete in order; this wait makes it explicit)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     const uint8_t* vrow = &s_v[w][prow * 128 + 8 * hh];
     bf16x8 vb[8];
 #pragma unroll
@@ -584,6 +604,9 @@ int dispatch_split(int G, int64_t B, int64_t H, int64_t KVH, int64_t T, int64_t 
   }
 }
 
+// The matrix-core decode addresses a (sequence, KV head)'s value rows with 32-bit offsets.
+bool mma_offsets_ok(int64_t T, int64_t KVH) { return (T + 32) * KVH * 128 <= 0xFFFFFFFFll; }
+
 bool cache_sizes_ok(int64_t B, int64_t T, int64_t KVH) {
   // B * T * KVH * 128 bytes must be addressable with 64-bit offsets
   if (B < 0 || T < 0 || KVH < 0) return false;
@@ -638,6 +661,7 @@ extern "C" int fp8_attention_decode(int64_t B, int64_t H, int64_t KVH, int64_t T
   if (KVH == 0 || H % KVH != 0) return FP8BS_ERR_SHAPE;
   const int64_t G = H / KVH;
   if (G != 1 && G != 2 && G != 4 && G != 8) return FP8BS_ERR_UNSUPPORTED;
+  if (G <= 4 && !mma_offsets_ok(T, KVH)) return FP8BS_ERR_UNSUPPORTED;
   if (B * KVH > 0x7FFFFFFF || B > INT64_MAX / 256 / H) return FP8BS_ERR_SHAPE;
   if (!isfinite(sm_scale)) return FP8BS_ERR_ARG;
   if (!q_bf16 || !seq_lens || !out_bf16 ||
@@ -684,6 +708,7 @@ extern "C" int fp8_attention_decode_split(int64_t B, int64_t H, int64_t KVH, int
   if (KVH == 0 || H % KVH != 0) return FP8BS_ERR_SHAPE;
   const int64_t G = H / KVH;
   if (G != 1 && G != 2 && G != 4) return FP8BS_ERR_UNSUPPORTED;
+  if (!mma_offsets_ok(T, KVH)) return FP8BS_ERR_UNSUPPORTED;
   const int64_t S = ceil_div(T, chunk);
   if (B * KVH > 0x7FFFFFFF || S > 0x7FFFFFFF / (B * KVH) || B > INT64_MAX / 256 / H)
     return FP8BS_ERR_SHAPE;

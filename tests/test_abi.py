@@ -292,3 +292,12 @@ def test_decode_split_tokens_choice():
         c = bsq.decode_split_tokens(B, KVH, T)
         assert c % 256 == 0 and c >= 256
         assert B * KVH * -(-T // c) <= 512 + B * KVH        # about the target, not far above
+
+
+def test_attention_decode_offset_limit():
+    # the matrix-core kernels (1, 2 or 4 query heads per KV head) address one sequence and KV
+    # head's rows with 32-bit offsets
+    big = (1 << 32) // (8 * 128)          # T with (T + 32) * 8 * 128 >= 2^32
+    assert attn(T=big, KVH=8, H=32) == bsq.ERR_UNSUPPORTED
+    assert attn_split(T=big, KVH=8, H=32, wsb=1 << 40) == bsq.ERR_UNSUPPORTED
+    assert attn(T=big - 64, KVH=8, H=32, q=None) == bsq.ERR_NULL   # within the limit: validated on
