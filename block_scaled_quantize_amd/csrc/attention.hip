@@ -15,14 +15,10 @@
 // blockwise quantizer (amax over the 8 lanes by DPP, the same scale, encode and NaN handling).
 //
 // Decode attention (HBM-bound: every cached byte is read once per step): one workgroup of 4
-// waves per (sequence, KV head).  A wave takes 8 tokens per step (G <= 4 query heads per KV
-// head; 4 tokens for G = 8), 8 (16) lanes per token, each lane 16 (8) consecutive elements of
-// the key and value rows, 4 steps per batch with all their loads in flight; dot products are
-// reduced over the token's lanes, the softmax is kept online in base 2 (running maximum per
-// head, wave-uniform, reduced across lanes once per batch; running sums per lane), and the
-// four waves' partial results are merged through LDS at the end.  For G <= 4 query heads per
-// KV head both products run on the matrix cores (attn_decode_mma_kernel); the VALU kernel
-// (attn_decode_kernel) serves G = 8.
+// waves per (sequence, KV head) -- or per (sequence, KV head, chunk of tokens) in the split
+// form, whose partial results a second kernel merges -- with the query-key and the
+// probability-value products on the matrix cores (attn_decode_mma_kernel, below), the softmax
+// online in base 2, and the four waves' partial results merged through LDS at the end.
 #include <math.h>
 
 #include "common.h"
@@ -64,34 +60,6 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
 // ---------------------------------------------------------------- decode attention
 constexpr int kAttnWaves = 4;   // waves per workgroup (one workgroup per sequence and KV head)
 
-// Two FP8 codes (bytes 0, 1 of w, or 2, 3 for HIGH) to fp32.
-template <int FMT, bool HIGH>
-__device__ __forceinline__ void decode_pair(uint32_t w, float& a, float& b) {
-  typedef float f2 __attribute__((ext_vector_type(2)));
-  f2 r;
-  if constexpr (FMT == FP8BS_E4M3) r = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HIGH);
-  else r = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, HIGH);
-  a = r.x;
-  b = r.y;
-}
-
-// A lane's DL cache bytes of one row (16 or 8), loaded ahead of their decode.
-template <int DL>
-struct Raw {
-  uint32_t w[DL / 4];
-};
-template <int DL>
-__device__ __forceinline__ Raw<DL> load_raw(const uint8_t* p) {
-  Raw<DL> r;
-  if constexpr (DL == 16) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
-  } else {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    r.w[0] = v.x; r.w[1] = v.y;
-  }
-  return r;
-}
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -134,191 +102,8 @@ __device__ __forceinline__ bf16x8 decode8_bf16(v2i w) {
   return bf16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
-// The codes as bf16 pairs (exact: every FP8 value is a bf16 value).
-template <int FMT, int DL>
-__device__ __forceinline__ void decode_raw_bf16(const Raw<DL>& r, bf16x2 (&f)[DL / 2]) {
-#pragma unroll
-  for (int i = 0; i < DL / 4; ++i) {
-    if constexpr (FMT == FP8BS_E4M3) {
-      f[2 * i] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.w[i], 1.0f, false);
-      f[2 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.w[i], 1.0f, true);
-    } else {
-      f[2 * i] = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(r.w[i], 1.0f, false);
-      f[2 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(r.w[i], 1.0f, true);
-    }
-  }
-}
-
-template <int FMT, int DL>
-__device__ __forceinline__ void decode_raw(const Raw<DL>& r, float (&f)[DL]) {
-#pragma unroll
-  for (int i = 0; i < DL / 4; ++i) {
-    decode_pair<FMT, false>(r.w[i], f[4 * i], f[4 * i + 1]);
-    decode_pair<FMT, true>(r.w[i], f[4 * i + 2], f[4 * i + 3]);
-  }
-}
-
-template <int FMT, int G, int DLANE, int KBATCH, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void attn_decode_kernel(
-    int64_t H, int64_t KVH, int64_t T, const uint16_t* __restrict__ q,
-    const uint8_t* __restrict__ k_codes, const float* __restrict__ k_si,
-    const uint8_t* __restrict__ v_codes, const float* __restrict__ v_si,
-    const int32_t* __restrict__ seq_lens, float score_scale, uint16_t* __restrict__ out) {
-  constexpr int DL = DLANE;             // elements of a row per lane (16 or 8)
-  constexpr int LPT = 128 / DL;         // lanes per token
-  constexpr int TPS = 64 / LPT;         // tokens per wave step
-  constexpr int kBatch = KBATCH;        // wave steps whose loads are in flight together
-  __shared__ float s_acc[WAVES][G][128];
-  __shared__ float s_m[WAVES][G], s_l[WAVES][G];
-
-  const int64_t b = blockIdx.x / KVH, kvh = blockIdx.x % KVH;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int tg = lane / LPT, d0 = (lane % LPT) * DL;
-  int64_t len = seq_lens[b];
-  len = len < 0 ? 0 : (len > T ? T : len);
-
-  // queries of the group's heads as bf16 pairs: q . k is summed by v_dot2_f32_bf16 (exact
-  // products, fp32 sums) against the keys decoded to bf16
-  bf16x2 qb[G][DL / 2];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const uint16_t* qp = q + ((b * H + kvh * G + g) * 128 + d0);
-#pragma unroll
-    for (int i = 0; i < DL; i += 8) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qp + i);
-      qb[g][i / 2] = __builtin_bit_cast(bf16x2, v.x);
-      qb[g][i / 2 + 1] = __builtin_bit_cast(bf16x2, v.y);
-      qb[g][i / 2 + 2] = __builtin_bit_cast(bf16x2, v.z);
-      qb[g][i / 2 + 3] = __builtin_bit_cast(bf16x2, v.w);
-    }
-  }
-
-  float m[G], l[G], acc[G][DL];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -INFINITY;
-    l[g] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < DL; ++i) acc[g][i] = 0.0f;
-  }
-
-  // Steps are taken kBatch at a time: the loads of all of them are issued before any is used,
-  // so that each wave keeps kBatch steps of cache rows in flight.
-  for (int64_t step0 = w; step0 * TPS < len; step0 += WAVES * kBatch) {
-    Raw<DL> kr[kBatch], vr[kBatch];
-    float ks[kBatch], vs[kBatch];
-    bool valid[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int64_t t = (step0 + u * WAVES) * TPS + tg;
-      valid[u] = t < len;
-      const int64_t row = (b * T + (valid[u] ? t : len - 1)) * KVH + kvh;   // in bounds
-      kr[u] = load_raw<DL>(k_codes + row * 128 + d0);
-      vr[u] = load_raw<DL>(v_codes + row * 128 + d0);
-      ks[u] = k_si[row];
-      vs[u] = v_si[row];
-    }
-    // The batch's scores first, so that the running maximum is reduced across lanes once per
-    // batch and head; then the probabilities and the value sums.
-    float s[kBatch][G];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      bf16x2 kb[DL / 2];
-      decode_raw_bf16<FMT, DL>(kr[u], kb);
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float dot = 0.0f;
-#pragma unroll
-        for (int i = 0; i < DL / 2; ++i) dot = __builtin_amdgcn_fdot2_f32_bf16(qb[g][i], kb[i], dot, false);
-#pragma unroll
-        for (int off = 1; off < LPT; off <<= 1) dot += __shfl_xor(dot, off);
-        s[u][g] = valid[u] ? dot * (ks[u] * score_scale) : -INFINITY;   // base-2 logits
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float mx = s[0][g];
-#pragma unroll
-      for (int u = 1; u < kBatch; ++u) mx = fmaxf(mx, s[u][g]);
-#pragma unroll
-      for (int off = LPT; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-      // the batch maximum is the same in every lane: a scalar branch, taken only when the
-      // running maximum grows (then the sums are rescaled; -inf for a batch without a token
-      // never is)
-      mx = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(mx)));
-      if (mx > m[g]) {
-        const float alpha = __builtin_amdgcn_exp2f(m[g] - mx);   // 0 when m = -inf
-        l[g] *= alpha;
-#pragma unroll
-        for (int i = 0; i < DL; ++i) acc[g][i] *= alpha;
-        m[g] = mx;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      float vf[DL];
-      decode_raw<FMT, DL>(vr[u], vf);
-      if (!valid[u]) {
-        // (a lane past the end re-reads the last token: its values must not reach acc, not
-        // even as 0 * inf)
-#pragma unroll
-        for (int i = 0; i < DL; ++i) vf[i] = 0.0f;
-      }
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float p = valid[u] ? __builtin_amdgcn_exp2f(s[u][g] - m[g]) : 0.0f;
-        l[g] += p;
-        const float pv = p * vs[u];
-#pragma unroll
-        for (int i = 0; i < DL; ++i) acc[g][i] = fmaf(pv, vf[i], acc[g][i]);
-      }
-    }
-  }
-
-  // sums over the wave's token groups, then the four waves through LDS
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-#pragma unroll
-    for (int off = LPT; off < 64; off <<= 1) {
-      l[g] += __shfl_xor(l[g], off);
-#pragma unroll
-      for (int i = 0; i < DL; ++i) acc[g][i] += __shfl_xor(acc[g][i], off);
-    }
-  }
-  if (tg == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-#pragma unroll
-      for (int i = 0; i < DL; ++i) s_acc[w][g][d0 + i] = acc[g][i];
-      if (lane == 0) {
-        s_m[w][g] = m[g];
-        s_l[w][g] = l[g];
-      }
-    }
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < G * 128; idx += 64 * WAVES) {
-    const int g = idx >> 7, d = idx & 127;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < WAVES; ++v) mx = fmaxf(mx, s_m[v][g]);
-    float num = 0.0f, den = 0.0f;
-    if (mx != -INFINITY) {
-#pragma unroll
-      for (int v = 0; v < WAVES; ++v) {
-        const float f = __builtin_amdgcn_exp2f(s_m[v][g] - mx);   // 0 for a wave without tokens
-        num = fmaf(f, s_acc[v][g][d], num);
-        den = fmaf(f, s_l[v][g], den);
-      }
-    }
-    const float o = den > 0.0f ? num / den : 0.0f;   // no cached token: zeros
-    typedef __bf16 bf1;
-    const bf1 ob = (bf1)o;
-    out[(b * H + kvh * G + g) * 128 + d] = __builtin_bit_cast(uint16_t, ob);
-  }
-}
-
-// Decode attention with both products on the matrix cores, for G <= 4 query heads per KV head.
+// Decode attention with both products on the matrix cores (G = 1, 2, 4 or 8 query heads per KV
+// head: the heads are MFMA rows, 4 per k group of lanes).
 // A wave takes 32 consecutive tokens per batch.  Scores: one v_mfma_f32_16x16x32_bf16 per 16
 // tokens and 32 elements, A = keys (row = token; the lanes of k group g feed elements
 // 32 g .. 32 g + 31 to the four MFMAs, so each loads 32 contiguous bytes of its token's row, decoded
@@ -344,7 +129,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_mma_kernel(
     const uint8_t* __restrict__ v_codes, const float* __restrict__ v_si,
     const int32_t* __restrict__ seq_lens, float score_scale, uint16_t* __restrict__ out,
     int64_t chunk = 0, int S = 1, float* __restrict__ part = nullptr) {
-  static_assert(G >= 1 && G <= 4, "heads as MFMA columns / rows");
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "heads as MFMA columns / rows");
   constexpr int W = kAttnWaves;
   constexpr int KT = 32;   // tokens per batch
   __shared__ float s_acc[W][G][128];
@@ -381,7 +166,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_mma_kernel(
 #pragma unroll
   for (int g = 0; g < G; ++g) m[g] = -INFINITY;
   float lsum = 0.0f;   // head col, this lane's tokens
-  v4f pacc[8];         // lanes 0..15: heads 0..3 of element 16 cb + lane
+  v4f pacc[8];         // k group qg (lanes 16 qg .. + 15): heads 4 qg .. 4 qg + 3 of element 16 cb + col
 #pragma unroll
   for (int cb = 0; cb < 8; ++cb) pacc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
   const int jj = col >> 1, hh = col & 1;   // the token row this lane points at in the value reads
@@ -451,8 +236,9 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_mma_kernel(
       if (mg > m[g]) {
         const float alpha = __builtin_amdgcn_exp2f(m[g] - mg);   // 0 when m = -inf
         if (col == g) lsum *= alpha;
+        const float ap = qg == g / 4 ? alpha : 1.0f;   // head g's value sums: k group g / 4
 #pragma unroll
-        for (int cb = 0; cb < 8; ++cb) pacc[cb][g] *= alpha;
+        for (int cb = 0; cb < 8; ++cb) pacc[cb][g % 4] *= ap;
         m[g] = mg;
       }
     }
@@ -486,15 +272,17 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_mma_kernel(
       pacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb[cb], pacc[cb], 0, 0, 0);
   }
 
-  // denominators over the 4 k groups; lanes 0..15 hold the value sums, lanes 0..G-1 the heads'
-  // denominators and maxima
+  // denominators over the 4 k groups; k group qg holds the value sums of heads 4 qg + r, lanes
+  // 0..G-1 the heads' denominators and maxima
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
-  if (lane < 16) {
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+  for (int r = 0; r < 4; ++r) {
+    const int g = 4 * qg + r;
+    if (g < G) {
 #pragma unroll
-      for (int cb = 0; cb < 8; ++cb) s_acc[w][g][16 * cb + lane] = pacc[cb][g];
+      for (int cb = 0; cb < 8; ++cb) s_acc[w][g][16 * cb + col] = pacc[cb][r];
+    }
   }
   if (lane < G) {
     float ml = 0.0f;
@@ -570,7 +358,7 @@ int dispatch_attn(int G, dim3 grid, hipStream_t st, int64_t H, int64_t KVH, int6
     case 1: return launch(attn_decode_mma_kernel<FMT, 1>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out, (int64_t)0, 1, (float*)nullptr);
     case 2: return launch(attn_decode_mma_kernel<FMT, 2>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out, (int64_t)0, 1, (float*)nullptr);
     case 4: return launch(attn_decode_mma_kernel<FMT, 4>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out, (int64_t)0, 1, (float*)nullptr);
-    case 8: return launch(attn_decode_kernel<FMT, 8, 8, 4, kAttnWaves>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out);
+    case 8: return launch(attn_decode_mma_kernel<FMT, 8>, grid, block, st, H, KVH, T, q, kc, ks, vc, vs, lens, c, out, (int64_t)0, 1, (float*)nullptr);
     default: return FP8BS_ERR_UNSUPPORTED;
   }
 }
@@ -600,6 +388,7 @@ int dispatch_split(int G, int64_t B, int64_t H, int64_t KVH, int64_t T, int64_t 
     case 1: return launch_split<FMT, 1>(B, H, KVH, T, chunk, S, st, q, kc, ks, vc, vs, lens, c, part, out);
     case 2: return launch_split<FMT, 2>(B, H, KVH, T, chunk, S, st, q, kc, ks, vc, vs, lens, c, part, out);
     case 4: return launch_split<FMT, 4>(B, H, KVH, T, chunk, S, st, q, kc, ks, vc, vs, lens, c, part, out);
+    case 8: return launch_split<FMT, 8>(B, H, KVH, T, chunk, S, st, q, kc, ks, vc, vs, lens, c, part, out);
     default: return FP8BS_ERR_UNSUPPORTED;
   }
 }
@@ -661,7 +450,7 @@ extern "C" int fp8_attention_decode(int64_t B, int64_t H, int64_t KVH, int64_t T
   if (KVH == 0 || H % KVH != 0) return FP8BS_ERR_SHAPE;
   const int64_t G = H / KVH;
   if (G != 1 && G != 2 && G != 4 && G != 8) return FP8BS_ERR_UNSUPPORTED;
-  if (G <= 4 && !mma_offsets_ok(T, KVH)) return FP8BS_ERR_UNSUPPORTED;
+  if (!mma_offsets_ok(T, KVH)) return FP8BS_ERR_UNSUPPORTED;
   if (B * KVH > 0x7FFFFFFF || B > INT64_MAX / 256 / H) return FP8BS_ERR_SHAPE;
   if (!isfinite(sm_scale)) return FP8BS_ERR_ARG;
   if (!q_bf16 || !seq_lens || !out_bf16 ||
@@ -707,7 +496,7 @@ extern "C" int fp8_attention_decode_split(int64_t B, int64_t H, int64_t KVH, int
   if (B == 0 || H == 0) return FP8BS_OK;
   if (KVH == 0 || H % KVH != 0) return FP8BS_ERR_SHAPE;
   const int64_t G = H / KVH;
-  if (G != 1 && G != 2 && G != 4) return FP8BS_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return FP8BS_ERR_UNSUPPORTED;
   if (!mma_offsets_ok(T, KVH)) return FP8BS_ERR_UNSUPPORTED;
   const int64_t S = ceil_div(T, chunk);
   if (B * KVH > 0x7FFFFFFF || S > 0x7FFFFFFF / (B * KVH) || B > INT64_MAX / 256 / H)

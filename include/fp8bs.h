@@ -276,11 +276,12 @@ int fp8_kv_cache_append(int64_t B, int64_t KVH, int64_t T, const void* k_new_bf1
  * clamped to [0, T] and the cache dequantized (code value x the head vector's factor):
  *   s_t = sm_scale * sum_d q[b][h][d] K[b][t][kv][d],  t < L_b
  *   out[b][h][:] = sum_t softmax(s)_t V[b][t][kv][:]     (zeros when L_b = 0)
- * computed in fp32 (softmax online, in base 2), output rounded to bf16.
+ * computed to fp32 accuracy (matrix-core bf16 products of the exactly decoded cache with the bf16
+ * queries and with the softmax weights split into bf16 hi + lo terms, fp32 sums, softmax online
+ * in base 2), output rounded to bf16.
  *   q_bf16: [B][H][128] (16-byte aligned); seq_lens: device int32 [B]; out_bf16: [B][H][128].
- *   H / KVH must be 1, 2, 4 or 8 (else FP8BS_ERR_UNSUPPORTED); for H / KVH <= 4 also
- *   (T + 32) * KVH * 128 < 2^32 (one sequence and KV head's rows addressed with 32-bit offsets;
- *   else FP8BS_ERR_UNSUPPORTED).  Tokens at or past L_b are never read.  sm_scale must be
+ *   H / KVH must be 1, 2, 4 or 8, and (T + 32) * KVH * 128 < 2^32 (one sequence and KV head's
+ *   rows are addressed with 32-bit offsets); else FP8BS_ERR_UNSUPPORTED.  Tokens at or past L_b are never read.  sm_scale must be
  *   finite.
  * Errors: FP8BS_ERR_ARG, FP8BS_ERR_SHAPE, FP8BS_ERR_NULL, FP8BS_ERR_ALIGN,
  * FP8BS_ERR_UNSUPPORTED, FP8BS_ERR_LAUNCH. */
@@ -299,7 +300,7 @@ int fp8_attention_decode(int64_t B, int64_t H, int64_t KVH, int64_t T, const voi
  *     null when T = 0), holding per (sequence, KV head, chunk, query head) the chunk's maximum
  *     logit, its sum of weights and its 128 weighted value sums (130 floats); its contents on
  *     entry do not matter.  Calls that share a workspace on different streams race.
- *   H / KVH must be 1, 2 or 4, and (T + 32) * KVH * 128 < 2^32 (else FP8BS_ERR_UNSUPPORTED).
+ *   H / KVH must be 1, 2, 4 or 8, and (T + 32) * KVH * 128 < 2^32 (else FP8BS_ERR_UNSUPPORTED).
  *   Other arguments as above.
  * Errors: as fp8_attention_decode; FP8BS_ERR_SHAPE also for a chunk that is not a positive
  * multiple of 32 or a workspace smaller than required. */

@@ -271,7 +271,7 @@ def test_attention_decode_split_validation():
     assert attn_split(chunk=-32) == bsq.ERR_SHAPE
     assert attn_split(KVH=0) == bsq.ERR_SHAPE
     assert attn_split(H=30, KVH=8) == bsq.ERR_SHAPE
-    assert attn_split(H=64, KVH=8) == bsq.ERR_UNSUPPORTED    # 8 query heads per KV head
+    assert attn_split(H=128, KVH=8) == bsq.ERR_UNSUPPORTED   # 16 query heads per KV head
     assert attn_split(wsb=need - 4) == bsq.ERR_SHAPE         # workspace too small
     assert attn_split(ws=None) == bsq.ERR_NULL
     assert attn_split(q=None) == bsq.ERR_NULL

@@ -74,7 +74,7 @@ def test_decode_parity_ragged(gpu, H, KVH, fmt):
     assert np.all(out[0] == 0.0)
 
 
-@pytest.mark.parametrize("H,KVH", [(8, 8), (8, 4), (32, 8)])
+@pytest.mark.parametrize("H,KVH", [(8, 8), (8, 4), (32, 8), (32, 4)])
 @pytest.mark.parametrize("fmt", [E4, E5])
 @pytest.mark.parametrize("split", [32, 96, 256])
 def test_decode_split_parity_ragged(gpu, H, KVH, fmt, split):
