@@ -113,8 +113,9 @@ __device__ __forceinline__ bf16x8 decode8_bf16(v2i w) {
 // pi(j) = 4 (l / 16) + j for j < 4, 16 + 4 (l / 16) + j - 4 otherwise), so the probabilities x
 // value factors never leave the registers; they are split into bf16 hi + lo terms (their sum
 // within 2^-17 of the fp32 weight; bf16 x bf16 products are exact in fp32).  Values: the rows
-// go to a per-wave LDS buffer and come back transposed (ds_read_b64_tr_b8: 8 tokens pi(j) of
-// one element per lane), decoded exactly to bf16; two MFMAs per 16 elements.  The softmax is
+// go to a per-wave LDS buffer by buffer_load ... lds and come back transposed
+// (ds_read_b64_tr_b8: 8 tokens pi(j) of one element per lane), decoded exactly to bf16; two
+// MFMAs per 16 elements.  The softmax is
 // online in base 2 with a wave-uniform running maximum per head, reduced once per batch.  The
 // batch's 32 key and 32 value factors are loaded one per lane and handed out through LDS (memory
 // instructions, not bytes, set the pace here: 9 loads per lane and batch).
@@ -184,9 +185,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_mma_kernel(
     for (int u = 0; u < 4; ++u)
       attn_dma16(vrsrc, (uint32_t)((t0 + 8 * u + (lane >> 3)) * KVH * 128 + (lane & 7) * 16),
                  __builtin_amdgcn_readfirstlane(vlds + u * 1024));
-    // all loads of the batch first: value rows (token 8u + lane / 8, 16 bytes), key pieces
-    // (token 16 ch + col, bytes 32 qg .. + 31), one factor per lane (lanes 0..31 the keys' of
-    // tokens 0..31, lanes 32..63 the values')
+    // then the batch's other loads: key pieces (token 16 ch + col, bytes 32 qg .. + 31) and one
+    // factor per lane (lanes 0..31 the keys' of tokens 0..31, lanes 32..63 the values')
     uint4 kraw[2][2];
     const float fac = (lane < 32 ? k_si : v_si)[row_of(t0 + (lane & 31))];
 #pragma unroll
