@@ -444,15 +444,20 @@ def bench_backward(args):
         layers.append(L)
     flops = sum(4.0 * M * L["N"] * L["K"] for L in layers)
 
-    def step():
+    def step(t=None):
+        def run(key, fn):
+            return fn() if t is None else t.time(key, fn)
         for L in layers:
+            n = L["name"]
             qx, six = bsq.quantize_delayed(L["x"], bsq.E4M3, L["sx"])
             qw, siw = bsq.quantize_delayed(L["w"], bsq.E4M3, L["sw"])
             qdy, sidy = bsq.quantize_delayed(L["dy"], bsq.E5M2, L["sdy"])
-            bsq.gemm_blockscaled(bsq.DGRAD, qdy, bsq.E5M2, bsq.PER_TENSOR, sidy, qw, bsq.E4M3,
-                                 bsq.PER_TENSOR, siw, c=L["dx"])
-            bsq.gemm_blockscaled(bsq.WGRAD, qdy, bsq.E5M2, bsq.PER_TENSOR, sidy, qx, bsq.E4M3,
-                                 bsq.PER_TENSOR, six, c=L["dw"])
+            run(n + "/dgrad", lambda: bsq.gemm_blockscaled(
+                bsq.DGRAD, qdy, bsq.E5M2, bsq.PER_TENSOR, sidy, qw, bsq.E4M3, bsq.PER_TENSOR,
+                siw, c=L["dx"]))
+            run(n + "/wgrad", lambda: bsq.gemm_blockscaled(
+                bsq.WGRAD, qdy, bsq.E5M2, bsq.PER_TENSOR, sidy, qx, bsq.E4M3, bsq.PER_TENSOR,
+                six, c=L["dw"]))
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -461,6 +466,19 @@ def bench_backward(args):
         step()
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / args.steps
+    # the GEMM launches with HIP events on their stream (per-tensor scales on both operands)
+    timer = EventTimer()
+    for _ in range(max(3, min(args.steps, 10))):
+        step(timer)
+    torch.cuda.synchronize()
+    per_layer, gemm_ms = {}, 0.0
+    for L in layers:
+        n, f1 = L["name"], 2.0 * M * L["N"] * L["K"]
+        dg, wg = timer.mean_ms(n + "/dgrad"), timer.mean_ms(n + "/wgrad")
+        gemm_ms += dg + wg
+        per_layer[n] = dict(dgrad_us=round(dg * 1e3, 2), dgrad_tflops=round(f1 / dg / 1e9, 1),
+                            wgrad_us=round(wg * 1e3, 2), wgrad_tflops=round(f1 / wg / 1e9, 1))
+    achieved = flops / gemm_ms / 1e9
     return dict(metric="block-scaled FP8 GEMM TFLOP/s, backward (dgrad + wgrad, delayed scaling)",
                 value=round(flops / dt / 1e12, 2), unit="TFLOP/s", n_gpus=1, steps=args.steps,
                 warmup=args.warmup, ms_per_step=round(dt * 1e3, 4), higher_is_better=True,
@@ -468,7 +486,12 @@ def bench_backward(args):
                 data="synthetic",
                 config=dict(workload="llama3.1-8b-backward-linear", tokens=M,
                             scaling="per-tensor delayed, history 16, max, margin 0"),
-                roofline=None)
+                roofline=dict(bound="mfma", achieved=round(achieved, 1), peak=FP8_PEAK_TFLOPS,
+                              unit="TFLOP/s", frac=round(achieved / FP8_PEAK_TFLOPS, 4),
+                              traffic=None,
+                              kernel="gemm_kernel<Cfg<256,256,2,4>,DGRAD|WGRAD,E5M2,E4M3,tensor>",
+                              mean_launch_us=round(gemm_ms / (2 * len(layers)) * 1e3, 2)),
+                layers=per_layer)
 
 
 def bench_backward_blockwise(args):
