@@ -25,6 +25,8 @@ E4M3, E5M2 = 0, 1
 BLOCK_1x128, BLOCK_128x128, PER_TENSOR = 0, 1, 2
 SCALE_FP32, SCALE_POW2 = 0, 1
 FPROP, DGRAD, WGRAD = 0, 1, 2
+# output-tile configurations of the *_tiled entry points (fp8bs_tile)
+TILE_AUTO, TILE_256x128_W4, TILE_256x128_W8, TILE_256x256_W8, TILE_128x128_W4 = 0, 1, 2, 3, 4
 
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_WORKSPACE, ERR_ARG = (
@@ -73,6 +75,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.fp8_gemm_blockscaled_qout.argtypes = [i64, i64, i64, vp, i64, i32, vp, vp, i64, i32, vp,
                                               i32, vp, i64, i32, vp, i64, vp, vp]
     lib.fp8_grouped_gemm_pow2.argtypes = lib.fp8_grouped_gemm.argtypes
+    lib.fp8_gemm_blockscaled_tiled.argtypes = [i32, i32] + lib.fp8_gemm_blockscaled.argtypes
+    lib.fp8_grouped_gemm_tiled.argtypes = [i32, i32] + lib.fp8_grouped_gemm.argtypes
+    lib.fp8_gemm_blockscaled_qout_tiled.argtypes = [i32] + lib.fp8_gemm_blockscaled_qout.argtypes
     lib.fp8_kv_cache_append.argtypes = [i64, i64, i64, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp]
     lib.fp8_attention_decode.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp,
                                          ctypes.c_float, i32, vp, vp]
@@ -84,7 +89,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
                  "fp8_cast_fp32",
                  "fp8_gemm_blockscaled", "fp8_grouped_gemm", "fp8_gemm_blockscaled_pow2",
                  "fp8_gemm_blockscaled_qout",
-                 "fp8_grouped_gemm_pow2"):
+                 "fp8_grouped_gemm_pow2", "fp8_gemm_blockscaled_tiled", "fp8_grouped_gemm_tiled",
+                 "fp8_gemm_blockscaled_qout_tiled"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -120,6 +126,31 @@ def _ptr(t: torch.Tensor | None) -> int | None:
 
 def _ceil(a: int, b: int) -> int:
     return -(-a // b)
+
+
+def _need(t: torch.Tensor, shape, dtype, what: str, contiguous: bool = True) -> None:
+    """Raise ValueError unless t is a device tensor of this shape and dtype (and contiguous)."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{what}: expected a device tensor")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or (contiguous and not t.is_contiguous()):
+        raise ValueError(f"{what}: expected a{' contiguous' if contiguous else ''} {dtype} tensor of "
+                         f"shape {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+
+
+def _need_matrix(t: torch.Tensor, shape, dtype, what: str) -> None:
+    """A row-major 2-D matrix of this shape (any row pitch, unit column stride)."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{what}: expected a device tensor")
+    if (t.dim() != 2 or tuple(t.shape) != tuple(shape) or t.dtype != dtype or
+            (t.shape[1] > 1 and t.stride(1) != 1) or t.stride(0) < max(1, t.shape[1])):
+        raise ValueError(f"{what}: expected a row-major {dtype} matrix of shape {tuple(shape)}, got "
+                         f"{t.dtype} {tuple(t.shape)} strides {tuple(t.stride())}")
+
+
+def _operand_scale_shape(gran: int, stored_rows: int, stored_cols: int) -> tuple[int, ...]:
+    if gran not in (BLOCK_1x128, BLOCK_128x128, PER_TENSOR):
+        raise ValueError("unknown scale granularity")
+    return scale_shape(stored_rows, stored_cols, gran)
 
 
 def scale_shape(rows: int, cols: int, gran: int) -> tuple[int, ...]:
@@ -221,10 +252,12 @@ def cast_fp32(x: torch.Tensor, fmt: int, q: torch.Tensor | None = None, stream=N
 
 def gemm_blockscaled(layout: int, a: torch.Tensor, fa: int, ga: int, sa: torch.Tensor,
                      b: torch.Tensor, fb: int, gb: int, sb: torch.Tensor,
-                     c: torch.Tensor | None = None, stream=None, pow2: bool = False) -> torch.Tensor:
+                     c: torch.Tensor | None = None, stream=None, pow2: bool = False,
+                     tile: int = TILE_AUTO) -> torch.Tensor:
     """Block-scaled FP8 GEMM, bf16 output.  a, b are uint8 code matrices as stored:
     FPROP a[M,K], b[N,K]; DGRAD a[M,K], b[K,N]; WGRAD a[K,M], b[K,N].  pow2=True calls
-    fp8_gemm_blockscaled_pow2 (scales must be powers of two; applied by the MFMA)."""
+    fp8_gemm_blockscaled_pow2 (scales must be powers of two; applied by the MFMA).  tile other
+    than TILE_AUTO calls fp8_gemm_blockscaled_tiled with that tile configuration."""
     if a.dtype != torch.uint8 or b.dtype != torch.uint8 or a.dim() != 2 or b.dim() != 2:
         raise ValueError("a and b must be 2-D uint8 code matrices")
     if layout == FPROP:
@@ -241,12 +274,20 @@ def gemm_blockscaled(layout: int, a: torch.Tensor, fa: int, ga: int, sa: torch.T
             raise ValueError("K mismatch")
     else:
         raise ValueError("unknown layout")
+    _need_matrix(a, a.shape, torch.uint8, "a")
+    _need_matrix(b, b.shape, torch.uint8, "b")
+    _need(sa, _operand_scale_shape(ga, *a.shape), torch.float32, "sa")
+    _need(sb, _operand_scale_shape(gb, *b.shape), torch.float32, "sb")
     if c is None:
         c = _bf16_out(M, N, a.device)
+    _need_matrix(c, (M, N), torch.bfloat16, "c")
+    args = (layout, M, N, K, _ptr(a), a.stride(0), fa, ga, _ptr(sa), _ptr(b), b.stride(0), fb, gb,
+            _ptr(sb), _ptr(c), c.stride(0), _stream(stream))
+    if tile != TILE_AUTO:
+        _check(load().fp8_gemm_blockscaled_tiled(tile, int(pow2), *args), "fp8_gemm_blockscaled_tiled")
+        return c
     name = "fp8_gemm_blockscaled_pow2" if pow2 else "fp8_gemm_blockscaled"
-    _check(getattr(load(), name)(layout, M, N, K, _ptr(a), a.stride(0), fa, ga, _ptr(sa),
-                                 _ptr(b), b.stride(0), fb, gb, _ptr(sb), _ptr(c),
-                                 c.stride(0), _stream(stream)), name)
+    _check(getattr(load(), name)(*args), name)
     return c
 
 
@@ -254,46 +295,71 @@ def gemm_blockscaled_qout(a: torch.Tensor, ga: int, sa: torch.Tensor, b: torch.T
                           sb: torch.Tensor, mode_out: int = SCALE_FP32, pow2_inputs: bool = False,
                           want_bf16: bool = True, c: torch.Tensor | None = None,
                           cq: torch.Tensor | None = None, cqs: torch.Tensor | None = None,
-                          stream=None):
+                          stream=None, tile: int = TILE_AUTO):
     """fprop GEMM (a[M,K] . b[N,K]^T, E4M3 codes) whose epilogue also quantizes the bf16 output
     in 1x128 blocks (E4M3).  Returns (c bf16 [M,N] or None, cq uint8 [M,N],
-    cqs float32 [ceil(N/128), M])."""
+    cqs float32 [ceil(N/128), M]).  tile other than TILE_AUTO calls
+    fp8_gemm_blockscaled_qout_tiled."""
     if a.dtype != torch.uint8 or b.dtype != torch.uint8 or a.dim() != 2 or b.dim() != 2:
         raise ValueError("a and b must be 2-D uint8 code matrices")
     (M, K), N = a.shape, b.shape[0]
     if b.shape[1] != K:
         raise ValueError("K mismatch")
+    _need_matrix(a, a.shape, torch.uint8, "a")
+    _need_matrix(b, b.shape, torch.uint8, "b")
+    _need(sa, _operand_scale_shape(ga, M, K), torch.float32, "sa")
+    _need(sb, _operand_scale_shape(gb, N, K), torch.float32, "sb")
     if c is None and want_bf16:
         c = _bf16_out(M, N, a.device)
+    if c is not None:
+        _need_matrix(c, (M, N), torch.bfloat16, "c")
     if cq is None:
         cq = torch.empty((M, N), dtype=torch.uint8, device=a.device)
+    _need_matrix(cq, (M, N), torch.uint8, "cq")
     if cqs is None:
         cqs = torch.empty(((N + 127) // 128, M), dtype=torch.float32, device=a.device)
-    _check(load().fp8_gemm_blockscaled_qout(M, N, K, _ptr(a), a.stride(0), ga, _ptr(sa), _ptr(b),
-                                            b.stride(0), gb, _ptr(sb), int(pow2_inputs),
-                                            _ptr(c) if c is not None else None,
-                                            c.stride(0) if c is not None else 0, mode_out,
-                                            _ptr(cq), cq.stride(0), _ptr(cqs), _stream(stream)),
-           "fp8_gemm_blockscaled_qout")
+    _need(cqs, ((N + 127) // 128, M), torch.float32, "cqs")
+    args = (M, N, K, _ptr(a), a.stride(0), ga, _ptr(sa), _ptr(b), b.stride(0), gb, _ptr(sb),
+            int(pow2_inputs), _ptr(c) if c is not None else None,
+            c.stride(0) if c is not None else 0, mode_out, _ptr(cq), cq.stride(0), _ptr(cqs),
+            _stream(stream))
+    if tile != TILE_AUTO:
+        _check(load().fp8_gemm_blockscaled_qout_tiled(tile, *args), "fp8_gemm_blockscaled_qout_tiled")
+    else:
+        _check(load().fp8_gemm_blockscaled_qout(*args), "fp8_gemm_blockscaled_qout")
     return c, cq, cqs
 
 
 def grouped_gemm(offsets: torch.Tensor, a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor,
                  sb: torch.Tensor, fa: int = E4M3, fb: int = E4M3,
-                 c: torch.Tensor | None = None, stream=None, pow2: bool = False) -> torch.Tensor:
+                 c: torch.Tensor | None = None, stream=None, pow2: bool = False,
+                 tile: int = TILE_AUTO) -> torch.Tensor:
     """Grouped FP8 GEMM: rows [offsets[g], offsets[g+1]) of a[total_M, K] times b[g][N, K]^T.
     offsets is a device int64 tensor of num_groups + 1 entries.  pow2=True calls
-    fp8_grouped_gemm_pow2 (power-of-two scales applied by the MFMA)."""
-    if offsets.dtype != torch.int64 or b.dim() != 3:
-        raise ValueError("offsets must be int64 and b must be [G, N, K]")
+    fp8_grouped_gemm_pow2 (power-of-two scales applied by the MFMA); tile other than TILE_AUTO
+    calls fp8_grouped_gemm_tiled."""
+    if b.dim() != 3 or b.dtype != torch.uint8 or not b.is_cuda:
+        raise ValueError("b must be a uint8 device tensor [G, N, K]")
     G, N, K = b.shape
+    if (b.stride(2) != 1 and K > 1) or b.stride(1) < K or (G > 1 and b.stride(0) != N * b.stride(1)):
+        raise ValueError("b must hold [G, N, K] with unit column stride and experts N rows apart")
+    _need(offsets, (G + 1,), torch.int64, "offsets")
+    if a.dim() != 2 or a.shape[1] != K:
+        raise ValueError("a must be [total_M, K]")
+    _need_matrix(a, a.shape, torch.uint8, "a")
     total_m = a.shape[0]
+    _need(sa, scale_shape(total_m, K, BLOCK_1x128), torch.float32, "sa")
+    _need(sb, (G, _ceil(N, 128), _ceil(K, 128)), torch.float32, "sb")
     if c is None:
         c = _bf16_out(total_m, N, a.device)
+    _need_matrix(c, (total_m, N), torch.bfloat16, "c")
+    args = (G, _ptr(offsets), total_m, N, K, _ptr(a), a.stride(0), fa, _ptr(sa), _ptr(b),
+            b.stride(1), fb, _ptr(sb), _ptr(c), c.stride(0), _stream(stream))
+    if tile != TILE_AUTO:
+        _check(load().fp8_grouped_gemm_tiled(tile, int(pow2), *args), "fp8_grouped_gemm_tiled")
+        return c
     name = "fp8_grouped_gemm_pow2" if pow2 else "fp8_grouped_gemm"
-    _check(getattr(load(), name)(G, _ptr(offsets), total_m, N, K, _ptr(a), a.stride(0), fa,
-                                 _ptr(sa), _ptr(b), b.stride(1), fb, _ptr(sb), _ptr(c),
-                                 c.stride(0), _stream(stream)), name)
+    _check(getattr(load(), name)(*args), name)
     return c
 
 

@@ -36,9 +36,8 @@
 
 #include <float.h>
 
-#include <stdlib.h>
-
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -866,49 +865,60 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
 }
 
 // Grouped: a persistent grid walks the concatenation of every group's m tiles (times the n
-// tiles).  Each workgroup first builds, in LDS, the group bounds (clamped to [0, M] and made
-// non-decreasing) and the prefix count of m tiles per group, then maps each of its tiles to
-// (group, m tile, n tile) by binary search.  With two LDS stages the next tile's first K block
-// is loaded while the current tile finishes (see gemm_tile).
+// tiles).  Each workgroup first builds, in LDS, the group bounds -- each offset clamped to
+// [0, M] and raised to the largest offset before it, so that groups never overlap and a
+// decreasing offset empties the groups it would have reopened -- and the prefix count of m
+// tiles per group, then maps each of its tiles to (group, m tile, n tile) by binary search.
+// With two LDS stages the next tile's first K block is loaded while the current tile finishes
+// (see gemm_tile).
 constexpr int kMaxGroups = 1024;
+
+// Inclusive scan of v over the workgroup's threads in index order (op: max or +), continued
+// from carry; also returns the total through carry.  Every thread of the workgroup calls it.
+template <int THREADS, bool MAX>
+__device__ __forceinline__ int block_scan(int v, int& carry, int* s_wave) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off);
+    if (lane >= off) v = MAX ? max(v, o) : v + o;
+  }
+  if (lane == 63) s_wave[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int before = carry;
+  for (int w = 0; w < (int)(threadIdx.x >> 6); ++w)
+    before = MAX ? max(before, s_wave[w]) : before + s_wave[w];
+  int total = carry;
+  for (int w = 0; w < THREADS / 64; ++w) total = MAX ? max(total, s_wave[w]) : total + s_wave[w];
+  carry = total;
+  __syncthreads();
+  return MAX ? max(before, v) : before + v;
+}
 
 template <class C, int FA, int FB, int SM>
 __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_prefix[kMaxGroups + 1];
-  __shared__ int s_lo[kMaxGroups + 1];   // clamped group offsets (M < 2^31)
+  __shared__ int s_lo[kMaxGroups + 1];   // group bounds, clamped and non-decreasing (M < 2^31)
   __shared__ int s_wave_sum[C::kWaves];
   constexpr int BM = C::BM;
   constexpr bool PF = C::kStages == 2;
   const int G = p.num_groups;
-  for (int gi = threadIdx.x; gi <= G; gi += C::kThreads)
-    s_lo[gi] = (int)std::min<int64_t>(std::max<int64_t>(p.offsets[gi], 0), p.M);
+  int run_max = 0;
+  for (int base = 0; base <= G; base += C::kThreads) {
+    const int gi = base + threadIdx.x;
+    const int v = gi <= G ? (int)std::min<int64_t>(std::max<int64_t>(p.offsets[gi], 0), p.M) : 0;
+    const int m = block_scan<C::kThreads, true>(v, run_max, s_wave_sum);
+    if (gi <= G) s_lo[gi] = m;
+  }
   __syncthreads();
   // m tiles per group, prefix-summed
   int carry = 0;
   for (int base = 0; base < G; base += C::kThreads) {
     const int gi = base + threadIdx.x;
-    int tiles = 0;
-    if (gi < G) {
-      const int lo = s_lo[gi], hi = std::max(s_lo[gi + 1], lo);
-      tiles = (hi - lo + BM - 1) / BM;
-    }
-    int v = tiles;
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(v, off);
-      if (lane >= off) v += o;
-    }
-    if (lane == 63) s_wave_sum[threadIdx.x >> 6] = v;
-    __syncthreads();
-    int before = carry;
-    for (int w = 0; w < (int)(threadIdx.x >> 6); ++w) before += s_wave_sum[w];
-    if (gi < G) s_prefix[gi + 1] = before + v;
-    int total = carry;
-    for (int w = 0; w < C::kWaves; ++w) total += s_wave_sum[w];
-    carry = total;
-    __syncthreads();
+    const int tiles = gi < G ? (s_lo[gi + 1] - s_lo[gi] + BM - 1) / BM : 0;
+    const int v = block_scan<C::kThreads, false>(tiles, carry, s_wave_sum);
+    if (gi < G) s_prefix[gi + 1] = v;
   }
   if (threadIdx.x == 0) s_prefix[0] = 0;
   __syncthreads();
@@ -929,7 +939,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(GemmParams
     // (the same in every lane: kept in scalar registers)
     const int gi = __builtin_amdgcn_readfirstlane(lo);
     const int glo = __builtin_amdgcn_readfirstlane(s_lo[gi]);
-    const int ghi = std::max(__builtin_amdgcn_readfirstlane(s_lo[gi + 1]), glo);
+    const int ghi = __builtin_amdgcn_readfirstlane(s_lo[gi + 1]);
     const int m0 = glo + __builtin_amdgcn_readfirstlane(mt - s_prefix[gi]) * BM;
     return Tile{gi, m0, std::min(m0 + BM, ghi), __builtin_amdgcn_readfirstlane(tn) * C::BN};
   };
@@ -959,14 +969,25 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(GemmParams
   }
 }
 
-template <typename KernelT>
-int launch_gemm(KernelT kernel, int blocks, int threads, int lds, hipStream_t st,
-                const GemmParams& p) {
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
-    return FP8BS_ERR_LAUNCH;
+// Launch one GEMM kernel.  Kernels that use more than 64 KiB of dynamic LDS need the limit
+// raised once per device; that is done on the first launch of each kernel instantiation on a
+// device (a bit per device, set after the call succeeded), so later launches only enqueue.
+constexpr int kMaxDevices = 64;
+
+template <auto KERNEL>
+int launch_gemm(int blocks, int threads, int lds, hipStream_t st, const GemmParams& p) {
+  static std::atomic<uint64_t> lds_ready{0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP8BS_ERR_LAUNCH;
+  const uint64_t bit = uint64_t(1) << dev;
+  if (!(lds_ready.load(std::memory_order_acquire) & bit)) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(KERNEL),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+      return FP8BS_ERR_LAUNCH;
+    lds_ready.fetch_or(bit, std::memory_order_acq_rel);
+  }
   void* args[] = {const_cast<GemmParams*>(&p)};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(blocks),
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(KERNEL), dim3(blocks),
                                  dim3(threads), args, lds, st);
   return e == hipSuccess ? FP8BS_OK : FP8BS_ERR_LAUNCH;
 }
@@ -982,24 +1003,31 @@ int launch_dense(GemmParams p, hipStream_t st) {
   p.tiles_m = (int)ceil_div(p.M, C::BM);
   p.tiles_n = (int)ceil_div(p.N, C::BN);
   if ((int64_t)p.tiles_m * p.tiles_n > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
-  return launch_gemm(gemm_kernel<C, LAYOUT, FA, FB, SM, QO>, p.tiles_m * p.tiles_n, C::kThreads,
-                     C::kLds, st, p);
+  return launch_gemm<gemm_kernel<C, LAYOUT, FA, FB, SM, QO>>(p.tiles_m * p.tiles_n, C::kThreads,
+                                                             C::kLds, st, p);
 }
 
-// Variant choice: the largest tile that still gives every CU at least one workgroup (two
-// waves per SIMD hide LDS and MFMA latency best).  FP8BS_GEMM_VARIANT (A, B, C or D) overrides
-// the choice, for tuning and tests.
-char pick_variant(int64_t M, int64_t N) {
-  const char* e = getenv("FP8BS_GEMM_VARIANT");
-  if (e && (e[0] == 'A' || e[0] == 'B' || e[0] == 'C' || e[0] == 'D')) return e[0];
+// Tile configuration of a dense GEMM: FP8BS_TILE_AUTO takes the largest tile that still gives
+// every CU at least one workgroup (two waves per SIMD hide LDS and MFMA latency best); any
+// other value of fp8bs_tile forces that configuration (the *_tiled entry points).
+char pick_variant(int64_t M, int64_t N, int tile) {
+  switch (tile) {
+    case FP8BS_TILE_256x128_W4: return 'A';
+    case FP8BS_TILE_256x128_W8: return 'B';
+    case FP8BS_TILE_256x256_W8: return 'C';
+    case FP8BS_TILE_128x128_W4: return 'D';
+    default: break;
+  }
   if (ceil_div(M, 256) * ceil_div(N, 256) >= 256) return 'C';
   if (ceil_div(M, 256) * ceil_div(N, 128) >= 256) return 'B';
   return 'D';
 }
 
+inline bool tile_ok(int tile) { return tile >= FP8BS_TILE_AUTO && tile <= FP8BS_TILE_128x128_W4; }
+
 template <int LAYOUT, int FA, int FB, int SM, int QO = 0>
-int dispatch_variant(const GemmParams& p, hipStream_t st) {
-  switch (pick_variant(p.M, p.N)) {
+int dispatch_variant(const GemmParams& p, int tile, hipStream_t st) {
+  switch (pick_variant(p.M, p.N, tile)) {
     case 'B': return launch_dense<CfgB, LAYOUT, FA, FB, SM, QO>(p, st);
     case 'C': return launch_dense<CfgC, LAYOUT, FA, FB, SM, QO>(p, st);
     case 'D': return launch_dense<CfgD, LAYOUT, FA, FB, SM, QO>(p, st);
@@ -1008,23 +1036,23 @@ int dispatch_variant(const GemmParams& p, hipStream_t st) {
 }
 
 template <int LAYOUT, int SM>
-int dispatch_formats(int fa, int fb, const GemmParams& p, hipStream_t st) {
-  if (fa == FP8BS_E4M3 && fb == FP8BS_E4M3) return dispatch_variant<LAYOUT, FP8BS_E4M3, FP8BS_E4M3, SM>(p, st);
-  if (fa == FP8BS_E5M2 && fb == FP8BS_E4M3) return dispatch_variant<LAYOUT, FP8BS_E5M2, FP8BS_E4M3, SM>(p, st);
-  if (fa == FP8BS_E4M3 && fb == FP8BS_E5M2) return dispatch_variant<LAYOUT, FP8BS_E4M3, FP8BS_E5M2, SM>(p, st);
-  return dispatch_variant<LAYOUT, FP8BS_E5M2, FP8BS_E5M2, SM>(p, st);
+int dispatch_formats(int fa, int fb, const GemmParams& p, int tile, hipStream_t st) {
+  if (fa == FP8BS_E4M3 && fb == FP8BS_E4M3) return dispatch_variant<LAYOUT, FP8BS_E4M3, FP8BS_E4M3, SM>(p, tile, st);
+  if (fa == FP8BS_E5M2 && fb == FP8BS_E4M3) return dispatch_variant<LAYOUT, FP8BS_E5M2, FP8BS_E4M3, SM>(p, tile, st);
+  if (fa == FP8BS_E4M3 && fb == FP8BS_E5M2) return dispatch_variant<LAYOUT, FP8BS_E4M3, FP8BS_E5M2, SM>(p, tile, st);
+  return dispatch_variant<LAYOUT, FP8BS_E5M2, FP8BS_E5M2, SM>(p, tile, st);
 }
 
 template <int SM>
-int dispatch_dense(int layout, int fa, int fb, const GemmParams& p, hipStream_t st) {
+int dispatch_dense(int layout, int fa, int fb, const GemmParams& p, int tile, hipStream_t st) {
   if constexpr (SM == kScaleFoldRows || SM == kScaleHwRows) {
     // 1x128 weight scales need a K-major weight operand: fprop only (checked by the caller)
-    return dispatch_formats<FP8BS_FPROP, SM>(fa, fb, p, st);
+    return dispatch_formats<FP8BS_FPROP, SM>(fa, fb, p, tile, st);
   }
   switch (layout) {
-    case FP8BS_FPROP: return dispatch_formats<FP8BS_FPROP, SM>(fa, fb, p, st);
-    case FP8BS_DGRAD: return dispatch_formats<FP8BS_DGRAD, SM>(fa, fb, p, st);
-    default: return dispatch_formats<FP8BS_WGRAD, SM>(fa, fb, p, st);
+    case FP8BS_FPROP: return dispatch_formats<FP8BS_FPROP, SM>(fa, fb, p, tile, st);
+    case FP8BS_DGRAD: return dispatch_formats<FP8BS_DGRAD, SM>(fa, fb, p, tile, st);
+    default: return dispatch_formats<FP8BS_WGRAD, SM>(fa, fb, p, tile, st);
   }
 }
 
@@ -1056,11 +1084,12 @@ bool scale_index(int gran, bool kmajor, bool weight_side, int64_t rows, int64_t 
   return false;
 }
 
-// Grouped GEMM tile choice (FP8BS_GROUPED_VARIANT = B, C or D overrides, for tuning).
-char pick_grouped_variant() {
-  const char* e = getenv("FP8BS_GROUPED_VARIANT");
-  if (e && (e[0] == 'B' || e[0] == 'C' || e[0] == 'D')) return e[0];
-  return 'C';   // fastest on the MoE shapes despite 10% padding in ragged 256-row tiles
+// Grouped GEMM tile configuration: FP8BS_TILE_AUTO takes 256x256 (fastest on the MoE shapes
+// despite the padding of ragged 256-row tiles); FP8BS_TILE_256x128_W8 and
+// FP8BS_TILE_128x128_W4 force the others.
+inline bool grouped_tile_ok(int tile) {
+  return tile == FP8BS_TILE_AUTO || tile == FP8BS_TILE_256x128_W8 ||
+         tile == FP8BS_TILE_256x256_W8 || tile == FP8BS_TILE_128x128_W4;
 }
 
 template <class C, int SM>
@@ -1069,18 +1098,19 @@ int launch_grouped(int fa, int fb, int cus, GemmParams p, hipStream_t st) {
   p.tiles_m = (int)(ceil_div(p.M, C::BM) + p.num_groups);   // upper bound on m tiles
   if ((int64_t)p.tiles_m * p.tiles_n > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
   const int blocks = (int)std::min<int64_t>((int64_t)p.tiles_m * p.tiles_n, std::max(cus, 1));
-  if (fa == FP8BS_E4M3 && fb == FP8BS_E4M3) return launch_gemm(grouped_gemm_kernel<C, FP8BS_E4M3, FP8BS_E4M3, SM>, blocks, C::kThreads, C::kLds, st, p);
-  if (fa == FP8BS_E5M2 && fb == FP8BS_E4M3) return launch_gemm(grouped_gemm_kernel<C, FP8BS_E5M2, FP8BS_E4M3, SM>, blocks, C::kThreads, C::kLds, st, p);
-  if (fa == FP8BS_E4M3 && fb == FP8BS_E5M2) return launch_gemm(grouped_gemm_kernel<C, FP8BS_E4M3, FP8BS_E5M2, SM>, blocks, C::kThreads, C::kLds, st, p);
-  return launch_gemm(grouped_gemm_kernel<C, FP8BS_E5M2, FP8BS_E5M2, SM>, blocks, C::kThreads, C::kLds, st, p);
+  constexpr int E4 = FP8BS_E4M3, E5 = FP8BS_E5M2;
+  if (fa == E4 && fb == E4) return launch_gemm<grouped_gemm_kernel<C, E4, E4, SM>>(blocks, C::kThreads, C::kLds, st, p);
+  if (fa == E5 && fb == E4) return launch_gemm<grouped_gemm_kernel<C, E5, E4, SM>>(blocks, C::kThreads, C::kLds, st, p);
+  if (fa == E4 && fb == E5) return launch_gemm<grouped_gemm_kernel<C, E4, E5, SM>>(blocks, C::kThreads, C::kLds, st, p);
+  return launch_gemm<grouped_gemm_kernel<C, E5, E5, SM>>(blocks, C::kThreads, C::kLds, st, p);
 }
 
 template <int SM>
-int dispatch_grouped(int fa, int fb, int cus, const GemmParams& p, hipStream_t st) {
-  switch (pick_grouped_variant()) {
-    case 'C': return launch_grouped<CfgC, SM>(fa, fb, cus, p, st);
-    case 'D': return launch_grouped<CfgD, SM>(fa, fb, cus, p, st);
-    default: return launch_grouped<CfgB, SM>(fa, fb, cus, p, st);
+int dispatch_grouped(int fa, int fb, int cus, const GemmParams& p, int tile, hipStream_t st) {
+  switch (tile) {
+    case FP8BS_TILE_256x128_W8: return launch_grouped<CfgB, SM>(fa, fb, cus, p, st);
+    case FP8BS_TILE_128x128_W4: return launch_grouped<CfgD, SM>(fa, fb, cus, p, st);
+    default: return launch_grouped<CfgC, SM>(fa, fb, cus, p, st);
   }
 }
 
@@ -1168,13 +1198,41 @@ inline int grouped_params(int32_t num_groups, const int64_t* group_offsets, int6
   return FP8BS_OK;
 }
 
+// Compute units of the current device, read once per device (the persistent grouped grid has
+// one workgroup per CU).  0 when the device cannot be queried.
 inline int device_cus() {
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    cus = 256;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus > 0) return cus;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return 0;
+  cached[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 
 }  // namespace
+
+// Entry-point bodies shared by the exported functions of gemm.hip and gemm_pow2.hip (each is
+// defined in one of them; hidden, not part of the C ABI).  pow2 = false: fp32 block scales
+// folded between K blocks; pow2 = true: power-of-2 scales given to the MFMA as E8M0.
+__attribute__((visibility("hidden"))) int gemm_dense_fp32(
+    int tile, int layout, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int fa,
+    int ga, const float* sa, const void* B, int64_t ldb, int fb, int gb, const float* sb,
+    void* C, int64_t ldc, hipStream_t st);
+__attribute__((visibility("hidden"))) int gemm_dense_pow2(
+    int tile, int layout, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int fa,
+    int ga, const float* sa, const void* B, int64_t ldb, int fb, int gb, const float* sb,
+    void* C, int64_t ldc, hipStream_t st);
+__attribute__((visibility("hidden"))) int gemm_grouped_fp32(
+    int tile, int32_t G, const int64_t* offsets, int64_t M, int64_t N, int64_t K, const void* A,
+    int64_t lda, int fa, const float* sa, const void* B, int64_t ldb, int fb, const float* sb,
+    void* C, int64_t ldc, hipStream_t st);
+__attribute__((visibility("hidden"))) int gemm_grouped_pow2(
+    int tile, int32_t G, const int64_t* offsets, int64_t M, int64_t N, int64_t K, const void* A,
+    int64_t lda, int fa, const float* sa, const void* B, int64_t ldb, int fb, const float* sb,
+    void* C, int64_t ldc, hipStream_t st);
+
 }  // namespace fp8bs

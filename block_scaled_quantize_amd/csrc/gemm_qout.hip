@@ -11,14 +11,14 @@
 
 using namespace fp8bs;
 
-extern "C" int fp8_gemm_blockscaled_qout(int64_t M, int64_t N, int64_t K, const void* A,
-                                         int64_t lda, int ga, const float* scale_inv_a,
-                                         const void* B, int64_t ldb, int gb,
-                                         const float* scale_inv_b, int pow2_inputs,
-                                         void* C_bf16, int64_t ldc, int mode_out, void* Cq,
-                                         int64_t ldcq, float* cq_scale_inv, void* stream) {
+namespace {
+
+int gemm_qout(int tile, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int ga,
+              const float* scale_inv_a, const void* B, int64_t ldb, int gb,
+              const float* scale_inv_b, int pow2_inputs, void* C_bf16, int64_t ldc,
+              int mode_out, void* Cq, int64_t ldcq, float* cq_scale_inv, hipStream_t st) {
   if ((mode_out != FP8BS_SCALE_FP32 && mode_out != FP8BS_SCALE_POW2) ||
-      (pow2_inputs != 0 && pow2_inputs != 1))
+      (pow2_inputs != 0 && pow2_inputs != 1) || !tile_ok(tile))
     return FP8BS_ERR_ARG;
   GemmParams p{};
   bool tensor_only = false, empty = false, b_rows = false;
@@ -35,16 +35,39 @@ extern "C" int fp8_gemm_blockscaled_qout(int64_t M, int64_t N, int64_t K, const 
   p.ldcq = ldcq;
   p.cqs = cq_scale_inv;
   p.cq_vec = aligned4(Cq) && ldcq % 4 == 0;
-  hipStream_t st = static_cast<hipStream_t>(stream);
   constexpr int E4 = FP8BS_E4M3, FP = FP8BS_FPROP;
   const bool pow2_out = mode_out == FP8BS_SCALE_POW2;
   // output codes: E4M3, 1 + 2 * format + power-of-2
   if (tensor_only)
-    return pow2_out ? dispatch_variant<FP, E4, E4, kScaleTensor, 2>(p, st)
-                    : dispatch_variant<FP, E4, E4, kScaleTensor, 1>(p, st);
+    return pow2_out ? dispatch_variant<FP, E4, E4, kScaleTensor, 2>(p, tile, st)
+                    : dispatch_variant<FP, E4, E4, kScaleTensor, 1>(p, tile, st);
   if (pow2_inputs)
-    return pow2_out ? dispatch_variant<FP, E4, E4, kScaleHw, 2>(p, st)
-                    : dispatch_variant<FP, E4, E4, kScaleHw, 1>(p, st);
-  return pow2_out ? dispatch_variant<FP, E4, E4, kScaleFold, 2>(p, st)
-                  : dispatch_variant<FP, E4, E4, kScaleFold, 1>(p, st);
+    return pow2_out ? dispatch_variant<FP, E4, E4, kScaleHw, 2>(p, tile, st)
+                    : dispatch_variant<FP, E4, E4, kScaleHw, 1>(p, tile, st);
+  return pow2_out ? dispatch_variant<FP, E4, E4, kScaleFold, 2>(p, tile, st)
+                  : dispatch_variant<FP, E4, E4, kScaleFold, 1>(p, tile, st);
+}
+
+}  // namespace
+
+extern "C" int fp8_gemm_blockscaled_qout(int64_t M, int64_t N, int64_t K, const void* A,
+                                         int64_t lda, int ga, const float* scale_inv_a,
+                                         const void* B, int64_t ldb, int gb,
+                                         const float* scale_inv_b, int pow2_inputs,
+                                         void* C_bf16, int64_t ldc, int mode_out, void* Cq,
+                                         int64_t ldcq, float* cq_scale_inv, void* stream) {
+  return gemm_qout(FP8BS_TILE_AUTO, M, N, K, A, lda, ga, scale_inv_a, B, ldb, gb, scale_inv_b,
+                   pow2_inputs, C_bf16, ldc, mode_out, Cq, ldcq, cq_scale_inv,
+                   static_cast<hipStream_t>(stream));
+}
+
+extern "C" int fp8_gemm_blockscaled_qout_tiled(int tile, int64_t M, int64_t N, int64_t K,
+                                               const void* A, int64_t lda, int ga,
+                                               const float* scale_inv_a, const void* B,
+                                               int64_t ldb, int gb, const float* scale_inv_b,
+                                               int pow2_inputs, void* C_bf16, int64_t ldc,
+                                               int mode_out, void* Cq, int64_t ldcq,
+                                               float* cq_scale_inv, void* stream) {
+  return gemm_qout(tile, M, N, K, A, lda, ga, scale_inv_a, B, ldb, gb, scale_inv_b, pow2_inputs,
+                   C_bf16, ldc, mode_out, Cq, ldcq, cq_scale_inv, static_cast<hipStream_t>(stream));
 }

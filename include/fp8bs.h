@@ -64,6 +64,17 @@ typedef enum {
   FP8BS_WGRAD = 2  /* C[M,N] = A[K,M]^T . B[K,N]   (A = dY, B = X, K = tokens; C = dW)    */
 } fp8bs_layout;
 
+/* Output-tile configuration of the GEMM kernels (the *_tiled entry points).  FP8BS_TILE_AUTO
+ * is the library's choice from the problem shape, which the untiled entry points always make;
+ * the others force one configuration (for tuning and for testing every configuration). */
+typedef enum {
+  FP8BS_TILE_AUTO = 0,
+  FP8BS_TILE_256x128_W4 = 1, /* 256 x 128 output tile, 4 waves, 3 LDS stages */
+  FP8BS_TILE_256x128_W8 = 2, /* 256 x 128, 8 waves, 3 stages */
+  FP8BS_TILE_256x256_W8 = 3, /* 256 x 256, 8 waves, 2 stages */
+  FP8BS_TILE_128x128_W4 = 4  /* 128 x 128, 4 waves, 3 stages */
+} fp8bs_tile;
+
 enum {
   FP8BS_OK = 0,
   FP8BS_ERR_NULL = -1,        /* a required pointer is NULL */
@@ -191,9 +202,12 @@ int fp8_gemm_blockscaled(int layout, int64_t M, int64_t N, int64_t K,
  * by expert g's weight: C[r, :] = A[r, :] . B[g]^T for those rows.
  *   num_groups:    0 .. 1024 (FP8BS_ERR_ARG beyond).
  *   group_offsets: DEVICE int64[num_groups + 1], non-decreasing, offsets[0] = 0,
- *                  offsets[num_groups] = total_M (empty groups allowed).  Offsets that break
- *                  these rules make the kernel skip the offending rows; they never cause an
- *                  out-of-range access.
+ *                  offsets[num_groups] = total_M (empty groups allowed).  Other offsets are
+ *                  read as e[g] = min(max(offsets[0..g], 0), total_M): each is clamped to
+ *                  [0, total_M] and raised to the largest offset before it, and group g covers
+ *                  rows [e[g], e[g+1]).  So groups never overlap, a decreasing offset leaves
+ *                  the groups it would reopen empty, rows outside [e[0], e[num_groups]) are
+ *                  not written, and no access goes out of range.
  *   A:  [total_M, K] codes (format fa), pitch lda; scale_inv_a: 1x128 blocks,
  *       float[ceil(K/128)][total_M].
  *   B:  [num_groups][N][K] codes (format fb), rows of pitch ldb, groups of stride N * ldb;
@@ -251,6 +265,30 @@ int fp8_grouped_gemm_pow2(int32_t num_groups, const int64_t* group_offsets, int6
                           int64_t N, int64_t K, const void* A, int64_t lda, int fa,
                           const float* scale_inv_a, const void* B, int64_t ldb, int fb,
                           const float* scale_inv_b, void* C_bf16, int64_t ldc, void* stream);
+
+/* The GEMM entry points with an explicit output-tile configuration `tile` (fp8bs_tile), for
+ * tuning and for tests that cover every configuration; the results equal those of the
+ * corresponding entry point up to fp32 summation order.  Same arguments and errors otherwise;
+ * FP8BS_ERR_ARG also for a tile value out of range.
+ *   fp8_gemm_blockscaled_tiled:      pow2 = 0 -> fp8_gemm_blockscaled, 1 -> ..._pow2.
+ *   fp8_grouped_gemm_tiled:          pow2 = 0 -> fp8_grouped_gemm, 1 -> ..._pow2; tile must
+ *                                    be AUTO, 256x128_W8, 256x256_W8 or 128x128_W4.
+ *   fp8_gemm_blockscaled_qout_tiled: fp8_gemm_blockscaled_qout. */
+int fp8_gemm_blockscaled_tiled(int tile, int pow2, int layout, int64_t M, int64_t N, int64_t K,
+                               const void* A, int64_t lda, int fa, int ga,
+                               const float* scale_inv_a, const void* B, int64_t ldb, int fb,
+                               int gb, const float* scale_inv_b, void* C_bf16, int64_t ldc,
+                               void* stream);
+int fp8_grouped_gemm_tiled(int tile, int pow2, int32_t num_groups, const int64_t* group_offsets,
+                           int64_t total_M, int64_t N, int64_t K, const void* A, int64_t lda,
+                           int fa, const float* scale_inv_a, const void* B, int64_t ldb, int fb,
+                           const float* scale_inv_b, void* C_bf16, int64_t ldc, void* stream);
+int fp8_gemm_blockscaled_qout_tiled(int tile, int64_t M, int64_t N, int64_t K, const void* A,
+                                    int64_t lda, int ga, const float* scale_inv_a,
+                                    const void* B, int64_t ldb, int gb,
+                                    const float* scale_inv_b, int pow2_inputs, void* C_bf16,
+                                    int64_t ldc, int mode_out, void* Cq, int64_t ldcq,
+                                    float* cq_scale_inv, void* stream);
 
 /* FP8 KV cache: write one token per sequence.  [P3] "Ganancias de rendimiento en el mundo real"
  * (FP8 extended to the KV cache); the cache format is the activation recipe of "El avance

@@ -177,6 +177,55 @@ def test_gemm_qout_validation():
     assert qout(M=0) == bsq.OK and qout(N=0, C=None) == bsq.OK
 
 
+def test_tiled_entry_validation():
+    """The entry points with an explicit tile configuration reject tile and pow2 values out of
+    range, and otherwise validate exactly as the plain entry points do."""
+    lib = bsq.load()
+    g = dict(layout=0, M=256, N=256, K=256, A=FAKE, lda=256, fa=0, ga=0, sa=FAKE, B=FAKE,
+             ldb=256, fb=0, gb=1, sb=FAKE, C=FAKE, ldc=256)
+
+    def tiled(tile, pow2, **kw):
+        a = dict(g, **kw)
+        return lib.fp8_gemm_blockscaled_tiled(tile, pow2, *a.values(), None)
+
+    for tile in (-1, 5, 99):
+        assert tiled(tile, 0) == bsq.ERR_ARG
+    assert tiled(bsq.TILE_256x256_W8, 2) == bsq.ERR_ARG
+    for tile in range(5):
+        for p2 in (0, 1):
+            assert tiled(tile, p2, layout=3) == bsq.ERR_ARG
+            assert tiled(tile, p2, M=-1) == bsq.ERR_SHAPE
+            assert tiled(tile, p2, A=None) == bsq.ERR_NULL
+            assert tiled(tile, p2, layout=2, ga=0) == bsq.ERR_UNSUPPORTED
+            assert tiled(tile, p2, M=0) == bsq.OK
+    gr = dict(G=4, off=FAKE, M=512, N=256, K=256, A=FAKE, lda=256, fa=0, sa=FAKE, B=FAKE,
+              ldb=256, fb=0, sb=FAKE, C=FAKE, ldc=256)
+
+    def gtiled(tile, pow2, **kw):
+        a = dict(gr, **kw)
+        return lib.fp8_grouped_gemm_tiled(tile, pow2, *a.values(), None)
+
+    for tile in (-1, bsq.TILE_256x128_W4, 5):               # 256x128 with 4 waves: dense only
+        assert gtiled(tile, 0) == bsq.ERR_ARG
+    assert gtiled(bsq.TILE_AUTO, 3) == bsq.ERR_ARG
+    for tile in (bsq.TILE_AUTO, bsq.TILE_256x128_W8, bsq.TILE_256x256_W8, bsq.TILE_128x128_W4):
+        assert gtiled(tile, 1, K=0) == bsq.ERR_SHAPE
+        assert gtiled(tile, 0, off=None) == bsq.ERR_NULL
+        assert gtiled(tile, 0, G=0) == bsq.OK
+    q = dict(M=256, N=256, K=256, A=FAKE, lda=256, ga=0, sa=FAKE, B=FAKE, ldb=256, gb=1, sb=FAKE,
+             p2=0, C=FAKE, ldc=256, mode=0, Cq=FAKE, ldcq=256, cqs=FAKE)
+
+    def qtiled(tile, **kw):
+        a = dict(q, **kw)
+        return lib.fp8_gemm_blockscaled_qout_tiled(tile, *a.values(), None)
+
+    assert qtiled(7) == bsq.ERR_ARG and qtiled(-2) == bsq.ERR_ARG
+    for tile in range(5):
+        assert qtiled(tile, Cq=None) == bsq.ERR_NULL
+        assert qtiled(tile, gb=0) == bsq.ERR_UNSUPPORTED
+        assert qtiled(tile, M=0) == bsq.OK
+
+
 def test_cast_validation():
     lib = bsq.load()
     assert lib.fp8_cast_fp32(FAKE, 16, 3, FAKE, None) == bsq.ERR_ARG

@@ -50,8 +50,12 @@ def device_scales(s: np.ndarray, gran) -> torch.Tensor:
     return logical_to_gpu_scales(s, gran)
 
 
+TILES = {"A": bsq.TILE_256x128_W4, "B": bsq.TILE_256x128_W8, "C": bsq.TILE_256x256_W8,
+         "D": bsq.TILE_128x128_W4}
+
+
 def run_gemm(gpu, layout, M, N, K, fa, ga, fb, gb, seed=0, pad=0, rows=None, c_guard=True,
-             pow2=False):
+             pow2=False, tile=0):
     """pow2: power-of-2 scales (SCALE_POW2 quantization) through fp8_gemm_blockscaled_pow2."""
     mode = oracle.SCALE_POW2 if pow2 else oracle.SCALE_FP32
     ashape = (M, K) if layout != WG else (K, M)
@@ -68,7 +72,7 @@ def run_gemm(gpu, layout, M, N, K, fa, ga, fb, gb, seed=0, pad=0, rows=None, c_g
     cstore = torch.full((M + 1, ldc), -7.0, dtype=torch.bfloat16, device="cuda")
     c = cstore[:M, :N]
     gpu.gemm_blockscaled(layout, ad, fa, ga, device_scales(sa, ga), bd, fb, gb,
-                         device_scales(sb, gb), c=c, pow2=pow2)
+                         device_scales(sb, gb), c=c, pow2=pow2, tile=tile)
     torch.cuda.synchronize()
     if c_guard:
         assert torch.all(cstore[:M, N:] == -7.0) and torch.all(cstore[M] == -7.0), "guard overwritten"
@@ -176,7 +180,7 @@ def test_deterministic(gpu):
 
 # ----------------------------------------------------------------------------- grouped
 
-def run_grouped(gpu, counts, N, K, seed=0, sample_rows=None, pow2=False):
+def run_grouped(gpu, counts, N, K, seed=0, sample_rows=None, pow2=False, tile=0):
     mode = oracle.SCALE_POW2 if pow2 else oracle.SCALE_FP32
     counts = np.asarray(counts, dtype=np.int64)
     G = len(counts)
@@ -193,7 +197,7 @@ def run_grouped(gpu, counts, N, K, seed=0, sample_rows=None, pow2=False):
     qbs, sbs = np.stack(qbs), np.stack(sbs)
     c = gpu.grouped_gemm(torch.from_numpy(off).cuda(), torch.from_numpy(qa).cuda(),
                          logical_to_gpu_scales(sa, B1), torch.from_numpy(qbs).cuda(),
-                         torch.from_numpy(sbs).cuda(), pow2=pow2)
+                         torch.from_numpy(sbs).cuda(), pow2=pow2, tile=tile)
     torch.cuda.synchronize()
     if sample_rows is None:
         ref = oracle.grouped_gemm(off, qa, sa, E4, qbs, sbs, E4)
@@ -232,14 +236,80 @@ def test_grouped_moe_config_sampled(gpu):
     run_grouped(gpu, counts, 1536, 2048, sample_rows=rows)
 
 
+@pytest.mark.parametrize("raw", [[40, 100, 50, 300, 250, 480, -5, 470],
+                                 [0, 100, 50, 300, 900, 250, -5, 470]])
+@pytest.mark.parametrize("pow2", [False, True])
+def test_grouped_offsets_out_of_order(gpu, raw, pow2):
+    """Offsets that decrease or leave [0, total_M] are read as e[g] = min(max(offsets[0..g], 0),
+    total_M): groups never overlap, rows outside [e[0], e[G]) keep their contents, and the
+    result is the same on every run (no two workgroups write one row)."""
+    M, N, K = 600, 256, 256
+    mode = oracle.SCALE_POW2 if pow2 else oracle.SCALE_FP32
+    raw = np.asarray(raw, dtype=np.int64)
+    G = len(raw) - 1
+    eff = np.minimum(np.maximum.accumulate(np.maximum(raw, 0)), M)
+    qa, sa = quantize_operand(synth.normal((M, K), 1.0, 0, "grouped-ooo/A"), E4, B1, mode)
+    qbs, sbs = zip(*[quantize_operand(synth.normal((N, K), 0.02, 0, f"grouped-ooo/W{g}"), E4,
+                                      B128, mode) for g in range(G)])
+    qbs, sbs = np.stack(qbs), np.stack(sbs)
+    outs = []
+    for _ in range(2):
+        c = torch.full((M, N), -7.0, dtype=torch.bfloat16, device="cuda")
+        gpu.grouped_gemm(torch.from_numpy(raw).cuda(), torch.from_numpy(qa).cuda(),
+                         logical_to_gpu_scales(sa, B1), torch.from_numpy(qbs).cuda(),
+                         torch.from_numpy(sbs).cuda(), c=c, pow2=pow2)
+        torch.cuda.synchronize()
+        outs.append(c)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), "not deterministic"
+    c = outs[0]
+    lo, hi = int(eff[0]), int(eff[-1])
+    assert torch.all(c[:lo] == -7.0) and torch.all(c[hi:] == -7.0), "rows outside the groups written"
+    ref = oracle.grouped_gemm(eff, qa, sa, E4, qbs, sbs, E4)
+    ad = oracle.dequantize(qa, E4, B1, sa)
+    mag = np.zeros_like(ref)
+    for g in range(G):
+        r0, r1 = int(eff[g]), int(eff[g + 1])
+        if r1 > r0:
+            mag[r0:r1] = np.abs(ad[r0:r1]) @ np.abs(oracle.dequantize(qbs[g], E4, B128, sbs[g])).T
+    gemm_check(c[lo:hi], ref[lo:hi], mag[lo:hi], "grouped, offsets out of order")
+
+
+def test_wrapper_rejects_bad_tensors(gpu):
+    """The Python binding checks shapes, dtypes and strides before calling the library."""
+    a = torch.zeros((256, 256), dtype=torch.uint8, device="cuda")
+    w = torch.zeros((4, 256, 256), dtype=torch.uint8, device="cuda")
+    sa = torch.ones((2, 256), device="cuda")
+    sw = torch.ones((4, 2, 2), device="cuda")
+    off = torch.tensor([0, 64, 128, 192, 256], dtype=torch.int64, device="cuda")
+    with pytest.raises(ValueError):      # experts not N rows apart (a sliced [G, N, K] view)
+        gpu.grouped_gemm(off, a, sa, w[:, :128], sw[:, :1])
+    with pytest.raises(ValueError):      # offsets need G + 1 entries
+        gpu.grouped_gemm(off[:4], a, sa, w, sw)
+    with pytest.raises(ValueError):      # K mismatch between a and the experts
+        gpu.grouped_gemm(off, a[:, :128], sa, w, sw)
+    with pytest.raises(ValueError):      # weight scales of the wrong shape
+        gpu.grouped_gemm(off, a, sa, w, sw[:, :, :1])
+    with pytest.raises(ValueError):      # activation scales of the wrong dtype
+        gpu.grouped_gemm(off, a, sa.double(), w, sw)
+    with pytest.raises(ValueError):      # output of the wrong shape
+        gpu.grouped_gemm(off, a, sa, w, sw, c=torch.empty((255, 256), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):      # dense: 1x128 scales of the wrong shape
+        gpu.gemm_blockscaled(FP, a, E4, B1, sa[:1], a, E4, B128, torch.ones((2, 2), device="cuda"))
+    with pytest.raises(ValueError):      # dense: output too small
+        gpu.gemm_blockscaled(FP, a, E4, B1, sa, a, E4, B128, torch.ones((2, 2), device="cuda"),
+                             c=torch.empty((256, 128), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):      # fused quantization: code output of the wrong shape
+        gpu.gemm_blockscaled_qout(a, B1, sa, a, B128, torch.ones((2, 2), device="cuda"),
+                                  cq=torch.empty((256, 255), dtype=torch.uint8, device="cuda"))
+
+
 @pytest.mark.parametrize("variant", ["A", "B", "C", "D"])
 @pytest.mark.parametrize("layout,fa,ga,fb,gb", [(FP, E4, B1, E4, B128), (DG, E5, B1, E4, B128),
                                                  (WG, E5, PT, E4, B128)])
-def test_every_tile_variant(gpu, monkeypatch, variant, layout, fa, ga, fb, gb):
-    """Each tile configuration the library can pick (FP8BS_GEMM_VARIANT forces one)."""
-    monkeypatch.setenv("FP8BS_GEMM_VARIANT", variant)
-    run_gemm(gpu, layout, 520, 390, 392, fa, ga, fb, gb)
-    run_gemm(gpu, layout, 256, 256, 256, fa, ga, fb, gb)
+def test_every_tile_variant(gpu, variant, layout, fa, ga, fb, gb):
+    """Each tile configuration the library can pick (forced through fp8_gemm_blockscaled_tiled)."""
+    run_gemm(gpu, layout, 520, 390, 392, fa, ga, fb, gb, tile=TILES[variant])
+    run_gemm(gpu, layout, 256, 256, 256, fa, ga, fb, gb, tile=TILES[variant])
 
 
 @pytest.mark.parametrize("K,N", [(128, 256), (256, 384), (208, 256), (640, 512)])
@@ -253,10 +323,9 @@ def test_grouped_persistent_tiles(gpu, K, N, pow2):
 
 
 @pytest.mark.parametrize("variant", ["B", "C", "D"])
-def test_grouped_every_tile_variant(gpu, monkeypatch, variant):
-    """Each tile configuration the grouped kernel can use (FP8BS_GROUPED_VARIANT forces one)."""
-    monkeypatch.setenv("FP8BS_GROUPED_VARIANT", variant)
-    run_grouped(gpu, [5, 0, 300, 1, 0, 257, 128, 513], 384, 400)
+def test_grouped_every_tile_variant(gpu, variant):
+    """Each tile configuration the grouped kernel can use (forced through fp8_grouped_gemm_tiled)."""
+    run_grouped(gpu, [5, 0, 300, 1, 0, 257, 128, 513], 384, 400, tile=TILES[variant])
 
 
 # ----------------------------------------------------------------------------- power-of-2 scales
@@ -286,9 +355,8 @@ def test_pow2_padded_pitches_with_nan_padding(gpu):
 @pytest.mark.parametrize("variant", ["A", "B", "C", "D"])
 @pytest.mark.parametrize("layout,fa,ga,fb,gb", [(FP, E4, B1, E4, B128), (DG, E5, B1, E4, B128),
                                                  (WG, E5, PT, E4, B128)])
-def test_pow2_every_tile_variant(gpu, monkeypatch, variant, layout, fa, ga, fb, gb):
-    monkeypatch.setenv("FP8BS_GEMM_VARIANT", variant)
-    run_gemm(gpu, layout, 520, 390, 392, fa, ga, fb, gb, pow2=True)
+def test_pow2_every_tile_variant(gpu, variant, layout, fa, ga, fb, gb):
+    run_gemm(gpu, layout, 520, 390, 392, fa, ga, fb, gb, pow2=True, tile=TILES[variant])
 
 
 def test_pow2_llama8b_fprop_full_size_sampled_rows(gpu):
@@ -354,9 +422,8 @@ def test_pow2_grouped_moe_config_sampled(gpu):
 
 
 @pytest.mark.parametrize("variant", ["B", "C", "D"])
-def test_pow2_grouped_every_tile_variant(gpu, monkeypatch, variant):
-    monkeypatch.setenv("FP8BS_GROUPED_VARIANT", variant)
-    run_grouped(gpu, [5, 0, 300, 1, 0, 257, 128, 513], 384, 400, pow2=True)
+def test_pow2_grouped_every_tile_variant(gpu, variant):
+    run_grouped(gpu, [5, 0, 300, 1, 0, 257, 128, 513], 384, 400, pow2=True, tile=TILES[variant])
 
 
 # ----------------------------------------------------------------------------- 1x128 x 1x128
@@ -372,10 +439,9 @@ def test_fprop_1x128_both_operands(gpu, M, N, K, pow2):
 
 @pytest.mark.parametrize("variant", ["A", "B", "C", "D"])
 @pytest.mark.parametrize("pow2", [False, True])
-def test_1x128_both_every_tile_variant(gpu, monkeypatch, variant, pow2):
-    monkeypatch.setenv("FP8BS_GEMM_VARIANT", variant)
-    run_gemm(gpu, FP, 520, 390, 392, E4, B1, E4, B1, pow2=pow2)
-    run_gemm(gpu, FP, 256, 256, 256, E5, B1, E5, B1, pow2=pow2)
+def test_1x128_both_every_tile_variant(gpu, variant, pow2):
+    run_gemm(gpu, FP, 520, 390, 392, E4, B1, E4, B1, pow2=pow2, tile=TILES[variant])
+    run_gemm(gpu, FP, 256, 256, 256, E5, B1, E5, B1, pow2=pow2, tile=TILES[variant])
 
 
 def wgrad_blockwise(gpu, tokens, n_out, k_in, fdy, pow2, rows=None, seed=0):

@@ -43,7 +43,7 @@ def device_codes(q: np.ndarray) -> torch.Tensor:
 
 
 def run_qout(gpu, M, N, K, ga, gb, pow2_in, mode_out, want_bf16=True, nan_row=None, seed=0,
-             check_oracle_gemm=True):
+             check_oracle_gemm=True, tile=0):
     mode_in = POW2 if pow2_in else FP32
     a = synth.activations_with_outliers(M, K, seed, "qout/A")
     b = synth.normal((N, K), 0.02, seed, "qout/B")
@@ -52,8 +52,9 @@ def run_qout(gpu, M, N, K, ga, gb, pow2_in, mode_out, want_bf16=True, nan_row=No
     if nan_row is not None:
         qa[nan_row, 3] = 0x7F                 # a NaN code: that output row becomes NaN
     ad, bd = device_codes(qa), device_codes(qb)
-    c, cq, cqs = gpu.gemm_blockscaled_qout(ad, ga, sad, bd, gb, sbd, mode_out, pow2_in, want_bf16)
-    c_plain = gpu.gemm_blockscaled(FP, ad, E4, ga, sad, bd, E4, gb, sbd, pow2=pow2_in)
+    c, cq, cqs = gpu.gemm_blockscaled_qout(ad, ga, sad, bd, gb, sbd, mode_out, pow2_in, want_bf16,
+                                           tile=tile)
+    c_plain = gpu.gemm_blockscaled(FP, ad, E4, ga, sad, bd, E4, gb, sbd, pow2=pow2_in, tile=tile)
     torch.cuda.synchronize()
     if want_bf16:
         assert torch.equal(c.view(torch.int16), c_plain.view(torch.int16)), "bf16 output differs"
@@ -104,10 +105,11 @@ def test_k_zero(gpu):
 
 
 @pytest.mark.parametrize("variant", ["A", "B", "C", "D"])
-def test_every_tile_variant(gpu, monkeypatch, variant):
-    monkeypatch.setenv("FP8BS_GEMM_VARIANT", variant)
-    run_qout(gpu, 520, 390, 392, B1, B128, False, FP32)
-    run_qout(gpu, 256, 256, 256, B1, B128, True, POW2)
+def test_every_tile_variant(gpu, variant):
+    tile = {"A": bsq.TILE_256x128_W4, "B": bsq.TILE_256x128_W8, "C": bsq.TILE_256x256_W8,
+            "D": bsq.TILE_128x128_W4}[variant]
+    run_qout(gpu, 520, 390, 392, B1, B128, False, FP32, tile=tile)
+    run_qout(gpu, 256, 256, 256, B1, B128, True, POW2, tile=tile)
 
 
 def test_llama8b_qkv_full_size(gpu):
