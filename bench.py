@@ -59,7 +59,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b-fprop",
                     choices=["llama8b-fprop", "llama8b-fprop-pow2", "quant-sweep", "moe", "backward",
-                             "backward-blockwise", "llama8b-fprop-qout", "kv-decode", "copy"])
+                             "backward-blockwise", "llama8b-fprop-qout", "kv-decode", "copy", "stream"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pow2", action="store_true",
                     help="moe, backward-blockwise: power-of-2 scales (E8M0 in the MFMA)")
@@ -355,6 +355,84 @@ def bench_quant_sweep(args):
     return res
 
 
+# ----------------------------------------------------------------------------- streaming ceiling
+
+STREAM_VARIANTS = {0: "one-shot, 16 el/lane", 1: "one-shot, 2x16 el/lane", 2: "one-shot, 4x16 el/lane",
+                   3: "2048 workgroups striding", 4: "4096 workgroups striding"}
+
+
+def bench_stream(args):
+    """The rate this GPU streams the quantizers' traffic at: plain kernels that read 2 bytes and
+    write 1 byte per element (libfp8bs_bench.so, five grid shapes), next to the 1x128 quantizer
+    on the same buffers (bf16 [rows, 4096] of 16M / 128M / 512M elements, rotating over more
+    than 512 MiB so that the last-level cache does not serve the inputs).  value = the best
+    streaming rate on the 512M-element tensor; quantizer_vs_stream = the quantizer's rate over
+    that ceiling."""
+    import ctypes
+    import block_scaled_quantize_amd as bsq
+    import synth
+    bsq.load()
+    blib = ctypes.CDLL(os.path.join(ROOT, "block_scaled_quantize_amd", "libfp8bs_bench.so"))
+    blib.fp8bs_bench_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                        ctypes.c_int, ctypes.c_void_p]
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream().cuda_stream
+    cases = {}
+    iters = max(args.steps, 10)
+
+    def timed(run):
+        for i in range(args.warmup):
+            run(i)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(iters)]
+        for i in range(iters):
+            ev[i][0].record()
+            run(i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+    for rows in (4096, 32768, 131072):
+        cols = 4096
+        n = rows * cols
+        nbuf = max(1, -(-(600 << 20) // (3 * n)))
+        base = synth.student_t((rows, cols), 3.0, 0, f"bench/sweep/{rows}x{cols}").to(dev)
+        xs = [base] + [base.roll(i, 0) for i in range(1, nbuf)]
+        ys = [torch.empty((rows, cols), dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+        ss = [torch.empty(bsq.scale_shape(rows, cols, bsq.BLOCK_1x128), dtype=torch.float32,
+                          device=dev) for _ in range(nbuf)]
+        entry = {}
+        for v, what in STREAM_VARIANTS.items():
+            def run(i, v=v):
+                rc = blib.fp8bs_bench_stream(xs[i % nbuf].data_ptr(), n, ys[i % nbuf].data_ptr(), v,
+                                             stream)
+                assert rc == 0
+            ms = timed(run)
+            entry[what] = round(3.0 * n / ms / 1e6, 1)
+        qbytes = 3.0 * n + 4.0 * n / 128
+        qms = timed(lambda i: bsq.quantize_blockwise(xs[i % nbuf], bsq.E4M3, bsq.BLOCK_1x128,
+                                                     q=ys[i % nbuf], scale_inv=ss[i % nbuf]))
+        best = max(entry.values())
+        cases[f"{rows}x{cols}"] = dict(stream_gbps=entry, best_stream_gbps=best,
+                                       quant_1x128_gbps=round(qbytes / qms / 1e6, 1),
+                                       quant_vs_stream=round(qbytes / qms / 1e6 / best, 4))
+        log(f"stream {rows}x{cols}: {entry}; quantizer {qbytes / qms / 1e6:.0f} GB/s")
+        del xs, ys, ss, base
+        torch.cuda.empty_cache()
+    head = cases["131072x4096"]
+    return dict(metric="streaming GB/s at the quantizers' traffic (2 B read + 1 B written per "
+                       "element), % of MI355X HBM peak",
+                value=head["best_stream_gbps"], unit="GB/s", n_gpus=1, steps=iters,
+                warmup=args.warmup, ms_per_step=None, higher_is_better=True, scaling="weak",
+                vs_baseline=None, dtype="bf16 -> u8", data="synthetic",
+                config=dict(workload="stream-ceiling", headline="131072x4096 (512M elements)"),
+                roofline=dict(bound="hbm", achieved=head["best_stream_gbps"], peak=HBM_PEAK_GBPS,
+                              unit="GB/s", frac=round(head["best_stream_gbps"] / HBM_PEAK_GBPS, 4),
+                              traffic=None, kernel="stream kernels (libfp8bs_bench.so)"),
+                quantizer_vs_stream=head["quant_vs_stream"], cases=cases)
+
+
 # ----------------------------------------------------------------------------- MoE grouped
 
 def bench_moe(args):
@@ -449,9 +527,9 @@ def bench_backward(args):
             return fn() if t is None else t.time(key, fn)
         for L in layers:
             n = L["name"]
-            qx, six = bsq.quantize_delayed(L["x"], bsq.E4M3, L["sx"])
-            qw, siw = bsq.quantize_delayed(L["w"], bsq.E4M3, L["sw"])
-            qdy, sidy = bsq.quantize_delayed(L["dy"], bsq.E5M2, L["sdy"])
+            qx, six = run(n + "/qx", lambda: bsq.quantize_delayed(L["x"], bsq.E4M3, L["sx"]))
+            qw, siw = run(n + "/qw", lambda: bsq.quantize_delayed(L["w"], bsq.E4M3, L["sw"]))
+            qdy, sidy = run(n + "/qdy", lambda: bsq.quantize_delayed(L["dy"], bsq.E5M2, L["sdy"]))
             run(n + "/dgrad", lambda: bsq.gemm_blockscaled(
                 bsq.DGRAD, qdy, bsq.E5M2, bsq.PER_TENSOR, sidy, qw, bsq.E4M3, bsq.PER_TENSOR,
                 siw, c=L["dx"]))
@@ -466,18 +544,28 @@ def bench_backward(args):
         step()
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / args.steps
-    # the GEMM launches with HIP events on their stream (per-tensor scales on both operands)
+    # every launch with HIP events on its stream: the GEMMs (per-tensor scales on both operands)
+    # and the delayed quantizer (cast + finalize of one tensor per event pair)
     timer = EventTimer()
     for _ in range(max(3, min(args.steps, 10))):
         step(timer)
     torch.cuda.synchronize()
-    per_layer, gemm_ms = {}, 0.0
+    per_layer, gemm_ms, q_ms, q_bytes = {}, 0.0, 0.0, 0.0
     for L in layers:
         n, f1 = L["name"], 2.0 * M * L["N"] * L["K"]
         dg, wg = timer.mean_ms(n + "/dgrad"), timer.mean_ms(n + "/wgrad")
         gemm_ms += dg + wg
+        quant = {}
+        for key, numel in (("qx", M * L["K"]), ("qw", L["N"] * L["K"]), ("qdy", M * L["N"])):
+            ms = timer.mean_ms(n + "/" + key)
+            nbytes = 3.0 * numel          # 2 B read + 1 B written per element (state: 68 B)
+            q_ms += ms
+            q_bytes += nbytes
+            quant[key + "_us"] = round(ms * 1e3, 2)
+            quant[key + "_gbps"] = round(nbytes / ms / 1e6, 1)
         per_layer[n] = dict(dgrad_us=round(dg * 1e3, 2), dgrad_tflops=round(f1 / dg / 1e9, 1),
-                            wgrad_us=round(wg * 1e3, 2), wgrad_tflops=round(f1 / wg / 1e9, 1))
+                            wgrad_us=round(wg * 1e3, 2), wgrad_tflops=round(f1 / wg / 1e9, 1),
+                            **quant)
     achieved = flops / gemm_ms / 1e9
     return dict(metric="block-scaled FP8 GEMM TFLOP/s, backward (dgrad + wgrad, delayed scaling)",
                 value=round(flops / dt / 1e12, 2), unit="TFLOP/s", n_gpus=1, steps=args.steps,
@@ -491,6 +579,12 @@ def bench_backward(args):
                               traffic=None,
                               kernel="gemm_kernel<Cfg<256,256,2,4>,DGRAD|WGRAD,E5M2,E4M3,tensor>",
                               mean_launch_us=round(gemm_ms / (2 * len(layers)) * 1e3, 2)),
+                delayed_quant=dict(bound="hbm", achieved_gbps=round(q_bytes / q_ms / 1e6, 1),
+                                   peak_gbps=HBM_PEAK_GBPS,
+                                   frac=round(q_bytes / q_ms / 1e6 / HBM_PEAK_GBPS, 4),
+                                   us_per_step=round(q_ms * 1e3, 1),
+                                   what="delayed_cast_kernel + delayed_finalize_kernel per tensor "
+                                        "(X, W E4M3; dY E5M2), 3 B per element"),
                 layers=per_layer)
 
 
@@ -818,6 +912,8 @@ def main():
         res = bench_fprop_qout(args)
     elif args.workload == "kv-decode":
         res = bench_kv_decode(args)
+    elif args.workload == "stream":
+        res = bench_stream(args)
     elif args.workload == "copy":
         res = bench_copy(args)
     else:

@@ -17,6 +17,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfp8bs.so")
+# streaming kernels the benchmark measures the device's streaming rate with (not the C ABI)
+BENCH_LIB = os.path.join(HERE, "libfp8bs_bench.so")
+BENCH_SOURCES = ["bench_stream.hip"]
 SOURCES = ["quantize.hip", "quantize_t.hip", "gemm.hip", "gemm_pow2.hip", "gemm_qout.hip",
            "attention.hip"]
 HEADERS = [os.path.join(CSRC, "common.h"), os.path.join(CSRC, "gemm_impl.h"),
@@ -58,18 +61,23 @@ def build(force: bool = False, jobs: int | None = None) -> str:
     if not os.path.exists(HIPCC) and shutil.which("hipcc") is None:
         raise RuntimeError("hipcc not found")
     os.makedirs(BUILD, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
+    jobs = jobs or min(len(SOURCES) + len(BENCH_SOURCES), os.cpu_count() or 1)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, force), SOURCES))
-    if force or not _newer(LIB, objs):
-        tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda s: _compile(s, force), SOURCES + BENCH_SOURCES))
+    _link(LIB, objs[:len(SOURCES)], force)
+    _link(BENCH_LIB, objs[len(SOURCES):], force)
+    return LIB
+
+
+def _link(lib: str, objs, force: bool) -> None:
+    if force or not _newer(lib, objs):
+        tmp = lib + ".tmp%d" % os.getpid()
         cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             sys.stderr.write(r.stdout + r.stderr)
             raise RuntimeError("link failed")
-        os.replace(tmp, LIB)
-    return LIB
+        os.replace(tmp, lib)
 
 
 if __name__ == "__main__":
