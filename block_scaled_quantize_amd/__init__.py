@@ -64,6 +64,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.fp8_quantize_blockwise.argtypes = [vp, i64, i64, i64, i32, i32, i32, vp, i64, vp, vp]
     lib.fp8_quantize_columnwise_t.argtypes = [vp, i64, i64, i64, i32, i32, vp, i64, vp, vp]
     lib.fp8_quantize_delayed.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.fp8_quantize_delayed_noalloc.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp]
     lib.fp8_quantize_delayed_workspace_size.argtypes = []
     lib.fp8_quantize_delayed_workspace_size.restype = sz
     lib.fp8_cast_fp32.argtypes = [vp, i64, i32, vp, vp]
@@ -86,6 +87,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.fp8_attention_decode_workspace_size.argtypes = [i64, i64, i64, i64, i64]
     lib.fp8_attention_decode_workspace_size.restype = sz
     for name in ("fp8_quantize_blockwise", "fp8_quantize_columnwise_t", "fp8_quantize_delayed",
+                 "fp8_quantize_delayed_noalloc",
                  "fp8_cast_fp32",
                  "fp8_gemm_blockscaled", "fp8_grouped_gemm", "fp8_gemm_blockscaled_pow2",
                  "fp8_gemm_blockscaled_qout",
@@ -220,8 +222,11 @@ class DelayedState:
 
 def quantize_delayed(x: torch.Tensor, fmt: int, state: DelayedState, mode: int = SCALE_FP32,
                      margin: int = 0, q: torch.Tensor | None = None,
-                     scale_inv_used: torch.Tensor | None = None, stream=None):
+                     scale_inv_used: torch.Tensor | None = None, stream=None,
+                     noalloc: bool = False):
     """One delayed-scaling step on a contiguous bf16 tensor; advances ``state`` on the device.
+    noalloc=True calls fp8_quantize_delayed_noalloc (the library's own scratch array instead of
+    state.workspace; q and scale_inv_used must then be given, since creating them allocates).
 
     Returns (codes uint8 with x's shape, scale_inv_used float32[1])."""
     if x.dtype != torch.bfloat16 or not x.is_contiguous():
@@ -230,6 +235,15 @@ def quantize_delayed(x: torch.Tensor, fmt: int, state: DelayedState, mode: int =
         q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     if scale_inv_used is None:
         scale_inv_used = torch.empty(1, dtype=torch.float32, device=x.device)
+    _need(q, x.shape, torch.uint8, "q")
+    _need(scale_inv_used, (1,), torch.float32, "scale_inv_used")
+    if noalloc:
+        _check(load().fp8_quantize_delayed_noalloc(_ptr(x), x.numel(), fmt, mode, margin,
+                                                   state.hist_len, _ptr(state.history),
+                                                   _ptr(state.scale), _ptr(q),
+                                                   _ptr(scale_inv_used), _stream(stream)),
+               "fp8_quantize_delayed_noalloc")
+        return q, scale_inv_used
     _check(load().fp8_quantize_delayed(_ptr(x), x.numel(), fmt, mode, margin, state.hist_len,
                                        _ptr(state.history), _ptr(state.scale), _ptr(q),
                                        _ptr(scale_inv_used), _ptr(state.workspace),

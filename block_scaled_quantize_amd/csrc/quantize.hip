@@ -14,6 +14,8 @@
 // (two 16-byte loads) and 16 bytes of output (one 16-byte store) per 16 elements.
 #include <float.h>
 
+#include <atomic>
+
 #include "common.h"
 
 namespace fp8bs {
@@ -314,28 +316,37 @@ extern "C" size_t fp8_quantize_delayed_workspace_size(void) {
   return sizeof(uint32_t) * kDelayedBlocks;
 }
 
-extern "C" int fp8_quantize_delayed(const void* x_bf16, int64_t numel, int fmt, int mode,
-                                    int margin, int hist_len, float* amax_history, float* scale,
-                                    void* q_out, float* scale_inv_used, void* workspace,
-                                    size_t workspace_bytes, void* stream) {
+namespace fp8bs {
+namespace {
+
+// Argument checks shared by the delayed entry points (the workspace is checked by the caller).
+int delayed_args_ok(const void* x_bf16, int64_t numel, int fmt, int mode, int margin,
+                    int hist_len, const float* amax_history, const float* scale, const void* q_out,
+                    const float* scale_inv_used) {
   if (!fmt_ok(fmt) || (mode != FP8BS_SCALE_FP32 && mode != FP8BS_SCALE_POW2) ||
       hist_len < 1 || hist_len > 1024 || margin < 0 || margin > 64)
     return FP8BS_ERR_ARG;
   if (numel < 0) return FP8BS_ERR_SHAPE;
   if (!amax_history || !scale || !scale_inv_used || (numel > 0 && (!x_bf16 || !q_out)))
     return FP8BS_ERR_NULL;
-  if (!workspace || workspace_bytes < fp8_quantize_delayed_workspace_size())
-    return FP8BS_ERR_WORKSPACE;
-  if (!aligned4(workspace) || !aligned4(amax_history) || !aligned4(scale) ||
-      !aligned4(scale_inv_used))
+  if (!aligned4(amax_history) || !aligned4(scale) || !aligned4(scale_inv_used))
     return FP8BS_ERR_ALIGN;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  return FP8BS_OK;
+}
+
+// Cast + finalize of one delayed step; `part` holds at least delayed_blocks(numel) words.
+int delayed_blocks(int64_t numel) {
   const int64_t nchunks = (numel + 15) / 16;
-  const int blocks = (int)std::min<int64_t>(kDelayedBlocks, std::max<int64_t>(1, ceil_div(nchunks, kThreads)));
+  return (int)std::min<int64_t>(kDelayedBlocks, std::max<int64_t>(1, ceil_div(nchunks, kThreads)));
+}
+
+int delayed_launch(const void* x_bf16, int64_t numel, int fmt, int mode, int margin,
+                   int hist_len, float* amax_history, float* scale, void* q_out,
+                   float* scale_inv_used, uint32_t* part, hipStream_t st) {
+  const int blocks = delayed_blocks(numel);
   const bool vec = aligned16(x_bf16) && aligned16(q_out);
   const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
   uint8_t* q = static_cast<uint8_t*>(q_out);
-  uint32_t* part = static_cast<uint32_t*>(workspace);
   int rc;
   if (fmt == FP8BS_E4M3)
     rc = vec ? launch(delayed_cast_kernel<FP8BS_E4M3, true>, dim3(blocks), dim3(kThreads), st, x, numel, scale, q, part)
@@ -352,6 +363,70 @@ extern "C" int fp8_quantize_delayed(const void* x_bf16, int64_t numel, int fmt, 
   return launch(delayed_finalize_kernel<FP8BS_E5M2>, dim3(1), dim3(kThreads), st,
                 (const uint32_t*)part, blocks, margin, pow2, hist_len, amax_history, scale,
                 scale_inv_used);
+}
+
+// Scratch memory of fp8_quantize_delayed_noalloc: the cast kernel's per-workgroup amax partials
+// (one word per workgroup; the cast grid never exceeds kDelayedBlocks workgroups, so its size
+// does not depend on the tensor).  Each device holds its own copy; host code reaches it only
+// through the address hipGetSymbolAddress returns on that device (the array's name is a host
+// stand-in there, not a device address).
+constexpr int kScratchWords = kDelayedBlocks;
+__device__ __align__(256) uint32_t scratch[kScratchWords];
+
+constexpr int kMaxDevices = 64;
+std::atomic<uint32_t*> g_scratch[kMaxDevices];
+
+// The device address of `scratch` on the current device, looked up on the first call there.
+uint32_t* scratch_on_current_device(int* status) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *status = FP8BS_ERR_LAUNCH;
+    return nullptr;
+  }
+  uint32_t* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* addr = nullptr;
+  if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) {
+    *status = FP8BS_ERR_LAUNCH;
+    return nullptr;
+  }
+  p = static_cast<uint32_t*>(addr);
+  g_scratch[dev].store(p, std::memory_order_release);
+  return p;
+}
+
+}  // namespace
+}  // namespace fp8bs
+
+extern "C" int fp8_quantize_delayed(const void* x_bf16, int64_t numel, int fmt, int mode,
+                                    int margin, int hist_len, float* amax_history, float* scale,
+                                    void* q_out, float* scale_inv_used, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  const int s = delayed_args_ok(x_bf16, numel, fmt, mode, margin, hist_len, amax_history, scale,
+                                q_out, scale_inv_used);
+  if (s != FP8BS_OK) return s;
+  if (!workspace || workspace_bytes < fp8_quantize_delayed_workspace_size())
+    return FP8BS_ERR_WORKSPACE;
+  if (!aligned4(workspace)) return FP8BS_ERR_ALIGN;
+  return delayed_launch(x_bf16, numel, fmt, mode, margin, hist_len, amax_history, scale, q_out,
+                        scale_inv_used, static_cast<uint32_t*>(workspace),
+                        static_cast<hipStream_t>(stream));
+}
+
+extern "C" int fp8_quantize_delayed_noalloc(const void* x_bf16, int64_t numel, int fmt, int mode,
+                                            int margin, int hist_len, float* amax_history,
+                                            float* scale, void* q_out, float* scale_inv_used,
+                                            void* stream) {
+  const int s = delayed_args_ok(x_bf16, numel, fmt, mode, margin, hist_len, amax_history, scale,
+                                q_out, scale_inv_used);
+  if (s != FP8BS_OK) return s;
+  static_assert(kScratchWords >= kDelayedBlocks, "scratch holds one partial per workgroup");
+  if (delayed_blocks(numel) > kScratchWords) return FP8BS_ERR_WORKSPACE;   // (never: capped)
+  int status = FP8BS_OK;
+  uint32_t* part = scratch_on_current_device(&status);
+  if (!part) return status;
+  return delayed_launch(x_bf16, numel, fmt, mode, margin, hist_len, amax_history, scale, q_out,
+                        scale_inv_used, part, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int fp8_cast_fp32(const float* x, int64_t n, int fmt, void* q_out, void* stream) {

@@ -158,6 +158,24 @@ int fp8_quantize_delayed(const void* x_bf16, int64_t numel, int fmt, int mode, i
 size_t fp8_quantize_delayed_workspace_size(void);
 
 /*
+ * fp8_quantize_delayed without the workspace argument, for callers that cannot allocate device
+ * memory (code captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc): the per-workgroup amax partials go to a scratch array the library holds in each
+ * device's memory for the life of the process (8 KiB: one 4-byte word for each of the at most
+ * 2048 workgroups of the cast, whatever numel is, so no tensor is too large for it).  Nothing
+ * is allocated or freed by the call; the array's device address is looked up once per device,
+ * on the first call there.  Arguments, results and errors as fp8_quantize_delayed (no
+ * FP8BS_ERR_WORKSPACE in practice; FP8BS_ERR_LAUNCH also if the scratch array cannot be
+ * located).  Every call on one device shares that device's array: calls that overlap on one
+ * GPU (different streams, or host threads, without ordering) race and must not be issued;
+ * calls ordered on one stream are safe.  Each call writes every partial it reads, so no
+ * clearing is needed between calls.
+ */
+int fp8_quantize_delayed_noalloc(const void* x_bf16, int64_t numel, int fmt, int mode, int margin,
+                                 int hist_len, float* amax_history, float* scale, void* q_out,
+                                 float* scale_inv_used, void* stream);
+
+/*
  * Saturating round-to-nearest-even cast of fp32 values to FP8 codes, no scaling
  * (q_out[i] = encode(x[i])).  The precision-conversion step of [P1] "Transformer Engine: la
  * base de software", exposed on its own.  Errors: FP8BS_ERR_NULL, FP8BS_ERR_SHAPE,

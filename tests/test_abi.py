@@ -226,6 +226,29 @@ def test_tiled_entry_validation():
         assert qtiled(tile, M=0) == bsq.OK
 
 
+def test_delayed_noalloc_validation():
+    """fp8_quantize_delayed_noalloc validates like fp8_quantize_delayed (no workspace argument);
+    invalid calls return before any device is touched."""
+    lib = bsq.load()
+    a = [FAKE, 1024, 0, 0, 0, 16, FAKE, FAKE, FAKE, FAKE, None]
+
+    def call(**kw):
+        b = list(a)
+        for k, v in kw.items():
+            b[int(k[1:])] = v
+        return lib.fp8_quantize_delayed_noalloc(*b)
+
+    assert call(a2=2) == bsq.ERR_ARG          # format
+    assert call(a3=3) == bsq.ERR_ARG          # scale mode
+    assert call(a4=-1) == bsq.ERR_ARG         # margin
+    assert call(a5=0) == bsq.ERR_ARG          # history length
+    assert call(a5=1025) == bsq.ERR_ARG
+    assert call(a1=-1) == bsq.ERR_SHAPE
+    assert call(a6=None) == bsq.ERR_NULL      # history
+    assert call(a0=None) == bsq.ERR_NULL      # input with numel > 0
+    assert call(a7=FAKE + 2) == bsq.ERR_ALIGN  # scale
+
+
 def test_cast_validation():
     lib = bsq.load()
     assert lib.fp8_cast_fp32(FAKE, 16, 3, FAKE, None) == bsq.ERR_ARG
