@@ -43,7 +43,8 @@ HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 GEMM_COUNTERS = os.path.join(ROOT, "profiles", "gemm_kernel_llama8b_fprop_counters.txt")
 GEMM_COUNTERS_POW2 = os.path.join(ROOT, "profiles", "gemm_kernel_pow2_llama8b_fprop_counters.txt")
 GEMM_SOURCES = [os.path.join(ROOT, "block_scaled_quantize_amd", "csrc", f)
-                for f in ("gemm_impl.h", "gemm.hip", "gemm_pow2.hip", "common.h")]
+                for f in ("gemm_impl.h", "gemm.hip", "gemm_fprop.hip", "gemm_fprop_pow2.hip",
+                          "gemm_dgrad.hip", "gemm_wgrad.hip", "gemm_grouped.hip", "common.h")]
 
 LAYERS_8B = [("qkv", 4096, 6144), ("o", 4096, 4096), ("gate_up", 4096, 28672), ("down", 14336, 4096)]
 

@@ -43,6 +43,37 @@
 #include "common.h"
 
 namespace fp8bs {
+
+// Arguments of one GEMM launch, as the kernels read them.
+struct GemmParams {
+  int64_t M, N, K;
+  const uint8_t* A;   // activation side (rows m)
+  int64_t lda;
+  const uint8_t* B;   // weight side (rows n)
+  int64_t ldb;
+  const float* sa;    // sa(m, kb) = sa[kb * sa_ks + (m >> sa_rshift) * sa_rs]
+  int64_t sa_ks, sa_rs, sa_bytes;
+  int sa_rshift;
+  const float* sb;    // sb(n, kb) = sb[kb * sb_ks + (n / 128) * sb_rs]
+  int64_t sb_ks, sb_rs, sb_bytes;
+  uint16_t* C;        // may be null when the output is only wanted quantized
+  int64_t ldc;
+  int tiles_m, tiles_n;
+  int c_vec;          // 8-byte output stores are aligned
+  int c_vec16;        // 16-byte output stores are aligned
+  // fused output quantization (1x128 blocks along N): codes Cq[M, N] (pitch ldcq) and
+  // dequantization factors cqs[ceil(N/128)][M]
+  uint8_t* Cq;
+  int64_t ldcq;
+  float* cqs;
+  int cq_vec;         // 4-byte code stores are aligned
+  // grouped GEMM only
+  const int64_t* offsets;
+  int num_groups;
+  int64_t b_group_stride;   // bytes between experts' weights
+  int64_t sb_group_stride;  // floats between experts' scales
+};
+
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -63,6 +94,8 @@ constexpr int kScaleHwRows = 4;
 
 constexpr int kGroupM = 8;      // tile-rows per L2 group in the tile order
 constexpr int kLdsBytes = 160 * 1024;
+constexpr int kStaticLdsReserve = 8448;   // the grouped kernel's group bounds and prefixes
+constexpr bool kPersistentDense = true;   // two-stage dense tiles on a persistent grid
 
 // Tile configuration: BM x BN output tile, WAVES_M x WAVES_N waves, each wave owning a
 // (BM / WAVES_M) x (BN / WAVES_N) block of 16x16 pieces.  Three LDS stages when they fit in
@@ -85,7 +118,14 @@ struct Cfg {
   static constexpr int kDummyBytes = 256;   // target of the scale DMAs of non-loading waves
   static constexpr int kStages = 3 * kStage + kDummyBytes <= kLdsBytes ? 3 : 2;
   static constexpr int kDummy = kStage * kStages;   // offset of the dummy slot
-  static constexpr int kLds = kDummy + kDummyBytes;
+  // Epilogue staging: per wave 16 output rows x 64 columns of bf16 (128 bytes, pitch 144), when
+  // it fits next to the stages and the grouped kernel's static LDS.
+  static constexpr int kEpiPitch = 144;
+  static constexpr int kEpiWaveBytes = 16 * kEpiPitch;
+  static constexpr int kEpi = kDummy + kDummyBytes;
+  static constexpr bool kStagedEpi =
+      kWTN == 64 && kEpi + kWaves * kEpiWaveBytes + kStaticLdsReserve <= kLdsBytes;
+  static constexpr int kLds = kEpi + (kStagedEpi ? kWaves * kEpiWaveBytes : 0);
   static constexpr int kXLoads = BM / 8 / kWaves;   // 1 KB DMA blocks of the X tile per wave
   static constexpr int kWLoads = BN / 8 / kWaves;   // ... of the W tile per wave
   static constexpr int kSaWaves = BM / 64;          // waves that load 64 scale words each
@@ -100,33 +140,6 @@ struct Cfg {
   static_assert(2 * kStage + kDummyBytes <= kLdsBytes, "LDS");
 };
 
-struct GemmParams {
-  int64_t M, N, K;
-  const uint8_t* A;   // activation side (rows m)
-  int64_t lda;
-  const uint8_t* B;   // weight side (rows n)
-  int64_t ldb;
-  const float* sa;    // sa(m, kb) = sa[kb * sa_ks + (m >> sa_rshift) * sa_rs]
-  int64_t sa_ks, sa_rs, sa_bytes;
-  int sa_rshift;
-  const float* sb;    // sb(n, kb) = sb[kb * sb_ks + (n / 128) * sb_rs]
-  int64_t sb_ks, sb_rs, sb_bytes;
-  uint16_t* C;        // may be null when the output is only wanted quantized
-  int64_t ldc;
-  int tiles_m, tiles_n;
-  int c_vec;          // 8-byte output stores are aligned
-  // fused output quantization (1x128 blocks along N): codes Cq[M, N] (pitch ldcq) and
-  // dequantization factors cqs[ceil(N/128)][M]
-  uint8_t* Cq;
-  int64_t ldcq;
-  float* cqs;
-  int cq_vec;         // 4-byte code stores are aligned
-  // grouped GEMM only
-  const int64_t* offsets;
-  int num_groups;
-  int64_t b_group_stride;   // bytes between experts' weights
-  int64_t sb_group_stride;  // floats between experts' scales
-};
 
 // ------------------------------------------------------------------ low-level helpers
 __device__ __forceinline__ u32x4 make_rsrc(const void* base, uint64_t nbytes) {
@@ -318,6 +331,63 @@ struct Tile {
 struct Carry {
   int stage0, prefetched, stores;
 };
+
+// The epilogue store of one 16x16 piece: this lane's 4 consecutive outputs of row m, rounded to
+// bf16 (round to nearest even) and stored with one 8-byte store when aligned.
+template <class C>
+__device__ __forceinline__ void store_piece(const GemmParams& p, const Tile& t, int wm, int wn,
+                                            int li, int g, int i, int j, v4f v) {
+  const int64_t m = (int64_t)t.m0 + wm * C::kWTM + 16 * j + li;
+  if (m >= t.m_end) return;
+  uint16_t* crow = p.C + m * p.ldc;
+  const int64_t n = (int64_t)t.n0 + wn * C::kWTN + 16 * i + 4 * g;
+  const uint32_t lo = pack_bf16x2(v[0], v[1]);
+  const uint32_t hi = pack_bf16x2(v[2], v[3]);
+  if (p.c_vec && n + 4 <= p.N) {
+    *reinterpret_cast<uint2*>(crow + n) = make_uint2(lo, hi);
+  } else {
+    const uint16_t h[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (n + e < p.N) crow[n + e] = h[e];
+  }
+}
+
+// The epilogue store of the 16 rows of m piece j (this wave's 64 columns): the lane's bf16
+// values go to the wave's own LDS rows, come back as 16-byte row chunks, and leave as whole
+// 128-byte row segments (8 rows per store instruction) instead of 32-byte pieces of 16 rows.
+template <class C>
+__device__ __forceinline__ void store_rows_staged(const GemmParams& p, const Tile& t, int wm,
+                                                  int wn, int lane, int j, const v4f (&v)[C::kNI],
+                                                  uint8_t* region) {
+  static_assert(C::kWTN == 64 && C::kNI == 4, "a wave's rows are 128 bytes");
+  const int li = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < C::kNI; ++i)
+    *reinterpret_cast<uint2*>(region + li * C::kEpiPitch + 32 * i + 8 * g) =
+        make_uint2(pack_bf16x2(v[i][0], v[i][1]), pack_bf16x2(v[i][2], v[i][3]));
+  wait_lds();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = 8 * h + (lane >> 3), c = lane & 7;
+    const uint4 d = *reinterpret_cast<const uint4*>(region + r * C::kEpiPitch + 16 * c);
+    const int64_t m = (int64_t)t.m0 + wm * C::kWTM + 16 * j + r;
+    const int64_t n = (int64_t)t.n0 + wn * C::kWTN + 8 * c;
+    if (m < t.m_end) {
+      uint16_t* crow = p.C + m * p.ldc;
+      if (n + 8 <= p.N) {
+        *reinterpret_cast<uint4*>(crow + n) = d;
+      } else {
+        const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (n + e < p.N) crow[n + e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+  }
+  wait_lds();   // (the next round rewrites the region)
+}
+
 
 // E8M0 code of a power-of-two scale: its binary32 exponent field (2^-127, the one subnormal
 // power of two a scale can take, has field 0 and is E8M0 code 0 as well).
@@ -798,28 +868,29 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
 
   // Epilogue: lane holds C[m][n .. n+3] of each piece.
   if (p.C) {
+    if (C::kStagedEpi && p.c_vec16) {
+      uint8_t* region = smem + C::kEpi + w * C::kEpiWaveBytes;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int64_t m = m0 + wm * C::kWTM + 16 * j + li;
-      if (m >= m_end) continue;
-      uint16_t* crow = p.C + m * p.ldc;
+      for (int j = 0; j < NJ; ++j) {
+        v4f v[NI];
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int64_t n = n0 + wn * C::kWTN + 16 * i + 4 * g;
-        v4f v = acc[i][j];
-        if constexpr (SM == kScaleTensor) v = v * post;
-        if (nkb == 0) v = v4f{0.f, 0.f, 0.f, 0.f};
-        const uint32_t lo = pack_bf16x2(v[0], v[1]);
-        const uint32_t hi = pack_bf16x2(v[2], v[3]);
-        if (p.c_vec && n + 4 <= p.N) {
-          *reinterpret_cast<uint2*>(crow + n) = make_uint2(lo, hi);
-        } else {
-          const uint16_t h[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < p.N) crow[n + e] = h[e];
+        for (int i = 0; i < NI; ++i) {
+          v[i] = acc[i][j];
+          if constexpr (SM == kScaleTensor) v[i] = v[i] * post;
+          if (nkb == 0) v[i] = v4f{0.f, 0.f, 0.f, 0.f};
         }
+        store_rows_staged<C>(p, t, wm, wn, lane, j, v, region);
       }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          v4f v = acc[i][j];
+          if constexpr (SM == kScaleTensor) v = v * post;
+          if (nkb == 0) v = v4f{0.f, 0.f, 0.f, 0.f};
+          store_piece<C>(p, t, wm, wn, li, g, i, j, v);
+        }
     }
   }
   if constexpr (QO != 0) quantize_out<C, SM, QO>(p, smem, acc, post, nkb, m0, m_end, n0);
@@ -831,11 +902,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
     for (int j = 0; j < NJ; ++j) jv += (m0 + wm * C::kWTM + 16 * j < m_end) ? 1 : 0;
 #pragma unroll
     for (int i = 0; i < NI; ++i) iv += (n0 + wn * C::kWTN + 16 * i < p.N) ? 1 : 0;
-    cy.stores = p.C ? iv * jv : 0;
+    // (staged epilogue: at least one store instruction per m piece whose first row is inside,
+    // when the wave's first column is)
+    cy.stores = p.C ? ((C::kStagedEpi && p.c_vec16) ? (iv > 0 ? jv : 0) : iv * jv) : 0;
     cy.prefetched = pf_live ? 1 : 0;
     cy.stage0 = (st0 + nkb) % C::kStages;
   }
 }
+
 
 // Map a linear workgroup id to a tile so that each of the 8 XCDs (ids are dealt round robin)
 // gets a contiguous range of tiles, ordered in groups of kGroupM tile-rows for L2 reuse.
@@ -862,6 +936,52 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
   const Tile t{0, m0, (int)std::min<int64_t>((int64_t)m0 + C::BM, p.M), tn * C::BN};
   Carry cy{0, 0, 0};
   gemm_tile<C, LAYOUT, FA, FB, SM, QO>(p, smem, t, t, false, cy);
+}
+
+// The kernel parameters, read again from the argument segment (scalar loads) where a
+// persistent kernel starts a tile, so that values derived from them are not kept live across
+// the whole tile loop.
+#if defined(__HIP_DEVICE_COMPILE__)
+#define FP8BS_REREAD_PARAMS(q, p)                                                      \
+  typedef const __attribute__((address_space(4))) GemmParams* ParamPtr;               \
+  ParamPtr pp_ = (ParamPtr)__builtin_amdgcn_kernarg_segment_ptr();                    \
+  asm volatile("" : "+s"(pp_));                                                       \
+  const GemmParams q = *pp_
+#else
+#define FP8BS_REREAD_PARAMS(q, p) const GemmParams& q = p   /* (host pass: never run) */
+#endif
+
+// Dense GEMM on a persistent grid (one workgroup per CU; 256x256 tiles, two LDS stages): each
+// workgroup walks tiles id, id + grid, ... in the XCD-local order of tile_of and loads the next
+// tile's first K block during the current tile's last block, so that block's load overlaps
+// the epilogue's stores.
+template <class C, int LAYOUT, int FA, int FB, int SM>
+__global__ __launch_bounds__(C::kThreads, 1) void gemm_persistent_kernel(GemmParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  static_assert(C::kStages == 2, "persistent dense GEMM: two-stage tiles");
+  const int total = p.tiles_m * p.tiles_n;
+  int id = blockIdx.x;
+  if (id >= total) return;
+  auto tile_at = [&](int i) {
+    int tm, tn;
+    tile_of(i, p.tiles_m, p.tiles_n, tm, tn);
+    const int m0 = __builtin_amdgcn_readfirstlane(tm) * C::BM;
+    return Tile{0, m0, (int)std::min<int64_t>((int64_t)m0 + C::BM, p.M),
+                __builtin_amdgcn_readfirstlane(tn) * C::BN};
+  };
+  Tile cur = tile_at(id);
+  Carry cy{0, 0, 0};
+  while (true) {
+    const int nid = id + (int)gridDim.x;
+    const bool has_next = nid < total;
+    const Tile nxt = has_next ? tile_at(nid) : cur;
+    FP8BS_REREAD_PARAMS(q, p);
+    gemm_tile<C, LAYOUT, FA, FB, SM, 0, true, true>(q, smem, cur, nxt, has_next, cy);
+    if (!has_next) break;
+    if (!cy.prefetched) __syncthreads();   // the next tile refills the LDS stages
+    cur = nxt;
+    id = nid;
+  }
 }
 
 // Grouped: a persistent grid walks the concatenation of every group's m tiles (times the n
@@ -951,16 +1071,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(GemmParams
     const int nid = id + (int)gridDim.x;
     const bool has_next = nid < total;
     const Tile nxt = has_next ? tile_at(nid) : cur;
-    // The parameters are read again from the argument segment for every tile (scalar loads),
-    // so that values derived from them are not kept live across the whole tile loop.
-#if defined(__HIP_DEVICE_COMPILE__)
-    typedef const __attribute__((address_space(4))) GemmParams* ParamPtr;
-    ParamPtr pp = (ParamPtr)__builtin_amdgcn_kernarg_segment_ptr();
-    asm volatile("" : "+s"(pp));
-    const GemmParams q = *pp;
-#else
-    const GemmParams& q = p;   // (host pass: the body is never run there)
-#endif
+    FP8BS_REREAD_PARAMS(q, p);
     gemm_tile<C, FP8BS_FPROP, FA, FB, SM, 0, PF, true>(q, smem, cur, nxt, has_next, cy);
     if (!has_next) break;
     if (!cy.prefetched) __syncthreads();   // the next tile refills the LDS stages
@@ -973,6 +1084,21 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(GemmParams
 // raised once per device; that is done on the first launch of each kernel instantiation on a
 // device (a bit per device, set after the call succeeded), so later launches only enqueue.
 constexpr int kMaxDevices = 64;
+
+// Compute units of the current device, read once per device (the persistent grouped grid has
+// one workgroup per CU).  0 when the device cannot be queried.
+inline int device_cus() {
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus > 0) return cus;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return 0;
+  cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
 
 template <auto KERNEL>
 int launch_gemm(int blocks, int threads, int lds, hipStream_t st, const GemmParams& p) {
@@ -998,13 +1124,22 @@ using CfgB = Cfg<256, 128, 4, 2>;   // 8 waves, 64 x 64 per wave, 3 stages
 using CfgC = Cfg<256, 256, 2, 4>;   // 8 waves, 128 x 64 per wave, 2 stages
 using CfgD = Cfg<128, 128, 2, 2>;   // 4 waves, 64 x 64 per wave (small M, grouped)
 
+// Two-stage tiles without fused output quantization run on the persistent grid (one
+// workgroup per CU, deferred epilogue); the others one workgroup per tile.
 template <class C, int LAYOUT, int FA, int FB, int SM, int QO = 0>
 int launch_dense(GemmParams p, hipStream_t st) {
   p.tiles_m = (int)ceil_div(p.M, C::BM);
   p.tiles_n = (int)ceil_div(p.N, C::BN);
   if ((int64_t)p.tiles_m * p.tiles_n > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
-  return launch_gemm<gemm_kernel<C, LAYOUT, FA, FB, SM, QO>>(p.tiles_m * p.tiles_n, C::kThreads,
-                                                             C::kLds, st, p);
+  const int tiles = p.tiles_m * p.tiles_n;
+  if constexpr (C::kStages == 2 && QO == 0 && kPersistentDense) {
+    const int cus = device_cus();
+    if (cus <= 0) return FP8BS_ERR_LAUNCH;
+    return launch_gemm<gemm_persistent_kernel<C, LAYOUT, FA, FB, SM>>(std::min(tiles, cus),
+                                                                      C::kThreads, C::kLds, st, p);
+  } else {
+    return launch_gemm<gemm_kernel<C, LAYOUT, FA, FB, SM, QO>>(tiles, C::kThreads, C::kLds, st, p);
+  }
 }
 
 // Tile configuration of a dense GEMM: FP8BS_TILE_AUTO takes the largest tile that still gives
@@ -1154,6 +1289,7 @@ inline int dense_params(int layout, int64_t M, int64_t N, int64_t K, const void*
   p.sb = scale_inv_b; p.sb_ks = sb.ks; p.sb_rs = sb.rs; p.sb_bytes = sb.bytes;
   p.C = static_cast<uint16_t*>(C_bf16); p.ldc = ldc;
   p.c_vec = (reinterpret_cast<uintptr_t>(C_bf16) % 8 == 0) && (ldc % 4 == 0);
+  p.c_vec16 = (reinterpret_cast<uintptr_t>(C_bf16) % 16 == 0) && (ldc % 8 == 0);
   tensor_only = ga == FP8BS_PER_TENSOR && gb == FP8BS_PER_TENSOR;
   b_rows = gb == FP8BS_BLOCK_1x128;   // only accepted for a K-major weight operand (fprop)
   return FP8BS_OK;
@@ -1190,6 +1326,7 @@ inline int grouped_params(int32_t num_groups, const int64_t* group_offsets, int6
   p.sb = scale_inv_b; p.sb_ks = 1; p.sb_rs = ceil_div(K, 128);
   p.C = static_cast<uint16_t*>(C_bf16); p.ldc = ldc;
   p.c_vec = (reinterpret_cast<uintptr_t>(C_bf16) % 8 == 0) && (ldc % 4 == 0);
+  p.c_vec16 = (reinterpret_cast<uintptr_t>(C_bf16) % 16 == 0) && (ldc % 8 == 0);
   p.offsets = group_offsets;
   p.num_groups = num_groups;
   p.b_group_stride = N * ldb;
@@ -1198,41 +1335,19 @@ inline int grouped_params(int32_t num_groups, const int64_t* group_offsets, int6
   return FP8BS_OK;
 }
 
-// Compute units of the current device, read once per device (the persistent grouped grid has
-// one workgroup per CU).  0 when the device cannot be queried.
-inline int device_cus() {
-  static std::atomic<int> cached[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-  int cus = cached[dev].load(std::memory_order_relaxed);
-  if (cus > 0) return cus;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    return 0;
-  cached[dev].store(cus, std::memory_order_relaxed);
-  return cus;
-}
-
 }  // namespace
 
-// Entry-point bodies shared by the exported functions of gemm.hip and gemm_pow2.hip (each is
-// defined in one of them; hidden, not part of the C ABI).  pow2 = false: fp32 block scales
-// folded between K blocks; pow2 = true: power-of-2 scales given to the MFMA as E8M0.
-__attribute__((visibility("hidden"))) int gemm_dense_fp32(
-    int tile, int layout, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int fa,
-    int ga, const float* sa, const void* B, int64_t ldb, int fb, int gb, const float* sb,
-    void* C, int64_t ldc, hipStream_t st);
-__attribute__((visibility("hidden"))) int gemm_dense_pow2(
-    int tile, int layout, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int fa,
-    int ga, const float* sa, const void* B, int64_t ldb, int fb, int gb, const float* sb,
-    void* C, int64_t ldc, hipStream_t st);
-__attribute__((visibility("hidden"))) int gemm_grouped_fp32(
-    int tile, int32_t G, const int64_t* offsets, int64_t M, int64_t N, int64_t K, const void* A,
-    int64_t lda, int fa, const float* sa, const void* B, int64_t ldb, int fb, const float* sb,
-    void* C, int64_t ldc, hipStream_t st);
-__attribute__((visibility("hidden"))) int gemm_grouped_pow2(
-    int tile, int32_t G, const int64_t* offsets, int64_t M, int64_t N, int64_t K, const void* A,
-    int64_t lda, int fa, const float* sa, const void* B, int64_t ldb, int fb, const float* sb,
-    void* C, int64_t ldc, hipStream_t st);
+// The dense kernels of one layout (and scale family) are instantiated in a translation unit of
+// their own, so that the library's sources compile in parallel: gemm_fprop.hip (fp32 block,
+// 1x128-both and per-tensor scales), gemm_fprop_pow2.hip (E8M0 scales), gemm_dgrad.hip,
+// gemm_wgrad.hip, gemm_grouped.hip.  sm is one of the kScale* modes above; hidden symbols, not
+// part of the C ABI.
+#define FP8BS_HIDDEN __attribute__((visibility("hidden")))
+FP8BS_HIDDEN int gemm_fprop_fp32(int sm, int fa, int fb, const GemmParams& p, int tile, hipStream_t st);
+FP8BS_HIDDEN int gemm_fprop_pow2(int sm, int fa, int fb, const GemmParams& p, int tile, hipStream_t st);
+FP8BS_HIDDEN int gemm_dgrad(int sm, int fa, int fb, const GemmParams& p, int tile, hipStream_t st);
+FP8BS_HIDDEN int gemm_wgrad(int sm, int fa, int fb, const GemmParams& p, int tile, hipStream_t st);
+FP8BS_HIDDEN int gemm_grouped(bool pow2, int fa, int fb, int cus, const GemmParams& p, int tile,
+                              hipStream_t st);
 
 }  // namespace fp8bs

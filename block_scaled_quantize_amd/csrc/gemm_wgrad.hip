@@ -1,0 +1,16 @@
+// Dense wgrad kernels (FP8BS_WGRAD layout) for fp32 block scales, per-tensor scales and power-of-2
+// (E8M0) block scales; device code in gemm_impl.h.
+#include "gemm_impl.h"
+
+namespace fp8bs {
+
+int gemm_wgrad(int sm, int fa, int fb, const GemmParams& p, int tile, hipStream_t st) {
+  switch (sm) {
+    case kScaleFold: return dispatch_formats<FP8BS_WGRAD, kScaleFold>(fa, fb, p, tile, st);
+    case kScaleTensor: return dispatch_formats<FP8BS_WGRAD, kScaleTensor>(fa, fb, p, tile, st);
+    case kScaleHw: return dispatch_formats<FP8BS_WGRAD, kScaleHw>(fa, fb, p, tile, st);
+    default: return FP8BS_ERR_UNSUPPORTED;
+  }
+}
+
+}  // namespace fp8bs
