@@ -686,14 +686,16 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
   auto scales_of = [&](const uint8_t* st) {
     return reinterpret_cast<const float*>(st + C::kXBytes + C::kWBytes);
   };
-  // First m piece of a block: its fragment, and the factor c of its rows (fold: sa * sb; MFMA
-  // scales and 1x128 weight scales: sa); the block's weight scale sbv (one per wave).
+  // First m piece of a block: its fragment, and the activation scale c of its rows (the fold's
+  // factor is c * sbv; the multiply is left to the end of the piece that precedes the piece's
+  // use, so that no wave waits on the scale's LDS read right after issuing it); the block's
+  // weight scale sbv (one per wave).
   auto first_x = [&](const uint8_t* st, v8i& xf, float& c, float& sbv) {
     const float* sat = scales_of(st);
     xf = frag_at<XK>(st, xb, wm * C::kWTM);
     if constexpr (FOLD && !ROWS) {
       sbv = sat[BM + (wn * C::kWTN) / 128];
-      c = sat[wm * C::kWTM + li] * sbv;
+      c = sat[wm * C::kWTM + li];
     } else if constexpr (HW && !ROWS) {
       sbv = sat[BM + (wn * C::kWTN) / 128];
       c = sat[wm * C::kWTM + li];
@@ -739,6 +741,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
     prepare(0);
     const uint8_t* st = stage_ptr(0);
     first_x(st, xf, ccur, sbv);
+    if constexpr (FOLD && !ROWS) ccur *= sbv;
 #pragma unroll
     for (int i = 0; i < NI; ++i) wf[i] = w_fragment(st, i);
     fold_row_scales(st, sbr);
@@ -781,8 +784,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
       float cnext = 0.0f;
       if (j + 1 < NJ) {
         xnext = frag_at<XK>(st, xb, wm * C::kWTM + 16 * j + 16);
-        if constexpr (FOLD && !ROWS) cnext = sat[mrow + 16] * sbv;
-        if constexpr (HW || ROWS) cnext = sat[mrow + 16];
+        if constexpr (FOLD || HW) cnext = sat[mrow + 16];   // (fold: times sbv at the end)
       }
       const bool turn = TURN && j == NJ - 1;   // block kb + 1 is published before this piece
       if (turn) {
@@ -847,7 +849,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
       cprev = ccur;
       if (j + 1 < NJ || TURN) {
         xf = xnext;
-        ccur = cnext;
+        // (fold with 128x128 weight scales: sbv is the next piece's block's, also after a turn)
+        ccur = (FOLD && !ROWS) ? cnext * sbv : cnext;
       }
     }
   };
