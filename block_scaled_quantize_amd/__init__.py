@@ -63,6 +63,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.fp8bs_status_string.restype = ctypes.c_char_p
     lib.fp8_quantize_blockwise.argtypes = [vp, i64, i64, i64, i32, i32, i32, vp, i64, vp, vp]
     lib.fp8_quantize_columnwise_t.argtypes = [vp, i64, i64, i64, i32, i32, vp, i64, vp, vp]
+    lib.fp8_quantize_blockwise_batched.argtypes = [i32, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp]
     lib.fp8_quantize_delayed.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.fp8_quantize_delayed_noalloc.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp]
     lib.fp8_quantize_delayed_workspace_size.argtypes = []
@@ -87,6 +88,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.fp8_attention_decode_workspace_size.argtypes = [i64, i64, i64, i64, i64]
     lib.fp8_attention_decode_workspace_size.restype = sz
     for name in ("fp8_quantize_blockwise", "fp8_quantize_columnwise_t", "fp8_quantize_delayed",
+                 "fp8_quantize_blockwise_batched",
                  "fp8_quantize_delayed_noalloc",
                  "fp8_cast_fp32",
                  "fp8_gemm_blockscaled", "fp8_grouped_gemm", "fp8_gemm_blockscaled_pow2",
@@ -183,6 +185,39 @@ def quantize_blockwise(x: torch.Tensor, fmt: int, gran: int, mode: int = SCALE_F
                                          _ptr(q), q.stride(0), _ptr(scale_inv), _stream(stream)),
            "fp8_quantize_blockwise")
     return q, scale_inv
+
+
+def quantize_blockwise_batched(xs, grans, fmt: int, mode: int = SCALE_FP32, qs=None,
+                               scale_invs=None, stream=None):
+    """Blockwise quantization of several 2-D bf16 matrices in one launch
+    (fp8_quantize_blockwise_batched); grans[i] is BLOCK_1x128 or BLOCK_128x128 for xs[i].
+
+    Returns (list of codes, list of scale_inv), as quantize_blockwise returns for each."""
+    n = len(xs)
+    if len(grans) != n:
+        raise ValueError("one granularity per tensor")
+    qs = list(qs) if qs is not None else [None] * n
+    scale_invs = list(scale_invs) if scale_invs is not None else [None] * n
+    for i, x in enumerate(xs):
+        if x.dtype != torch.bfloat16 or x.dim() != 2 or (x.shape[1] > 1 and x.stride(1) != 1):
+            raise ValueError("each x must be a 2-D bf16 matrix with unit column stride")
+        rows, cols = x.shape
+        if qs[i] is None:
+            qs[i] = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+        _need_matrix(qs[i], (rows, cols), torch.uint8, f"q[{i}]")
+        shape = _operand_scale_shape(grans[i], rows, cols)
+        if scale_invs[i] is None:
+            scale_invs[i] = torch.empty(shape, dtype=torch.float32, device=x.device)
+        _need(scale_invs[i], shape, torch.float32, f"scale_inv[{i}]")
+    P = ctypes.c_void_p * max(n, 1)
+    I64 = ctypes.c_int64 * max(n, 1)
+    I32 = ctypes.c_int * max(n, 1)
+    _check(load().fp8_quantize_blockwise_batched(
+        n, P(*[_ptr(x) for x in xs]), I64(*[x.shape[0] for x in xs]), I64(*[x.shape[1] for x in xs]),
+        I64(*[x.stride(0) for x in xs]), I32(*grans), fmt, mode, P(*[_ptr(q) for q in qs]),
+        I64(*[q.stride(0) for q in qs]), P(*[_ptr(s) for s in scale_invs]), _stream(stream)),
+        "fp8_quantize_blockwise_batched")
+    return qs, scale_invs
 
 
 def quantize_columnwise_t(x: torch.Tensor, fmt: int, mode: int = SCALE_FP32,

@@ -376,7 +376,9 @@ __device__ __forceinline__ void store_rows_staged(const GemmParams& p, const Til
     if (m < t.m_end) {
       uint16_t* crow = p.C + m * p.ldc;
       if (n + 8 <= p.N) {
-        *reinterpret_cast<uint4*>(crow + n) = d;
+        // non-temporal: full lines go straight to memory instead of filling the caches with
+        // dirty output that the next kernel would have to write back
+        __builtin_nontemporal_store(u32x4{d.x, d.y, d.z, d.w}, reinterpret_cast<u32x4*>(crow + n));
       } else {
         const uint32_t w[4] = {d.x, d.y, d.z, d.w};
 #pragma unroll

@@ -82,14 +82,15 @@ constexpr int kRowsPerThread = 1;
 constexpr int kRows1 = (kThreads / 8) * kRowsPerThread;  // 32
 
 template <int FMT, bool POW2, bool VEC>
-__global__ __launch_bounds__(kThreads) void quant_1x128_kernel(
-    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
-    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale_inv) {
+__device__ __forceinline__ void quant_1x128_body(const uint16_t* __restrict__ x, int64_t rows,
+                                                 int64_t cols, int64_t ld_x,
+                                                 uint8_t* __restrict__ q, int64_t ld_q,
+                                                 float* __restrict__ scale_inv, int64_t bid) {
   const int t = threadIdx.x;
   const int64_t nbc = (cols + 127) >> 7;
-  const int64_t cb = blockIdx.x % nbc;
+  const int64_t cb = bid % nbc;
   const int64_t c0 = cb * 128 + (t & 7) * 16;
-  const int64_t r0 = (int64_t)(blockIdx.x / nbc) * kRows1 + (t >> 3);
+  const int64_t r0 = (bid / nbc) * kRows1 + (t >> 3);
   uint32_t d[kRowsPerThread][8];
 #pragma unroll
   for (int j = 0; j < kRowsPerThread; ++j)
@@ -105,17 +106,25 @@ __global__ __launch_bounds__(kThreads) void quant_1x128_kernel(
   }
 }
 
+template <int FMT, bool POW2, bool VEC>
+__global__ __launch_bounds__(kThreads) void quant_1x128_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale_inv) {
+  quant_1x128_body<FMT, POW2, VEC>(x, rows, cols, ld_x, q, ld_q, scale_inv, blockIdx.x);
+}
+
 // ---------------------------------------------------------------- 128x128 tiles
 // One workgroup per tile.  Thread t covers columns (t % 8) * 16 .. +16 of rows
 // t / 8 + 32 * i, i = 0..3; the tile amax is reduced across the workgroup through LDS.
 template <int FMT, bool POW2, bool VEC>
-__global__ __launch_bounds__(kThreads) void quant_128x128_kernel(
-    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
-    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale_inv) {
-  __shared__ uint32_t wave_amax[kThreads / 64];
+__device__ __forceinline__ void quant_128x128_body(const uint16_t* __restrict__ x, int64_t rows,
+                                                   int64_t cols, int64_t ld_x,
+                                                   uint8_t* __restrict__ q, int64_t ld_q,
+                                                   float* __restrict__ scale_inv, int64_t bid,
+                                                   uint32_t* wave_amax) {
   const int t = threadIdx.x;
   const int64_t nbc = (cols + 127) >> 7;
-  const int64_t tr = blockIdx.x / nbc, tc = blockIdx.x % nbc;
+  const int64_t tr = bid / nbc, tc = bid % nbc;
   const int64_t c0 = tc * 128 + (t & 7) * 16;
   const int64_t rbase = tr * 128 + (t >> 3);
   uint32_t d[4][8];
@@ -139,6 +148,54 @@ __global__ __launch_bounds__(kThreads) void quant_128x128_kernel(
   for (int i = 0; i < 4; ++i)
     store16<VEC>(q, rows, cols, ld_q, rbase + 32 * i, c0, encode_block_values<FMT>(d[i], s, finite));
   if (t == 0) scale_inv[tr * nbc + tc] = 1.0f / s;
+}
+
+template <int FMT, bool POW2, bool VEC>
+__global__ __launch_bounds__(kThreads) void quant_128x128_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale_inv) {
+  __shared__ uint32_t wave_amax[kThreads / 64];
+  quant_128x128_body<FMT, POW2, VEC>(x, rows, cols, ld_x, q, ld_q, scale_inv, blockIdx.x,
+                                     wave_amax);
+}
+
+// ---------------------------------------------------------------- several tensors, one launch
+// Up to kMaxBatch tensors quantized by one grid: workgroup b belongs to the tensor whose range
+// of the prefix-summed workgroup counts holds b and runs that tensor's 1x128 or 128x128 body
+// (the same code as the single-tensor kernels, so the results are identical).  One launch for
+// all of a step's weights spares the ramp and tail of each small launch.
+constexpr int kMaxBatch = 16;
+
+struct QuantTensor {
+  const uint16_t* x;
+  int64_t rows, cols, ld_x;
+  uint8_t* q;
+  int64_t ld_q;
+  float* s;
+  int64_t first;   // first workgroup of the tensor
+  int gran, vec;
+};
+struct QuantBatch {
+  QuantTensor t[kMaxBatch];
+  int count;
+};
+
+template <int FMT, bool POW2>
+__global__ __launch_bounds__(kThreads) void quant_batched_kernel(QuantBatch b) {
+  __shared__ uint32_t wave_amax[kThreads / 64];
+  const int64_t bid = blockIdx.x;
+  int k = 0;
+  for (int i = 1; i < b.count; ++i)
+    if (b.t[i].first <= bid) k = i;
+  const QuantTensor& t = b.t[k];
+  const int64_t local = bid - t.first;
+  if (t.gran == FP8BS_BLOCK_1x128) {
+    if (t.vec) quant_1x128_body<FMT, POW2, true>(t.x, t.rows, t.cols, t.ld_x, t.q, t.ld_q, t.s, local);
+    else quant_1x128_body<FMT, POW2, false>(t.x, t.rows, t.cols, t.ld_x, t.q, t.ld_q, t.s, local);
+  } else {
+    if (t.vec) quant_128x128_body<FMT, POW2, true>(t.x, t.rows, t.cols, t.ld_x, t.q, t.ld_q, t.s, local, wave_amax);
+    else quant_128x128_body<FMT, POW2, false>(t.x, t.rows, t.cols, t.ld_x, t.q, t.ld_q, t.s, local, wave_amax);
+  }
 }
 
 // ---------------------------------------------------------------- delayed per-tensor
@@ -310,6 +367,55 @@ extern "C" int fp8_quantize_blockwise(const void* x_bf16, int64_t rows, int64_t 
                                           scale_inv_out, st);
   return dispatch_blockwise<FP8BS_E5M2>(pow2, vec, x, rows, cols, ld_x, gran, q, ld_q,
                                         scale_inv_out, st);
+}
+
+extern "C" int fp8_quantize_blockwise_batched(int count, const void* const* x_bf16,
+                                              const int64_t* rows, const int64_t* cols,
+                                              const int64_t* ld_x, const int* gran, int fmt,
+                                              int mode, void* const* q_out, const int64_t* ld_q,
+                                              float* const* scale_inv_out, void* stream) {
+  if (!fmt_ok(fmt) || (mode != FP8BS_SCALE_FP32 && mode != FP8BS_SCALE_POW2) || count < 0 ||
+      count > kMaxBatch)
+    return FP8BS_ERR_ARG;
+  if (count == 0) return FP8BS_OK;
+  if (!x_bf16 || !rows || !cols || !ld_x || !gran || !q_out || !ld_q || !scale_inv_out)
+    return FP8BS_ERR_NULL;
+  QuantBatch b{};
+  int64_t total = 0;
+  for (int i = 0; i < count; ++i) {
+    const int64_t r = rows[i], c = cols[i];
+    if (gran[i] != FP8BS_BLOCK_1x128 && gran[i] != FP8BS_BLOCK_128x128) return FP8BS_ERR_ARG;
+    if (r < 0 || c < 0 || ld_x[i] < c || ld_q[i] < c) return FP8BS_ERR_SHAPE;
+    if (r > 0 && c > 0) {
+      if (!x_bf16[i] || !q_out[i] || !scale_inv_out[i]) return FP8BS_ERR_NULL;
+      if (r > INT64_MAX / ld_x[i]) return FP8BS_ERR_SHAPE;
+      if (!aligned4(scale_inv_out[i])) return FP8BS_ERR_ALIGN;
+    }
+    QuantTensor& t = b.t[b.count];
+    const int64_t nb_rows = gran[i] == FP8BS_BLOCK_1x128 ? ceil_div(r, kRows1) : ceil_div(r, 128);
+    const int64_t blocks = (r > 0 && c > 0) ? nb_rows * ceil_div(c, 128) : 0;
+    if (blocks == 0) continue;   // an empty tensor takes no workgroup
+    t.x = static_cast<const uint16_t*>(x_bf16[i]);
+    t.rows = r; t.cols = c; t.ld_x = ld_x[i];
+    t.q = static_cast<uint8_t*>(q_out[i]);
+    t.ld_q = ld_q[i];
+    t.s = scale_inv_out[i];
+    t.first = total;
+    t.gran = gran[i];
+    t.vec = aligned16(x_bf16[i]) && aligned16(q_out[i]) && ld_x[i] % 8 == 0 && ld_q[i] % 16 == 0;
+    total += blocks;
+    ++b.count;
+  }
+  if (total > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
+  if (total == 0) return FP8BS_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)total), block(kThreads);
+  const bool pow2 = mode == FP8BS_SCALE_POW2;
+  if (fmt == FP8BS_E4M3)
+    return pow2 ? launch(quant_batched_kernel<FP8BS_E4M3, true>, grid, block, st, b)
+                : launch(quant_batched_kernel<FP8BS_E4M3, false>, grid, block, st, b);
+  return pow2 ? launch(quant_batched_kernel<FP8BS_E5M2, true>, grid, block, st, b)
+              : launch(quant_batched_kernel<FP8BS_E5M2, false>, grid, block, st, b);
 }
 
 extern "C" size_t fp8_quantize_delayed_workspace_size(void) {

@@ -110,6 +110,26 @@ int fp8_quantize_blockwise(const void* x_bf16, int64_t rows, int64_t cols, int64
                            float* scale_inv_out, void* stream);
 
 /*
+ * Blockwise quantization of several bf16 matrices in one launch: tensor i is quantized exactly as
+ * fp8_quantize_blockwise(x_bf16[i], rows[i], cols[i], ld_x[i], fmt, gran[i], mode, q_out[i],
+ * ld_q[i], scale_inv_out[i]) would quantize it (same codes, same scale layout).  [P3] "Ganancias
+ * de rendimiento en el mundo real": the scales of every layer's weights are recalibrated each
+ * step, and the quantization kernels' overhead counts; one grid for all of a step's weights
+ * avoids a launch ramp and tail per tensor.
+ *   count: 0 .. 16 tensors; the per-tensor arguments are HOST arrays of count entries (the
+ *          pointers in them are device pointers); gran[i] is FP8BS_BLOCK_1x128 or
+ *          FP8BS_BLOCK_128x128; fmt and mode apply to every tensor.
+ * Empty tensors are skipped.  Every tensor is validated as in fp8_quantize_blockwise before
+ * anything is launched; the first error found is returned.  Errors: FP8BS_ERR_NULL,
+ * FP8BS_ERR_SHAPE, FP8BS_ERR_ALIGN, FP8BS_ERR_ARG (also count outside 0 .. 16),
+ * FP8BS_ERR_LAUNCH.
+ */
+int fp8_quantize_blockwise_batched(int count, const void* const* x_bf16, const int64_t* rows,
+                                   const int64_t* cols, const int64_t* ld_x, const int* gran,
+                                   int fmt, int mode, void* const* q_out, const int64_t* ld_q,
+                                   float* const* scale_inv_out, void* stream);
+
+/*
  * Columnwise quantization with transposed output: blocks of 128 consecutive rows of one column
  * of x[rows, cols] (pitch ld_x elements), codes written transposed to qt_out[cols, rows] (pitch
  * ld_qt bytes): qt_out[c][r] = enc(x[r][c] * s(r / 128, c)).  [P3] "El avance técnico": one

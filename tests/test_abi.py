@@ -226,6 +226,32 @@ def test_tiled_entry_validation():
         assert qtiled(tile, M=0) == bsq.OK
 
 
+def test_quantize_batched_validation():
+    """fp8_quantize_blockwise_batched checks every tensor before launching anything."""
+    import ctypes
+    lib = bsq.load()
+    P, I64, I32 = ctypes.c_void_p * 2, ctypes.c_int64 * 2, ctypes.c_int * 2
+
+    def call(n=2, x=(FAKE, FAKE), rows=(4, 8), cols=(256, 128), ldx=(256, 128), gran=(0, 1),
+             fmt=0, mode=0, q=(FAKE, FAKE), ldq=(256, 128), s=(FAKE, FAKE)):
+        return lib.fp8_quantize_blockwise_batched(n, P(*x), I64(*rows), I64(*cols), I64(*ldx),
+                                                  I32(*gran), fmt, mode, P(*q), I64(*ldq), P(*s),
+                                                  None)
+
+    assert call(n=-1) == bsq.ERR_ARG and call(n=17) == bsq.ERR_ARG
+    assert call(fmt=2) == bsq.ERR_ARG and call(mode=2) == bsq.ERR_ARG
+    assert call(gran=(0, 2)) == bsq.ERR_ARG            # per tensor: the delayed entry point
+    assert call(rows=(4, -1)) == bsq.ERR_SHAPE
+    assert call(ldx=(256, 100)) == bsq.ERR_SHAPE
+    assert call(ldq=(255, 128)) == bsq.ERR_SHAPE
+    assert call(x=(FAKE, None)) == bsq.ERR_NULL
+    assert call(s=(FAKE, FAKE + 2)) == bsq.ERR_ALIGN
+    assert call(n=0) == bsq.OK
+    assert call(rows=(0, 0), x=(None, None)) == bsq.OK   # empty tensors: nothing to launch
+    assert lib.fp8_quantize_blockwise_batched(1, None, None, None, None, None, 0, 0, None, None,
+                                              None, None) == bsq.ERR_NULL
+
+
 def test_delayed_noalloc_validation():
     """fp8_quantize_delayed_noalloc validates like fp8_quantize_delayed (no workspace argument);
     invalid calls return before any device is touched."""

@@ -174,3 +174,46 @@ def test_cast_all_fp32_patterns(gpu, fmt):
         del x32
         want = oracle.encode_bit_range(fmt, base, chunk)
         assert_bytes_equal(q, want, f"cast chunk {base:#x}")
+
+
+# ----------------------------------------------------------------------------- several tensors
+# fp8_quantize_blockwise_batched: one launch for several tensors ("NVIDIA NeMo RL ...", section
+# "Ganancias de rendimiento en el mundo real": every layer's weight scales are recalibrated each
+# step); each tensor's codes and scales equal the oracle's, bit for bit.
+
+@pytest.mark.parametrize("fmt,mode", [(bsq.E4M3, bsq.SCALE_FP32), (bsq.E5M2, bsq.SCALE_POW2)])
+def test_batched_mixed_tensors(gpu, fmt, mode):
+    shapes = [(300, 260), (0, 128), (128, 128), (1, 7), (513, 1000), (64, 4096), (129, 0), (256, 384)]
+    grans = [bsq.BLOCK_128x128, bsq.BLOCK_1x128, bsq.BLOCK_1x128, bsq.BLOCK_128x128,
+             bsq.BLOCK_1x128, bsq.BLOCK_128x128, bsq.BLOCK_1x128, bsq.BLOCK_1x128]
+    xs_cpu = [synth.student_t(s, 3.0, i, f"batched/x{i}") if s[0] * s[1] else
+              torch.zeros(s, dtype=torch.bfloat16) for i, s in enumerate(shapes)]
+    xs = []
+    for i, x in enumerate(xs_cpu):
+        if i % 3 == 2:       # an odd row pitch: the unaligned path
+            big = torch.zeros((x.shape[0], x.shape[1] + 3), dtype=torch.bfloat16)
+            big[:, :x.shape[1]] = x
+            xs.append(big.cuda()[:, :x.shape[1]])
+        else:
+            xs.append(x.cuda())
+    qs, ss = gpu.quantize_blockwise_batched(xs, grans, fmt, mode)
+    torch.cuda.synchronize()
+    for i, (x, gran) in enumerate(zip(xs_cpu, grans)):
+        if x.numel() == 0:
+            continue
+        qo, so = oracle.quantize_blockwise(bits(x), fmt, gran, mode)
+        assert_bytes_equal(qs[i].cpu().numpy(), qo, f"batched codes {i} {tuple(x.shape)}")
+        assert_bytes_equal(f32_bits(gpu_scales_to_logical(ss[i], gran)), f32_bits(so),
+                           f"batched scales {i}")
+
+
+def test_batched_equals_single_on_8b_weights(gpu):
+    """The four Llama-3.1-8B weights in one launch give what four single launches give."""
+    ws = [synth.normal((n, k), 0.02, 0, f"batched8b/W{n}x{k}").cuda()
+          for k, n in [(4096, 6144), (4096, 4096), (4096, 28672), (14336, 4096)]]
+    grans = [bsq.BLOCK_128x128] * 4
+    qs, ss = gpu.quantize_blockwise_batched(ws, grans, bsq.E4M3)
+    for w, q, s in zip(ws, qs, ss):
+        q1, s1 = gpu.quantize_blockwise(w, bsq.E4M3, bsq.BLOCK_128x128)
+        torch.cuda.synchronize()
+        assert torch.equal(q, q1) and torch.equal(s.view(torch.int32), s1.view(torch.int32))
