@@ -67,6 +67,7 @@ struct GemmParams {
   int64_t ldcq;
   float* cqs;
   int cq_vec;         // 4-byte code stores are aligned
+  int cq_vec16;       // 16-byte code stores are aligned
   // grouped GEMM only
   const int64_t* offsets;
   int num_groups;
@@ -443,6 +444,12 @@ __device__ __forceinline__ void quantize_out(const GemmParams& p, uint8_t* smem,
   }
   __syncthreads();
   const int64_t blk = (n0 >> 7) + (wn >> 1);   // 128-column block of this wave
+  // Codes leave through the wave's epilogue region when 16-byte stores are aligned: the 16 rows
+  // of a piece as 64-byte row segments, 16 rows per store instruction, instead of 4 bytes per
+  // lane and piece.
+  constexpr int kQPitch = 80;
+  const bool staged = C::kStagedEpi && p.cq_vec16;
+  uint8_t* region = smem + C::kEpi + w * C::kEpiWaveBytes;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int row = wm * C::kWTM + 16 * j + li;
@@ -450,11 +457,9 @@ __device__ __forceinline__ void quantize_out(const GemmParams& p, uint8_t* smem,
     const uint32_t a = max(s_amax[(wn & ~1) * BM + row], s_amax[(wn | 1) * BM + row]);
     const float s = scale_from_amax_bits<QF, QP>(a);
     const bool finite = a < 0x7F80u;
-    if (m >= m_end) continue;
-    uint8_t* qrow = p.Cq + m * p.ldcq;
+    uint32_t codes[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int64_t n = n0 + wn * C::kWTN + 16 * i + 4 * g;
       float y0 = bf16_lo(bv[i][j][0]) * s, y1 = bf16_hi(bv[i][j][0]) * s;
       float y2 = bf16_lo(bv[i][j][1]) * s, y3 = bf16_hi(bv[i][j][1]) * s;
       if (!finite) {
@@ -464,17 +469,45 @@ __device__ __forceinline__ void quantize_out(const GemmParams& p, uint8_t* smem,
         y2 = __builtin_amdgcn_fmed3f(y2, -F, F);
         y3 = __builtin_amdgcn_fmed3f(y3, -F, F);
       }
-      uint32_t code = cvt4<QF>(y0, y1, y2, y3);
-      if (!finite) code = patch_nan_pair(patch_nan_pair(code, bv[i][j][0], 0), bv[i][j][1], 1);
-      if (p.cq_vec && n + 4 <= p.N) {
-        *reinterpret_cast<uint32_t*>(qrow + n) = code;
-      } else {
+      codes[i] = cvt4<QF>(y0, y1, y2, y3);
+      if (!finite) codes[i] = patch_nan_pair(patch_nan_pair(codes[i], bv[i][j][0], 0), bv[i][j][1], 1);
+    }
+    if (staged) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (n + e < p.N) qrow[n + e] = (uint8_t)(code >> (8 * e));
+      for (int i = 0; i < NI; ++i)
+        *reinterpret_cast<uint32_t*>(region + li * kQPitch + 16 * i + 4 * g) = codes[i];
+      wait_lds();
+      const int r = lane >> 2, c = lane & 3;
+      const uint4 d = *reinterpret_cast<const uint4*>(region + r * kQPitch + 16 * c);
+      const int64_t mr = m0 + wm * C::kWTM + 16 * j + r;
+      const int64_t n = n0 + wn * C::kWTN + 16 * c;
+      if (mr < m_end) {
+        uint8_t* qrow = p.Cq + mr * p.ldcq;
+        if (n + 16 <= p.N) {
+          __builtin_nontemporal_store(u32x4{d.x, d.y, d.z, d.w}, reinterpret_cast<u32x4*>(qrow + n));
+        } else {
+          const uint32_t wd[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (n + e < p.N) qrow[n + e] = (uint8_t)(wd[e >> 2] >> (8 * (e & 3)));
+        }
+      }
+      wait_lds();   // (the next piece rewrites the region)
+    } else if (m < m_end) {
+      uint8_t* qrow = p.Cq + m * p.ldcq;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int64_t n = n0 + wn * C::kWTN + 16 * i + 4 * g;
+        if (p.cq_vec && n + 4 <= p.N) {
+          *reinterpret_cast<uint32_t*>(qrow + n) = codes[i];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < p.N) qrow[n + e] = (uint8_t)(codes[i] >> (8 * e));
+        }
       }
     }
-    if (g == 0 && (wn & 1) == 0 && blk * 128 < p.N) p.cqs[blk * p.M + m] = 1.0f / s;
+    if (m < m_end && g == 0 && (wn & 1) == 0 && blk * 128 < p.N) p.cqs[blk * p.M + m] = 1.0f / s;
   }
 }
 

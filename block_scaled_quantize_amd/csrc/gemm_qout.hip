@@ -35,6 +35,7 @@ int gemm_qout(int tile, int64_t M, int64_t N, int64_t K, const void* A, int64_t 
   p.ldcq = ldcq;
   p.cqs = cq_scale_inv;
   p.cq_vec = aligned4(Cq) && ldcq % 4 == 0;
+  p.cq_vec16 = aligned16(Cq) && ldcq % 16 == 0;
   constexpr int E4 = FP8BS_E4M3, FP = FP8BS_FPROP;
   const bool pow2_out = mode_out == FP8BS_SCALE_POW2;
   // output codes: E4M3, 1 + 2 * format + power-of-2
