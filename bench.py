@@ -231,7 +231,7 @@ def bench_llama8b(args, pow2: bool = False):
                       traffic=traffic["bytes"], traffic_unit="HBM bytes per launch",
                       traffic_algorithmic=traffic["algorithmic"], traffic_source=traffic["source"],
                       # the tile chooser takes the 256x256 tile for all four shapes
-                      kernel="gemm_kernel<Cfg<256,256,2,4>,FPROP,E4M3,E4M3,%s>" % ("hw" if pow2 else "fold"),
+                      kernel="gemm_persistent_kernel<Cfg<256,256,2,4>,FPROP,E4M3,E4M3,%s>" % ("hw" if pow2 else "fold"),
                       per_launch_flops=mean_launch_flops, mean_launch_us=round(mean_launch_ms * 1e3, 2)),
         gemm_only_tflops=round(sum(gemm_flops) / sum(gemm_ms) / 1e9, 1),
         quant_gbps=round(q_bytes / q_ms / 1e6, 1),
@@ -584,7 +584,7 @@ def bench_backward(args):
                 roofline=dict(bound="mfma", achieved=round(achieved, 1), peak=FP8_PEAK_TFLOPS,
                               unit="TFLOP/s", frac=round(achieved / FP8_PEAK_TFLOPS, 4),
                               traffic=None,
-                              kernel="gemm_kernel<Cfg<256,256,2,4>,DGRAD|WGRAD,E5M2,E4M3,tensor>",
+                              kernel="gemm_persistent_kernel<Cfg<256,256,2,4>,DGRAD|WGRAD,E5M2,E4M3,tensor>",
                               mean_launch_us=round(gemm_ms / (2 * len(layers)) * 1e3, 2)),
                 delayed_quant=dict(bound="hbm", achieved_gbps=round(q_bytes / q_ms / 1e6, 1),
                                    peak_gbps=HBM_PEAK_GBPS,
@@ -671,7 +671,7 @@ def bench_backward_blockwise(args):
                 roofline=dict(bound="mfma", achieved=round(achieved, 1), peak=FP8_PEAK_TFLOPS,
                               unit="TFLOP/s", frac=round(achieved / FP8_PEAK_TFLOPS, 4),
                               traffic=None,
-                              kernel="gemm_kernel<Cfg<256,256,2,4>,FPROP,E4M3,E4M3,%s> (wgrad)"
+                              kernel="gemm_persistent_kernel<Cfg<256,256,2,4>,FPROP,E4M3,E4M3,%s> (wgrad)"
                                      % ("hw-rows" if args.pow2 else "fold-rows"),
                               mean_launch_us=round(float(np.mean(wg_ms)) * 1e3, 2)),
                 layers=per)
