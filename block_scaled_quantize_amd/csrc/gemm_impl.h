@@ -145,13 +145,21 @@ struct Cfg {
 // ------------------------------------------------------------------ low-level helpers
 __device__ __forceinline__ u32x4 make_rsrc(const void* base, uint64_t nbytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t n = nbytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)nbytes;
+  const uint32_t n = (uint32_t)(nbytes >> 32) != 0u ? 0xFFFFFFFFu : (uint32_t)nbytes;
   u32x4 r;
   r.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
   r.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));   // stride 0
   r.z = __builtin_amdgcn_readfirstlane(n);
   r.w = 0x00020000u;                                           // raw 32-bit data format
   return r;
+}
+
+// The descriptor size of a DMA source with avail readable bytes from its base (none when
+// avail <= 0 or the block is not live), clamped to 32 bits.
+__device__ __forceinline__ uint64_t dma_bytes(int64_t avail, bool live) {
+  const uint32_t hi = (uint32_t)((uint64_t)avail >> 32), lo = (uint32_t)avail;
+  const uint32_t n = (int32_t)hi < 0 ? 0u : (hi != 0u ? 0xFFFFFFFFu : lo);
+  return live ? n : 0u;
 }
 
 // 16 bytes per lane from buffer offset voff to LDS address lds + 16 * lane.  Offsets at or past
@@ -201,62 +209,74 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>(p);
 }
 
-// Per-lane parts of the fragment addresses, computed once per tile.  A piece's rows (K-major)
-// or columns (MN-major) start at a multiple of 16, u, the same in every lane; the swizzle then
-// depends on the lane only, and the piece's address is the lane's base plus 128 u (K-major: an
-// immediate offset for constant u) or the base XOR the piece's chunk (MN-major).
+// Per-lane parts of the fragment addresses of one wave's pieces of a tile side, computed once
+// per tile.  The wave's pieces start at row (K-major) or column (MN-major) u0 and follow every
+// 16; the swizzle then depends on the lane only.  K-major: piece r is at the lane's address
+// + 2048 r, an immediate offset of the LDS read.  MN-major (tile [halves][128 k][128 columns],
+// a wave's columns inside one half): piece r is at the lane's address XOR 16 r, the chunk bits
+// 4..6 (u0 % 128 is a multiple of the wave's column span, so it and 16 r share no bit).
 template <bool KMAJOR>
 struct FragBase {
-  int a[KMAJOR ? 2 : 4];
+  uint32_t a[KMAJOR ? 2 : 4];
 };
-__device__ __forceinline__ FragBase<true> frag_base_k(int li, int g) {
+__device__ __forceinline__ FragBase<true> frag_base_k(int li, int g, int u0) {
   const int sw = swz_k(li);
-  return FragBase<true>{{li * 128 + (((2 * g) ^ sw) << 4), li * 128 + (((2 * g + 1) ^ sw) << 4)}};
+  const uint32_t r = (uint32_t)(u0 + li) * 128u;
+  return FragBase<true>{{r + ((((2 * g) ^ sw) << 4)), r + ((((2 * g + 1) ^ sw) << 4))}};
 }
-__device__ __forceinline__ FragBase<false> frag_base_mn(int li, int g) {
+__device__ __forceinline__ FragBase<false> frag_base_mn(int li, int g, int u0) {
   FragBase<false> b;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int k = 32 * g + 8 * t + (li >> 1);
-    b.a[t] = (k * 128 + 8 * (li & 1)) | (swz_mn(k) << 4);   // bits 4..6 of k * 128 + ... are 0
+    // bits 4..6 of k * 128 + 8 (li & 1) are 0
+    const uint32_t lane = (uint32_t)((k * 128 + 8 * (li & 1)) | (swz_mn(k) << 4));
+    b.a[t] = (lane ^ (uint32_t)(u0 & 0x70)) + (uint32_t)(u0 >> 7) * 16384u;
   }
   return b;
 }
-// The 32-byte MFMA fragment of lane (li, g) for the piece at u (u % 16 == 0, wave-uniform):
-// bytes k = 32g .. 32g+31 of tile row u + li (K-major tile), or of column u + li of an MN-major
-// tile ([halves][128 k][128 columns]), gathered by four 8x8 byte transposes across lanes (source
-// lane 2j + h of each 16-lane group points at row k0 + j, bytes 8h .. 8h + 7 of the chunk).
-__device__ __forceinline__ v8i frag_k_at(const uint8_t* tile, const FragBase<true>& b, int u) {
-  const uint8_t* base = tile + u * 128;
-  const uint4 lo = *reinterpret_cast<const uint4*>(base + b.a[0]);
-  const uint4 hi = *reinterpret_cast<const uint4*>(base + b.a[1]);
-  v8i v;
-  v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-  v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-  return v;
+template <bool KMAJOR>
+__device__ __forceinline__ FragBase<KMAJOR> frag_base(int li, int g, int u0) {
+  if constexpr (KMAJOR) return frag_base_k(li, g, u0);
+  else return frag_base_mn(li, g, u0);
 }
-__device__ __forceinline__ v8i frag_mn_at(const uint8_t* tile, const FragBase<false>& b, int u) {
-  const uint8_t* half = tile + (u >> 7) * 16384;
-  const int chunk = ((u & 127) >> 4) << 4;
-  v8i v;
+// The bases in the LDS tile at address tile_lds (a multiple of 128, so that the MN-major XOR
+// stays inside the lane's part), made opaque so that the compiler keeps one address per base
+// and reaches the pieces by immediate offsets (K-major) or one XOR (MN-major).
+template <bool KMAJOR>
+__device__ __forceinline__ FragBase<KMAJOR> frag_at_tile(FragBase<KMAJOR> b, uint32_t tile_lds) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const uint8_t* p = half + (b.a[t] ^ chunk);
-    v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)p);
-    v[2 * t] = r.x;
-    v[2 * t + 1] = r.y;
+  for (int t = 0; t < (KMAJOR ? 2 : 4); ++t) {
+    b.a[t] += tile_lds;
+    asm volatile("" : "+v"(b.a[t]));
+  }
+  return b;
+}
+typedef __attribute__((address_space(3))) const u32x4 lds_u4_t;
+typedef __attribute__((address_space(3))) const float lds_f32_t;
+__device__ __forceinline__ float lds_f32(uint32_t a) { return *(lds_f32_t*)a; }
+// The 32-byte MFMA fragment of lane (li, g) for the wave's piece r: bytes k = 32g .. 32g+31 of
+// the piece's row li (K-major tile), or of its column li in an MN-major tile, gathered by four
+// 8x8 byte transposes across lanes (source lane 2j + h of each 16-lane group points at row
+// k0 + j, bytes 8h .. 8h + 7 of the chunk).
+template <bool KMAJOR>
+__device__ __forceinline__ v8i frag_piece(const FragBase<KMAJOR>& b, int r) {
+  v8i v;
+  if constexpr (KMAJOR) {
+    const u32x4 lo = *(lds_u4_t*)(b.a[0] + 2048u * (uint32_t)r);
+    const u32x4 hi = *(lds_u4_t*)(b.a[1] + 2048u * (uint32_t)r);
+    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+    v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (__attribute__((address_space(3))) v2i*)(b.a[t] ^ (16u * (uint32_t)r)));
+      v[2 * t] = x.x;
+      v[2 * t + 1] = x.y;
+    }
   }
   return v;
-}
-template <bool KMAJOR>
-__device__ __forceinline__ v8i frag_at(const uint8_t* tile, const FragBase<KMAJOR>& b, int u) {
-  if constexpr (KMAJOR) return frag_k_at(tile, b, u);
-  else return frag_mn_at(tile, b, u);
-}
-template <bool KMAJOR>
-__device__ __forceinline__ FragBase<KMAJOR> frag_base(int li, int g) {
-  if constexpr (KMAJOR) return frag_base_k(li, g);
-  else return frag_base_mn(li, g);
 }
 
 
@@ -625,7 +645,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
         base = p.A + k0 * p.lda + tm0;
         avail = (K - k0) * p.lda - tm0;
       }
-      d.x = make_rsrc(base, (avail > 0 && live) ? (uint64_t)avail : 0);
+      d.x = make_rsrc(base, dma_bytes(avail, live));
     }
     {
       const uint8_t* base;
@@ -637,25 +657,25 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
         base = tBw + k0 * p.ldb + tn0;
         avail = (K - k0) * p.ldb - tn0;
       }
-      d.w = make_rsrc(base, (avail > 0 && live) ? (uint64_t)avail : 0);
+      d.w = make_rsrc(base, dma_bytes(avail, live));
     }
     if constexpr (STAGED) {
       const int64_t offa = kk * p.sa_ks + (tm0 >> p.sa_rshift) * p.sa_rs;
       const int64_t lefta = p.sa_bytes - offa * 4;
-      d.sa = make_rsrc(p.sa + offa, (lefta > 0 && live) ? (uint64_t)lefta : 0);
+      d.sa = make_rsrc(p.sa + offa, dma_bytes(lefta, live));
       const int64_t offb = kk * p.sb_ks + (ROWS ? tn0 : (tn0 >> 7)) * p.sb_rs;
       const int64_t leftb = sb_bytes - offb * 4;
-      d.sb = make_rsrc(tsb + offb, (leftb > 0 && live) ? (uint64_t)leftb : 0);
+      d.sb = make_rsrc(tsb + offb, dma_bytes(leftb, live));
     }
     return d;
   };
   auto dma_part = [&](const BlockDma& d, int q) {
     if (q < C::kXLoads) {
-      dma16(d.x, xoff[q], __builtin_amdgcn_readfirstlane(d.sbase + (w * C::kXLoads + q) * 1024));
+      dma16(d.x, xoff[q], __builtin_amdgcn_readfirstlane(d.sbase + (wu * C::kXLoads + q) * 1024));
     } else if (q < C::kXLoads + C::kWLoads) {
       const int qw = q - C::kXLoads;
       dma16(d.w, woff[qw],
-            __builtin_amdgcn_readfirstlane(d.sbase + C::kXBytes + (w * C::kWLoads + qw) * 1024));
+            __builtin_amdgcn_readfirstlane(d.sbase + C::kXBytes + (wu * C::kWLoads + qw) * 1024));
     } else if (kOneScale && q == C::kXLoads + C::kWLoads) {
       // Scales of the K block: one activation word per tile row (waves [0, kSaWaves)) and the
       // weight words (the weight-scale loaders); every wave issues one such instruction, so
@@ -664,17 +684,16 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
       const uint32_t sbdst = d.sbase + C::kXBytes + C::kWBytes + BM * 4 +
                              (ROWS ? (wu - C::kSbRowWave0) * 256 : 0);
       dma4(sa_loader ? d.sa : d.sb, sa_loader ? saoff : (sb_loader ? sboff : 0xFFFFFFFFu),
-           __builtin_amdgcn_readfirstlane(
-               sa_loader ? d.sbase + C::kXBytes + C::kWBytes + wu * 256
-                         : (sb_loader ? sbdst : lds0 + C::kDummy)));
+           __builtin_amdgcn_readfirstlane(sa_loader ? d.sbase + C::kXBytes + C::kWBytes + wu * 256
+                                                    : (sb_loader ? sbdst : lds0 + C::kDummy)));
     } else if (q == C::kXLoads + C::kWLoads) {
       // (two scale instructions per wave: activation words, then weight words)
       dma4(d.sa, sa_loader ? saoff : 0xFFFFFFFFu,
-           __builtin_amdgcn_readfirstlane(sa_loader ? d.sbase + C::kXBytes + C::kWBytes + w * 256
+           __builtin_amdgcn_readfirstlane(sa_loader ? d.sbase + C::kXBytes + C::kWBytes + wu * 256
                                                     : lds0 + C::kDummy));
     } else {
       const uint32_t dst = d.sbase + C::kXBytes + C::kWBytes + BM * 4 +
-                           (ROWS ? (w - C::kSbRowWave0) * 256 : 0);
+                           (ROWS ? (wu - C::kSbRowWave0) * 256 : 0);
       dma4(d.sb, sb_loader ? sboff : 0xFFFFFFFFu,
            __builtin_amdgcn_readfirstlane(sb_loader ? dst : lds0 + C::kDummy));
     }
@@ -714,12 +733,20 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
       __syncthreads();
     }
   };
-  // Fragment address bases (re-declared opaque at every block, so that the compiler computes a
-  // piece's address where it is used instead of keeping every piece's address live).
-  FragBase<XK> xb = frag_base<XK>(li, g);
-  FragBase<WK> wb = frag_base<WK>(li, g);
+  // Fragment address bases of the wave's pieces (per tile; frag_at_tile adds a stage's address
+  // once per block), and the byte offset of the lane's first activation scale in a stage.
+  const FragBase<XK> xb = frag_base<XK>(li, g, wm * C::kWTM);
+  const FragBase<WK> wb = frag_base<WK>(li, g, wn * C::kWTN);
+  const uint32_t sc_lane = (uint32_t)(C::kXBytes + C::kWBytes + 4 * (wm * C::kWTM + li));
   auto scales_of = [&](const uint8_t* st) {
     return reinterpret_cast<const float*>(st + C::kXBytes + C::kWBytes);
+  };
+  // The lane's activation-scale address in a stage (opaque, like the fragment bases): piece r's
+  // scale is at + 64 r.
+  auto scale_base = [&](const uint8_t* st) {
+    uint32_t a = lds_addr(st) + sc_lane;
+    asm volatile("" : "+v"(a));
+    return a;
   };
   // First m piece of a block: its fragment, and the activation scale c of its rows (the fold's
   // factor is c * sbv; the multiply is left to the end of the piece that precedes the piece's
@@ -727,16 +754,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
   // weight scale sbv (one per wave).
   auto first_x = [&](const uint8_t* st, v8i& xf, float& c, float& sbv) {
     const float* sat = scales_of(st);
-    xf = frag_at<XK>(st, xb, wm * C::kWTM);
-    if constexpr (FOLD && !ROWS) {
-      sbv = sat[BM + (wn * C::kWTN) / 128];
-      c = sat[wm * C::kWTM + li];
-    } else if constexpr (HW && !ROWS) {
-      sbv = sat[BM + (wn * C::kWTN) / 128];
-      c = sat[wm * C::kWTM + li];
-    } else if constexpr (ROWS) {
-      c = sat[wm * C::kWTM + li];
-    }
+    xf = frag_piece<XK>(frag_at_tile<XK>(xb, lds_addr(st)), 0);
+    if constexpr ((FOLD || HW) && !ROWS) sbv = sat[BM + (wn * C::kWTN) / 128];
+    if constexpr (FOLD || HW) c = lds_f32(scale_base(st));
   };
   // 1x128 weight scales of a block: fold, those of this lane's 4 output columns; MFMA, that of
   // its A-operand row.
@@ -755,8 +775,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
       for (int i = 0; i < NI; ++i) wbr[i] = e8m0_of(sat[BM + wn * C::kWTN + 16 * i + li]);
     }
   };
-  auto w_fragment = [&](const uint8_t* st, int i) {
-    return frag_at<WK>(st + C::kXBytes, wb, wn * C::kWTN + 16 * i);
+  // The weight-side bases of a stage: piece i by frag_piece(wbase, i).
+  auto w_bases = [&](const uint8_t* st) {
+    return frag_at_tile<WK>(wb, lds_addr(st) + C::kXBytes);
   };
 
   const bool prefetched = PF && cy.prefetched;   // block 0 was issued by the previous tile
@@ -777,8 +798,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
     const uint8_t* st = stage_ptr(0);
     first_x(st, xf, ccur, sbv);
     if constexpr (FOLD && !ROWS) ccur *= sbv;
+    const FragBase<WK> ws = w_bases(st);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) wf[i] = w_fragment(st, i);
+    for (int i = 0; i < NI; ++i) wf[i] = frag_piece<WK>(ws, i);
     fold_row_scales(st, sbr);
     mfma_row_scales(st, wbr);
     if constexpr (kBurst) {
@@ -798,12 +820,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
     constexpr bool PREP = decltype(prep_tag)::value;
     const uint8_t* st = stage_ptr(kb);
     const uint8_t* stn = stage_ptr(kb + 1);
-    const float* sat = scales_of(st);
     const int wbyte = (HW && !ROWS) ? e8m0_of(sbv) : 0;   // weight scale of the block
-#pragma unroll
-    for (int t = 0; t < (XK ? 2 : 4); ++t) asm volatile("" : "+v"(xb.a[t]));
-#pragma unroll
-    for (int t = 0; t < (WK ? 2 : 4); ++t) asm volatile("" : "+v"(wb.a[t]));
+    const FragBase<XK> xs = frag_at_tile<XK>(xb, lds_addr(st));
+    const uint32_t scs = scale_base(st);
+    FragBase<WK> wsn;
     // DMA of block kb + kStages - 1 (into the slot of block kb - 1): its first NI instructions
     // were issued at the previous hand-over, the rest go here (in the last block only when it
     // is the next tile's first block, PF).  DMA of block kb + kStages: started at this block's
@@ -814,12 +834,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
     if constexpr (CONT) dcont = block_dma(kb + C::kStages - 1, std::bool_constant<!TURN>{});
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int mrow = wm * C::kWTM + 16 * j + li;
       v8i xnext;
       float cnext = 0.0f;
       if (j + 1 < NJ) {
-        xnext = frag_at<XK>(st, xb, wm * C::kWTM + 16 * j + 16);
-        if constexpr (FOLD || HW) cnext = sat[mrow + 16];   // (fold: times sbv at the end)
+        xnext = frag_piece<XK>(xs, j + 1);
+        if constexpr (FOLD || HW) cnext = lds_f32(scs + 64u * (uint32_t)(j + 1));   // (fold: times sbv at the end)
       }
       const bool turn = TURN && j == NJ - 1;   // block kb + 1 is published before this piece
       if (turn) {
@@ -830,6 +849,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
         if constexpr (PREP) prepare(kb + 1);
         if constexpr (!kBurst) dturn = block_dma(kb + C::kStages, std::bool_constant<PF && PREP>{});
         first_x(stn, xnext, cnext, sbv);
+        wsn = w_bases(stn);
         __builtin_amdgcn_sched_barrier(0);
       }
       const int xbyte = HW ? e8m0_of(ccur) : 0;   // activation scale of this lane's row
@@ -864,7 +884,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
                                                                        FA, 0, 0, 0, 0);
         }
         if (turn) {
-          wf[i] = w_fragment(stn, i);
+          wf[i] = frag_piece<WK>(wsn, i);
           if (!kBurst && i < kPerStage) dma_part(dturn, i);
         } else if constexpr (CONT) {
           const int q = NI + j * NI + i;
@@ -967,7 +987,7 @@ __device__ __forceinline__ void tile_of(int id, int tiles_m, int tiles_n, int& t
 
 template <class C, int LAYOUT, int FA, int FB, int SM, int QO = 0>
 __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  extern __shared__ __attribute__((aligned(128))) uint8_t smem[];
   int tm, tn;
   tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
   const int m0 = tm * C::BM;
@@ -995,7 +1015,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
 // the epilogue's stores.
 template <class C, int LAYOUT, int FA, int FB, int SM>
 __global__ __launch_bounds__(C::kThreads, 1) void gemm_persistent_kernel(GemmParams p) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  extern __shared__ __attribute__((aligned(128))) uint8_t smem[];
   static_assert(C::kStages == 2, "persistent dense GEMM: two-stage tiles");
   const int total = p.tiles_m * p.tiles_n;
   int id = blockIdx.x;
@@ -1055,7 +1075,7 @@ __device__ __forceinline__ int block_scan(int v, int& carry, int* s_wave) {
 
 template <class C, int FA, int FB, int SM>
 __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(GemmParams p) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  extern __shared__ __attribute__((aligned(128))) uint8_t smem[];
   __shared__ int s_prefix[kMaxGroups + 1];
   __shared__ int s_lo[kMaxGroups + 1];   // group bounds, clamped and non-decreasing (M < 2^31)
   __shared__ int s_wave_sum[C::kWaves];
