@@ -162,6 +162,21 @@ __device__ __forceinline__ uint64_t dma_bytes(int64_t avail, bool live) {
   return live ? n : 0u;
 }
 
+// Descriptor of a K-major operand's K block at byte offset k0 from the tile's K block 0: av0 = the
+// bytes readable from the tile's K block 0, clamped to 32 bits once per tile (0 when none); the
+// block's size is av0 - k0, in 32 bits.  The same reads as the exact size: a block's DMA stays
+// below 256 rows of the pitch (< 2^31), and a clamped size minus k0 (< 2^23) stays above that.
+// A nonzero av0 is at least one row's pitch, which is at least K > k0 for every block inside K,
+// so the subtraction does not wrap.  Scale arrays (below 4 GiB, never clamped) use the same form:
+// a tile's live K blocks read words of the array.
+__device__ __forceinline__ uint32_t clamp_bytes(int64_t v) {
+  return v <= 0 ? 0u : (v >= (int64_t)0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)v);
+}
+__device__ __forceinline__ u32x4 make_rsrc_k(const void* base, uint32_t av0, uint32_t k0,
+                                             bool live) {
+  return make_rsrc(base, (live && av0 != 0u) ? av0 - k0 : 0u);
+}
+
 // 16 bytes per lane from buffer offset voff to LDS address lds + 16 * lane.  Offsets at or past
 // the descriptor's size read as zero.
 __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t voff, uint32_t lds) {
@@ -611,6 +626,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
   // block after the hand-over piece's MFMAs measured faster.
   constexpr bool kBurst = ROWS;
   static_assert(kPerStage - NI <= (NJ - 1) * NI, "every DMA part precedes the next turn");
+  // readable bytes of the K-major sides from the tile's K block 0
+  const uint32_t x_av0 = __builtin_amdgcn_readfirstlane(XK ? clamp_bytes((m_end - m0) * p.lda) : 0u);
+  const uint32_t w_av0 = __builtin_amdgcn_readfirstlane(WK ? clamp_bytes((p.N - n0) * p.ldb) : 0u);
+  // ... and of the scale arrays from the tile's first scale word
+  const uint32_t sa_av0 = __builtin_amdgcn_readfirstlane(
+      STAGED ? clamp_bytes(p.sa_bytes - 4 * ((m0 >> p.sa_rshift) * p.sa_rs)) : 0u);
+  const uint32_t sb_av0 = __builtin_amdgcn_readfirstlane(
+      STAGED ? clamp_bytes(sb_bytes - 4 * ((ROWS ? n0 : (n0 >> 7)) * p.sb_rs)) : 0u);
   // DMA of one K block: the buffer descriptors (empty for blocks past the last: they read
   // zeros into a slot no block reads) and the LDS stage; dma_part(d, q) issues this wave's q-th
   // DMA instruction of the block (compile-time q once the callers' loops are unrolled).
@@ -624,7 +647,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
   auto block_dma = [&](int kb, auto nx_tag) {
     constexpr bool NX = decltype(nx_tag)::value;
     BlockDma d;
-    d.sbase = lds0 + ((kb + st0) % C::kStages) * C::kStage;
+    d.sbase = lds0 + ((uint32_t)(kb + st0) % C::kStages) * C::kStage;
     const bool live = NX ? pf_live : kb < nkb;
     int64_t tm0 = m0, tme = m_end, tn0 = n0, kk = kb;
     const uint8_t* tBw = Bw;
@@ -637,35 +660,33 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
     const int64_t k0 = kk * 128;
     {
       const uint8_t* base;
-      int64_t avail;
       if constexpr (XK) {   // rows past the tile's m_end read as zero
         base = p.A + tm0 * p.lda + k0;
-        avail = (tme - tm0) * p.lda - k0;
+        d.x = make_rsrc_k(base, NX ? clamp_bytes((tme - tm0) * p.lda) : x_av0, (uint32_t)k0, live);
       } else {
         base = p.A + k0 * p.lda + tm0;
-        avail = (K - k0) * p.lda - tm0;
+        d.x = make_rsrc(base, dma_bytes((K - k0) * p.lda - tm0, live));
       }
-      d.x = make_rsrc(base, dma_bytes(avail, live));
     }
     {
       const uint8_t* base;
-      int64_t avail;
       if constexpr (WK) {
         base = tBw + tn0 * p.ldb + k0;
-        avail = (p.N - tn0) * p.ldb - k0;
+        d.w = make_rsrc_k(base, NX ? clamp_bytes((p.N - tn0) * p.ldb) : w_av0, (uint32_t)k0, live);
       } else {
         base = tBw + k0 * p.ldb + tn0;
-        avail = (K - k0) * p.ldb - tn0;
+        d.w = make_rsrc(base, dma_bytes((K - k0) * p.ldb - tn0, live));
       }
-      d.w = make_rsrc(base, dma_bytes(avail, live));
     }
     if constexpr (STAGED) {
-      const int64_t offa = kk * p.sa_ks + (tm0 >> p.sa_rshift) * p.sa_rs;
-      const int64_t lefta = p.sa_bytes - offa * 4;
-      d.sa = make_rsrc(p.sa + offa, dma_bytes(lefta, live));
-      const int64_t offb = kk * p.sb_ks + (ROWS ? tn0 : (tn0 >> 7)) * p.sb_rs;
-      const int64_t leftb = sb_bytes - offb * 4;
-      d.sb = make_rsrc(tsb + offb, dma_bytes(leftb, live));
+      // (scale arrays are below 4 GiB: the bytes from the tile's first scale word, less the
+      // K block's offset, in 32 bits; see make_rsrc_k)
+      const int64_t rowa = (tm0 >> p.sa_rshift) * p.sa_rs;
+      const uint32_t sa_av = NX ? clamp_bytes(p.sa_bytes - 4 * rowa) : sa_av0;
+      d.sa = make_rsrc_k(p.sa + kk * p.sa_ks + rowa, sa_av, (uint32_t)(4 * kk * p.sa_ks), live);
+      const int64_t rowb = (ROWS ? tn0 : (tn0 >> 7)) * p.sb_rs;
+      const uint32_t sb_av = NX ? clamp_bytes(sb_bytes - 4 * rowb) : sb_av0;
+      d.sb = make_rsrc_k(tsb + kk * p.sb_ks + rowb, sb_av, (uint32_t)(4 * kk * p.sb_ks), live);
     }
     return d;
   };
@@ -723,7 +744,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
     if constexpr (C::kStages == 3) wait_vm<kPerStage>();
     else wait_vm<0>();
   };
-  auto stage_ptr = [&](int kb) { return smem + ((kb + st0) % C::kStages) * C::kStage; };
+  auto stage_ptr = [&](int kb) { return smem + ((uint32_t)(kb + st0) % C::kStages) * C::kStage; };
   auto prepare = [&](int kb) {
     // ragged K: the last block's bytes past K are zeroed before anyone reads them
     if (kb == nkb - 1 && krem < 128 && (XK || WK)) {
@@ -964,7 +985,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
     // when the wave's first column is)
     cy.stores = p.C ? ((C::kStagedEpi && p.c_vec16) ? (iv > 0 ? jv : 0) : iv * jv) : 0;
     cy.prefetched = pf_live ? 1 : 0;
-    cy.stage0 = (st0 + nkb) % C::kStages;
+    cy.stage0 = (int)((uint32_t)(st0 + nkb) % C::kStages);
   }
 }
 
@@ -1339,6 +1360,8 @@ inline int dense_params(int layout, int64_t M, int64_t N, int64_t K, const void*
   ScaleIndex sa{}, sb{};
   if (!scale_index(ga, xk, false, M, K, sa) || !scale_index(gb, wk, true, N, K, sb))
     return FP8BS_ERR_UNSUPPORTED;
+  // scale arrays below 4 GiB (the kernels size their scale DMA in 32 bits)
+  if (sa.bytes >= (int64_t(1) << 32) || sb.bytes >= (int64_t(1) << 32)) return FP8BS_ERR_SHAPE;
   p = GemmParams{};
   p.M = M; p.N = N; p.K = K;
   p.A = static_cast<const uint8_t*>(A); p.lda = lda;
@@ -1390,6 +1413,8 @@ inline int grouped_params(int32_t num_groups, const int64_t* group_offsets, int6
   p.b_group_stride = N * ldb;
   p.sb_group_stride = ceil_div(N, 128) * ceil_div(K, 128);
   p.sb_bytes = p.sb_group_stride * 4;   // one group's weight scales
+  // scale arrays below 4 GiB (the kernels size their scale DMA in 32 bits)
+  if (p.sa_bytes >= (int64_t(1) << 32) || p.sb_bytes >= (int64_t(1) << 32)) return FP8BS_ERR_SHAPE;
   return FP8BS_OK;
 }
 

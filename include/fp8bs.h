@@ -224,7 +224,8 @@ int fp8_cast_fp32(const float* x, int64_t n, int fmt, void* q_out, void* stream)
  *   C_bf16: [M,N] pitch ldc (elements).
  * M, N or K == 0: C is left untouched when M or N is 0; with K == 0, C is set to zeros.
  * Requirements: 16-byte aligned A and B with lda % 16 == 0 and ldb % 16 == 0, 4-byte aligned C
- * with ldc % 2 == 0 (FP8BS_ERR_ALIGN otherwise); pitches at least the row widths.
+ * with ldc % 2 == 0 (FP8BS_ERR_ALIGN otherwise); pitches at least the row widths.  Size limits
+ * (FP8BS_ERR_SHAPE): lda, ldb < 2^23; M, N < 2^31 - 256; each scale array below 4 GiB.
  * Errors: FP8BS_ERR_NULL, FP8BS_ERR_SHAPE, FP8BS_ERR_ALIGN, FP8BS_ERR_UNSUPPORTED,
  * FP8BS_ERR_ARG, FP8BS_ERR_LAUNCH.
  */
@@ -251,7 +252,8 @@ int fp8_gemm_blockscaled(int layout, int64_t M, int64_t N, int64_t K,
  *   B:  [num_groups][N][K] codes (format fb), rows of pitch ldb, groups of stride N * ldb;
  *       scale_inv_b: float[num_groups][ceil(N/128)][ceil(K/128)].
  *   C:  [total_M, N] bf16, pitch ldc.
- * Alignment as for fp8_gemm_blockscaled.  Errors: FP8BS_ERR_NULL, FP8BS_ERR_SHAPE,
+ * Alignment and size limits as for fp8_gemm_blockscaled (total_M for M; scale_inv_a and one
+ * group's scale_inv_b below 4 GiB).  Errors: FP8BS_ERR_NULL, FP8BS_ERR_SHAPE,
  * FP8BS_ERR_ALIGN, FP8BS_ERR_ARG, FP8BS_ERR_LAUNCH.
  */
 int fp8_grouped_gemm(int32_t num_groups, const int64_t* group_offsets, int64_t total_M,

@@ -111,6 +111,9 @@ def test_gemm_validation(entry):
     assert gemm(layout=2, ga=1, gb=0) == bsq.ERR_UNSUPPORTED   # wgrad: B is MN-major
     assert gemm(layout=1, ga=0, gb=0) == bsq.ERR_UNSUPPORTED   # dgrad: B is MN-major
     assert gemm(M=0) == bsq.OK and gemm(N=0, C=None) == bsq.OK
+    # scale arrays of 4 GiB or more (1x128 scales of 2^30 rows x 4 K blocks): rejected before
+    # any launch
+    assert gemm(M=1 << 30, K=512, lda=512) == bsq.ERR_SHAPE
 
 
 def grouped(entry="fp8_grouped_gemm", **kw):
@@ -133,6 +136,7 @@ def test_grouped_validation(entry):
     assert grouped(lda=64) == bsq.ERR_SHAPE
     assert grouped(off=FAKE + 4) == bsq.ERR_ALIGN
     assert grouped(M=0) == bsq.OK and grouped(G=0) == bsq.OK
+    assert grouped(M=1 << 30, K=512, lda=512) == bsq.ERR_SHAPE   # activation scales >= 4 GiB
 
 
 def qcol(**kw):
