@@ -874,6 +874,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
         __builtin_amdgcn_sched_barrier(0);
       }
       const int xbyte = HW ? e8m0_of(ccur) : 0;   // activation scale of this lane's row
+      // The piece's MFMAs and folds issue at raised wave priority: when both waves of a SIMD
+      // are ready, the one feeding the matrix core goes first (measured 1.5% faster than equal
+      // priorities, 1.1% faster than raising it only after the hand-over).
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         if constexpr (FOLD) {
@@ -913,6 +917,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_s_setprio(0);
       if (turn) {
         mfma_row_scales(stn, wbr);
         if constexpr (kBurst) issue(kb + C::kStages, std::bool_constant<PF && PREP>{});
