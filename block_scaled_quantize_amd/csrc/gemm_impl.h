@@ -981,14 +981,18 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
   if constexpr (PF) {
     // Store instructions the wave issued above, at least: one per (n piece, m piece) whose first
     // column and row lie inside the output (a lane of that piece stores).
-    int iv = 0, jv = 0;
+    int iv = 0, jv = 0, hv = 0;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) jv += (m0 + wm * C::kWTM + 16 * j < m_end) ? 1 : 0;
+    for (int j = 0; j < NJ; ++j) {
+      jv += (m0 + wm * C::kWTM + 16 * j < m_end) ? 1 : 0;
+      hv += (m0 + wm * C::kWTM + 16 * j < m_end) ? 1 : 0;
+      hv += (m0 + wm * C::kWTM + 16 * j + 8 < m_end) ? 1 : 0;
+    }
 #pragma unroll
     for (int i = 0; i < NI; ++i) iv += (n0 + wn * C::kWTN + 16 * i < p.N) ? 1 : 0;
-    // (staged epilogue: at least one store instruction per m piece whose first row is inside,
-    // when the wave's first column is)
-    cy.stores = p.C ? ((C::kStagedEpi && p.c_vec16) ? (iv > 0 ? jv : 0) : iv * jv) : 0;
+    // (staged epilogue: at least one store instruction per 8-row half of an m piece whose first
+    // row is inside, when the wave's first column is)
+    cy.stores = p.C ? ((C::kStagedEpi && p.c_vec16) ? (iv > 0 ? hv : 0) : iv * jv) : 0;
     cy.prefetched = pf_live ? 1 : 0;
     cy.stage0 = (int)((uint32_t)(st0 + nkb) % C::kStages);
   }
