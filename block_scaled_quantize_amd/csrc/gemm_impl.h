@@ -342,16 +342,26 @@ __device__ __forceinline__ void wait_lds() {
   asm volatile("" ::: "memory");
 }
 
-// Wait until at most min(n, N) vector-memory operations are outstanding (n >= 0, made
-// wave-uniform here so that the choice is a scalar branch).
-template <int N>
-__device__ __forceinline__ void wait_vm_atmost(int n) {
-  if constexpr (N == 0) {
-    wait_vm<0>();
+// Wait until at most min(n, HI) vector-memory operations are outstanding, for LO <= min(n, HI)
+// (n wave-uniform): a binary search over the waitcnt immediates, a handful of scalar branches
+// instead of one per value.
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vm_range(int n) {
+  if constexpr (LO >= HI) {
+    wait_vm<HI>();
   } else {
-    if (__builtin_amdgcn_readfirstlane(n) >= N) wait_vm<N>();
-    else wait_vm_atmost<N - 1>(n);
+    constexpr int MID = (LO + HI + 1) / 2;
+    if (n >= MID) wait_vm_range<MID, HI>(n);
+    else wait_vm_range<LO, MID - 1>(n);
   }
+}
+// Wait until at most min(n, N) are outstanding (n >= 0); FAST, a count that is checked first
+// (the one a whole tile gives).
+template <int N, int FAST = N>
+__device__ __forceinline__ void wait_vm_atmost(int n) {
+  n = __builtin_amdgcn_readfirstlane(n);
+  if (n == FAST) wait_vm<FAST>();
+  else wait_vm_range<0, N>(n);
 }
 
 // One output tile: group g (0 for a dense GEMM), rows [m0, m_end), columns from n0.
@@ -812,7 +822,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
   for (int i = 0; i < NI; ++i) P[i] = v4f{0.f, 0.f, 0.f, 0.f};   // pending products (fold)
   if (nkb > 0) {
     // block 0 issued during the previous tile: only that tile's later stores may be pending
-    if (prefetched) wait_vm_atmost<NI * NJ>(cy.stores);
+    if (prefetched) wait_vm_atmost<NI * NJ, (C::kStagedEpi ? 2 * NJ : NI * NJ)>(cy.stores);
     else wait_next();
     barrier();
     prepare(0);
