@@ -1149,13 +1149,16 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(GemmParams
   auto tile_at = [&](int id) {
     int mt, tn;
     tile_of(id, m_tiles, tiles_n, mt, tn);
-    int lo = 0, hi = G - 1;   // last group with s_prefix[g] <= mt
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_prefix[mid] <= mt) lo = mid; else hi = mid - 1;
+    // the last group with s_prefix[g] <= mt (the prefix does not decrease): the number of
+    // g in [1, G) with s_prefix[g] <= mt, counted 64 groups at a time by the wave's lanes (one
+    // LDS round trip per 64 groups instead of one per step of a binary search)
+    int cnt = 0;
+    for (int base = 1; base < G; base += 64) {
+      const int gq = base + (int)(threadIdx.x & 63);
+      cnt += __popcll(__ballot(gq < G && s_prefix[gq] <= mt));
     }
     // (the same in every lane: kept in scalar registers)
-    const int gi = __builtin_amdgcn_readfirstlane(lo);
+    const int gi = __builtin_amdgcn_readfirstlane(cnt);
     const int glo = __builtin_amdgcn_readfirstlane(s_lo[gi]);
     const int ghi = __builtin_amdgcn_readfirstlane(s_lo[gi + 1]);
     const int m0 = glo + __builtin_amdgcn_readfirstlane(mt - s_prefix[gi]) * BM;
