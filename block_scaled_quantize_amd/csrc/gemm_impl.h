@@ -565,10 +565,14 @@ __device__ __forceinline__ void quantize_out(const GemmParams& p, uint8_t* smem,
 // PF (persistent workgroups, two LDS stages, no fused quantization): when has_next and the tile
 // has at least two K blocks, the next tile's first K block is loaded into the free stage while
 // this tile's last block runs, and the next tile starts without waiting for this tile's stores.
+// The next tile, nt = next_tile(), is then formed at the start of the tile's last-but-one block
+// (its lookup overlaps the K loop instead of following the epilogue); nt is left as it was
+// otherwise.
 template <class C, int LAYOUT, int FA, int FB, int SM, int QO = 0, bool PF = false,
-          bool PERSIST = PF>
+          bool PERSIST = PF, class NextTile>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, const Tile& t,
-                                          const Tile& nt, bool has_next, Carry& cy) {
+                                          Tile& nt, const NextTile& next_tile, bool has_next,
+                                          Carry& cy) {
   static_assert(!PF || (C::kStages == 2 && QO == 0), "cross-tile prefetch: two stages, bf16 out");
   const int64_t m0 = t.m0, m_end = t.m_end, n0 = t.n0;
   const uint8_t* Bw = p.B + (int64_t)t.g * p.b_group_stride;
@@ -849,6 +853,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
   auto run_block = [&](int kb, auto turn_tag, auto prep_tag) {
     constexpr bool TURN = decltype(turn_tag)::value;
     constexpr bool PREP = decltype(prep_tag)::value;
+    if constexpr (PF && PREP) {
+      if (pf_live) nt = next_tile();   // (first needed by this block's hand-over)
+    }
     const uint8_t* st = stage_ptr(kb);
     const uint8_t* stn = stage_ptr(kb + 1);
     const int wbyte = (HW && !ROWS) ? e8m0_of(sbv) : 0;   // weight scale of the block
@@ -1033,7 +1040,8 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
   const int m0 = tm * C::BM;
   const Tile t{0, m0, (int)std::min<int64_t>((int64_t)m0 + C::BM, p.M), tn * C::BN};
   Carry cy{0, 0, 0};
-  gemm_tile<C, LAYOUT, FA, FB, SM, QO>(p, smem, t, t, false, cy);
+  Tile nt = t;
+  gemm_tile<C, LAYOUT, FA, FB, SM, QO>(p, smem, t, nt, [&]() { return t; }, false, cy);
 }
 
 // The kernel parameters, read again from the argument segment (scalar loads) where a
@@ -1072,11 +1080,15 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_persistent_kernel(GemmPar
   while (true) {
     const int nid = id + (int)gridDim.x;
     const bool has_next = nid < total;
-    const Tile nxt = has_next ? tile_at(nid) : cur;
+    Tile nxt = cur;
     FP8BS_REREAD_PARAMS(q, p);
-    gemm_tile<C, LAYOUT, FA, FB, SM, 0, true, true>(q, smem, cur, nxt, has_next, cy);
+    gemm_tile<C, LAYOUT, FA, FB, SM, 0, true, true>(q, smem, cur, nxt,
+                                                    [&]() { return tile_at(nid); }, has_next, cy);
     if (!has_next) break;
-    if (!cy.prefetched) __syncthreads();   // the next tile refills the LDS stages
+    if (!cy.prefetched) {
+      __syncthreads();   // the next tile refills the LDS stages
+      nxt = tile_at(nid);   // (not formed during the tile: fewer than two K blocks)
+    }
     cur = nxt;
     id = nid;
   }
@@ -1171,11 +1183,16 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(GemmParams
   while (true) {
     const int nid = id + (int)gridDim.x;
     const bool has_next = nid < total;
-    const Tile nxt = has_next ? tile_at(nid) : cur;
+    Tile nxt = cur;
     FP8BS_REREAD_PARAMS(q, p);
-    gemm_tile<C, FP8BS_FPROP, FA, FB, SM, 0, PF, true>(q, smem, cur, nxt, has_next, cy);
+    gemm_tile<C, FP8BS_FPROP, FA, FB, SM, 0, PF, true>(q, smem, cur, nxt,
+                                                       [&]() { return tile_at(nid); }, has_next,
+                                                       cy);
     if (!has_next) break;
-    if (!cy.prefetched) __syncthreads();   // the next tile refills the LDS stages
+    if (!cy.prefetched) {
+      __syncthreads();   // the next tile refills the LDS stages
+      nxt = tile_at(nid);   // (not formed during the tile: fewer than two K blocks, or no prefetch)
+    }
     cur = nxt;
     id = nid;
   }
