@@ -884,6 +884,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
         wait_lds();   // this wave's reads of stage kb have completed
         wait_next();
         barrier();
+        if constexpr (PREP && !FOLD) {
+          // (the accumulations so far are complete here: otherwise the compiler may sink the
+          // MFMAs of this block past the ragged-K branch of prepare, keeping their fragments
+          // live -- and spilled -- across it)
+#pragma unroll
+          for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int jj = 0; jj + 1 < NJ; ++jj) asm volatile("" : "+v"(acc[i][jj]));
+        }
         if constexpr (PREP) prepare(kb + 1);
         if constexpr (!kBurst) dturn = block_dma(kb + C::kStages, std::bool_constant<PF && PREP>{});
         first_x(stn, xnext, cnext, sbv);
