@@ -312,6 +312,20 @@ def test_every_tile_variant(gpu, variant, layout, fa, ga, fb, gb):
     run_gemm(gpu, layout, 256, 256, 256, fa, ga, fb, gb, tile=TILES[variant])
 
 
+@pytest.mark.parametrize("K", [128, 200, 256, 640])
+@pytest.mark.parametrize("layout,fa,ga,fb,gb,pow2", [(FP, E4, B1, E4, B128, False),
+                                                    (FP, E4, B1, E4, B128, True),
+                                                    (DG, E5, PT, E4, PT, False),
+                                                    (WG, E5, PT, E4, PT, False)])
+def test_dense_persistent_tile_walk(gpu, K, layout, fa, ga, fb, gb, pow2):
+    """324 tiles of 256x256 on the persistent grid: a workgroup takes a second tile, formed while
+    its first runs (two or more K blocks) or after it (one K block), with the next tile's first
+    K block loaded during the current tile's last (two or more K blocks, ragged K included).
+    Four sampled rows in each of the 18 tile rows cover every tile."""
+    rows = np.array([256 * t + o for t in range(18) for o in (0, 97, 200, 255)])
+    run_gemm(gpu, layout, 4608, 4608, K, fa, ga, fb, gb, pow2=pow2, rows=rows)
+
+
 @pytest.mark.parametrize("K,N", [(128, 256), (256, 384), (208, 256), (640, 512)])
 @pytest.mark.parametrize("pow2", [False, True])
 def test_grouped_persistent_tiles(gpu, K, N, pow2):
@@ -320,6 +334,17 @@ def test_grouped_persistent_tiles(gpu, K, N, pow2):
     nothing to overlap --, 2 -- the first block hands over --, 2 with a ragged K, 5)."""
     counts = [3000] * 24 + [17, 0, 700]
     run_grouped(gpu, counts, N, K, seed=K, pow2=pow2)
+
+
+@pytest.mark.parametrize("G", [300, 1024])
+@pytest.mark.parametrize("pow2", [False, True])
+def test_grouped_many_groups(gpu, G, pow2):
+    """Hundreds of groups, up to the 1024 the kernel allows (the tile's group is found 64 prefix
+    entries at a time, so every 64-group chunk of the prefix is searched), many of them empty or
+    a few rows long."""
+    sizes = [0, 1, 7, 64, 130, 0, 256, 33, 300, 2] if G == 300 else [0, 1, 5, 17, 0, 40, 3, 0]
+    counts = [sizes[(g * 7 + g // 5) % len(sizes)] for g in range(G)]
+    run_grouped(gpu, counts, 128, 256, seed=G, pow2=pow2)
 
 
 @pytest.mark.parametrize("variant", ["B", "C", "D"])
