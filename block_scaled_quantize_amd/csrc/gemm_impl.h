@@ -436,6 +436,65 @@ __device__ __forceinline__ void store_rows_staged(const GemmParams& p, const Til
   wait_lds();   // (the next round rewrites the region)
 }
 
+// LDS accesses of one wave stay in issue order, so a wave can exchange data between its own
+// lanes through LDS with no wait: this only keeps the compiler from moving LDS accesses across.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The staged epilogue of a wave whose 128 x 64 block lies wholly inside the output (16-byte
+// aligned rows): the same LDS round trip and full-line stores as store_rows_staged, without
+// per-lane bounds checks, with the row address stepped instead of recomputed, and with piece
+// j + 1 written to the region while piece j's stores go out (the accumulators are zero when K
+// is empty, so no zeroing is needed).
+template <class C, int SM, class Acc>
+__device__ __forceinline__ void store_wave_staged(const GemmParams& p, const Tile& t, int wm, int wn,
+                                                  int lane, const Acc& acc, float post,
+                                                  uint8_t* region) {
+  static_assert(C::kWTN == 64 && C::kNI == 4, "a wave's rows are 128 bytes");
+  constexpr int NI = C::kNI, NJ = C::kNJ;
+  const int li = lane & 15, g = lane >> 4;
+  const int r = lane >> 3, c = lane & 7;
+  uint16_t* base = p.C + ((int64_t)t.m0 + wm * C::kWTM + r) * p.ldc + (t.n0 + wn * C::kWTN + 8 * c);
+  const int64_t row8 = 8 * p.ldc;
+  uint8_t* wr = region + li * C::kEpiPitch + 8 * g;
+  const uint8_t* rd = region + r * C::kEpiPitch + 16 * c;
+  auto put = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      v4f v = acc[i][j];
+      if constexpr (SM == kScaleTensor) v = v * post;
+      *reinterpret_cast<uint2*>(wr + 32 * i) =
+          make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    }
+  };
+  uint4 d[2];
+  auto get = [&]() {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) d[h] = *reinterpret_cast<const uint4*>(rd + 8 * h * C::kEpiPitch);
+  };
+  put(0);
+  wave_lds_fence();
+  get();
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const uint4 e0 = d[0], e1 = d[1];
+    if (j + 1 < NJ) {
+      wave_lds_fence();   // (the reads of piece j precede these writes in the LDS queue)
+      put(j + 1);
+    }
+    __builtin_nontemporal_store(u32x4{e0.x, e0.y, e0.z, e0.w},
+                                reinterpret_cast<u32x4*>(base + (2 * j) * row8));
+    __builtin_nontemporal_store(u32x4{e1.x, e1.y, e1.z, e1.w},
+                                reinterpret_cast<u32x4*>(base + (2 * j + 1) * row8));
+    if (j + 1 < NJ) {
+      wave_lds_fence();
+      get();
+    }
+  }
+}
 
 // E8M0 code of a power-of-two scale: its binary32 exponent field (2^-127, the one subnormal
 // power of two a scale can take, has field 0 and is E8M0 code 0 as well).
@@ -978,7 +1037,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
 
   // Epilogue: lane holds C[m][n .. n+3] of each piece.
   if (p.C) {
-    if (C::kStagedEpi && p.c_vec16) {
+    // (the wave's block inside the output: one test per tile)
+    const bool whole = m0 + wm * C::kWTM + C::kWTM <= m_end && n0 + wn * C::kWTN + C::kWTN <= p.N;
+    if (C::kStagedEpi && p.c_vec16 && whole) {
+      store_wave_staged<C, SM>(p, t, wm, wn, lane, acc, post, smem + C::kEpi + w * C::kEpiWaveBytes);
+    } else if (C::kStagedEpi && p.c_vec16) {
       uint8_t* region = smem + C::kEpi + w * C::kEpiWaveBytes;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
