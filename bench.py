@@ -27,6 +27,7 @@ llama8b-fprop-qout (the GEMM quantizing its own output against GEMM + quantizer)
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -60,7 +61,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b-fprop",
                     choices=["llama8b-fprop", "llama8b-fprop-pow2", "quant-sweep", "moe", "backward",
-                             "backward-blockwise", "llama8b-fprop-qout", "kv-decode", "copy", "stream"])
+                             "backward-blockwise", "llama8b-fprop-qout", "kv-decode", "copy", "stream",
+                             "mfma-ceiling"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pow2", action="store_true",
                     help="moe, backward-blockwise: power-of-2 scales (E8M0 in the MFMA)")
@@ -126,6 +128,82 @@ def cpu_cores() -> int:
         return len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
         return os.cpu_count() or 1
+
+
+# ----------------------------------------------------------------------------- matrix-core ceiling
+
+def mfma_sustained(codes, shape: int = 0, launches: int = 20, steps: int = 1000) -> float:
+    """TFLOP/s the matrix core sustains on register operands holding `codes` (16384 E4M3 bytes
+    on the GPU: 8 operand sets of 64 lanes x 32 bytes) -- independent MFMAs in a loop, 512-thread
+    workgroups (two waves per SIMD, as the GEMM tiles), one per CU (each takes 96 KiB of LDS), no
+    memory traffic inside the loop (libfp8bs_bench.so).  shape 0: 16x16x128, 1: 32x32x64.  Mean
+    over `launches` back-to-back launches of about a millisecond each, after 3 warm-up launches."""
+    blib = ctypes.CDLL(os.path.join(ROOT, "block_scaled_quantize_amd", "libfp8bs_bench.so"))
+    blib.fp8bs_bench_mfma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    blib.fp8bs_bench_mfma.restype = ctypes.c_int
+    codes = codes.contiguous()
+    assert codes.dtype == torch.uint8 and codes.numel() == 16384 and codes.is_cuda
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(cus * 512, dtype=torch.float32, device=codes.device)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def launch():
+        rc = blib.fp8bs_bench_mfma(codes.data_ptr(), out.data_ptr(), shape, steps, cus, 96 * 1024,
+                                   stream)
+        if rc != 0:
+            raise RuntimeError("fp8bs_bench_mfma failed")
+    for _ in range(3):
+        launch()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(launches)]
+    for a, b in ev:
+        a.record()
+        launch()
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    flops = 2.0 * cus * 8 * steps * 32 * 16 * 16 * 128
+    return flops / ms / 1e9
+
+
+def bench_mfma_ceiling(args):
+    """The rate the matrix core sustains on register operands (no memory traffic): the practical
+    ceiling of an FP8 GEMM with the same operand bits, against the 5.0 PFLOP/s dense peak (which
+    assumes the peak shader clock).  Codes: those of the 8B fprop workload's gate_up layer
+    (weights, normal(0, 0.02), 128x128 scales; activations with outlier channels, 1x128 scales),
+    uniform random E4M3 codes of magnitude below 448, and zeros."""
+    import block_scaled_quantize_amd as bsq
+    import synth
+    bsq.load()
+    dev = torch.device("cuda", 0)
+    w = synth.normal((64, 128), 0.02, 0, "bench/8b/gate_up/W").to(dev)
+    x = synth.activations_with_outliers(64, 128, 0, "bench/8b/gate_up/X").to(dev)
+    qw, _ = bsq.quantize_blockwise(w, bsq.E4M3, bsq.BLOCK_128x128, bsq.SCALE_FP32)
+    qx, _ = bsq.quantize_blockwise(x, bsq.E4M3, bsq.BLOCK_1x128, bsq.SCALE_FP32)
+    g = torch.Generator().manual_seed(0)
+    rnd = (torch.randint(0, 0x7F, (16384,), generator=g, dtype=torch.int32) |
+           (torch.randint(0, 2, (16384,), generator=g, dtype=torch.int32) << 7)).to(torch.uint8)
+    sets = {"8b_gate_up_codes": torch.cat([qw.reshape(-1), qx.reshape(-1)]),
+            "uniform_random_codes": rnd.to(dev),
+            "zeros": torch.zeros(16384, dtype=torch.uint8, device=dev)}
+    cases = {}
+    for name, codes in sets.items():
+        for shape, label in ((0, "16x16x128"), (1, "32x32x64")):
+            tf = mfma_sustained(codes, shape, launches=max(args.steps, 10))
+            cases[f"{name}/{label}"] = round(tf, 1)
+            log(f"mfma {label} {name}: {tf:.0f} TFLOP/s")
+    head = cases["8b_gate_up_codes/16x16x128"]
+    return dict(metric="sustained FP8 MFMA TFLOP/s on register operands (matrix-core ceiling)",
+                value=head, unit="TFLOP/s", n_gpus=1, steps=max(args.steps, 10), warmup=3,
+                ms_per_step=None, higher_is_better=True, scaling="weak", vs_baseline=None,
+                dtype="fp8e4m3 x fp8e4m3 -> fp32 acc", data="synthetic",
+                config=dict(workload="mfma-ceiling", headline="8B gate_up codes, 16x16x128"),
+                roofline=dict(bound="mfma", achieved=head, peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
+                              frac=round(head / FP8_PEAK_TFLOPS, 4), traffic=None,
+                              kernel="mfma_loop_kernel (libfp8bs_bench.so)"),
+                cases=cases)
 
 
 # ----------------------------------------------------------------------------- 8B fprop
@@ -215,6 +293,11 @@ def bench_llama8b(args, pow2: bool = False):
     mean_launch_ms = float(np.mean(gemm_ms))
     achieved = mean_launch_flops / mean_launch_ms / 1e9
     traffic = measured_traffic(GEMM_COUNTERS_POW2 if pow2 else GEMM_COUNTERS, GEMM_SOURCES)
+    # the matrix core's own sustained rate on this workload's codes (gate_up weight and
+    # activation codes in registers, no memory traffic): what the GEMM's clock allows
+    gu = layers[2]
+    ceiling = mfma_sustained(torch.cat([gu["qw"].reshape(-1)[:8192], gu["qx"].reshape(-1)[:8192]]))
+    log(f"matrix core on the workload's codes: {ceiling:.0f} TFLOP/s")
     scales = "power-of-2 (E8M0 in the MFMA)" if pow2 else "fp32"
     result = dict(
         metric="block-scaled FP8 GEMM TFLOP/s (+quantize GB/s), % of MI355X FP8/HBM peak",
@@ -234,6 +317,12 @@ def bench_llama8b(args, pow2: bool = False):
                       kernel="gemm_persistent_kernel<Cfg<256,256,2,4>,FPROP,E4M3,E4M3,%s>" % ("hw" if pow2 else "fold"),
                       per_launch_flops=mean_launch_flops, mean_launch_us=round(mean_launch_ms * 1e3, 2)),
         gemm_only_tflops=round(sum(gemm_flops) / sum(gemm_ms) / 1e9, 1),
+        mfma_sustained=dict(tflops=round(ceiling, 1),
+                            gemm_frac=round(achieved / ceiling, 4),
+                            what="V_MFMA 16x16x128 E4M3 loop on register operands holding the "
+                                 "gate_up layer's weight and activation codes, two waves per "
+                                 "SIMD, no memory traffic (libfp8bs_bench.so): the rate the "
+                                 "clock allows with these operand bits"),
         quant_gbps=round(q_bytes / q_ms / 1e6, 1),
         quant_hbm_frac=round(q_bytes / q_ms / 1e6 / HBM_PEAK_GBPS, 4),
         quant_weights=dict(us=round(qw_ms * 1e3, 2), gbps=round(w_bytes / qw_ms / 1e6, 1),
@@ -921,6 +1010,8 @@ def main():
         res = bench_kv_decode(args)
     elif args.workload == "stream":
         res = bench_stream(args)
+    elif args.workload == "mfma-ceiling":
+        res = bench_mfma_ceiling(args)
     elif args.workload == "copy":
         res = bench_copy(args)
     else:

@@ -17,9 +17,10 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfp8bs.so")
-# streaming kernels the benchmark measures the device's streaming rate with (not the C ABI)
+# kernels the benchmark measures the device's streaming rate and sustained matrix-core rate with
+# (not the C ABI)
 BENCH_LIB = os.path.join(HERE, "libfp8bs_bench.so")
-BENCH_SOURCES = ["bench_stream.hip"]
+BENCH_SOURCES = ["bench_stream.hip", "bench_mfma.hip"]
 # (the GEMM kernels are split over several files so that they compile in parallel)
 SOURCES = ["gemm_fprop.hip", "gemm_fprop_pow2.hip", "gemm_dgrad.hip", "gemm_wgrad.hip",
            "gemm_grouped.hip", "gemm_qout.hip", "gemm.hip", "quantize.hip", "quantize_t.hip",

@@ -403,3 +403,25 @@ def test_attention_decode_offset_limit():
     assert attn(T=big, KVH=8, H=32) == bsq.ERR_UNSUPPORTED
     assert attn_split(T=big, KVH=8, H=32, wsb=1 << 40) == bsq.ERR_UNSUPPORTED
     assert attn(T=big - 64, KVH=8, H=32, q=None) == bsq.ERR_NULL   # within the limit: validated on
+
+
+def test_bench_library_probes_reject_invalid_arguments():
+    """libfp8bs_bench.so (the benchmark's streaming and matrix-core probes, not the C ABI) loads,
+    exports both probes, and rejects invalid arguments before launching anything."""
+    import os
+    path = os.path.join(os.path.dirname(bsq.__file__), "libfp8bs_bench.so")
+    blib = ctypes.CDLL(path)
+    blib.fp8bs_bench_mfma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    blib.fp8bs_bench_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                        ctypes.c_int, ctypes.c_void_p]
+    mfma = blib.fp8bs_bench_mfma
+    assert mfma(None, FAKE, 0, 10, 256, 0, None) == -1          # no codes
+    assert mfma(FAKE, None, 0, 10, 256, 0, None) == -1          # no output
+    assert mfma(FAKE_ODD, FAKE, 0, 10, 256, 0, None) == -1      # misaligned codes
+    assert mfma(FAKE, FAKE, 2, 10, 256, 0, None) == -1          # no such shape
+    assert mfma(FAKE, FAKE, 0, 0, 256, 0, None) == -1           # no steps
+    assert mfma(FAKE, FAKE, 0, 10, 0, 0, None) == -1            # no workgroups
+    assert mfma(FAKE, FAKE, 0, 10, 256, 161 * 1024, None) == -1  # more LDS than a CU has
+    assert blib.fp8bs_bench_stream(None, 16, FAKE, 0, None) == -1
+    assert blib.fp8bs_bench_stream(FAKE, 15, FAKE, 0, None) == -1
