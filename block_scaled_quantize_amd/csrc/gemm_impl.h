@@ -444,15 +444,16 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// The staged epilogue of a wave whose 128 x 64 block lies wholly inside the output (16-byte
-// aligned rows): the same LDS round trip and full-line stores as store_rows_staged, without
-// per-lane bounds checks, with the row address stepped instead of recomputed, and with piece
-// j + 1 written to the region while piece j's stores go out (the accumulators are zero when K
-// is empty, so no zeroing is needed).
-template <class C, int SM, class Acc>
+// The staged epilogue of a wave whose 64 columns lie inside the output (16-byte aligned rows):
+// the same LDS round trip and full-line stores as store_rows_staged, without per-lane column
+// tests, with the row address stepped instead of recomputed, and with piece j + 1 written to the
+// region while piece j's stores go out (the accumulators are zero when K is empty, so no zeroing
+// is needed).  ROWS_CUT: only the wave's first `rows` rows are inside (a lane stores its row if
+// it is); otherwise all 128 are.
+template <class C, int SM, bool ROWS_CUT, class Acc>
 __device__ __forceinline__ void store_wave_staged(const GemmParams& p, const Tile& t, int wm, int wn,
                                                   int lane, const Acc& acc, float post,
-                                                  uint8_t* region) {
+                                                  uint8_t* region, int rows) {
   static_assert(C::kWTN == 64 && C::kNI == 4, "a wave's rows are 128 bytes");
   constexpr int NI = C::kNI, NJ = C::kNJ;
   const int li = lane & 15, g = lane >> 4;
@@ -485,10 +486,12 @@ __device__ __forceinline__ void store_wave_staged(const GemmParams& p, const Til
       wave_lds_fence();   // (the reads of piece j precede these writes in the LDS queue)
       put(j + 1);
     }
-    __builtin_nontemporal_store(u32x4{e0.x, e0.y, e0.z, e0.w},
-                                reinterpret_cast<u32x4*>(base + (2 * j) * row8));
-    __builtin_nontemporal_store(u32x4{e1.x, e1.y, e1.z, e1.w},
-                                reinterpret_cast<u32x4*>(base + (2 * j + 1) * row8));
+    if (!ROWS_CUT || r + 16 * j < rows)
+      __builtin_nontemporal_store(u32x4{e0.x, e0.y, e0.z, e0.w},
+                                  reinterpret_cast<u32x4*>(base + (2 * j) * row8));
+    if (!ROWS_CUT || r + 16 * j + 8 < rows)
+      __builtin_nontemporal_store(u32x4{e1.x, e1.y, e1.z, e1.w},
+                                  reinterpret_cast<u32x4*>(base + (2 * j + 1) * row8));
     if (j + 1 < NJ) {
       wave_lds_fence();
       get();
@@ -627,8 +630,10 @@ __device__ __forceinline__ void quantize_out(const GemmParams& p, uint8_t* smem,
 // The next tile, nt = next_tile(), is then formed at the start of the tile's last-but-one block
 // (its lookup overlaps the K loop instead of following the epilogue); nt is left as it was
 // otherwise.
+// CUT_ROWS (grouped GEMM: every expert's last tile is cut): waves whose rows end inside the tile
+// also take the epilogue without column tests.
 template <class C, int LAYOUT, int FA, int FB, int SM, int QO = 0, bool PF = false,
-          bool PERSIST = PF, class NextTile>
+          bool PERSIST = PF, bool CUT_ROWS = false, class NextTile>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, const Tile& t,
                                           Tile& nt, const NextTile& next_tile, bool has_next,
                                           Carry& cy) {
@@ -1037,12 +1042,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
 
   // Epilogue: lane holds C[m][n .. n+3] of each piece.
   if (p.C) {
-    // (the wave's block inside the output: one test per tile)
-    const bool whole = m0 + wm * C::kWTM + C::kWTM <= m_end && n0 + wn * C::kWTN + C::kWTN <= p.N;
-    if (C::kStagedEpi && p.c_vec16 && whole) {
-      store_wave_staged<C, SM>(p, t, wm, wn, lane, acc, post, smem + C::kEpi + w * C::kEpiWaveBytes);
+    // (the wave's columns inside the output, and how many of its rows: tests once per tile)
+    const bool cols_in = n0 + wn * C::kWTN + C::kWTN <= p.N;
+    const int rows_in = (int)std::min<int64_t>(m_end - (m0 + wm * C::kWTM), C::kWTM);
+    uint8_t* const region = smem + C::kEpi + w * C::kEpiWaveBytes;
+    if (C::kStagedEpi && p.c_vec16 && cols_in && rows_in == C::kWTM) {
+      store_wave_staged<C, SM, false>(p, t, wm, wn, lane, acc, post, region, rows_in);
+    } else if (CUT_ROWS && C::kStagedEpi && p.c_vec16 && cols_in) {
+      if (rows_in > 0) store_wave_staged<C, SM, true>(p, t, wm, wn, lane, acc, post, region, rows_in);
     } else if (C::kStagedEpi && p.c_vec16) {
-      uint8_t* region = smem + C::kEpi + w * C::kEpiWaveBytes;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         v4f v[NI];
@@ -1257,7 +1265,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(GemmParams
     const bool has_next = nid < total;
     Tile nxt = cur;
     FP8BS_REREAD_PARAMS(q, p);
-    gemm_tile<C, FP8BS_FPROP, FA, FB, SM, 0, PF, true>(q, smem, cur, nxt,
+    gemm_tile<C, FP8BS_FPROP, FA, FB, SM, 0, PF, true, true>(q, smem, cur, nxt,
                                                        [&]() { return tile_at(nid); }, has_next,
                                                        cy);
     if (!has_next) break;
