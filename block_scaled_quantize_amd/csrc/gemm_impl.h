@@ -551,11 +551,17 @@ __device__ __forceinline__ void quantize_out(const GemmParams& p, uint8_t* smem,
   }
   __syncthreads();
   const int64_t blk = (n0 >> 7) + (wn >> 1);   // 128-column block of this wave
-  // Codes leave through the wave's epilogue region when 16-byte stores are aligned: the 16 rows
-  // of a piece as 64-byte row segments, 16 rows per store instruction, instead of 4 bytes per
-  // lane and piece.
+  // Codes of a tile whose columns all lie inside the output (16-byte aligned rows) are gathered
+  // in the free operand stages as [row][column] (pitch kTPitch, after the amax words) and leave
+  // as whole 256-byte tile rows, 4 rows per store instruction.  Otherwise they leave through the
+  // wave's epilogue region when 16-byte stores are aligned: the 16 rows of a piece as 64-byte row
+  // segments, 16 rows per store instruction, instead of 4 bytes per lane and piece.
   constexpr int kQPitch = 80;
-  const bool staged = C::kStagedEpi && p.cq_vec16;
+  constexpr int kTPitch = C::BN + 16;   // (4-byte writes of a piece: 64 distinct banks)
+  static_assert(C::kWavesN * BM * 4 + BM * kTPitch <= C::kStages * C::kStage, "codes tile");
+  uint8_t* const tile_codes = smem + C::kWavesN * BM * 4;
+  const bool whole_cols = p.cq_vec16 && n0 + C::BN <= p.N;
+  const bool staged = C::kStagedEpi && p.cq_vec16 && !whole_cols;
   uint8_t* region = smem + C::kEpi + w * C::kEpiWaveBytes;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
@@ -579,7 +585,12 @@ __device__ __forceinline__ void quantize_out(const GemmParams& p, uint8_t* smem,
       codes[i] = cvt4<QF>(y0, y1, y2, y3);
       if (!finite) codes[i] = patch_nan_pair(patch_nan_pair(codes[i], bv[i][j][0], 0), bv[i][j][1], 1);
     }
-    if (staged) {
+    if (whole_cols) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        *reinterpret_cast<uint32_t*>(tile_codes + row * kTPitch + wn * C::kWTN + 16 * i + 4 * g) =
+            codes[i];
+    } else if (staged) {
 #pragma unroll
       for (int i = 0; i < NI; ++i)
         *reinterpret_cast<uint32_t*>(region + li * kQPitch + 16 * i + 4 * g) = codes[i];
@@ -615,6 +626,21 @@ __device__ __forceinline__ void quantize_out(const GemmParams& p, uint8_t* smem,
       }
     }
     if (m < m_end && g == 0 && (wn & 1) == 0 && blk * 128 < p.N) p.cqs[blk * p.M + m] = 1.0f / s;
+  }
+  if (whole_cols) {
+    __syncthreads();   // every wave's codes are in the tile
+    constexpr int kRowsPerWave = BM / C::kWaves;
+    constexpr int kLanesPerRow = C::BN / 16;
+    static_assert(64 % kLanesPerRow == 0 && kRowsPerWave % (64 / kLanesPerRow) == 0, "code rows");
+    const int c = lane % kLanesPerRow;
+#pragma unroll
+    for (int q = 0; q < kRowsPerWave / (64 / kLanesPerRow); ++q) {
+      const int row = w * kRowsPerWave + q * (64 / kLanesPerRow) + lane / kLanesPerRow;
+      const uint4 d = *reinterpret_cast<const uint4*>(tile_codes + row * kTPitch + 16 * c);
+      if (m0 + row < m_end)
+        __builtin_nontemporal_store(u32x4{d.x, d.y, d.z, d.w},
+                                    reinterpret_cast<u32x4*>(p.Cq + (m0 + row) * p.ldcq + n0 + 16 * c));
+    }
   }
 }
 
