@@ -16,6 +16,13 @@ Sources, by page title and section (nothing is copied from them):
   extremo" (hotbookzone.com), section "El avance técnico" (E4M3 blocks: 128x128 for weights,
   1x128 for activations; FP8 linear layers) and section "Por qué esto es importante para la
   economía de la IA" (power-of-2 scale factors).
+* "Infraestructura de Entrenamiento FP8 ...", sections "Estrategias de escalado y estabilidad"
+  (block scaling, MXFP8: separate scale factors for blocks within a tensor) and "Blackwell MXFP8
+  y NVFP4: mirando hacia adelante" (hardware-accelerated block scaling).  The pages state neither
+  the block size nor the scale format; the reading here is the microscaling one: blocks of 32
+  consecutive elements along a row, one power-of-two scale per block stored as an E8M0 byte
+  (the biased binary exponent, 2^(code - 127); code 255 is NaN), the scale chosen by the same
+  power-of-2 rule as the blockwise quantizer.
 
 GEMM reference: dequantize both operands to fp64 (exact), then one fp64 matrix product per
 layout.  It is exact up to the rounding of fp64 accumulation, which is far below the
@@ -35,7 +42,7 @@ _SRC = os.path.join(_HERE, "fp8_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 E4M3, E5M2 = 0, 1
-BLOCK_1x128, BLOCK_128x128, PER_TENSOR = 0, 1, 2
+BLOCK_1x128, BLOCK_128x128, PER_TENSOR, BLOCK_1x32 = 0, 1, 2, 3
 SCALE_FP32, SCALE_POW2 = 0, 1
 FPROP, DGRAD, WGRAD = 0, 1, 2
 
@@ -147,6 +154,8 @@ def _as_bf16_bits(x) -> np.ndarray:
 def block_shape(gran: int, rows: int, cols: int) -> tuple[int, int]:
     if gran == BLOCK_1x128:
         return 1, 128
+    if gran == BLOCK_1x32:
+        return 1, 32
     if gran == BLOCK_128x128:
         return 128, 128
     if gran == PER_TENSOR:
@@ -157,19 +166,55 @@ def block_shape(gran: int, rows: int, cols: int) -> tuple[int, int]:
 def quantize_blockwise(x, fmt: int, gran: int, mode: int, nthreads: int | None = None):
     """Blockwise quantization of a 2-D bf16 matrix.
 
-    Returns (codes uint8 [R, C], scale_inv float32 [ceil(R/bh), ceil(C/128)]) where the scale
+    Returns (codes uint8 [R, C], scale_inv float32 [ceil(R/bh), ceil(C/bw)]) where the scale
     array is in logical block order (block row, block column).
     """
     xb = _as_bf16_bits(x)
     if xb.ndim != 2:
         raise ValueError("expected a 2-D matrix")
     rows, cols = xb.shape
-    bh = 1 if gran == BLOCK_1x128 else 128
+    bh, bw = block_shape(gran, rows, cols)
     q = np.empty((rows, cols), dtype=np.uint8)
-    si = np.empty(((rows + bh - 1) // bh, (cols + 127) // 128), dtype=np.float32)
+    si = np.empty(((rows + bh - 1) // bh, (cols + bw - 1) // bw), dtype=np.float32)
     _check(_lib().o_quantize_blockwise(_ptr(xb), rows, cols, fmt, gran, mode, _ptr(q), _ptr(si),
                                        nthreads or default_threads()), "quantize_blockwise")
     return q, si
+
+
+def e8m0_decode(codes) -> np.ndarray:
+    """E8M0 scale bytes as fp64 values: 2^(code - 127), NaN for code 255."""
+    c = np.asarray(codes, dtype=np.int64)
+    out = np.ldexp(1.0, c - 127)
+    return np.where(c == 255, np.nan, out)
+
+
+def e8m0_of_pow2(values) -> np.ndarray:
+    """The E8M0 byte of each power of two in [2^-127, 2^127] (its binary exponent + 127)."""
+    v = np.asarray(values, dtype=np.float64)
+    m, e = np.frexp(v)                   # v = m * 2^e, m in [0.5, 1)
+    if not np.all(m == 0.5):
+        raise ValueError("not a power of two")
+    code = e - 1 + 127
+    if np.any(code < 0) or np.any(code > 254):
+        raise ValueError("outside the E8M0 range")
+    return code.astype(np.uint8)
+
+
+def quantize_mx(x, fmt: int, nthreads: int | None = None):
+    """Microscaling quantization of a 2-D bf16 matrix: blocks of 32 consecutive elements along
+    each row, the power-of-2 scale rule, dequantization factors stored as E8M0 bytes.
+
+    Returns (codes uint8 [R, C], scale bytes uint8 [R, ceil(C/32)])."""
+    q, si = quantize_blockwise(x, fmt, BLOCK_1x32, SCALE_POW2, nthreads)
+    return q, e8m0_of_pow2(si)
+
+
+def gemm_mx(qa, fa: int, sa_e8m0, qb, fb: int, sb_e8m0) -> np.ndarray:
+    """fp64 reference of the microscaling GEMM C = A . B^T, A[M, K] and B[N, K] stored row-major
+    with one E8M0 scale per 32 consecutive K elements of a row (scale arrays [M, ceil(K/32)] and
+    [N, ceil(K/32)])."""
+    return gemm(FPROP, qa, fa, BLOCK_1x32, e8m0_decode(sa_e8m0), qb, fb, BLOCK_1x32,
+                e8m0_decode(sb_e8m0))
 
 
 def quantize_columnwise_t(x, fmt: int, mode: int, nthreads: int | None = None):

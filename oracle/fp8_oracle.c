@@ -47,7 +47,7 @@
 #include <string.h>
 
 enum { O_E4M3 = 0, O_E5M2 = 1 };
-enum { O_BLOCK_1x128 = 0, O_BLOCK_128x128 = 1 };
+enum { O_BLOCK_1x128 = 0, O_BLOCK_128x128 = 1, O_BLOCK_1x32 = 3 };
 enum { O_SCALE_FP32 = 0, O_SCALE_POW2 = 1 };
 
 /* Format parameters, from the bit splits named in [P1] and the readings above. */
@@ -240,6 +240,7 @@ typedef struct {
   int64_t rows, cols;
   int fmt, mode;
   int64_t bh;          /* block height: 1 or 128 */
+  int64_t bw;          /* block width: 128, or 32 (one row by 32 columns) */
   int64_t nbc;         /* blocks per row of blocks */
   uint8_t* q;
   float* scale_inv;    /* logical [ceil(rows/bh)][nbc] */
@@ -251,8 +252,8 @@ static void o_bw_task(void* p, int64_t b, int64_t e) {
     int64_t r0 = bi * c->bh;
     int64_t r1 = r0 + c->bh < c->rows ? r0 + c->bh : c->rows;
     for (int64_t bj = 0; bj < c->nbc; ++bj) {
-      int64_t c0 = bj * 128;
-      int64_t c1 = c0 + 128 < c->cols ? c0 + 128 : c->cols;
+      int64_t c0 = bj * c->bw;
+      int64_t c1 = c0 + c->bw < c->cols ? c0 + c->bw : c->cols;
       /* step 1: largest magnitude in the block (finite flag for NaN / Inf) */
       float amax = 0.0f;
       int finite = 1;
@@ -282,13 +283,15 @@ static void o_bw_task(void* p, int64_t b, int64_t e) {
 /*
  * Blockwise quantization of a contiguous row-major bf16 matrix x[rows][cols].
  * gran O_BLOCK_1x128: a block is one row by 128 consecutive columns;
- * gran O_BLOCK_128x128: a block is a 128x128 tile.  Edge blocks are clipped.
+ * gran O_BLOCK_128x128: a block is a 128x128 tile;
+ * gran O_BLOCK_1x32: a block is one row by 32 consecutive columns (the microscaling blocks).
+ * Edge blocks are clipped.
  * q[rows][cols] receives the codes; scale_inv receives one fp32 per block in the logical
  * order [block row][block column].  Returns 0, or -1 on a bad argument.
  */
 int o_quantize_blockwise(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int gran,
                          int mode, uint8_t* q, float* scale_inv, int nthreads) {
-  if (!o_fmt_ok(fmt) || (gran != O_BLOCK_1x128 && gran != O_BLOCK_128x128) ||
+  if (!o_fmt_ok(fmt) || (gran != O_BLOCK_1x128 && gran != O_BLOCK_128x128 && gran != O_BLOCK_1x32) ||
       (mode != O_SCALE_FP32 && mode != O_SCALE_POW2) || rows < 0 || cols < 0)
     return -1;
   if (rows == 0 || cols == 0) return 0;
@@ -299,8 +302,9 @@ int o_quantize_blockwise(const uint16_t* x, int64_t rows, int64_t cols, int fmt,
   c.cols = cols;
   c.fmt = fmt;
   c.mode = mode;
-  c.bh = gran == O_BLOCK_1x128 ? 1 : 128;
-  c.nbc = (cols + 127) / 128;
+  c.bh = gran == O_BLOCK_128x128 ? 128 : 1;
+  c.bw = gran == O_BLOCK_1x32 ? 32 : 128;
+  c.nbc = (cols + c.bw - 1) / c.bw;
   c.q = q;
   c.scale_inv = scale_inv;
   int64_t nbr = (rows + c.bh - 1) / c.bh;
