@@ -22,7 +22,7 @@ LIB = os.path.join(HERE, "libfp8bs.so")
 BENCH_LIB = os.path.join(HERE, "libfp8bs_bench.so")
 BENCH_SOURCES = ["bench_stream.hip", "bench_mfma.hip"]
 # (the GEMM kernels are split over several files so that they compile in parallel)
-SOURCES = ["gemm_fprop.hip", "gemm_fprop_pow2.hip", "gemm_dgrad.hip", "gemm_wgrad.hip",
+SOURCES = ["gemm_fprop.hip", "gemm_fprop_pow2.hip", "gemm_mx.hip", "gemm_dgrad.hip", "gemm_wgrad.hip",
            "gemm_grouped.hip", "gemm_qout.hip", "gemm.hip", "quantize.hip", "quantize_t.hip",
            "attention.hip"]
 HEADERS = [os.path.join(CSRC, "common.h"), os.path.join(CSRC, "gemm_impl.h"),

@@ -1,6 +1,6 @@
 // Block-scaled FP8 GEMM entry points (dense and grouped; fp32 and power-of-2 scales; with an
 // explicit tile configuration): argument checks and the choice of kernel set.  The kernels are
-// instantiated per layout in gemm_fprop.hip, gemm_fprop_pow2.hip, gemm_dgrad.hip,
+// instantiated per layout in gemm_fprop.hip, gemm_fprop_pow2.hip, gemm_mx.hip, gemm_dgrad.hip,
 // gemm_wgrad.hip and gemm_grouped.hip; the device code is in gemm_impl.h.
 //
 // Method: "NVIDIA NeMo RL logra una aceleración del 48% con entrenamiento de precisión FP8 de
@@ -33,6 +33,29 @@ int gemm_dense(bool pow2, int tile, int layout, int64_t M, int64_t N, int64_t K,
   }
 }
 
+// Microscaling GEMM (fprop): the dense checks with per-tensor stand-ins for the scales, then
+// the scale words of both operands: row r, K block kb at byte r * ld_s + 4 kb.
+int gemm_mx_entry(int tile, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int fa,
+                  const void* sa, int64_t ld_sa, const void* B, int64_t ldb, int fb,
+                  const void* sb, int64_t ld_sb, void* C, int64_t ldc, hipStream_t st) {
+  GemmParams p{};
+  bool tensor_only = false, empty = false, b_rows = false;
+  const float* fa_s = static_cast<const float*>(sa);
+  const float* fb_s = static_cast<const float*>(sb);
+  int s = dense_params(FP8BS_FPROP, M, N, K, A, lda, fa, FP8BS_PER_TENSOR, fa_s, B, ldb, fb,
+                       FP8BS_PER_TENSOR, fb_s, C, ldc, p, tensor_only, empty, b_rows);
+  if (s != FP8BS_OK || empty) return s;
+  if (K == 0) return gemm_fprop_fp32(kScaleTensor, fa, fb, p, tile, st);   // zeros
+  const int64_t chunks = ceil_div(K, 32);
+  if (ld_sa < chunks || ld_sb < chunks) return FP8BS_ERR_SHAPE;
+  if (ld_sa % 4 || ld_sb % 4 || !aligned4(sa) || !aligned4(sb)) return FP8BS_ERR_ALIGN;
+  // scale arrays below 4 GiB (the kernels size their scale DMA in 32 bits)
+  if (M * ld_sa >= (int64_t(1) << 32) || N * ld_sb >= (int64_t(1) << 32)) return FP8BS_ERR_SHAPE;
+  p.sa_ks = 1; p.sa_rs = ld_sa / 4; p.sa_rshift = 0; p.sa_bytes = M * ld_sa;
+  p.sb_ks = 1; p.sb_rs = ld_sb / 4; p.sb_bytes = N * ld_sb;
+  return gemm_fprop_mx(fa, fb, p, tile, st);
+}
+
 int gemm_grouped_entry(bool pow2, int tile, int32_t G, const int64_t* offsets, int64_t M,
                        int64_t N, int64_t K, const void* A, int64_t lda, int fa, const float* sa,
                        const void* B, int64_t ldb, int fb, const float* sb, void* C, int64_t ldc,
@@ -51,6 +74,14 @@ int gemm_grouped_entry(bool pow2, int tile, int32_t G, const int64_t* offsets, i
 }  // namespace fp8bs
 
 using namespace fp8bs;
+
+extern "C" int fp8_gemm_mx(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int fa,
+                           const void* scale_e8m0_a, int64_t ld_sa, const void* B, int64_t ldb,
+                           int fb, const void* scale_e8m0_b, int64_t ld_sb, void* C_bf16,
+                           int64_t ldc, void* stream) {
+  return gemm_mx_entry(FP8BS_TILE_AUTO, M, N, K, A, lda, fa, scale_e8m0_a, ld_sa, B, ldb, fb,
+                       scale_e8m0_b, ld_sb, C_bf16, ldc, static_cast<hipStream_t>(stream));
+}
 
 extern "C" int fp8_gemm_blockscaled(int layout, int64_t M, int64_t N, int64_t K, const void* A,
                                     int64_t lda, int fa, int ga, const float* scale_inv_a,

@@ -92,6 +92,10 @@ constexpr int kScaleHw = 2;       // power-of-2 block scales, applied by the MFM
 // element by its own sa[m] * sb[n]; the MFMA takes a per-lane E8M0 weight scale.
 constexpr int kScaleFoldRows = 3;
 constexpr int kScaleHwRows = 4;
+// Microscaling: E8M0 scale bytes, one per 32 K elements of every row of both operands.  The
+// four bytes of a row and K block travel as one word (as the 1x128 scales of kScaleHwRows do),
+// and each lane gives the MFMA the byte of its own 32-wide k chunk.
+constexpr int kScaleMx = 5;
 
 constexpr int kGroupM = 8;      // tile-rows per L2 group in the tile order
 constexpr int kLdsBytes = 160 * 1024;
@@ -238,6 +242,16 @@ __device__ __forceinline__ FragBase<true> frag_base_k(int li, int g, int u0) {
   const int sw = swz_k(li);
   const uint32_t r = (uint32_t)(u0 + li) * 128u;
   return FragBase<true>{{r + ((((2 * g) ^ sw) << 4)), r + ((((2 * g + 1) ^ sw) << 4))}};
+}
+// The K order of the 16x16x128 FP8 MFMA as its block scales see it: a lane's first 16 bytes are
+// k = 16 g .. 16 g + 15 and its last 16 bytes k = 64 + 16 g .., so the 32-wide scale chunk c
+// (the scale byte of lane 16 c + row) covers k = 32 c .. 32 c + 31 only when the fragments are
+// read in that order (16-byte chunks g and g + 4).  Products summed without per-chunk scales do
+// not depend on the order, so only the microscaling path reads its K-major fragments this way.
+__device__ __forceinline__ FragBase<true> frag_base_k_mx(int li, int g, int u0) {
+  const int sw = swz_k(li);
+  const uint32_t r = (uint32_t)(u0 + li) * 128u;
+  return FragBase<true>{{r + (((g ^ sw) << 4)), r + ((((g + 4) ^ sw) << 4))}};
 }
 __device__ __forceinline__ FragBase<false> frag_base_mn(int li, int g, int u0) {
   FragBase<false> b;
@@ -670,9 +684,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
   const int64_t sb_bytes = p.sb_bytes;
   constexpr bool XK = LAYOUT != FP8BS_WGRAD;   // activation side K-major?
   constexpr bool WK = LAYOUT == FP8BS_FPROP;   // weight side K-major?
-  constexpr bool ROWS = SM == kScaleFoldRows || SM == kScaleHwRows;   // 1x128 weight scales
+  // per-row weight scale words: 1x128 weight scales, or the microscaling bytes
+  constexpr bool ROWS = SM == kScaleFoldRows || SM == kScaleHwRows || SM == kScaleMx;
   constexpr bool FOLD = SM == kScaleFold || SM == kScaleFoldRows;
-  constexpr bool HW = SM == kScaleHw || SM == kScaleHwRows;
+  constexpr bool HW = SM == kScaleHw || SM == kScaleHwRows || SM == kScaleMx;
+  constexpr bool MX = SM == kScaleMx;
   constexpr bool STAGED = SM != kScaleTensor;   // block scales staged in LDS with the operands
   constexpr int BM = C::BM, BN = C::BN, NI = C::kNI, NJ = C::kNJ;
   // (PERSIST, a loop over tiles: the thread id is made opaque per tile, so that values derived
@@ -855,13 +871,27 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
       uint8_t* st = stage_ptr(kb);
       if constexpr (XK) zero_k_tail<BM, C::kThreads>(st, krem);
       if constexpr (WK) zero_k_tail<BN, C::kThreads>(st + C::kXBytes, krem);
+      if constexpr (MX) {
+        // scale bytes of the 32-wide chunks past K (row padding, any value -- an E8M0 NaN
+        // would turn the zeroed products into NaN) become 2^0
+        const int keep = (krem + 31) >> 5;
+        const uint32_t mask = keep >= 4 ? 0xFFFFFFFFu : ((1u << (8 * keep)) - 1u);
+        uint32_t* sw = reinterpret_cast<uint32_t*>(st + C::kXBytes + C::kWBytes);
+        for (int id = threadIdx.x; id < BM + BN; id += C::kThreads)
+          sw[id] = (sw[id] & mask) | (0x7F7F7F7Fu & ~mask);
+      }
       __syncthreads();
     }
   };
   // Fragment address bases of the wave's pieces (per tile; frag_at_tile adds a stage's address
   // once per block), and the byte offset of the lane's first activation scale in a stage.
-  const FragBase<XK> xb = frag_base<XK>(li, g, wm * C::kWTM);
-  const FragBase<WK> wb = frag_base<WK>(li, g, wn * C::kWTN);
+  FragBase<XK> xb = frag_base<XK>(li, g, wm * C::kWTM);
+  FragBase<WK> wb = frag_base<WK>(li, g, wn * C::kWTN);
+  if constexpr (MX) {
+    static_assert(XK && WK, "microscaling: K-major operands (fprop)");
+    xb = frag_base_k_mx(li, g, wm * C::kWTM);
+    wb = frag_base_k_mx(li, g, wn * C::kWTN);
+  }
   const uint32_t sc_lane = (uint32_t)(C::kXBytes + C::kWBytes + 4 * (wm * C::kWTM + li));
   auto scales_of = [&](const uint8_t* st) {
     return reinterpret_cast<const float*>(st + C::kXBytes + C::kWBytes);
@@ -897,7 +927,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
     if constexpr (ROWS && HW) {
       const float* sat = scales_of(st);
 #pragma unroll
-      for (int i = 0; i < NI; ++i) wbr[i] = e8m0_of(sat[BM + wn * C::kWTN + 16 * i + li]);
+      for (int i = 0; i < NI; ++i) {
+        const float v = sat[BM + wn * C::kWTN + 16 * i + li];
+        wbr[i] = MX ? (int)((__float_as_uint(v) >> (8 * g)) & 0xFFu) : e8m0_of(v);
+      }
     }
   };
   // The weight-side bases of a stage: piece i by frag_piece(wbase, i).
@@ -989,7 +1022,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
         wsn = w_bases(stn);
         __builtin_amdgcn_sched_barrier(0);
       }
-      const int xbyte = HW ? e8m0_of(ccur) : 0;   // activation scale of this lane's row
+      // activation scale of this lane's row (microscaling: and of its k chunk)
+      const int xbyte = !HW ? 0 : MX ? (int)((__float_as_uint(ccur) >> (8 * g)) & 0xFFu) : e8m0_of(ccur);
       // The piece's MFMAs and folds issue at raised wave priority: when both waves of a SIMD
       // are ready, the one feeding the matrix core goes first (measured 1.5% faster than equal
       // priorities, 1.1% faster than raising it only after the hand-over).
@@ -1567,12 +1601,14 @@ inline int grouped_params(int32_t num_groups, const int64_t* group_offsets, int6
 
 // The dense kernels of one layout (and scale family) are instantiated in a translation unit of
 // their own, so that the library's sources compile in parallel: gemm_fprop.hip (fp32 block,
-// 1x128-both and per-tensor scales), gemm_fprop_pow2.hip (E8M0 scales), gemm_dgrad.hip,
+// 1x128-both and per-tensor scales), gemm_fprop_pow2.hip (E8M0 scales), gemm_mx.hip
+// (microscaling), gemm_dgrad.hip,
 // gemm_wgrad.hip, gemm_grouped.hip.  sm is one of the kScale* modes above; hidden symbols, not
 // part of the C ABI.
 #define FP8BS_HIDDEN __attribute__((visibility("hidden")))
 FP8BS_HIDDEN int gemm_fprop_fp32(int sm, int fa, int fb, const GemmParams& p, int tile, hipStream_t st);
 FP8BS_HIDDEN int gemm_fprop_pow2(int sm, int fa, int fb, const GemmParams& p, int tile, hipStream_t st);
+FP8BS_HIDDEN int gemm_fprop_mx(int fa, int fb, const GemmParams& p, int tile, hipStream_t st);
 FP8BS_HIDDEN int gemm_dgrad(int sm, int fa, int fb, const GemmParams& p, int tile, hipStream_t st);
 FP8BS_HIDDEN int gemm_wgrad(int sm, int fa, int fb, const GemmParams& p, int tile, hipStream_t st);
 FP8BS_HIDDEN int gemm_grouped(bool pow2, int fa, int fb, int cus, const GemmParams& p, int tile,

@@ -113,6 +113,47 @@ __global__ __launch_bounds__(kThreads) void quant_1x128_kernel(
   quant_1x128_body<FMT, POW2, VEC>(x, rows, cols, ld_x, q, ld_q, scale_inv, blockIdx.x);
 }
 
+// ---------------------------------------------------------------- microscaling (1x32) blocks
+// The 1x128 geometry (32 rows x 128 columns per workgroup, 16 elements per lane) with a block
+// per pair of lanes: the pair's amax, the power-of-2 scale, and as the stored dequantization
+// factor its E8M0 byte (the binary exponent of 1/s, biased by 127).  The four bytes of a row's
+// 128 columns are gathered into the group's first lane and leave as one 4-byte store when the
+// scale rows allow it (S4), else byte by byte; bytes past ceil(cols / 32) are not written.
+template <int FMT, bool VEC, bool S4>
+__global__ __launch_bounds__(kThreads) void quant_mx_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+    uint8_t* __restrict__ q, int64_t ld_q, uint8_t* __restrict__ se, int64_t ld_s) {
+  const int t = threadIdx.x;
+  const int64_t nbc = (cols + 127) >> 7;
+  const int64_t bid = blockIdx.x;
+  const int64_t cb = bid % nbc;
+  const int64_t c0 = cb * 128 + (t & 7) * 16;
+  const int64_t r = (bid / nbc) * kRows1 + (t >> 3);
+  uint32_t d[8];
+  load16<VEC>(x, rows, cols, ld_x, r, c0, d);
+  uint32_t amax = amax16_bits(d);
+  const uint32_t other = __builtin_amdgcn_mov_dpp(amax, 0xB1, 0xF, 0xF, false);   // lane t ^ 1
+  amax = amax > other ? amax : other;
+  const float s = scale_from_amax_bits<FMT, true>(amax);
+  store16<VEC>(q, rows, cols, ld_q, r, c0, encode_block_values<FMT>(d, s, amax < 0x7F80u));
+  // s = 2^e with e in [-120, 127]: 1/s has the biased exponent 254 - field(s) (0 for 2^-127)
+  const uint32_t code = 254u - ((__float_as_uint(s) >> 23) & 0xFFu);
+  uint32_t w = code | ((uint32_t)__shfl_xor((int)code, 2) << 8);
+  w |= (uint32_t)__shfl_xor((int)w, 4) << 16;
+  if ((t & 7) == 0 && r < rows) {
+    const int64_t chunks = (cols + 31) >> 5;
+    const int64_t k0 = cb * 4;
+    uint8_t* dst = se + r * ld_s + k0;
+    if (S4 && k0 + 4 <= chunks) {
+      *reinterpret_cast<uint32_t*>(dst) = w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (k0 + i < chunks) dst[i] = (uint8_t)(w >> (8 * i));
+    }
+  }
+}
+
 // ---------------------------------------------------------------- 128x128 tiles
 // One workgroup per tile.  Thread t covers columns (t % 8) * 16 .. +16 of rows
 // t / 8 + 32 * i, i = 0..3; the tile amax is reduced across the workgroup through LDS.
@@ -343,6 +384,33 @@ int dispatch_blockwise(bool pow2, bool vec, const uint16_t* x, int64_t rows, int
 }  // namespace fp8bs
 
 using namespace fp8bs;
+
+extern "C" int fp8_quantize_mx(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                               int fmt, void* q_out, int64_t ld_q, void* scale_e8m0_out,
+                               int64_t ld_s, void* stream) {
+  if (!fmt_ok(fmt)) return FP8BS_ERR_ARG;
+  if (rows < 0 || cols < 0 || ld_x < cols || ld_q < cols || ld_s < ceil_div(cols, 32))
+    return FP8BS_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return FP8BS_OK;
+  if (!x_bf16 || !q_out || !scale_e8m0_out) return FP8BS_ERR_NULL;
+  if (ceil_div(rows, kRows1) * ceil_div(cols, 128) > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
+  if (rows > INT64_MAX / ld_x || rows > INT64_MAX / ld_q || rows > INT64_MAX / ld_s)
+    return FP8BS_ERR_SHAPE;
+  const bool vec = aligned16(x_bf16) && aligned16(q_out) && ld_x % 8 == 0 && ld_q % 16 == 0;
+  const bool s4 = aligned4(scale_e8m0_out) && ld_s % 4 == 0;
+  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
+  uint8_t* q = static_cast<uint8_t*>(q_out);
+  uint8_t* se = static_cast<uint8_t*>(scale_e8m0_out);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)(ceil_div(rows, kRows1) * ceil_div(cols, 128)));
+  auto go = [&](auto kernel) { return launch(kernel, grid, dim3(kThreads), st, x, rows, cols, ld_x, q, ld_q, se, ld_s); };
+  if (fmt == FP8BS_E4M3) {
+    if (vec) return s4 ? go(quant_mx_kernel<FP8BS_E4M3, true, true>) : go(quant_mx_kernel<FP8BS_E4M3, true, false>);
+    return s4 ? go(quant_mx_kernel<FP8BS_E4M3, false, true>) : go(quant_mx_kernel<FP8BS_E4M3, false, false>);
+  }
+  if (vec) return s4 ? go(quant_mx_kernel<FP8BS_E5M2, true, true>) : go(quant_mx_kernel<FP8BS_E5M2, true, false>);
+  return s4 ? go(quant_mx_kernel<FP8BS_E5M2, false, true>) : go(quant_mx_kernel<FP8BS_E5M2, false, false>);
+}
 
 extern "C" int fp8_quantize_blockwise(const void* x_bf16, int64_t rows, int64_t cols,
                                       int64_t ld_x, int fmt, int gran, int mode, void* q_out,

@@ -109,6 +109,24 @@ int fp8_quantize_blockwise(const void* x_bf16, int64_t rows, int64_t cols, int64
                            int fmt, int gran, int mode, void* q_out, int64_t ld_q,
                            float* scale_inv_out, void* stream);
 
+/* Microscaling (MXFP8) quantization -- "Infraestructura de Entrenamiento FP8: Precisión Numérica
+ * de Nueva Generación", sections "Estrategias de escalado y estabilidad" (block scaling, MXFP8)
+ * and "Blackwell MXFP8 y NVFP4: mirando hacia adelante" (hardware-accelerated block scaling).
+ * The pages state neither the block size nor the scale format; here a block is 32 consecutive
+ * elements of a row and its scale an E8M0 byte.  Per block: the power-of-2 rule of
+ * fp8_quantize_blockwise in FP8BS_SCALE_POW2 mode (s = the largest power of two with
+ * amax * s <= FMAX; 1 for all-zero or non-finite blocks), codes = the saturating RNE encode of
+ * x * s (NaN inputs give NaN codes), and the stored byte is the E8M0 code of the dequantization
+ * factor 1/s, i.e. its binary exponent + 127 (2^(byte - 127) = 1/s; never 255).
+ *   x_bf16          [rows][ld_x] bf16, device; ld_x >= cols
+ *   q_out           [rows][ld_q] codes, device; ld_q >= cols
+ *   scale_e8m0_out  [rows][ld_s] bytes, device; ld_s >= ceil(cols / 32); byte j of row r is the
+ *                   factor of columns 32 j .. 32 j + 31; bytes past ceil(cols / 32) are left alone
+ * rows == 0 or cols == 0: no-op.  Caller-owned memory, nothing allocated; asynchronous on stream.
+ * Errors: FP8BS_ERR_ARG (fmt), FP8BS_ERR_SHAPE, FP8BS_ERR_NULL, FP8BS_ERR_LAUNCH. */
+int fp8_quantize_mx(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
+                    void* q_out, int64_t ld_q, void* scale_e8m0_out, int64_t ld_s, void* stream);
+
 /*
  * Blockwise quantization of several bf16 matrices in one launch: tensor i is quantized exactly as
  * fp8_quantize_blockwise(x_bf16[i], rows[i], cols[i], ld_x[i], fmt, gran[i], mode, q_out[i],
@@ -282,6 +300,25 @@ int fp8_gemm_blockscaled_qout(int64_t M, int64_t N, int64_t K, const void* A, in
                               int gb, const float* scale_inv_b, int pow2_inputs, void* C_bf16,
                               int64_t ldc, int mode_out, void* Cq, int64_t ldcq,
                               float* cq_scale_inv, void* stream);
+
+/* Microscaling (MXFP8) GEMM, fprop layout -- the sections of fp8_quantize_mx.  C[M][N] (bf16,
+ * round to nearest even) = sum over k of A[m][k] * 2^(sa[m][k/32] - 127) * B[n][k] *
+ * 2^(sb[n][k/32] - 127): A[M][lda] and B[N][ldb] are FP8 codes of formats fa / fb (K-major,
+ * the fp8_gemm_blockscaled fprop operands), sa[M][ld_sa] and sb[N][ld_sb] their E8M0 scale bytes
+ * as fp8_quantize_mx writes them.  The matrix cores apply the scales (the scaled MFMA, one byte
+ * per lane and 32-wide k chunk) and accumulate in fp32.  A scale byte of 255 (E8M0 NaN) makes
+ * the products of its block NaN.
+ *   lda, ldb: multiples of 16, >= K, < 2^23; A, B 16-byte aligned
+ *   ld_sa, ld_sb: multiples of 4, >= ceil(K / 32); sa, sb 4-byte aligned; the arrays hold
+ *   M * ld_sa and N * ld_sb bytes (whole rows: the kernels read each row's bytes of a 128-wide
+ *   K block as one word; bytes of 32-wide chunks past K are read but ignored); each below 4 GiB
+ *   C_bf16: [M][ldc], ldc >= N, 4-byte aligned, even ldc
+ * M == 0 or N == 0: no-op; K == 0: C = 0.  Errors: FP8BS_ERR_ARG (formats), FP8BS_ERR_SHAPE,
+ * FP8BS_ERR_NULL, FP8BS_ERR_ALIGN, FP8BS_ERR_LAUNCH. */
+int fp8_gemm_mx(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int fa,
+                const void* scale_e8m0_a, int64_t ld_sa, const void* B, int64_t ldb, int fb,
+                const void* scale_e8m0_b, int64_t ld_sb, void* C_bf16, int64_t ldc,
+                void* stream);
 
 /* Block-scaled FP8 GEMM with power-of-2 scales -- "NVIDIA NeMo RL logra una aceleración del 48%
  * ...", section "Por qué esto es importante para la economía de la IA" (the power-of-2 scale

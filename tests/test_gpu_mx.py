@@ -1,0 +1,177 @@
+"""Microscaling (MXFP8) path on the GPU against the oracle: fp8_quantize_mx bit for bit (codes
+and E8M0 scale bytes), fp8_gemm_mx within the GEMM tolerance of tests/helpers.py on seeded
+inputs quantized by the oracle (ragged M, N and K, K chunks past K whose padding scale bytes
+hold NaN codes), and the argument checks that need device memory."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_quantize_amd as bsq
+import oracle
+import synth
+from helpers import assert_bytes_equal, gemm_check
+
+pytestmark = pytest.mark.gpu
+E4, E5 = oracle.E4M3, oracle.E5M2
+
+
+def mx_cols(k):
+    return -(-(-(-k // 32)) // 4) * 4
+
+
+def run_quant(gpu, rows, cols, fmt, x=None, pitch=None, seed=0):
+    if x is None:
+        x = synth.activations_with_outliers(rows, cols, seed, f"mx/quant/{rows}x{cols}")
+    ld = pitch if pitch is not None else cols
+    store = torch.zeros((rows, ld), dtype=torch.bfloat16)
+    store[:, :cols] = x
+    xd = store.cuda()[:, :cols]
+    nch = -(-cols // 32)
+    sw = nch if pitch is None else mx_cols(cols) + 4          # byte stores / word stores
+    scales = torch.full((rows, sw), 0xAB, dtype=torch.uint8, device="cuda")
+    q, s = gpu.quantize_mx(xd, fmt, scales=scales)
+    torch.cuda.synchronize()
+    qo, so = oracle.quantize_mx(x, fmt)
+    assert_bytes_equal(q.cpu().numpy(), qo, f"codes {rows}x{cols}")
+    sc = s.cpu().numpy()
+    assert_bytes_equal(sc[:, :nch], so, f"scale bytes {rows}x{cols}")
+    assert np.all(sc[:, nch:] == 0xAB), "bytes past ceil(cols/32) written"
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 32), (3, 70), (37, 300), (64, 4096), (33, 128), (5, 1)])
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_quantize_mx_bit_exact(gpu, rows, cols, fmt):
+    run_quant(gpu, rows, cols, fmt)
+
+
+def test_quantize_mx_word_stores_and_pitch(gpu):
+    run_quant(gpu, 40, 512, E4, pitch=520)     # 16-byte rows, 4-byte scale stores
+    run_quant(gpu, 40, 200, E4, pitch=264)
+
+
+def test_quantize_mx_special_blocks(gpu):
+    x = synth.activations_with_outliers(8, 256, 1, "mx/special")
+    x[0, :32] = 0.0                                   # zero block
+    x[1, 3] = float("nan")                            # NaN block
+    x[2, 40] = float("inf")
+    x[3, 70] = float("-inf")
+    x[4, 96:128] = torch.tensor(1e-40).bfloat16()     # bf16 subnormals: the largest scale
+    x[5, 130] = 3.0e38                                # huge magnitude: the smallest scale
+    run_quant(gpu, 8, 256, E4, x=x)
+    run_quant(gpu, 8, 256, E5, x=x)
+
+
+def test_quantize_mx_full_size(gpu):
+    x = synth.activations_with_outliers(8192, 4096, 0, "bench/8b/qkv/X")
+    run_quant(gpu, 8192, 4096, E4, x=x)
+
+
+def device_codes(q: np.ndarray, ld: int) -> torch.Tensor:
+    rows, cols = q.shape
+    store = torch.full((rows, ld), 0x7F, dtype=torch.uint8)      # NaN codes in the padding
+    store[:, :cols] = torch.from_numpy(q)
+    return store.cuda()[:, :cols]
+
+
+def device_scale_bytes(s: np.ndarray, k: int) -> torch.Tensor:
+    rows, nch = s.shape
+    store = torch.full((rows, mx_cols(k)), 0xFF, dtype=torch.uint8)   # E8M0 NaN in the padding
+    store[:, :nch] = torch.from_numpy(s)
+    return store.cuda()
+
+
+def run_gemm_mx(gpu, M, N, K, fa=E4, fb=E4, seed=0, rows=None):
+    a = synth.activations_with_outliers(M, K, seed, "mx/gemm/A")
+    b = synth.normal((N, K), 0.02, seed, "mx/gemm/B")
+    qa, sa = oracle.quantize_mx(a, fa)
+    qb, sb = oracle.quantize_mx(b, fb)
+    ad, bd = device_codes(qa, -(-K // 16) * 16), device_codes(qb, -(-K // 16) * 16 + 16)
+    ldc = -(-N // 2) * 2 + 8
+    cstore = torch.full((M + 1, ldc), -7.0, dtype=torch.bfloat16, device="cuda")
+    c = cstore[:M, :N]
+    gpu.gemm_mx(ad, device_scale_bytes(sa, K), bd, device_scale_bytes(sb, K), fa, fb, c=c)
+    torch.cuda.synchronize()
+    assert torch.all(cstore[:M, N:] == -7.0) and torch.all(cstore[M] == -7.0), "guard overwritten"
+    adq = oracle.dequantize(qa, fa, oracle.BLOCK_1x32, oracle.e8m0_decode(sa))
+    bdq = oracle.dequantize(qb, fb, oracle.BLOCK_1x32, oracle.e8m0_decode(sb))
+    if rows is not None:
+        adq = adq[rows]
+        c = c[torch.as_tensor(rows, device="cuda")]
+    ref = adq @ bdq.T
+    return gemm_check(c, ref, np.abs(adq) @ np.abs(bdq).T, f"mx {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 128, 128), (300, 260, 200), (129, 384, 512), (1000, 1000, 1000),
+                                   (4160, 256, 384), (256, 256, 160), (100, 300, 96), (17, 33, 32)])
+def test_gemm_mx(gpu, M, N, K):
+    run_gemm_mx(gpu, M, N, K)
+
+
+@pytest.mark.parametrize("fa,fb", [(E5, E4), (E4, E5), (E5, E5)])
+def test_gemm_mx_formats(gpu, fa, fb):
+    run_gemm_mx(gpu, 300, 260, 456, fa, fb)
+
+
+def test_gemm_mx_matches_oracle_gemm_reference(gpu):
+    # the oracle's own microscaling GEMM reference (decoded scale bytes, fp64 product)
+    a = synth.activations_with_outliers(64, 256, 3, "mx/ref/A")
+    b = synth.normal((128, 256), 0.02, 3, "mx/ref/B")
+    qa, sa = oracle.quantize_mx(a, E4)
+    qb, sb = oracle.quantize_mx(b, E4)
+    c = gpu.gemm_mx(device_codes(qa, 256), device_scale_bytes(sa, 256), device_codes(qb, 256),
+                    device_scale_bytes(sb, 256))
+    torch.cuda.synchronize()
+    ref = oracle.gemm_mx(qa, E4, sa, qb, E4, sb)
+    adq = oracle.dequantize(qa, E4, oracle.BLOCK_1x32, oracle.e8m0_decode(sa))
+    bdq = oracle.dequantize(qb, E4, oracle.BLOCK_1x32, oracle.e8m0_decode(sb))
+    gemm_check(c, ref, np.abs(adq) @ np.abs(bdq).T, "mx vs oracle.gemm_mx")
+
+
+def test_gemm_mx_full_size_sampled(gpu):
+    rows = list(range(0, 8192, 97))
+    run_gemm_mx(gpu, 8192, 4096, 4096, rows=rows)
+
+
+def test_gemm_mx_empty_and_k0(gpu):
+    a = torch.zeros((0, 64), dtype=torch.uint8, device="cuda")
+    b = torch.zeros((8, 64), dtype=torch.uint8, device="cuda")
+    s0 = torch.zeros((0, 4), dtype=torch.uint8, device="cuda")
+    s8 = torch.zeros((8, 4), dtype=torch.uint8, device="cuda")
+    assert gpu.gemm_mx(a, s0, b, s8).shape == (0, 8)
+    a = torch.zeros((5, 0), dtype=torch.uint8, device="cuda")
+    b = torch.zeros((6, 0), dtype=torch.uint8, device="cuda")
+    c = torch.full((5, 6), 3.0, dtype=torch.bfloat16, device="cuda")
+    lib = gpu.load()
+    sa = torch.zeros((5, 4), dtype=torch.uint8, device="cuda")
+    sb = torch.zeros((6, 4), dtype=torch.uint8, device="cuda")
+    rc = lib.fp8_gemm_mx(5, 6, 0, a.data_ptr(), 16, E4, sa.data_ptr(), 4, b.data_ptr(), 16, E4,
+                         sb.data_ptr(), 4, c.data_ptr(), 6, None)
+    torch.cuda.synchronize()
+    assert rc == 0 and torch.all(c == 0)
+
+
+def test_mx_argument_checks(gpu):
+    lib = gpu.load()
+    a = torch.zeros((64, 128), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((64, 4), dtype=torch.uint8, device="cuda")
+    c = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
+    def call(**kw):
+        v = dict(M=64, N=64, K=128, A=a.data_ptr(), lda=128, fa=E4, sa=s.data_ptr(), ld_sa=4,
+                 B=a.data_ptr(), ldb=128, fb=E4, sb=s.data_ptr(), ld_sb=4, C=c.data_ptr(), ldc=64)
+        v.update(kw)
+        return lib.fp8_gemm_mx(v["M"], v["N"], v["K"], v["A"], v["lda"], v["fa"], v["sa"], v["ld_sa"],
+                               v["B"], v["ldb"], v["fb"], v["sb"], v["ld_sb"], v["C"], v["ldc"], None)
+    assert call() == bsq.OK
+    torch.cuda.synchronize()
+    assert call(fa=3) == bsq.ERR_ARG
+    assert call(ld_sa=2) == bsq.ERR_SHAPE          # fewer than ceil(K / 32) bytes
+    assert call(ld_sb=6) == bsq.ERR_ALIGN          # not a multiple of 4
+    assert call(sa=s.data_ptr() + 2) == bsq.ERR_ALIGN
+    assert call(sa=None) == bsq.ERR_NULL
+    assert call(lda=100) == bsq.ERR_SHAPE
+    x = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((4, 64), dtype=torch.uint8, device="cuda")
+    se = torch.zeros((4, 2), dtype=torch.uint8, device="cuda")
+    assert lib.fp8_quantize_mx(x.data_ptr(), 4, 64, 64, 2, q.data_ptr(), 64, se.data_ptr(), 2, None) == bsq.ERR_ARG
+    assert lib.fp8_quantize_mx(x.data_ptr(), 4, 64, 64, E4, q.data_ptr(), 64, se.data_ptr(), 1, None) == bsq.ERR_SHAPE
+    assert lib.fp8_quantize_mx(None, 4, 64, 64, E4, q.data_ptr(), 64, se.data_ptr(), 2, None) == bsq.ERR_NULL
