@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--workload", default="llama8b-fprop",
                     choices=["llama8b-fprop", "llama8b-fprop-pow2", "quant-sweep", "moe", "backward",
                              "backward-blockwise", "llama8b-fprop-qout", "kv-decode", "copy", "stream",
-                             "mfma-ceiling"])
+                             "mfma-ceiling", "llama8b-fprop-mx"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pow2", action="store_true",
                     help="moe, backward-blockwise: power-of-2 scales (E8M0 in the MFMA)")
@@ -332,6 +332,91 @@ def bench_llama8b(args, pow2: bool = False):
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_8b(layers, M, mode=mode)
     return result
+
+
+def bench_llama8b_mx(args):
+    """The 8B fprop step with microscaling (MXFP8) operands: every step quantizes all four W and,
+    per layer, X into 32-element row blocks with E8M0 scale bytes (fp8_quantize_mx) and runs
+    fp8_gemm_mx (the scales applied by the scaled MFMA).  Inputs as the default workload."""
+    import block_scaled_quantize_amd as bsq
+    import synth
+    bsq.load()
+    M = args.tokens
+    dev = torch.device("cuda", 0)
+    layers = []
+    for name, k, n in LAYERS_8B:
+        x = synth.activations_with_outliers(M, k, 0, f"bench/8b/{name}/X").to(dev)
+        w = synth.normal((n, k), 0.02, 0, f"bench/8b/{name}/W").to(dev)
+        layers.append(dict(
+            name=name, K=k, N=n, x=x, w=w,
+            qx=torch.empty((M, k), dtype=torch.uint8, device=dev),
+            sx=torch.empty(bsq.mx_scale_shape(M, k), dtype=torch.uint8, device=dev),
+            qw=torch.empty((n, k), dtype=torch.uint8, device=dev),
+            sw=torch.empty(bsq.mx_scale_shape(n, k), dtype=torch.uint8, device=dev),
+            y=torch.empty((M, n), dtype=torch.bfloat16, device=dev)))
+    torch.cuda.synchronize()
+    flops = sum(2.0 * M * L["N"] * L["K"] for L in layers)
+
+    def step(timer=None):
+        for L in layers:
+            def qw():
+                bsq.quantize_mx(L["w"], bsq.E4M3, q=L["qw"], scales=L["sw"])
+            def qx():
+                bsq.quantize_mx(L["x"], bsq.E4M3, q=L["qx"], scales=L["sx"])
+            def mm():
+                bsq.gemm_mx(L["qx"], L["sx"], L["qw"], L["sw"], c=L["y"])
+            if timer is None:
+                qw(); qx(); mm()
+            else:
+                timer.time(("qw", L["name"]), qw)
+                timer.time(("qx", L["name"]), qx)
+                timer.time(("gemm", L["name"]), mm)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    timer = EventTimer()
+    for _ in range(max(3, min(args.steps, 10))):
+        step(timer)
+    torch.cuda.synchronize()
+    per_layer, gemm_ms, gemm_flops = {}, [], []
+    q_bytes, q_ms = 0.0, 0.0
+    for L in layers:
+        g = timer.mean_ms(("gemm", L["name"]))
+        f = 2.0 * M * L["N"] * L["K"]
+        gemm_ms.append(g)
+        gemm_flops.append(f)
+        xb = M * L["K"] * 3 + M * L["K"] / 32
+        wb = L["N"] * L["K"] * 3 + L["N"] * L["K"] / 32
+        qx_ms, qw_ms = timer.mean_ms(("qx", L["name"])), timer.mean_ms(("qw", L["name"]))
+        q_bytes += xb + wb
+        q_ms += qx_ms + qw_ms
+        per_layer[L["name"]] = dict(gemm_us=round(g * 1e3, 2), gemm_tflops=round(f / g / 1e9, 1),
+                                    quant_x_us=round(qx_ms * 1e3, 2), quant_w_us=round(qw_ms * 1e3, 2))
+    achieved = float(np.mean(gemm_flops)) / float(np.mean(gemm_ms)) / 1e9
+    return dict(
+        metric="microscaling FP8 GEMM TFLOP/s (+quantize GB/s), % of MI355X FP8/HBM peak",
+        value=round(flops / dt / 1e12, 2), unit="TFLOP/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=round(dt * 1e3, 4), higher_is_better=True,
+        scaling="weak", vs_baseline=None, dtype="fp8e4m3 x fp8e4m3 -> fp32 acc -> bf16",
+        data="synthetic",
+        config=dict(workload="llama3.1-8b-fprop-linear-mxfp8", tokens=M,
+                    layers="qkv 4096->6144, o 4096->4096, gate_up 4096->28672, down 14336->4096",
+                    scales="E8M0 bytes, one per 32 K elements of every row of X and W (all four W "
+                           "and every X re-quantized each step)", parallelism="single GPU"),
+        roofline=dict(bound="mfma", achieved=round(achieved, 1), peak=FP8_PEAK_TFLOPS,
+                      unit="TFLOP/s", frac=round(achieved / FP8_PEAK_TFLOPS, 4), traffic=None,
+                      kernel="gemm_persistent_kernel<Cfg<256,256,2,4>,FPROP,E4M3,E4M3,mx>",
+                      mean_launch_us=round(float(np.mean(gemm_ms)) * 1e3, 2)),
+        gemm_only_tflops=round(sum(gemm_flops) / sum(gemm_ms) / 1e9, 1),
+        quant_gbps=round(q_bytes / q_ms / 1e6, 1),
+        quant_hbm_frac=round(q_bytes / q_ms / 1e6 / HBM_PEAK_GBPS, 4),
+        layers=per_layer)
 
 
 def cpu_baseline_8b(layers, M, rows: int | None = None, min_seconds: float = 10.0, mode: int = 0):
@@ -996,6 +1081,8 @@ def main():
         res = bench_llama8b(args)
     elif args.workload == "llama8b-fprop-pow2":
         res = bench_llama8b(args, pow2=True)
+    elif args.workload == "llama8b-fprop-mx":
+        res = bench_llama8b_mx(args)
     elif args.workload == "quant-sweep":
         res = bench_quant_sweep(args)
     elif args.workload == "moe":

@@ -63,9 +63,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.fp8bs_status_string.restype = ctypes.c_char_p
     lib.fp8_quantize_blockwise.argtypes = [vp, i64, i64, i64, i32, i32, i32, vp, i64, vp, vp]
     lib.fp8_quantize_columnwise_t.argtypes = [vp, i64, i64, i64, i32, i32, vp, i64, vp, vp]
-    lib.fp8_quantize_mx.argtypes = [vp, i64, i64, i64, i32, vp, i64, vp, i64, vp]
-    lib.fp8_gemm_mx.argtypes = [i64, i64, i64, vp, i64, i32, vp, i64, vp, i64, i32, vp, i64, vp,
-                                i64, vp]
+    lib.fp8_quantize_mx.argtypes = [vp, i64, i64, i64, i32, vp, i64, vp, vp]
+    lib.fp8_gemm_mx.argtypes = [i64, i64, i64, vp, i64, i32, vp, vp, i64, i32, vp, vp, i64, vp]
     lib.fp8_quantize_blockwise_batched.argtypes = [i32, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp]
     lib.fp8_quantize_delayed.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.fp8_quantize_delayed_noalloc.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp]
@@ -190,41 +189,36 @@ def quantize_blockwise(x: torch.Tensor, fmt: int, gran: int, mode: int = SCALE_F
     return q, scale_inv
 
 
-def mx_scale_cols(cols: int) -> int:
-    """Bytes per row of a microscaling scale array for `cols` elements: one per 32, padded to a
-    multiple of 4 (the pitch fp8_gemm_mx needs)."""
-    return _ceil(_ceil(cols, 32), 4) * 4
+def mx_scale_shape(rows: int, cols: int) -> tuple[int, int, int]:
+    """Shape of a microscaling scale array: [ceil(cols / 128)][rows][4] E8M0 bytes."""
+    return (_ceil(cols, 128), rows, 4)
 
 
 def quantize_mx(x: torch.Tensor, fmt: int, q: torch.Tensor | None = None,
                 scales: torch.Tensor | None = None, stream=None):
     """Microscaling quantization of a 2-D bf16 matrix: 32-element row blocks, E8M0 scale bytes.
 
-    Returns (codes uint8 [rows, cols], scale bytes uint8 [rows, mx_scale_cols(cols)]; the
-    padding bytes past ceil(cols / 32) of a new array are zero)."""
+    Returns (codes uint8 [rows, cols], scale bytes uint8 mx_scale_shape(rows, cols))."""
     if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be a 2-D bf16 matrix with unit column stride")
     rows, cols = x.shape
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     if scales is None:
-        scales = torch.zeros((rows, mx_scale_cols(cols)), dtype=torch.uint8, device=x.device)
+        scales = torch.empty(mx_scale_shape(rows, cols), dtype=torch.uint8, device=x.device)
     _need_matrix(q, (rows, cols), torch.uint8, "q")
-    if scales.dtype != torch.uint8 or scales.dim() != 2 or scales.shape[0] != rows or \
-            scales.shape[1] < _ceil(cols, 32) or scales.stride(1) != 1:
-        raise ValueError("scales must be uint8 [rows, >= ceil(cols / 32)] with unit column stride")
+    _need(scales, mx_scale_shape(rows, cols), torch.uint8, "scales")
     _check(load().fp8_quantize_mx(_ptr(x), rows, cols, x.stride(0), fmt, _ptr(q), q.stride(0),
-                                  _ptr(scales), scales.stride(0), _stream(stream)),
-           "fp8_quantize_mx")
+                                  _ptr(scales), _stream(stream)), "fp8_quantize_mx")
     return q, scales
 
 
 def gemm_mx(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor,
             fa: int = E4M3, fb: int = E4M3, c: torch.Tensor | None = None,
             stream=None) -> torch.Tensor:
-    """Microscaling FP8 GEMM C[M, N] = A[M, K] . B[N, K]^T with E8M0 scale bytes sa[M, ld_sa],
-    sb[N, ld_sb] (one per 32 K elements, pitches multiples of 4: mx_scale_cols(K) for arrays
-    from quantize_mx), bf16 output."""
+    """Microscaling FP8 GEMM C[M, N] = A[M, K] . B[N, K]^T with E8M0 scale bytes
+    sa mx_scale_shape(M, K) and sb mx_scale_shape(N, K) (as quantize_mx writes them), bf16
+    output."""
     if a.dtype != torch.uint8 or b.dtype != torch.uint8 or a.dim() != 2 or b.dim() != 2:
         raise ValueError("a and b must be 2-D uint8 code matrices")
     (M, K), N = a.shape, b.shape[0]
@@ -232,17 +226,13 @@ def gemm_mx(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor
         raise ValueError("K mismatch")
     _need_matrix(a, a.shape, torch.uint8, "a")
     _need_matrix(b, b.shape, torch.uint8, "b")
-    for t, rows, what in ((sa, M, "sa"), (sb, N, "sb")):
-        if t.dtype != torch.uint8 or t.dim() != 2 or t.shape[0] != rows or t.stride(1) != 1 or \
-                t.shape[1] < _ceil(K, 32) or t.stride(0) < t.shape[1] or \
-                (rows > 1 and t.stride(0) != t.shape[1]):
-            raise ValueError(f"{what} must be uint8 [{rows}, >= ceil(K / 32)], rows contiguous")
+    _need(sa, mx_scale_shape(M, K), torch.uint8, "sa")
+    _need(sb, mx_scale_shape(N, K), torch.uint8, "sb")
     if c is None:
         c = _bf16_out(M, N, a.device)
     _need_matrix(c, (M, N), torch.bfloat16, "c")
-    _check(load().fp8_gemm_mx(M, N, K, _ptr(a), a.stride(0), fa, _ptr(sa), sa.stride(0), _ptr(b),
-                              b.stride(0), fb, _ptr(sb), sb.stride(0), _ptr(c), c.stride(0),
-                              _stream(stream)), "fp8_gemm_mx")
+    _check(load().fp8_gemm_mx(M, N, K, _ptr(a), a.stride(0), fa, _ptr(sa), _ptr(b), b.stride(0),
+                              fb, _ptr(sb), _ptr(c), c.stride(0), _stream(stream)), "fp8_gemm_mx")
     return c
 
 

@@ -34,10 +34,10 @@ int gemm_dense(bool pow2, int tile, int layout, int64_t M, int64_t N, int64_t K,
 }
 
 // Microscaling GEMM (fprop): the dense checks with per-tensor stand-ins for the scales, then
-// the scale words of both operands: row r, K block kb at byte r * ld_s + 4 kb.
+// the scale words of both operands: row r, K block kb at word kb * rows + r (the 1x128 layout).
 int gemm_mx_entry(int tile, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int fa,
-                  const void* sa, int64_t ld_sa, const void* B, int64_t ldb, int fb,
-                  const void* sb, int64_t ld_sb, void* C, int64_t ldc, hipStream_t st) {
+                  const void* sa, const void* B, int64_t ldb, int fb, const void* sb, void* C,
+                  int64_t ldc, hipStream_t st) {
   GemmParams p{};
   bool tensor_only = false, empty = false, b_rows = false;
   const float* fa_s = static_cast<const float*>(sa);
@@ -46,13 +46,12 @@ int gemm_mx_entry(int tile, int64_t M, int64_t N, int64_t K, const void* A, int6
                        FP8BS_PER_TENSOR, fb_s, C, ldc, p, tensor_only, empty, b_rows);
   if (s != FP8BS_OK || empty) return s;
   if (K == 0) return gemm_fprop_fp32(kScaleTensor, fa, fb, p, tile, st);   // zeros
-  const int64_t chunks = ceil_div(K, 32);
-  if (ld_sa < chunks || ld_sb < chunks) return FP8BS_ERR_SHAPE;
-  if (ld_sa % 4 || ld_sb % 4 || !aligned4(sa) || !aligned4(sb)) return FP8BS_ERR_ALIGN;
+  if (!aligned4(sa) || !aligned4(sb)) return FP8BS_ERR_ALIGN;
+  const int64_t nkb = ceil_div(K, 128);
   // scale arrays below 4 GiB (the kernels size their scale DMA in 32 bits)
-  if (M * ld_sa >= (int64_t(1) << 32) || N * ld_sb >= (int64_t(1) << 32)) return FP8BS_ERR_SHAPE;
-  p.sa_ks = 1; p.sa_rs = ld_sa / 4; p.sa_rshift = 0; p.sa_bytes = M * ld_sa;
-  p.sb_ks = 1; p.sb_rs = ld_sb / 4; p.sb_bytes = N * ld_sb;
+  if (nkb * M * 4 >= (int64_t(1) << 32) || nkb * N * 4 >= (int64_t(1) << 32)) return FP8BS_ERR_SHAPE;
+  p.sa_ks = M; p.sa_rs = 1; p.sa_rshift = 0; p.sa_bytes = nkb * M * 4;
+  p.sb_ks = N; p.sb_rs = 1; p.sb_bytes = nkb * N * 4;
   return gemm_fprop_mx(fa, fb, p, tile, st);
 }
 
@@ -76,11 +75,10 @@ int gemm_grouped_entry(bool pow2, int tile, int32_t G, const int64_t* offsets, i
 using namespace fp8bs;
 
 extern "C" int fp8_gemm_mx(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int fa,
-                           const void* scale_e8m0_a, int64_t ld_sa, const void* B, int64_t ldb,
-                           int fb, const void* scale_e8m0_b, int64_t ld_sb, void* C_bf16,
-                           int64_t ldc, void* stream) {
-  return gemm_mx_entry(FP8BS_TILE_AUTO, M, N, K, A, lda, fa, scale_e8m0_a, ld_sa, B, ldb, fb,
-                       scale_e8m0_b, ld_sb, C_bf16, ldc, static_cast<hipStream_t>(stream));
+                           const void* scale_e8m0_a, const void* B, int64_t ldb, int fb,
+                           const void* scale_e8m0_b, void* C_bf16, int64_t ldc, void* stream) {
+  return gemm_mx_entry(FP8BS_TILE_AUTO, M, N, K, A, lda, fa, scale_e8m0_a, B, ldb, fb,
+                       scale_e8m0_b, C_bf16, ldc, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int fp8_gemm_blockscaled(int layout, int64_t M, int64_t N, int64_t K, const void* A,

@@ -117,12 +117,13 @@ __global__ __launch_bounds__(kThreads) void quant_1x128_kernel(
 // The 1x128 geometry (32 rows x 128 columns per workgroup, 16 elements per lane) with a block
 // per pair of lanes: the pair's amax, the power-of-2 scale, and as the stored dequantization
 // factor its E8M0 byte (the binary exponent of 1/s, biased by 127).  The four bytes of a row's
-// 128 columns are gathered into the group's first lane and leave as one 4-byte store when the
-// scale rows allow it (S4), else byte by byte; bytes past ceil(cols / 32) are not written.
-template <int FMT, bool VEC, bool S4>
+// 128 columns are gathered into the group's first lane and leave as one 4-byte word at
+// [column block][row] (the blocks of a column block contiguous over the rows, as the 1x128
+// scales); chunks past the matrix are empty blocks: 127 (2^0).
+template <int FMT, bool VEC>
 __global__ __launch_bounds__(kThreads) void quant_mx_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
-    uint8_t* __restrict__ q, int64_t ld_q, uint8_t* __restrict__ se, int64_t ld_s) {
+    uint8_t* __restrict__ q, int64_t ld_q, uint32_t* __restrict__ se) {
   const int t = threadIdx.x;
   const int64_t nbc = (cols + 127) >> 7;
   const int64_t bid = blockIdx.x;
@@ -140,18 +141,7 @@ __global__ __launch_bounds__(kThreads) void quant_mx_kernel(
   const uint32_t code = 254u - ((__float_as_uint(s) >> 23) & 0xFFu);
   uint32_t w = code | ((uint32_t)__shfl_xor((int)code, 2) << 8);
   w |= (uint32_t)__shfl_xor((int)w, 4) << 16;
-  if ((t & 7) == 0 && r < rows) {
-    const int64_t chunks = (cols + 31) >> 5;
-    const int64_t k0 = cb * 4;
-    uint8_t* dst = se + r * ld_s + k0;
-    if (S4 && k0 + 4 <= chunks) {
-      *reinterpret_cast<uint32_t*>(dst) = w;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (k0 + i < chunks) dst[i] = (uint8_t)(w >> (8 * i));
-    }
-  }
+  if ((t & 7) == 0 && r < rows) se[cb * rows + r] = w;
 }
 
 // ---------------------------------------------------------------- 128x128 tiles
@@ -387,29 +377,24 @@ using namespace fp8bs;
 
 extern "C" int fp8_quantize_mx(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
                                int fmt, void* q_out, int64_t ld_q, void* scale_e8m0_out,
-                               int64_t ld_s, void* stream) {
+                               void* stream) {
   if (!fmt_ok(fmt)) return FP8BS_ERR_ARG;
-  if (rows < 0 || cols < 0 || ld_x < cols || ld_q < cols || ld_s < ceil_div(cols, 32))
-    return FP8BS_ERR_SHAPE;
+  if (rows < 0 || cols < 0 || ld_x < cols || ld_q < cols) return FP8BS_ERR_SHAPE;
   if (rows == 0 || cols == 0) return FP8BS_OK;
   if (!x_bf16 || !q_out || !scale_e8m0_out) return FP8BS_ERR_NULL;
   if (ceil_div(rows, kRows1) * ceil_div(cols, 128) > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
-  if (rows > INT64_MAX / ld_x || rows > INT64_MAX / ld_q || rows > INT64_MAX / ld_s)
-    return FP8BS_ERR_SHAPE;
+  if (rows > INT64_MAX / ld_x || rows > INT64_MAX / ld_q) return FP8BS_ERR_SHAPE;
+  if (!aligned4(scale_e8m0_out)) return FP8BS_ERR_ALIGN;
   const bool vec = aligned16(x_bf16) && aligned16(q_out) && ld_x % 8 == 0 && ld_q % 16 == 0;
-  const bool s4 = aligned4(scale_e8m0_out) && ld_s % 4 == 0;
   const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
   uint8_t* q = static_cast<uint8_t*>(q_out);
-  uint8_t* se = static_cast<uint8_t*>(scale_e8m0_out);
+  uint32_t* se = static_cast<uint32_t*>(scale_e8m0_out);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)(ceil_div(rows, kRows1) * ceil_div(cols, 128)));
-  auto go = [&](auto kernel) { return launch(kernel, grid, dim3(kThreads), st, x, rows, cols, ld_x, q, ld_q, se, ld_s); };
-  if (fmt == FP8BS_E4M3) {
-    if (vec) return s4 ? go(quant_mx_kernel<FP8BS_E4M3, true, true>) : go(quant_mx_kernel<FP8BS_E4M3, true, false>);
-    return s4 ? go(quant_mx_kernel<FP8BS_E4M3, false, true>) : go(quant_mx_kernel<FP8BS_E4M3, false, false>);
-  }
-  if (vec) return s4 ? go(quant_mx_kernel<FP8BS_E5M2, true, true>) : go(quant_mx_kernel<FP8BS_E5M2, true, false>);
-  return s4 ? go(quant_mx_kernel<FP8BS_E5M2, false, true>) : go(quant_mx_kernel<FP8BS_E5M2, false, false>);
+  auto go = [&](auto kernel) { return launch(kernel, grid, dim3(kThreads), st, x, rows, cols, ld_x, q, ld_q, se); };
+  if (fmt == FP8BS_E4M3)
+    return vec ? go(quant_mx_kernel<FP8BS_E4M3, true>) : go(quant_mx_kernel<FP8BS_E4M3, false>);
+  return vec ? go(quant_mx_kernel<FP8BS_E5M2, true>) : go(quant_mx_kernel<FP8BS_E5M2, false>);
 }
 
 extern "C" int fp8_quantize_blockwise(const void* x_bf16, int64_t rows, int64_t cols,

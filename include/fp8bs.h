@@ -120,12 +120,14 @@ int fp8_quantize_blockwise(const void* x_bf16, int64_t rows, int64_t cols, int64
  * factor 1/s, i.e. its binary exponent + 127 (2^(byte - 127) = 1/s; never 255).
  *   x_bf16          [rows][ld_x] bf16, device; ld_x >= cols
  *   q_out           [rows][ld_q] codes, device; ld_q >= cols
- *   scale_e8m0_out  [rows][ld_s] bytes, device; ld_s >= ceil(cols / 32); byte j of row r is the
- *                   factor of columns 32 j .. 32 j + 31; bytes past ceil(cols / 32) are left alone
+ *   scale_e8m0_out  [ceil(cols / 128)][rows][4] bytes, device, 4-byte aligned: byte i of word
+ *                   (c, r) is the factor of row r, columns 128 c + 32 i .. + 31 (the column
+ *                   block-major order of the 1x128 scales); chunks past cols hold 127 (2^0)
  * rows == 0 or cols == 0: no-op.  Caller-owned memory, nothing allocated; asynchronous on stream.
- * Errors: FP8BS_ERR_ARG (fmt), FP8BS_ERR_SHAPE, FP8BS_ERR_NULL, FP8BS_ERR_LAUNCH. */
+ * Errors: FP8BS_ERR_ARG (fmt), FP8BS_ERR_SHAPE, FP8BS_ERR_NULL, FP8BS_ERR_ALIGN,
+ * FP8BS_ERR_LAUNCH. */
 int fp8_quantize_mx(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
-                    void* q_out, int64_t ld_q, void* scale_e8m0_out, int64_t ld_s, void* stream);
+                    void* q_out, int64_t ld_q, void* scale_e8m0_out, void* stream);
 
 /*
  * Blockwise quantization of several bf16 matrices in one launch: tensor i is quantized exactly as
@@ -302,23 +304,21 @@ int fp8_gemm_blockscaled_qout(int64_t M, int64_t N, int64_t K, const void* A, in
                               float* cq_scale_inv, void* stream);
 
 /* Microscaling (MXFP8) GEMM, fprop layout -- the sections of fp8_quantize_mx.  C[M][N] (bf16,
- * round to nearest even) = sum over k of A[m][k] * 2^(sa[m][k/32] - 127) * B[n][k] *
- * 2^(sb[n][k/32] - 127): A[M][lda] and B[N][ldb] are FP8 codes of formats fa / fb (K-major,
- * the fp8_gemm_blockscaled fprop operands), sa[M][ld_sa] and sb[N][ld_sb] their E8M0 scale bytes
- * as fp8_quantize_mx writes them.  The matrix cores apply the scales (the scaled MFMA, one byte
- * per lane and 32-wide k chunk) and accumulate in fp32.  A scale byte of 255 (E8M0 NaN) makes
- * the products of its block NaN.
+ * round to nearest even) = sum over k of A[m][k] * 2^(sa(m, k/32) - 127) * B[n][k] *
+ * 2^(sb(n, k/32) - 127): A[M][lda] and B[N][ldb] are FP8 codes of formats fa / fb (K-major,
+ * the fp8_gemm_blockscaled fprop operands), sa [ceil(K/128)][M][4] and sb [ceil(K/128)][N][4]
+ * their E8M0 scale bytes in the layout fp8_quantize_mx writes.  The matrix cores apply the
+ * scales (the scaled MFMA, one byte per lane and 32-wide k chunk) and accumulate in fp32.  A
+ * scale byte of 255 (E8M0 NaN) makes the products of its block NaN; bytes of chunks past K are
+ * ignored.
  *   lda, ldb: multiples of 16, >= K, < 2^23; A, B 16-byte aligned
- *   ld_sa, ld_sb: multiples of 4, >= ceil(K / 32); sa, sb 4-byte aligned; the arrays hold
- *   M * ld_sa and N * ld_sb bytes (whole rows: the kernels read each row's bytes of a 128-wide
- *   K block as one word; bytes of 32-wide chunks past K are read but ignored); each below 4 GiB
+ *   sa, sb: 4-byte aligned, each below 4 GiB
  *   C_bf16: [M][ldc], ldc >= N, 4-byte aligned, even ldc
  * M == 0 or N == 0: no-op; K == 0: C = 0.  Errors: FP8BS_ERR_ARG (formats), FP8BS_ERR_SHAPE,
  * FP8BS_ERR_NULL, FP8BS_ERR_ALIGN, FP8BS_ERR_LAUNCH. */
 int fp8_gemm_mx(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int fa,
-                const void* scale_e8m0_a, int64_t ld_sa, const void* B, int64_t ldb, int fb,
-                const void* scale_e8m0_b, int64_t ld_sb, void* C_bf16, int64_t ldc,
-                void* stream);
+                const void* scale_e8m0_a, const void* B, int64_t ldb, int fb,
+                const void* scale_e8m0_b, void* C_bf16, int64_t ldc, void* stream);
 
 /* Block-scaled FP8 GEMM with power-of-2 scales -- "NVIDIA NeMo RL logra una aceleración del 48%
  * ...", section "Por qué esto es importante para la economía de la IA" (the power-of-2 scale

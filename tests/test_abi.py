@@ -429,22 +429,21 @@ def test_bench_library_probes_reject_invalid_arguments():
 
 def test_mx_validation():
     lib = bsq.load()
-    # quantizer: format, scale pitch, null pointers; empty is a no-op
-    assert lib.fp8_quantize_mx(FAKE, 4, 64, 64, 2, FAKE, 64, FAKE, 2, None) == bsq.ERR_ARG
-    assert lib.fp8_quantize_mx(FAKE, 4, 64, 64, 0, FAKE, 64, FAKE, 1, None) == bsq.ERR_SHAPE
-    assert lib.fp8_quantize_mx(FAKE, 4, 64, 32, 0, FAKE, 64, FAKE, 2, None) == bsq.ERR_SHAPE
-    assert lib.fp8_quantize_mx(None, 4, 64, 64, 0, FAKE, 64, FAKE, 2, None) == bsq.ERR_NULL
-    assert lib.fp8_quantize_mx(None, 0, 64, 64, 0, None, 64, None, 2, None) == bsq.OK
-    # GEMM: scale pitch below ceil(K / 32), not a multiple of 4, misaligned scales
+    # quantizer: format, pitches, null pointers, scale alignment; empty is a no-op
+    assert lib.fp8_quantize_mx(FAKE, 4, 64, 64, 2, FAKE, 64, FAKE, None) == bsq.ERR_ARG
+    assert lib.fp8_quantize_mx(FAKE, 4, 64, 32, 0, FAKE, 64, FAKE, None) == bsq.ERR_SHAPE
+    assert lib.fp8_quantize_mx(FAKE, 4, 64, 64, 0, FAKE, 63, FAKE, None) == bsq.ERR_SHAPE
+    assert lib.fp8_quantize_mx(None, 4, 64, 64, 0, FAKE, 64, FAKE, None) == bsq.ERR_NULL
+    assert lib.fp8_quantize_mx(FAKE, 4, 64, 64, 0, FAKE, 64, FAKE_ODD, None) == bsq.ERR_ALIGN
+    assert lib.fp8_quantize_mx(None, 0, 64, 64, 0, None, 64, None, None) == bsq.OK
+    # GEMM: formats, misaligned scales, null scales, pitches; empty is a no-op
     def gemm(**kw):
-        v = dict(M=64, N=64, K=128, lda=128, fa=0, sa=FAKE, ld_sa=4, ldb=128, fb=0, sb=FAKE,
-                 ld_sb=4, C=FAKE, ldc=64)
+        v = dict(M=64, N=64, K=128, lda=128, fa=0, sa=FAKE, ldb=128, fb=0, sb=FAKE, C=FAKE, ldc=64)
         v.update(kw)
-        return lib.fp8_gemm_mx(v["M"], v["N"], v["K"], FAKE, v["lda"], v["fa"], v["sa"], v["ld_sa"],
-                               FAKE, v["ldb"], v["fb"], v["sb"], v["ld_sb"], v["C"], v["ldc"], None)
+        return lib.fp8_gemm_mx(v["M"], v["N"], v["K"], FAKE, v["lda"], v["fa"], v["sa"], FAKE,
+                               v["ldb"], v["fb"], v["sb"], v["C"], v["ldc"], None)
     assert gemm(fb=5) == bsq.ERR_ARG
-    assert gemm(ld_sa=3) == bsq.ERR_SHAPE
-    assert gemm(ld_sa=8, ld_sb=10) == bsq.ERR_ALIGN
     assert gemm(sb=FAKE + 2) == bsq.ERR_ALIGN
     assert gemm(sa=None) == bsq.ERR_NULL
+    assert gemm(ldb=100) == bsq.ERR_SHAPE
     assert gemm(M=0) == bsq.OK

@@ -1,7 +1,8 @@
 """Microscaling (MXFP8) path on the GPU against the oracle: fp8_quantize_mx bit for bit (codes
-and E8M0 scale bytes), fp8_gemm_mx within the GEMM tolerance of tests/helpers.py on seeded
-inputs quantized by the oracle (ragged M, N and K, K chunks past K whose padding scale bytes
-hold NaN codes), and the argument checks that need device memory."""
+and E8M0 scale bytes, in the C ABI's [ceil(cols/128)][rows][4] layout), fp8_gemm_mx within the
+GEMM tolerance of tests/helpers.py on seeded inputs quantized by the oracle (ragged M, N and K;
+the scale bytes of chunks past K hold NaN codes, which the kernel must ignore), and the
+argument checks that need device memory."""
 import numpy as np
 import pytest
 import torch
@@ -15,8 +16,14 @@ pytestmark = pytest.mark.gpu
 E4, E5 = oracle.E4M3, oracle.E5M2
 
 
-def mx_cols(k):
-    return -(-(-(-k // 32)) // 4) * 4
+def abi_scales(s: np.ndarray, pad: int) -> np.ndarray:
+    """The oracle's [rows][ceil(cols/32)] scale bytes in the C ABI layout [ceil(cols/128)][rows][4]
+    (chunks past the last one filled with `pad`)."""
+    rows, nch = s.shape
+    nb = -(-nch // 4)
+    full = np.full((rows, nb * 4), pad, dtype=np.uint8)
+    full[:, :nch] = s
+    return np.ascontiguousarray(full.reshape(rows, nb, 4).transpose(1, 0, 2))
 
 
 def run_quant(gpu, rows, cols, fmt, x=None, pitch=None, seed=0):
@@ -26,16 +33,13 @@ def run_quant(gpu, rows, cols, fmt, x=None, pitch=None, seed=0):
     store = torch.zeros((rows, ld), dtype=torch.bfloat16)
     store[:, :cols] = x
     xd = store.cuda()[:, :cols]
-    nch = -(-cols // 32)
-    sw = nch if pitch is None else mx_cols(cols) + 4          # byte stores / word stores
-    scales = torch.full((rows, sw), 0xAB, dtype=torch.uint8, device="cuda")
+    scales = torch.full(bsq.mx_scale_shape(rows, cols), 0xAB, dtype=torch.uint8, device="cuda")
     q, s = gpu.quantize_mx(xd, fmt, scales=scales)
     torch.cuda.synchronize()
     qo, so = oracle.quantize_mx(x, fmt)
     assert_bytes_equal(q.cpu().numpy(), qo, f"codes {rows}x{cols}")
-    sc = s.cpu().numpy()
-    assert_bytes_equal(sc[:, :nch], so, f"scale bytes {rows}x{cols}")
-    assert np.all(sc[:, nch:] == 0xAB), "bytes past ceil(cols/32) written"
+    # (chunks past the matrix are empty blocks: 2^0)
+    assert_bytes_equal(s.cpu().numpy(), abi_scales(so, 127), f"scale bytes {rows}x{cols}")
 
 
 @pytest.mark.parametrize("rows,cols", [(1, 32), (3, 70), (37, 300), (64, 4096), (33, 128), (5, 1)])
@@ -44,8 +48,8 @@ def test_quantize_mx_bit_exact(gpu, rows, cols, fmt):
     run_quant(gpu, rows, cols, fmt)
 
 
-def test_quantize_mx_word_stores_and_pitch(gpu):
-    run_quant(gpu, 40, 512, E4, pitch=520)     # 16-byte rows, 4-byte scale stores
+def test_quantize_mx_pitch(gpu):
+    run_quant(gpu, 40, 512, E4, pitch=520)     # 16-byte rows
     run_quant(gpu, 40, 200, E4, pitch=264)
 
 
@@ -74,10 +78,8 @@ def device_codes(q: np.ndarray, ld: int) -> torch.Tensor:
 
 
 def device_scale_bytes(s: np.ndarray, k: int) -> torch.Tensor:
-    rows, nch = s.shape
-    store = torch.full((rows, mx_cols(k)), 0xFF, dtype=torch.uint8)   # E8M0 NaN in the padding
-    store[:, :nch] = torch.from_numpy(s)
-    return store.cuda()
+    # chunks past K hold the E8M0 NaN byte: the kernel must ignore them
+    return torch.from_numpy(abi_scales(s, 0xFF)).cuda()
 
 
 def run_gemm_mx(gpu, M, N, K, fa=E4, fb=E4, seed=0, rows=None):
@@ -135,17 +137,17 @@ def test_gemm_mx_full_size_sampled(gpu):
 def test_gemm_mx_empty_and_k0(gpu):
     a = torch.zeros((0, 64), dtype=torch.uint8, device="cuda")
     b = torch.zeros((8, 64), dtype=torch.uint8, device="cuda")
-    s0 = torch.zeros((0, 4), dtype=torch.uint8, device="cuda")
-    s8 = torch.zeros((8, 4), dtype=torch.uint8, device="cuda")
+    s0 = torch.zeros(bsq.mx_scale_shape(0, 64), dtype=torch.uint8, device="cuda")
+    s8 = torch.zeros(bsq.mx_scale_shape(8, 64), dtype=torch.uint8, device="cuda")
     assert gpu.gemm_mx(a, s0, b, s8).shape == (0, 8)
     a = torch.zeros((5, 0), dtype=torch.uint8, device="cuda")
     b = torch.zeros((6, 0), dtype=torch.uint8, device="cuda")
     c = torch.full((5, 6), 3.0, dtype=torch.bfloat16, device="cuda")
     lib = gpu.load()
-    sa = torch.zeros((5, 4), dtype=torch.uint8, device="cuda")
-    sb = torch.zeros((6, 4), dtype=torch.uint8, device="cuda")
-    rc = lib.fp8_gemm_mx(5, 6, 0, a.data_ptr(), 16, E4, sa.data_ptr(), 4, b.data_ptr(), 16, E4,
-                         sb.data_ptr(), 4, c.data_ptr(), 6, None)
+    sa = torch.zeros((1, 5, 4), dtype=torch.uint8, device="cuda")
+    sb = torch.zeros((1, 6, 4), dtype=torch.uint8, device="cuda")
+    rc = lib.fp8_gemm_mx(5, 6, 0, a.data_ptr(), 16, E4, sa.data_ptr(), b.data_ptr(), 16, E4,
+                         sb.data_ptr(), c.data_ptr(), 6, None)
     torch.cuda.synchronize()
     assert rc == 0 and torch.all(c == 0)
 
@@ -153,25 +155,24 @@ def test_gemm_mx_empty_and_k0(gpu):
 def test_mx_argument_checks(gpu):
     lib = gpu.load()
     a = torch.zeros((64, 128), dtype=torch.uint8, device="cuda")
-    s = torch.zeros((64, 4), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((1, 64, 4), dtype=torch.uint8, device="cuda")
     c = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
     def call(**kw):
-        v = dict(M=64, N=64, K=128, A=a.data_ptr(), lda=128, fa=E4, sa=s.data_ptr(), ld_sa=4,
-                 B=a.data_ptr(), ldb=128, fb=E4, sb=s.data_ptr(), ld_sb=4, C=c.data_ptr(), ldc=64)
+        v = dict(M=64, N=64, K=128, A=a.data_ptr(), lda=128, fa=E4, sa=s.data_ptr(),
+                 B=a.data_ptr(), ldb=128, fb=E4, sb=s.data_ptr(), C=c.data_ptr(), ldc=64)
         v.update(kw)
-        return lib.fp8_gemm_mx(v["M"], v["N"], v["K"], v["A"], v["lda"], v["fa"], v["sa"], v["ld_sa"],
-                               v["B"], v["ldb"], v["fb"], v["sb"], v["ld_sb"], v["C"], v["ldc"], None)
+        return lib.fp8_gemm_mx(v["M"], v["N"], v["K"], v["A"], v["lda"], v["fa"], v["sa"],
+                               v["B"], v["ldb"], v["fb"], v["sb"], v["C"], v["ldc"], None)
     assert call() == bsq.OK
     torch.cuda.synchronize()
     assert call(fa=3) == bsq.ERR_ARG
-    assert call(ld_sa=2) == bsq.ERR_SHAPE          # fewer than ceil(K / 32) bytes
-    assert call(ld_sb=6) == bsq.ERR_ALIGN          # not a multiple of 4
     assert call(sa=s.data_ptr() + 2) == bsq.ERR_ALIGN
     assert call(sa=None) == bsq.ERR_NULL
     assert call(lda=100) == bsq.ERR_SHAPE
     x = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
     q = torch.zeros((4, 64), dtype=torch.uint8, device="cuda")
-    se = torch.zeros((4, 2), dtype=torch.uint8, device="cuda")
-    assert lib.fp8_quantize_mx(x.data_ptr(), 4, 64, 64, 2, q.data_ptr(), 64, se.data_ptr(), 2, None) == bsq.ERR_ARG
-    assert lib.fp8_quantize_mx(x.data_ptr(), 4, 64, 64, E4, q.data_ptr(), 64, se.data_ptr(), 1, None) == bsq.ERR_SHAPE
-    assert lib.fp8_quantize_mx(None, 4, 64, 64, E4, q.data_ptr(), 64, se.data_ptr(), 2, None) == bsq.ERR_NULL
+    se = torch.zeros((1, 4, 4), dtype=torch.uint8, device="cuda")
+    assert lib.fp8_quantize_mx(x.data_ptr(), 4, 64, 64, 2, q.data_ptr(), 64, se.data_ptr(), None) == bsq.ERR_ARG
+    assert lib.fp8_quantize_mx(x.data_ptr(), 4, 64, 32, E4, q.data_ptr(), 64, se.data_ptr(), None) == bsq.ERR_SHAPE
+    assert lib.fp8_quantize_mx(x.data_ptr(), 4, 64, 64, E4, q.data_ptr(), 64, se.data_ptr() + 1, None) == bsq.ERR_ALIGN
+    assert lib.fp8_quantize_mx(None, 4, 64, 64, E4, q.data_ptr(), 64, se.data_ptr(), None) == bsq.ERR_NULL
