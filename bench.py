@@ -20,7 +20,9 @@ Other workloads (--workload): llama8b-fprop-pow2 (the same step with power-of-2 
 GEMM applying them as E8M0 block scales in the MFMA), quant-sweep (HBM-bound quantizer), moe
 (grouped GEMM; --pow2 for power-of-2 scales), backward (delayed-scaled dgrad / wgrad),
 backward-blockwise (dgrad + blockwise wgrad on columnwise-quantized operands; --pow2),
-llama8b-fprop-qout (the GEMM quantizing its own output against GEMM + quantizer), kv-decode
+llama8b-fprop-qout (the GEMM quantizing its own output against GEMM + quantizer),
+llama8b-fprop-mx (the same step in microscaling form: 32-element row blocks with E8M0 scale
+bytes on X and W, the scales applied by the scaled MFMA), kv-decode
 (FP8 KV-cache write + grouped-query decode attention, Llama-3.1-8B attention shape), copy
 (counter calibration).  Each prints one JSON line.
 """
@@ -43,9 +45,11 @@ FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 GEMM_COUNTERS = os.path.join(ROOT, "profiles", "gemm_kernel_llama8b_fprop_counters.txt")
 GEMM_COUNTERS_POW2 = os.path.join(ROOT, "profiles", "gemm_kernel_pow2_llama8b_fprop_counters.txt")
+GEMM_COUNTERS_MX = os.path.join(ROOT, "profiles", "gemm_kernel_mx_llama8b_fprop_counters.txt")
 GEMM_SOURCES = [os.path.join(ROOT, "block_scaled_quantize_amd", "csrc", f)
                 for f in ("gemm_impl.h", "gemm.hip", "gemm_fprop.hip", "gemm_fprop_pow2.hip",
-                          "gemm_dgrad.hip", "gemm_wgrad.hip", "gemm_grouped.hip", "common.h")]
+                          "gemm_dgrad.hip", "gemm_wgrad.hip", "gemm_grouped.hip", "gemm_mx.hip",
+                          "common.h")]
 
 LAYERS_8B = [("qkv", 4096, 6144), ("o", 4096, 4096), ("gate_up", 4096, 28672), ("down", 14336, 4096)]
 
@@ -398,8 +402,10 @@ def bench_llama8b_mx(args):
         q_ms += qx_ms + qw_ms
         per_layer[L["name"]] = dict(gemm_us=round(g * 1e3, 2), gemm_tflops=round(f / g / 1e9, 1),
                                     quant_x_us=round(qx_ms * 1e3, 2), quant_w_us=round(qw_ms * 1e3, 2))
-    achieved = float(np.mean(gemm_flops)) / float(np.mean(gemm_ms)) / 1e9
-    return dict(
+    mean_launch_flops = float(np.mean(gemm_flops))
+    achieved = mean_launch_flops / float(np.mean(gemm_ms)) / 1e9
+    traffic = measured_traffic(GEMM_COUNTERS_MX, GEMM_SOURCES)
+    result = dict(
         metric="microscaling FP8 GEMM TFLOP/s (+quantize GB/s), % of MI355X FP8/HBM peak",
         value=round(flops / dt / 1e12, 2), unit="TFLOP/s", n_gpus=1, steps=args.steps,
         warmup=args.warmup, ms_per_step=round(dt * 1e3, 4), higher_is_better=True,
@@ -410,13 +416,46 @@ def bench_llama8b_mx(args):
                     scales="E8M0 bytes, one per 32 K elements of every row of X and W (all four W "
                            "and every X re-quantized each step)", parallelism="single GPU"),
         roofline=dict(bound="mfma", achieved=round(achieved, 1), peak=FP8_PEAK_TFLOPS,
-                      unit="TFLOP/s", frac=round(achieved / FP8_PEAK_TFLOPS, 4), traffic=None,
+                      unit="TFLOP/s", frac=round(achieved / FP8_PEAK_TFLOPS, 4),
+                      traffic=traffic["bytes"], traffic_unit="HBM bytes per launch",
+                      traffic_algorithmic=traffic["algorithmic"], traffic_source=traffic["source"],
                       kernel="gemm_persistent_kernel<Cfg<256,256,2,4>,FPROP,E4M3,E4M3,mx>",
+                      per_launch_flops=mean_launch_flops,
                       mean_launch_us=round(float(np.mean(gemm_ms)) * 1e3, 2)),
         gemm_only_tflops=round(sum(gemm_flops) / sum(gemm_ms) / 1e9, 1),
         quant_gbps=round(q_bytes / q_ms / 1e6, 1),
         quant_hbm_frac=round(q_bytes / q_ms / 1e6 / HBM_PEAK_GBPS, 4),
         layers=per_layer)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_8b_mx(layers, M)
+    return result
+
+
+def cpu_baseline_8b_mx(layers, M, rows: int = 1024, min_seconds: float = 10.0):
+    """The oracle on a bounded sample of the microscaling step: `rows` token rows of each layer's
+    activation and the full weights quantized into 32-element blocks, dequantized and multiplied
+    in fp64, repeated until min_seconds have passed.  TFLOP/s of the GEMM flops done."""
+    import oracle
+    oracle.build()
+    rows = min(rows, M)
+    host = [(L["x"][:rows].cpu().contiguous().view(torch.int16).numpy().view(np.uint16),
+             L["w"].cpu().contiguous().view(torch.int16).numpy().view(np.uint16), L) for L in layers]
+    t0 = time.perf_counter()
+    flops, reps = 0.0, 0
+    while reps == 0 or time.perf_counter() - t0 < min_seconds:
+        for xs, ws, L in host:
+            qx, sx = oracle.quantize_mx(xs, oracle.E4M3)
+            qw, sw = oracle.quantize_mx(ws, oracle.E4M3)
+            oracle.gemm_mx(qx, oracle.E4M3, sx, qw, oracle.E4M3, sw)
+            flops += 2.0 * rows * L["N"] * L["K"]
+        reps += 1
+    dt = time.perf_counter() - t0
+    blas = blas_threads()
+    return dict(value=round(flops / dt / 1e12, 5), unit="TFLOP/s", cores=max(cpu_cores(), blas),
+                kind="oracle",
+                sample=f"{rows} of {M} token rows per layer (all four layers, full weights "
+                       f"re-quantized) x {reps} repetitions, {dt:.1f} s; C oracle threads "
+                       f"{cpu_cores()}, BLAS threads {blas}")
 
 
 def cpu_baseline_8b(layers, M, rows: int | None = None, min_seconds: float = 10.0, mode: int = 0):
