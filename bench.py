@@ -578,12 +578,16 @@ def bench_quant_sweep(args):
 # ----------------------------------------------------------------------------- streaming ceiling
 
 STREAM_VARIANTS = {0: "one-shot, 16 el/lane", 1: "one-shot, 2x16 el/lane", 2: "one-shot, 4x16 el/lane",
-                   3: "2048 workgroups striding", 4: "4096 workgroups striding"}
+                   3: "2048 workgroups striding", 4: "4096 workgroups striding",
+                   5: "one-shot, non-temporal loads", 6: "one-shot, non-temporal stores",
+                   7: "one-shot, non-temporal loads and stores",
+                   8: "32-row x 128-column tiles (the short-row quantizer's geometry)"}
 
 
 def bench_stream(args):
     """The rate this GPU streams the quantizers' traffic at: plain kernels that read 2 bytes and
-    write 1 byte per element (libfp8bs_bench.so, five grid shapes), next to the 1x128 quantizer
+    write 1 byte per element (libfp8bs_bench.so: grid shapes, non-temporal accesses, the
+    short-row quantizer's tile geometry), next to the 1x128 quantizer
     on the same buffers (bf16 [rows, 4096] of 16M / 128M / 512M elements, rotating over more
     than 512 MiB so that the last-level cache does not serve the inputs).  value = the best
     streaming rate on the 512M-element tensor; quantizer_vs_stream = the quantizer's rate over

@@ -425,6 +425,8 @@ def test_bench_library_probes_reject_invalid_arguments():
     assert mfma(FAKE, FAKE, 0, 10, 256, 161 * 1024, None) == -1  # more LDS than a CU has
     assert blib.fp8bs_bench_stream(None, 16, FAKE, 0, None) == -1
     assert blib.fp8bs_bench_stream(FAKE, 15, FAKE, 0, None) == -1
+    assert blib.fp8bs_bench_stream(FAKE, 16, FAKE, 9, None) == -1      # no such variant
+    assert blib.fp8bs_bench_stream(FAKE, 4096, FAKE, 8, None) == -1    # not whole 32-row tiles
 
 
 def test_mx_validation():

@@ -70,6 +70,35 @@ def test_quantize_mx_full_size(gpu):
     run_quant(gpu, 8192, 4096, E4, x=x)
 
 
+@pytest.mark.parametrize("rows,cols", [(1, 1024), (7, 2048), (130, 14336)])
+def test_quantize_mx_long_rows(gpu, rows, cols):
+    for fmt in (E4, E5):
+        run_quant(gpu, rows, cols, fmt)
+    run_quant(gpu, rows, cols, E4, pitch=cols + 64)
+
+
+def test_quantize_mx_beyond_cache_sampled(gpu):
+    """Codes larger than the 256 MB last-level cache ([65540, 4096], non-temporal code stores):
+    the kernel quantizes the whole tensor, the oracle checks sampled row bands (blocks are per
+    row, so a band is checked exactly), the last band ragged."""
+    rows, cols = 65540, 4096
+    xd = torch.zeros((rows, cols), dtype=torch.bfloat16, device="cuda")
+    bands = [(0, 64), (20000, 20064), (rows - 68, rows)]
+    host = {}
+    for lo, hi in bands:
+        t = synth.activations_with_outliers(hi - lo, cols, 3, f"mx/big/{lo}")
+        host[lo] = t
+        xd[lo:hi] = t.cuda()
+    q, s = gpu.quantize_mx(xd, E4)
+    torch.cuda.synchronize()
+    for lo, hi in bands:
+        qo, so = oracle.quantize_mx(host[lo], E4)
+        assert_bytes_equal(q[lo:hi].cpu().numpy(), qo, f"codes rows {lo}..{hi}")
+        assert_bytes_equal(s[:, lo:hi].cpu().numpy(), abi_scales(so, 127), f"scales rows {lo}..{hi}")
+    del xd, q, s
+    torch.cuda.empty_cache()
+
+
 def device_codes(q: np.ndarray, ld: int) -> torch.Tensor:
     rows, cols = q.shape
     store = torch.full((rows, ld), 0x7F, dtype=torch.uint8)      # NaN codes in the padding

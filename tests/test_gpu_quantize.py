@@ -64,6 +64,21 @@ def test_ragged_shapes(gpu, shape, gran):
             run_parity(gpu, x, fmt, gran, mode, what=f"{shape}")
 
 
+@pytest.mark.parametrize("shape", [(1, 1024), (5, 2048), (131, 3072), (6, 14336)])
+def test_long_rows(gpu, shape):
+    """Rows of a multiple of 1024 columns take the long-row kernel (4 rows per workgroup): ragged
+    row counts, both formats and scale modes, packed and padded pitches, and an odd pitch that
+    falls back to the 32-row tile."""
+    x = synth.student_t(shape, 3.0, 4, f"long/{shape}")
+    for fmt in FMTS:
+        for mode in MODES:
+            run_parity(gpu, x, fmt, bsq.BLOCK_1x128, mode, what=f"long {shape}")
+    run_parity(gpu, x, bsq.E4M3, bsq.BLOCK_1x128, bsq.SCALE_FP32, pitch_pad=64, qpad=32,
+               what=f"long {shape} padded pitch")
+    run_parity(gpu, x, bsq.E4M3, bsq.BLOCK_1x128, bsq.SCALE_FP32, pitch_pad=1, qpad=3,
+               what=f"long {shape} odd pitch")
+
+
 @pytest.mark.parametrize("gran", GRANS)
 def test_strided_and_unaligned_pitch(gpu, gran):
     x = synth.normal((200, 384), 1.0, 2, "pitch")
