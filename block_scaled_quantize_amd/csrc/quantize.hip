@@ -243,6 +243,51 @@ __global__ __launch_bounds__(kThreads) void quant_128x128_kernel(
                                      wave_amax);
 }
 
+// Tensors whose codes exceed the 256 MB last-level cache, rows of a multiple of 512 columns
+// (16-byte aligned): a 512-lane workgroup takes 4 tiles side by side (128 rows x 512 columns)
+// and stores its codes non-temporally.  Each half-wave streams 1 KiB of one row (4 tiles x 8 lanes
+// x 16 elements), a wave two rows, the 8 waves 16 rows per pass, 8 passes; a lane keeps its 8
+// pieces (one per pass) in registers until the tiles' maxima are known.  Tile maxima: over the
+// lane's pieces, the 8 lanes of the tile's row segment (DPP), the two half-waves (one shuffle)
+// and the 8 waves (LDS).  Measured 10-12% faster than the 32-row tiles from 512M elements up,
+// but 8-11% slower at 16M (a quarter as many workgroups: one per CU), about equal at 128M.
+constexpr int kThreadsW = 512;
+template <int FMT, bool POW2, bool NTS>
+__global__ __launch_bounds__(kThreadsW) void quant_128x128_wide_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale_inv) {
+  __shared__ uint32_t s_amax[kThreadsW / 64][4];
+  const int t = threadIdx.x;
+  const int w = t >> 6, h = (t >> 5) & 1, li = t & 31;
+  const int64_t nbc = cols >> 9;                       // 512-column groups
+  const int64_t tr = blockIdx.x / nbc, cg = blockIdx.x % nbc;
+  const int64_t c0 = cg * 512 + li * 16;
+  const int64_t r0 = tr * 128 + 2 * w + h;
+  uint32_t d[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) load16<true>(x, rows, cols, ld_x, r0 + 16 * i, c0, d[i]);
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t a = amax16_bits(d[i]);
+    m = m > a ? m : a;
+  }
+  m = group8_max(m);
+  const uint32_t o = (uint32_t)__shfl_xor((int)m, 32);
+  m = m > o ? m : o;
+  if ((t & 39) == 0) s_amax[w][li >> 3] = m;          // lanes 0, 8, 16, 24 of the wave
+  __syncthreads();
+  uint32_t amax = s_amax[0][li >> 3];
+#pragma unroll
+  for (int v = 1; v < kThreadsW / 64; ++v) amax = amax > s_amax[v][li >> 3] ? amax : s_amax[v][li >> 3];
+  const float s = scale_from_amax_bits<FMT, POW2>(amax);
+  const bool finite = amax < 0x7F80u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    store16<true, NTS>(q, rows, cols, ld_q, r0 + 16 * i, c0, encode_block_values<FMT>(d[i], s, finite));
+  if (t < 32 && (t & 7) == 0) scale_inv[tr * (cols >> 7) + cg * 4 + (t >> 3)] = 1.0f / s;
+}
+
 // ---------------------------------------------------------------- several tensors, one launch
 // Up to kMaxBatch tensors quantized by one grid: workgroup b belongs to the tensor whose range
 // of the prefix-summed workgroup counts holds b and runs that tensor's 1x128 or 128x128 body
@@ -414,6 +459,11 @@ int launch_blockwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x
     dim3 grid((unsigned)(ceil_div(rows, kRows1) * ceil_div(cols, 128)));
     return launch(quant_1x128_kernel<FMT, POW2, VEC>, grid, dim3(kThreads), st, x, rows, cols,
                   ld_x, q, ld_q, s);
+  }
+  if (VEC && cols % 512 == 0 && rows * cols > kNtStoreBytes) {
+    dim3 grid((unsigned)(ceil_div(rows, 128) * (cols >> 9)));
+    return launch(quant_128x128_wide_kernel<FMT, POW2, true>, grid, dim3(kThreadsW), st, x, rows,
+                  cols, ld_x, q, ld_q, s);
   }
   dim3 grid((unsigned)(ceil_div(rows, 128) * ceil_div(cols, 128)));
   return launch(quant_128x128_kernel<FMT, POW2, VEC>, grid, dim3(kThreads), st, x, rows, cols,

@@ -64,18 +64,20 @@ def test_ragged_shapes(gpu, shape, gran):
             run_parity(gpu, x, fmt, gran, mode, what=f"{shape}")
 
 
-@pytest.mark.parametrize("shape", [(1, 1024), (5, 2048), (131, 3072), (6, 14336)])
-def test_long_rows(gpu, shape):
-    """Rows of a multiple of 1024 columns take the long-row kernel (4 rows per workgroup): ragged
-    row counts, both formats and scale modes, packed and padded pitches, and an odd pitch that
-    falls back to the 32-row tile."""
+@pytest.mark.parametrize("shape", [(1, 1024), (5, 2048), (131, 3072), (6, 14336), (1, 512),
+                                   (300, 1536), (129, 512)])
+@pytest.mark.parametrize("gran", GRANS)
+def test_long_rows(gpu, shape, gran):
+    """Rows of a multiple of 1024 columns take the long-row 1x128 kernel (4 rows per workgroup):
+    ragged row counts, both formats and scale modes, packed and padded pitches, and an odd pitch
+    that falls back to the 32-row tiles (128x128 on the same shapes: the 32-row tiles)."""
     x = synth.student_t(shape, 3.0, 4, f"long/{shape}")
     for fmt in FMTS:
         for mode in MODES:
-            run_parity(gpu, x, fmt, bsq.BLOCK_1x128, mode, what=f"long {shape}")
-    run_parity(gpu, x, bsq.E4M3, bsq.BLOCK_1x128, bsq.SCALE_FP32, pitch_pad=64, qpad=32,
+            run_parity(gpu, x, fmt, gran, mode, what=f"long {shape}")
+    run_parity(gpu, x, bsq.E4M3, gran, bsq.SCALE_FP32, pitch_pad=64, qpad=32,
                what=f"long {shape} padded pitch")
-    run_parity(gpu, x, bsq.E4M3, bsq.BLOCK_1x128, bsq.SCALE_FP32, pitch_pad=1, qpad=3,
+    run_parity(gpu, x, bsq.E4M3, gran, bsq.SCALE_FP32, pitch_pad=1, qpad=3,
                what=f"long {shape} odd pitch")
 
 
@@ -167,6 +169,34 @@ def test_sweep_512m_sampled(gpu):
             assert_bytes_equal(f32_bits(sg), f32_bits(so), f"band {b} scales")
         del xd, q, s
         torch.cuda.empty_cache()
+
+
+def test_beyond_cache_ragged_sampled(gpu):
+    """Codes larger than the 256 MB last-level cache with a ragged last tile row ([65540, 4096]:
+    the 4-tile 128x128 kernel and the long-row 1x128 kernel, both with non-temporal code
+    stores), fp32 scales; sampled row bands checked exactly, the last one ragged."""
+    rows, cols = 65540, 4096
+    xd = torch.zeros((rows, cols), dtype=torch.bfloat16, device="cuda")
+    bands = [(0, 128), (30080, 30208), (rows - 4, rows)]
+    host = {}
+    for lo, hi in bands:
+        t = synth.student_t((hi - lo, cols), 3.0, 8, f"big/{lo}")
+        host[lo] = t
+        xd[lo:hi] = t.cuda()
+    for gran in GRANS:
+        q, s = gpu.quantize_blockwise(xd, bsq.E4M3, gran, bsq.SCALE_FP32)
+        torch.cuda.synchronize()
+        for lo, hi in bands:
+            qo, so = oracle.quantize_blockwise(bits(host[lo]), bsq.E4M3, gran, bsq.SCALE_FP32)
+            assert_bytes_equal(q[lo:hi].cpu().numpy(), qo, f"codes rows {lo}..{hi}")
+            if gran == bsq.BLOCK_1x128:
+                sg = s[:, lo:hi].cpu().numpy().T
+            else:
+                sg = s[lo // 128:lo // 128 + 1].cpu().numpy()
+            assert_bytes_equal(f32_bits(sg), f32_bits(so), f"scales rows {lo}..{hi}")
+        del q, s
+    del xd
+    torch.cuda.empty_cache()
 
 
 def test_deterministic(gpu):
