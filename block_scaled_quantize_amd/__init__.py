@@ -63,6 +63,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.fp8bs_status_string.restype = ctypes.c_char_p
     lib.fp8_quantize_blockwise.argtypes = [vp, i64, i64, i64, i32, i32, i32, vp, i64, vp, vp]
     lib.fp8_quantize_columnwise_t.argtypes = [vp, i64, i64, i64, i32, i32, vp, i64, vp, vp]
+    lib.fp8_quantize_mx_columnwise_t.argtypes = [vp, i64, i64, i64, i32, vp, i64, vp, vp]
     lib.fp8_quantize_mx.argtypes = [vp, i64, i64, i64, i32, vp, i64, vp, vp]
     lib.fp8_gemm_mx.argtypes = [i64, i64, i64, vp, i64, i32, vp, vp, i64, i32, vp, vp, i64, vp]
     lib.fp8_quantize_blockwise_batched.argtypes = [i32, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp]
@@ -89,7 +90,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
                                                ctypes.c_float, i32, i64, vp, sz, vp, vp]
     lib.fp8_attention_decode_workspace_size.argtypes = [i64, i64, i64, i64, i64]
     lib.fp8_attention_decode_workspace_size.restype = sz
-    for name in ("fp8_quantize_blockwise", "fp8_quantize_columnwise_t", "fp8_quantize_delayed",
+    for name in ("fp8_quantize_blockwise", "fp8_quantize_columnwise_t",
+                 "fp8_quantize_mx_columnwise_t", "fp8_quantize_delayed",
                  "fp8_quantize_blockwise_batched",
                  "fp8_quantize_delayed_noalloc",
                  "fp8_cast_fp32",
@@ -288,6 +290,28 @@ def quantize_columnwise_t(x: torch.Tensor, fmt: int, mode: int = SCALE_FP32,
                                             qt.stride(0), _ptr(scale_inv), _stream(stream)),
            "fp8_quantize_columnwise_t")
     return qt, scale_inv
+
+
+def quantize_mx_columnwise_t(x: torch.Tensor, fmt: int, qt: torch.Tensor | None = None,
+                             scales: torch.Tensor | None = None, stream=None):
+    """Microscaling quantization along columns (blocks of 32 rows of one column) of a 2-D bf16
+    matrix x[rows, cols], codes written transposed.
+
+    Returns (codes uint8 [cols, rows] = the codes of x^T, scale bytes uint8
+    mx_scale_shape(cols, rows) = the microscaling scale layout of x^T)."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 matrix with unit column stride")
+    rows, cols = x.shape
+    if qt is None:
+        qt = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(mx_scale_shape(cols, rows), dtype=torch.uint8, device=x.device)
+    _need_matrix(qt, (cols, rows), torch.uint8, "qt")
+    _need(scales, mx_scale_shape(cols, rows), torch.uint8, "scales")
+    _check(load().fp8_quantize_mx_columnwise_t(_ptr(x), rows, cols, x.stride(0), fmt, _ptr(qt),
+                                               qt.stride(0), _ptr(scales), _stream(stream)),
+           "fp8_quantize_mx_columnwise_t")
+    return qt, scales
 
 
 def delayed_workspace_size() -> int:

@@ -19,6 +19,11 @@
 // LDS.  The codes are staged in LDS as [column][row] (column pitch 136 bytes, so the 8-byte
 // writes of a wave spread over the banks) and leave as whole 128-byte rows of the transposed
 // matrix, 16 bytes per lane.
+//
+// The microscaling form (fp8_quantize_mx_columnwise_t) takes blocks of 32 rows of one column
+// with E8M0 scale bytes ("Infraestructura de Entrenamiento FP8: Precisión Numérica de Nueva
+// Generación", sections "Estrategias de escalado y estabilidad" and "Blackwell MXFP8 y NVFP4:
+// mirando hacia adelante"): the weight- and data-gradient operands of the microscaling GEMM.
 #include <float.h>
 
 #include "common.h"
@@ -160,6 +165,109 @@ __global__ __launch_bounds__(kThreadsT) void quant_128x1_t_kernel(
   }
 }
 
+// Microscaling form (blocks of 32 rows of one column, power-of-2 scales stored as E8M0 bytes, as
+// fp8_quantize_mx does along rows): the same tile, lanes and transposed code stores.  A wave's
+// four row groups are exactly one 32-row block, so a column's block maximum needs only the
+// shuffles inside the wave.  The E8M0 byte is 254 minus the exponent field of s (the exponent of
+// 1/s), and the four blocks of a tile column (one per wave) leave as one 4-byte word at
+// [128-row block][column]: the microscaling scale layout of x^T.
+template <int FMT, bool VEC>
+__global__ __launch_bounds__(kThreadsT) void quant_mx_t_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+    uint8_t* __restrict__ qt, int64_t ld_qt, uint32_t* __restrict__ se) {
+  __shared__ uint32_t s_e8[128];   // per tile column, byte w = the factor of wave w's block
+  __shared__ __attribute__((aligned(16))) uint8_t s_t[128 * 136];
+  const int t = threadIdx.x;
+  const int lane = t & 63, wv = t >> 6;
+  const int cg = t & 15, rg = t >> 4;
+  const int64_t nbc = (cols + 127) >> 7;
+  const int64_t rb = blockIdx.x / nbc, cb = blockIdx.x % nbc;
+  const int64_t r0 = rb * 128 + 8 * rg;
+  const int64_t c0 = cb * 128 + 8 * cg;
+
+  uint32_t d[8][4];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint4 v = load8<VEC>(x, rows, cols, ld_x, r0 + k, c0);
+    d[k][0] = v.x; d[k][1] = v.y; d[k][2] = v.z; d[k][3] = v.w;
+  }
+  uint32_t m[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    u16x2 v = mag2(d[0][p]);
+#pragma unroll
+    for (int k = 1; k < 8; ++k) v = max2(v, mag2(d[k][p]));
+    uint32_t b = __builtin_bit_cast(uint32_t, v);
+    b = __builtin_bit_cast(uint32_t, max2(__builtin_bit_cast(u16x2, b),
+                                           __builtin_bit_cast(u16x2, (uint32_t)__shfl_xor((int)b, 16))));
+    b = __builtin_bit_cast(uint32_t, max2(__builtin_bit_cast(u16x2, b),
+                                           __builtin_bit_cast(u16x2, (uint32_t)__shfl_xor((int)b, 32))));
+    m[p] = b;
+  }
+  float s[8];
+  bool finite = true;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t a = (j & 1) ? (m[j >> 1] >> 16) : (m[j >> 1] & 0xFFFFu);
+    s[j] = scale_from_amax_bits<FMT, true>(a);
+    finite = finite && a < 0x7F80u;
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      reinterpret_cast<uint8_t*>(s_e8)[4 * (8 * cg + j) + wv] =
+          (uint8_t)(254u - ((__float_as_uint(s[j]) >> 23) & 0xFFu));
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int p = j >> 1;
+    float y[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y[k] = ((j & 1) ? bf16_hi(d[k][p]) : bf16_lo(d[k][p])) * s[j];
+    if (!finite) {
+      constexpr float F = Format<FMT>::fmax;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) y[k] = __builtin_amdgcn_fmed3f(y[k], -F, F);
+    }
+    uint32_t lo = cvt4<FMT>(y[0], y[1], y[2], y[3]);
+    uint32_t hi = cvt4<FMT>(y[4], y[5], y[6], y[7]);
+    if (!finite) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t b = ((j & 1) ? (d[k][p] >> 16) : d[k][p]) & 0xFFFFu;
+        if ((b & 0x7FFFu) > 0x7F80u) {
+          const uint32_t code = 0x7Fu | ((b >> 8) & 0x80u);
+          const int sh = 8 * (k & 3);
+          if (k < 4) lo = (lo & ~(0xFFu << sh)) | (code << sh);
+          else hi = (hi & ~(0xFFu << sh)) | (code << sh);
+        }
+      }
+    }
+    *reinterpret_cast<uint2*>(s_t + (8 * cg + j) * 136 + 8 * rg) = make_uint2(lo, hi);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int col = (t >> 3) + 32 * u, chunk = t & 7;
+    const int64_t c = cb * 128 + col;
+    const int64_t r = rb * 128 + 16 * chunk;
+    if (c >= cols || r >= rows) continue;
+    const uint8_t* src = s_t + col * 136 + 16 * chunk;
+    const uint2 a = *reinterpret_cast<const uint2*>(src);
+    const uint2 b = *reinterpret_cast<const uint2*>(src + 8);
+    uint8_t* dst = qt + c * ld_qt + r;
+    if (VEC && r + 16 <= rows) {
+      *reinterpret_cast<uint4*>(dst) = make_uint4(a.x, a.y, b.x, b.y);
+    } else {
+      const uint32_t w4[4] = {a.x, a.y, b.x, b.y};
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if (r + k < rows) dst[k] = (uint8_t)(w4[k >> 2] >> (8 * (k & 3)));
+    }
+  }
+  if (t < 128 && cb * 128 + t < cols) se[rb * cols + cb * 128 + t] = s_e8[t];
+}
+
 template <int FMT>
 int dispatch_columnwise_t(bool pow2, bool vec, const uint16_t* x, int64_t rows, int64_t cols,
                           int64_t ld_x, uint8_t* qt, int64_t ld_qt, float* s, hipStream_t st) {
@@ -197,4 +305,27 @@ extern "C" int fp8_quantize_columnwise_t(const void* x_bf16, int64_t rows, int64
                                              scale_inv_out, st);
   return dispatch_columnwise_t<FP8BS_E5M2>(pow2, vec, x, rows, cols, ld_x, qt, ld_qt,
                                            scale_inv_out, st);
+}
+
+extern "C" int fp8_quantize_mx_columnwise_t(const void* x_bf16, int64_t rows, int64_t cols,
+                                            int64_t ld_x, int fmt, void* qt_out, int64_t ld_qt,
+                                            void* scale_e8m0_out, void* stream) {
+  if (!fmt_ok(fmt)) return FP8BS_ERR_ARG;
+  if (rows < 0 || cols < 0 || ld_x < cols || ld_qt < rows) return FP8BS_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return FP8BS_OK;
+  if (!x_bf16 || !qt_out || !scale_e8m0_out) return FP8BS_ERR_NULL;
+  if (ceil_div(rows, 128) * ceil_div(cols, 128) > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
+  if (rows > INT64_MAX / ld_x || cols > INT64_MAX / ld_qt) return FP8BS_ERR_SHAPE;
+  if (!aligned4(scale_e8m0_out)) return FP8BS_ERR_ALIGN;
+  const bool vec = aligned16(x_bf16) && aligned16(qt_out) && ld_x % 8 == 0 && ld_qt % 16 == 0;
+  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
+  uint8_t* qt = static_cast<uint8_t*>(qt_out);
+  uint32_t* se = static_cast<uint32_t*>(scale_e8m0_out);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)(ceil_div(rows, 128) * ceil_div(cols, 128)));
+  const dim3 block(kThreadsT);
+  auto go = [&](auto kernel) { return launch(kernel, grid, block, st, x, rows, cols, ld_x, qt, ld_qt, se); };
+  if (fmt == FP8BS_E4M3)
+    return vec ? go(quant_mx_t_kernel<FP8BS_E4M3, true>) : go(quant_mx_t_kernel<FP8BS_E4M3, false>);
+  return vec ? go(quant_mx_t_kernel<FP8BS_E5M2, true>) : go(quant_mx_t_kernel<FP8BS_E5M2, false>);
 }

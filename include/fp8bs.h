@@ -169,6 +169,25 @@ int fp8_quantize_columnwise_t(const void* x_bf16, int64_t rows, int64_t cols, in
                               int fmt, int mode, void* qt_out, int64_t ld_qt,
                               float* scale_inv_out, void* stream);
 
+/* Microscaling (MXFP8) quantization along columns, codes written transposed -- the sections of
+ * fp8_quantize_mx.  A block is 32 consecutive rows of one column of x[rows][cols], i.e. a
+ * 32-element row block of x^T, quantized exactly as fp8_quantize_mx quantizes x^T (power-of-2
+ * rule, saturating RNE codes, NaN codes for NaN inputs, E8M0 byte of 1/s).  It gives the
+ * microscaling GEMM the operands of the products that contract over the rows of x: the weight
+ * gradient dW = dY^T . X (x = dY and x = X, blocks along tokens) and the data gradient
+ * dX = dY . W (x = W, blocks along its output features), both run by fp8_gemm_mx.
+ *   x_bf16          [rows][ld_x] bf16, device; ld_x >= cols
+ *   qt_out          [cols][ld_qt] codes of x^T, device; ld_qt >= rows
+ *   scale_e8m0_out  [ceil(rows / 128)][cols][4] bytes, device, 4-byte aligned: the layout
+ *                   fp8_quantize_mx writes for x^T (byte i of word (b, c): rows 128 b + 32 i ..
+ *                   + 31 of column c); blocks past the last row hold 127 (2^0)
+ * rows == 0 or cols == 0: no-op.  Caller-owned memory, nothing allocated; asynchronous on stream.
+ * Errors: FP8BS_ERR_ARG (fmt), FP8BS_ERR_SHAPE, FP8BS_ERR_NULL, FP8BS_ERR_ALIGN,
+ * FP8BS_ERR_LAUNCH. */
+int fp8_quantize_mx_columnwise_t(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                                 int fmt, void* qt_out, int64_t ld_qt, void* scale_e8m0_out,
+                                 void* stream);
+
 /*
  * One step of per-tensor delayed scaling on a contiguous bf16 tensor x[numel].
  * [P1] "Transformer Engine: la base de software": the scale used in a step comes from the

@@ -217,6 +217,19 @@ def gemm_mx(qa, fa: int, sa_e8m0, qb, fb: int, sb_e8m0) -> np.ndarray:
                 e8m0_decode(sb_e8m0))
 
 
+def quantize_mx_columnwise_t(x, fmt: int, nthreads: int | None = None):
+    """Microscaling quantization along columns: blocks of 32 consecutive rows of one column of
+    x[R, C], codes returned transposed.  Such a block is, by definition, a 32-element row block
+    of x^T, so this is quantize_mx of the transpose (the microscaling form of the weight- and
+    data-gradient operands, whose contraction runs along the rows of x).
+
+    Returns (codes uint8 [C, R] (of x^T), scale bytes uint8 [C, ceil(R/32)])."""
+    xb = _as_bf16_bits(x)
+    if xb.ndim != 2:
+        raise ValueError("expected a 2-D matrix")
+    return quantize_mx(np.ascontiguousarray(xb.T), fmt, nthreads)
+
+
 def quantize_columnwise_t(x, fmt: int, mode: int, nthreads: int | None = None):
     """Columnwise quantization: blocks of 128 consecutive rows of one column of x[R, C], codes
     returned transposed.  A block of 128 rows of column c of x is, by definition, a 1x128 block

@@ -438,6 +438,14 @@ def test_mx_validation():
     assert lib.fp8_quantize_mx(None, 4, 64, 64, 0, FAKE, 64, FAKE, None) == bsq.ERR_NULL
     assert lib.fp8_quantize_mx(FAKE, 4, 64, 64, 0, FAKE, 64, FAKE_ODD, None) == bsq.ERR_ALIGN
     assert lib.fp8_quantize_mx(None, 0, 64, 64, 0, None, 64, None, None) == bsq.OK
+    # columnwise form: the transposed codes' rows hold `rows` codes
+    qmt = lib.fp8_quantize_mx_columnwise_t
+    assert qmt(FAKE, 256, 64, 64, 2, FAKE, 256, FAKE, None) == bsq.ERR_ARG
+    assert qmt(FAKE, 256, 64, 63, 0, FAKE, 256, FAKE, None) == bsq.ERR_SHAPE
+    assert qmt(FAKE, 256, 64, 64, 0, FAKE, 255, FAKE, None) == bsq.ERR_SHAPE
+    assert qmt(FAKE, 256, 64, 64, 0, None, 256, FAKE, None) == bsq.ERR_NULL
+    assert qmt(FAKE, 256, 64, 64, 0, FAKE, 256, FAKE_ODD, None) == bsq.ERR_ALIGN
+    assert qmt(None, 0, 64, 64, 0, None, 0, None, None) == bsq.OK
     # GEMM: formats, misaligned scales, null scales, pitches; empty is a no-op
     def gemm(**kw):
         v = dict(M=64, N=64, K=128, lda=128, fa=0, sa=FAKE, ldb=128, fb=0, sb=FAKE, C=FAKE, ldc=64)

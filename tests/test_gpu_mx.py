@@ -205,3 +205,81 @@ def test_mx_argument_checks(gpu):
     assert lib.fp8_quantize_mx(x.data_ptr(), 4, 64, 32, E4, q.data_ptr(), 64, se.data_ptr(), None) == bsq.ERR_SHAPE
     assert lib.fp8_quantize_mx(x.data_ptr(), 4, 64, 64, E4, q.data_ptr(), 64, se.data_ptr() + 1, None) == bsq.ERR_ALIGN
     assert lib.fp8_quantize_mx(None, 4, 64, 64, E4, q.data_ptr(), 64, se.data_ptr(), None) == bsq.ERR_NULL
+
+
+# ------------------------------------------------------------------ columnwise (transposed) form
+
+def run_quant_t(gpu, rows, cols, fmt, x=None, pitch=None, seed=0):
+    if x is None:
+        x = synth.activations_with_outliers(rows, cols, seed, f"mx/quant_t/{rows}x{cols}")
+    ld = pitch if pitch is not None else cols
+    store = torch.zeros((rows, ld), dtype=torch.bfloat16)
+    store[:, :cols] = x
+    xd = store.cuda()[:, :cols]
+    ldq = rows + (16 if pitch is not None else 0)
+    qstore = torch.full((cols, ldq), 0xA5, dtype=torch.uint8, device="cuda")
+    scales = torch.full(bsq.mx_scale_shape(cols, rows), 0xAB, dtype=torch.uint8, device="cuda")
+    q, s = gpu.quantize_mx_columnwise_t(xd, fmt, qt=qstore[:, :rows], scales=scales)
+    torch.cuda.synchronize()
+    qo, so = oracle.quantize_mx_columnwise_t(x, fmt)
+    assert_bytes_equal(q.cpu().numpy(), qo, f"transposed codes {rows}x{cols}")
+    assert_bytes_equal(s.cpu().numpy(), abi_scales(so, 127), f"scale bytes {rows}x{cols}")
+    assert torch.all(qstore[:, rows:] == 0xA5), "codes past the transposed rows written"
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 1), (33, 70), (300, 129), (128, 128), (4096, 256),
+                                       (70, 5)])
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_quantize_mx_columnwise_bit_exact(gpu, rows, cols, fmt):
+    run_quant_t(gpu, rows, cols, fmt)
+
+
+def test_quantize_mx_columnwise_pitch_and_specials(gpu):
+    run_quant_t(gpu, 200, 384, E4, pitch=392)
+    x = synth.activations_with_outliers(96, 64, 5, "mx/quant_t/special")
+    x[:, 3] = 0.0                                     # all-zero blocks: byte 127
+    x[10, 7] = float("nan")
+    x[40, 9] = float("inf")
+    x[70:, 11] = torch.tensor(1e-40).bfloat16()       # bf16 subnormals: the largest scale
+    x[5, 13] = 3.0e38                                 # huge magnitude: the smallest scale
+    run_quant_t(gpu, 96, 64, E4, x=x)
+    run_quant_t(gpu, 96, 64, E5, x=x)
+
+
+def test_quantize_mx_columnwise_full_size(gpu):
+    x = synth.activations_with_outliers(8192, 4096, 0, "bench/8b/qkv/X")
+    run_quant_t(gpu, 8192, 4096, E4, x=x)
+
+
+def test_mx_backward_wgrad_and_dgrad(gpu):
+    """The microscaling backward on the GPU path end to end: dW = dY^T . X from the columnwise
+    codes of dY and X (blocks of 32 tokens), dX = dY . W from dY's row codes and W's columnwise
+    codes (blocks of 32 output features); against the oracle's quantizers and fp64 products."""
+    M, N, K = 528, 384, 256       # tokens (ragged: 16.5 blocks of 32), out features, in features
+    dy = synth.normal((M, N), 1e-3, 6, "mx/bwd/dY")
+    x = synth.activations_with_outliers(M, K, 6, "mx/bwd/X")
+    w = synth.normal((N, K), 0.02, 6, "mx/bwd/W")
+    dyd, xd, wd = dy.cuda(), x.cuda(), w.cuda()
+    # weight gradient [N, K], contraction over the M tokens
+    qdyt, sdyt = gpu.quantize_mx_columnwise_t(dyd, E4)
+    qxt, sxt = gpu.quantize_mx_columnwise_t(xd, E4)
+    dw = gpu.gemm_mx(qdyt, sdyt, qxt, sxt)
+    # data gradient [M, K], contraction over the N output features
+    qdy, sdy = gpu.quantize_mx(dyd, E4)
+    qwt, swt = gpu.quantize_mx_columnwise_t(wd, E4)
+    dx = gpu.gemm_mx(qdy, sdy, qwt, swt)
+    torch.cuda.synchronize()
+
+    def ref(qa, sa, qb, sb):
+        a = oracle.dequantize(qa, E4, oracle.BLOCK_1x32, oracle.e8m0_decode(sa))
+        b = oracle.dequantize(qb, E4, oracle.BLOCK_1x32, oracle.e8m0_decode(sb))
+        return a @ b.T, np.abs(a) @ np.abs(b).T
+
+    o_dyt, o_sdyt = oracle.quantize_mx_columnwise_t(dy, E4)
+    o_xt, o_sxt = oracle.quantize_mx_columnwise_t(x, E4)
+    r, mag = ref(o_dyt, o_sdyt, o_xt, o_sxt)
+    gemm_check(dw, r, mag, "mx wgrad")
+    o_dy, o_sdy = oracle.quantize_mx(dy, E4)
+    o_wt, o_swt = oracle.quantize_mx_columnwise_t(w, E4)
+    r, mag = ref(o_dy, o_sdy, o_wt, o_swt)
+    gemm_check(dx, r, mag, "mx dgrad")

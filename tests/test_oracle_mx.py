@@ -119,3 +119,18 @@ def test_gemm_mx_brute_force(oracle_lib):
                 acc += da[m, k] * 2.0 ** (int(sa[m, k // 32]) - 127) * db[n, k] * 2.0 ** (int(sb[n, k // 32]) - 127)
             want[m, n] = acc
     assert np.allclose(got, want, rtol=1e-12, atol=0)
+
+
+def test_columnwise_mx_is_per_column_row_quantization():
+    """Columnwise microscaling on a non-square matrix: column c of x, quantized as one row of
+    32-element blocks, gives row c of the transposed codes and scale bytes (a swapped
+    orientation would mix columns or fail the shape); the ragged last block of 70 rows is a
+    6-element block."""
+    x = synth.activations_with_outliers(70, 5, 3, "oracle/mx/colwise")
+    xb = bits_of(x)
+    q, s = oracle.quantize_mx_columnwise_t(xb, E4M3)
+    assert q.shape == (5, 70) and s.shape == (5, 3)
+    for c in range(5):
+        qc, sc = oracle.quantize_mx(np.ascontiguousarray(xb[:, c][None, :]), E4M3)
+        assert np.array_equal(q[c], qc[0]), c
+        assert np.array_equal(s[c], sc[0]), c
