@@ -22,7 +22,8 @@ GEMM applying them as E8M0 block scales in the MFMA), quant-sweep (HBM-bound qua
 backward-blockwise (dgrad + blockwise wgrad on columnwise-quantized operands; --pow2),
 llama8b-fprop-qout (the GEMM quantizing its own output against GEMM + quantizer),
 llama8b-fprop-mx (the same step in microscaling form: 32-element row blocks with E8M0 scale
-bytes on X and W, the scales applied by the scaled MFMA), kv-decode
+bytes on X and W, the scales applied by the scaled MFMA), backward-mx (dgrad + wgrad in
+microscaling form, operands quantized along rows or, transposed, along columns), kv-decode
 (FP8 KV-cache write + grouped-query decode attention, Llama-3.1-8B attention shape), copy
 (counter calibration).  Each prints one JSON line.
 """
@@ -66,7 +67,7 @@ def parse():
     ap.add_argument("--workload", default="llama8b-fprop",
                     choices=["llama8b-fprop", "llama8b-fprop-pow2", "quant-sweep", "moe", "backward",
                              "backward-blockwise", "llama8b-fprop-qout", "kv-decode", "copy", "stream",
-                             "mfma-ceiling", "llama8b-fprop-mx"])
+                             "mfma-ceiling", "llama8b-fprop-mx", "backward-mx"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pow2", action="store_true",
                     help="moe, backward-blockwise: power-of-2 scales (E8M0 in the MFMA)")
@@ -894,6 +895,92 @@ def bench_backward_blockwise(args):
                 layers=per)
 
 
+def bench_backward_mx(args):
+    """8B-shaped backward linear layers in microscaling form (32-element blocks with E8M0 scale
+    bytes).  Per layer and step: dY quantized along out-features (fp8_quantize_mx, the dgrad A
+    operand) and along tokens with transposed codes (fp8_quantize_mx_columnwise_t, wgrad A), X
+    along tokens transposed (wgrad B), W along out-features transposed (dgrad B); dgrad
+    dX = dY . W and wgrad dW = dY^T . X, both by fp8_gemm_mx.  Inputs as backward-blockwise."""
+    import block_scaled_quantize_amd as bsq
+    import synth
+    bsq.load()
+    dev = torch.device("cuda", 0)
+    M = args.tokens
+    E4 = bsq.E4M3
+    layers = []
+    for name, k, n in LAYERS_8B:
+        layers.append(dict(
+            name=name, K=k, N=n,
+            x=synth.activations_with_outliers(M, k, 0, f"bench/bwdb/{name}/X").to(dev),
+            w=synth.normal((n, k), 0.02, 0, f"bench/bwdb/{name}/W").to(dev),
+            dy=synth.normal((M, n), 1e-3, 0, f"bench/bwdb/{name}/dY").to(dev),
+            dx=torch.empty((M, k), dtype=torch.bfloat16, device=dev),
+            dw=torch.empty((n, k), dtype=torch.bfloat16, device=dev)))
+    torch.cuda.synchronize()
+    flops = sum(4.0 * M * L["N"] * L["K"] for L in layers)
+    timer = EventTimer()
+
+    def step(t=None):
+        def run(key, fn):
+            return fn() if t is None else t.time((key, L["name"]), fn)
+        for L in layers:
+            qdy, sdy = run("q_dy", lambda: bsq.quantize_mx(L["dy"], E4))
+            qwt, swt = run("q_wT", lambda: bsq.quantize_mx_columnwise_t(L["w"], E4))
+            dyt, sdyt = run("q_dyT", lambda: bsq.quantize_mx_columnwise_t(L["dy"], E4))
+            xt, sxt = run("q_xT", lambda: bsq.quantize_mx_columnwise_t(L["x"], E4))
+            run("dgrad", lambda: bsq.gemm_mx(qdy, sdy, qwt, swt, c=L["dx"]))
+            run("wgrad", lambda: bsq.gemm_mx(dyt, sdyt, xt, sxt, c=L["dw"]))
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    for _ in range(max(3, min(args.steps, 10))):
+        step(timer)
+    torch.cuda.synchronize()
+    per, g_ms, g_f = {}, [], []
+    q_bytes, q_ms = 0.0, 0.0
+    for L in layers:
+        f = 2.0 * M * L["N"] * L["K"]
+        d = {}
+        for key in ("dgrad", "wgrad"):
+            ms = timer.mean_ms((key, L["name"]))
+            d[f"{key}_us"] = round(ms * 1e3, 2)
+            d[f"{key}_tflops"] = round(f / ms / 1e9, 1)
+            g_ms.append(ms)
+            g_f.append(f)
+        for key, n_el in (("q_dy", M * L["N"]), ("q_wT", L["N"] * L["K"]), ("q_dyT", M * L["N"]),
+                          ("q_xT", M * L["K"])):
+            ms = timer.mean_ms((key, L["name"]))
+            byts = 3.0 * n_el + n_el / 32
+            d[f"{key}_us"] = round(ms * 1e3, 2)
+            d[f"{key}_gbps"] = round(byts / ms / 1e6, 1)
+            q_bytes += byts
+            q_ms += ms
+        per[L["name"]] = d
+    achieved = float(np.mean(g_f)) / float(np.mean(g_ms)) / 1e9
+    return dict(metric="microscaling FP8 GEMM TFLOP/s, backward (dgrad + wgrad)",
+                value=round(flops / dt / 1e12, 2), unit="TFLOP/s", n_gpus=1, steps=args.steps,
+                warmup=args.warmup, ms_per_step=round(dt * 1e3, 4), higher_is_better=True,
+                scaling="weak", vs_baseline=None, dtype="fp8e4m3 x fp8e4m3 -> fp32 acc -> bf16",
+                data="synthetic",
+                config=dict(workload="llama3.1-8b-backward-mxfp8", tokens=M,
+                            scaling="32-element blocks, E8M0 bytes: dY along out-features "
+                            "(dgrad), dY^T, X^T along tokens (wgrad), W^T along out-features"),
+                roofline=dict(bound="mfma", achieved=round(achieved, 1), peak=FP8_PEAK_TFLOPS,
+                              unit="TFLOP/s", frac=round(achieved / FP8_PEAK_TFLOPS, 4),
+                              traffic=None,
+                              kernel="gemm_persistent_kernel<Cfg<256,256,2,4>,FPROP,E4M3,E4M3,mx> "
+                                     "(dgrad and wgrad launches)",
+                              mean_launch_us=round(float(np.mean(g_ms)) * 1e3, 2)),
+                quant_gbps=round(q_bytes / q_ms / 1e6, 1),
+                quant_hbm_frac=round(q_bytes / q_ms / 1e6 / HBM_PEAK_GBPS, 4),
+                layers=per)
+
+
 def bench_fprop_qout(args):
     """The 8B fprop layers with the output quantized in the GEMM epilogue (the next layer's 1x128
     E4M3 operand), against the same GEMM followed by the separate quantizer.  Per layer and step:
@@ -1124,6 +1211,8 @@ def main():
         res = bench_llama8b(args)
     elif args.workload == "llama8b-fprop-pow2":
         res = bench_llama8b(args, pow2=True)
+    elif args.workload == "backward-mx":
+        res = bench_backward_mx(args)
     elif args.workload == "llama8b-fprop-mx":
         res = bench_llama8b_mx(args)
     elif args.workload == "quant-sweep":
