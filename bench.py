@@ -816,9 +816,10 @@ def bench_backward(args):
 def bench_backward_blockwise(args):
     """8B-shaped backward linear layers in the block recipe ("NVIDIA NeMo RL ...", section "El
     avance técnico"; E4M3 gradients).  Per layer and step: dY quantized 1x128 along out-features
-    (dgrad operand) and columnwise over tokens (wgrad operand, transposed), X quantized columnwise
-    over tokens (transposed), W re-quantized 128x128; dgrad dX = dY . W (128x128 weight tiles),
-    wgrad dW = dY^T . X (1x128 scales on both operands).  --pow2: power-of-2 scales everywhere."""
+    (dgrad operand) and columnwise over tokens (wgrad operand, transposed) in one pass
+    (fp8_quantize_1x128_and_columnwise_t), X quantized columnwise over tokens (transposed), W
+    re-quantized 128x128; dgrad dX = dY . W (128x128 weight tiles), wgrad dW = dY^T . X (1x128
+    scales on both operands).  --pow2: power-of-2 scales everywhere."""
     import block_scaled_quantize_amd as bsq
     import synth
     bsq.load()
@@ -843,9 +844,9 @@ def bench_backward_blockwise(args):
         def run(key, fn):
             return fn() if t is None else t.time((key, L["name"]), fn)
         for L in layers:
-            qdy, sdy = run("q_dy", lambda: bsq.quantize_blockwise(L["dy"], E4, B1, mode))
+            qdy, sdy, dyt, sdyt = run("q_dy", lambda: bsq.quantize_1x128_and_columnwise_t(
+                L["dy"], E4, mode))
             qw, sw = run("q_w", lambda: bsq.quantize_blockwise(L["w"], E4, B128, mode))
-            dyt, sdyt = run("q_dyT", lambda: bsq.quantize_columnwise_t(L["dy"], E4, mode))
             xt, sxt = run("q_xT", lambda: bsq.quantize_columnwise_t(L["x"], E4, mode))
             run("dgrad", lambda: bsq.gemm_blockscaled(bsq.DGRAD, qdy, E4, B1, sdy, qw, E4, B128, sw,
                                                       c=L["dx"], pow2=args.pow2))
@@ -870,7 +871,8 @@ def bench_backward_blockwise(args):
             ms = timer.mean_ms((key, L["name"]))
             d[f"{key}_us"] = round(ms * 1e3, 2)
             d[f"{key}_tflops"] = round(f / ms / 1e9, 1)
-        for key, byts in (("q_dyT", 3.0 * M * L["N"]), ("q_xT", 3.0 * M * L["K"])):
+        # dY: 2 B read, 1 B of row codes and 1 B of transposed codes per element
+        for key, byts in (("q_dy", 4.0 * M * L["N"]), ("q_xT", 3.0 * M * L["K"])):
             ms = timer.mean_ms((key, L["name"]))
             d[f"{key}_us"] = round(ms * 1e3, 2)
             d[f"{key}_gbps"] = round(byts / ms / 1e6, 1)
@@ -884,8 +886,8 @@ def bench_backward_blockwise(args):
                 scaling="weak", vs_baseline=None, dtype="fp8e4m3 x fp8e4m3 -> fp32 acc -> bf16",
                 data="synthetic",
                 config=dict(workload="llama3.1-8b-backward-blockwise" + ("-pow2" if args.pow2 else ""),
-                            tokens=M, scaling="dY 1x128 (dgrad), dY^T and X^T columnwise 128x1 "
-                            "(wgrad), W 128x128"),
+                            tokens=M, scaling="dY 1x128 (dgrad) and dY^T columnwise 128x1 (wgrad) "
+                            "in one pass, X^T columnwise 128x1 (wgrad), W 128x128"),
                 roofline=dict(bound="mfma", achieved=round(achieved, 1), peak=FP8_PEAK_TFLOPS,
                               unit="TFLOP/s", frac=round(achieved / FP8_PEAK_TFLOPS, 4),
                               traffic=None,

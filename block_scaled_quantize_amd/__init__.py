@@ -64,6 +64,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.fp8_quantize_blockwise.argtypes = [vp, i64, i64, i64, i32, i32, i32, vp, i64, vp, vp]
     lib.fp8_quantize_columnwise_t.argtypes = [vp, i64, i64, i64, i32, i32, vp, i64, vp, vp]
     lib.fp8_quantize_mx_columnwise_t.argtypes = [vp, i64, i64, i64, i32, vp, i64, vp, vp]
+    lib.fp8_quantize_1x128_and_columnwise_t.argtypes = [vp, i64, i64, i64, i32, i32, vp, i64, vp,
+                                                        vp, i64, vp, vp]
     lib.fp8_quantize_mx.argtypes = [vp, i64, i64, i64, i32, vp, i64, vp, vp]
     lib.fp8_gemm_mx.argtypes = [i64, i64, i64, vp, i64, i32, vp, vp, i64, i32, vp, vp, i64, vp]
     lib.fp8_quantize_blockwise_batched.argtypes = [i32, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp]
@@ -91,7 +93,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.fp8_attention_decode_workspace_size.argtypes = [i64, i64, i64, i64, i64]
     lib.fp8_attention_decode_workspace_size.restype = sz
     for name in ("fp8_quantize_blockwise", "fp8_quantize_columnwise_t",
-                 "fp8_quantize_mx_columnwise_t", "fp8_quantize_delayed",
+                 "fp8_quantize_mx_columnwise_t", "fp8_quantize_1x128_and_columnwise_t",
+                 "fp8_quantize_delayed",
                  "fp8_quantize_blockwise_batched",
                  "fp8_quantize_delayed_noalloc",
                  "fp8_cast_fp32",
@@ -290,6 +293,36 @@ def quantize_columnwise_t(x: torch.Tensor, fmt: int, mode: int = SCALE_FP32,
                                             qt.stride(0), _ptr(scale_inv), _stream(stream)),
            "fp8_quantize_columnwise_t")
     return qt, scale_inv
+
+
+def quantize_1x128_and_columnwise_t(x: torch.Tensor, fmt: int, mode: int = SCALE_FP32,
+                                    q: torch.Tensor | None = None,
+                                    scale_inv: torch.Tensor | None = None,
+                                    qt: torch.Tensor | None = None,
+                                    scale_inv_t: torch.Tensor | None = None, stream=None):
+    """quantize_blockwise(x, fmt, BLOCK_1x128, mode) and quantize_columnwise_t(x, fmt, mode) in
+    one pass over x.  Returns (q, scale_inv, qt, scale_inv_t) as those two calls would."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 matrix with unit column stride")
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if scale_inv is None:
+        scale_inv = torch.empty(scale_shape(rows, cols, BLOCK_1x128), dtype=torch.float32,
+                                device=x.device)
+    if qt is None:
+        qt = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    if scale_inv_t is None:
+        scale_inv_t = torch.empty(((rows + 127) // 128, cols), dtype=torch.float32, device=x.device)
+    _need_matrix(q, (rows, cols), torch.uint8, "q")
+    _need_matrix(qt, (cols, rows), torch.uint8, "qt")
+    _need(scale_inv, scale_shape(rows, cols, BLOCK_1x128), torch.float32, "scale_inv")
+    _need(scale_inv_t, ((rows + 127) // 128, cols), torch.float32, "scale_inv_t")
+    _check(load().fp8_quantize_1x128_and_columnwise_t(
+        _ptr(x), rows, cols, x.stride(0), fmt, mode, _ptr(q), q.stride(0), _ptr(scale_inv),
+        _ptr(qt), qt.stride(0), _ptr(scale_inv_t), _stream(stream)),
+        "fp8_quantize_1x128_and_columnwise_t")
+    return q, scale_inv, qt, scale_inv_t
 
 
 def quantize_mx_columnwise_t(x: torch.Tensor, fmt: int, qt: torch.Tensor | None = None,

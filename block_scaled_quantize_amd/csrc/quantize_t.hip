@@ -51,10 +51,15 @@ __device__ __forceinline__ uint4 load8(const uint16_t* __restrict__ x, int64_t r
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-template <int FMT, bool POW2, bool VEC>
+// ROWS: the same pass also quantizes x in 1x128 blocks along its rows (fp8_quantize_blockwise's
+// codes q[rows][ld_q] and scales scale_inv_rows[ceil(cols/128)][rows]): a tile row spans the 16
+// lanes of one row group -- one DPP row of the wave -- 8 columns each, so its maximum is four
+// DPP steps, and each lane stores its 8 codes of the row as one 8-byte run.
+template <int FMT, bool POW2, bool VEC, bool ROWS = false>
 __global__ __launch_bounds__(kThreadsT) void quant_128x1_t_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
-    uint8_t* __restrict__ qt, int64_t ld_qt, float* __restrict__ scale_inv) {
+    uint8_t* __restrict__ qt, int64_t ld_qt, float* __restrict__ scale_inv,
+    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale_inv_rows) {
   __shared__ uint32_t s_max[4][16][4];   // [wave][column chunk][column pair], packed 16-bit
   const int t = threadIdx.x;
   const int lane = t & 63, wv = t >> 6;
@@ -69,6 +74,47 @@ __global__ __launch_bounds__(kThreadsT) void quant_128x1_t_kernel(
   for (int k = 0; k < 8; ++k) {
     const uint4 v = load8<VEC>(x, rows, cols, ld_x, r0 + k, c0);
     d[k][0] = v.x; d[k][1] = v.y; d[k][2] = v.z; d[k][3] = v.w;
+  }
+
+  if constexpr (ROWS) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int64_t r = r0 + k;
+      uint32_t a = hmax(max2(max2(mag2(d[k][0]), mag2(d[k][1])), max2(mag2(d[k][2]), mag2(d[k][3]))));
+      a = group8_max(a);
+      const uint32_t o = __builtin_amdgcn_mov_dpp(a, 0x140, 0xF, 0xF, false);   // row_mirror
+      a = a > o ? a : o;
+      const float sr = scale_from_amax_bits<FMT, POW2>(a);
+      float y[8];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        y[2 * p] = bf16_lo(d[k][p]) * sr;
+        y[2 * p + 1] = bf16_hi(d[k][p]) * sr;
+      }
+      const bool fin = a < 0x7F80u;
+      if (!fin) {
+        constexpr float F = Format<FMT>::fmax;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = __builtin_amdgcn_fmed3f(y[i], -F, F);
+      }
+      uint32_t lo = cvt4<FMT>(y[0], y[1], y[2], y[3]);
+      uint32_t hi = cvt4<FMT>(y[4], y[5], y[6], y[7]);
+      if (!fin) {
+        lo = patch_nan_pair(patch_nan_pair(lo, d[k][0], 0), d[k][1], 1);
+        hi = patch_nan_pair(patch_nan_pair(hi, d[k][2], 0), d[k][3], 1);
+      }
+      if (r < rows && c0 < cols) {
+        uint8_t* dst = q + r * ld_q + c0;
+        if (VEC && c0 + 8 <= cols) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (c0 + i < cols) dst[i] = (uint8_t)((i < 4 ? lo : hi) >> (8 * (i & 3)));
+        }
+        if (cg == 0) scale_inv_rows[cb * rows + r] = 1.0f / sr;
+      }
+    }
   }
 
   // Column maxima: over this lane's 8 rows, then over the wave's 4 row groups (lanes that
@@ -273,11 +319,13 @@ int dispatch_columnwise_t(bool pow2, bool vec, const uint16_t* x, int64_t rows, 
                           int64_t ld_x, uint8_t* qt, int64_t ld_qt, float* s, hipStream_t st) {
   const dim3 grid((unsigned)(ceil_div(rows, 128) * ceil_div(cols, 128)));
   const dim3 block(kThreadsT);
+  auto go = [&](auto kernel) {
+    return launch(kernel, grid, block, st, x, rows, cols, ld_x, qt, ld_qt, s, (uint8_t*)nullptr,
+                  (int64_t)0, (float*)nullptr);
+  };
   if (pow2)
-    return vec ? launch(quant_128x1_t_kernel<FMT, true, true>, grid, block, st, x, rows, cols, ld_x, qt, ld_qt, s)
-               : launch(quant_128x1_t_kernel<FMT, true, false>, grid, block, st, x, rows, cols, ld_x, qt, ld_qt, s);
-  return vec ? launch(quant_128x1_t_kernel<FMT, false, true>, grid, block, st, x, rows, cols, ld_x, qt, ld_qt, s)
-             : launch(quant_128x1_t_kernel<FMT, false, false>, grid, block, st, x, rows, cols, ld_x, qt, ld_qt, s);
+    return vec ? go(quant_128x1_t_kernel<FMT, true, true>) : go(quant_128x1_t_kernel<FMT, true, false>);
+  return vec ? go(quant_128x1_t_kernel<FMT, false, true>) : go(quant_128x1_t_kernel<FMT, false, false>);
 }
 
 }  // namespace
@@ -328,4 +376,42 @@ extern "C" int fp8_quantize_mx_columnwise_t(const void* x_bf16, int64_t rows, in
   if (fmt == FP8BS_E4M3)
     return vec ? go(quant_mx_t_kernel<FP8BS_E4M3, true>) : go(quant_mx_t_kernel<FP8BS_E4M3, false>);
   return vec ? go(quant_mx_t_kernel<FP8BS_E5M2, true>) : go(quant_mx_t_kernel<FP8BS_E5M2, false>);
+}
+
+extern "C" int fp8_quantize_1x128_and_columnwise_t(const void* x_bf16, int64_t rows, int64_t cols,
+                                                   int64_t ld_x, int fmt, int mode, void* q_out,
+                                                   int64_t ld_q, float* scale_inv_out,
+                                                   void* qt_out, int64_t ld_qt,
+                                                   float* scale_inv_t_out, void* stream) {
+  if (!fmt_ok(fmt) || (mode != FP8BS_SCALE_FP32 && mode != FP8BS_SCALE_POW2)) return FP8BS_ERR_ARG;
+  if (rows < 0 || cols < 0 || ld_x < cols || ld_q < cols || ld_qt < rows) return FP8BS_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return FP8BS_OK;
+  if (!x_bf16 || !q_out || !scale_inv_out || !qt_out || !scale_inv_t_out) return FP8BS_ERR_NULL;
+  if (ceil_div(rows, 128) * ceil_div(cols, 128) > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
+  if (rows > INT64_MAX / ld_x || rows > INT64_MAX / ld_q || cols > INT64_MAX / ld_qt)
+    return FP8BS_ERR_SHAPE;
+  if (!aligned4(scale_inv_out) || !aligned4(scale_inv_t_out)) return FP8BS_ERR_ALIGN;
+  const bool vec = aligned16(x_bf16) && aligned16(qt_out) && ld_x % 8 == 0 && ld_qt % 16 == 0 &&
+                   (reinterpret_cast<uintptr_t>(q_out) & 7u) == 0 && ld_q % 8 == 0;
+  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
+  uint8_t* q = static_cast<uint8_t*>(q_out);
+  uint8_t* qt = static_cast<uint8_t*>(qt_out);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)(ceil_div(rows, 128) * ceil_div(cols, 128)));
+  const dim3 block(kThreadsT);
+  auto go = [&](auto kernel) {
+    return launch(kernel, grid, block, st, x, rows, cols, ld_x, qt, ld_qt, scale_inv_t_out, q, ld_q,
+                  scale_inv_out);
+  };
+  const bool pow2 = mode == FP8BS_SCALE_POW2;
+  if (fmt == FP8BS_E4M3) {
+    if (pow2) return vec ? go(quant_128x1_t_kernel<FP8BS_E4M3, true, true, true>)
+                         : go(quant_128x1_t_kernel<FP8BS_E4M3, true, false, true>);
+    return vec ? go(quant_128x1_t_kernel<FP8BS_E4M3, false, true, true>)
+               : go(quant_128x1_t_kernel<FP8BS_E4M3, false, false, true>);
+  }
+  if (pow2) return vec ? go(quant_128x1_t_kernel<FP8BS_E5M2, true, true, true>)
+                       : go(quant_128x1_t_kernel<FP8BS_E5M2, true, false, true>);
+  return vec ? go(quant_128x1_t_kernel<FP8BS_E5M2, false, true, true>)
+             : go(quant_128x1_t_kernel<FP8BS_E5M2, false, false, true>);
 }

@@ -169,6 +169,21 @@ int fp8_quantize_columnwise_t(const void* x_bf16, int64_t rows, int64_t cols, in
                               int fmt, int mode, void* qt_out, int64_t ld_qt,
                               float* scale_inv_out, void* stream);
 
+/* fp8_quantize_blockwise with FP8BS_BLOCK_1x128 and fp8_quantize_columnwise_t in one pass over x
+ * (one read of the bf16 tensor for both, e.g. the output gradient dY of a layer: its 1x128
+ * codes feed the data-gradient GEMM, its transposed 128x1 codes the weight-gradient GEMM) --
+ * the sections of those two functions.  Results are bit for bit those of the two calls:
+ *   q_out [rows][ld_q], scale_inv_out float[ceil(cols/128)][rows]       (fp8_quantize_blockwise)
+ *   qt_out [cols][ld_qt], scale_inv_t_out float[ceil(rows/128)][cols]   (fp8_quantize_columnwise_t)
+ * with the same fmt and mode for both.  Requirements: ld_x >= cols, ld_q >= cols, ld_qt >= rows.
+ * rows == 0 or cols == 0 is a no-op.  Caller-owned device buffers; nothing is allocated.
+ * Errors: FP8BS_ERR_NULL, FP8BS_ERR_SHAPE, FP8BS_ERR_ALIGN (a scale array not 4-byte aligned),
+ * FP8BS_ERR_ARG, FP8BS_ERR_LAUNCH. */
+int fp8_quantize_1x128_and_columnwise_t(const void* x_bf16, int64_t rows, int64_t cols,
+                                        int64_t ld_x, int fmt, int mode, void* q_out, int64_t ld_q,
+                                        float* scale_inv_out, void* qt_out, int64_t ld_qt,
+                                        float* scale_inv_t_out, void* stream);
+
 /* Microscaling (MXFP8) quantization along columns, codes written transposed -- the sections of
  * fp8_quantize_mx.  A block is 32 consecutive rows of one column of x[rows][cols], i.e. a
  * 32-element row block of x^T, quantized exactly as fp8_quantize_mx quantizes x^T (power-of-2

@@ -146,6 +146,25 @@ def qcol(**kw):
                                                 a["mode"], a["qt"], a["ldqt"], a["s"], None)
 
 
+def test_quantize_rows_and_columnwise_validation():
+    f = bsq.load().fp8_quantize_1x128_and_columnwise_t
+    def call(**kw):
+        a = dict(x=FAKE, rows=256, cols=128, ldx=128, fmt=0, mode=0, q=FAKE, ldq=128, s=FAKE,
+                 qt=FAKE, ldqt=256, st=FAKE)
+        a.update(kw)
+        return f(a["x"], a["rows"], a["cols"], a["ldx"], a["fmt"], a["mode"], a["q"], a["ldq"],
+                 a["s"], a["qt"], a["ldqt"], a["st"], None)
+    assert call(fmt=2) == bsq.ERR_ARG
+    assert call(mode=5) == bsq.ERR_ARG
+    assert call(ldq=100) == bsq.ERR_SHAPE
+    assert call(ldqt=255) == bsq.ERR_SHAPE
+    assert call(q=None) == bsq.ERR_NULL
+    assert call(st=None) == bsq.ERR_NULL
+    assert call(s=FAKE_ODD) == bsq.ERR_ALIGN
+    assert call(st=FAKE_ODD) == bsq.ERR_ALIGN
+    assert call(rows=0) == bsq.OK and call(cols=0, x=None) == bsq.OK
+
+
 def test_quantize_columnwise_validation():
     assert qcol(fmt=2) == bsq.ERR_ARG
     assert qcol(mode=5) == bsq.ERR_ARG
