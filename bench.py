@@ -899,8 +899,8 @@ def bench_backward_blockwise(args):
 
 def bench_backward_mx(args):
     """8B-shaped backward linear layers in microscaling form (32-element blocks with E8M0 scale
-    bytes).  Per layer and step: dY quantized along out-features (fp8_quantize_mx, the dgrad A
-    operand) and along tokens with transposed codes (fp8_quantize_mx_columnwise_t, wgrad A), X
+    bytes).  Per layer and step: dY quantized along out-features (the dgrad A operand) and along
+    tokens with transposed codes (wgrad A) in one pass (fp8_quantize_mx_and_columnwise_t), X
     along tokens transposed (wgrad B), W along out-features transposed (dgrad B); dgrad
     dX = dY . W and wgrad dW = dY^T . X, both by fp8_gemm_mx.  Inputs as backward-blockwise."""
     import block_scaled_quantize_amd as bsq
@@ -926,9 +926,8 @@ def bench_backward_mx(args):
         def run(key, fn):
             return fn() if t is None else t.time((key, L["name"]), fn)
         for L in layers:
-            qdy, sdy = run("q_dy", lambda: bsq.quantize_mx(L["dy"], E4))
+            qdy, sdy, dyt, sdyt = run("q_dy", lambda: bsq.quantize_mx_and_columnwise_t(L["dy"], E4))
             qwt, swt = run("q_wT", lambda: bsq.quantize_mx_columnwise_t(L["w"], E4))
-            dyt, sdyt = run("q_dyT", lambda: bsq.quantize_mx_columnwise_t(L["dy"], E4))
             xt, sxt = run("q_xT", lambda: bsq.quantize_mx_columnwise_t(L["x"], E4))
             run("dgrad", lambda: bsq.gemm_mx(qdy, sdy, qwt, swt, c=L["dx"]))
             run("wgrad", lambda: bsq.gemm_mx(dyt, sdyt, xt, sxt, c=L["dw"]))
@@ -954,10 +953,11 @@ def bench_backward_mx(args):
             d[f"{key}_tflops"] = round(f / ms / 1e9, 1)
             g_ms.append(ms)
             g_f.append(f)
-        for key, n_el in (("q_dy", M * L["N"]), ("q_wT", L["N"] * L["K"]), ("q_dyT", M * L["N"]),
-                          ("q_xT", M * L["K"])):
+        # dY: 2 B read, 1 B of row codes, 1 B of transposed codes (and two scale bytes per 32)
+        for key, n_el, per_el in (("q_dy", M * L["N"], 4.0 + 2 / 32), ("q_wT", L["N"] * L["K"], 3.0 + 1 / 32),
+                                  ("q_xT", M * L["K"], 3.0 + 1 / 32)):
             ms = timer.mean_ms((key, L["name"]))
-            byts = 3.0 * n_el + n_el / 32
+            byts = per_el * n_el
             d[f"{key}_us"] = round(ms * 1e3, 2)
             d[f"{key}_gbps"] = round(byts / ms / 1e6, 1)
             q_bytes += byts

@@ -66,6 +66,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.fp8_quantize_mx_columnwise_t.argtypes = [vp, i64, i64, i64, i32, vp, i64, vp, vp]
     lib.fp8_quantize_1x128_and_columnwise_t.argtypes = [vp, i64, i64, i64, i32, i32, vp, i64, vp,
                                                         vp, i64, vp, vp]
+    lib.fp8_quantize_mx_and_columnwise_t.argtypes = [vp, i64, i64, i64, i32, vp, i64, vp, vp, i64,
+                                                     vp, vp]
     lib.fp8_quantize_mx.argtypes = [vp, i64, i64, i64, i32, vp, i64, vp, vp]
     lib.fp8_gemm_mx.argtypes = [i64, i64, i64, vp, i64, i32, vp, vp, i64, i32, vp, vp, i64, vp]
     lib.fp8_quantize_blockwise_batched.argtypes = [i32, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp]
@@ -94,6 +96,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.fp8_attention_decode_workspace_size.restype = sz
     for name in ("fp8_quantize_blockwise", "fp8_quantize_columnwise_t",
                  "fp8_quantize_mx_columnwise_t", "fp8_quantize_1x128_and_columnwise_t",
+                 "fp8_quantize_mx_and_columnwise_t",
                  "fp8_quantize_delayed",
                  "fp8_quantize_blockwise_batched",
                  "fp8_quantize_delayed_noalloc",
@@ -323,6 +326,33 @@ def quantize_1x128_and_columnwise_t(x: torch.Tensor, fmt: int, mode: int = SCALE
         _ptr(qt), qt.stride(0), _ptr(scale_inv_t), _stream(stream)),
         "fp8_quantize_1x128_and_columnwise_t")
     return q, scale_inv, qt, scale_inv_t
+
+
+def quantize_mx_and_columnwise_t(x: torch.Tensor, fmt: int, q: torch.Tensor | None = None,
+                                 scales: torch.Tensor | None = None,
+                                 qt: torch.Tensor | None = None,
+                                 scales_t: torch.Tensor | None = None, stream=None):
+    """quantize_mx(x, fmt) and quantize_mx_columnwise_t(x, fmt) in one pass over x.
+    Returns (q, scales, qt, scales_t) as those two calls would."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 matrix with unit column stride")
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(mx_scale_shape(rows, cols), dtype=torch.uint8, device=x.device)
+    if qt is None:
+        qt = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    if scales_t is None:
+        scales_t = torch.empty(mx_scale_shape(cols, rows), dtype=torch.uint8, device=x.device)
+    _need_matrix(q, (rows, cols), torch.uint8, "q")
+    _need_matrix(qt, (cols, rows), torch.uint8, "qt")
+    _need(scales, mx_scale_shape(rows, cols), torch.uint8, "scales")
+    _need(scales_t, mx_scale_shape(cols, rows), torch.uint8, "scales_t")
+    _check(load().fp8_quantize_mx_and_columnwise_t(
+        _ptr(x), rows, cols, x.stride(0), fmt, _ptr(q), q.stride(0), _ptr(scales), _ptr(qt),
+        qt.stride(0), _ptr(scales_t), _stream(stream)), "fp8_quantize_mx_and_columnwise_t")
+    return q, scales, qt, scales_t
 
 
 def quantize_mx_columnwise_t(x: torch.Tensor, fmt: int, qt: torch.Tensor | None = None,

@@ -217,10 +217,15 @@ __global__ __launch_bounds__(kThreadsT) void quant_128x1_t_kernel(
 // shuffles inside the wave.  The E8M0 byte is 254 minus the exponent field of s (the exponent of
 // 1/s), and the four blocks of a tile column (one per wave) leave as one 4-byte word at
 // [128-row block][column]: the microscaling scale layout of x^T.
-template <int FMT, bool VEC>
+// ROWS: the same pass also quantizes x along its rows as fp8_quantize_mx does (codes
+// q[rows][ld_q], scale words se_rows[ceil(cols/128)][rows]): a 32-column row block is one quad
+// of the row group's 16 lanes (two DPP steps), and lane 0 of the row group gathers the four
+// blocks' bytes of its 128 columns into one word.
+template <int FMT, bool VEC, bool ROWS = false>
 __global__ __launch_bounds__(kThreadsT) void quant_mx_t_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
-    uint8_t* __restrict__ qt, int64_t ld_qt, uint32_t* __restrict__ se) {
+    uint8_t* __restrict__ qt, int64_t ld_qt, uint32_t* __restrict__ se,
+    uint8_t* __restrict__ q, int64_t ld_q, uint32_t* __restrict__ se_rows) {
   __shared__ uint32_t s_e8[128];   // per tile column, byte w = the factor of wave w's block
   __shared__ __attribute__((aligned(16))) uint8_t s_t[128 * 136];
   const int t = threadIdx.x;
@@ -236,6 +241,52 @@ __global__ __launch_bounds__(kThreadsT) void quant_mx_t_kernel(
   for (int k = 0; k < 8; ++k) {
     const uint4 v = load8<VEC>(x, rows, cols, ld_x, r0 + k, c0);
     d[k][0] = v.x; d[k][1] = v.y; d[k][2] = v.z; d[k][3] = v.w;
+  }
+  if constexpr (ROWS) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int64_t r = r0 + k;
+      uint32_t a = hmax(max2(max2(mag2(d[k][0]), mag2(d[k][1])), max2(mag2(d[k][2]), mag2(d[k][3]))));
+      uint32_t o = __builtin_amdgcn_mov_dpp(a, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+      a = a > o ? a : o;
+      o = __builtin_amdgcn_mov_dpp(a, 0x4E, 0xF, 0xF, false);            // quad_perm [2,3,0,1]
+      a = a > o ? a : o;
+      const float sr = scale_from_amax_bits<FMT, true>(a);
+      float y[8];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        y[2 * p] = bf16_lo(d[k][p]) * sr;
+        y[2 * p + 1] = bf16_hi(d[k][p]) * sr;
+      }
+      const bool fin = a < 0x7F80u;
+      if (!fin) {
+        constexpr float F = Format<FMT>::fmax;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = __builtin_amdgcn_fmed3f(y[i], -F, F);
+      }
+      uint32_t lo = cvt4<FMT>(y[0], y[1], y[2], y[3]);
+      uint32_t hi = cvt4<FMT>(y[4], y[5], y[6], y[7]);
+      if (!fin) {
+        lo = patch_nan_pair(patch_nan_pair(lo, d[k][0], 0), d[k][1], 1);
+        hi = patch_nan_pair(patch_nan_pair(hi, d[k][2], 0), d[k][3], 1);
+      }
+      // the bytes of the row's four 32-column blocks, from lanes 0, 4, 8, 12 of the row group
+      const uint32_t byte = 254u - ((__float_as_uint(sr) >> 23) & 0xFFu);
+      const uint32_t word = byte | ((uint32_t)__shfl_down((int)byte, 4) << 8) |
+                            ((uint32_t)__shfl_down((int)byte, 8) << 16) |
+                            ((uint32_t)__shfl_down((int)byte, 12) << 24);
+      if (r < rows && c0 < cols) {
+        uint8_t* dst = q + r * ld_q + c0;
+        if (VEC && c0 + 8 <= cols) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (c0 + i < cols) dst[i] = (uint8_t)((i < 4 ? lo : hi) >> (8 * (i & 3)));
+        }
+        if (cg == 0) se_rows[cb * rows + r] = word;
+      }
+    }
   }
   uint32_t m[4];
 #pragma unroll
@@ -372,10 +423,45 @@ extern "C" int fp8_quantize_mx_columnwise_t(const void* x_bf16, int64_t rows, in
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)(ceil_div(rows, 128) * ceil_div(cols, 128)));
   const dim3 block(kThreadsT);
-  auto go = [&](auto kernel) { return launch(kernel, grid, block, st, x, rows, cols, ld_x, qt, ld_qt, se); };
+  auto go = [&](auto kernel) {
+    return launch(kernel, grid, block, st, x, rows, cols, ld_x, qt, ld_qt, se, (uint8_t*)nullptr,
+                  (int64_t)0, (uint32_t*)nullptr);
+  };
   if (fmt == FP8BS_E4M3)
     return vec ? go(quant_mx_t_kernel<FP8BS_E4M3, true>) : go(quant_mx_t_kernel<FP8BS_E4M3, false>);
   return vec ? go(quant_mx_t_kernel<FP8BS_E5M2, true>) : go(quant_mx_t_kernel<FP8BS_E5M2, false>);
+}
+
+extern "C" int fp8_quantize_mx_and_columnwise_t(const void* x_bf16, int64_t rows, int64_t cols,
+                                                int64_t ld_x, int fmt, void* q_out, int64_t ld_q,
+                                                void* scale_e8m0_out, void* qt_out, int64_t ld_qt,
+                                                void* scale_e8m0_t_out, void* stream) {
+  if (!fmt_ok(fmt)) return FP8BS_ERR_ARG;
+  if (rows < 0 || cols < 0 || ld_x < cols || ld_q < cols || ld_qt < rows) return FP8BS_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return FP8BS_OK;
+  if (!x_bf16 || !q_out || !scale_e8m0_out || !qt_out || !scale_e8m0_t_out) return FP8BS_ERR_NULL;
+  if (ceil_div(rows, 128) * ceil_div(cols, 128) > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
+  if (rows > INT64_MAX / ld_x || rows > INT64_MAX / ld_q || cols > INT64_MAX / ld_qt)
+    return FP8BS_ERR_SHAPE;
+  if (!aligned4(scale_e8m0_out) || !aligned4(scale_e8m0_t_out)) return FP8BS_ERR_ALIGN;
+  const bool vec = aligned16(x_bf16) && aligned16(qt_out) && ld_x % 8 == 0 && ld_qt % 16 == 0 &&
+                   (reinterpret_cast<uintptr_t>(q_out) & 7u) == 0 && ld_q % 8 == 0;
+  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
+  uint8_t* q = static_cast<uint8_t*>(q_out);
+  uint8_t* qt = static_cast<uint8_t*>(qt_out);
+  uint32_t* se = static_cast<uint32_t*>(scale_e8m0_out);
+  uint32_t* set = static_cast<uint32_t*>(scale_e8m0_t_out);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)(ceil_div(rows, 128) * ceil_div(cols, 128)));
+  const dim3 block(kThreadsT);
+  auto go = [&](auto kernel) {
+    return launch(kernel, grid, block, st, x, rows, cols, ld_x, qt, ld_qt, set, q, ld_q, se);
+  };
+  if (fmt == FP8BS_E4M3)
+    return vec ? go(quant_mx_t_kernel<FP8BS_E4M3, true, true>)
+               : go(quant_mx_t_kernel<FP8BS_E4M3, false, true>);
+  return vec ? go(quant_mx_t_kernel<FP8BS_E5M2, true, true>)
+             : go(quant_mx_t_kernel<FP8BS_E5M2, false, true>);
 }
 
 extern "C" int fp8_quantize_1x128_and_columnwise_t(const void* x_bf16, int64_t rows, int64_t cols,

@@ -203,6 +203,20 @@ int fp8_quantize_mx_columnwise_t(const void* x_bf16, int64_t rows, int64_t cols,
                                  int fmt, void* qt_out, int64_t ld_qt, void* scale_e8m0_out,
                                  void* stream);
 
+/* fp8_quantize_mx and fp8_quantize_mx_columnwise_t in one pass over x (one read of, e.g., the
+ * output gradient dY for both microscaling backward products) -- the sections of those two
+ * functions; results bit for bit those of the two calls:
+ *   q_out [rows][ld_q], scale_e8m0_out [ceil(cols/128)][rows][4]           (fp8_quantize_mx)
+ *   qt_out [cols][ld_qt], scale_e8m0_t_out [ceil(rows/128)][cols][4]       (..._columnwise_t)
+ * Requirements: ld_x >= cols, ld_q >= cols, ld_qt >= rows; scale arrays 4-byte aligned.
+ * rows == 0 or cols == 0 is a no-op.  Caller-owned device buffers; nothing is allocated.
+ * Errors: FP8BS_ERR_ARG (fmt), FP8BS_ERR_SHAPE, FP8BS_ERR_NULL, FP8BS_ERR_ALIGN,
+ * FP8BS_ERR_LAUNCH. */
+int fp8_quantize_mx_and_columnwise_t(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                                     int fmt, void* q_out, int64_t ld_q, void* scale_e8m0_out,
+                                     void* qt_out, int64_t ld_qt, void* scale_e8m0_t_out,
+                                     void* stream);
+
 /*
  * One step of per-tensor delayed scaling on a contiguous bf16 tensor x[numel].
  * [P1] "Transformer Engine: la base de software": the scale used in a step comes from the

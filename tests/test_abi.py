@@ -465,6 +465,15 @@ def test_mx_validation():
     assert qmt(FAKE, 256, 64, 64, 0, None, 256, FAKE, None) == bsq.ERR_NULL
     assert qmt(FAKE, 256, 64, 64, 0, FAKE, 256, FAKE_ODD, None) == bsq.ERR_ALIGN
     assert qmt(None, 0, 64, 64, 0, None, 0, None, None) == bsq.OK
+    # rows and columns in one pass
+    qmr = lib.fp8_quantize_mx_and_columnwise_t
+    assert qmr(FAKE, 256, 64, 64, 2, FAKE, 64, FAKE, FAKE, 256, FAKE, None) == bsq.ERR_ARG
+    assert qmr(FAKE, 256, 64, 64, 0, FAKE, 63, FAKE, FAKE, 256, FAKE, None) == bsq.ERR_SHAPE
+    assert qmr(FAKE, 256, 64, 64, 0, FAKE, 64, FAKE, FAKE, 255, FAKE, None) == bsq.ERR_SHAPE
+    assert qmr(FAKE, 256, 64, 64, 0, FAKE, 64, FAKE, None, 256, FAKE, None) == bsq.ERR_NULL
+    assert qmr(FAKE, 256, 64, 64, 0, FAKE, 64, FAKE_ODD, FAKE, 256, FAKE, None) == bsq.ERR_ALIGN
+    assert qmr(FAKE, 256, 64, 64, 0, FAKE, 64, FAKE, FAKE, 256, FAKE_ODD, None) == bsq.ERR_ALIGN
+    assert qmr(None, 0, 64, 64, 0, None, 64, None, None, 0, None, None) == bsq.OK
     # GEMM: formats, misaligned scales, null scales, pitches; empty is a no-op
     def gemm(**kw):
         v = dict(M=64, N=64, K=128, lda=128, fa=0, sa=FAKE, ldb=128, fb=0, sb=FAKE, C=FAKE, ldc=64)

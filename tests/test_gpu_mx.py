@@ -209,7 +209,7 @@ def test_mx_argument_checks(gpu):
 
 # ------------------------------------------------------------------ columnwise (transposed) form
 
-def run_quant_t(gpu, rows, cols, fmt, x=None, pitch=None, seed=0):
+def run_quant_t(gpu, rows, cols, fmt, x=None, pitch=None, seed=0, fused=False):
     if x is None:
         x = synth.activations_with_outliers(rows, cols, seed, f"mx/quant_t/{rows}x{cols}")
     ld = pitch if pitch is not None else cols
@@ -219,36 +219,53 @@ def run_quant_t(gpu, rows, cols, fmt, x=None, pitch=None, seed=0):
     ldq = rows + (16 if pitch is not None else 0)
     qstore = torch.full((cols, ldq), 0xA5, dtype=torch.uint8, device="cuda")
     scales = torch.full(bsq.mx_scale_shape(cols, rows), 0xAB, dtype=torch.uint8, device="cuda")
-    q, s = gpu.quantize_mx_columnwise_t(xd, fmt, qt=qstore[:, :rows], scales=scales)
-    torch.cuda.synchronize()
+    if fused:
+        rstore = torch.full((rows, cols + 16), 0x5A, dtype=torch.uint8, device="cuda")
+        rscales = torch.full(bsq.mx_scale_shape(rows, cols), 0xAB, dtype=torch.uint8, device="cuda")
+        qr, sr, q, s = gpu.quantize_mx_and_columnwise_t(xd, fmt, q=rstore[:, :cols], scales=rscales,
+                                                        qt=qstore[:, :rows], scales_t=scales)
+        torch.cuda.synchronize()
+        qro, sro = oracle.quantize_mx(x, fmt)
+        assert_bytes_equal(qr.cpu().numpy(), qro, f"row codes {rows}x{cols}")
+        assert_bytes_equal(sr.cpu().numpy(), abi_scales(sro, 127), f"row scale bytes {rows}x{cols}")
+        assert torch.all(rstore[:, cols:] == 0x5A), "row codes past the columns written"
+    else:
+        q, s = gpu.quantize_mx_columnwise_t(xd, fmt, qt=qstore[:, :rows], scales=scales)
+        torch.cuda.synchronize()
     qo, so = oracle.quantize_mx_columnwise_t(x, fmt)
     assert_bytes_equal(q.cpu().numpy(), qo, f"transposed codes {rows}x{cols}")
     assert_bytes_equal(s.cpu().numpy(), abi_scales(so, 127), f"scale bytes {rows}x{cols}")
     assert torch.all(qstore[:, rows:] == 0xA5), "codes past the transposed rows written"
 
 
+FUSED = pytest.mark.parametrize("fused", [False, True], ids=["columnwise", "rows+columnwise"])
+
+
+@FUSED
 @pytest.mark.parametrize("rows,cols", [(1, 1), (33, 70), (300, 129), (128, 128), (4096, 256),
                                        (70, 5)])
 @pytest.mark.parametrize("fmt", [E4, E5])
-def test_quantize_mx_columnwise_bit_exact(gpu, rows, cols, fmt):
-    run_quant_t(gpu, rows, cols, fmt)
+def test_quantize_mx_columnwise_bit_exact(gpu, rows, cols, fmt, fused):
+    run_quant_t(gpu, rows, cols, fmt, fused=fused)
 
 
-def test_quantize_mx_columnwise_pitch_and_specials(gpu):
-    run_quant_t(gpu, 200, 384, E4, pitch=392)
+@FUSED
+def test_quantize_mx_columnwise_pitch_and_specials(gpu, fused):
+    run_quant_t(gpu, 200, 384, E4, pitch=392, fused=fused)
     x = synth.activations_with_outliers(96, 64, 5, "mx/quant_t/special")
     x[:, 3] = 0.0                                     # all-zero blocks: byte 127
     x[10, 7] = float("nan")
     x[40, 9] = float("inf")
     x[70:, 11] = torch.tensor(1e-40).bfloat16()       # bf16 subnormals: the largest scale
     x[5, 13] = 3.0e38                                 # huge magnitude: the smallest scale
-    run_quant_t(gpu, 96, 64, E4, x=x)
-    run_quant_t(gpu, 96, 64, E5, x=x)
+    run_quant_t(gpu, 96, 64, E4, x=x, fused=fused)
+    run_quant_t(gpu, 96, 64, E5, x=x, fused=fused)
 
 
-def test_quantize_mx_columnwise_full_size(gpu):
+@FUSED
+def test_quantize_mx_columnwise_full_size(gpu, fused):
     x = synth.activations_with_outliers(8192, 4096, 0, "bench/8b/qkv/X")
-    run_quant_t(gpu, 8192, 4096, E4, x=x)
+    run_quant_t(gpu, 8192, 4096, E4, x=x, fused=fused)
 
 
 def test_mx_backward_wgrad_and_dgrad(gpu):
