@@ -71,6 +71,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pow2", action="store_true",
                     help="moe, backward-blockwise: power-of-2 scales (E8M0 in the MFMA)")
+    ap.add_argument("--mx", action="store_true",
+                    help="moe: microscaling scales (32-element blocks, E8M0 bytes)")
     ap.add_argument("--tokens", type=int, default=8192)
     ap.add_argument("--kv-split", type=int, default=-1,
                     help="kv-decode: tokens per chunk of fp8_attention_decode_split (0: unsplit, "
@@ -663,11 +665,14 @@ def bench_stream(args):
 def bench_moe(args):
     """Grouped FP8 GEMM of a Qwen3-30B-A3B-shaped MoE layer: 128 experts, 16384 tokens routed
     top-8 with Zipf(1.1) popularity (131072 rows sorted by expert); gate/up 2048 -> 1536 and
-    down 768 -> 2048 per expert, 1x128 activation / 128x128 weight E4M3 scales, bf16 out."""
+    down 768 -> 2048 per expert, 1x128 activation / 128x128 weight E4M3 scales, bf16 out.
+    --pow2: power-of-2 scales applied by the MFMA; --mx: microscaling (32-element blocks with
+    E8M0 bytes on the activations and every expert's weights, fp8_grouped_gemm_mx)."""
     import block_scaled_quantize_amd as bsq
     import synth
     bsq.load()
     dev = torch.device("cuda", 0)
+    mx = getattr(args, "mx", False)
     counts = synth.moe_routing(16384, 128, 8, 1.1, 0)
     off = torch.from_numpy(synth.offsets_from_counts(counts)).to(dev)
     T = int(counts.sum())
@@ -676,27 +681,45 @@ def bench_moe(args):
     for name, K, N in (("gate_up", 2048, 1536), ("down", 768, 2048)):
         x = synth.normal((T, K), 1.0, 0, f"bench/moe/{name}/X").to(dev)
         mode = bsq.SCALE_POW2 if args.pow2 else bsq.SCALE_FP32
-        qx, sx = bsq.quantize_blockwise(x, bsq.E4M3, bsq.BLOCK_1x128, mode)
+        if mx:
+            qx, sx = bsq.quantize_mx(x, bsq.E4M3)
+        else:
+            qx, sx = bsq.quantize_blockwise(x, bsq.E4M3, bsq.BLOCK_1x128, mode)
         del x
         qw = torch.empty((128, N, K), dtype=torch.uint8, device=dev)
-        sw = torch.empty((128, N // 128, K // 128), dtype=torch.float32, device=dev)
+        if mx:
+            sw = torch.empty((128,) + bsq.mx_scale_shape(N, K), dtype=torch.uint8, device=dev)
+        else:
+            sw = torch.empty((128, N // 128, K // 128), dtype=torch.float32, device=dev)
         for e in range(128):
             w = synth.normal((N, K), 0.02, 0, f"bench/moe/{name}/W{e}").to(dev)
-            bsq.quantize_blockwise(w, bsq.E4M3, bsq.BLOCK_128x128, mode, q=qw[e], scale_inv=sw[e])
+            if mx:
+                bsq.quantize_mx(w, bsq.E4M3, q=qw[e], scales=sw[e])
+            else:
+                bsq.quantize_blockwise(w, bsq.E4M3, bsq.BLOCK_128x128, mode, q=qw[e], scale_inv=sw[e])
         c = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+
+        def run():
+            if mx:
+                bsq.grouped_gemm_mx(off, qx, sx, qw, sw, c=c)
+            else:
+                bsq.grouped_gemm(off, qx, sx, qw, sw, c=c, pow2=args.pow2)
         for _ in range(args.warmup):
-            bsq.grouped_gemm(off, qx, sx, qw, sw, c=c, pow2=args.pow2)
+            run()
         torch.cuda.synchronize()
         iters = max(args.steps, 5)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
         for a, b in ev:
             a.record()
-            bsq.grouped_gemm(off, qx, sx, qw, sw, c=c, pow2=args.pow2)
+            run()
             b.record()
         torch.cuda.synchronize()
         ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
         flops = 2.0 * T * N * K
-        byts = T * K + 128 * N * K + 2 * T * N + 4 * T * K / 128 + 4 * 128 * (N // 128) * (K // 128)
+        if mx:
+            byts = T * K + 128 * N * K + 2 * T * N + T * K / 32 + 128 * N * K / 32
+        else:
+            byts = T * K + 128 * N * K + 2 * T * N + 4 * T * K / 128 + 4 * 128 * (N // 128) * (K // 128)
         t_mfma = flops / (FP8_PEAK_TFLOPS * 1e12)
         t_hbm = byts / (HBM_PEAK_GBPS * 1e9)
         bound = "mfma" if t_mfma >= t_hbm else "hbm"
@@ -713,14 +736,14 @@ def bench_moe(args):
                 steps=max(args.steps, 5), warmup=args.warmup, ms_per_step=round(total_ms, 4),
                 higher_is_better=True, scaling="weak", vs_baseline=None,
                 dtype="fp8e4m3 x fp8e4m3 -> fp32 acc -> bf16", data="synthetic",
-                config=dict(workload="qwen3-30b-a3b-moe-experts" + ("-pow2" if args.pow2 else ""),
+                config=dict(workload="qwen3-30b-a3b-moe-experts" + ("-mxfp8" if mx else "-pow2" if args.pow2 else ""),
                             experts=128, tokens=16384, topk=8,
                             routing="Zipf(1.1)", rows=T),
                 roofline=dict(bound=gu["bound"], achieved=gu["tflops"], peak=FP8_PEAK_TFLOPS,
                               unit="TFLOP/s", frac=round(gu["tflops"] / FP8_PEAK_TFLOPS, 4),
                               traffic=None,
                               kernel="grouped_gemm_kernel<Cfg<256,256,2,4>,E4M3,E4M3,%s>"
-                                     % ("hw" if args.pow2 else "fold")),
+                                     % ("mx" if mx else "hw" if args.pow2 else "fold")),
                 layers=out)
 
 

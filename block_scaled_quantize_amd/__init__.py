@@ -68,6 +68,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
                                                         vp, i64, vp, vp]
     lib.fp8_quantize_mx_and_columnwise_t.argtypes = [vp, i64, i64, i64, i32, vp, i64, vp, vp, i64,
                                                      vp, vp]
+    lib.fp8_grouped_gemm_mx.argtypes = [i32, vp, i64, i64, i64, vp, i64, i32, vp, vp, i64, i32, vp,
+                                        vp, i64, vp]
     lib.fp8_quantize_mx.argtypes = [vp, i64, i64, i64, i32, vp, i64, vp, vp]
     lib.fp8_gemm_mx.argtypes = [i64, i64, i64, vp, i64, i32, vp, vp, i64, i32, vp, vp, i64, vp]
     lib.fp8_quantize_blockwise_batched.argtypes = [i32, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp]
@@ -96,7 +98,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.fp8_attention_decode_workspace_size.restype = sz
     for name in ("fp8_quantize_blockwise", "fp8_quantize_columnwise_t",
                  "fp8_quantize_mx_columnwise_t", "fp8_quantize_1x128_and_columnwise_t",
-                 "fp8_quantize_mx_and_columnwise_t",
+                 "fp8_quantize_mx_and_columnwise_t", "fp8_grouped_gemm_mx",
                  "fp8_quantize_delayed",
                  "fp8_quantize_blockwise_batched",
                  "fp8_quantize_delayed_noalloc",
@@ -545,6 +547,33 @@ def grouped_gemm(offsets: torch.Tensor, a: torch.Tensor, sa: torch.Tensor, b: to
         return c
     name = "fp8_grouped_gemm_pow2" if pow2 else "fp8_grouped_gemm"
     _check(getattr(load(), name)(*args), name)
+    return c
+
+
+def grouped_gemm_mx(offsets: torch.Tensor, a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor,
+                    sb: torch.Tensor, fa: int = E4M3, fb: int = E4M3,
+                    c: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Grouped microscaling GEMM: rows [offsets[g], offsets[g+1]) of a[total_M, K] times
+    b[g][N, K]^T, with E8M0 scale bytes sa mx_scale_shape(total_M, K) and sb
+    [G, *mx_scale_shape(N, K)] (quantize_mx of a and of each expert)."""
+    if b.dim() != 3 or b.dtype != torch.uint8 or not b.is_cuda:
+        raise ValueError("b must be a uint8 device tensor [G, N, K]")
+    G, N, K = b.shape
+    if (b.stride(2) != 1 and K > 1) or b.stride(1) < K or (G > 1 and b.stride(0) != N * b.stride(1)):
+        raise ValueError("b must hold [G, N, K] with unit column stride and experts N rows apart")
+    _need(offsets, (G + 1,), torch.int64, "offsets")
+    if a.dim() != 2 or a.shape[1] != K:
+        raise ValueError("a must be [total_M, K]")
+    _need_matrix(a, a.shape, torch.uint8, "a")
+    total_m = a.shape[0]
+    _need(sa, mx_scale_shape(total_m, K), torch.uint8, "sa")
+    _need(sb, (G,) + mx_scale_shape(N, K), torch.uint8, "sb")
+    if c is None:
+        c = _bf16_out(total_m, N, a.device)
+    _need_matrix(c, (total_m, N), torch.bfloat16, "c")
+    _check(load().fp8_grouped_gemm_mx(G, _ptr(offsets), total_m, N, K, _ptr(a), a.stride(0), fa,
+                                      _ptr(sa), _ptr(b), b.stride(1), fb, _ptr(sb), _ptr(c),
+                                      c.stride(0), _stream(stream)), "fp8_grouped_gemm_mx")
     return c
 
 

@@ -55,6 +55,25 @@ int gemm_mx_entry(int tile, int64_t M, int64_t N, int64_t K, const void* A, int6
   return gemm_fprop_mx(fa, fb, p, tile, st);
 }
 
+int grouped_mx_entry(int tile, int32_t G, const int64_t* offsets, int64_t M, int64_t N, int64_t K,
+                     const void* A, int64_t lda, int fa, const void* sa, const void* B,
+                     int64_t ldb, int fb, const void* sb, void* C, int64_t ldc, hipStream_t st) {
+  GemmParams p{};
+  bool empty = false;
+  const int s = grouped_params(G, offsets, M, N, K, A, lda, fa, static_cast<const float*>(sa), B,
+                               ldb, fb, static_cast<const float*>(sb), C, ldc, p, empty);
+  if (s != FP8BS_OK || empty) return s;
+  if (!aligned4(sa) || !aligned4(sb)) return FP8BS_ERR_ALIGN;
+  // expert g's weight scale words: [ceil(K/128)][N] from sb + g * ceil(K/128) * N
+  p.sb_ks = N; p.sb_rs = 1;
+  p.sb_group_stride = ceil_div(K, 128) * N;
+  p.sb_bytes = p.sb_group_stride * 4;
+  if (p.sb_bytes >= (int64_t(1) << 32)) return FP8BS_ERR_SHAPE;
+  const int cus = device_cus();
+  if (cus <= 0) return FP8BS_ERR_LAUNCH;
+  return gemm_grouped_mx(fa, fb, cus, p, tile, st);
+}
+
 int gemm_grouped_entry(bool pow2, int tile, int32_t G, const int64_t* offsets, int64_t M,
                        int64_t N, int64_t K, const void* A, int64_t lda, int fa, const float* sa,
                        const void* B, int64_t ldb, int fb, const float* sb, void* C, int64_t ldc,
@@ -79,6 +98,16 @@ extern "C" int fp8_gemm_mx(int64_t M, int64_t N, int64_t K, const void* A, int64
                            const void* scale_e8m0_b, void* C_bf16, int64_t ldc, void* stream) {
   return gemm_mx_entry(FP8BS_TILE_AUTO, M, N, K, A, lda, fa, scale_e8m0_a, B, ldb, fb,
                        scale_e8m0_b, C_bf16, ldc, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int fp8_grouped_gemm_mx(int32_t num_groups, const int64_t* group_offsets,
+                                   int64_t total_M, int64_t N, int64_t K, const void* A,
+                                   int64_t lda, int fa, const void* scale_e8m0_a, const void* B,
+                                   int64_t ldb, int fb, const void* scale_e8m0_b, void* C_bf16,
+                                   int64_t ldc, void* stream) {
+  return grouped_mx_entry(FP8BS_TILE_AUTO, num_groups, group_offsets, total_M, N, K, A, lda, fa,
+                          scale_e8m0_a, B, ldb, fb, scale_e8m0_b, C_bf16, ldc,
+                          static_cast<hipStream_t>(stream));
 }
 
 extern "C" int fp8_gemm_blockscaled(int layout, int64_t M, int64_t N, int64_t K, const void* A,

@@ -1617,6 +1617,8 @@ inline int grouped_params(int32_t num_groups, const int64_t* group_offsets, int6
 FP8BS_HIDDEN int gemm_fprop_fp32(int sm, int fa, int fb, const GemmParams& p, int tile, hipStream_t st);
 FP8BS_HIDDEN int gemm_fprop_pow2(int sm, int fa, int fb, const GemmParams& p, int tile, hipStream_t st);
 FP8BS_HIDDEN int gemm_fprop_mx(int fa, int fb, const GemmParams& p, int tile, hipStream_t st);
+FP8BS_HIDDEN int gemm_grouped_mx(int fa, int fb, int cus, const GemmParams& p, int tile,
+                                 hipStream_t st);
 FP8BS_HIDDEN int gemm_dgrad(int sm, int fa, int fb, const GemmParams& p, int tile, hipStream_t st);
 FP8BS_HIDDEN int gemm_wgrad(int sm, int fa, int fb, const GemmParams& p, int tile, hipStream_t st);
 FP8BS_HIDDEN int gemm_grouped(bool pow2, int fa, int fb, int cus, const GemmParams& p, int tile,

@@ -368,6 +368,20 @@ int fp8_gemm_mx(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int
                 const void* scale_e8m0_a, const void* B, int64_t ldb, int fb,
                 const void* scale_e8m0_b, void* C_bf16, int64_t ldc, void* stream);
 
+/* Grouped (mixture-of-experts) microscaling GEMM -- the passages of fp8_grouped_gemm (experts)
+ * and fp8_quantize_mx (microscaling).  Groups, offsets, A, B, C, alignment and size limits as
+ * fp8_grouped_gemm; the scales are E8M0 bytes, one per 32 K elements of every row, applied by
+ * the matrix cores as in fp8_gemm_mx:
+ *   scale_e8m0_a: [ceil(K/128)][total_M][4] bytes (fp8_quantize_mx of A)
+ *   scale_e8m0_b: [num_groups][ceil(K/128)][N][4] bytes (fp8_quantize_mx of each expert's B,
+ *                 one after the other)
+ * both 4-byte aligned (FP8BS_ERR_ALIGN); scale_e8m0_a and one expert's scales below 4 GiB.
+ * Errors: FP8BS_ERR_NULL, FP8BS_ERR_SHAPE, FP8BS_ERR_ALIGN, FP8BS_ERR_ARG, FP8BS_ERR_LAUNCH. */
+int fp8_grouped_gemm_mx(int32_t num_groups, const int64_t* group_offsets, int64_t total_M,
+                        int64_t N, int64_t K, const void* A, int64_t lda, int fa,
+                        const void* scale_e8m0_a, const void* B, int64_t ldb, int fb,
+                        const void* scale_e8m0_b, void* C_bf16, int64_t ldc, void* stream);
+
 /* Block-scaled FP8 GEMM with power-of-2 scales -- "NVIDIA NeMo RL logra una aceleración del 48%
  * ...", section "Por qué esto es importante para la economía de la IA" (the power-of-2 scale
  * option).  Same arguments, layouts, granularities, scale arrays, results and errors as

@@ -474,6 +474,22 @@ def test_mx_validation():
     assert qmr(FAKE, 256, 64, 64, 0, FAKE, 64, FAKE_ODD, FAKE, 256, FAKE, None) == bsq.ERR_ALIGN
     assert qmr(FAKE, 256, 64, 64, 0, FAKE, 64, FAKE, FAKE, 256, FAKE_ODD, None) == bsq.ERR_ALIGN
     assert qmr(None, 0, 64, 64, 0, None, 64, None, None, 0, None, None) == bsq.OK
+    # grouped form
+    gmx = lib.fp8_grouped_gemm_mx
+    def grouped(**kw):
+        v = dict(G=4, off=FAKE, M=512, N=256, K=256, lda=256, fa=0, sa=FAKE, ldb=256, fb=0, sb=FAKE,
+                 C=FAKE, ldc=256)
+        v.update(kw)
+        return gmx(v["G"], v["off"], v["M"], v["N"], v["K"], FAKE, v["lda"], v["fa"], v["sa"], FAKE,
+                   v["ldb"], v["fb"], v["sb"], v["C"], v["ldc"], None)
+    assert grouped(G=-1) == bsq.ERR_ARG
+    assert grouped(fb=9) == bsq.ERR_ARG
+    assert grouped(K=0) == bsq.ERR_SHAPE
+    assert grouped(off=None) == bsq.ERR_NULL
+    assert grouped(sb=None) == bsq.ERR_NULL
+    assert grouped(sa=FAKE + 2) == bsq.ERR_ALIGN
+    assert grouped(sb=FAKE + 1) == bsq.ERR_ALIGN
+    assert grouped(M=0) == bsq.OK and grouped(G=0) == bsq.OK
     # GEMM: formats, misaligned scales, null scales, pitches; empty is a no-op
     def gemm(**kw):
         v = dict(M=64, N=64, K=128, lda=128, fa=0, sa=FAKE, ldb=128, fb=0, sb=FAKE, C=FAKE, ldc=64)

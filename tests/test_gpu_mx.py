@@ -300,3 +300,48 @@ def test_mx_backward_wgrad_and_dgrad(gpu):
     o_wt, o_swt = oracle.quantize_mx_columnwise_t(w, E4)
     r, mag = ref(o_dy, o_sdy, o_wt, o_swt)
     gemm_check(dx, r, mag, "mx dgrad")
+
+
+# ------------------------------------------------------------------ grouped (MoE) form
+
+def run_grouped_mx(gpu, counts, N, K, seed, sample_rows=None):
+    counts = np.asarray(counts, dtype=np.int64)
+    G = len(counts)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    T = int(off[-1])
+    a = synth.activations_with_outliers(T, K, seed, f"mx/grouped/A/{T}x{K}")
+    qa, sa = oracle.quantize_mx(a, E4)
+    qbs, sbs = [], []
+    for g in range(G):
+        b = synth.normal((N, K), 0.02, seed + g, f"mx/grouped/B{g}/{N}x{K}")
+        qb, sb = oracle.quantize_mx(b, E4)
+        qbs.append(qb)
+        sbs.append(sb)
+    bd = torch.from_numpy(np.stack(qbs)).cuda()
+    sbd = torch.stack([device_scale_bytes(s, K) for s in sbs])      # NaN bytes past K
+    c = gpu.grouped_gemm_mx(torch.from_numpy(off).cuda(), device_codes(qa, K), device_scale_bytes(sa, K),
+                            bd, sbd)
+    torch.cuda.synchronize()
+    adq = oracle.dequantize(qa, E4, oracle.BLOCK_1x32, oracle.e8m0_decode(sa))
+    rows = np.arange(T) if sample_rows is None else np.asarray(sample_rows)
+    group_of = np.searchsorted(off, rows, side="right") - 1
+    ref = np.zeros((len(rows), N))
+    mag = np.zeros((len(rows), N))
+    for g in np.unique(group_of):
+        sel = np.nonzero(group_of == g)[0]
+        bdq = oracle.dequantize(qbs[g], E4, oracle.BLOCK_1x32, oracle.e8m0_decode(sbs[g]))
+        ref[sel] = adq[rows[sel]] @ bdq.T
+        mag[sel] = np.abs(adq[rows[sel]]) @ np.abs(bdq).T
+    gemm_check(c[torch.as_tensor(rows, device="cuda")], ref, mag, f"grouped mx {G} groups")
+
+
+def test_grouped_gemm_mx_ragged_groups(gpu):
+    # empty groups, a one-row group, groups across tile boundaries, ragged K (10 chunks of 32)
+    run_grouped_mx(gpu, [0, 1, 300, 0, 257, 130, 64], 384, 320, 11)
+
+
+def test_grouped_gemm_mx_moe_shape_sampled(gpu):
+    # 32 experts with Zipf routing, gate/up-shaped experts (N 1536, K 2048), sampled rows
+    counts = synth.moe_routing(2048, 32, 8, 1.1, 5)
+    rows = np.arange(0, int(counts.sum()), 37)
+    run_grouped_mx(gpu, counts, 1536, 2048, 12, sample_rows=rows)
