@@ -1225,8 +1225,8 @@ def bench_copy(args):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(see the sharding notes in the design document)", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path; the kernels "
+              "run on one GPU's share of the work", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
