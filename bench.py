@@ -47,6 +47,9 @@ HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 GEMM_COUNTERS = os.path.join(ROOT, "profiles", "gemm_kernel_llama8b_fprop_counters.txt")
 GEMM_COUNTERS_POW2 = os.path.join(ROOT, "profiles", "gemm_kernel_pow2_llama8b_fprop_counters.txt")
 GEMM_COUNTERS_MX = os.path.join(ROOT, "profiles", "gemm_kernel_mx_llama8b_fprop_counters.txt")
+QUANT_COUNTERS = os.path.join(ROOT, "profiles", "quantize_kernels_sweep_counters.txt")
+QUANT_SOURCES = [os.path.join(ROOT, "block_scaled_quantize_amd", "csrc", f)
+                 for f in ("quantize.hip", "common.h")]
 GEMM_SOURCES = [os.path.join(ROOT, "block_scaled_quantize_amd", "csrc", f)
                 for f in ("gemm_impl.h", "gemm.hip", "gemm_fprop.hip", "gemm_fprop_pow2.hip",
                           "gemm_dgrad.hip", "gemm_wgrad.hip", "gemm_grouped.hip", "gemm_mx.hip",
@@ -549,6 +552,7 @@ def bench_quant_sweep(args):
         del xs, base
         torch.cuda.empty_cache()
     head = cases["131072x4096/1x128/fp32"]
+    traffic = measured_traffic(QUANT_COUNTERS, QUANT_SOURCES)
     res = dict(metric="quantize GB/s (bf16 -> E4M3 codes + scales), % of MI355X HBM peak",
                value=head["gbps"], unit="GB/s", n_gpus=1, steps=max(args.steps, 10),
                warmup=args.warmup, ms_per_step=head["us"] / 1e3, higher_is_better=True,
@@ -557,8 +561,11 @@ def bench_quant_sweep(args):
                config=dict(workload="quantizer-sweep", headline="131072x4096 1x128 fp32-scale",
                            distribution="Student-t(3)"),
                roofline=dict(bound="hbm", achieved=head["gbps"], peak=HBM_PEAK_GBPS, unit="GB/s",
-                             frac=head["hbm_frac"], traffic=None,
-                             kernel="quant_1x128_kernel<E4M3,fp32,vec>",
+                             frac=head["hbm_frac"], traffic=traffic["bytes"],
+                             traffic_unit="HBM bytes per launch",
+                             traffic_algorithmic=traffic["algorithmic"],
+                             traffic_source=traffic["source"],
+                             kernel="quant_1x128_rows_kernel<E4M3,fp32,non-temporal stores>",
                              per_launch_bytes=head["bytes"], mean_launch_us=head["us"]),
                cases=cases)
     if not args.no_cpu_baseline:
