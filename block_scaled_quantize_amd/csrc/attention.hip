@@ -138,8 +138,18 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_mma_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t s_v[W][KT * 128];
   __shared__ __attribute__((aligned(16))) float s_f[W][2 * KT];   // the batch's K, V factors
 
-  const int64_t bh = SPLIT ? blockIdx.x / S : blockIdx.x;   // sequence x KV head
-  const int sp = SPLIT ? (int)(blockIdx.x % S) : 0;
+  // Workgroup ids are dealt to the 8 XCDs round robin; the whole-sequence form renumbers them so
+  // that each XCD takes a contiguous range (sequence-major): the KV heads of a sequence then share
+  // one XCD's L2, where the token-major factor lines they all read are fetched once instead of
+  // once per head (3% faster on 64 sequences; the split form measured slower with it).
+  int64_t id = blockIdx.x;
+  if constexpr (!SPLIT) {
+    const int64_t n = gridDim.x, q8 = n / 8, r8 = n % 8;
+    const int64_t xcd = blockIdx.x % 8, local = blockIdx.x / 8;
+    id = xcd < r8 ? xcd * (q8 + 1) + local : r8 * (q8 + 1) + (xcd - r8) * q8 + local;
+  }
+  const int64_t bh = SPLIT ? id / S : id;   // sequence x KV head
+  const int sp = SPLIT ? (int)(id % S) : 0;
   const int64_t b = bh / KVH, kvh = bh % KVH;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15, qg = lane >> 4;   // MFMA row / column, and k group
