@@ -27,6 +27,8 @@
  *      1x128 blocks of a [R, C] matrix ....... float[ceil(C/128)][R]  (column block major)
  *      128x128 tiles of a [R, C] matrix ...... float[ceil(R/128)][ceil(C/128)]
  *      per tensor ............................. float[1]
+ *      microscaling (32-element row blocks) ... E8M0 bytes [ceil(C/128)][R][4] (byte i of a word:
+ *                                               columns 128 c + 32 i .. + 31; 2^(byte - 127))
  *  - Quantization: for each block, amax = max |x|; s = fl32(FMAX / amax) (IEEE division);
  *    amax == 0 or non-finite -> s = 1; s == +inf -> FLT_MAX; power-of-2 mode rounds s down to
  *    2^floor(log2 s); each code = round-to-nearest-even of fl32(x * s), saturating at +-FMAX
