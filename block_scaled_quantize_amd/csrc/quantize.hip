@@ -33,9 +33,8 @@ constexpr int64_t kNtStoreBytes = int64_t(256) << 20;
 
 // ---------------------------------------------------------------- element access
 // Load 16 consecutive bf16 of row r starting at column c0 into 8 dwords.  Elements outside the
-// matrix read as +0 (they do not change an amax).  VEC: 16-byte aligned rows.  NT: non-temporal
-// loads.
-template <bool VEC, bool NT = false>
+// matrix read as +0 (they do not change an amax).  VEC: 16-byte aligned rows.
+template <bool VEC>
 __device__ __forceinline__ void load16(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                        int64_t ld, int64_t r, int64_t c0, uint32_t (&d)[8]) {
   if (r >= rows || c0 >= cols) {
@@ -45,17 +44,10 @@ __device__ __forceinline__ void load16(const uint16_t* __restrict__ x, int64_t r
   }
   const uint16_t* p = x + r * ld + c0;
   if (VEC && c0 + 16 <= cols) {
-    if constexpr (NT) {
-      const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-      const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 8));
-      d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w;
-      d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
-    } else {
-      const uint4 a = *reinterpret_cast<const uint4*>(p);
-      const uint4 b = *reinterpret_cast<const uint4*>(p + 8);
-      d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w;
-      d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
-    }
+    const uint4 a = *reinterpret_cast<const uint4*>(p);
+    const uint4 b = *reinterpret_cast<const uint4*>(p + 8);
+    d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w;
+    d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
     return;
   }
 #pragma unroll
