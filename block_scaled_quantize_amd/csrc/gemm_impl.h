@@ -97,7 +97,7 @@ constexpr int kScaleHwRows = 4;
 // and each lane gives the MFMA the byte of its own 32-wide k chunk.
 constexpr int kScaleMx = 5;
 
-constexpr int kGroupM = 8;      // tile-rows per L2 group in the tile order
+constexpr int kGroupM = 4;      // tile-rows per L2 group in the tile order (2, 4, 6, 8, 16 measured)
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kStaticLdsReserve = 8448;   // the grouped kernel's group bounds and prefixes
 constexpr bool kPersistentDense = true;   // two-stage dense tiles on a persistent grid
