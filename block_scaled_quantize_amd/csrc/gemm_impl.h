@@ -97,7 +97,8 @@ constexpr int kScaleHwRows = 4;
 // and each lane gives the MFMA the byte of its own 32-wide k chunk.
 constexpr int kScaleMx = 5;
 
-constexpr int kGroupM = 4;      // tile-rows per L2 group in the tile order (2, 4, 6, 8, 16 measured)
+constexpr int kGroupM = 4;      // tile-rows per L2 group in the dense tile order (2, 4, 6, 8, 16 measured)
+constexpr int kGroupMGrouped = 8;   // ... in the grouped (MoE) order (4 and 8 measured)
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kStaticLdsReserve = 8448;   // the grouped kernel's group bounds and prefixes
 constexpr bool kPersistentDense = true;   // two-stage dense tiles on a persistent grid
@@ -1165,16 +1166,17 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
 
 
 // Map a linear workgroup id to a tile so that each of the 8 XCDs (ids are dealt round robin)
-// gets a contiguous range of tiles, ordered in groups of kGroupM tile-rows for L2 reuse.
+// gets a contiguous range of tiles, ordered in groups of GROUP_M tile-rows for L2 reuse.
+template <int GROUP_M = kGroupM>
 __device__ __forceinline__ void tile_of(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int total = tiles_m * tiles_n;
   const int q = total / 8, r = total % 8;
   const int xcd = id % 8, local = id / 8;
   const int pid = xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
-  const int width = kGroupM * tiles_n;
+  const int width = GROUP_M * tiles_n;
   const int grp = pid / width;
-  const int first = grp * kGroupM;
-  const int gsz = min(tiles_m - first, kGroupM);
+  const int first = grp * GROUP_M;
+  const int gsz = min(tiles_m - first, GROUP_M);
   const int in = pid % width;
   tm = first + in % gsz;
   tn = in / gsz;
@@ -1308,7 +1310,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(GemmParams
   // tiles, so the 32 workgroups of an XCD share A rows and expert weight tiles in its L2.
   auto tile_at = [&](int id) {
     int mt, tn;
-    tile_of(id, m_tiles, tiles_n, mt, tn);
+    tile_of<kGroupMGrouped>(id, m_tiles, tiles_n, mt, tn);
     // the last group with s_prefix[g] <= mt (the prefix does not decrease): the number of
     // g in [1, G) with s_prefix[g] <= mt, counted 64 groups at a time by the wave's lanes (one
     // LDS round trip per 64 groups instead of one per step of a binary search)
