@@ -501,3 +501,25 @@ def test_mx_validation():
     assert gemm(sa=None) == bsq.ERR_NULL
     assert gemm(ldb=100) == bsq.ERR_SHAPE
     assert gemm(M=0) == bsq.OK
+
+
+def test_binding_rejects_bad_tensors_before_any_call():
+    """The Python wrappers of the microscaling and one-pass entry points validate dtype, rank and
+    device before marshalling anything (CPU tensors here: nothing reaches the library)."""
+    import torch
+    x = torch.zeros((4, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        bsq.quantize_mx(x.float(), bsq.E4M3)                        # not bf16
+    with pytest.raises(ValueError):
+        bsq.quantize_mx_columnwise_t(x[:, ::2], bsq.E4M3)           # column stride 2
+    with pytest.raises(ValueError):
+        bsq.quantize_mx_and_columnwise_t(x.reshape(-1), bsq.E4M3)   # not 2-D
+    with pytest.raises(ValueError):
+        bsq.quantize_1x128_and_columnwise_t(x, bsq.E4M3)            # host tensors
+    a = torch.zeros((4, 128), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        bsq.gemm_mx(a, torch.zeros((1, 4, 4), dtype=torch.uint8), a[:, :64],
+                    torch.zeros((1, 4, 4), dtype=torch.uint8))      # K mismatch
+    with pytest.raises(ValueError):
+        bsq.grouped_gemm_mx(torch.zeros(2, dtype=torch.int64), a, torch.zeros((1, 4, 4), dtype=torch.uint8),
+                            a, torch.zeros((1, 4, 4), dtype=torch.uint8))   # b not [G, N, K]
